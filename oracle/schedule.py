@@ -1,0 +1,161 @@
+"""Expected task lists of the persistent kernels (test infrastructure only).
+
+This is an independent Python re-derivation, by explicit enumeration, of the
+ticket -> task schedule the GPU library computes in closed form. The GPU trace
+must reproduce it exactly. It follows the pages' tile-centric scheme:
+
+  * TileLink talk summary, "Technical Deep Dive": a wait takes only a tile id;
+    rank id, barrier id, tiles per rank and barriers per rank are recovered
+    from it by an affine map for static workloads, and from lookup tables
+    passed as parameters for dynamic (MoE) workloads;
+  * same section: pull mode has two barriers (data ready at the source, then
+    transfer complete); the "transfer complete" barrier is the per-slab flag
+    published here by copy tasks;
+  * same section: swizzling reorders tile access and communication so the
+    communication lines up with compute -- here the tiles start at the local
+    rank's rows and walk the other ranks in rotated order, and copies are
+    issued in that same rotated order.
+
+Schedule definition (shared contract with the device code; written here
+independently):
+
+AG-GEMM (rank count R, rows per rank m, gathered M = R*m, tile BM x BN, slab
+rows S, copy-task rows CT with S % CT == 0):
+  chunk sequence for copies: swizzled -> (l+1, l+2, ..., l+R-1, l) mod R;
+  natural -> (0, 1, ..., R-1).
+  copy ticket u < R*ceil(m/CT): chunk = seq[u // ceil(m/CT)], piece t = u % ..,
+  rows [c*m + t*CT, c*m + min((t+1)*CT, m)), slab (c, (t*CT)//S).
+  tile tickets follow the copies: v = ticket - n_copy; row block
+  rb = (rb0 + v // n_cb) % n_rb with rb0 = (l*m)//BM when swizzled, else 0;
+  column block cb = v % n_cb. A tile waits for every slab overlapping its rows
+  that belongs to a chunk other than the local one (local rows are read from
+  the local shard directly).
+GEMM-RS: tiles only, same rotation with rb0 = (l*M/R)//BM when swizzled.
+MoE: the AG-GEMM copy list, then one tile per (expert e, column block cb,
+  row tile rt) in that nesting order; expert e's rows
+  [off_e + rt*BM, min(off_e + (rt+1)*BM, off_{e+1})) of the expert-sorted slot
+  list. A tile waits for every non-local slab between the slab of its first
+  token and the slab of its last token (tokens ascend within an expert).
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import List, Tuple
+
+
+def _cdiv(a: int, b: int) -> int:
+    return -(-a // b)
+
+
+@dataclass(frozen=True)
+class CopyTask:
+    ticket: int
+    chunk: int
+    piece: int
+    row0: int       # first gathered row
+    row1: int       # one past the last gathered row
+    slab: int       # global slab id chunk*bpr + s
+
+
+@dataclass(frozen=True)
+class Tile:
+    ticket: int
+    rb: int
+    cb: int
+    deps: Tuple[int, ...]   # global slab ids waited on
+
+
+def copy_sequence(R: int, local: int, swizzle: bool) -> List[int]:
+    if swizzle:
+        return [(local + p) % R for p in range(1, R)] + [local]
+    return list(range(R))
+
+
+def copy_tasks(R, m, S, CT, local, swizzle, first_ticket=0) -> List[CopyTask]:
+    if S % CT:
+        raise ValueError("slab rows must be a multiple of copy-task rows")
+    bpr = _cdiv(m, S)
+    out = []
+    ticket = first_ticket
+    for c in copy_sequence(R, local, swizzle):
+        t = 0
+        r = 0
+        while r < m:
+            r1 = min(r + CT, m)
+            out.append(CopyTask(ticket, c, t, c * m + r, c * m + r1, c * bpr + r // S))
+            ticket += 1
+            t += 1
+            r = r1
+    return out
+
+
+def slab_targets(R, m, S, CT) -> List[int]:
+    """Number of copy tasks that complete each slab (global slab order)."""
+    bpr = _cdiv(m, S)
+    tgt = [0] * (R * bpr)
+    for c in range(R):
+        r = 0
+        while r < m:
+            tgt[c * bpr + r // S] += 1
+            r = min(r + CT, m)
+    return tgt
+
+
+def ag_gemm_plan(R, m, K, N, local, BM, BN, S, CT, swizzle=True, mode="fused"):
+    """Full ticket list for the AG-GEMM kernel: list of CopyTask and Tile."""
+    M = R * m
+    n_rb, n_cb = _cdiv(M, BM), _cdiv(N, BN)
+    bpr = _cdiv(m, S)
+    tasks = []
+    if mode in ("fused", "copy_only"):
+        tasks += copy_tasks(R, m, S, CT, local, swizzle)
+    if mode in ("fused", "gemm_only"):
+        rb0 = (local * m) // BM if swizzle else 0
+        base = len(tasks)
+        for v in range(n_rb * n_cb):
+            rb = (rb0 + v // n_cb) % n_rb
+            cb = v % n_cb
+            deps = set()
+            if mode == "fused":
+                for row in range(rb * BM, min((rb + 1) * BM, M)):
+                    c = row // m
+                    if c != local:
+                        deps.add(c * bpr + (row % m) // S)
+            tasks.append(Tile(base + v, rb, cb, tuple(sorted(deps))))
+    return tasks
+
+
+def gemm_rs_plan(R, M, N, local, BM, BN, swizzle=True):
+    """Ticket list of the GEMM-RS kernel: (ticket, rb, cb, is_local_block)."""
+    n_rb, n_cb = _cdiv(M, BM), _cdiv(N, BN)
+    blk = M // R
+    rb0 = (local * blk) // BM if swizzle else 0
+    out = []
+    for v in range(n_rb * n_cb):
+        rb = (rb0 + v // n_cb) % n_rb
+        cb = v % n_cb
+        lo, hi = rb * BM, min((rb + 1) * BM, M)
+        has_local = lo < (local + 1) * blk and hi > local * blk
+        out.append((v, rb, cb, has_local))
+    return out
+
+
+def moe_tiles(counts, offsets, perm, topk, R, m, N, local, BM, BN, S):
+    """MoE tile list in ticket order after the copies:
+    tuples (expert, row_start, nrows, cb, deps)."""
+    bpr = _cdiv(m, S)
+    n_cb = _cdiv(N, BN)
+    out = []
+    for e in range(len(counts)):
+        nrt = _cdiv(int(counts[e]), BM)
+        for cb in range(n_cb):
+            for rt in range(nrt):
+                r0 = int(offsets[e]) + rt * BM
+                r1 = min(r0 + BM, int(offsets[e + 1]))
+                t_first = int(perm[r0]) // topk
+                t_last = int(perm[r1 - 1]) // topk
+                s_lo = (t_first // m) * bpr + (t_first % m) // S
+                s_hi = (t_last // m) * bpr + (t_last % m) // S
+                deps = tuple(s for s in range(s_lo, s_hi + 1) if s // bpr != local)
+                out.append((e, r0, r1 - r0, cb, deps))
+    return out

@@ -1,0 +1,104 @@
+"""Invariants of the expected schedules (oracle/schedule.py), checked by
+brute-force enumeration: every tile exactly once, every gathered row copied
+exactly once, every dependency published by tasks with smaller tickets, and
+the rotated (swizzled) order starting at the local rank."""
+import itertools
+
+import numpy as np
+import pytest
+
+from oracle import schedule as sch
+import oracle
+
+CASES = [
+    # R, m, K, N, local, BM, BN, S, CT
+    (4, 128, 256, 256, 0, 128, 224, 128, 32),
+    (8, 512, 4096, 1792, 0, 128, 224, 128, 32),
+    (8, 1024, 8192, 3584, 0, 256, 224, 256, 16),
+    (8, 1024, 8192, 3584, 3, 256, 224, 256, 16),
+    (3, 100, 64, 72, 1, 64, 32, 48, 16),      # ragged: m % BM != 0, N % BN != 0
+    (5, 37, 32, 40, 4, 32, 32, 32, 8),
+]
+
+
+@pytest.mark.parametrize("case", CASES)
+@pytest.mark.parametrize("swizzle", [True, False])
+def test_ag_gemm_plan_invariants(case, swizzle):
+    R, m, K, N, local, BM, BN, S, CT = case
+    M = R * m
+    plan = sch.ag_gemm_plan(R, m, K, N, local, BM, BN, S, CT, swizzle)
+    assert [t.ticket for t in plan] == list(range(len(plan)))
+    copies = [t for t in plan if isinstance(t, sch.CopyTask)]
+    tiles = [t for t in plan if isinstance(t, sch.Tile)]
+    # every gathered row copied exactly once
+    rows = np.zeros(M, dtype=np.int64)
+    for c in copies:
+        rows[c.row0:c.row1] += 1
+        assert c.row0 // m == c.chunk and (c.row1 - 1) // m == c.chunk
+    assert np.all(rows == 1)
+    # every tile exactly once
+    n_rb, n_cb = -(-M // BM), -(-N // BN)
+    assert sorted((t.rb, t.cb) for t in tiles) == sorted(itertools.product(range(n_rb), range(n_cb)))
+    # each slab completes by exactly its target number of copies, all with
+    # tickets smaller than any tile that waits on it
+    tgt = sch.slab_targets(R, m, S, CT)
+    done = {}
+    for c in copies:
+        done.setdefault(c.slab, []).append(c.ticket)
+    assert {s: len(v) for s, v in done.items()} == {s: n for s, n in enumerate(tgt) if n}
+    for t in tiles:
+        for s in t.deps:
+            assert max(done[s]) < t.ticket
+            assert s // (-(-m // S)) != local
+    # swizzled: the first tile row block contains the local rank's first row,
+    # and the first copies are for rank local+1
+    if swizzle:
+        assert tiles[0].rb * BM <= local * m < (tiles[0].rb + 1) * BM
+        if R > 1:
+            assert copies[0].chunk == (local + 1) % R
+        assert copies[-1].chunk == local
+    else:
+        assert tiles[0].rb == 0 and copies[0].chunk == 0
+
+
+def test_ag_gemm_plan_modes():
+    args = (4, 128, 256, 256, 1, 128, 224, 128, 32)
+    full = sch.ag_gemm_plan(*args)
+    g = sch.ag_gemm_plan(*args, mode="gemm_only")
+    c = sch.ag_gemm_plan(*args, mode="copy_only")
+    assert all(isinstance(t, sch.Tile) and not t.deps for t in g)
+    assert all(isinstance(t, sch.CopyTask) for t in c)
+    assert len(g) + len(c) == len(full)
+
+
+@pytest.mark.parametrize("R,M,N,local,BM,BN", [(8, 4096, 4096, 0, 256, 256), (8, 4096, 4096, 5, 256, 256),
+                                               (4, 96, 40, 2, 16, 16), (3, 90, 50, 1, 32, 32)])
+def test_gemm_rs_plan_invariants(R, M, N, local, BM, BN):
+    plan = sch.gemm_rs_plan(R, M, N, local, BM, BN)
+    n_rb, n_cb = -(-M // BM), -(-N // BN)
+    assert sorted((rb, cb) for _, rb, cb, _ in plan) == sorted(itertools.product(range(n_rb), range(n_cb)))
+    blk = M // R
+    assert plan[0][3]                                  # local row block first
+    assert plan[0][1] * BM <= local * blk < (plan[0][1] + 1) * BM
+    # the local flags mark exactly the tiles that touch the local block
+    for _, rb, cb, loc in plan:
+        assert loc == (rb * BM < (local + 1) * blk and min((rb + 1) * BM, M) > local * blk)
+
+
+def test_moe_tiles_cover_every_slot_once():
+    rng = np.random.default_rng(4)
+    R, m, N, E, BM, BN, S, local = 8, 64, 96, 6, 32, 32, 32, 2
+    lg = rng.standard_normal((R * m, E)).astype(np.float32)
+    ids, _ = oracle.route_topk(lg, 2)
+    counts, offsets, perm = oracle.sort_by_expert(ids, E)
+    tiles = sch.moe_tiles(counts, offsets, perm, 2, R, m, N, local, BM, BN, S)
+    n_cb = -(-N // BN)
+    cover = np.zeros((R * m * 2, n_cb), dtype=np.int64)
+    bpr = -(-m // S)
+    for e, r0, nr, cb, deps in tiles:
+        assert 0 < nr <= BM and offsets[e] <= r0 and r0 + nr <= offsets[e + 1]
+        cover[perm[r0:r0 + nr], cb] += 1
+        toks = perm[r0:r0 + nr] // 2
+        need = {(t // m) * bpr + (t % m) // S for t in toks if t // m != local}
+        assert need <= set(deps)
+    assert np.all(cover == 1)

@@ -1,0 +1,182 @@
+"""Seeded synthetic inputs for the five tensor-parallel LLM-layer workloads.
+
+This module is shared by the CPU oracle, the tests and the benchmark. It holds
+no arithmetic of the method itself (no gather, product, reduction or routing):
+it only draws random numbers and encodes them as bfloat16 bit patterns, so the
+GPU path and the oracle read the very same bytes.
+
+Recipe (the pages fix only the layer kind; shapes and seeds are the workload
+definitions below):
+  * generator: ``numpy.random.default_rng(seed)`` (PCG64), float64 draws;
+  * float64 -> float32 by numpy's cast (round-to-nearest-even), then
+    float32 -> bfloat16 by round-to-nearest-even on the low 16 bits;
+  * "N(0, s)" means a normal with standard deviation s;
+  * draw order: every operand in the order it is listed in the workload.
+
+bf16 tensors are returned as ``numpy.uint16`` arrays of raw bit patterns.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+from typing import Dict, List, Optional
+
+import numpy as np
+
+__all__ = [
+    "f32_to_bf16_bits", "bf16_bits_to_f32", "AgGemmInputs", "GemmRsInputs",
+    "MoeInputs", "make_ag_gemm", "make_gemm_rs", "make_moe", "WORKLOADS",
+    "workload",
+]
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Encode float32 values as bfloat16 bits, round-to-nearest-even.
+
+    Inputs here are finite draws, so NaN/Inf handling is only kept correct
+    enough not to turn a NaN into Inf (quiet bit forced)."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    bias = np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))
+    out = ((u + bias) >> np.uint32(16)).astype(np.uint16)
+    nan = np.isnan(x)
+    if nan.any():
+        out[nan] = ((u[nan] >> np.uint32(16)) | np.uint32(0x40)).astype(np.uint16)
+    return out
+
+
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    """Decode bfloat16 bits (uint16) to float32 (exact)."""
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def _draw_bf16(rng: np.random.Generator, shape, dist: str, scale: float) -> np.ndarray:
+    if dist == "uniform":
+        v = rng.uniform(-scale, scale, size=shape)
+    elif dist == "normal":
+        v = rng.normal(0.0, scale, size=shape)
+    else:
+        raise ValueError(f"unknown distribution {dist!r}")
+    return f32_to_bf16_bits(v.astype(np.float32))
+
+
+@dataclass
+class AgGemmInputs:
+    """C = gather(A_0..A_{R-1}) x B; a_chunks[r] is rank r's [m, K] shard."""
+    R: int
+    m: int
+    K: int
+    N: int
+    a_chunks: List[np.ndarray]          # R x uint16 [m, K]
+    b: np.ndarray                       # uint16 [K, N]
+    seed: int = 0
+
+
+@dataclass
+class GemmRsInputs:
+    """out_l = row block l of (A x B + sum of the peers' partials)."""
+    R: int
+    M: int
+    K: int
+    N: int
+    local_rank: int
+    a: np.ndarray                       # uint16 [M, K]
+    b: np.ndarray                       # uint16 [K, N]
+    peers: Dict[int, np.ndarray]        # rank s != local -> uint16 [M, N]
+    seed: int = 0
+
+
+@dataclass
+class MoeInputs:
+    """Gathered tokens routed top-k over E experts, then a per-expert GEMM."""
+    R: int
+    m: int
+    K: int
+    N: int
+    E: int
+    topk: int
+    a_chunks: List[np.ndarray]          # R x uint16 [m, K]
+    logits: np.ndarray                  # float32 [R*m, E]
+    w: np.ndarray                       # uint16 [E, K, N]
+    seed: int = 0
+
+
+def make_ag_gemm(R: int, m: int, K: int, N: int, seed: int,
+                 dist: str = "normal", scale: float = 0.02) -> AgGemmInputs:
+    """Draw order: A_0 ... A_{R-1}, then B."""
+    rng = np.random.default_rng(seed)
+    chunks = [_draw_bf16(rng, (m, K), dist, scale) for _ in range(R)]
+    b = _draw_bf16(rng, (K, N), dist, scale)
+    return AgGemmInputs(R, m, K, N, chunks, b, seed)
+
+
+def make_gemm_rs(R: int, M: int, K: int, N: int, seed: int, local_rank: int = 0,
+                 dist: str = "normal", scale: float = 0.02,
+                 peer_scale: Optional[float] = None) -> GemmRsInputs:
+    """Draw order: A, B, then the peer partials P_s for s != local_rank in
+    ascending s, all N(0, scale) unless ``peer_scale`` is given."""
+    rng = np.random.default_rng(seed)
+    a = _draw_bf16(rng, (M, K), dist, scale)
+    b = _draw_bf16(rng, (K, N), dist, scale)
+    ps = scale if peer_scale is None else peer_scale
+    peers = {s: _draw_bf16(rng, (M, N), dist, ps) for s in range(R) if s != local_rank}
+    return GemmRsInputs(R, M, K, N, local_rank, a, b, peers, seed)
+
+
+def make_moe(R: int, m: int, K: int, N: int, E: int, seed: int, topk: int = 2,
+             scale: float = 0.02) -> MoeInputs:
+    """Draw order: A_0 ... A_{R-1} ~ N(0, scale); router logits float32
+    N(0, 1) [R*m, E]; then W_0 ... W_{E-1} ~ N(0, scale) [K, N] (one expert
+    at a time, so peak host memory stays near one expert's float64 draw)."""
+    rng = np.random.default_rng(seed)
+    chunks = [_draw_bf16(rng, (m, K), "normal", scale) for _ in range(R)]
+    logits = rng.normal(0.0, 1.0, size=(R * m, E)).astype(np.float32)
+    w = np.empty((E, K, N), dtype=np.uint16)
+    for e in range(E):
+        w[e] = _draw_bf16(rng, (K, N), "normal", scale)
+    return MoeInputs(R, m, K, N, E, topk, chunks, logits, w, seed)
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    op: str            # "ag_gemm" | "gemm_rs" | "ag_grouped_gemm"
+    params: dict = field(default_factory=dict)
+
+    def flops(self) -> float:
+        p = self.params
+        if self.op == "ag_gemm":
+            return 2.0 * p["R"] * p["m"] * p["K"] * p["N"]
+        if self.op == "gemm_rs":
+            return 2.0 * p["M"] * p["K"] * p["N"]
+        return 2.0 * p["R"] * p["m"] * p["topk"] * p["K"] * p["N"]
+
+    def make(self, **over):
+        p = dict(self.params)
+        p.update(over)
+        if self.op == "ag_gemm":
+            return make_ag_gemm(p["R"], p["m"], p["K"], p["N"], p["seed"],
+                                p.get("dist", "normal"), p.get("scale", 0.02))
+        if self.op == "gemm_rs":
+            return make_gemm_rs(p["R"], p["M"], p["K"], p["N"], p["seed"],
+                                p.get("local_rank", 0))
+        return make_moe(p["R"], p["m"], p["K"], p["N"], p["E"], p["seed"], p["topk"])
+
+
+# The five workloads: one GPU's share of tensor-parallel (TP=8) LLM FFN layers
+# (8B-class: hidden 4096, FFN 14336; 70B-class: hidden 8192, FFN 28672) plus a
+# tiny case and a top-2 MoE layer with 32 experts.
+WORKLOADS = {
+    "ag_gemm_tiny": Workload("ag_gemm_tiny", "ag_gemm",
+                             dict(R=4, m=128, K=256, N=256, seed=0, dist="uniform", scale=1.0)),
+    "ag_gemm_8b": Workload("ag_gemm_8b", "ag_gemm",
+                           dict(R=8, m=512, K=4096, N=1792, seed=1)),
+    "gemm_rs_8b": Workload("gemm_rs_8b", "gemm_rs",
+                           dict(R=8, M=4096, K=1792, N=4096, seed=2, local_rank=0)),
+    "ag_gemm_70b": Workload("ag_gemm_70b", "ag_gemm",
+                            dict(R=8, m=1024, K=8192, N=3584, seed=3)),
+    "ag_moe": Workload("ag_moe", "ag_grouped_gemm",
+                       dict(R=8, m=512, K=4096, N=1792, E=32, topk=2, seed=4)),
+}
+
+
+def workload(name: str) -> Workload:
+    return WORKLOADS[name]
