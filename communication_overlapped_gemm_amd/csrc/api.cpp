@@ -1,0 +1,457 @@
+// C-ABI layer: argument checks, tile/slab plan resolution, workspace layout
+// and launches. Every entry point returns an OCG_* status and enqueues
+// nothing when it returns an error.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <new>
+
+#include "ocg_internal.h"
+
+using namespace ocg;
+
+struct ocg_handle_s {
+  int device;
+  int cus;
+  int resident[3][OCG_TILE_COUNT];  // per op and tile preset, 0 = not queried yet
+};
+
+namespace {
+
+constexpr uint64_t kTicksPerUs = 100;  // s_memrealtime runs at 100 MHz
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Workspace sections, sized for the worst plan a call of this shape can pick
+// (smallest slab, tile and strip sizes).
+WsLayout layout(int op, int R, int64_t m, int64_t K, int64_t N, int E, int topk) {
+  WsLayout L{};
+  size_t off = sizeof(WsHeader);
+  int64_t rows = (op == OCG_OP_GEMM_RS) ? m : (int64_t)R * m;
+  L.max_slabs = (op == OCG_OP_GEMM_RS) ? 0 : (int)(R * cdiv((int)m, kMinSlabRows));
+  L.max_rs_tiles = (op == OCG_OP_GEMM_RS) ? cdiv((int)rows, 128) * cdiv((int)N, 128) : 0;
+  L.slab_cnt = off;
+  off = align256(off + sizeof(uint32_t) * L.max_slabs);
+  L.slab_flag = off;
+  off = align256(off + sizeof(uint32_t) * L.max_slabs);
+  L.rs_flag = off;
+  off = align256(off + sizeof(uint32_t) * L.max_rs_tiles);
+  L.moe_off = L.moe_lut = L.moe_perm = off;
+  L.max_moe_tiles = 0;
+  if (op == OCG_OP_AG_GROUPED_GEMM) {
+    int slots = (int)(rows * topk);
+    L.max_moe_tiles = (cdiv(slots, tile_bm(kMoeTile)) + E) * cdiv((int)N, tile_bn(kMoeTile));
+    L.moe_off = off;
+    off = align256(off + sizeof(int32_t) * (E + 1));
+    L.moe_lut = off;
+    off = align256(off + sizeof(int32_t) * 8 * (size_t)L.max_moe_tiles);
+    L.moe_perm = off;
+    off = align256(off + sizeof(int32_t) * (size_t)slots);
+  }
+  (void)K;
+  L.total = off;
+  return L;
+}
+
+bool shape_ok(int R, int64_t m, int64_t K, int64_t N) {
+  if (R < 1 || R > kMaxRanks || m < 1 || K < 64 || N < 8) return false;
+  if (K % 64 != 0 || N % 8 != 0) return false;
+  // 32-bit element/byte offsets inside buffer descriptors and tile math
+  if ((int64_t)R * m > (1 << 30) || K > (1 << 20) || N > (1 << 20)) return false;
+  if (K * N * 2 > 0xFFFFFFFFll) return false;
+  return true;
+}
+
+// Estimated cost of a tile preset: rounds of the persistent grid times the
+// tile area, derated for the smaller wave tiles.
+int choose_tile(int64_t M, int64_t N, int cus) {
+  static const double eff[OCG_TILE_COUNT] = {1.0, 0.9, 1.0, 0.75};
+  int best = OCG_TILE_128x128;
+  double best_cost = 1e300;
+  for (int t = 0; t < OCG_TILE_COUNT; ++t) {
+    int64_t tiles = cdiv((int)M, tile_bm(t)) * (int64_t)cdiv((int)N, tile_bn(t));
+    int64_t rounds = (tiles + cus - 1) / cus;
+    double cost = (double)rounds * tile_bm(t) * tile_bn(t) / eff[t];
+    if (cost < best_cost - 1e-9) {
+      best_cost = cost;
+      best = t;
+    }
+  }
+  return best;
+}
+
+struct Resolved {
+  int tile, BM, BN, S, CT;
+};
+
+int resolve(int op, int R, int64_t m, int64_t K, int64_t N, const ocg_config& c, int cus, Resolved* r) {
+  int64_t M = (op == OCG_OP_GEMM_RS) ? m : R * m;
+  r->tile = (op == OCG_OP_AG_GROUPED_GEMM) ? kMoeTile : (c.tile < 0 ? choose_tile(M, N, cus) : c.tile);
+  if (r->tile < 0 || r->tile >= OCG_TILE_COUNT) return OCG_ERR_INVALID_ARG;
+  if (op == OCG_OP_AG_GROUPED_GEMM && c.tile >= 0 && c.tile != kMoeTile) return OCG_ERR_INVALID_ARG;
+  r->BM = tile_bm(r->tile);
+  r->BN = tile_bn(r->tile);
+  r->S = c.slab_rows > 0 ? c.slab_rows : r->BM;
+  if (r->S < kMinSlabRows) return OCG_ERR_INVALID_ARG;
+  if (c.copy_rows > 0) {
+    r->CT = c.copy_rows;
+  } else {
+    // about 256 KiB per copy task, a power of two dividing the slab
+    int64_t ct = (128 * 1024) / (K > 0 ? K : 1);
+    int p2 = 1;
+    while ((int64_t)p2 * 2 <= ct) p2 *= 2;
+    r->CT = p2 < r->S ? p2 : r->S;
+    while (r->S % r->CT) r->CT /= 2;
+  }
+  if (r->CT < 1 || r->S % r->CT) return OCG_ERR_INVALID_ARG;
+  return OCG_OK;
+}
+
+int reduce_rows(int64_t N) {
+  int64_t rr = (32 * 1024) / (2 * N);  // ~32 KiB of each partial per strip
+  return rr < 1 ? 1 : (int)rr;
+}
+
+ocg_config cfg_or_default(const ocg_config* c) {
+  ocg_config d;
+  ocg_config_default(&d);
+  return c ? *c : d;
+}
+
+int grid_for(ocg_handle h, int op, int tile, int tasks, const ocg_config& c) {
+  if (c.grid > 0) return c.grid;
+  int& r = h->resident[op][tile];
+  if (r == 0) r = resident_per_cu(op, tile);
+  int g = r * h->cus;
+  if (tasks < g) g = tasks;
+  return g < 1 ? 1 : g;
+}
+
+Common make_common(void* ws, const ocg_config& c) {
+  Common cm;
+  cm.hdr = (WsHeader*)ws;
+  uint64_t us = c.spin_timeout_us ? c.spin_timeout_us : 1000000u;
+  cm.timeout_ticks = us * kTicksPerUs;
+  cm.trace = (ocg_trace_rec*)c.trace;
+  cm.trace_cap = c.trace ? c.trace_capacity : 0;
+  cm.fault_skip_slab = c.fault_skip_slab;
+  return cm;
+}
+
+bool device_matches(ocg_handle h) {
+  int d = -1;
+  return hipGetDevice(&d) == hipSuccess && d == h->device;
+}
+
+}  // namespace
+
+
+extern "C" {
+
+void ocg_config_default(ocg_config* c) {
+  if (!c) return;
+  memset(c, 0, sizeof(*c));
+  c->tile = OCG_TILE_AUTO;
+  c->swizzle = 1;
+  c->mode = OCG_MODE_FUSED;
+  c->fault_skip_slab = -1;
+}
+
+int ocg_create(int device, ocg_handle* out) {
+  if (!out) return OCG_ERR_INVALID_ARG;
+  *out = nullptr;
+  int n = 0;
+  if (hipGetDeviceCount(&n) != hipSuccess || n <= 0) return OCG_ERR_NO_DEVICE;
+  if (device < 0 || device >= n) return OCG_ERR_NO_DEVICE;
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, device) != hipSuccess) return OCG_ERR_HIP;
+  if (strncmp(prop.gcnArchName, "gfx950", 6) != 0) return OCG_ERR_UNSUPPORTED_SHAPE;
+  ocg_handle h = new (std::nothrow) ocg_handle_s();
+  if (!h) return OCG_ERR_HIP;
+  h->device = device;
+  h->cus = prop.multiProcessorCount;
+  *out = h;
+  return OCG_OK;
+}
+
+void ocg_destroy(ocg_handle h) { delete h; }
+
+size_t ocg_workspace_bytes(int op, int R, int64_t m, int64_t K, int64_t N, int E, int topk) {
+  if (op < 0 || op > 2) return 0;
+  if (op == OCG_OP_GEMM_RS) {
+    if (R < 1 || R > kMaxRanks || m < R || m % R) return 0;
+    if (!shape_ok(1, m, K, N)) return 0;
+  } else if (!shape_ok(R, m, K, N)) {
+    return 0;
+  }
+  if (op == OCG_OP_AG_GROUPED_GEMM &&
+      (E < 1 || E > kMaxExperts || topk < 1 || topk > kMaxTopk || topk > E || (int64_t)R * m * topk > kMaxRouteSlots))
+    return 0;
+  return layout(op, R, m, K, N, E, topk).total;
+}
+
+int ocg_workspace_init(ocg_handle h, void* ws, size_t bytes, void* stream) {
+  if (!h || !ws || bytes < sizeof(WsHeader) || (bytes & 3) || !aligned16(ws)) return OCG_ERR_INVALID_ARG;
+  if (!device_matches(h)) return OCG_ERR_INVALID_ARG;
+  hipError_t e = launch_fill_u32((uint32_t*)ws, bytes / 4, 0u, 0, (hipStream_t)stream);
+  return e == hipSuccess ? OCG_OK : OCG_ERR_HIP;
+}
+
+int ocg_ag_gemm(ocg_handle h, const void* const* a_chunks, int R, int local_rank, int64_t m, int64_t K,
+                const void* b, int64_t N, void* a_gathered, void* c, void* ws, size_t ws_bytes,
+                const ocg_config* cfgp, void* stream) {
+  if (!h || !a_chunks || !b || !a_gathered || !c || !ws) return OCG_ERR_INVALID_ARG;
+  if (!shape_ok(R, m, K, N)) return OCG_ERR_UNSUPPORTED_SHAPE;
+  if (local_rank < 0 || local_rank >= R) return OCG_ERR_INVALID_ARG;
+  for (int r = 0; r < R; ++r)
+    if (!a_chunks[r] || !aligned16(a_chunks[r])) return OCG_ERR_INVALID_ARG;
+  if (!aligned16(b) || !aligned16(a_gathered) || !aligned16(c) || !aligned16(ws)) return OCG_ERR_INVALID_ARG;
+  ocg_config cfg = cfg_or_default(cfgp);
+  if (cfg.mode < 0 || cfg.mode > 2) return OCG_ERR_INVALID_ARG;
+  WsLayout L = layout(OCG_OP_AG_GEMM, R, m, K, N, 0, 0);
+  if (ws_bytes < L.total) return OCG_ERR_WORKSPACE_TOO_SMALL;
+  if (!device_matches(h)) return OCG_ERR_INVALID_ARG;
+  Resolved rv;
+  int st = resolve(OCG_OP_AG_GEMM, R, m, K, N, cfg, h->cus, &rv);
+  if (st) return st;
+  AgArgs a{};
+  for (int r = 0; r < R; ++r) a.chunks[r] = (const uint16_t*)a_chunks[r];
+  a.b = (const uint16_t*)b;
+  a.a_gathered = (uint16_t*)a_gathered;
+  a.c = (uint16_t*)c;
+  a.slab_cnt = (uint32_t*)((char*)ws + L.slab_cnt);
+  a.slab_flag = (uint32_t*)((char*)ws + L.slab_flag);
+  a.plan = make_ag_plan(R, local_rank, (int)m, (int)K, (int)N, rv.BM, rv.BN, rv.S, rv.CT, cfg.swizzle ? 1 : 0,
+                        cfg.mode);
+  if (a.plan.R * a.plan.bpr > L.max_slabs) return OCG_ERR_INVALID_ARG;
+  a.cm = make_common(ws, cfg);
+  int tasks = a.plan.n_copy + a.plan.n_tiles;
+  int grid = grid_for(h, OCG_OP_AG_GEMM, rv.tile, tasks, cfg);
+  return launch_ag_gemm(a, rv.tile, grid, (hipStream_t)stream) == hipSuccess ? OCG_OK : OCG_ERR_HIP;
+}
+
+int ocg_gemm_rs(ocg_handle h, const void* A, const void* B, int64_t M, int64_t K, int64_t N, int R, int local_rank,
+                const void* const* peer_partials, void* partial, void* out, void* ws, size_t ws_bytes,
+                const ocg_config* cfgp, void* stream) {
+  if (!h || !A || !B || !peer_partials || !partial || !out || !ws) return OCG_ERR_INVALID_ARG;
+  if (R < 1 || R > kMaxRanks || M < R || M % R) return OCG_ERR_UNSUPPORTED_SHAPE;
+  if (!shape_ok(1, M, K, N)) return OCG_ERR_UNSUPPORTED_SHAPE;
+  if (local_rank < 0 || local_rank >= R) return OCG_ERR_INVALID_ARG;
+  for (int s = 0; s < R; ++s)
+    if (s != local_rank && (!peer_partials[s] || !aligned16(peer_partials[s]))) return OCG_ERR_INVALID_ARG;
+  if (!aligned16(A) || !aligned16(B) || !aligned16(partial) || !aligned16(out) || !aligned16(ws))
+    return OCG_ERR_INVALID_ARG;
+  ocg_config cfg = cfg_or_default(cfgp);
+  WsLayout L = layout(OCG_OP_GEMM_RS, R, M, K, N, 0, 0);
+  if (ws_bytes < L.total) return OCG_ERR_WORKSPACE_TOO_SMALL;
+  if (!device_matches(h)) return OCG_ERR_INVALID_ARG;
+  Resolved rv;
+  int st = resolve(OCG_OP_GEMM_RS, R, M, K, N, cfg, h->cus, &rv);
+  if (st) return st;
+  RsArgs a{};
+  a.a = (const uint16_t*)A;
+  a.b = (const uint16_t*)B;
+  for (int s = 0; s < R; ++s) a.peers[s] = (s == local_rank) ? nullptr : (const uint16_t*)peer_partials[s];
+  a.partial = (uint16_t*)partial;
+  a.out = (uint16_t*)out;
+  a.tile_flag = (uint32_t*)((char*)ws + L.rs_flag);
+  a.plan = make_rs_plan(R, local_rank, (int)M, (int)K, (int)N, rv.BM, rv.BN, reduce_rows(N), cfg.swizzle ? 1 : 0);
+  if (a.plan.n_tiles > L.max_rs_tiles) return OCG_ERR_INVALID_ARG;
+  a.peer_flags = cfg.peer_flags;
+  a.peer_flag_value = cfg.peer_flag_value;
+  a.local_rb0 = (local_rank * a.plan.blk) / rv.BM;
+  a.local_nrb = cdiv(a.plan.blk, rv.BM);
+  if (cfg.peer_flags && a.plan.blk % rv.BM) return OCG_ERR_UNSUPPORTED_SHAPE;
+  a.cm = make_common(ws, cfg);
+  int grid = grid_for(h, OCG_OP_GEMM_RS, rv.tile, a.plan.n_tiles + a.plan.n_red, cfg);
+  return launch_gemm_rs(a, rv.tile, grid, (hipStream_t)stream) == hipSuccess ? OCG_OK : OCG_ERR_HIP;
+}
+
+int ocg_ag_grouped_gemm(ocg_handle h, const void* const* a_chunks, int R, int local_rank, int64_t m, int64_t K,
+                        const float* logits, int E, int topk, const void* w, int64_t N, void* a_gathered,
+                        int32_t* topk_ids, float* topk_w, int32_t* perm, int32_t* expert_offsets, void* out,
+                        void* ws, size_t ws_bytes, const ocg_config* cfgp, void* stream) {
+  if (!h || !a_chunks || !logits || !w || !a_gathered || !topk_ids || !topk_w || !out || !ws)
+    return OCG_ERR_INVALID_ARG;
+  if (!shape_ok(R, m, K, N)) return OCG_ERR_UNSUPPORTED_SHAPE;
+  if (E < 1 || E > kMaxExperts || topk < 1 || topk > kMaxTopk || topk > E) return OCG_ERR_UNSUPPORTED_SHAPE;
+  if ((int64_t)R * m * topk > kMaxRouteSlots) return OCG_ERR_UNSUPPORTED_SHAPE;
+  if ((int64_t)E * K * N * 2 > (int64_t)1 << 40) return OCG_ERR_UNSUPPORTED_SHAPE;
+  if (local_rank < 0 || local_rank >= R) return OCG_ERR_INVALID_ARG;
+  for (int r = 0; r < R; ++r)
+    if (!a_chunks[r] || !aligned16(a_chunks[r])) return OCG_ERR_INVALID_ARG;
+  if (!aligned16(w) || !aligned16(a_gathered) || !aligned16(out) || !aligned16(ws)) return OCG_ERR_INVALID_ARG;
+  ocg_config cfg = cfg_or_default(cfgp);
+  if (cfg.mode < 0 || cfg.mode > 2) return OCG_ERR_INVALID_ARG;
+  WsLayout L = layout(OCG_OP_AG_GROUPED_GEMM, R, m, K, N, E, topk);
+  if (ws_bytes < L.total) return OCG_ERR_WORKSPACE_TOO_SMALL;
+  if (!device_matches(h)) return OCG_ERR_INVALID_ARG;
+  Resolved rv;
+  int st = resolve(OCG_OP_AG_GROUPED_GEMM, R, m, K, N, cfg, h->cus, &rv);
+  if (st) return st;
+  int32_t* perm_buf = perm ? perm : (int32_t*)((char*)ws + L.moe_perm);
+  MoeArgs a{};
+  for (int r = 0; r < R; ++r) a.chunks[r] = (const uint16_t*)a_chunks[r];
+  a.w = (const uint16_t*)w;
+  a.a_gathered = (uint16_t*)a_gathered;
+  a.out = (uint16_t*)out;
+  a.perm = perm_buf;
+  a.lut = (const int32_t*)((char*)ws + L.moe_lut);
+  a.slab_cnt = (uint32_t*)((char*)ws + L.slab_cnt);
+  a.slab_flag = (uint32_t*)((char*)ws + L.slab_flag);
+  a.topk = topk;
+  a.E = E;
+  a.plan = make_ag_plan(R, local_rank, (int)m, (int)K, (int)N, rv.BM, rv.BN, rv.S, rv.CT, cfg.swizzle ? 1 : 0,
+                        cfg.mode);
+  if (a.plan.R * a.plan.bpr > L.max_slabs) return OCG_ERR_INVALID_ARG;
+  a.cm = make_common(ws, cfg);
+  RouteArgs r{};
+  r.logits = logits;
+  r.topk_ids = topk_ids;
+  r.topk_w = topk_w;
+  r.perm = perm_buf;
+  r.offsets = (int32_t*)((char*)ws + L.moe_off);
+  r.user_offsets = expert_offsets;
+  r.lut = (int32_t*)((char*)ws + L.moe_lut);
+  r.hdr = (WsHeader*)ws;
+  r.T = (int)(R * m);
+  r.E = E;
+  r.topk = topk;
+  r.BM = rv.BM;
+  r.n_cb = cdiv((int)N, rv.BN);
+  r.m = (int)m;
+  r.S = rv.S;
+  r.bpr = a.plan.bpr;
+  r.local = local_rank;
+  r.max_tiles = L.max_moe_tiles;
+  int grid = grid_for(h, OCG_OP_AG_GROUPED_GEMM, rv.tile, a.plan.n_copy + L.max_moe_tiles, cfg);
+  return launch_moe(r, a, grid, (hipStream_t)stream) == hipSuccess ? OCG_OK : OCG_ERR_HIP;
+}
+
+int ocg_signal(uint32_t* flags, int count, uint32_t value, void* stream) {
+  if (!flags || count < 0 || ((uintptr_t)flags & 3)) return OCG_ERR_INVALID_ARG;
+  return launch_fill_u32(flags, (size_t)count, value, 1, (hipStream_t)stream) == hipSuccess ? OCG_OK : OCG_ERR_HIP;
+}
+
+int ocg_check(ocg_handle h, void* ws) {
+  if (!h || !ws) return OCG_ERR_INVALID_ARG;
+  WsHeader* hdr = (WsHeader*)ws;
+  uint32_t err = 0;
+  if (hipMemcpy(&err, &hdr->error, sizeof(err), hipMemcpyDeviceToHost) != hipSuccess) return OCG_ERR_HIP;
+  if (err) {
+    uint32_t zero = 0;
+    if (hipMemcpy(&hdr->error, &zero, sizeof(zero), hipMemcpyHostToDevice) != hipSuccess) return OCG_ERR_HIP;
+    return OCG_ERR_TIMEOUT;
+  }
+  return OCG_OK;
+}
+
+const char* ocg_status_string(int s) {
+  switch (s) {
+    case OCG_OK: return "ok";
+    case OCG_ERR_INVALID_ARG: return "invalid argument";
+    case OCG_ERR_UNSUPPORTED_SHAPE: return "unsupported shape or device";
+    case OCG_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case OCG_ERR_HIP: return "HIP runtime error";
+    case OCG_ERR_TIMEOUT: return "a flag wait timed out";
+    case OCG_ERR_NO_DEVICE: return "no such device";
+  }
+  return "unknown status";
+}
+
+int ocg_plan_info(int op, int R, int local_rank, int64_t m, int64_t K, int64_t N, const ocg_config* cfgp,
+                  int64_t out[8]) {
+  if (!out || op < 0 || op > 2) return OCG_ERR_INVALID_ARG;
+  if (op == OCG_OP_GEMM_RS) {
+    if (R < 1 || R > kMaxRanks || m < R || m % R || !shape_ok(1, m, K, N)) return OCG_ERR_UNSUPPORTED_SHAPE;
+  } else if (!shape_ok(R, m, K, N)) {
+    return OCG_ERR_UNSUPPORTED_SHAPE;
+  }
+  if (local_rank < 0 || local_rank >= R) return OCG_ERR_INVALID_ARG;
+  ocg_config cfg = cfg_or_default(cfgp);
+  Resolved rv;
+  int st = resolve(op, R, m, K, N, cfg, 256, &rv);
+  if (st) return st;
+  out[0] = rv.tile;
+  out[1] = rv.BM;
+  out[2] = rv.BN;
+  out[3] = rv.S;
+  out[4] = rv.CT;
+  if (op == OCG_OP_GEMM_RS) {
+    RsPlan p = make_rs_plan(R, local_rank, (int)m, (int)K, (int)N, rv.BM, rv.BN, reduce_rows(N), cfg.swizzle);
+    out[5] = p.n_red;
+    out[6] = p.n_tiles;
+    out[7] = p.RR;
+  } else {
+    AgPlan p = make_ag_plan(R, local_rank, (int)m, (int)K, (int)N, rv.BM, rv.BN, rv.S, rv.CT, cfg.swizzle,
+                            cfg.mode);
+    out[5] = p.n_copy;
+    out[6] = p.n_tiles;
+    out[7] = (int64_t)R * p.bpr;
+  }
+  return OCG_OK;
+}
+
+int ocg_plan_task(int op, int R, int local_rank, int64_t m, int64_t K, int64_t N, const ocg_config* cfgp,
+                  int64_t ticket, int64_t desc[8]) {
+  if (!desc) return OCG_ERR_INVALID_ARG;
+  for (int i = 0; i < 8; ++i) desc[i] = -1;
+  desc[0] = 0;
+  int64_t info[8];
+  int st = ocg_plan_info(op, R, local_rank, m, K, N, cfgp, info);
+  if (st) return st;
+  ocg_config cfg = cfg_or_default(cfgp);
+  if (op == OCG_OP_GEMM_RS) {
+    RsPlan p = make_rs_plan(R, local_rank, (int)m, (int)K, (int)N, (int)info[1], (int)info[2], (int)info[7],
+                            cfg.swizzle);
+    if (ticket < 0 || ticket >= p.n_tiles + p.n_red) return OCG_OK;
+    if (ticket < p.n_tiles) {
+      int rb, cb;
+      tile_of(p.n_rb, p.n_cb, p.rb0, (int)ticket, &rb, &cb);
+      desc[0] = 3;
+      desc[1] = rb;
+      desc[2] = cb;
+      desc[3] = rs_tile_touches_local(p, rb) ? 1 : 0;
+    } else {
+      int r0, r1;
+      rs_strip(p, (int)(ticket - p.n_tiles), &r0, &r1);
+      desc[0] = 5;
+      desc[1] = r0;
+      desc[2] = r1;
+    }
+    return OCG_OK;
+  }
+  AgPlan p = make_ag_plan(R, local_rank, (int)m, (int)K, (int)N, (int)info[1], (int)info[2], (int)info[3],
+                          (int)info[4], cfg.swizzle, cfg.mode);
+  if (ticket < 0 || ticket >= p.n_copy + (op == OCG_OP_AG_GEMM ? p.n_tiles : 0)) return OCG_OK;
+  if (ticket < p.n_copy) {
+    CopyDesc d = copy_desc(p, (int)ticket);
+    desc[0] = 1;
+    desc[1] = d.chunk;
+    desc[2] = d.piece;
+    desc[3] = d.row0;
+    desc[4] = d.row1;
+    desc[5] = d.slab;
+    return OCG_OK;
+  }
+  int rb, cb;
+  tile_of(p.n_rb, p.n_cb, p.rb0, (int)(ticket - p.n_copy), &rb, &cb);
+  desc[0] = 2;
+  desc[1] = rb;
+  desc[2] = cb;
+  int r0 = rb * p.BM, r1 = r0 + p.BM < p.M ? r0 + p.BM : p.M;
+  int k = 0;
+  int n = for_each_dep_slab(p.m, p.S, p.bpr, p.local, r0, r1, [&](int s) {
+    if (k < 4) desc[4 + k] = s;
+    ++k;
+  });
+  desc[3] = p.mode == 0 ? n : 0;
+  if (p.mode != 0)
+    for (int i = 4; i < 8; ++i) desc[i] = -1;
+  return OCG_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,830 @@
+// gfx950 kernels of the communication-overlapped GEMM library.
+//
+// One persistent kernel per operation. Each workgroup (4 waves of 64) loops:
+// take a ticket (one atomic), run the task it names, repeat. Tasks are either
+// copy tasks (pull one piece of a peer's shard into the gathered buffer, then
+// publish the slab's flag: "produce_tile_notify") or GEMM tiles (wait for the
+// flags of the slabs they read: "consume_tile_wait", then an LDS-staged bf16
+// MFMA main loop). The primitives follow "TileLink: Generating Efficient
+// Compute-Communication Overlapping Kernels using Tile-Centric Primitives"
+// (MLSys 2025 talk summary), "Technical Deep Dive": signal primitives between
+// producer and consumer tiles; a notify lowered to a synchronisation, the
+// tile id and an atomic; pull-mode transfers whose "transfer complete"
+// barrier is the slab flag.
+//
+// Memory-model contract (agent scope, all 8 XCDs):
+//   producer: stores; every thread release-fences (waits for its stores and
+//   writes back the XCD's L2); workgroup barrier; one thread bumps the slab
+//   counter (acq_rel) and the last finisher stores the flag (release).
+//   consumer: one thread polls the flag with relaxed loads, then issues one
+//   acquire fence (invalidates stale cache lines) before the barrier that
+//   releases the workgroup into the main loop. Polls are bounded in time.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "ocg_internal.h"
+
+namespace ocg {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+typedef __attribute__((address_space(1))) const u32x4_t* gcptr16;
+typedef __attribute__((address_space(1))) u32x4_t* gptr16;
+typedef __attribute__((address_space(1))) u32x2_t* gptr8;
+typedef __attribute__((address_space(1))) const u32x2_t* gcptr8;
+
+constexpr int BK = 64;        // K step of the main loop
+constexpr int LDK = BK + 8;   // padded LDS row (elements): 144 B rows keep ds_read_b128 conflict-free
+
+template <int BM, int BN>
+struct TileShape {
+  static constexpr int WM = BM / 2, WN = BN / 2;   // 2 x 2 waves
+  static constexpr int FM = WM / 16, FN = WN / 16; // 16x16 MFMA fragments per wave
+  static constexpr int A_ELEMS = BM * LDK;         // A tile [BM][BK] (k contiguous)
+  static constexpr int B_ELEMS = BN * LDK;         // B tile transposed [BN][BK] (k contiguous)
+  static constexpr int STAGE = A_ELEMS + B_ELEMS;
+  static constexpr int LDS_ELEMS = 2 * STAGE;      // double buffered
+  static constexpr int A_LOADS = BM * (BK / 8) / kThreads;  // 16-byte loads per thread
+  static constexpr int B_BLOCKS = (BK / 8) * (BN / 8);      // 8x8 blocks per K step
+  static_assert(WN % 16 == 0 && WM % 16 == 0, "wave tile must hold whole fragments");
+  static_assert(B_BLOCKS <= kThreads, "one 8x8 B block per thread");
+  static_assert(LDS_ELEMS * 2 <= 163840, "fits the 160 KiB LDS of a gfx950 CU");
+};
+
+__device__ __forceinline__ u32x4_t gload16(const void* p) { return *(gcptr16)p; }
+__device__ __forceinline__ void gstore16(void* p, u32x4_t v) { *(gptr16)p = v; }
+__device__ __forceinline__ void gstore8(void* p, u32x2_t v) { *(gptr8)p = v; }
+__device__ __forceinline__ u32x2_t gload8(const void* p) { return *(gcptr8)p; }
+
+__device__ __forceinline__ uint64_t now_ticks() { return __builtin_amdgcn_s_memrealtime(); }
+
+__device__ __forceinline__ uint32_t xcc_id() {
+  uint32_t v;
+  asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(v));
+  return v & 0xf;
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+
+// Round-to-nearest-even fp32 -> bf16 pair (hardware v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// ---------------------------------------------------------------- flags
+
+// consume_tile_wait: bounded relaxed poll, then one acquire fence.
+__device__ bool wait_flag(const uint32_t* flag, uint32_t want, const Common& cm, uint32_t* seen) {
+  uint64_t t0 = now_ticks();
+  uint32_t v = __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  bool ok = true;
+  while (v != want) {
+    if (now_ticks() - t0 > cm.timeout_ticks) {
+      ok = false;
+      break;
+    }
+    __builtin_amdgcn_s_sleep(1);
+    v = __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  if (!ok) __hip_atomic_fetch_or(&cm.hdr->error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  *seen = v;
+  return ok;
+}
+
+// produce_tile_notify for copy tasks: called by every thread after its
+// stores; returns (to thread 0) whether this task published the slab flag.
+__device__ bool publish_slab(uint32_t* cnt, uint32_t* flag, int slab, int target, uint32_t epoch,
+                             const Common& cm, uint32_t* s_bcast) {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  __syncthreads();
+  bool published = false;
+  if (threadIdx.x == 0) {
+    uint32_t old = __hip_atomic_fetch_add(&cnt[slab], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    if ((int)old + 1 == target) {
+      __hip_atomic_store(&cnt[slab], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (slab != cm.fault_skip_slab)
+        __hip_atomic_store(&flag[slab], epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+      published = true;
+    }
+  }
+  return published;
+}
+
+// ---------------------------------------------------------------- copy
+
+// Pull `n16` 16-byte granules from src to dst with all 256 threads, 16
+// granules in flight per thread.
+__device__ __forceinline__ void copy_granules(const uint16_t* src, uint16_t* dst, size_t n16) {
+  constexpr int U = 16;
+  const u32x4_t* s = (const u32x4_t*)src;
+  u32x4_t* d = (u32x4_t*)dst;
+  size_t i = threadIdx.x;
+  for (; i + (size_t)(U - 1) * kThreads < n16; i += (size_t)U * kThreads) {
+    u32x4_t v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = gload16(s + i + (size_t)u * kThreads);
+#pragma unroll
+    for (int u = 0; u < U; ++u) gstore16(d + i + (size_t)u * kThreads, v[u]);
+  }
+  for (; i < n16; i += kThreads) gstore16(d + i, gload16(s + i));
+}
+
+// One copy task of the AllGather (pull mode): rows [row0, row1) of the
+// gathered matrix come from rank `chunk`'s shard.
+__device__ void run_copy_task(const AgPlan& p, const uint16_t* const* chunks, uint16_t* a_gathered,
+                              uint32_t* slab_cnt, uint32_t* slab_flag, int u, uint32_t epoch,
+                              const Common& cm, uint32_t ticket, uint32_t* s_bcast) {
+  uint64_t t0 = now_ticks();
+  CopyDesc d = copy_desc(p, u);
+  const uint16_t* src = chunks[d.chunk] + (size_t)(d.row0 - d.chunk * p.m) * p.K;
+  uint16_t* dst = a_gathered + (size_t)d.row0 * p.K;
+  copy_granules(src, dst, (size_t)(d.row1 - d.row0) * p.K / 8);
+  int target = slab_target(p.m, p.S, p.CT, p.bpr, d.slab);
+  bool pub = publish_slab(slab_cnt, slab_flag, d.slab, target, epoch, cm, s_bcast);
+  if (threadIdx.x == 0 && cm.trace && ticket < cm.trace_cap) {
+    ocg_trace_rec* r = cm.trace + ticket;
+    uint64_t t1 = now_ticks();
+    r->ticket = ticket; r->kind = 1; r->a = d.chunk; r->b = d.piece; r->c = d.slab; r->d = pub;
+    r->hw = (xcc_id() << 16) | blockIdx.x; r->epoch = epoch;
+    r->t_start = t0; r->t_ready = t1; r->t_end = t1; r->flag_seen = 0; r->pad = 0;
+  }
+}
+
+// ---------------------------------------------------------------- MFMA tile engine
+
+// Per-thread A-row sources for one tile: each thread stages A_LOADS rows of
+// the BM x 64 A tile per K step; `rows[q]` already points at the thread's
+// 16-byte column within the row (k = 0).
+template <int BM, int BN>
+struct ARows {
+  const uint16_t* rows[TileShape<BM, BN>::A_LOADS];
+};
+
+template <int BM, int BN>
+__device__ __forceinline__ void load_a(const ARows<BM, BN>& ar, int kt, u32x4_t* ra) {
+#pragma unroll
+  for (int q = 0; q < TileShape<BM, BN>::A_LOADS; ++q) ra[q] = gload16(ar.rows[q] + kt * BK);
+}
+
+template <int BM, int BN>
+__device__ __forceinline__ void store_a(uint16_t* st, const u32x4_t* ra) {
+  const int t = threadIdx.x;
+#pragma unroll
+  for (int q = 0; q < TileShape<BM, BN>::A_LOADS; ++q) {
+    int i = t + kThreads * q;
+    int row = i >> 3, kc = i & 7;
+    *(u32x4_t*)(st + row * LDK + kc * 8) = ra[q];
+  }
+}
+
+// B tile: thread t < B_BLOCKS owns the 8x8 block (k rows 8*kb.., columns
+// 8*j..) of the 64 x BN tile; rows beyond K read as zero (buffer range).
+template <int BM, int BN>
+__device__ __forceinline__ void load_b(__amdgpu_buffer_rsrc_t rs, int N, int n0, int kt, u32x4_t* rb) {
+  const int t = threadIdx.x;
+  if (t < TileShape<BM, BN>::B_BLOCKS) {
+    int kb = t & 7, j = t >> 3;
+    int k = kt * BK + kb * 8;
+    int off = (k * N + n0 + j * 8) * 2;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) rb[r] = __builtin_amdgcn_raw_buffer_load_b128(rs, off + r * N * 2, 0, 0);
+  }
+}
+
+// Transpose the 8x8 bf16 block in registers and store it k-contiguous:
+// LDS row n holds B[k][n] for the 64 k of the step.
+template <int BM, int BN>
+__device__ __forceinline__ void store_b(uint16_t* st, const u32x4_t* rb) {
+  const int t = threadIdx.x;
+  if (t < TileShape<BM, BN>::B_BLOCKS) {
+    int kb = t & 7, j = t >> 3;
+    uint16_t* base = st + TileShape<BM, BN>::A_ELEMS + (j * 8) * LDK + kb * 8;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const int dw = c >> 1;
+      u32x4_t o;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        uint32_t x = rb[2 * i][dw], y = rb[2 * i + 1][dw];
+        o[i] = (c & 1) ? ((x >> 16) | (y & 0xFFFF0000u)) : ((x & 0xFFFFu) | (y << 16));
+      }
+      *(u32x4_t*)(base + c * LDK) = o;
+    }
+  }
+}
+
+// acc[f][g] holds C[m = wm*WM + 16f + (lane & 15)][n = wn*WN + 16g + 4*(lane >> 4) + e].
+// The MFMA's A operand carries B^T (rows = n) and its B operand carries A
+// (columns = m), so each lane ends up with 4 consecutive columns of one row.
+template <int BM, int BN>
+__device__ __forceinline__ void mainloop(uint16_t* smem, const ARows<BM, BN>& ar, __amdgpu_buffer_rsrc_t brs,
+                                         int N, int n0, int nk,
+                                         f32x4_t (&acc)[TileShape<BM, BN>::FM][TileShape<BM, BN>::FN]) {
+  using TS = TileShape<BM, BN>;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int koff = (lane >> 4) * 8;
+  const int arow = wm * TS::WM + (lane & 15);
+  const int brow = wn * TS::WN + (lane & 15);
+#pragma unroll
+  for (int f = 0; f < TS::FM; ++f)
+#pragma unroll
+    for (int g = 0; g < TS::FN; ++g) acc[f][g] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  u32x4_t ra[TS::A_LOADS];
+  u32x4_t rb[8];
+  load_a<BM, BN>(ar, 0, ra);
+  load_b<BM, BN>(brs, N, n0, 0, rb);
+  store_a<BM, BN>(smem, ra);
+  store_b<BM, BN>(smem, rb);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    uint16_t* cur = smem + (kt & 1) * TS::STAGE;
+    uint16_t* nxt = smem + ((kt & 1) ^ 1) * TS::STAGE;
+    const bool more = kt + 1 < nk;
+    if (more) {
+      load_a<BM, BN>(ar, kt + 1, ra);
+      load_b<BM, BN>(brs, N, n0, kt + 1, rb);
+    }
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      bf16x8_t af[TS::FM], bfr[TS::FN];
+#pragma unroll
+      for (int f = 0; f < TS::FM; ++f)
+        af[f] = *(const bf16x8_t*)(cur + (arow + 16 * f) * LDK + ks * 32 + koff);
+#pragma unroll
+      for (int g = 0; g < TS::FN; ++g)
+        bfr[g] = *(const bf16x8_t*)(cur + TS::A_ELEMS + (brow + 16 * g) * LDK + ks * 32 + koff);
+#pragma unroll
+      for (int f = 0; f < TS::FM; ++f)
+#pragma unroll
+        for (int g = 0; g < TS::FN; ++g)
+          acc[f][g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[g], af[f], acc[f][g], 0, 0, 0);
+    }
+    if (more) {
+      store_a<BM, BN>(nxt, ra);
+      store_b<BM, BN>(nxt, rb);
+    }
+    __syncthreads();
+  }
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// Epilogue: the fp32 tile is rounded to bf16 and staged in LDS as
+// [BM][BN + 8] (reusing the operand buffers), then streamed out in 16-byte
+// row chunks so every global store is a full, coalesced 16-byte write.
+template <int BM, int BN>
+struct CStage {
+  static constexpr int LD = BN + 8;
+  static constexpr int CPR = BN / 8;   // 16-byte chunks per row
+  static_assert(BM * LD <= TileShape<BM, BN>::LDS_ELEMS, "C tile fits in the operand buffers");
+};
+
+template <int BM, int BN>
+__device__ __forceinline__ void stage_c(uint16_t* cst,
+                                        const f32x4_t (&acc)[TileShape<BM, BN>::FM][TileShape<BM, BN>::FN]) {
+  using TS = TileShape<BM, BN>;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+#pragma unroll
+  for (int f = 0; f < TS::FM; ++f) {
+    const int row = wm * TS::WM + 16 * f + (lane & 15);
+#pragma unroll
+    for (int g = 0; g < TS::FN; ++g) {
+      const int col = wn * TS::WN + 16 * g + 4 * (lane >> 4);
+      u32x2_t v = {pack_bf16x2(acc[f][g][0], acc[f][g][1]), pack_bf16x2(acc[f][g][2], acc[f][g][3])};
+      *(u32x2_t*)(cst + row * CStage<BM, BN>::LD + col) = v;
+    }
+  }
+  __syncthreads();
+}
+
+// f(row_in_tile, col_in_tile, 16-byte value) over every chunk of the tile.
+template <int BM, int BN, class F>
+__device__ __forceinline__ void for_each_c_chunk(const uint16_t* cst, F f) {
+  using CS = CStage<BM, BN>;
+  for (int i = threadIdx.x; i < BM * CS::CPR; i += kThreads) {
+    const int row = i / CS::CPR, c8 = i - row * CS::CPR;
+    f(row, c8 * 8, *(const u32x4_t*)(cst + row * CS::LD + c8 * 8));
+  }
+}
+
+// ---------------------------------------------------------------- common loop pieces
+
+__device__ __forceinline__ uint32_t read_epoch(WsHeader* hdr, uint32_t* s_bcast) {
+  if (threadIdx.x == 0) {
+    uint32_t e = __hip_atomic_load(&hdr->epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
+    s_bcast[1] = e ? e : 1u;
+  }
+  __syncthreads();
+  return s_bcast[1];
+}
+
+__device__ __forceinline__ uint32_t next_ticket(WsHeader* hdr, uint32_t* s_bcast) {
+  __syncthreads();
+  if (threadIdx.x == 0)
+    s_bcast[0] = __hip_atomic_fetch_add(&hdr->ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  return s_bcast[0];
+}
+
+// Last workgroup out resets the ticket and done counters and records the epoch.
+__device__ __forceinline__ void finish(WsHeader* hdr, uint32_t epoch) {
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t d = __hip_atomic_fetch_add(&hdr->done, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    if (d + 1 == gridDim.x) {
+      __hip_atomic_store(&hdr->ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(&hdr->done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(&hdr->epoch, epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
+__device__ __forceinline__ void trace_tile(const Common& cm, uint32_t ticket, uint32_t kind, uint32_t a, uint32_t b,
+                                           uint32_t c, uint32_t d, uint32_t epoch, uint64_t t0, uint64_t t1,
+                                           uint32_t seen) {
+  if (threadIdx.x == 0 && cm.trace && ticket < cm.trace_cap) {
+    ocg_trace_rec* r = cm.trace + ticket;
+    r->ticket = ticket; r->kind = kind; r->a = a; r->b = b; r->c = c; r->d = d;
+    r->hw = (xcc_id() << 16) | blockIdx.x; r->epoch = epoch;
+    r->t_start = t0; r->t_ready = t1; r->t_end = now_ticks(); r->flag_seen = seen; r->pad = 0;
+  }
+}
+
+// ---------------------------------------------------------------- AG-GEMM
+
+template <int BM, int BN>
+__global__ __launch_bounds__(kThreads, 1) void ag_gemm_kernel(AgArgs args) {
+  using TS = TileShape<BM, BN>;
+  __shared__ __attribute__((aligned(16))) uint16_t smem[TS::LDS_ELEMS];
+  __shared__ uint32_t s_bcast[8];
+  const AgPlan& p = args.plan;
+  const Common& cm = args.cm;
+  const uint32_t epoch = read_epoch(cm.hdr, s_bcast);
+  const uint32_t n_tasks = (uint32_t)(p.n_copy + p.n_tiles);
+  const __amdgpu_buffer_rsrc_t brs = make_rsrc(args.b, (uint32_t)((size_t)p.K * p.N * 2));
+  const int nk = p.K / BK;
+
+  for (;;) {
+    const uint32_t ticket = next_ticket(cm.hdr, s_bcast);
+    if (ticket >= n_tasks) break;
+    if ((int)ticket < p.n_copy) {
+      run_copy_task(p, args.chunks, args.a_gathered, args.slab_cnt, args.slab_flag, (int)ticket, epoch, cm,
+                    ticket, s_bcast);
+      continue;
+    }
+    const uint64_t t0 = now_ticks();
+    int rb, cb;
+    tile_of(p.n_rb, p.n_cb, p.rb0, (int)ticket - p.n_copy, &rb, &cb);
+    const int r0 = rb * BM, r1 = min(r0 + BM, p.M);
+    int nwait = 0;
+    uint32_t seen = 0;
+    if (p.mode == 0 && threadIdx.x == 0) {
+      nwait = for_each_dep_slab(p.m, p.S, p.bpr, p.local, r0, r1, [&](int s) {
+        wait_flag(&args.slab_flag[s], epoch, cm, &seen);
+      });
+    }
+    const uint64_t t1 = now_ticks();
+    __syncthreads();
+    // Rows of the local chunk come from the local shard; all others from the
+    // gathered buffer filled by the copy tasks.
+    ARows<BM, BN> ar;
+#pragma unroll
+    for (int q = 0; q < TS::A_LOADS; ++q) {
+      int i = threadIdx.x + kThreads * q;
+      int row = min(r0 + (i >> 3), p.M - 1);
+      int kc = (i & 7) * 8;
+      int c = row / p.m;
+      ar.rows[q] = (c == p.local) ? args.chunks[c] + (size_t)(row - c * p.m) * p.K + kc
+                                  : args.a_gathered + (size_t)row * p.K + kc;
+    }
+    f32x4_t acc[TS::FM][TS::FN];
+    const int n0 = cb * BN;
+    mainloop<BM, BN>(smem, ar, brs, p.N, n0, nk, acc);
+    stage_c<BM, BN>(smem, acc);
+    for_each_c_chunk<BM, BN>(smem, [&](int row, int col, u32x4_t v) {
+      if (r0 + row < p.M && n0 + col < p.N) gstore16(args.c + (size_t)(r0 + row) * p.N + n0 + col, v);
+    });
+    trace_tile(cm, ticket, 2, rb, cb, nwait, 0, epoch, t0, t1, seen);
+  }
+  finish(cm.hdr, epoch);
+}
+
+// ---------------------------------------------------------------- GEMM-RS
+
+// Reduce strip: out rows [r0, r1) = bf16( sum over ranks s = 0..R-1, in
+// that order, of the bf16 partials P_s ), fp32 accumulation, one rounding.
+// Every 16-byte chunk issues the loads of all ranks before adding, U chunks
+// per round, so each thread keeps up to U * R loads in flight.
+__device__ void run_reduce_strip(const RsArgs& a, int r0, int r1) {
+  constexpr int U = 2;
+  const RsPlan& p = a.plan;
+  const int lo = p.local * p.blk;
+  const size_t first = (size_t)r0 * p.N / 8, n16 = (size_t)(r1 - r0) * p.N / 8;
+  for (size_t base = threadIdx.x; base < n16; base += (size_t)U * kThreads) {
+    u32x4_t v[U][kMaxRanks];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const size_t i = base + (size_t)u * kThreads;
+      if (i >= n16) continue;
+#pragma unroll
+      for (int s = 0; s < kMaxRanks; ++s) {
+        if (s < p.R) {
+          const uint16_t* src = (s == p.local) ? a.partial : a.peers[s];
+          v[u][s] = gload16(src + (first + i) * 8);
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const size_t i = base + (size_t)u * kThreads;
+      if (i >= n16) continue;
+      float acc[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] = bf16_to_f32((v[u][0][e >> 1] >> ((e & 1) * 16)) & 0xFFFFu);
+#pragma unroll
+      for (int s = 1; s < kMaxRanks; ++s) {
+        if (s < p.R) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[e] += bf16_to_f32((v[u][s][e >> 1] >> ((e & 1) * 16)) & 0xFFFFu);
+        }
+      }
+      u32x4_t o = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]), pack_bf16x2(acc[4], acc[5]),
+                   pack_bf16x2(acc[6], acc[7])};
+      gstore16(a.out + (first + i) * 8 - (size_t)lo * p.N, o);
+    }
+  }
+}
+
+template <int BM, int BN>
+__global__ __launch_bounds__(kThreads, 1) void gemm_rs_kernel(RsArgs args) {
+  using TS = TileShape<BM, BN>;
+  __shared__ __attribute__((aligned(16))) uint16_t smem[TS::LDS_ELEMS];
+  __shared__ uint32_t s_bcast[8];
+  const RsPlan& p = args.plan;
+  const Common& cm = args.cm;
+  const uint32_t epoch = read_epoch(cm.hdr, s_bcast);
+  const __amdgpu_buffer_rsrc_t brs = make_rsrc(args.b, (uint32_t)((size_t)p.K * p.N * 2));
+  const int nk = p.K / BK;
+  const uint32_t n_tasks = (uint32_t)(p.n_tiles + p.n_red);
+
+  for (;;) {
+    const uint32_t ticket = next_ticket(cm.hdr, s_bcast);
+    if (ticket >= n_tasks) break;
+    const uint64_t t0 = now_ticks();
+    if ((int)ticket >= p.n_tiles) {
+      // consume_tile_wait on the local tiles of the strip, peer_tile_wait on
+      // the peers' tiles, then the fixed-order reduce.
+      int r0, r1;
+      rs_strip(p, (int)ticket - p.n_tiles, &r0, &r1);
+      uint32_t seen = 0;
+      int nwait = 0;
+      if (threadIdx.x == 0) {
+        for (int rb = r0 / BM; rb <= (r1 - 1) / BM; ++rb)
+          for (int cb = 0; cb < p.n_cb; ++cb) {
+            wait_flag(&args.tile_flag[rb * p.n_cb + cb], epoch, cm, &seen);
+            ++nwait;
+            if (args.peer_flags) {
+              const int t_local = (rb - args.local_rb0) * p.n_cb + cb;
+              const int per_rank = args.local_nrb * p.n_cb;
+              for (int s = 0; s < p.R; ++s) {
+                if (s == p.local) continue;
+                wait_flag(&args.peer_flags[s * per_rank + t_local], args.peer_flag_value, cm, &seen);
+                ++nwait;
+              }
+            }
+          }
+      }
+      const uint64_t t1 = now_ticks();
+      __syncthreads();
+      run_reduce_strip(args, r0, r1);
+      trace_tile(cm, ticket, 5, r0, r1, nwait, 0, epoch, t0, t1, seen);
+      continue;
+    }
+    int rb, cb;
+    tile_of(p.n_rb, p.n_cb, p.rb0, (int)ticket, &rb, &cb);
+    const int r0 = rb * BM;
+    ARows<BM, BN> ar;
+#pragma unroll
+    for (int q = 0; q < TS::A_LOADS; ++q) {
+      int i = threadIdx.x + kThreads * q;
+      int row = min(r0 + (i >> 3), p.M - 1);
+      ar.rows[q] = args.a + (size_t)row * p.K + (i & 7) * 8;
+    }
+    f32x4_t acc[TS::FM][TS::FN];
+    const int n0 = cb * BN;
+    mainloop<BM, BN>(smem, ar, brs, p.N, n0, nk, acc);
+    stage_c<BM, BN>(smem, acc);
+    for_each_c_chunk<BM, BN>(smem, [&](int row, int col, u32x4_t v) {
+      if (r0 + row < p.M && n0 + col < p.N) gstore16(args.partial + (size_t)(r0 + row) * p.N + n0 + col, v);
+    });
+    // produce_tile_notify: the bf16 partial tile is in memory (the send buffer).
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    __syncthreads();
+    if (threadIdx.x == 0)
+      __hip_atomic_store(&args.tile_flag[rb * p.n_cb + cb], epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    trace_tile(cm, ticket, 3, rb, cb, rs_tile_touches_local(p, rb) ? 1u : 0u, 0, epoch, t0, t0, 0);
+  }
+  finish(cm.hdr, epoch);
+}
+
+// ---------------------------------------------------------------- MoE routing
+
+// Single-workgroup routing: top-k of the fp32 logits (ties -> lower expert),
+// softmax weights, per-expert counts, offsets, stable expert-sorted slot list
+// and the grouped-tile lookup table (the dynamic dependency table).
+__global__ __launch_bounds__(kRouteThreads, 1) void moe_route_kernel(RouteArgs a) {
+  __shared__ uint8_t s_ids[kMaxRouteSlots];
+  __shared__ uint16_t s_perm[kMaxRouteSlots];
+  __shared__ int s_cnt[kMaxExperts];
+  __shared__ int s_off[kMaxExperts + 1];
+  __shared__ int s_run[kMaxExperts];
+  __shared__ int s_tbase[kMaxExperts + 1];
+  __shared__ int s_wcnt[kRouteThreads / 64][kMaxExperts];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int T = a.T, E = a.E, K = a.topk, S = T * K;
+  if (tid < kMaxExperts) {
+    s_cnt[tid] = 0;
+    s_run[tid] = 0;
+  }
+  __syncthreads();
+
+  for (int t = tid; t < T; t += kRouteThreads) {
+    const float* lg = a.logits + (size_t)t * E;
+    float bv[kMaxTopk];
+    int bi[kMaxTopk];
+#pragma unroll
+    for (int j = 0; j < kMaxTopk; ++j) {
+      bv[j] = 0.f;
+      bi[j] = -1;
+    }
+    for (int e = 0; e < E; ++e) {
+      float v = lg[e];
+      // insertion keeping the first (lowest-index) of equal logits ahead
+      int pos = K;
+      for (int j = K - 1; j >= 0; --j)
+        if (bi[j] < 0 || v > bv[j]) pos = j;
+      if (pos < K) {
+        for (int j = K - 1; j > pos; --j) {
+          bv[j] = bv[j - 1];
+          bi[j] = bi[j - 1];
+        }
+        bv[pos] = v;
+        bi[pos] = e;
+      }
+    }
+    const float mx = bv[0];
+    float sum = 0.f;
+    for (int e = 0; e < E; ++e) sum += __expf(lg[e] - mx);
+    for (int j = 0; j < K; ++j) {
+      a.topk_ids[t * K + j] = bi[j];
+      a.topk_w[t * K + j] = __expf(bv[j] - mx) / sum;
+      s_ids[t * K + j] = (uint8_t)bi[j];
+      atomicAdd(&s_cnt[bi[j]], 1);
+    }
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int o = 0, tb = 0;
+    for (int e = 0; e < E; ++e) {
+      s_off[e] = o;
+      s_tbase[e] = tb;
+      o += s_cnt[e];
+      tb += cdiv(s_cnt[e], a.BM) * a.n_cb;
+    }
+    s_off[E] = o;
+    s_tbase[E] = tb;
+    a.hdr->n_tiles = (uint32_t)min(tb, a.max_tiles);
+  }
+  __syncthreads();
+  if (tid <= E) {
+    a.offsets[tid] = s_off[tid];
+    if (a.user_offsets) a.user_offsets[tid] = s_off[tid];
+  }
+
+  // Stable positions: slots are visited in index order, 1024 per round.
+  for (int base = 0; base < S; base += kRouteThreads) {
+    for (int i = tid; i < (kRouteThreads / 64) * kMaxExperts; i += kRouteThreads) (&s_wcnt[0][0])[i] = 0;
+    __syncthreads();
+    const int s = base + tid;
+    const int e = s < S ? (int)s_ids[s] : -1;
+    uint64_t todo = __ballot(e >= 0);
+    int rank = 0;
+    while (todo) {
+      const int leader = __builtin_ctzll(todo);
+      const int x = __shfl(e, leader);
+      const uint64_t same = __ballot(e == x);
+      if (e == x) rank = __builtin_popcountll(same & ((1ull << lane) - 1ull));
+      if (lane == 0) s_wcnt[wave][x] = __builtin_popcountll(same);
+      todo &= ~same;
+    }
+    __syncthreads();
+    if (tid < E) {
+      int run = s_run[tid];
+      for (int w = 0; w < kRouteThreads / 64; ++w) {
+        int c = s_wcnt[w][tid];
+        s_wcnt[w][tid] = run;
+        run += c;
+      }
+      s_run[tid] = run;
+    }
+    __syncthreads();
+    if (e >= 0) {
+      const int pos = s_off[e] + s_wcnt[wave][e] + rank;
+      a.perm[pos] = s;
+      s_perm[pos] = (uint16_t)s;
+    }
+    __syncthreads();
+  }
+
+  // Lookup table: one entry per (expert, column block, row tile).
+  for (int e = 0; e < E; ++e) {
+    const int nrt = cdiv(s_cnt[e], a.BM);
+    const int n = nrt * a.n_cb;
+    for (int i = tid; i < n; i += kRouteThreads) {
+      const int cb = i / nrt, rt = i - cb * nrt;
+      const int idx = s_tbase[e] + i;
+      if (idx >= a.max_tiles) continue;
+      const int r0 = s_off[e] + rt * a.BM;
+      const int r1 = min(r0 + a.BM, s_off[e + 1]);
+      const int tf = s_perm[r0] / K, tl = s_perm[r1 - 1] / K;
+      int32_t* L = a.lut + (size_t)idx * 8;
+      L[0] = e;
+      L[1] = r0;
+      L[2] = r1 - r0;
+      L[3] = cb;
+      L[4] = (tf / a.m) * a.bpr + (tf % a.m) / a.S;
+      L[5] = (tl / a.m) * a.bpr + (tl % a.m) / a.S;
+      L[6] = 0;
+      L[7] = 0;
+    }
+  }
+}
+
+// ---------------------------------------------------------------- AG + grouped GEMM
+
+template <int BM, int BN>
+__global__ __launch_bounds__(kThreads, 1) void moe_gemm_kernel(MoeArgs args) {
+  using TS = TileShape<BM, BN>;
+  __shared__ __attribute__((aligned(16))) uint16_t smem[TS::LDS_ELEMS];
+  __shared__ uint32_t s_bcast[8];
+  const AgPlan& p = args.plan;
+  const Common& cm = args.cm;
+  const uint32_t epoch = read_epoch(cm.hdr, s_bcast);
+  if (threadIdx.x == 0) s_bcast[2] = __hip_atomic_load(&cm.hdr->n_tiles, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  const uint32_t n_tiles = p.mode == 2 ? 0u : s_bcast[2];
+  const uint32_t n_tasks = (uint32_t)p.n_copy + n_tiles;
+  const int nk = p.K / BK;
+  const size_t wstride = (size_t)p.K * p.N;
+
+  for (;;) {
+    const uint32_t ticket = next_ticket(cm.hdr, s_bcast);
+    if (ticket >= n_tasks) break;
+    if ((int)ticket < p.n_copy) {
+      run_copy_task(p, args.chunks, args.a_gathered, args.slab_cnt, args.slab_flag, (int)ticket, epoch, cm,
+                    ticket, s_bcast);
+      continue;
+    }
+    const uint64_t t0 = now_ticks();
+    const int32_t* L = args.lut + (size_t)(ticket - p.n_copy) * 8;
+    const int e = L[0], r0 = L[1], nrows = L[2], cb = L[3], s_lo = L[4], s_hi = L[5];
+    uint32_t seen = 0;
+    int nwait = 0;
+    if (p.mode == 0 && threadIdx.x == 0) {
+      for (int s = s_lo; s <= s_hi; ++s) {
+        if (s / p.bpr == p.local) continue;
+        wait_flag(&args.slab_flag[s], epoch, cm, &seen);
+        ++nwait;
+      }
+    }
+    const uint64_t t1 = now_ticks();
+    __syncthreads();
+    ARows<BM, BN> ar;
+#pragma unroll
+    for (int q = 0; q < TS::A_LOADS; ++q) {
+      int i = threadIdx.x + kThreads * q;
+      int rr = min(i >> 3, nrows - 1);
+      int tok = args.perm[r0 + rr] / args.topk;
+      int c = tok / p.m;
+      int kc = (i & 7) * 8;
+      ar.rows[q] = (c == p.local) ? args.chunks[c] + (size_t)(tok - c * p.m) * p.K + kc
+                                  : args.a_gathered + (size_t)tok * p.K + kc;
+    }
+    const __amdgpu_buffer_rsrc_t brs = make_rsrc(args.w + (size_t)e * wstride, (uint32_t)(wstride * 2));
+    f32x4_t acc[TS::FM][TS::FN];
+    const int n0 = cb * BN;
+    mainloop<BM, BN>(smem, ar, brs, p.N, n0, nk, acc);
+    stage_c<BM, BN>(smem, acc);
+    // local scatter: row rr of the tile is token-slot perm[r0 + rr]
+    for_each_c_chunk<BM, BN>(smem, [&](int rr, int col, u32x4_t v) {
+      if (rr < nrows && n0 + col < p.N) {
+        const int slot = args.perm[r0 + rr];
+        gstore16(args.out + (size_t)slot * p.N + n0 + col, v);
+      }
+    });
+    trace_tile(cm, ticket, 4, e, r0, nrows, cb | ((uint32_t)nwait << 16), epoch, t0, t1, seen);
+  }
+  finish(cm.hdr, epoch);
+}
+
+// ---------------------------------------------------------------- fill
+
+__global__ void fill_u32_kernel(uint32_t* p, size_t n, uint32_t v, int release) {
+  size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  for (; i < n; i += (size_t)gridDim.x * blockDim.x) {
+    if (release)
+      __hip_atomic_store(p + i, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+    else
+      p[i] = v;
+  }
+}
+
+// ---------------------------------------------------------------- launchers
+
+template <int BM, int BN>
+static hipError_t ag_launch(const AgArgs& a, int grid, hipStream_t s) {
+  hipLaunchKernelGGL((ag_gemm_kernel<BM, BN>), dim3(grid), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int BM, int BN>
+static hipError_t rs_launch(const RsArgs& a, int grid, hipStream_t s) {
+  hipLaunchKernelGGL((gemm_rs_kernel<BM, BN>), dim3(grid), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_ag_gemm(const AgArgs& a, int tile, int grid, hipStream_t s) {
+  switch (tile) {
+    case OCG_TILE_256x224: return ag_launch<256, 224>(a, grid, s);
+    case OCG_TILE_128x224: return ag_launch<128, 224>(a, grid, s);
+    case OCG_TILE_256x256: return ag_launch<256, 256>(a, grid, s);
+    case OCG_TILE_128x128: return ag_launch<128, 128>(a, grid, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_gemm_rs(const RsArgs& a, int tile, int grid, hipStream_t s) {
+  switch (tile) {
+    case OCG_TILE_256x224: return rs_launch<256, 224>(a, grid, s);
+    case OCG_TILE_128x224: return rs_launch<128, 224>(a, grid, s);
+    case OCG_TILE_256x256: return rs_launch<256, 256>(a, grid, s);
+    case OCG_TILE_128x128: return rs_launch<128, 128>(a, grid, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_moe(const RouteArgs& r, const MoeArgs& a, int grid, hipStream_t s) {
+  hipLaunchKernelGGL(moe_route_kernel, dim3(1), dim3(kRouteThreads), 0, s, r);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((moe_gemm_kernel<128, 224>), dim3(grid), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_u32(uint32_t* p, size_t n, uint32_t v, int release, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  size_t blocks = (n + 255) / 256;
+  if (blocks > 1024) blocks = 1024;
+  hipLaunchKernelGGL(fill_u32_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p, n, v, release);
+  return hipGetLastError();
+}
+
+template <class K>
+static int occ(K kern) {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, kThreads, 0) != hipSuccess) return 1;
+  return n > 0 ? n : 1;
+}
+
+int resident_per_cu(int op, int tile) {
+  if (op == OCG_OP_AG_GROUPED_GEMM) return occ(moe_gemm_kernel<128, 224>);
+  if (op == OCG_OP_AG_GEMM) {
+    switch (tile) {
+      case OCG_TILE_256x224: return occ(ag_gemm_kernel<256, 224>);
+      case OCG_TILE_128x224: return occ(ag_gemm_kernel<128, 224>);
+      case OCG_TILE_256x256: return occ(ag_gemm_kernel<256, 256>);
+      case OCG_TILE_128x128: return occ(ag_gemm_kernel<128, 128>);
+    }
+  } else {
+    switch (tile) {
+      case OCG_TILE_256x224: return occ(gemm_rs_kernel<256, 224>);
+      case OCG_TILE_128x224: return occ(gemm_rs_kernel<128, 224>);
+      case OCG_TILE_256x256: return occ(gemm_rs_kernel<256, 256>);
+      case OCG_TILE_128x128: return occ(gemm_rs_kernel<128, 128>);
+    }
+  }
+  return 1;
+}
+
+}  // namespace ocg

@@ -1,0 +1,106 @@
+// Internal launch parameters shared by the C-ABI layer (api.cpp) and the
+// kernels (kernels.hip). Not part of the public interface.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/ocg.h"
+#include "sched.h"
+
+namespace ocg {
+
+constexpr int kMaxRanks = 16;
+constexpr int kThreads = 256;         // every persistent kernel: 4 waves of 64
+constexpr int kRouteThreads = 1024;   // routing kernel: 16 waves
+constexpr int kMaxRouteSlots = 16384; // token slots the routing kernel holds in LDS
+constexpr int kMaxExperts = 64;
+constexpr int kMaxTopk = 4;
+constexpr int kMinSlabRows = 16;
+constexpr int kMoeTile = OCG_TILE_128x224;
+
+// Workspace header (first 256 bytes of every workspace).
+struct WsHeader {
+  uint32_t ticket;     // next ticket of the running persistent kernel
+  uint32_t done;       // workgroups that finished the running kernel
+  uint32_t epoch;      // epoch of the last completed call (flags carry epochs)
+  uint32_t error;      // bit 0: a flag wait timed out
+  uint32_t n_tiles;    // MoE: grouped tiles of the current routing
+  uint32_t pad[59];
+};
+static_assert(sizeof(WsHeader) == 256, "header is 256 bytes");
+
+// Byte offsets of the workspace sections for one call shape.
+struct WsLayout {
+  size_t slab_cnt, slab_flag, rs_flag, moe_off, moe_lut, moe_perm, total;
+  int max_slabs, max_rs_tiles, max_moe_tiles;
+};
+
+struct Common {
+  WsHeader* hdr;
+  uint64_t timeout_ticks;   // bound on each wait, 100 MHz ticks
+  ocg_trace_rec* trace;
+  uint32_t trace_cap;
+  int fault_skip_slab;
+};
+
+struct AgArgs {
+  const uint16_t* chunks[kMaxRanks];
+  const uint16_t* b;
+  uint16_t* a_gathered;
+  uint16_t* c;
+  uint32_t* slab_cnt;
+  uint32_t* slab_flag;
+  AgPlan plan;
+  Common cm;
+};
+
+struct RsArgs {
+  const uint16_t* a;
+  const uint16_t* b;
+  const uint16_t* peers[kMaxRanks];
+  uint16_t* partial;
+  uint16_t* out;
+  uint32_t* tile_flag;          // notify flag per tile (row-major rb*n_cb+cb)
+  const uint32_t* peer_flags;   // [R][local-block tiles] or null (local block aligned to BM)
+  uint32_t peer_flag_value;
+  int local_rb0, local_nrb;     // row blocks of the local block (peer flag indexing)
+  RsPlan plan;
+  Common cm;
+};
+
+struct MoeArgs {
+  const uint16_t* chunks[kMaxRanks];
+  const uint16_t* w;            // [E][K][N]
+  uint16_t* a_gathered;
+  uint16_t* out;
+  const int32_t* perm;          // expert-sorted token-slot list
+  const int32_t* lut;           // [tiles][8]: e, r0, nrows, cb, slab_lo, slab_hi
+  uint32_t* slab_cnt;
+  uint32_t* slab_flag;
+  int topk, E;
+  AgPlan plan;                  // copy plan (tiles come from the lookup table)
+  Common cm;
+};
+
+struct RouteArgs {
+  const float* logits;
+  int32_t* topk_ids;
+  float* topk_w;
+  int32_t* perm;
+  int32_t* offsets;             // workspace copy [E+1]
+  int32_t* user_offsets;        // optional
+  int32_t* lut;
+  WsHeader* hdr;
+  int T, E, topk, BM, n_cb, m, S, bpr, local, max_tiles;
+};
+
+// Launchers (kernels.hip). Return hipSuccess or the launch error.
+hipError_t launch_ag_gemm(const AgArgs& a, int tile, int grid, hipStream_t s);
+hipError_t launch_gemm_rs(const RsArgs& a, int tile, int grid, hipStream_t s);
+hipError_t launch_moe(const RouteArgs& r, const MoeArgs& a, int grid, hipStream_t s);
+hipError_t launch_fill_u32(uint32_t* p, size_t n, uint32_t v, int release, hipStream_t s);
+// Resident workgroups per CU of each persistent kernel (op, tile preset).
+int resident_per_cu(int op, int tile);
+
+}  // namespace ocg

@@ -1,0 +1,154 @@
+// Closed-form ticket -> task maps of the persistent kernels (host and device).
+//
+// Tile-centric scheduling after "TileLink: Generating Efficient
+// Compute-Communication Overlapping Kernels using Tile-Centric Primitives"
+// (MLSys 2025 talk summary), section "Technical Deep Dive": a wait names only
+// a tile; its rank, barrier (slab), tiles per rank and barriers per rank
+// follow from affine maps for static workloads; swizzling reorders tile
+// access and transfers so transfers line up with compute.
+//
+// AG-GEMM plan. Gathered rows M = R*m; rank chunk c owns rows [c*m, (c+1)*m).
+// A chunk is cut into slabs of S rows (one published flag each) and into copy
+// tasks of CT rows (S % CT == 0). Tickets [0, n_copy) are copy tasks in the
+// chunk sequence local+1, local+2, ..., local+R-1, local (swizzled) or
+// 0..R-1 (natural); tickets [n_copy, n_copy + n_tiles) are GEMM tiles, row
+// blocks rotated to start at the block holding the local chunk's first row.
+// Every tile's flag dependencies are copy tasks with smaller tickets and copy
+// tasks never wait, so dynamic ticketing cannot deadlock.
+#pragma once
+
+#include <stdint.h>
+
+#if defined(__HIPCC__)
+#define OCG_HD __host__ __device__ __forceinline__
+#else
+#define OCG_HD inline
+#endif
+
+namespace ocg {
+
+OCG_HD int cdiv(int a, int b) { return (a + b - 1) / b; }
+
+struct AgPlan {
+  int R, local, m, M, K, N;
+  int BM, BN, S, CT;
+  int swizzle, mode;
+  int n_rb, n_cb, bpr, n_tpc, n_copy, n_tiles, rb0;
+};
+
+// mode: 0 fused, 1 gemm only, 2 copy only
+OCG_HD AgPlan make_ag_plan(int R, int local, int m, int K, int N, int BM, int BN, int S, int CT,
+                           int swizzle, int mode) {
+  AgPlan p;
+  p.R = R; p.local = local; p.m = m; p.M = R * m; p.K = K; p.N = N;
+  p.BM = BM; p.BN = BN; p.S = S; p.CT = CT; p.swizzle = swizzle; p.mode = mode;
+  p.n_rb = cdiv(p.M, BM);
+  p.n_cb = cdiv(N, BN);
+  p.bpr = cdiv(m, S);
+  p.n_tpc = cdiv(m, CT);
+  p.n_copy = (mode == 1) ? 0 : R * p.n_tpc;
+  p.n_tiles = (mode == 2) ? 0 : p.n_rb * p.n_cb;
+  p.rb0 = swizzle ? (int)(((long long)local * m) / BM) : 0;
+  return p;
+}
+
+// Chunk copied at position q of the copy sequence.
+OCG_HD int copy_chunk(const AgPlan& p, int q) {
+  if (!p.swizzle) return q;
+  return (q < p.R - 1) ? (p.local + 1 + q) % p.R : p.local;
+}
+
+struct CopyDesc {
+  int chunk, piece, row0, row1, slab;
+};
+
+OCG_HD CopyDesc copy_desc(const AgPlan& p, int u) {
+  CopyDesc d;
+  int q = u / p.n_tpc;
+  d.piece = u - q * p.n_tpc;
+  d.chunk = copy_chunk(p, q);
+  int r0 = d.piece * p.CT;
+  int r1 = r0 + p.CT < p.m ? r0 + p.CT : p.m;
+  d.row0 = d.chunk * p.m + r0;
+  d.row1 = d.chunk * p.m + r1;
+  d.slab = d.chunk * p.bpr + r0 / p.S;
+  return d;
+}
+
+// Copy tasks that complete slab `slab` (global id chunk*bpr + s).
+OCG_HD int slab_target(int m, int S, int CT, int bpr, int slab) {
+  int s = slab % bpr;
+  int per = S / CT;
+  int n_tpc = cdiv(m, CT);
+  int first = s * per;
+  int left = n_tpc - first;
+  return left < per ? left : per;
+}
+
+// Tile v (0-based among tiles) -> (rb, cb).
+OCG_HD void tile_of(int n_rb, int n_cb, int rb0, int v, int* rb, int* cb) {
+  int q = v / n_cb;
+  *cb = v - q * n_cb;
+  int r = rb0 + q;
+  *rb = r >= n_rb ? r - n_rb : r;
+}
+
+// Slabs (excluding the local chunk) overlapping gathered rows [r0, r1):
+// visits them in ascending order, calling f(slab).
+template <class F>
+OCG_HD int for_each_dep_slab(int m, int S, int bpr, int local, int r0, int r1, F f) {
+  int n = 0;
+  if (r1 <= r0) return 0;
+  int c0 = r0 / m, c1 = (r1 - 1) / m;
+  for (int c = c0; c <= c1; ++c) {
+    if (c == local) continue;
+    int lo = (c == c0) ? r0 - c * m : 0;
+    int hi = (c == c1) ? r1 - c * m : m;  // exclusive
+    int s0 = lo / S, s1 = (hi - 1) / S;
+    for (int s = s0; s <= s1; ++s) {
+      f(c * bpr + s);
+      ++n;
+    }
+  }
+  return n;
+}
+
+// GEMM-RS plan: tickets [0, n_tiles) are GEMM tiles of the full partial
+// (local row block first when swizzled); tickets [n_tiles, n_tiles + n_red)
+// are reduce strips of RR rows of the local block [local*blk, (local+1)*blk).
+struct RsPlan {
+  int R, local, M, K, N, BM, BN, blk, RR;
+  int n_rb, n_cb, n_tiles, n_red, rb0;
+};
+
+OCG_HD RsPlan make_rs_plan(int R, int local, int M, int K, int N, int BM, int BN, int RR, int swizzle) {
+  RsPlan p;
+  p.R = R; p.local = local; p.M = M; p.K = K; p.N = N; p.BM = BM; p.BN = BN; p.RR = RR;
+  p.blk = M / R;
+  p.n_rb = cdiv(M, BM);
+  p.n_cb = cdiv(N, BN);
+  p.n_tiles = p.n_rb * p.n_cb;
+  p.n_red = cdiv(p.blk, RR);
+  p.rb0 = swizzle ? (int)(((long long)local * p.blk) / BM) : 0;
+  return p;
+}
+
+// Reduce strip j -> gathered rows [*r0, *r1).
+OCG_HD void rs_strip(const RsPlan& p, int j, int* r0, int* r1) {
+  int lo = p.local * p.blk;
+  *r0 = lo + j * p.RR;
+  int e = *r0 + p.RR;
+  *r1 = e < lo + p.blk ? e : lo + p.blk;
+}
+
+OCG_HD bool rs_tile_touches_local(const RsPlan& p, int rb) {
+  int lo = rb * p.BM;
+  int hi = lo + p.BM < p.M ? lo + p.BM : p.M;
+  return lo < (p.local + 1) * p.blk && hi > p.local * p.blk;
+}
+
+// Tile presets: {BM, BN}.
+OCG_HD int tile_bm(int t) { return (t == 1 || t == 3) ? 128 : 256; }
+OCG_HD int tile_bn(int t) { return t == 2 ? 256 : (t == 3 ? 128 : 224); }
+
+}  // namespace ocg

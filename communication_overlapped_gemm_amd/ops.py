@@ -1,0 +1,200 @@
+"""Torch-facing wrappers of the C ABI: validate tensors, allocate outputs with
+torch, pass raw pointers and the current HIP stream. Every step of the path
+runs in the HIP library; nothing here computes."""
+from __future__ import annotations
+
+import ctypes as C
+from typing import Dict, Optional, Sequence, Tuple
+
+import torch
+
+from . import _lib
+from ._lib import Config, check, default_config, lib
+
+_handles: Dict[int, C.c_void_p] = {}
+_workspaces: Dict[tuple, "Workspace"] = {}
+
+
+def _device_index(t: Optional[torch.Tensor] = None) -> int:
+    return t.device.index if t is not None else torch.cuda.current_device()
+
+
+def handle(device: Optional[int] = None) -> C.c_void_p:
+    dev = torch.cuda.current_device() if device is None else device
+    h = _handles.get(dev)
+    if h is None:
+        h = C.c_void_p()
+        check(lib.ocg_create(dev, C.byref(h)), "ocg_create")
+        _handles[dev] = h
+    return h
+
+
+def _stream_ptr(stream: Optional[torch.cuda.Stream]) -> int:
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+class Workspace:
+    """Caller-owned scratch of one operation shape (flags, tickets, routing
+    tables), cleared once by the library's fill kernel."""
+
+    def __init__(self, op: int, R: int, m: int, K: int, N: int, E: int = 0, topk: int = 0,
+                 device: Optional[int] = None, stream=None):
+        n = lib.ocg_workspace_bytes(op, R, m, K, N, E, topk)
+        if n == 0:
+            raise _lib.OcgError(_lib.ERR_UNSUPPORTED_SHAPE, "ocg_workspace_bytes")
+        dev = torch.cuda.current_device() if device is None else device
+        self.buf = torch.empty(n, dtype=torch.uint8, device=f"cuda:{dev}")
+        self.nbytes = n
+        self.device = dev
+        check(lib.ocg_workspace_init(handle(dev), self.ptr, n, _stream_ptr(stream)), "ocg_workspace_init")
+
+    @property
+    def ptr(self) -> int:
+        return self.buf.data_ptr()
+
+    def check(self) -> None:
+        """Raise if a flag wait of an earlier call timed out (synchronises)."""
+        torch.cuda.synchronize(self.device)
+        check(lib.ocg_check(handle(self.device), self.ptr), "ocg_check")
+
+    @classmethod
+    def cached(cls, op, R, m, K, N, E=0, topk=0, device=None):
+        dev = torch.cuda.current_device() if device is None else device
+        key = (op, R, m, K, N, E, topk, dev)
+        ws = _workspaces.get(key)
+        if ws is None:
+            ws = _workspaces[key] = cls(op, R, m, K, N, E, topk, dev)
+        return ws
+
+
+def _check_bf16(t: torch.Tensor, name: str, shape=None) -> None:
+    if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous bfloat16 CUDA tensor")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _cfg(config: Optional[Config], **kw) -> Config:
+    c = config if config is not None else default_config()
+    for k, v in kw.items():
+        if v is not None:
+            setattr(c, k, v)
+    return c
+
+
+def ag_gemm(a_chunks: Sequence[torch.Tensor], b: torch.Tensor, local_rank: int = 0, *,
+            a_gathered: Optional[torch.Tensor] = None, c: Optional[torch.Tensor] = None,
+            workspace: Optional[Workspace] = None, config: Optional[Config] = None,
+            stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Fused AllGather-GEMM. Returns (c, a_gathered)."""
+    R = len(a_chunks)
+    m, K = a_chunks[0].shape
+    N = b.shape[1]
+    for r, t in enumerate(a_chunks):
+        _check_bf16(t, f"a_chunks[{r}]", (m, K))
+    _check_bf16(b, "b", (K, N))
+    dev = b.device
+    if a_gathered is None:
+        a_gathered = torch.empty((R * m, K), dtype=torch.bfloat16, device=dev)
+    if c is None:
+        c = torch.empty((R * m, N), dtype=torch.bfloat16, device=dev)
+    _check_bf16(a_gathered, "a_gathered", (R * m, K))
+    _check_bf16(c, "c", (R * m, N))
+    ws = workspace or Workspace.cached(_lib.OP_AG_GEMM, R, m, K, N, device=dev.index)
+    ptrs = (C.c_void_p * R)(*[t.data_ptr() for t in a_chunks])
+    cfg = _cfg(config)
+    check(lib.ocg_ag_gemm(handle(dev.index), ptrs, R, local_rank, m, K, b.data_ptr(), N, a_gathered.data_ptr(),
+                          c.data_ptr(), ws.ptr, ws.nbytes, C.byref(cfg), _stream_ptr(stream)), "ocg_ag_gemm")
+    return c, a_gathered
+
+
+def gemm_rs(a: torch.Tensor, b: torch.Tensor, peer_partials: Sequence[Optional[torch.Tensor]], local_rank: int = 0,
+            *, partial: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+            workspace: Optional[Workspace] = None, config: Optional[Config] = None,
+            stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Fused GEMM-ReduceScatter (one rank's share). Returns (partial, out)."""
+    R = len(peer_partials)
+    M, K = a.shape
+    N = b.shape[1]
+    _check_bf16(a, "a")
+    _check_bf16(b, "b", (K, N))
+    ptrs = (C.c_void_p * R)()
+    for s, p in enumerate(peer_partials):
+        if s == local_rank:
+            continue
+        _check_bf16(p, f"peer_partials[{s}]", (M, N))
+        ptrs[s] = p.data_ptr()
+    dev = a.device
+    if partial is None:
+        partial = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    if out is None:
+        out = torch.empty((M // R, N), dtype=torch.bfloat16, device=dev)
+    _check_bf16(partial, "partial", (M, N))
+    _check_bf16(out, "out", (M // R, N))
+    ws = workspace or Workspace.cached(_lib.OP_GEMM_RS, R, M, K, N, device=dev.index)
+    cfg = _cfg(config)
+    check(lib.ocg_gemm_rs(handle(dev.index), a.data_ptr(), b.data_ptr(), M, K, N, R, local_rank, ptrs,
+                          partial.data_ptr(), out.data_ptr(), ws.ptr, ws.nbytes, C.byref(cfg),
+                          _stream_ptr(stream)), "ocg_gemm_rs")
+    return partial, out
+
+
+def ag_grouped_gemm(a_chunks: Sequence[torch.Tensor], logits: torch.Tensor, w: torch.Tensor, topk: int = 2,
+                    local_rank: int = 0, *, workspace: Optional[Workspace] = None,
+                    config: Optional[Config] = None, stream=None, outputs: Optional[dict] = None) -> dict:
+    """AllGather + top-k routing + grouped GEMM. Returns a dict with out,
+    a_gathered, topk_ids, topk_w, perm and expert_offsets."""
+    R = len(a_chunks)
+    m, K = a_chunks[0].shape
+    E, K2, N = w.shape
+    if K2 != K:
+        raise ValueError("w must be [E, K, N]")
+    for r, t in enumerate(a_chunks):
+        _check_bf16(t, f"a_chunks[{r}]", (m, K))
+    _check_bf16(w, "w")
+    if logits.dtype != torch.float32 or not logits.is_contiguous() or tuple(logits.shape) != (R * m, E):
+        raise ValueError("logits must be a contiguous float32 [R*m, E] CUDA tensor")
+    dev = w.device
+    T = R * m
+    o = dict(outputs or {})
+    o.setdefault("a_gathered", torch.empty((T, K), dtype=torch.bfloat16, device=dev))
+    o.setdefault("topk_ids", torch.empty((T, topk), dtype=torch.int32, device=dev))
+    o.setdefault("topk_w", torch.empty((T, topk), dtype=torch.float32, device=dev))
+    o.setdefault("perm", torch.empty((T * topk,), dtype=torch.int32, device=dev))
+    o.setdefault("expert_offsets", torch.empty((E + 1,), dtype=torch.int32, device=dev))
+    o.setdefault("out", torch.empty((T * topk, N), dtype=torch.bfloat16, device=dev))
+    ws = workspace or Workspace.cached(_lib.OP_AG_GROUPED_GEMM, R, m, K, N, E, topk, device=dev.index)
+    ptrs = (C.c_void_p * R)(*[t.data_ptr() for t in a_chunks])
+    cfg = _cfg(config)
+    check(lib.ocg_ag_grouped_gemm(handle(dev.index), ptrs, R, local_rank, m, K, logits.data_ptr(), E, topk,
+                                  w.data_ptr(), N, o["a_gathered"].data_ptr(), o["topk_ids"].data_ptr(),
+                                  o["topk_w"].data_ptr(), o["perm"].data_ptr(), o["expert_offsets"].data_ptr(),
+                                  o["out"].data_ptr(), ws.ptr, ws.nbytes, C.byref(cfg), _stream_ptr(stream)),
+          "ocg_ag_grouped_gemm")
+    return o
+
+
+def signal(flags: torch.Tensor, value: int, stream=None) -> None:
+    """Peer-notify stand-in: write `value` into every uint32 of `flags`."""
+    if flags.dtype not in (torch.int32, torch.uint32) or not flags.is_contiguous():
+        raise ValueError("flags must be a contiguous 32-bit tensor")
+    check(lib.ocg_signal(flags.data_ptr(), flags.numel(), value & 0xFFFFFFFF, _stream_ptr(stream)), "ocg_signal")
+
+
+def plan_info(op: int, R: int, local_rank: int, m: int, K: int, N: int, config: Optional[Config] = None) -> dict:
+    """Host-only: the resolved tile/slab/copy plan of a call."""
+    out = _lib.I64x8()
+    cfg = _cfg(config)
+    check(lib.ocg_plan_info(op, R, local_rank, m, K, N, C.byref(cfg), out), "ocg_plan_info")
+    keys = ["tile", "BM", "BN", "slab_rows", "copy_rows", "n_copy_or_strips", "n_tiles", "n_slabs_or_strip_rows"]
+    return dict(zip(keys, list(out)))
+
+
+def plan_task(op: int, R: int, local_rank: int, m: int, K: int, N: int, ticket: int,
+              config: Optional[Config] = None) -> list:
+    """Host-only: the task a ticket names (see ocg_plan_task)."""
+    out = _lib.I64x8()
+    cfg = _cfg(config)
+    check(lib.ocg_plan_task(op, R, local_rank, m, K, N, C.byref(cfg), ticket, out), "ocg_plan_task")
+    return list(out)

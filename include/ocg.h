@@ -1,0 +1,218 @@
+/*
+ * ocg.h -- communication-overlapped GEMM for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of the fused tile-centric AllGather-GEMM, GEMM-ReduceScatter and
+ * AllGather + MoE grouped GEMM, each computing one GPU's share of a
+ * tensor-parallel LLM layer. The operations are the ones named in
+ * "TileLink: Generating Efficient Compute-Communication Overlapping Kernels
+ * using Tile-Centric Primitives" (MLSys 2025 talk summary), sections "Key
+ * Findings" (AllGather-GEMM, GEMM-ReduceScatter), "Technical Deep Dive"
+ * (tile signals, pull transfers, swizzled tile order, lookup tables for
+ * dynamic dependencies) and "Experimental Setup & Results" (MoE:
+ * AllGather -> GroupGEMM -> ... -> local scatter).
+ *
+ * Conventions (every entry point):
+ *   - Matrices are row-major. "bf16" buffers hold raw bfloat16 bit patterns
+ *     (uint16). Every matrix pointer is a DEVICE pointer owned by the caller;
+ *     the library never frees or retains it past the call.
+ *   - Peer ranks are given as an array of R device pointers (a host array,
+ *     read during the call only). On one GPU they point at local stand-in
+ *     buffers; across GPUs they would be IPC-mapped peer buffers.
+ *   - Calls are asynchronous on `stream` (a hipStream_t passed as void*; NULL
+ *     means the default stream) and allocate no device memory: every scratch
+ *     word (tickets, flags, counters, routing tables, error word) lives in the
+ *     caller's workspace, sized by ocg_workspace_bytes() and cleared once by
+ *     ocg_workspace_init(). Calls that share a workspace must be ordered on
+ *     one stream; concurrent calls on one workspace race.
+ *   - Return value: OCG_OK or a negative OCG_ERR_* code. On an error return
+ *     nothing has been enqueued. No C++ exception or abort crosses the ABI.
+ *     A flag wait that exceeds its time bound is recorded in the workspace's
+ *     error word and reported by ocg_check() after the stream has drained.
+ *   - Shapes: K must be a multiple of 64, N a multiple of 8, 1 <= R <= 16.
+ *     M, N and the per-rank rows m may leave ragged tiles. Pointers to bf16
+ *     matrices must be 16-byte aligned.
+ */
+#ifndef OCG_H_
+#define OCG_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define OCG_OK 0
+#define OCG_ERR_INVALID_ARG (-1)
+#define OCG_ERR_UNSUPPORTED_SHAPE (-2)
+#define OCG_ERR_WORKSPACE_TOO_SMALL (-3)
+#define OCG_ERR_HIP (-4)
+#define OCG_ERR_TIMEOUT (-5)
+#define OCG_ERR_NO_DEVICE (-6)
+
+#define OCG_OP_AG_GEMM 0
+#define OCG_OP_GEMM_RS 1
+#define OCG_OP_AG_GROUPED_GEMM 2
+
+/* Fused (default), GEMM tiles only with every flag treated as published
+ * (measurement of the GEMM part; expects the gathered buffer filled), or
+ * copy tasks only (measurement of the gather part). */
+#define OCG_MODE_FUSED 0
+#define OCG_MODE_GEMM_ONLY 1
+#define OCG_MODE_COPY_ONLY 2
+
+/* Tile presets (rows x columns of C per workgroup tile, K step 64). */
+#define OCG_TILE_AUTO (-1)
+#define OCG_TILE_256x224 0
+#define OCG_TILE_128x224 1
+#define OCG_TILE_256x256 2
+#define OCG_TILE_128x128 3
+#define OCG_TILE_COUNT 4
+
+/* Trace record written per executed task when ocg_config.trace is set
+ * (indexed by ticket; 64 bytes). kind: 1 copy task, 2 AG-GEMM tile,
+ * 3 GEMM-RS tile, 4 MoE tile, 5 GEMM-RS reduce strip. Times are the GPU's
+ * constant 100 MHz clock. */
+typedef struct ocg_trace_rec {
+  uint32_t ticket, kind;
+  uint32_t a, b, c, d;   /* copy: chunk, piece, slab, published(0/1)
+                            AG tile: rb, cb, #slabs waited, 0
+                            RS tile: rb, cb, local-block(0/1), 0
+                            MoE tile: expert, row start, rows, cb | (#slabs waited << 16)
+                            RS strip: row0, row1, #flags waited, 0 */
+  uint32_t hw;           /* (XCC id << 16) | workgroup id */
+  uint32_t epoch;        /* epoch of the call */
+  uint64_t t_start, t_ready, t_end; /* ready = dependencies satisfied (tiles)
+                                       or flag published (copy) */
+  uint32_t flag_seen, pad;
+} ocg_trace_rec;
+
+typedef struct ocg_config {
+  int32_t tile;             /* OCG_TILE_* preset, or OCG_TILE_AUTO */
+  int32_t slab_rows;        /* rows of a rank chunk per published flag; 0 = tile rows */
+  int32_t copy_rows;        /* rows per copy task (must divide slab_rows); 0 = auto */
+  int32_t swizzle;          /* 1 = tiles and copies start at the local rank and rotate
+                               (default); 0 = natural rank order */
+  int32_t mode;             /* OCG_MODE_* */
+  int32_t grid;             /* persistent workgroups; 0 = resident capacity */
+  uint32_t spin_timeout_us; /* bound on every flag wait, microseconds; 0 = 1 s */
+  int32_t fault_skip_slab;  /* test hook: this slab's flag is never published; -1 = off */
+  void* trace;              /* device array of ocg_trace_rec indexed by ticket, or NULL */
+  uint32_t trace_capacity;  /* records in `trace` */
+  const uint32_t* peer_flags; /* GEMM-RS: device array [R][tiles of the local row block],
+                                 written by peers when their partial tile has landed;
+                                 NULL = all peer partials are complete */
+  uint32_t peer_flag_value;   /* value meaning "landed" in peer_flags */
+} ocg_config;
+
+/* Opaque per-device handle: device id, compute-unit count and the resident
+ * capacity of each persistent kernel. */
+typedef struct ocg_handle_s* ocg_handle;
+
+/* Fill `cfg` with defaults (auto tile, swizzled, fused, 1 s timeout, no
+ * trace, no fault injection). */
+void ocg_config_default(ocg_config* cfg);
+
+/* Create a handle for `device` (HIP ordinal). Returns OCG_ERR_NO_DEVICE if no
+ * such device exists and OCG_ERR_UNSUPPORTED_SHAPE if it is not gfx950. */
+int ocg_create(int device, ocg_handle* out);
+void ocg_destroy(ocg_handle h);
+
+/* Workspace bytes for `op`: AG_GEMM (R, m = rows per rank, K, N),
+ * GEMM_RS (R, m = M total rows, K, N), AG_GROUPED_GEMM (R, m, K, N, E, topk).
+ * Unused arguments are ignored. Returns 0 on invalid arguments. */
+size_t ocg_workspace_bytes(int op, int R, int64_t m, int64_t K, int64_t N, int E, int topk);
+
+/* Clear a workspace once before its first use (a fill kernel on `stream`). */
+int ocg_workspace_init(ocg_handle h, void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * AllGather-GEMM: a_gathered = concat_r a_chunks[r] (row block r = rank r),
+ * C = a_gathered x B, fp32 accumulation, C rounded to bf16 (nearest-even).
+ *   a_chunks[r] : bf16 [m, K] of rank r (r = 0..R-1), read
+ *   b           : bf16 [K, N], read
+ *   a_gathered  : bf16 [R*m, K], written (every row, the local one included)
+ *   c           : bf16 [R*m, N], written
+ * Copy tasks pull each peer chunk into a_gathered slab by slab and publish a
+ * per-slab flag; GEMM tiles wait on the flags of the slabs they read (the
+ * local rank's rows are read from its own shard and never wait).
+ */
+int ocg_ag_gemm(ocg_handle h, const void* const* a_chunks, int R, int local_rank,
+                int64_t m, int64_t K, const void* b, int64_t N, void* a_gathered, void* c,
+                void* workspace, size_t ws_bytes, const ocg_config* cfg, void* stream);
+
+/*
+ * GEMM-ReduceScatter (one rank's share):
+ *   partial = A x B rounded to bf16 (this rank's send buffer, every row);
+ *   out     = bf16( sum_{s=0..R-1} P_s[rows local*M/R .. (local+1)*M/R) )
+ * where P_local is `partial` and P_s (s != local) are peer_partials[s]. The
+ * sum runs in fp32 over the bf16 partials in ascending rank order s = 0..R-1
+ * with a single rounding at the end, so it is reproducible bit for bit.
+ *   a                : bf16 [M, K];  b: bf16 [K, N]   (M % R == 0)
+ *   peer_partials[s] : bf16 [M, N] for s != local_rank (entry local ignored)
+ *   partial          : bf16 [M, N], written
+ *   out              : bf16 [M/R, N], written
+ * Tiles outside the local row block publish a per-tile flag after storing
+ * their partial (the signal a peer would wait on).
+ */
+int ocg_gemm_rs(ocg_handle h, const void* a, const void* b, int64_t M, int64_t K, int64_t N,
+                int R, int local_rank, const void* const* peer_partials, void* partial, void* out,
+                void* workspace, size_t ws_bytes, const ocg_config* cfg, void* stream);
+
+/*
+ * AllGather + MoE grouped GEMM: tokens t = 0..R*m-1 of the gathered
+ * activations are routed to the top-k experts of their fp32 logits (equal
+ * logits: lower expert first; slot 0 = largest), grouped by expert (stable
+ * in token, slot) and multiplied by the expert's weight:
+ *   out[t*topk + j] = a_gathered[t] x W[topk_ids[t][j]]     (token-slot order)
+ *   logits      : fp32 [R*m, E], read (E <= 64, topk in 1..4)
+ *   w           : bf16 [E, K, N] contiguous, read
+ *   a_gathered  : bf16 [R*m, K], written
+ *   topk_ids    : int32 [R*m, topk], written
+ *   topk_w      : fp32 [R*m, topk], written (softmax probability of each pick)
+ *   perm        : int32 [R*m*topk], written: token-slot indices sorted by expert
+ *   expert_offsets : int32 [E+1], written (may be NULL): row offsets of each
+ *                    expert in `perm`
+ *   out         : bf16 [R*m*topk, N], written
+ * The grouped tiles wait on the flags of every peer slab their tokens come
+ * from (a per-tile lookup table built on the device after routing).
+ */
+int ocg_ag_grouped_gemm(ocg_handle h, const void* const* a_chunks, int R, int local_rank,
+                        int64_t m, int64_t K, const float* logits, int E, int topk,
+                        const void* w, int64_t N, void* a_gathered, int32_t* topk_ids,
+                        float* topk_w, int32_t* perm, int32_t* expert_offsets, void* out,
+                        void* workspace, size_t ws_bytes, const ocg_config* cfg, void* stream);
+
+/* Stand-in for a peer's remote notify: writes `value` into `count` uint32
+ * flags at `flags` (device) with release semantics, on `stream`. */
+int ocg_signal(uint32_t* flags, int count, uint32_t value, void* stream);
+
+/* After the stream has drained: returns OCG_ERR_TIMEOUT if any flag wait of
+ * an earlier call on `workspace` exceeded its bound (and clears the record),
+ * OCG_OK otherwise. Synchronous (reads one word). */
+int ocg_check(ocg_handle h, void* workspace);
+
+const char* ocg_status_string(int status);
+
+/* ---- host-only planning queries (no GPU needed; used by tests/tools) ---- */
+
+/* Resolved plan parameters for a call with config `cfg` (NULL = defaults):
+ * out[0]=tile preset, out[1]=BM, out[2]=BN, out[3]=slab rows,
+ * out[4]=copy rows, out[5]=#copy tasks, out[6]=#tiles (static ops),
+ * out[7]=#slabs. For GEMM_RS pass m = M. Returns OCG_OK or an error. */
+int ocg_plan_info(int op, int R, int local_rank, int64_t m, int64_t K, int64_t N,
+                  const ocg_config* cfg, int64_t out[8]);
+
+/* Task of ticket `ticket` in the AG-GEMM / GEMM-RS plan:
+ * desc[0]=kind (1 copy, 2 AG tile, 3 RS tile, 0 none),
+ * copy: desc[1]=chunk, [2]=piece, [3]=row0, [4]=row1, [5]=slab;
+ * tile: desc[1]=rb, [2]=cb, [3]=#dependency slabs (AG) or local-block (RS),
+ *       [4..7]=first four dependency slab ids (-1 if none). */
+int ocg_plan_task(int op, int R, int local_rank, int64_t m, int64_t K, int64_t N,
+                  const ocg_config* cfg, int64_t ticket, int64_t desc[8]);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* OCG_H_ */

@@ -17,7 +17,7 @@ Parity status per function (see each docstring for the pin):
     tests (brute force, closed forms, identities, library special cases).
 """
 from .reference import (  # noqa: F401
-    decode_bf16, encode_bf16_rne, ag_gemm, ag_gemm_entries, gemm_rs,
+    decode_bf16, encode_bf16_rne, ag_gemm, ag_gemm_entries, ag_gemm_block, gemm_rs,
     gemm_rs_entries, reduce_fixed_order, route_topk, sort_by_expert,
     ag_grouped_gemm, ag_grouped_gemm_entries,
 )

@@ -96,6 +96,16 @@ def ag_gemm_entries(a_chunks, b_bits, rows, cols):
     return np.einsum("ik,ik->i", a_rows, b_cols)
 
 
+def ag_gemm_block(a_chunks, b_bits, rows, cols):
+    """The block C[rows][:, cols] of ``ag_gemm`` (float64), for sampled checks
+    at full size: gathered rows times the selected columns of B."""
+    rows = np.asarray(rows, dtype=np.int64)
+    cols = np.asarray(cols, dtype=np.int64)
+    m = a_chunks[0].shape[0]
+    a_rows = np.stack([decode_bf16(a_chunks[int(r) // m][int(r) % m]) for r in rows])
+    return a_rows @ decode_bf16(np.asarray(b_bits)[:, cols])
+
+
 # --------------------------------------------------------------------------
 # GEMM-ReduceScatter  [TL-KF], [TL-TDD]
 # --------------------------------------------------------------------------

@@ -30,7 +30,12 @@ rows S, copy-task rows CT with S % CT == 0):
   column block cb = v % n_cb. A tile waits for every slab overlapping its rows
   that belongs to a chunk other than the local one (local rows are read from
   the local shard directly).
-GEMM-RS: tiles only, same rotation with rb0 = (l*M/R)//BM when swizzled.
+GEMM-RS: tickets [0, n_tiles) are GEMM tiles, same rotation with
+  rb0 = (l*M/R)//BM when swizzled; each stores its bf16 partial and publishes
+  its tile flag. Tickets [n_tiles, n_tiles + ceil(blk/RR)) are reduce tasks
+  over RR-row strips of the local block [l*blk, (l+1)*blk), blk = M/R, in
+  ascending row order; a strip waits for the flags of every tile of the row
+  blocks it overlaps (and for the peers' flags of those tiles).
 MoE: the AG-GEMM copy list, then one tile per (expert e, column block cb,
   row tile rt) in that nesting order; expert e's rows
   [off_e + rt*BM, min(off_e + (rt+1)*BM, off_{e+1})) of the expert-sorted slot
@@ -125,8 +130,12 @@ def ag_gemm_plan(R, m, K, N, local, BM, BN, S, CT, swizzle=True, mode="fused"):
     return tasks
 
 
-def gemm_rs_plan(R, M, N, local, BM, BN, swizzle=True):
-    """Ticket list of the GEMM-RS kernel: (ticket, rb, cb, is_local_block)."""
+def gemm_rs_plan(R, M, N, local, BM, BN, RR, swizzle=True):
+    """Ticket list of the GEMM-RS kernel.
+
+    Tiles: ("tile", ticket, rb, cb, touches_local_block).
+    Reduce strips: ("reduce", ticket, row0, row1, deps) with gathered-row range
+    [row0, row1) inside the local block and deps the (rb, cb) tiles waited on."""
     n_rb, n_cb = _cdiv(M, BM), _cdiv(N, BN)
     blk = M // R
     rb0 = (local * blk) // BM if swizzle else 0
@@ -136,7 +145,15 @@ def gemm_rs_plan(R, M, N, local, BM, BN, swizzle=True):
         cb = v % n_cb
         lo, hi = rb * BM, min((rb + 1) * BM, M)
         has_local = lo < (local + 1) * blk and hi > local * blk
-        out.append((v, rb, cb, has_local))
+        out.append(("tile", v, rb, cb, has_local))
+    t = n_rb * n_cb
+    r = local * blk
+    while r < (local + 1) * blk:
+        r1 = min(r + RR, (local + 1) * blk)
+        deps = tuple((rb, cb) for rb in range(r // BM, (r1 - 1) // BM + 1) for cb in range(n_cb))
+        out.append(("reduce", t, r, r1, deps))
+        t += 1
+        r = r1
     return out
 
 

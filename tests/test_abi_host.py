@@ -1,0 +1,131 @@
+"""Host-only checks of the C-ABI library (no GPU needed): it loads, exports
+every function include/ocg.h declares, rejects bad arguments with status
+codes, and its closed-form ticket schedule equals the oracle's enumerated
+re-derivation ticket by ticket."""
+import ctypes as C
+import os
+import re
+import subprocess
+
+import pytest
+
+import communication_overlapped_gemm_amd as ocg
+from communication_overlapped_gemm_amd import _lib
+from oracle import schedule as sch
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ocg.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ocg_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_exports():
+    assert declared_functions() == sorted(ocg.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    out = subprocess.run(["nm", "-D", "--defined-only", ocg.LIB_PATH], capture_output=True, text=True, check=True)
+    exported = set(re.findall(r"\bT (ocg_\w+)", out.stdout))
+    missing = [f for f in declared_functions() if f not in exported]
+    assert not missing, f"not exported: {missing}"
+    for f in declared_functions():
+        assert hasattr(ocg.lib, f)
+
+
+def test_status_strings_and_defaults():
+    assert ocg.status_string(ocg.OK) == "ok"
+    assert "timed out" in ocg.status_string(ocg.ERR_TIMEOUT)
+    c = ocg.default_config()
+    assert c.tile == -1 and c.swizzle == 1 and c.mode == 0 and c.fault_skip_slab == -1 and not c.trace
+
+
+def test_workspace_bytes_validation():
+    lib = ocg.lib
+    assert lib.ocg_workspace_bytes(0, 8, 1024, 8192, 3584, 0, 0) > 256
+    assert lib.ocg_workspace_bytes(0, 8, 1024, 8190, 3584, 0, 0) == 0      # K % 64
+    assert lib.ocg_workspace_bytes(0, 8, 1024, 8192, 3583, 0, 0) == 0      # N % 8
+    assert lib.ocg_workspace_bytes(0, 17, 1024, 8192, 3584, 0, 0) == 0     # R > 16
+    assert lib.ocg_workspace_bytes(1, 8, 4095, 1792, 4096, 0, 0) == 0      # M % R
+    assert lib.ocg_workspace_bytes(2, 8, 512, 4096, 1792, 32, 2) > 0
+    assert lib.ocg_workspace_bytes(2, 8, 512, 4096, 1792, 65, 2) == 0      # E > 64
+    assert lib.ocg_workspace_bytes(2, 8, 512, 4096, 1792, 32, 5) == 0      # topk > 4
+    assert lib.ocg_workspace_bytes(3, 8, 512, 4096, 1792, 0, 0) == 0       # bad op
+
+
+def test_entry_points_reject_null_arguments_without_a_device():
+    lib = ocg.lib
+    cfg = ocg.default_config()
+    ptrs = (C.c_void_p * 2)()
+    assert lib.ocg_ag_gemm(None, ptrs, 2, 0, 64, 64, None, 64, None, None, None, 0, C.byref(cfg), None) \
+        == ocg.ERR_INVALID_ARG
+    assert lib.ocg_gemm_rs(None, None, None, 64, 64, 64, 2, 0, ptrs, None, None, None, 0, C.byref(cfg), None) \
+        == ocg.ERR_INVALID_ARG
+    assert lib.ocg_signal(None, 4, 1, None) == ocg.ERR_INVALID_ARG
+    assert lib.ocg_create(0, None) == ocg.ERR_INVALID_ARG
+
+
+def test_plan_info_tile_choice():
+    # 70B share: 256x224 tiles (exactly 512 = two rounds of 256 CUs)
+    p = ocg.plan_info(ocg.OP_AG_GEMM, 8, 0, 1024, 8192, 3584)
+    assert (p["BM"], p["BN"], p["n_tiles"]) == (256, 224, 512)
+    # 8B share: 128x224 (256 tiles, one round)
+    p = ocg.plan_info(ocg.OP_AG_GEMM, 8, 0, 512, 4096, 1792)
+    assert (p["BM"], p["BN"], p["n_tiles"]) == (128, 224, 256)
+    p = ocg.plan_info(ocg.OP_GEMM_RS, 8, 0, 4096, 1792, 4096)
+    assert (p["BM"], p["BN"], p["n_tiles"]) == (256, 256, 256)
+
+
+AG_CASES = [
+    # R, m, K, N, local, tile
+    (4, 128, 256, 256, 0, -1),
+    (8, 512, 4096, 1792, 0, -1),
+    (8, 1024, 8192, 3584, 0, -1),
+    (8, 1024, 8192, 3584, 3, -1),
+    (3, 100, 64, 72, 1, ocg.TILE_128x128),
+    (5, 37, 128, 40, 4, ocg.TILE_128x128),
+    (3, 300, 192, 520, 2, ocg.TILE_256x224),
+]
+
+
+@pytest.mark.parametrize("case", AG_CASES)
+@pytest.mark.parametrize("swizzle", [1, 0])
+@pytest.mark.parametrize("mode", ["fused", "gemm_only", "copy_only"])
+def test_ag_plan_matches_oracle_schedule(case, swizzle, mode):
+    R, m, K, N, local, tile = case
+    modes = {"fused": 0, "gemm_only": 1, "copy_only": 2}
+    cfg = ocg.default_config(tile=tile, swizzle=swizzle, mode=modes[mode])
+    info = ocg.plan_info(ocg.OP_AG_GEMM, R, local, m, K, N, cfg)
+    want = sch.ag_gemm_plan(R, m, K, N, local, info["BM"], info["BN"], info["slab_rows"], info["copy_rows"],
+                            bool(swizzle), mode)
+    assert len(want) == info["n_copy_or_strips"] + info["n_tiles"]
+    for t in want + [None]:
+        ticket = len(want) if t is None else t.ticket
+        d = ocg.plan_task(ocg.OP_AG_GEMM, R, local, m, K, N, ticket, cfg)
+        if t is None:
+            assert d[0] == 0
+        elif isinstance(t, sch.CopyTask):
+            assert d[:6] == [1, t.chunk, t.piece, t.row0, t.row1, t.slab]
+        else:
+            deps = list(t.deps)
+            assert d[:4] == [2, t.rb, t.cb, len(deps)]
+            assert d[4:4 + min(4, len(deps))] == deps[:4]
+
+
+@pytest.mark.parametrize("R,M,K,N,local,tile", [(8, 4096, 1792, 4096, 0, -1), (8, 4096, 1792, 4096, 5, -1),
+                                                (4, 96, 64, 40, 2, ocg.TILE_128x128),
+                                                (3, 600, 128, 264, 1, ocg.TILE_256x224)])
+def test_rs_plan_matches_oracle_schedule(R, M, K, N, local, tile):
+    cfg = ocg.default_config(tile=tile)
+    info = ocg.plan_info(ocg.OP_GEMM_RS, R, local, M, K, N, cfg)
+    want = sch.gemm_rs_plan(R, M, N, local, info["BM"], info["BN"], info["n_slabs_or_strip_rows"])
+    for t in want:
+        d = ocg.plan_task(ocg.OP_GEMM_RS, R, local, M, K, N, t[1], cfg)
+        if t[0] == "tile":
+            assert d[:4] == [3, t[2], t[3], int(t[4])]
+        else:
+            assert d[:3] == [5, t[2], t[3]]
+    assert ocg.plan_task(ocg.OP_GEMM_RS, R, local, M, K, N, len(want), cfg)[0] == 0

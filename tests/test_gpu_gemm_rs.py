@@ -1,0 +1,127 @@
+"""GPU parity of the fused GEMM-ReduceScatter: the bf16 partial against the
+float64 oracle, the reduced row block against the oracle and -- bit for bit --
+against the fixed-order float32 reduce of the GPU's own partial and the peer
+partials, the notify/reduce ordering in the trace, and the peer-flag wait."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import schedule as sch
+import workloads
+from gpu_util import Trace, assert_gate, poison, say, to_bits, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def run(ocg, x, cfg=None, workspace=None):
+    a, b = to_dev(x.a), to_dev(x.b)
+    peers = [None if s == x.local_rank else to_dev(x.peers[s]) for s in range(x.R)]
+    part = poison((x.M, x.N))
+    out = poison((x.M // x.R, x.N))
+    ocg.gemm_rs(a, b, peers, x.local_rank, partial=part, out=out, config=cfg, workspace=workspace)
+    torch.cuda.synchronize()
+    return to_bits(part), to_bits(out)
+
+
+def check_reduce_bits(x, part_bits, out_bits):
+    blk = x.M // x.R
+    lo = x.local_rank * blk
+    blocks = [part_bits[lo:lo + blk] if s == x.local_rank else x.peers[s][lo:lo + blk] for s in range(x.R)]
+    want = oracle.reduce_fixed_order(blocks)
+    diff = int((want != out_bits).sum())
+    assert diff == 0, f"{diff} reduced elements differ from the fixed-order float32 reduce"
+
+
+SMALL = [
+    # name, R, M, K, N, local, tile
+    ("r4_128x128", 4, 96, 64, 40, 2, 3),
+    ("r3_256x224", 3, 600, 128, 264, 1, 0),
+    ("r8_l0", 8, 1024, 256, 512, 0, -1),
+    ("r8_l5", 8, 1024, 256, 512, 5, -1),
+    ("r2_256x256", 2, 512, 192, 264, 1, 2),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
+def test_gemm_rs_small_full(ocg, case):
+    name, R, M, K, N, local, tile = case
+    x = workloads.make_gemm_rs(R, M, K, N, seed=200 + R + local, local_rank=local, dist="uniform", scale=1.0)
+    say("gemm_rs", name)
+    part, out = run(ocg, x, ocg.default_config(tile=tile))
+    p_ref, o_ref = oracle.gemm_rs(x.a, x.b, x.peers, R, local)
+    assert_gate(part, p_ref, name + " partial")
+    assert_gate(out, o_ref, name + " out")
+    check_reduce_bits(x, part, out)
+    ocg.Workspace.cached(ocg.OP_GEMM_RS, R, M, K, N).check()
+
+
+def test_gemm_rs_trace_notify_before_reduce(ocg):
+    R, M, K, N, local = 4, 512, 128, 456, 1
+    x = workloads.make_gemm_rs(R, M, K, N, seed=31, local_rank=local, dist="uniform", scale=1.0)
+    cfg = ocg.default_config(tile=ocg.TILE_128x128)
+    info = ocg.plan_info(ocg.OP_GEMM_RS, R, local, M, K, N, cfg)
+    plan = sch.gemm_rs_plan(R, M, N, local, info["BM"], info["BN"], info["n_slabs_or_strip_rows"])
+    tr = Trace(len(plan) + 4)
+    tr.attach(cfg)
+    say("gemm_rs trace")
+    part, out = run(ocg, x, cfg)
+    recs = tr.read(len(plan))
+    assert np.array_equal(recs["ticket"], np.arange(len(plan)))
+    done = {}
+    for t, r in zip(plan, recs):
+        if t[0] == "tile":
+            assert (r["kind"], r["a"], r["b"], r["c"]) == (3, t[2], t[3], int(t[4]))
+            done[(t[2], t[3])] = int(r["t_end"])
+    for t, r in zip(plan, recs):
+        if t[0] == "reduce":
+            assert (r["kind"], r["a"], r["b"], r["c"]) == (5, t[2], t[3], len(t[4]))
+            assert r["flag_seen"] == r["epoch"]
+            # the strip starts reducing only after every tile it reads was notified
+            assert int(r["t_ready"]) >= max(done[d] for d in t[4]) - 0
+    check_reduce_bits(x, part, out)
+
+
+def test_gemm_rs_peer_flags(ocg):
+    """peer_tile_wait stand-in: flags a peer would set remotely. Signalled ->
+    the call completes and matches; never signalled (host-forced, 2 ms bound)
+    -> the timeout is reported and the kernel still drains."""
+    R, M, K, N, local = 4, 512, 128, 256, 2
+    x = workloads.make_gemm_rs(R, M, K, N, seed=41, local_rank=local, dist="uniform", scale=1.0)
+    cfg = ocg.default_config(tile=ocg.TILE_128x128)
+    info = ocg.plan_info(ocg.OP_GEMM_RS, R, local, M, K, N, cfg)
+    local_tiles = (M // R // info["BM"]) * (-(-N // info["BN"]))
+    flags = torch.zeros(R * local_tiles, dtype=torch.int32, device="cuda")
+    ws = ocg.Workspace(ocg.OP_GEMM_RS, R, M, K, N)
+    say("gemm_rs peer flags signalled")
+    ocg.signal(flags, 7)
+    cfg.peer_flags = flags.data_ptr()
+    cfg.peer_flag_value = 7
+    part, out = run(ocg, x, cfg, ws)
+    ws.check()
+    check_reduce_bits(x, part, out)
+    say("gemm_rs peer flags never signalled")
+    cfg.peer_flag_value = 8
+    cfg.spin_timeout_us = 2000
+    run(ocg, x, cfg, ws)
+    with pytest.raises(ocg.OcgError) as ei:
+        ws.check()
+    assert ei.value.code == ocg.ERR_TIMEOUT
+
+
+def test_gemm_rs_8b_share(ocg):
+    x = workloads.workload("gemm_rs_8b").make()
+    say("gemm_rs_8b")
+    part, out = run(ocg, x)
+    check_reduce_bits(x, part, out)
+    blk = x.M // x.R
+    # the reduced block in full against the float64 definition
+    a_blk = oracle.decode_bf16(x.a[:blk])
+    p_blk = a_blk @ oracle.decode_bf16(x.b)
+    o_ref = p_blk + sum(oracle.decode_bf16(x.peers[s][:blk]) for s in range(1, x.R))
+    assert_gate(out, o_ref, "gemm_rs_8b out")
+    # partial: sampled rows from every row block, all columns
+    rng = np.random.default_rng(3)
+    rows = np.unique(np.concatenate([rng.integers(0, x.M, 48), [0, x.M - 1]]))
+    p_rows = oracle.decode_bf16(x.a[rows]) @ oracle.decode_bf16(x.b)
+    assert_gate(part[rows], p_rows, "gemm_rs_8b partial rows")

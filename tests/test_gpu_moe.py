@@ -1,0 +1,97 @@
+"""GPU parity of AllGather + MoE routing + grouped GEMM: routing outputs bit
+for bit (top-k ids, expert-sorted slot list, offsets), gate weights to 1e-5,
+every output row within the gate against the float64 oracle, the gathered
+buffer bit for bit, and the lookup-table tiles against the oracle's list."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import schedule as sch
+import workloads
+from gpu_util import Trace, assert_gate, poison, say, to_bits, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def run(ocg, x, local=0, cfg=None, logits=None):
+    chunks = [to_dev(c) for c in x.a_chunks]
+    lg = torch.from_numpy(np.ascontiguousarray(x.logits if logits is None else logits)).cuda()
+    w = to_dev(x.w)
+    T = x.R * x.m
+    outs = dict(a_gathered=poison((T, x.K)), out=poison((T * x.topk, x.N)))
+    o = ocg.ag_grouped_gemm(chunks, lg, w, x.topk, local, config=cfg, outputs=outs)
+    torch.cuda.synchronize()
+    return o
+
+
+def check(ocg, x, o, name, logits=None):
+    lg = x.logits if logits is None else logits
+    res = oracle.ag_grouped_gemm(x.a_chunks, lg, x.w, x.topk)
+    assert np.array_equal(o["topk_ids"].cpu().numpy(), res["ids"]), "top-k ids"
+    assert np.array_equal(o["expert_offsets"].cpu().numpy(), res["offsets"]), "expert offsets"
+    assert np.array_equal(o["perm"].cpu().numpy(), res["perm"]), "expert-sorted slot list"
+    w_gpu = o["topk_w"].cpu().numpy().astype(np.float64)
+    assert np.all(np.abs(w_gpu - res["weights"]) <= 1e-5 * np.abs(res["weights"]) + 1e-7), "gate weights"
+    assert np.array_equal(to_bits(o["a_gathered"]), res["a_full"])
+    assert_gate(to_bits(o["out"]), res["out"], name)
+    return res
+
+
+SMALL = [
+    # name, R, m, K, N, E, topk, local
+    ("r2_e6", 2, 64, 128, 96, 6, 2, 0),
+    ("r4_e8_l3", 4, 100, 192, 232, 8, 2, 3),
+    ("r3_e5_top1", 3, 50, 64, 40, 5, 1, 1),
+    ("r2_e16_top4", 2, 300, 128, 456, 16, 4, 1),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
+def test_moe_small_full(ocg, case):
+    name, R, m, K, N, E, topk, local = case
+    x = workloads.make_moe(R, m, K, N, E, seed=300 + E, topk=topk, scale=0.5)
+    say("moe", name)
+    o = run(ocg, x, local)
+    check(ocg, x, o, name)
+
+
+def test_moe_ties_and_empty_experts(ocg):
+    """Planted exact ties (whole rows equal, pairs equal) and experts that no
+    token picks: the tie rule (lower expert first) and empty groups."""
+    x = workloads.make_moe(2, 96, 64, 72, 8, seed=11, topk=2, scale=0.5)
+    lg = x.logits.copy()
+    lg[::5] = np.float32(0.5)
+    lg[1::3, 6] = lg[1::3, 2]
+    lg[:, 7] = np.float32(-30.0)         # expert 7 is never chosen
+    say("moe ties")
+    o = run(ocg, x, 1, logits=lg)
+    check(ocg, x, o, "ties", logits=lg)
+
+
+def test_moe_lookup_table_tiles(ocg):
+    x = workloads.make_moe(4, 128, 128, 448, 8, seed=12, topk=2, scale=0.5)
+    cfg = ocg.default_config()
+    info = ocg.plan_info(ocg.OP_AG_GROUPED_GEMM, 4, 0, 128, 128, 448, cfg)
+    res = oracle.ag_grouped_gemm(x.a_chunks, x.logits, x.w, 2)
+    tiles = sch.moe_tiles(res["counts"], res["offsets"], res["perm"], 2, 4, 128, 448, 0, info["BM"],
+                          info["BN"], info["slab_rows"])
+    n = info["n_copy_or_strips"] + len(tiles)
+    tr = Trace(n + 16)
+    tr.attach(cfg)
+    say("moe trace")
+    o = run(ocg, x, 0, cfg)
+    recs = tr.read(n)
+    assert np.array_equal(recs["ticket"], np.arange(n))
+    got = [(int(r["a"]), int(r["b"]), int(r["c"]), int(r["d"]) & 0xFFFF, int(r["d"]) >> 16)
+           for r in recs[info["n_copy_or_strips"]:]]
+    want = [(e, r0, nr, cb, len(deps)) for e, r0, nr, cb, deps in tiles]
+    assert got == want, "grouped tiles follow the lookup table once each"
+    check(ocg, x, o, "lut")
+
+
+def test_moe_full_workload(ocg):
+    x = workloads.workload("ag_moe").make()
+    say("moe full workload")
+    o = run(ocg, x, 0)
+    check(ocg, x, o, "ag_moe")

@@ -159,6 +159,8 @@ def test_ag_gemm_entries_match_full():
     rows = rng.integers(0, 24, 50)
     cols = rng.integers(0, 10, 50)
     assert np.allclose(oracle.ag_gemm_entries(chunks, b, rows, cols), c[rows, cols], rtol=1e-14)
+    br, bc = rows[:7], cols[:5]
+    assert np.allclose(oracle.ag_gemm_block(chunks, b, br, bc), c[np.ix_(br, bc)], rtol=1e-14)
 
 
 # ---------------------------------------------------------------- GEMM-RS

@@ -71,18 +71,28 @@ def test_ag_gemm_plan_modes():
     assert len(g) + len(c) == len(full)
 
 
-@pytest.mark.parametrize("R,M,N,local,BM,BN", [(8, 4096, 4096, 0, 256, 256), (8, 4096, 4096, 5, 256, 256),
-                                               (4, 96, 40, 2, 16, 16), (3, 90, 50, 1, 32, 32)])
-def test_gemm_rs_plan_invariants(R, M, N, local, BM, BN):
-    plan = sch.gemm_rs_plan(R, M, N, local, BM, BN)
+@pytest.mark.parametrize("R,M,N,local,BM,BN,RR", [(8, 4096, 4096, 0, 256, 256, 4), (8, 4096, 4096, 5, 256, 256, 4),
+                                                  (4, 96, 40, 2, 16, 16, 5), (3, 90, 50, 1, 32, 32, 7)])
+def test_gemm_rs_plan_invariants(R, M, N, local, BM, BN, RR):
+    plan = sch.gemm_rs_plan(R, M, N, local, BM, BN, RR)
+    assert [t[1] for t in plan] == list(range(len(plan)))
+    tiles = [t for t in plan if t[0] == "tile"]
+    reds = [t for t in plan if t[0] == "reduce"]
     n_rb, n_cb = -(-M // BM), -(-N // BN)
-    assert sorted((rb, cb) for _, rb, cb, _ in plan) == sorted(itertools.product(range(n_rb), range(n_cb)))
+    assert sorted((rb, cb) for _, _, rb, cb, _ in tiles) == sorted(itertools.product(range(n_rb), range(n_cb)))
     blk = M // R
-    assert plan[0][3]                                  # local row block first
-    assert plan[0][1] * BM <= local * blk < (plan[0][1] + 1) * BM
-    # the local flags mark exactly the tiles that touch the local block
-    for _, rb, cb, loc in plan:
+    assert tiles[0][4]                                 # local row block first
+    assert tiles[0][2] * BM <= local * blk < (tiles[0][2] + 1) * BM
+    for _, _, rb, cb, loc in tiles:
         assert loc == (rb * BM < (local + 1) * blk and min((rb + 1) * BM, M) > local * blk)
+    # reduce strips cover the local block exactly once, after the tiles they read
+    rows = np.zeros(M, dtype=np.int64)
+    tick = {(rb, cb): t for _, t, rb, cb, _ in tiles}
+    for _, t, r0, r1, deps in reds:
+        rows[r0:r1] += 1
+        need = {(rb, cb) for rb in range(n_rb) for cb in range(n_cb) if rb * BM < r1 and (rb + 1) * BM > r0}
+        assert set(deps) == need and all(tick[d] < t for d in deps)
+    assert np.all(rows[local * blk:(local + 1) * blk] == 1) and rows.sum() == blk
 
 
 def test_moe_tiles_cover_every_slot_once():
