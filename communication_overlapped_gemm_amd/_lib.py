@@ -24,7 +24,7 @@ ERR_NO_DEVICE = -6
 
 OP_AG_GEMM, OP_GEMM_RS, OP_AG_GROUPED_GEMM = 0, 1, 2
 MODE_FUSED, MODE_GEMM_ONLY, MODE_COPY_ONLY = 0, 1, 2
-TILE_AUTO, TILE_256x224, TILE_128x224, TILE_256x256, TILE_128x128 = -1, 0, 1, 2, 3
+TILE_AUTO, TILE_256x224, TILE_128x224, TILE_128x256, TILE_128x128 = -1, 0, 1, 2, 3
 
 EXPORTS = [
     "ocg_config_default", "ocg_create", "ocg_destroy", "ocg_workspace_bytes",
@@ -48,7 +48,7 @@ class TraceRec(C.Structure):
         ("ticket", C.c_uint32), ("kind", C.c_uint32), ("a", C.c_uint32), ("b", C.c_uint32),
         ("c", C.c_uint32), ("d", C.c_uint32), ("hw", C.c_uint32), ("epoch", C.c_uint32),
         ("t_start", C.c_uint64), ("t_ready", C.c_uint64), ("t_end", C.c_uint64),
-        ("flag_seen", C.c_uint32), ("pad", C.c_uint32),
+        ("flag_seen", C.c_uint32), ("queue", C.c_uint32),
     ]
 
 

@@ -68,7 +68,7 @@ bool shape_ok(int R, int64_t m, int64_t K, int64_t N) {
 // Estimated cost of a tile preset: rounds of the persistent grid times the
 // tile area, derated for the smaller wave tiles.
 int choose_tile(int64_t M, int64_t N, int cus) {
-  static const double eff[OCG_TILE_COUNT] = {1.0, 0.9, 1.0, 0.75};
+  static const double eff[OCG_TILE_COUNT] = {1.0, 0.9, 0.92, 0.75};
   int best = OCG_TILE_128x128;
   double best_cost = 1e300;
   for (int t = 0; t < OCG_TILE_COUNT; ++t) {
@@ -415,6 +415,10 @@ int ocg_plan_task(int op, int R, int local_rank, int64_t m, int64_t K, int64_t N
       desc[1] = rb;
       desc[2] = cb;
       desc[3] = rs_tile_touches_local(p, rb) ? 1 : 0;
+      int q, t;
+      tile_queue((int)ticket, &q, &t);
+      desc[4] = q;
+      desc[5] = t;
     } else {
       int r0, r1;
       rs_strip(p, (int)(ticket - p.n_tiles), &r0, &r1);

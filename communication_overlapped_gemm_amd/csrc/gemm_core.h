@@ -1,0 +1,276 @@
+// bf16 MFMA tile engine for gfx950 (one workgroup = 4 waves, one tile).
+//
+// Tile BM x BN, K consumed in stages of 32. The four waves are stacked along
+// M: wave w owns rows [w*BM/4, (w+1)*BM/4) and every column, computed with
+// v_mfma_f32_32x32x16_bf16 (one 32x32 accumulator per (32-row, 32-col) block).
+//
+// Stage s of the K loop lives in slot s % S of an S-slot LDS ring:
+//   A part [BM][32] bf16, 64-byte rows; the 16-byte chunk c of row r is stored
+//     at chunk position c ^ swz_a(r) (conflict-free 16-lane row reads);
+//   B part [BN/32 blocks][32 k][32 n] bf16, 64-byte rows, kept k-major as in
+//     memory; the 32-byte halves of row k swap when bit 3 of k is set. The MFMA
+//     operand (8 consecutive k of one column per lane) is read with the gfx950
+//     transposing LDS read ds_read_b64_tr_b16.
+// Slots are filled by direct-to-LDS 16-byte loads (global_load_lds_dwordx4 for
+// A rows, buffer_load_dwordx4 ... lds for B with out-of-range rows reading as
+// zero), S-1 stages ahead. They are issued from inline assembly so the
+// compiler does not add its own whole-queue waits before every LDS read; the
+// explicit vmcnt waits plus one barrier per stage order them. Fragments of
+// stage k+1 are read into registers while stage k's MFMAs run.
+//
+// The MFMA's A operand carries B (rows = n) and its B operand carries A
+// (columns = m), so each lane ends with 4 consecutive output columns of one
+// row: acc[f][g][4*q + r] = C[m = w*BM/4 + 32f + (lane & 31)]
+//                          [n = 32g + 8q + 4*(lane >> 5) + r].
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ocg {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+#define OCG_LDS __attribute__((address_space(3)))
+
+constexpr int BKS = 32;   // K per stage
+
+template <int BM, int BN>
+struct Gemm {
+  static constexpr int S = 4;                       // LDS ring slots
+  static constexpr int WM = BM / 4;                 // rows per wave
+  static constexpr int FM = WM / 32, FN = BN / 32;  // 32x32 blocks per wave
+  static constexpr int A_BYTES = BM * BKS * 2;
+  static constexpr int B_BYTES = BN * BKS * 2;
+  static constexpr int STAGE = A_BYTES + B_BYTES;
+  static constexpr int A_INST = A_BYTES / 1024;     // 1 KiB DMA instructions per stage
+  static constexpr int B_INST = B_BYTES / 1024;
+  static constexpr int A_PER_WAVE = A_INST / 4;
+  static constexpr int B_MAX = (B_INST + 3) / 4, B_MIN = B_INST / 4;  // B instructions j -> wave j % 4
+  static constexpr int LD_C = BN + 8;               // epilogue staging row (elements)
+  static constexpr int LDS_BYTES = (S * STAGE > BM * LD_C * 2) ? S * STAGE : BM * LD_C * 2;
+  static_assert(WM % 32 == 0 && BN % 32 == 0, "whole 32x32 blocks per wave");
+  static_assert(A_INST % 4 == 0, "A DMA instructions split evenly over the waves");
+  static_assert(LDS_BYTES <= 160 * 1024 - 64, "fits the 160 KiB LDS of a gfx950 CU");
+};
+
+__device__ __forceinline__ int swz_a(int r) { return ((r >> 1) & 3) ^ ((r >> 3) & 1); }
+__device__ __forceinline__ int swz_b(int k) { return (k >> 3) & 1; }
+
+__device__ __forceinline__ uint32_t lds_u32(OCG_LDS const void* p) { return (uint32_t)(uintptr_t)p; }
+
+__device__ __forceinline__ void dma_global(uint32_t lds, const void* g) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(g) : "memory", "m0");
+}
+__device__ __forceinline__ void dma_buffer(uint32_t lds, __amdgpu_buffer_rsrc_t r, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(lds), "v"(voff), "s"(r)
+               : "memory", "m0");
+}
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+template <int BM, int BN>
+struct Frags {
+  bf16x8_t a[Gemm<BM, BN>::FM][2];   // [32-row block][k16 half]
+  bf16x8_t b[Gemm<BM, BN>::FN][2];   // [32-col block][k16 half]
+};
+
+template <int BM, int BN>
+struct TileCtx {
+  const char* rowp[Gemm<BM, BN>::A_PER_WAVE];  // A row of DMA instruction i for this lane, at k = 0
+  __amdgpu_buffer_rsrc_t brs;                   // B [K][N] (out-of-range reads return 0)
+  int N, n0, nk;
+};
+
+// Row of the tile that lane `lane` of DMA instruction i (of wave `wave`) loads.
+template <int BM, int BN>
+__device__ __forceinline__ int dma_row(int wave, int i, int lane) {
+  return (wave * Gemm<BM, BN>::A_PER_WAVE + i) * 16 + (lane >> 2);
+}
+
+template <int BM, int BN>
+__device__ __forceinline__ void issue_stage(uint32_t slot, const TileCtx<BM, BN>& t, int s, int wave) {
+  using G = Gemm<BM, BN>;
+  const int lane = threadIdx.x & 63;
+  const int kbyte = s * BKS * 2;
+#pragma unroll
+  for (int i = 0; i < G::A_PER_WAVE; ++i) {
+    const int blk = wave * G::A_PER_WAVE + i;
+    const int r = blk * 16 + (lane >> 2);
+    const int c = (lane & 3) ^ swz_a(r);
+    dma_global(slot + blk * 1024, t.rowp[i] + kbyte + c * 16);
+  }
+#pragma unroll
+  for (int i = 0; i < G::B_MAX; ++i) {
+    const int j = wave + 4 * i;
+    if (j < G::B_INST) {
+      const int nb = j >> 1, k = (j & 1) * 16 + (lane >> 2);
+      const int c = (lane & 3) ^ (2 * swz_b(k));
+      // byte offset of B[s*32 + k][n0 + 32*nb + 8*c]; K*N*2 < 2^32 (unsigned math)
+      dma_buffer(slot + G::A_BYTES + j * 1024, t.brs,
+                 ((uint32_t)(s * BKS + k) * (uint32_t)t.N + (uint32_t)(t.n0 + nb * 32 + c * 8)) * 2u);
+    }
+  }
+}
+
+// Wait until at most `n` stages of this wave's DMA loads are outstanding.
+template <int BM, int BN>
+__device__ __forceinline__ void wait_stages(int n, bool big) {
+  using G = Gemm<BM, BN>;
+  constexpr int LB = G::A_PER_WAVE + G::B_MAX, LS = G::A_PER_WAVE + G::B_MIN;
+  if (n <= 0) {
+    vm_wait<0>();
+  } else if (n == 1) {
+    if (big) vm_wait<LB>(); else vm_wait<LS>();
+  } else {
+    if (big) vm_wait<2 * LB>(); else vm_wait<2 * LS>();
+  }
+}
+
+struct FragAddr {
+  uint32_t a0, a1;   // A block f=0 for k16 half 0 / 1 (block f adds f*2048)
+  uint32_t b;        // B block g, half ks, rows lo/hi: + g*2048 + ks*1024 + hi*256
+};
+
+template <int BM, int BN>
+__device__ __forceinline__ FragAddr frag_addr(int wave) {
+  using G = Gemm<BM, BN>;
+  const int lane = threadIdx.x & 63;
+  FragAddr fa;
+  const int r = wave * G::WM + (lane & 31);
+  const int h = lane >> 5, s = swz_a(r);
+  fa.a0 = r * 64 + ((h ^ s) * 16);
+  fa.a1 = r * 64 + (((2 | h) ^ s) * 16);
+  const int q = lane >> 4, j = lane & 15;
+  const int kk = 8 * (q >> 1) + (j >> 2);
+  fa.b = G::A_BYTES + kk * 64 + (((q & 1) ^ swz_b(kk)) * 32) + (j & 3) * 8;
+  return fa;
+}
+
+template <int BM, int BN>
+__device__ __forceinline__ void read_frags(OCG_LDS const char* st, const FragAddr& fa, Frags<BM, BN>& fr) {
+  using G = Gemm<BM, BN>;
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+    for (int g = 0; g < G::FN; ++g) {
+      bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((OCG_LDS bf16x4_t*)(st + fa.b + g * 2048 + ks * 1024));
+      bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+          (OCG_LDS bf16x4_t*)(st + fa.b + g * 2048 + ks * 1024 + 256));
+      fr.b[g][ks] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+#pragma unroll
+  for (int f = 0; f < G::FM; ++f) {
+    fr.a[f][0] = *(OCG_LDS const bf16x8_t*)(st + fa.a0 + f * 2048);
+    fr.a[f][1] = *(OCG_LDS const bf16x8_t*)(st + fa.a1 + f * 2048);
+  }
+}
+
+template <int BM, int BN>
+__device__ __forceinline__ void mfma_frags(const Frags<BM, BN>& fr,
+                                           f32x16_t (&acc)[Gemm<BM, BN>::FM][Gemm<BM, BN>::FN]) {
+  using G = Gemm<BM, BN>;
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+    for (int f = 0; f < G::FM; ++f)
+#pragma unroll
+      for (int g = 0; g < G::FN; ++g)
+        acc[f][g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr.b[g][ks], fr.a[f][ks], acc[f][g], 0, 0, 0);
+}
+
+// C tile += A[rows of t.rowp][0:K] x B[0:K][n0:n0+BN], K = 32 * t.nk (nk even).
+// Starts and ends with every wave past a barrier; LDS is free afterwards.
+template <int BM, int BN>
+__device__ __forceinline__ void mainloop(OCG_LDS char* smem, const TileCtx<BM, BN>& t,
+                                         f32x16_t (&acc)[Gemm<BM, BN>::FM][Gemm<BM, BN>::FN]) {
+  using G = Gemm<BM, BN>;
+  constexpr int S = G::S;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const bool big = (wave + 4 * (G::B_MAX - 1)) < G::B_INST;   // this wave issues B_MAX B loads
+  const uint32_t base = lds_u32(smem);
+  const FragAddr fa = frag_addr<BM, BN>(wave);
+  const int nk = t.nk;
+#pragma unroll
+  for (int f = 0; f < G::FM; ++f)
+#pragma unroll
+    for (int g = 0; g < G::FN; ++g) acc[f][g] = f32x16_t{};
+  const int pro = nk < S - 1 ? nk : S - 1;
+  for (int s = 0; s < pro; ++s) issue_stage<BM, BN>(base + s * G::STAGE, t, s, wave);
+  Frags<BM, BN> f0, f1;
+  wait_stages<BM, BN>(pro - 1, big);
+  lds_barrier();
+  read_frags<BM, BN>(smem, fa, f0);
+  auto step = [&](int k, Frags<BM, BN>& cur, Frags<BM, BN>& nxt) {
+    if (k + 1 < nk) {
+      // stages issued: 0 .. min(k+S-2, nk-1); stage k+1 must have landed
+      const int issued = (k + S - 2 < nk - 1 ? k + S - 2 : nk - 1);
+      wait_stages<BM, BN>(issued - (k + 1), big);
+      lds_barrier();
+      if (k + S - 1 < nk) issue_stage<BM, BN>(base + ((k + S - 1) % S) * G::STAGE, t, k + S - 1, wave);
+      read_frags<BM, BN>(smem + ((k + 1) % S) * G::STAGE, fa, nxt);
+    }
+    mfma_frags<BM, BN>(cur, acc);
+  };
+  for (int k = 0; k < nk; k += 2) {
+    step(k, f0, f1);
+    step(k + 1, f1, f0);
+  }
+  lds_barrier();
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// Round the tile to bf16 (nearest-even, v_cvt_pk_bf16_f32) and stage it in
+// LDS as [BM][BN + 8]; ends with a barrier.
+template <int BM, int BN>
+__device__ __forceinline__ void stage_c(OCG_LDS char* smem, const f32x16_t (&acc)[Gemm<BM, BN>::FM][Gemm<BM, BN>::FN]) {
+  using G = Gemm<BM, BN>;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  OCG_LDS uint16_t* cst = (OCG_LDS uint16_t*)smem;
+#pragma unroll
+  for (int f = 0; f < G::FM; ++f) {
+    const int row = wave * G::WM + 32 * f + (lane & 31);
+#pragma unroll
+    for (int g = 0; g < G::FN; ++g) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int col = 32 * g + 8 * q + 4 * (lane >> 5);
+        u32x2_t v = {pack_bf16x2(acc[f][g][4 * q + 0], acc[f][g][4 * q + 1]),
+                     pack_bf16x2(acc[f][g][4 * q + 2], acc[f][g][4 * q + 3])};
+        *(OCG_LDS u32x2_t*)(cst + row * G::LD_C + col) = v;
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  __syncthreads();
+}
+
+// f(row_in_tile, col_in_tile, 16-byte value) over every 16-byte chunk of the
+// staged tile, consecutive threads on consecutive chunks of a row.
+template <int BM, int BN, class F>
+__device__ __forceinline__ void for_each_c_chunk(OCG_LDS const char* smem, F f) {
+  using G = Gemm<BM, BN>;
+  constexpr int CPR = BN / 8;
+  OCG_LDS const uint16_t* cst = (OCG_LDS const uint16_t*)smem;
+  for (int i = threadIdx.x; i < BM * CPR; i += 256) {
+    const int row = i / CPR, c8 = i - row * CPR;
+    f(row, c8 * 8, *(OCG_LDS const u32x4_t*)(cst + row * G::LD_C + c8 * 8));
+  }
+}
+
+}  // namespace ocg

@@ -1,16 +1,17 @@
 // gfx950 kernels of the communication-overlapped GEMM library.
 //
-// One persistent kernel per operation. Each workgroup (4 waves of 64) loops:
-// take a ticket (one atomic), run the task it names, repeat. Tasks are either
-// copy tasks (pull one piece of a peer's shard into the gathered buffer, then
-// publish the slab's flag: "produce_tile_notify") or GEMM tiles (wait for the
-// flags of the slabs they read: "consume_tile_wait", then an LDS-staged bf16
-// MFMA main loop). The primitives follow "TileLink: Generating Efficient
-// Compute-Communication Overlapping Kernels using Tile-Centric Primitives"
-// (MLSys 2025 talk summary), "Technical Deep Dive": signal primitives between
-// producer and consumer tiles; a notify lowered to a synchronisation, the
-// tile id and an atomic; pull-mode transfers whose "transfer complete"
-// barrier is the slab flag.
+// One persistent kernel per operation. Each workgroup (4 waves of 64) first
+// takes copy tasks from a global ticket counter -- pull one piece of a peer's
+// shard into the gathered buffer, then publish the slab's flag
+// ("produce_tile_notify") -- and then GEMM tiles from its XCD's queue, each
+// tile waiting on the flags of the slabs it reads ("consume_tile_wait")
+// before the MFMA main loop of gemm_core.h. The primitives follow "TileLink:
+// Generating Efficient Compute-Communication Overlapping Kernels using
+// Tile-Centric Primitives" (MLSys 2025 talk summary), "Technical Deep Dive":
+// signal primitives between producer and consumer tiles; a notify lowered to
+// a synchronisation, the tile id and an atomic; pull transfers whose
+// "transfer complete" barrier is the slab flag; lookup tables for the
+// dynamic (MoE) dependencies.
 //
 // Memory-model contract (agent scope, all 8 XCDs):
 //   producer: stores; every thread release-fences (waits for its stores and
@@ -22,43 +23,16 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "gemm_core.h"
 #include "ocg_internal.h"
 
 namespace ocg {
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
-
 typedef __attribute__((address_space(1))) const u32x4_t* gcptr16;
 typedef __attribute__((address_space(1))) u32x4_t* gptr16;
-typedef __attribute__((address_space(1))) u32x2_t* gptr8;
-typedef __attribute__((address_space(1))) const u32x2_t* gcptr8;
-
-constexpr int BK = 64;        // K step of the main loop
-constexpr int LDK = BK + 8;   // padded LDS row (elements): 144 B rows keep ds_read_b128 conflict-free
-
-template <int BM, int BN>
-struct TileShape {
-  static constexpr int WM = BM / 2, WN = BN / 2;   // 2 x 2 waves
-  static constexpr int FM = WM / 16, FN = WN / 16; // 16x16 MFMA fragments per wave
-  static constexpr int A_ELEMS = BM * LDK;         // A tile [BM][BK] (k contiguous)
-  static constexpr int B_ELEMS = BN * LDK;         // B tile transposed [BN][BK] (k contiguous)
-  static constexpr int STAGE = A_ELEMS + B_ELEMS;
-  static constexpr int LDS_ELEMS = 2 * STAGE;      // double buffered
-  static constexpr int A_LOADS = BM * (BK / 8) / kThreads;  // 16-byte loads per thread
-  static constexpr int B_BLOCKS = (BK / 8) * (BN / 8);      // 8x8 blocks per K step
-  static_assert(WN % 16 == 0 && WM % 16 == 0, "wave tile must hold whole fragments");
-  static_assert(B_BLOCKS <= kThreads, "one 8x8 B block per thread");
-  static_assert(LDS_ELEMS * 2 <= 163840, "fits the 160 KiB LDS of a gfx950 CU");
-};
 
 __device__ __forceinline__ u32x4_t gload16(const void* p) { return *(gcptr16)p; }
 __device__ __forceinline__ void gstore16(void* p, u32x4_t v) { *(gptr16)p = v; }
-__device__ __forceinline__ void gstore8(void* p, u32x2_t v) { *(gptr8)p = v; }
-__device__ __forceinline__ u32x2_t gload8(const void* p) { return *(gcptr8)p; }
 
 __device__ __forceinline__ uint64_t now_ticks() { return __builtin_amdgcn_s_memrealtime(); }
 
@@ -69,12 +43,6 @@ __device__ __forceinline__ uint32_t xcc_id() {
 }
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
-
-// Round-to-nearest-even fp32 -> bf16 pair (hardware v_cvt_pk_bf16_f32).
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  bf16x2_t v = {(__bf16)lo, (__bf16)hi};
-  return __builtin_bit_cast(uint32_t, v);
-}
 
 // ---------------------------------------------------------------- flags
 
@@ -100,7 +68,7 @@ __device__ bool wait_flag(const uint32_t* flag, uint32_t want, const Common& cm,
 // produce_tile_notify for copy tasks: called by every thread after its
 // stores; returns (to thread 0) whether this task published the slab flag.
 __device__ bool publish_slab(uint32_t* cnt, uint32_t* flag, int slab, int target, uint32_t epoch,
-                             const Common& cm, uint32_t* s_bcast) {
+                             const Common& cm) {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
   __syncthreads();
   bool published = false;
@@ -139,225 +107,84 @@ __device__ __forceinline__ void copy_granules(const uint16_t* src, uint16_t* dst
 // gathered matrix come from rank `chunk`'s shard.
 __device__ void run_copy_task(const AgPlan& p, const uint16_t* const* chunks, uint16_t* a_gathered,
                               uint32_t* slab_cnt, uint32_t* slab_flag, int u, uint32_t epoch,
-                              const Common& cm, uint32_t ticket, uint32_t* s_bcast) {
+                              const Common& cm) {
   uint64_t t0 = now_ticks();
   CopyDesc d = copy_desc(p, u);
   const uint16_t* src = chunks[d.chunk] + (size_t)(d.row0 - d.chunk * p.m) * p.K;
   uint16_t* dst = a_gathered + (size_t)d.row0 * p.K;
   copy_granules(src, dst, (size_t)(d.row1 - d.row0) * p.K / 8);
   int target = slab_target(p.m, p.S, p.CT, p.bpr, d.slab);
-  bool pub = publish_slab(slab_cnt, slab_flag, d.slab, target, epoch, cm, s_bcast);
-  if (threadIdx.x == 0 && cm.trace && ticket < cm.trace_cap) {
-    ocg_trace_rec* r = cm.trace + ticket;
+  bool pub = publish_slab(slab_cnt, slab_flag, d.slab, target, epoch, cm);
+  if (threadIdx.x == 0 && cm.trace && (uint32_t)u < cm.trace_cap) {
+    ocg_trace_rec* r = cm.trace + u;
     uint64_t t1 = now_ticks();
-    r->ticket = ticket; r->kind = 1; r->a = d.chunk; r->b = d.piece; r->c = d.slab; r->d = pub;
+    r->ticket = u; r->kind = 1; r->a = d.chunk; r->b = d.piece; r->c = d.slab; r->d = pub;
     r->hw = (xcc_id() << 16) | blockIdx.x; r->epoch = epoch;
-    r->t_start = t0; r->t_ready = t1; r->t_end = t1; r->flag_seen = 0; r->pad = 0;
+    r->t_start = t0; r->t_ready = t1; r->t_end = t1; r->flag_seen = 0; r->queue = 0;
   }
 }
 
-// ---------------------------------------------------------------- MFMA tile engine
-
-// Per-thread A-row sources for one tile: each thread stages A_LOADS rows of
-// the BM x 64 A tile per K step; `rows[q]` already points at the thread's
-// 16-byte column within the row (k = 0).
-template <int BM, int BN>
-struct ARows {
-  const uint16_t* rows[TileShape<BM, BN>::A_LOADS];
-};
-
-template <int BM, int BN>
-__device__ __forceinline__ void load_a(const ARows<BM, BN>& ar, int kt, u32x4_t* ra) {
-#pragma unroll
-  for (int q = 0; q < TileShape<BM, BN>::A_LOADS; ++q) ra[q] = gload16(ar.rows[q] + kt * BK);
-}
-
-template <int BM, int BN>
-__device__ __forceinline__ void store_a(uint16_t* st, const u32x4_t* ra) {
-  const int t = threadIdx.x;
-#pragma unroll
-  for (int q = 0; q < TileShape<BM, BN>::A_LOADS; ++q) {
-    int i = t + kThreads * q;
-    int row = i >> 3, kc = i & 7;
-    *(u32x4_t*)(st + row * LDK + kc * 8) = ra[q];
-  }
-}
-
-// B tile: thread t < B_BLOCKS owns the 8x8 block (k rows 8*kb.., columns
-// 8*j..) of the 64 x BN tile; rows beyond K read as zero (buffer range).
-template <int BM, int BN>
-__device__ __forceinline__ void load_b(__amdgpu_buffer_rsrc_t rs, int N, int n0, int kt, u32x4_t* rb) {
-  const int t = threadIdx.x;
-  if (t < TileShape<BM, BN>::B_BLOCKS) {
-    int kb = t & 7, j = t >> 3;
-    int k = kt * BK + kb * 8;
-    int off = (k * N + n0 + j * 8) * 2;
-#pragma unroll
-    for (int r = 0; r < 8; ++r) rb[r] = __builtin_amdgcn_raw_buffer_load_b128(rs, off + r * N * 2, 0, 0);
-  }
-}
-
-// Transpose the 8x8 bf16 block in registers and store it k-contiguous:
-// LDS row n holds B[k][n] for the 64 k of the step.
-template <int BM, int BN>
-__device__ __forceinline__ void store_b(uint16_t* st, const u32x4_t* rb) {
-  const int t = threadIdx.x;
-  if (t < TileShape<BM, BN>::B_BLOCKS) {
-    int kb = t & 7, j = t >> 3;
-    uint16_t* base = st + TileShape<BM, BN>::A_ELEMS + (j * 8) * LDK + kb * 8;
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const int dw = c >> 1;
-      u32x4_t o;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        uint32_t x = rb[2 * i][dw], y = rb[2 * i + 1][dw];
-        o[i] = (c & 1) ? ((x >> 16) | (y & 0xFFFF0000u)) : ((x & 0xFFFFu) | (y << 16));
-      }
-      *(u32x4_t*)(base + c * LDK) = o;
-    }
-  }
-}
-
-// acc[f][g] holds C[m = wm*WM + 16f + (lane & 15)][n = wn*WN + 16g + 4*(lane >> 4) + e].
-// The MFMA's A operand carries B^T (rows = n) and its B operand carries A
-// (columns = m), so each lane ends up with 4 consecutive columns of one row.
-template <int BM, int BN>
-__device__ __forceinline__ void mainloop(uint16_t* smem, const ARows<BM, BN>& ar, __amdgpu_buffer_rsrc_t brs,
-                                         int N, int n0, int nk,
-                                         f32x4_t (&acc)[TileShape<BM, BN>::FM][TileShape<BM, BN>::FN]) {
-  using TS = TileShape<BM, BN>;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int koff = (lane >> 4) * 8;
-  const int arow = wm * TS::WM + (lane & 15);
-  const int brow = wn * TS::WN + (lane & 15);
-#pragma unroll
-  for (int f = 0; f < TS::FM; ++f)
-#pragma unroll
-    for (int g = 0; g < TS::FN; ++g) acc[f][g] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-  u32x4_t ra[TS::A_LOADS];
-  u32x4_t rb[8];
-  load_a<BM, BN>(ar, 0, ra);
-  load_b<BM, BN>(brs, N, n0, 0, rb);
-  store_a<BM, BN>(smem, ra);
-  store_b<BM, BN>(smem, rb);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    uint16_t* cur = smem + (kt & 1) * TS::STAGE;
-    uint16_t* nxt = smem + ((kt & 1) ^ 1) * TS::STAGE;
-    const bool more = kt + 1 < nk;
-    if (more) {
-      load_a<BM, BN>(ar, kt + 1, ra);
-      load_b<BM, BN>(brs, N, n0, kt + 1, rb);
-    }
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      bf16x8_t af[TS::FM], bfr[TS::FN];
-#pragma unroll
-      for (int f = 0; f < TS::FM; ++f)
-        af[f] = *(const bf16x8_t*)(cur + (arow + 16 * f) * LDK + ks * 32 + koff);
-#pragma unroll
-      for (int g = 0; g < TS::FN; ++g)
-        bfr[g] = *(const bf16x8_t*)(cur + TS::A_ELEMS + (brow + 16 * g) * LDK + ks * 32 + koff);
-#pragma unroll
-      for (int f = 0; f < TS::FM; ++f)
-#pragma unroll
-        for (int g = 0; g < TS::FN; ++g)
-          acc[f][g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[g], af[f], acc[f][g], 0, 0, 0);
-    }
-    if (more) {
-      store_a<BM, BN>(nxt, ra);
-      store_b<BM, BN>(nxt, rb);
-    }
-    __syncthreads();
-  }
-}
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
-}
-
-// Epilogue: the fp32 tile is rounded to bf16 and staged in LDS as
-// [BM][BN + 8] (reusing the operand buffers), then streamed out in 16-byte
-// row chunks so every global store is a full, coalesced 16-byte write.
-template <int BM, int BN>
-struct CStage {
-  static constexpr int LD = BN + 8;
-  static constexpr int CPR = BN / 8;   // 16-byte chunks per row
-  static_assert(BM * LD <= TileShape<BM, BN>::LDS_ELEMS, "C tile fits in the operand buffers");
-};
-
-template <int BM, int BN>
-__device__ __forceinline__ void stage_c(uint16_t* cst,
-                                        const f32x4_t (&acc)[TileShape<BM, BN>::FM][TileShape<BM, BN>::FN]) {
-  using TS = TileShape<BM, BN>;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-#pragma unroll
-  for (int f = 0; f < TS::FM; ++f) {
-    const int row = wm * TS::WM + 16 * f + (lane & 15);
-#pragma unroll
-    for (int g = 0; g < TS::FN; ++g) {
-      const int col = wn * TS::WN + 16 * g + 4 * (lane >> 4);
-      u32x2_t v = {pack_bf16x2(acc[f][g][0], acc[f][g][1]), pack_bf16x2(acc[f][g][2], acc[f][g][3])};
-      *(u32x2_t*)(cst + row * CStage<BM, BN>::LD + col) = v;
-    }
-  }
-  __syncthreads();
-}
-
-// f(row_in_tile, col_in_tile, 16-byte value) over every chunk of the tile.
-template <int BM, int BN, class F>
-__device__ __forceinline__ void for_each_c_chunk(const uint16_t* cst, F f) {
-  using CS = CStage<BM, BN>;
-  for (int i = threadIdx.x; i < BM * CS::CPR; i += kThreads) {
-    const int row = i / CS::CPR, c8 = i - row * CS::CPR;
-    f(row, c8 * 8, *(const u32x4_t*)(cst + row * CS::LD + c8 * 8));
-  }
-}
-
-// ---------------------------------------------------------------- common loop pieces
+// ---------------------------------------------------------------- scheduling helpers
 
 __device__ __forceinline__ uint32_t read_epoch(WsHeader* hdr, uint32_t* s_bcast) {
   if (threadIdx.x == 0) {
     uint32_t e = __hip_atomic_load(&hdr->epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
     s_bcast[1] = e ? e : 1u;
+    s_bcast[3] = xcc_id();
   }
   __syncthreads();
   return s_bcast[1];
 }
 
-__device__ __forceinline__ uint32_t next_ticket(WsHeader* hdr, uint32_t* s_bcast) {
+__device__ __forceinline__ uint32_t next_ticket(uint32_t* counter, uint32_t* s_bcast) {
   __syncthreads();
   if (threadIdx.x == 0)
-    s_bcast[0] = __hip_atomic_fetch_add(&hdr->ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_bcast[0] = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
   return s_bcast[0];
 }
 
-// Last workgroup out resets the ticket and done counters and records the epoch.
+// Next tile from the XCD queues: own XCD first, then the others in turn.
+// `*q` carries the queue being drained between calls (starts at the XCD id,
+// `*tried` at 0). Returns the tile index, or -1 when every queue is empty.
+__device__ __forceinline__ int next_tile(WsHeader* hdr, int n_tiles, int* q, int* tried, uint32_t* s_bcast,
+                                         uint32_t* t_out) {
+  while (*tried < kXcds) {
+    const uint32_t t = next_ticket(&hdr->xtick[*q], s_bcast);
+    const int v = xcd_tile(*q, (int)t, n_tiles);
+    if (v >= 0) {
+      *t_out = t;
+      return v;
+    }
+    *q = (*q + 1) % kXcds;
+    ++*tried;
+  }
+  return -1;
+}
+
+// Last workgroup out resets the counters and records the epoch.
 __device__ __forceinline__ void finish(WsHeader* hdr, uint32_t epoch) {
   __syncthreads();
   if (threadIdx.x == 0) {
     uint32_t d = __hip_atomic_fetch_add(&hdr->done, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
     if (d + 1 == gridDim.x) {
       __hip_atomic_store(&hdr->ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      for (int q = 0; q < kXcds; ++q)
+        __hip_atomic_store(&hdr->xtick[q], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_store(&hdr->done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_store(&hdr->epoch, epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 }
 
-__device__ __forceinline__ void trace_tile(const Common& cm, uint32_t ticket, uint32_t kind, uint32_t a, uint32_t b,
+__device__ __forceinline__ void trace_task(const Common& cm, uint32_t slot, uint32_t kind, uint32_t a, uint32_t b,
                                            uint32_t c, uint32_t d, uint32_t epoch, uint64_t t0, uint64_t t1,
-                                           uint32_t seen) {
-  if (threadIdx.x == 0 && cm.trace && ticket < cm.trace_cap) {
-    ocg_trace_rec* r = cm.trace + ticket;
-    r->ticket = ticket; r->kind = kind; r->a = a; r->b = b; r->c = c; r->d = d;
+                                           uint32_t seen, uint32_t queue_ticket) {
+  if (threadIdx.x == 0 && cm.trace && slot < cm.trace_cap) {
+    ocg_trace_rec* r = cm.trace + slot;
+    r->ticket = slot; r->kind = kind; r->a = a; r->b = b; r->c = c; r->d = d;
     r->hw = (xcc_id() << 16) | blockIdx.x; r->epoch = epoch;
-    r->t_start = t0; r->t_ready = t1; r->t_end = now_ticks(); r->flag_seen = seen; r->pad = 0;
+    r->t_start = t0; r->t_ready = t1; r->t_end = now_ticks(); r->flag_seen = seen; r->queue = queue_ticket;
   }
 }
 
@@ -365,27 +192,35 @@ __device__ __forceinline__ void trace_tile(const Common& cm, uint32_t ticket, ui
 
 template <int BM, int BN>
 __global__ __launch_bounds__(kThreads, 1) void ag_gemm_kernel(AgArgs args) {
-  using TS = TileShape<BM, BN>;
-  __shared__ __attribute__((aligned(16))) uint16_t smem[TS::LDS_ELEMS];
+  using G = Gemm<BM, BN>;
+  __shared__ __attribute__((aligned(1024))) char smem_raw[G::LDS_BYTES];
   __shared__ uint32_t s_bcast[8];
+  OCG_LDS char* smem = (OCG_LDS char*)smem_raw;
   const AgPlan& p = args.plan;
   const Common& cm = args.cm;
   const uint32_t epoch = read_epoch(cm.hdr, s_bcast);
-  const uint32_t n_tasks = (uint32_t)(p.n_copy + p.n_tiles);
-  const __amdgpu_buffer_rsrc_t brs = make_rsrc(args.b, (uint32_t)((size_t)p.K * p.N * 2));
-  const int nk = p.K / BK;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
 
+  // copy tasks
   for (;;) {
-    const uint32_t ticket = next_ticket(cm.hdr, s_bcast);
-    if (ticket >= n_tasks) break;
-    if ((int)ticket < p.n_copy) {
-      run_copy_task(p, args.chunks, args.a_gathered, args.slab_cnt, args.slab_flag, (int)ticket, epoch, cm,
-                    ticket, s_bcast);
-      continue;
-    }
+    const uint32_t u = next_ticket(&cm.hdr->ticket, s_bcast);
+    if ((int)u >= p.n_copy) break;
+    run_copy_task(p, args.chunks, args.a_gathered, args.slab_cnt, args.slab_flag, (int)u, epoch, cm);
+  }
+  // GEMM tiles
+  int q = (int)s_bcast[3] % kXcds, tried = 0;
+  uint32_t qt = 0;
+  TileCtx<BM, BN> t;
+  t.brs = make_rsrc(args.b, (uint32_t)((size_t)p.K * p.N * 2));
+  t.N = p.N;
+  t.nk = p.K / BKS;
+  for (;;) {
+    const int v = next_tile(cm.hdr, p.n_tiles, &q, &tried, s_bcast, &qt);
+    if (v < 0) break;
     const uint64_t t0 = now_ticks();
     int rb, cb;
-    tile_of(p.n_rb, p.n_cb, p.rb0, (int)ticket - p.n_copy, &rb, &cb);
+    tile_of(p.n_rb, p.n_cb, p.rb0, v, &rb, &cb);
     const int r0 = rb * BM, r1 = min(r0 + BM, p.M);
     int nwait = 0;
     uint32_t seen = 0;
@@ -398,24 +233,22 @@ __global__ __launch_bounds__(kThreads, 1) void ag_gemm_kernel(AgArgs args) {
     __syncthreads();
     // Rows of the local chunk come from the local shard; all others from the
     // gathered buffer filled by the copy tasks.
-    ARows<BM, BN> ar;
 #pragma unroll
-    for (int q = 0; q < TS::A_LOADS; ++q) {
-      int i = threadIdx.x + kThreads * q;
-      int row = min(r0 + (i >> 3), p.M - 1);
-      int kc = (i & 7) * 8;
-      int c = row / p.m;
-      ar.rows[q] = (c == p.local) ? args.chunks[c] + (size_t)(row - c * p.m) * p.K + kc
-                                  : args.a_gathered + (size_t)row * p.K + kc;
+    for (int i = 0; i < G::A_PER_WAVE; ++i) {
+      const int row = min(r0 + dma_row<BM, BN>(wave, i, lane), p.M - 1);
+      const int c = row / p.m;
+      t.rowp[i] = (const char*)((c == p.local) ? args.chunks[c] + (size_t)(row - c * p.m) * p.K
+                                               : args.a_gathered + (size_t)row * p.K);
     }
-    f32x4_t acc[TS::FM][TS::FN];
     const int n0 = cb * BN;
-    mainloop<BM, BN>(smem, ar, brs, p.N, n0, nk, acc);
+    t.n0 = n0;
+    f32x16_t acc[G::FM][G::FN];
+    mainloop<BM, BN>(smem, t, acc);
     stage_c<BM, BN>(smem, acc);
-    for_each_c_chunk<BM, BN>(smem, [&](int row, int col, u32x4_t v) {
-      if (r0 + row < p.M && n0 + col < p.N) gstore16(args.c + (size_t)(r0 + row) * p.N + n0 + col, v);
+    for_each_c_chunk<BM, BN>(smem, [&](int row, int col, u32x4_t val) {
+      if (r0 + row < p.M && n0 + col < p.N) gstore16(args.c + (size_t)(r0 + row) * p.N + n0 + col, val);
     });
-    trace_tile(cm, ticket, 2, rb, cb, nwait, 0, epoch, t0, t1, seen);
+    trace_task(cm, (uint32_t)(p.n_copy + v), 2, rb, cb, nwait, 0, epoch, t0, t1, seen, ((uint32_t)q << 16) | qt);
   }
   finish(cm.hdr, epoch);
 }
@@ -468,72 +301,81 @@ __device__ void run_reduce_strip(const RsArgs& a, int r0, int r1) {
 
 template <int BM, int BN>
 __global__ __launch_bounds__(kThreads, 1) void gemm_rs_kernel(RsArgs args) {
-  using TS = TileShape<BM, BN>;
-  __shared__ __attribute__((aligned(16))) uint16_t smem[TS::LDS_ELEMS];
+  using G = Gemm<BM, BN>;
+  __shared__ __attribute__((aligned(1024))) char smem_raw[G::LDS_BYTES];
   __shared__ uint32_t s_bcast[8];
+  OCG_LDS char* smem = (OCG_LDS char*)smem_raw;
   const RsPlan& p = args.plan;
   const Common& cm = args.cm;
   const uint32_t epoch = read_epoch(cm.hdr, s_bcast);
-  const __amdgpu_buffer_rsrc_t brs = make_rsrc(args.b, (uint32_t)((size_t)p.K * p.N * 2));
-  const int nk = p.K / BK;
-  const uint32_t n_tasks = (uint32_t)(p.n_tiles + p.n_red);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
 
+  int q = (int)s_bcast[3] % kXcds, tried = 0;
+  uint32_t qt = 0;
+  TileCtx<BM, BN> t;
+  t.brs = make_rsrc(args.b, (uint32_t)((size_t)p.K * p.N * 2));
+  t.N = p.N;
+  t.nk = p.K / BKS;
   for (;;) {
-    const uint32_t ticket = next_ticket(cm.hdr, s_bcast);
-    if (ticket >= n_tasks) break;
+    const int v = next_tile(cm.hdr, p.n_tiles, &q, &tried, s_bcast, &qt);
+    if (v < 0) break;
     const uint64_t t0 = now_ticks();
-    if ((int)ticket >= p.n_tiles) {
-      // consume_tile_wait on the local tiles of the strip, peer_tile_wait on
-      // the peers' tiles, then the fixed-order reduce.
-      int r0, r1;
-      rs_strip(p, (int)ticket - p.n_tiles, &r0, &r1);
-      uint32_t seen = 0;
-      int nwait = 0;
-      if (threadIdx.x == 0) {
-        for (int rb = r0 / BM; rb <= (r1 - 1) / BM; ++rb)
-          for (int cb = 0; cb < p.n_cb; ++cb) {
-            wait_flag(&args.tile_flag[rb * p.n_cb + cb], epoch, cm, &seen);
-            ++nwait;
-            if (args.peer_flags) {
-              const int t_local = (rb - args.local_rb0) * p.n_cb + cb;
-              const int per_rank = args.local_nrb * p.n_cb;
-              for (int s = 0; s < p.R; ++s) {
-                if (s == p.local) continue;
-                wait_flag(&args.peer_flags[s * per_rank + t_local], args.peer_flag_value, cm, &seen);
-                ++nwait;
-              }
-            }
-          }
-      }
-      const uint64_t t1 = now_ticks();
-      __syncthreads();
-      run_reduce_strip(args, r0, r1);
-      trace_tile(cm, ticket, 5, r0, r1, nwait, 0, epoch, t0, t1, seen);
-      continue;
-    }
     int rb, cb;
-    tile_of(p.n_rb, p.n_cb, p.rb0, (int)ticket, &rb, &cb);
+    tile_of(p.n_rb, p.n_cb, p.rb0, v, &rb, &cb);
     const int r0 = rb * BM;
-    ARows<BM, BN> ar;
 #pragma unroll
-    for (int q = 0; q < TS::A_LOADS; ++q) {
-      int i = threadIdx.x + kThreads * q;
-      int row = min(r0 + (i >> 3), p.M - 1);
-      ar.rows[q] = args.a + (size_t)row * p.K + (i & 7) * 8;
+    for (int i = 0; i < G::A_PER_WAVE; ++i) {
+      const int row = min(r0 + dma_row<BM, BN>(wave, i, lane), p.M - 1);
+      t.rowp[i] = (const char*)(args.a + (size_t)row * p.K);
     }
-    f32x4_t acc[TS::FM][TS::FN];
     const int n0 = cb * BN;
-    mainloop<BM, BN>(smem, ar, brs, p.N, n0, nk, acc);
+    t.n0 = n0;
+    f32x16_t acc[G::FM][G::FN];
+    mainloop<BM, BN>(smem, t, acc);
     stage_c<BM, BN>(smem, acc);
-    for_each_c_chunk<BM, BN>(smem, [&](int row, int col, u32x4_t v) {
-      if (r0 + row < p.M && n0 + col < p.N) gstore16(args.partial + (size_t)(r0 + row) * p.N + n0 + col, v);
+    for_each_c_chunk<BM, BN>(smem, [&](int row, int col, u32x4_t val) {
+      if (r0 + row < p.M && n0 + col < p.N) gstore16(args.partial + (size_t)(r0 + row) * p.N + n0 + col, val);
     });
     // produce_tile_notify: the bf16 partial tile is in memory (the send buffer).
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
     __syncthreads();
     if (threadIdx.x == 0)
       __hip_atomic_store(&args.tile_flag[rb * p.n_cb + cb], epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-    trace_tile(cm, ticket, 3, rb, cb, rs_tile_touches_local(p, rb) ? 1u : 0u, 0, epoch, t0, t0, 0);
+    trace_task(cm, (uint32_t)v, 3, rb, cb, rs_tile_touches_local(p, rb) ? 1u : 0u, 0, epoch, t0, t0, 0,
+               ((uint32_t)q << 16) | qt);
+  }
+  // reduce strips, once every tile has been claimed
+  for (;;) {
+    const uint32_t j = next_ticket(&cm.hdr->ticket, s_bcast);
+    if ((int)j >= p.n_red) break;
+    const uint64_t t0 = now_ticks();
+    // consume_tile_wait on the local tiles of the strip, peer_tile_wait on
+    // the peers' tiles, then the fixed-order reduce.
+    int r0, r1;
+    rs_strip(p, (int)j, &r0, &r1);
+    uint32_t seen = 0;
+    int nwait = 0;
+    if (threadIdx.x == 0) {
+      for (int rb = r0 / BM; rb <= (r1 - 1) / BM; ++rb)
+        for (int cb = 0; cb < p.n_cb; ++cb) {
+          wait_flag(&args.tile_flag[rb * p.n_cb + cb], epoch, cm, &seen);
+          ++nwait;
+          if (args.peer_flags) {
+            const int t_local = (rb - args.local_rb0) * p.n_cb + cb;
+            const int per_rank = args.local_nrb * p.n_cb;
+            for (int s = 0; s < p.R; ++s) {
+              if (s == p.local) continue;
+              wait_flag(&args.peer_flags[s * per_rank + t_local], args.peer_flag_value, cm, &seen);
+              ++nwait;
+            }
+          }
+        }
+    }
+    const uint64_t t1 = now_ticks();
+    __syncthreads();
+    run_reduce_strip(args, r0, r1);
+    trace_task(cm, (uint32_t)(p.n_tiles + j), 5, r0, r1, nwait, 0, epoch, t0, t1, seen, 0);
   }
   finish(cm.hdr, epoch);
 }
@@ -675,29 +517,35 @@ __global__ __launch_bounds__(kRouteThreads, 1) void moe_route_kernel(RouteArgs a
 
 template <int BM, int BN>
 __global__ __launch_bounds__(kThreads, 1) void moe_gemm_kernel(MoeArgs args) {
-  using TS = TileShape<BM, BN>;
-  __shared__ __attribute__((aligned(16))) uint16_t smem[TS::LDS_ELEMS];
+  using G = Gemm<BM, BN>;
+  __shared__ __attribute__((aligned(1024))) char smem_raw[G::LDS_BYTES];
   __shared__ uint32_t s_bcast[8];
+  OCG_LDS char* smem = (OCG_LDS char*)smem_raw;
   const AgPlan& p = args.plan;
   const Common& cm = args.cm;
   const uint32_t epoch = read_epoch(cm.hdr, s_bcast);
   if (threadIdx.x == 0) s_bcast[2] = __hip_atomic_load(&cm.hdr->n_tiles, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
-  const uint32_t n_tiles = p.mode == 2 ? 0u : s_bcast[2];
-  const uint32_t n_tasks = (uint32_t)p.n_copy + n_tiles;
-  const int nk = p.K / BK;
+  const int n_tiles = p.mode == 2 ? 0 : (int)s_bcast[2];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
   const size_t wstride = (size_t)p.K * p.N;
 
   for (;;) {
-    const uint32_t ticket = next_ticket(cm.hdr, s_bcast);
-    if (ticket >= n_tasks) break;
-    if ((int)ticket < p.n_copy) {
-      run_copy_task(p, args.chunks, args.a_gathered, args.slab_cnt, args.slab_flag, (int)ticket, epoch, cm,
-                    ticket, s_bcast);
-      continue;
-    }
+    const uint32_t u = next_ticket(&cm.hdr->ticket, s_bcast);
+    if ((int)u >= p.n_copy) break;
+    run_copy_task(p, args.chunks, args.a_gathered, args.slab_cnt, args.slab_flag, (int)u, epoch, cm);
+  }
+  int q = (int)s_bcast[3] % kXcds, tried = 0;
+  uint32_t qt = 0;
+  TileCtx<BM, BN> t;
+  t.N = p.N;
+  t.nk = p.K / BKS;
+  for (;;) {
+    const int v = next_tile(cm.hdr, n_tiles, &q, &tried, s_bcast, &qt);
+    if (v < 0) break;
     const uint64_t t0 = now_ticks();
-    const int32_t* L = args.lut + (size_t)(ticket - p.n_copy) * 8;
+    const int32_t* L = args.lut + (size_t)v * 8;
     const int e = L[0], r0 = L[1], nrows = L[2], cb = L[3], s_lo = L[4], s_hi = L[5];
     uint32_t seen = 0;
     int nwait = 0;
@@ -710,30 +558,29 @@ __global__ __launch_bounds__(kThreads, 1) void moe_gemm_kernel(MoeArgs args) {
     }
     const uint64_t t1 = now_ticks();
     __syncthreads();
-    ARows<BM, BN> ar;
 #pragma unroll
-    for (int q = 0; q < TS::A_LOADS; ++q) {
-      int i = threadIdx.x + kThreads * q;
-      int rr = min(i >> 3, nrows - 1);
-      int tok = args.perm[r0 + rr] / args.topk;
-      int c = tok / p.m;
-      int kc = (i & 7) * 8;
-      ar.rows[q] = (c == p.local) ? args.chunks[c] + (size_t)(tok - c * p.m) * p.K + kc
-                                  : args.a_gathered + (size_t)tok * p.K + kc;
+    for (int i = 0; i < G::A_PER_WAVE; ++i) {
+      const int rr = min(dma_row<BM, BN>(wave, i, lane), nrows - 1);
+      const int tok = args.perm[r0 + rr] / args.topk;
+      const int c = tok / p.m;
+      t.rowp[i] = (const char*)((c == p.local) ? args.chunks[c] + (size_t)(tok - c * p.m) * p.K
+                                               : args.a_gathered + (size_t)tok * p.K);
     }
-    const __amdgpu_buffer_rsrc_t brs = make_rsrc(args.w + (size_t)e * wstride, (uint32_t)(wstride * 2));
-    f32x4_t acc[TS::FM][TS::FN];
+    t.brs = make_rsrc(args.w + (size_t)e * wstride, (uint32_t)(wstride * 2));
     const int n0 = cb * BN;
-    mainloop<BM, BN>(smem, ar, brs, p.N, n0, nk, acc);
+    t.n0 = n0;
+    f32x16_t acc[G::FM][G::FN];
+    mainloop<BM, BN>(smem, t, acc);
     stage_c<BM, BN>(smem, acc);
     // local scatter: row rr of the tile is token-slot perm[r0 + rr]
-    for_each_c_chunk<BM, BN>(smem, [&](int rr, int col, u32x4_t v) {
+    for_each_c_chunk<BM, BN>(smem, [&](int rr, int col, u32x4_t val) {
       if (rr < nrows && n0 + col < p.N) {
         const int slot = args.perm[r0 + rr];
-        gstore16(args.out + (size_t)slot * p.N + n0 + col, v);
+        gstore16(args.out + (size_t)slot * p.N + n0 + col, val);
       }
     });
-    trace_tile(cm, ticket, 4, e, r0, nrows, cb | ((uint32_t)nwait << 16), epoch, t0, t1, seen);
+    trace_task(cm, (uint32_t)(p.n_copy + v), 4, e, r0, nrows, cb | ((uint32_t)nwait << 16), epoch, t0, t1, seen,
+               ((uint32_t)q << 16) | qt);
   }
   finish(cm.hdr, epoch);
 }
@@ -768,7 +615,7 @@ hipError_t launch_ag_gemm(const AgArgs& a, int tile, int grid, hipStream_t s) {
   switch (tile) {
     case OCG_TILE_256x224: return ag_launch<256, 224>(a, grid, s);
     case OCG_TILE_128x224: return ag_launch<128, 224>(a, grid, s);
-    case OCG_TILE_256x256: return ag_launch<256, 256>(a, grid, s);
+    case OCG_TILE_128x256: return ag_launch<128, 256>(a, grid, s);
     case OCG_TILE_128x128: return ag_launch<128, 128>(a, grid, s);
   }
   return hipErrorInvalidValue;
@@ -778,7 +625,7 @@ hipError_t launch_gemm_rs(const RsArgs& a, int tile, int grid, hipStream_t s) {
   switch (tile) {
     case OCG_TILE_256x224: return rs_launch<256, 224>(a, grid, s);
     case OCG_TILE_128x224: return rs_launch<128, 224>(a, grid, s);
-    case OCG_TILE_256x256: return rs_launch<256, 256>(a, grid, s);
+    case OCG_TILE_128x256: return rs_launch<128, 256>(a, grid, s);
     case OCG_TILE_128x128: return rs_launch<128, 128>(a, grid, s);
   }
   return hipErrorInvalidValue;
@@ -813,14 +660,14 @@ int resident_per_cu(int op, int tile) {
     switch (tile) {
       case OCG_TILE_256x224: return occ(ag_gemm_kernel<256, 224>);
       case OCG_TILE_128x224: return occ(ag_gemm_kernel<128, 224>);
-      case OCG_TILE_256x256: return occ(ag_gemm_kernel<256, 256>);
+      case OCG_TILE_128x256: return occ(ag_gemm_kernel<128, 256>);
       case OCG_TILE_128x128: return occ(ag_gemm_kernel<128, 128>);
     }
   } else {
     switch (tile) {
       case OCG_TILE_256x224: return occ(gemm_rs_kernel<256, 224>);
       case OCG_TILE_128x224: return occ(gemm_rs_kernel<128, 224>);
-      case OCG_TILE_256x256: return occ(gemm_rs_kernel<256, 256>);
+      case OCG_TILE_128x256: return occ(gemm_rs_kernel<128, 256>);
       case OCG_TILE_128x128: return occ(gemm_rs_kernel<128, 128>);
     }
   }

@@ -26,7 +26,8 @@ struct WsHeader {
   uint32_t epoch;      // epoch of the last completed call (flags carry epochs)
   uint32_t error;      // bit 0: a flag wait timed out
   uint32_t n_tiles;    // MoE: grouped tiles of the current routing
-  uint32_t pad[59];
+  uint32_t xtick[8];   // next ticket of each XCD's tile queue
+  uint32_t pad[51];
 };
 static_assert(sizeof(WsHeader) == 256, "header is 256 bytes");
 

@@ -9,12 +9,17 @@
 //
 // AG-GEMM plan. Gathered rows M = R*m; rank chunk c owns rows [c*m, (c+1)*m).
 // A chunk is cut into slabs of S rows (one published flag each) and into copy
-// tasks of CT rows (S % CT == 0). Tickets [0, n_copy) are copy tasks in the
+// tasks of CT rows (S % CT == 0). Copy tasks are numbered 0..n_copy-1 in the
 // chunk sequence local+1, local+2, ..., local+R-1, local (swizzled) or
-// 0..R-1 (natural); tickets [n_copy, n_copy + n_tiles) are GEMM tiles, row
-// blocks rotated to start at the block holding the local chunk's first row.
-// Every tile's flag dependencies are copy tasks with smaller tickets and copy
-// tasks never wait, so dynamic ticketing cannot deadlock.
+// 0..R-1 (natural) and handed out by one global ticket counter. GEMM tiles are
+// numbered 0..n_tiles-1 in grouped order: row blocks rotated to start at the
+// block holding the local chunk's first row, taken in groups of kGroup, each
+// group walked column block by column block. Tiles are cut into batches of
+// kBatch consecutive tiles dealt round-robin to kXcds queues; a workgroup
+// drains the queue of the XCD it runs on, then the others. Concurrent tiles of
+// one XCD thereby share A and B panels in that XCD's L2. A workgroup takes
+// tiles only once every copy ticket has been claimed, tiles wait only on copy
+// tasks, and copy tasks never wait: the schedule cannot deadlock.
 #pragma once
 
 #include <stdint.h>
@@ -85,12 +90,34 @@ OCG_HD int slab_target(int m, int S, int CT, int bpr, int slab) {
   return left < per ? left : per;
 }
 
-// Tile v (0-based among tiles) -> (rb, cb).
+constexpr int kGroup = 4;    // row blocks per group of the tile order
+constexpr int kBatch = 32;   // consecutive tiles per XCD batch (one per CU of an XCD)
+constexpr int kXcds = 8;     // XCDs of an MI355X (hardware queue id range of XCC_ID)
+
+// Tile v (0-based, grouped order) -> (rb, cb).
 OCG_HD void tile_of(int n_rb, int n_cb, int rb0, int v, int* rb, int* cb) {
-  int q = v / n_cb;
-  *cb = v - q * n_cb;
-  int r = rb0 + q;
+  const int per_group = kGroup * n_cb;
+  const int grp = v / per_group;
+  const int rho0 = grp * kGroup;
+  const int gsz = n_rb - rho0 < kGroup ? n_rb - rho0 : kGroup;
+  const int w = v - grp * per_group;
+  *cb = w / gsz;
+  const int r = rb0 + rho0 + (w - *cb * gsz);
   *rb = r >= n_rb ? r - n_rb : r;
+}
+
+// Ticket t of XCD queue q -> tile index, or -1 once the queue is exhausted.
+OCG_HD int xcd_tile(int q, int t, int n_tiles) {
+  const int beta = (t / kBatch) * kXcds + q;
+  const int v = beta * kBatch + (t % kBatch);
+  return v < n_tiles ? v : -1;
+}
+
+// Tile index -> (queue, ticket).
+OCG_HD void tile_queue(int v, int* q, int* t) {
+  const int beta = v / kBatch;
+  *q = beta % kXcds;
+  *t = (beta / kXcds) * kBatch + v % kBatch;
 }
 
 // Slabs (excluding the local chunk) overlapping gathered rows [r0, r1):
@@ -113,9 +140,11 @@ OCG_HD int for_each_dep_slab(int m, int S, int bpr, int local, int r0, int r1, F
   return n;
 }
 
-// GEMM-RS plan: tickets [0, n_tiles) are GEMM tiles of the full partial
-// (local row block first when swizzled); tickets [n_tiles, n_tiles + n_red)
-// are reduce strips of RR rows of the local block [local*blk, (local+1)*blk).
+// GEMM-RS plan: tiles 0..n_tiles-1 of the full partial in the grouped order
+// above (local row block first when swizzled), handed out by the XCD queues;
+// then reduce strips 0..n_red-1 of RR rows of the local block
+// [local*blk, (local+1)*blk), handed out by the global counter once every tile
+// has been claimed.
 struct RsPlan {
   int R, local, M, K, N, BM, BN, blk, RR;
   int n_rb, n_cb, n_tiles, n_red, rb0;
@@ -147,8 +176,8 @@ OCG_HD bool rs_tile_touches_local(const RsPlan& p, int rb) {
   return lo < (p.local + 1) * p.blk && hi > p.local * p.blk;
 }
 
-// Tile presets: {BM, BN}.
-OCG_HD int tile_bm(int t) { return (t == 1 || t == 3) ? 128 : 256; }
+// Tile presets: {BM, BN} = {256,224}, {128,224}, {128,256}, {128,128}.
+OCG_HD int tile_bm(int t) { return t == 0 ? 256 : 128; }
 OCG_HD int tile_bn(int t) { return t == 2 ? 256 : (t == 3 ? 128 : 224); }
 
 }  // namespace ocg

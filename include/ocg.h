@@ -65,14 +65,16 @@ extern "C" {
 #define OCG_TILE_AUTO (-1)
 #define OCG_TILE_256x224 0
 #define OCG_TILE_128x224 1
-#define OCG_TILE_256x256 2
+#define OCG_TILE_128x256 2
 #define OCG_TILE_128x128 3
 #define OCG_TILE_COUNT 4
 
 /* Trace record written per executed task when ocg_config.trace is set
- * (indexed by ticket; 64 bytes). kind: 1 copy task, 2 AG-GEMM tile,
- * 3 GEMM-RS tile, 4 MoE tile, 5 GEMM-RS reduce strip. Times are the GPU's
- * constant 100 MHz clock. */
+ * (64 bytes), at slot: AG-GEMM / MoE copy task u -> u, tile v -> n_copy + v;
+ * GEMM-RS tile v -> v, reduce strip j -> n_tiles + j (v = tile index in the
+ * grouped tile order). kind: 1 copy task, 2 AG-GEMM tile, 3 GEMM-RS tile,
+ * 4 MoE tile, 5 GEMM-RS reduce strip. Times are the GPU's constant 100 MHz
+ * clock. */
 typedef struct ocg_trace_rec {
   uint32_t ticket, kind;
   uint32_t a, b, c, d;   /* copy: chunk, piece, slab, published(0/1)
@@ -84,7 +86,8 @@ typedef struct ocg_trace_rec {
   uint32_t epoch;        /* epoch of the call */
   uint64_t t_start, t_ready, t_end; /* ready = dependencies satisfied (tiles)
                                        or flag published (copy) */
-  uint32_t flag_seen, pad;
+  uint32_t flag_seen;
+  uint32_t queue;        /* tiles: (XCD queue << 16) | ticket within that queue */
 } ocg_trace_rec;
 
 typedef struct ocg_config {
@@ -203,11 +206,15 @@ const char* ocg_status_string(int status);
 int ocg_plan_info(int op, int R, int local_rank, int64_t m, int64_t K, int64_t N,
                   const ocg_config* cfg, int64_t out[8]);
 
-/* Task of ticket `ticket` in the AG-GEMM / GEMM-RS plan:
- * desc[0]=kind (1 copy, 2 AG tile, 3 RS tile, 0 none),
+/* Task at trace slot `ticket` of the AG-GEMM / GEMM-RS plan (slots as for
+ * ocg_trace_rec: AG copies, then AG tiles; RS tiles, then RS strips):
+ * desc[0]=kind (1 copy, 2 AG tile, 3 RS tile, 5 RS strip, 0 none),
  * copy: desc[1]=chunk, [2]=piece, [3]=row0, [4]=row1, [5]=slab;
- * tile: desc[1]=rb, [2]=cb, [3]=#dependency slabs (AG) or local-block (RS),
- *       [4..7]=first four dependency slab ids (-1 if none). */
+ * AG tile: desc[1]=rb, [2]=cb, [3]=#dependency slabs, [4..7]=first four
+ *          dependency slab ids (-1 if none);
+ * RS tile: desc[1]=rb, [2]=cb, [3]=local-block (0/1), [4]=XCD queue,
+ *          [5]=ticket within the queue;
+ * RS strip: desc[1]=row0, [2]=row1. */
 int ocg_plan_task(int op, int R, int local_rank, int64_t m, int64_t K, int64_t N,
                   const ocg_config* cfg, int64_t ticket, int64_t desc[8]);
 

@@ -25,17 +25,24 @@ rows S, copy-task rows CT with S % CT == 0):
   natural -> (0, 1, ..., R-1).
   copy ticket u < R*ceil(m/CT): chunk = seq[u // ceil(m/CT)], piece t = u % ..,
   rows [c*m + t*CT, c*m + min((t+1)*CT, m)), slab (c, (t*CT)//S).
-  tile tickets follow the copies: v = ticket - n_copy; row block
-  rb = (rb0 + v // n_cb) % n_rb with rb0 = (l*m)//BM when swizzled, else 0;
-  column block cb = v % n_cb. A tile waits for every slab overlapping its rows
+  tiles follow the copies: tile v sits at slot n_copy + v. Tile order: the
+  row blocks in rotated order rb0, rb0+1, ... (mod n_rb), rb0 = (l*m)//BM
+  when swizzled, else 0, are cut into groups of GROUP consecutive blocks;
+  the groups are taken in turn and each group is walked column block by
+  column block, all of the group's row blocks for one column block before
+  the next column block. A tile waits for every slab overlapping its rows
   that belongs to a chunk other than the local one (local rows are read from
   the local shard directly).
-GEMM-RS: tickets [0, n_tiles) are GEMM tiles, same rotation with
-  rb0 = (l*M/R)//BM when swizzled; each stores its bf16 partial and publishes
-  its tile flag. Tickets [n_tiles, n_tiles + ceil(blk/RR)) are reduce tasks
-  over RR-row strips of the local block [l*blk, (l+1)*blk), blk = M/R, in
-  ascending row order; a strip waits for the flags of every tile of the row
-  blocks it overlaps (and for the peers' flags of those tiles).
+  Tiles are dealt to XCDS queues in batches of BATCH consecutive tiles, batch
+  b to queue b % XCDS; a queue's tickets 0, 1, ... name its tiles in order.
+  (The queue a tile sits in sets only which L2 serves it, not its result.)
+GEMM-RS: slots [0, n_tiles) are GEMM tiles in the same order and queues,
+  with rb0 = (l*M/R)//BM when swizzled; each stores its bf16 partial and
+  publishes its tile flag. Slots [n_tiles, n_tiles + ceil(blk/RR)) are
+  reduce tasks over RR-row strips of the local block [l*blk, (l+1)*blk),
+  blk = M/R, in ascending row order; a strip waits for the flags of every
+  tile of the row blocks it overlaps (and for the peers' flags of those
+  tiles).
 MoE: the AG-GEMM copy list, then one tile per (expert e, column block cb,
   row tile rt) in that nesting order; expert e's rows
   [off_e + rt*BM, min(off_e + (rt+1)*BM, off_{e+1})) of the expert-sorted slot
@@ -48,8 +55,41 @@ from dataclasses import dataclass
 from typing import List, Tuple
 
 
+GROUP = 4     # row blocks per group of the tile order
+BATCH = 32    # consecutive tiles per queue batch
+XCDS = 8      # tile queues, one per XCD
+
+
 def _cdiv(a: int, b: int) -> int:
     return -(-a // b)
+
+
+def tile_order(n_rb: int, n_cb: int, rb0: int) -> List[Tuple[int, int]]:
+    """(rb, cb) of tiles 0, 1, ... in the grouped, rotated order."""
+    rows = [(rb0 + i) % n_rb for i in range(n_rb)]
+    out = []
+    for g in range(0, n_rb, GROUP):
+        for cb in range(n_cb):
+            for rb in rows[g:g + GROUP]:
+                out.append((rb, cb))
+    return out
+
+
+def tile_queues(n_tiles: int) -> List[List[int]]:
+    """queues[q][t] = tile taken by ticket t of XCD queue q."""
+    queues: List[List[int]] = [[] for _ in range(XCDS)]
+    for b, start in enumerate(range(0, n_tiles, BATCH)):
+        queues[b % XCDS].extend(range(start, min(start + BATCH, n_tiles)))
+    return queues
+
+
+def queue_of(n_tiles: int):
+    """tile index -> (queue, ticket within the queue)."""
+    where = {}
+    for q, lst in enumerate(tile_queues(n_tiles)):
+        for t, v in enumerate(lst):
+            where[v] = (q, t)
+    return where
 
 
 @dataclass(frozen=True)
@@ -64,10 +104,12 @@ class CopyTask:
 
 @dataclass(frozen=True)
 class Tile:
-    ticket: int
+    ticket: int             # trace slot
     rb: int
     cb: int
     deps: Tuple[int, ...]   # global slab ids waited on
+    queue: int = 0          # XCD queue holding the tile
+    qticket: int = 0        # ticket of the tile within that queue
 
 
 def copy_sequence(R: int, local: int, swizzle: bool) -> List[int]:
@@ -117,35 +159,33 @@ def ag_gemm_plan(R, m, K, N, local, BM, BN, S, CT, swizzle=True, mode="fused"):
     if mode in ("fused", "gemm_only"):
         rb0 = (local * m) // BM if swizzle else 0
         base = len(tasks)
-        for v in range(n_rb * n_cb):
-            rb = (rb0 + v // n_cb) % n_rb
-            cb = v % n_cb
+        where = queue_of(n_rb * n_cb)
+        for v, (rb, cb) in enumerate(tile_order(n_rb, n_cb, rb0)):
             deps = set()
             if mode == "fused":
                 for row in range(rb * BM, min((rb + 1) * BM, M)):
                     c = row // m
                     if c != local:
                         deps.add(c * bpr + (row % m) // S)
-            tasks.append(Tile(base + v, rb, cb, tuple(sorted(deps))))
+            tasks.append(Tile(base + v, rb, cb, tuple(sorted(deps)), *where[v]))
     return tasks
 
 
 def gemm_rs_plan(R, M, N, local, BM, BN, RR, swizzle=True):
     """Ticket list of the GEMM-RS kernel.
 
-    Tiles: ("tile", ticket, rb, cb, touches_local_block).
-    Reduce strips: ("reduce", ticket, row0, row1, deps) with gathered-row range
+    Tiles: ("tile", slot, rb, cb, touches_local_block, queue, queue_ticket).
+    Reduce strips: ("reduce", slot, row0, row1, deps) with gathered-row range
     [row0, row1) inside the local block and deps the (rb, cb) tiles waited on."""
     n_rb, n_cb = _cdiv(M, BM), _cdiv(N, BN)
     blk = M // R
     rb0 = (local * blk) // BM if swizzle else 0
     out = []
-    for v in range(n_rb * n_cb):
-        rb = (rb0 + v // n_cb) % n_rb
-        cb = v % n_cb
+    where = queue_of(n_rb * n_cb)
+    for v, (rb, cb) in enumerate(tile_order(n_rb, n_cb, rb0)):
         lo, hi = rb * BM, min((rb + 1) * BM, M)
         has_local = lo < (local + 1) * blk and hi > local * blk
-        out.append(("tile", v, rb, cb, has_local))
+        out.append(("tile", v, rb, cb, has_local, *where[v]))
     t = n_rb * n_cb
     r = local * blk
     while r < (local + 1) * blk:

@@ -57,7 +57,7 @@ def assert_gate(got_bits: np.ndarray, want: np.ndarray, what: str, tight: bool =
 
 TRACE_DTYPE = np.dtype([("ticket", "<u4"), ("kind", "<u4"), ("a", "<u4"), ("b", "<u4"), ("c", "<u4"),
                         ("d", "<u4"), ("hw", "<u4"), ("epoch", "<u4"), ("t_start", "<u8"), ("t_ready", "<u8"),
-                        ("t_end", "<u8"), ("flag_seen", "<u4"), ("pad", "<u4")])
+                        ("t_end", "<u8"), ("flag_seen", "<u4"), ("queue", "<u4")])
 assert TRACE_DTYPE.itemsize == 64
 
 

@@ -75,8 +75,9 @@ def test_plan_info_tile_choice():
     # 8B share: 128x224 (256 tiles, one round)
     p = ocg.plan_info(ocg.OP_AG_GEMM, 8, 0, 512, 4096, 1792)
     assert (p["BM"], p["BN"], p["n_tiles"]) == (128, 224, 256)
+    # GEMM-RS 4096 x 4096: 128x256 (512 tiles, two full rounds)
     p = ocg.plan_info(ocg.OP_GEMM_RS, 8, 0, 4096, 1792, 4096)
-    assert (p["BM"], p["BN"], p["n_tiles"]) == (256, 256, 256)
+    assert (p["BM"], p["BN"], p["n_tiles"]) == (128, 256, 512)
 
 
 AG_CASES = [
@@ -125,7 +126,7 @@ def test_rs_plan_matches_oracle_schedule(R, M, K, N, local, tile):
     for t in want:
         d = ocg.plan_task(ocg.OP_GEMM_RS, R, local, M, K, N, t[1], cfg)
         if t[0] == "tile":
-            assert d[:4] == [3, t[2], t[3], int(t[4])]
+            assert d[:6] == [3, t[2], t[3], int(t[4]), t[5], t[6]]
         else:
             assert d[:3] == [5, t[2], t[3]]
     assert ocg.plan_task(ocg.OP_GEMM_RS, R, local, M, K, N, len(want), cfg)[0] == 0

@@ -31,7 +31,7 @@ SMALL = [
     ("ragged_128x128", 3, 100, 64, 72, 1, 3, "uniform"),
     ("ragged_r5", 5, 37, 128, 40, 4, 3, "uniform"),
     ("ragged_256x224", 3, 300, 192, 520, 2, 0, "normal"),
-    ("r2_256x256", 2, 256, 512, 264, 1, 2, "uniform"),
+    ("r2_128x256", 2, 256, 512, 264, 1, 2, "uniform"),
     ("r1_128x224", 1, 200, 128, 232, 0, 1, "uniform"),
     ("r8_128x224", 8, 96, 320, 448, 6, 1, "normal"),
 ]
@@ -69,6 +69,7 @@ def _check_trace(ocg, x, local, cfg, recs):
     for t, r in zip(plan, recs):
         if isinstance(t, sch.Tile):
             assert (r["kind"], r["a"], r["b"], r["c"]) == (2, t.rb, t.cb, len(t.deps))
+            assert int(r["queue"]) == (t.queue << 16) | t.qticket, "tile taken from its XCD queue"
             if t.deps:
                 assert r["flag_seen"] == epoch, "the tile saw its flag at this call's epoch"
                 # consumed only after every slab it reads was published

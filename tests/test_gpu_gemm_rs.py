@@ -39,7 +39,7 @@ SMALL = [
     ("r3_256x224", 3, 600, 128, 264, 1, 0),
     ("r8_l0", 8, 1024, 256, 512, 0, -1),
     ("r8_l5", 8, 1024, 256, 512, 5, -1),
-    ("r2_256x256", 2, 512, 192, 264, 1, 2),
+    ("r2_128x256", 2, 512, 192, 264, 1, 2),
 ]
 
 
@@ -74,6 +74,7 @@ def test_gemm_rs_trace_notify_before_reduce(ocg):
     for t, r in zip(plan, recs):
         if t[0] == "tile":
             assert (r["kind"], r["a"], r["b"], r["c"]) == (3, t[2], t[3], int(t[4]))
+            assert int(r["queue"]) == (t[5] << 16) | t[6], "tile taken from its XCD queue"
             done[(t[2], t[3])] = int(r["t_end"])
     for t, r in zip(plan, recs):
         if t[0] == "reduce":

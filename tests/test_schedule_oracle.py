@@ -79,15 +79,15 @@ def test_gemm_rs_plan_invariants(R, M, N, local, BM, BN, RR):
     tiles = [t for t in plan if t[0] == "tile"]
     reds = [t for t in plan if t[0] == "reduce"]
     n_rb, n_cb = -(-M // BM), -(-N // BN)
-    assert sorted((rb, cb) for _, _, rb, cb, _ in tiles) == sorted(itertools.product(range(n_rb), range(n_cb)))
+    assert sorted((t[2], t[3]) for t in tiles) == sorted(itertools.product(range(n_rb), range(n_cb)))
     blk = M // R
     assert tiles[0][4]                                 # local row block first
     assert tiles[0][2] * BM <= local * blk < (tiles[0][2] + 1) * BM
-    for _, _, rb, cb, loc in tiles:
+    for _, _, rb, cb, loc, _, _ in tiles:
         assert loc == (rb * BM < (local + 1) * blk and min((rb + 1) * BM, M) > local * blk)
     # reduce strips cover the local block exactly once, after the tiles they read
     rows = np.zeros(M, dtype=np.int64)
-    tick = {(rb, cb): t for _, t, rb, cb, _ in tiles}
+    tick = {(rb, cb): t for _, t, rb, cb, _, _, _ in tiles}
     for _, t, r0, r1, deps in reds:
         rows[r0:r1] += 1
         need = {(rb, cb) for rb in range(n_rb) for cb in range(n_cb) if rb * BM < r1 and (rb + 1) * BM > r0}
@@ -112,3 +112,38 @@ def test_moe_tiles_cover_every_slot_once():
         need = {(t // m) * bpr + (t % m) // S for t in toks if t // m != local}
         assert need <= set(deps)
     assert np.all(cover == 1)
+
+
+@pytest.mark.parametrize("n_rb,n_cb,rb0", [(32, 16, 0), (32, 16, 4), (10, 3, 7), (1, 1, 0), (5, 9, 2), (7, 1, 6)])
+def test_tile_order_groups(n_rb, n_cb, rb0):
+    """Every tile once; the first GROUP tiles of a group share one column
+    block and span GROUP consecutive (rotated) row blocks; the first tile is
+    row block rb0."""
+    order = sch.tile_order(n_rb, n_cb, rb0)
+    assert sorted(order) == sorted(itertools.product(range(n_rb), range(n_cb)))
+    assert order[0] == (rb0, 0)
+    rot = [(rb - rb0) % n_rb for rb, _ in order]
+    per = sch.GROUP * n_cb
+    for v, (rb, cb) in enumerate(order):
+        g = v // per
+        assert g * sch.GROUP <= rot[v] < min((g + 1) * sch.GROUP, n_rb)
+        if v % per:
+            prev_cb = order[v - 1][1]
+            assert cb == prev_cb or cb == prev_cb + 1
+
+
+@pytest.mark.parametrize("n_tiles", [0, 1, 31, 32, 33, 255, 256, 257, 512, 1000, 1792])
+def test_tile_queues_partition(n_tiles):
+    """The queues partition the tiles; each queue holds whole batches of
+    consecutive tiles in ascending order; batches go round-robin."""
+    qs = sch.tile_queues(n_tiles)
+    assert len(qs) == sch.XCDS
+    assert sorted(v for q in qs for v in q) == list(range(n_tiles))
+    for q, lst in enumerate(qs):
+        assert lst == sorted(lst)
+        for v in lst:
+            assert (v // sch.BATCH) % sch.XCDS == q
+    where = sch.queue_of(n_tiles)
+    for v in range(n_tiles):
+        q, t = where[v]
+        assert qs[q][t] == v
