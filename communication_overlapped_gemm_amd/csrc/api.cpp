@@ -107,6 +107,7 @@ int resolve(int op, int R, int64_t m, int64_t K, int64_t N, const ocg_config& c,
     while (r->S % r->CT) r->CT /= 2;
   }
   if (r->CT < 1 || r->S % r->CT) return OCG_ERR_INVALID_ARG;
+  if ((int64_t)r->CT * K * 2 >= ((int64_t)1 << 31)) return OCG_ERR_INVALID_ARG;  // one copy task < 2 GiB
   return OCG_OK;
 }
 

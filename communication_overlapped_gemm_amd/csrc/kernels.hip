@@ -13,13 +13,17 @@
 // "transfer complete" barrier is the slab flag; lookup tables for the
 // dynamic (MoE) dependencies.
 //
-// Memory-model contract (agent scope, all 8 XCDs):
-//   producer: stores; every thread release-fences (waits for its stores and
-//   writes back the XCD's L2); workgroup barrier; one thread bumps the slab
-//   counter (acq_rel) and the last finisher stores the flag (release).
-//   consumer: one thread polls the flag with relaxed loads, then issues one
-//   acquire fence (invalidates stale cache lines) before the barrier that
-//   releases the workgroup into the main loop. Polls are bounded in time.
+// Memory-model contract (agent scope, all 8 XCDs). Data that another
+// workgroup consumes inside the same launch (gathered rows, GEMM-RS partial
+// tiles) is written with agent-coherent stores (cache policy SC1, the
+// encoding of a relaxed agent-scope atomic store on this chip family), which
+// complete at the agent's point of coherence instead of staying dirty in one
+// XCD's L2. A producer therefore publishes by waiting for its own stores to
+// complete (vmcnt 0), a workgroup barrier, then one relaxed agent-scope atomic
+// on the counter / flag -- no L2 writeback, which measured ~20 us per publish
+// on a busy XCD. A consumer's thread 0 polls the flag with relaxed loads,
+// bounded in time, then issues one acquire fence (drops stale cache lines)
+// before the barrier that releases the workgroup into its loads.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -65,19 +69,31 @@ __device__ bool wait_flag(const uint32_t* flag, uint32_t want, const Common& cm,
   return ok;
 }
 
+// Wait until every store this thread issued has completed (for the
+// agent-coherent stores below: is visible at agent scope).
+__device__ __forceinline__ void drain_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Cache-policy immediate of buffer stores: SC1 = agent-scope coherent.
+constexpr int kAgentCoherent = 16;
+
+__device__ __forceinline__ void store16_agent(__amdgpu_buffer_rsrc_t rs, uint32_t byte_off, u32x4_t v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, rs, (int)byte_off, 0, kAgentCoherent);
+}
+
 // produce_tile_notify for copy tasks: called by every thread after its
-// stores; returns (to thread 0) whether this task published the slab flag.
+// agent-coherent stores; returns (to thread 0) whether this task published
+// the slab flag (the last of the slab's copy tasks does).
 __device__ bool publish_slab(uint32_t* cnt, uint32_t* flag, int slab, int target, uint32_t epoch,
                              const Common& cm) {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  drain_stores();
   __syncthreads();
   bool published = false;
   if (threadIdx.x == 0) {
-    uint32_t old = __hip_atomic_fetch_add(&cnt[slab], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    uint32_t old = __hip_atomic_fetch_add(&cnt[slab], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if ((int)old + 1 == target) {
       __hip_atomic_store(&cnt[slab], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       if (slab != cm.fault_skip_slab)
-        __hip_atomic_store(&flag[slab], epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&flag[slab], epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       published = true;
     }
   }
@@ -86,21 +102,21 @@ __device__ bool publish_slab(uint32_t* cnt, uint32_t* flag, int slab, int target
 
 // ---------------------------------------------------------------- copy
 
-// Pull `n16` 16-byte granules from src to dst with all 256 threads, 16
-// granules in flight per thread.
-__device__ __forceinline__ void copy_granules(const uint16_t* src, uint16_t* dst, size_t n16) {
+// Pull `n16` 16-byte granules from src to dst (agent-coherent stores) with
+// all 256 threads, 16 granules in flight per thread. n16 * 16 < 2^31.
+__device__ __forceinline__ void copy_granules(const uint16_t* src, uint16_t* dst, uint32_t n16) {
   constexpr int U = 16;
   const u32x4_t* s = (const u32x4_t*)src;
-  u32x4_t* d = (u32x4_t*)dst;
-  size_t i = threadIdx.x;
-  for (; i + (size_t)(U - 1) * kThreads < n16; i += (size_t)U * kThreads) {
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(dst, n16 * 16u);
+  uint32_t i = threadIdx.x;
+  for (; i + (uint32_t)(U - 1) * kThreads < n16; i += (uint32_t)U * kThreads) {
     u32x4_t v[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) v[u] = gload16(s + i + (size_t)u * kThreads);
+    for (int u = 0; u < U; ++u) v[u] = gload16(s + i + u * kThreads);
 #pragma unroll
-    for (int u = 0; u < U; ++u) gstore16(d + i + (size_t)u * kThreads, v[u]);
+    for (int u = 0; u < U; ++u) store16_agent(rs, (i + u * kThreads) * 16u, v[u]);
   }
-  for (; i < n16; i += kThreads) gstore16(d + i, gload16(s + i));
+  for (; i < n16; i += kThreads) store16_agent(rs, i * 16u, gload16(s + i));
 }
 
 // One copy task of the AllGather (pull mode): rows [row0, row1) of the
@@ -112,7 +128,7 @@ __device__ void run_copy_task(const AgPlan& p, const uint16_t* const* chunks, ui
   CopyDesc d = copy_desc(p, u);
   const uint16_t* src = chunks[d.chunk] + (size_t)(d.row0 - d.chunk * p.m) * p.K;
   uint16_t* dst = a_gathered + (size_t)d.row0 * p.K;
-  copy_granules(src, dst, (size_t)(d.row1 - d.row0) * p.K / 8);
+  copy_granules(src, dst, (uint32_t)((size_t)(d.row1 - d.row0) * p.K / 8));
   int target = slab_target(p.m, p.S, p.CT, p.bpr, d.slab);
   bool pub = publish_slab(slab_cnt, slab_flag, d.slab, target, epoch, cm);
   if (threadIdx.x == 0 && cm.trace && (uint32_t)u < cm.trace_cap) {
@@ -162,17 +178,20 @@ __device__ __forceinline__ int next_tile(WsHeader* hdr, int n_tiles, int* q, int
   return -1;
 }
 
-// Last workgroup out resets the counters and records the epoch.
+// Last workgroup out resets the counters and records the epoch. Relaxed
+// atomics suffice: a workgroup arrives here only after its last ticket
+// fetch returned (its value decided the exit), and the next launch on the
+// stream is ordered after this one by the kernel boundary.
 __device__ __forceinline__ void finish(WsHeader* hdr, uint32_t epoch) {
   __syncthreads();
   if (threadIdx.x == 0) {
-    uint32_t d = __hip_atomic_fetch_add(&hdr->done, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    uint32_t d = __hip_atomic_fetch_add(&hdr->done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (d + 1 == gridDim.x) {
       __hip_atomic_store(&hdr->ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       for (int q = 0; q < kXcds; ++q)
         __hip_atomic_store(&hdr->xtick[q], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_store(&hdr->done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(&hdr->epoch, epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(&hdr->epoch, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 }
@@ -334,14 +353,18 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_rs_kernel(RsArgs args) {
     f32x16_t acc[G::FM][G::FN];
     mainloop<BM, BN>(smem, t, acc);
     stage_c<BM, BN>(smem, acc);
+    // The bf16 partial tile (the send buffer) is consumed by reduce strips of
+    // this launch: agent-coherent stores, rows r0.. of the partial.
+    const int rows = min(BM, p.M - r0);
+    const __amdgpu_buffer_rsrc_t prs = make_rsrc(args.partial + (size_t)r0 * p.N, (uint32_t)((size_t)rows * p.N * 2));
     for_each_c_chunk<BM, BN>(smem, [&](int row, int col, u32x4_t val) {
-      if (r0 + row < p.M && n0 + col < p.N) gstore16(args.partial + (size_t)(r0 + row) * p.N + n0 + col, val);
+      if (row < rows && n0 + col < p.N) store16_agent(prs, (uint32_t)(((size_t)row * p.N + n0 + col) * 2), val);
     });
-    // produce_tile_notify: the bf16 partial tile is in memory (the send buffer).
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    // produce_tile_notify
+    drain_stores();
     __syncthreads();
     if (threadIdx.x == 0)
-      __hip_atomic_store(&args.tile_flag[rb * p.n_cb + cb], epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(&args.tile_flag[rb * p.n_cb + cb], epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     trace_task(cm, (uint32_t)v, 3, rb, cb, rs_tile_touches_local(p, rb) ? 1u : 0u, 0, epoch, t0, t0, 0,
                ((uint32_t)q << 16) | qt);
   }

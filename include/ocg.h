@@ -93,7 +93,8 @@ typedef struct ocg_trace_rec {
 typedef struct ocg_config {
   int32_t tile;             /* OCG_TILE_* preset, or OCG_TILE_AUTO */
   int32_t slab_rows;        /* rows of a rank chunk per published flag; 0 = tile rows */
-  int32_t copy_rows;        /* rows per copy task (must divide slab_rows); 0 = auto */
+  int32_t copy_rows;        /* rows per copy task (must divide slab_rows;
+                               rows * K * 2 < 2 GiB); 0 = auto */
   int32_t swizzle;          /* 1 = tiles and copies start at the local rank and rotate
                                (default); 0 = natural rank order */
   int32_t mode;             /* OCG_MODE_* */
