@@ -12,11 +12,15 @@
 //     operand (8 consecutive k of one column per lane) is read with the gfx950
 //     transposing LDS read ds_read_b64_tr_b16.
 // Slots are filled by direct-to-LDS 16-byte loads (global_load_lds_dwordx4 for
-// A rows, buffer_load_dwordx4 ... lds for B with out-of-range rows reading as
+// A rows, buffer_load_dwordx4 ... lds for B with out-of-range reads returning
 // zero), S-1 stages ahead. They are issued from inline assembly so the
 // compiler does not add its own whole-queue waits before every LDS read; the
-// explicit vmcnt waits plus one barrier per stage order them. Fragments of
-// stage k+1 are read into registers while stage k's MFMAs run.
+// explicit vmcnt waits plus one barrier per stage order them. Every wave
+// issues the same number of loads per stage (a spare B load goes to a dummy
+// LDS block), so the waits are constants and the steady-state loop has no
+// branches. With one wave per SIMD an instruction only overlaps a 32-cycle
+// MFMA if it sits between MFMAs in program order, so the fragment reads of
+// stage k+1 and the loads of stage k+3 are interleaved with stage k's MFMAs.
 //
 // The MFMA's A operand carries B (rows = n) and its B operand carries A
 // (columns = m), so each lane ends with 4 consecutive output columns of one
@@ -50,11 +54,16 @@ struct Gemm {
   static constexpr int A_INST = A_BYTES / 1024;     // 1 KiB DMA instructions per stage
   static constexpr int B_INST = B_BYTES / 1024;
   static constexpr int A_PER_WAVE = A_INST / 4;
-  static constexpr int B_MAX = (B_INST + 3) / 4, B_MIN = B_INST / 4;  // B instructions j -> wave j % 4
+  static constexpr int B_PER_WAVE = (B_INST + 3) / 4;  // B instruction j = wave + 4*i
+  static constexpr bool SPARE = 4 * B_PER_WAVE > B_INST;
+  static constexpr int NDMA = A_PER_WAVE + B_PER_WAVE;  // loads per wave per stage
+  static constexpr int DUMMY = S * STAGE;            // 1 KiB sink of spare and past-the-end loads
+  static constexpr int RING = S * STAGE + 1024;
   static constexpr int LD_C = BN + 8;               // epilogue staging row (elements)
-  static constexpr int LDS_BYTES = (S * STAGE > BM * LD_C * 2) ? S * STAGE : BM * LD_C * 2;
+  static constexpr int LDS_BYTES = (RING > BM * LD_C * 2) ? RING : BM * LD_C * 2;
   static_assert(WM % 32 == 0 && BN % 32 == 0, "whole 32x32 blocks per wave");
   static_assert(A_INST % 4 == 0, "A DMA instructions split evenly over the waves");
+  static_assert(NDMA <= 2 * FN, "every load of a stage has an MFMA group to sit behind");
   static_assert(LDS_BYTES <= 160 * 1024 - 64, "fits the 160 KiB LDS of a gfx950 CU");
 };
 
@@ -99,42 +108,65 @@ __device__ __forceinline__ int dma_row(int wave, int i, int lane) {
   return (wave * Gemm<BM, BN>::A_PER_WAVE + i) * 16 + (lane >> 2);
 }
 
+// Per-tile constants of this wave's loads: the A instruction i loads rows
+// 16*(wave*A_PER_WAVE + i) + lane/4, chunk (lane & 3) ^ swz_a(row), into the
+// slot's 1 KiB block wave*A_PER_WAVE + i; B instruction i (j = wave + 4i)
+// loads k row (j & 1)*16 + lane/4 of column block j/2, chunk pair
+// (lane & 3) ^ 2*swz_b(k), into block j of the slot's B part (or the dummy).
 template <int BM, int BN>
-__device__ __forceinline__ void issue_stage(uint32_t slot, const TileCtx<BM, BN>& t, int s, int wave) {
+struct DmaPlan {
+  const char* a[Gemm<BM, BN>::A_PER_WAVE];     // per lane, stage 0
+  uint32_t b_off[Gemm<BM, BN>::B_PER_WAVE];    // per lane byte offset in B, stage 0
+  uint32_t b_step;                             // bytes of B per stage (32 rows)
+};
+
+template <int BM, int BN>
+__device__ __forceinline__ DmaPlan<BM, BN> make_dma_plan(const TileCtx<BM, BN>& t, int wave) {
   using G = Gemm<BM, BN>;
   const int lane = threadIdx.x & 63;
-  const int kbyte = s * BKS * 2;
+  DmaPlan<BM, BN> d;
 #pragma unroll
   for (int i = 0; i < G::A_PER_WAVE; ++i) {
-    const int blk = wave * G::A_PER_WAVE + i;
-    const int r = blk * 16 + (lane >> 2);
-    const int c = (lane & 3) ^ swz_a(r);
-    dma_global(slot + blk * 1024, t.rowp[i] + kbyte + c * 16);
+    const int r = (wave * G::A_PER_WAVE + i) * 16 + (lane >> 2);
+    d.a[i] = t.rowp[i] + ((lane & 3) ^ swz_a(r)) * 16;
   }
 #pragma unroll
-  for (int i = 0; i < G::B_MAX; ++i) {
+  for (int i = 0; i < G::B_PER_WAVE; ++i) {
+    int j = wave + 4 * i;
+    if (j >= G::B_INST) j -= 4;   // spare load: repeat a real one into the dummy block
+    const int nb = j >> 1, k = (j & 1) * 16 + (lane >> 2);
+    const int c = (lane & 3) ^ (2 * swz_b(k));
+    // byte offset of B[k][n0 + 32*nb + 8*c]; K*N*2 < 2^32 (unsigned math)
+    d.b_off[i] = ((uint32_t)k * (uint32_t)t.N + (uint32_t)(t.n0 + nb * 32 + c * 8)) * 2u;
+  }
+  d.b_step = (uint32_t)BKS * (uint32_t)t.N * 2u;
+  return d;
+}
+
+// Load number `I` (0 <= I < NDMA) of this wave for stage `s` into `slot`; with
+// `sink` set (a stage past the end, re-reading stage s) every load lands in
+// the dummy block instead.
+template <int BM, int BN, int I>
+__device__ __forceinline__ void dma_one(uint32_t slot, bool sink, uint32_t base, const DmaPlan<BM, BN>& d,
+                                        const __amdgpu_buffer_rsrc_t& brs, int s, int wave) {
+  using G = Gemm<BM, BN>;
+  if constexpr (I < G::A_PER_WAVE) {
+    const uint32_t dst = sink ? base + G::DUMMY : slot + (wave * G::A_PER_WAVE + I) * 1024;
+    dma_global(dst, d.a[I] + s * (BKS * 2));
+  } else {
+    constexpr int i = I - G::A_PER_WAVE;
     const int j = wave + 4 * i;
-    if (j < G::B_INST) {
-      const int nb = j >> 1, k = (j & 1) * 16 + (lane >> 2);
-      const int c = (lane & 3) ^ (2 * swz_b(k));
-      // byte offset of B[s*32 + k][n0 + 32*nb + 8*c]; K*N*2 < 2^32 (unsigned math)
-      dma_buffer(slot + G::A_BYTES + j * 1024, t.brs,
-                 ((uint32_t)(s * BKS + k) * (uint32_t)t.N + (uint32_t)(t.n0 + nb * 32 + c * 8)) * 2u);
-    }
+    const uint32_t dst = (sink || j >= G::B_INST) ? base + G::DUMMY : slot + G::A_BYTES + j * 1024;
+    dma_buffer(dst, brs, d.b_off[i] + (uint32_t)s * d.b_step);
   }
 }
 
-// Wait until at most `n` stages of this wave's DMA loads are outstanding.
-template <int BM, int BN>
-__device__ __forceinline__ void wait_stages(int n, bool big) {
-  using G = Gemm<BM, BN>;
-  constexpr int LB = G::A_PER_WAVE + G::B_MAX, LS = G::A_PER_WAVE + G::B_MIN;
-  if (n <= 0) {
-    vm_wait<0>();
-  } else if (n == 1) {
-    if (big) vm_wait<LB>(); else vm_wait<LS>();
-  } else {
-    if (big) vm_wait<2 * LB>(); else vm_wait<2 * LS>();
+template <int BM, int BN, int I = 0>
+__device__ __forceinline__ void dma_stage(uint32_t slot, bool sink, uint32_t base, const DmaPlan<BM, BN>& d,
+                                          const __amdgpu_buffer_rsrc_t& brs, int s, int wave) {
+  if constexpr (I < Gemm<BM, BN>::NDMA) {
+    dma_one<BM, BN, I>(slot, sink, base, d, brs, s, wave);
+    dma_stage<BM, BN, I + 1>(slot, sink, base, d, brs, s, wave);
   }
 }
 
@@ -177,56 +209,106 @@ __device__ __forceinline__ void read_frags(OCG_LDS const char* st, const FragAdd
   }
 }
 
-template <int BM, int BN>
-__device__ __forceinline__ void mfma_frags(const Frags<BM, BN>& fr,
-                                           f32x16_t (&acc)[Gemm<BM, BN>::FM][Gemm<BM, BN>::FN]) {
+// s_waitcnt lgkmcnt(0) with vmcnt and expcnt left open (gfx9 encoding), as a
+// builtin so the compiler's own wait insertion knows every LDS read is done.
+// The scheduling fences keep it from being hoisted above the MFMAs.
+__device__ __forceinline__ void lds_reads_done() {
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// MFMA group G (k half G / FN, column block G % FN) of `cur`, preceded by the
+// two transposing reads of the same block of `nxt` and followed by load G of
+// stage `s` (G < NDMA).
+template <int BM, int BN, int GI = 0>
+__device__ __forceinline__ void mfma_groups(const Frags<BM, BN>& cur, Frags<BM, BN>& nxt, OCG_LDS const char* st,
+                                            const FragAddr& fa,
+                                            f32x16_t (&acc)[Gemm<BM, BN>::FM][Gemm<BM, BN>::FN],
+                                            uint32_t slot, bool sink, uint32_t base, const DmaPlan<BM, BN>& d,
+                                            const __amdgpu_buffer_rsrc_t& brs, int s, int wave) {
   using G = Gemm<BM, BN>;
-#pragma unroll
-  for (int ks = 0; ks < 2; ++ks)
+  if constexpr (GI < 2 * G::FN) {
+    constexpr int ks = GI / G::FN, g = GI % G::FN;
+    bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((OCG_LDS bf16x4_t*)(st + fa.b + g * 2048 + ks * 1024));
+    bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+        (OCG_LDS bf16x4_t*)(st + fa.b + g * 2048 + ks * 1024 + 256));
+    nxt.b[g][ks] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
     for (int f = 0; f < G::FM; ++f)
+      acc[f][g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur.b[g][ks], cur.a[f][ks], acc[f][g], 0, 0, 0);
+    if constexpr (GI < G::NDMA) dma_one<BM, BN, GI>(slot, sink, base, d, brs, s, wave);
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_groups<BM, BN, GI + 1>(cur, nxt, st, fa, acc, slot, sink, base, d, brs, s, wave);
+  }
+}
+
+// One K stage: MFMAs of `cur`, with the fragment reads of the next stage from
+// `st` (into `nxt`) and the loads of stage `s` into `slot` spread between
+// them. No MFMA depends on a read issued in the same stage.
+template <int BM, int BN>
+__device__ __forceinline__ void stage_body(const Frags<BM, BN>& cur, Frags<BM, BN>& nxt, OCG_LDS const char* st,
+                                           const FragAddr& fa,
+                                           f32x16_t (&acc)[Gemm<BM, BN>::FM][Gemm<BM, BN>::FN],
+                                           uint32_t slot, bool sink, uint32_t base, const DmaPlan<BM, BN>& d,
+                                           const __amdgpu_buffer_rsrc_t& brs, int s, int wave) {
+  using G = Gemm<BM, BN>;
 #pragma unroll
-      for (int g = 0; g < G::FN; ++g)
-        acc[f][g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr.b[g][ks], fr.a[f][ks], acc[f][g], 0, 0, 0);
+  for (int f = 0; f < G::FM; ++f) {
+    nxt.a[f][0] = *(OCG_LDS const bf16x8_t*)(st + fa.a0 + f * 2048);
+    nxt.a[f][1] = *(OCG_LDS const bf16x8_t*)(st + fa.a1 + f * 2048);
+  }
+  mfma_groups<BM, BN>(cur, nxt, st, fa, acc, slot, sink, base, d, brs, s, wave);
+  // The reads of `nxt` had the whole MFMA block to land.
+  lds_reads_done();
 }
 
 // C tile += A[rows of t.rowp][0:K] x B[0:K][n0:n0+BN], K = 32 * t.nk (nk even).
 // Starts and ends with every wave past a barrier; LDS is free afterwards.
+//
+// Stage j lives in slot j % 4. Every step k is the same code: wait until at
+// most one stage of this wave's loads is in flight (stage k+1 has landed),
+// barrier (everyone's has, and every wave finished reading slot (k-1) % 4 in
+// step k-2), then compute stage k while reading stage k+1 and loading stage
+// k+3 into slot (k+3) % 4 = (k-1) % 4. Stages past the end re-read the last
+// stage into the dummy block, so the per-step load count and wait are
+// constants; in the last step the fragment reads fetch a stale slot whose
+// values are never used.
 template <int BM, int BN>
 __device__ __forceinline__ void mainloop(OCG_LDS char* smem, const TileCtx<BM, BN>& t,
                                          f32x16_t (&acc)[Gemm<BM, BN>::FM][Gemm<BM, BN>::FN]) {
   using G = Gemm<BM, BN>;
-  constexpr int S = G::S;
+  static_assert(G::S == 4, "slot arithmetic below assumes a 4-slot ring");
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const bool big = (wave + 4 * (G::B_MAX - 1)) < G::B_INST;   // this wave issues B_MAX B loads
   const uint32_t base = lds_u32(smem);
   const FragAddr fa = frag_addr<BM, BN>(wave);
+  const DmaPlan<BM, BN> d = make_dma_plan<BM, BN>(t, wave);
   const int nk = t.nk;
 #pragma unroll
   for (int f = 0; f < G::FM; ++f)
 #pragma unroll
     for (int g = 0; g < G::FN; ++g) acc[f][g] = f32x16_t{};
-  const int pro = nk < S - 1 ? nk : S - 1;
-  for (int s = 0; s < pro; ++s) issue_stage<BM, BN>(base + s * G::STAGE, t, s, wave);
-  Frags<BM, BN> f0, f1;
-  wait_stages<BM, BN>(pro - 1, big);
+  // prologue: stages 0, 1, 2 (stage 2 sinks when nk == 2)
+  dma_stage<BM, BN>(base, false, base, d, t.brs, 0, wave);
+  dma_stage<BM, BN>(base + G::STAGE, false, base, d, t.brs, 1, wave);
+  dma_stage<BM, BN>(base + 2 * G::STAGE, nk <= 2, base, d, t.brs, nk <= 2 ? nk - 1 : 2, wave);
+  vm_wait<2 * G::NDMA>();
   lds_barrier();
+  Frags<BM, BN> f0, f1;
   read_frags<BM, BN>(smem, fa, f0);
+  lds_reads_done();
   auto step = [&](int k, Frags<BM, BN>& cur, Frags<BM, BN>& nxt) {
-    if (k + 1 < nk) {
-      // stages issued: 0 .. min(k+S-2, nk-1); stage k+1 must have landed
-      const int issued = (k + S - 2 < nk - 1 ? k + S - 2 : nk - 1);
-      wait_stages<BM, BN>(issued - (k + 1), big);
-      lds_barrier();
-      if (k + S - 1 < nk) issue_stage<BM, BN>(base + ((k + S - 1) % S) * G::STAGE, t, k + S - 1, wave);
-      read_frags<BM, BN>(smem + ((k + 1) % S) * G::STAGE, fa, nxt);
-    }
-    mfma_frags<BM, BN>(cur, acc);
+    vm_wait<G::NDMA>();
+    lds_barrier();
+    const bool sink = k + 3 >= nk;
+    stage_body<BM, BN>(cur, nxt, smem + ((k + 1) & 3) * G::STAGE, fa, acc, base + ((k + 3) & 3) * G::STAGE, sink,
+                       base, d, t.brs, sink ? nk - 1 : k + 3, wave);
   };
   for (int k = 0; k < nk; k += 2) {
     step(k, f0, f1);
     step(k + 1, f1, f0);
   }
+  vm_wait<0>();   // no load may still target LDS when the tile's LDS is reused
   lds_barrier();
 }
 
