@@ -16,9 +16,8 @@
 // zero), S-1 stages ahead. They are issued from inline assembly so the
 // compiler does not add its own whole-queue waits before every LDS read; the
 // explicit vmcnt waits plus one barrier per stage order them. Every wave
-// issues the same number of loads per stage (a spare B load goes to a dummy
-// LDS block), so the waits are constants and the steady-state loop has no
-// branches. With one wave per SIMD an instruction only overlaps a 32-cycle
+// issues the same number of loads per stage, so the waits are constants and
+// the K loop has no branches. With one wave per SIMD an instruction only overlaps a 32-cycle
 // MFMA if it sits between MFMAs in program order, so the fragment reads of
 // stage k+1 and the loads of stage k+3 are interleaved with stage k's MFMAs.
 //
@@ -55,10 +54,8 @@ struct Gemm {
   static constexpr int B_INST = B_BYTES / 1024;
   static constexpr int A_PER_WAVE = A_INST / 4;
   static constexpr int B_PER_WAVE = (B_INST + 3) / 4;  // B instruction j = wave + 4*i
-  static constexpr bool SPARE = 4 * B_PER_WAVE > B_INST;
   static constexpr int NDMA = A_PER_WAVE + B_PER_WAVE;  // loads per wave per stage
-  static constexpr int DUMMY = S * STAGE;            // 1 KiB sink of spare and past-the-end loads
-  static constexpr int RING = S * STAGE + 1024;
+  static constexpr int RING = S * STAGE;
   static constexpr int LD_C = BN + 8;               // epilogue staging row (elements)
   static constexpr int LDS_BYTES = (RING > BM * LD_C * 2) ? RING : BM * LD_C * 2;
   static_assert(WM % 32 == 0 && BN % 32 == 0, "whole 32x32 blocks per wave");
@@ -112,11 +109,14 @@ __device__ __forceinline__ int dma_row(int wave, int i, int lane) {
 // 16*(wave*A_PER_WAVE + i) + lane/4, chunk (lane & 3) ^ swz_a(row), into the
 // slot's 1 KiB block wave*A_PER_WAVE + i; B instruction i (j = wave + 4i)
 // loads k row (j & 1)*16 + lane/4 of column block j/2, chunk pair
-// (lane & 3) ^ 2*swz_b(k), into block j of the slot's B part (or the dummy).
+// (lane & 3) ^ 2*swz_b(k), into block j of the slot's B part. A wave whose
+// last j is past the B blocks repeats its previous B load (same source, same
+// LDS bytes), so every wave issues NDMA loads per stage.
 template <int BM, int BN>
 struct DmaPlan {
   const char* a[Gemm<BM, BN>::A_PER_WAVE];     // per lane, stage 0
   uint32_t b_off[Gemm<BM, BN>::B_PER_WAVE];    // per lane byte offset in B, stage 0
+  uint32_t b_dst[Gemm<BM, BN>::B_PER_WAVE];    // LDS offset within a slot (wave-uniform)
   uint32_t b_step;                             // bytes of B per stage (32 rows)
 };
 
@@ -133,40 +133,36 @@ __device__ __forceinline__ DmaPlan<BM, BN> make_dma_plan(const TileCtx<BM, BN>& 
 #pragma unroll
   for (int i = 0; i < G::B_PER_WAVE; ++i) {
     int j = wave + 4 * i;
-    if (j >= G::B_INST) j -= 4;   // spare load: repeat a real one into the dummy block
+    if (j >= G::B_INST) j -= 4;
     const int nb = j >> 1, k = (j & 1) * 16 + (lane >> 2);
     const int c = (lane & 3) ^ (2 * swz_b(k));
     // byte offset of B[k][n0 + 32*nb + 8*c]; K*N*2 < 2^32 (unsigned math)
     d.b_off[i] = ((uint32_t)k * (uint32_t)t.N + (uint32_t)(t.n0 + nb * 32 + c * 8)) * 2u;
+    d.b_dst[i] = (uint32_t)(G::A_BYTES + j * 1024);
   }
   d.b_step = (uint32_t)BKS * (uint32_t)t.N * 2u;
   return d;
 }
 
-// Load number `I` (0 <= I < NDMA) of this wave for stage `s` into `slot`; with
-// `sink` set (a stage past the end, re-reading stage s) every load lands in
-// the dummy block instead.
+// Load number `I` (0 <= I < NDMA) of this wave for stage `s` into `slot`.
 template <int BM, int BN, int I>
-__device__ __forceinline__ void dma_one(uint32_t slot, bool sink, uint32_t base, const DmaPlan<BM, BN>& d,
-                                        const __amdgpu_buffer_rsrc_t& brs, int s, int wave) {
+__device__ __forceinline__ void dma_one(uint32_t slot, const DmaPlan<BM, BN>& d, const __amdgpu_buffer_rsrc_t& brs,
+                                        int s, int wave) {
   using G = Gemm<BM, BN>;
   if constexpr (I < G::A_PER_WAVE) {
-    const uint32_t dst = sink ? base + G::DUMMY : slot + (wave * G::A_PER_WAVE + I) * 1024;
-    dma_global(dst, d.a[I] + s * (BKS * 2));
+    dma_global(slot + (wave * G::A_PER_WAVE + I) * 1024, d.a[I] + s * (BKS * 2));
   } else {
     constexpr int i = I - G::A_PER_WAVE;
-    const int j = wave + 4 * i;
-    const uint32_t dst = (sink || j >= G::B_INST) ? base + G::DUMMY : slot + G::A_BYTES + j * 1024;
-    dma_buffer(dst, brs, d.b_off[i] + (uint32_t)s * d.b_step);
+    dma_buffer(slot + d.b_dst[i], brs, d.b_off[i] + (uint32_t)s * d.b_step);
   }
 }
 
 template <int BM, int BN, int I = 0>
-__device__ __forceinline__ void dma_stage(uint32_t slot, bool sink, uint32_t base, const DmaPlan<BM, BN>& d,
-                                          const __amdgpu_buffer_rsrc_t& brs, int s, int wave) {
+__device__ __forceinline__ void dma_stage(uint32_t slot, const DmaPlan<BM, BN>& d, const __amdgpu_buffer_rsrc_t& brs,
+                                          int s, int wave) {
   if constexpr (I < Gemm<BM, BN>::NDMA) {
-    dma_one<BM, BN, I>(slot, sink, base, d, brs, s, wave);
-    dma_stage<BM, BN, I + 1>(slot, sink, base, d, brs, s, wave);
+    dma_one<BM, BN, I>(slot, d, brs, s, wave);
+    dma_stage<BM, BN, I + 1>(slot, d, brs, s, wave);
   }
 }
 
@@ -225,7 +221,7 @@ template <int BM, int BN, int GI = 0>
 __device__ __forceinline__ void mfma_groups(const Frags<BM, BN>& cur, Frags<BM, BN>& nxt, OCG_LDS const char* st,
                                             const FragAddr& fa,
                                             f32x16_t (&acc)[Gemm<BM, BN>::FM][Gemm<BM, BN>::FN],
-                                            uint32_t slot, bool sink, uint32_t base, const DmaPlan<BM, BN>& d,
+                                            uint32_t slot, const DmaPlan<BM, BN>& d,
                                             const __amdgpu_buffer_rsrc_t& brs, int s, int wave) {
   using G = Gemm<BM, BN>;
   if constexpr (GI < 2 * G::FN) {
@@ -237,9 +233,9 @@ __device__ __forceinline__ void mfma_groups(const Frags<BM, BN>& cur, Frags<BM, 
 #pragma unroll
     for (int f = 0; f < G::FM; ++f)
       acc[f][g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur.b[g][ks], cur.a[f][ks], acc[f][g], 0, 0, 0);
-    if constexpr (GI < G::NDMA) dma_one<BM, BN, GI>(slot, sink, base, d, brs, s, wave);
+    if constexpr (GI < G::NDMA) dma_one<BM, BN, GI>(slot, d, brs, s, wave);
     __builtin_amdgcn_sched_barrier(0);
-    mfma_groups<BM, BN, GI + 1>(cur, nxt, st, fa, acc, slot, sink, base, d, brs, s, wave);
+    mfma_groups<BM, BN, GI + 1>(cur, nxt, st, fa, acc, slot, d, brs, s, wave);
   }
 }
 
@@ -250,7 +246,7 @@ template <int BM, int BN>
 __device__ __forceinline__ void stage_body(const Frags<BM, BN>& cur, Frags<BM, BN>& nxt, OCG_LDS const char* st,
                                            const FragAddr& fa,
                                            f32x16_t (&acc)[Gemm<BM, BN>::FM][Gemm<BM, BN>::FN],
-                                           uint32_t slot, bool sink, uint32_t base, const DmaPlan<BM, BN>& d,
+                                           uint32_t slot, const DmaPlan<BM, BN>& d,
                                            const __amdgpu_buffer_rsrc_t& brs, int s, int wave) {
   using G = Gemm<BM, BN>;
 #pragma unroll
@@ -258,7 +254,7 @@ __device__ __forceinline__ void stage_body(const Frags<BM, BN>& cur, Frags<BM, B
     nxt.a[f][0] = *(OCG_LDS const bf16x8_t*)(st + fa.a0 + f * 2048);
     nxt.a[f][1] = *(OCG_LDS const bf16x8_t*)(st + fa.a1 + f * 2048);
   }
-  mfma_groups<BM, BN>(cur, nxt, st, fa, acc, slot, sink, base, d, brs, s, wave);
+  mfma_groups<BM, BN>(cur, nxt, st, fa, acc, slot, d, brs, s, wave);
   // The reads of `nxt` had the whole MFMA block to land.
   lds_reads_done();
 }
@@ -270,10 +266,10 @@ __device__ __forceinline__ void stage_body(const Frags<BM, BN>& cur, Frags<BM, B
 // most one stage of this wave's loads is in flight (stage k+1 has landed),
 // barrier (everyone's has, and every wave finished reading slot (k-1) % 4 in
 // step k-2), then compute stage k while reading stage k+1 and loading stage
-// k+3 into slot (k+3) % 4 = (k-1) % 4. Stages past the end re-read the last
-// stage into the dummy block, so the per-step load count and wait are
-// constants; in the last step the fragment reads fetch a stale slot whose
-// values are never used.
+// k+3 into slot (k+3) % 4 = (k-1) % 4. Past the end the loads repeat stage
+// nk-1 into that free slot, which is never read again, so the per-step load
+// count and wait are constants; in the last step the fragment reads fetch a
+// stale slot whose values are never used.
 template <int BM, int BN>
 __device__ __forceinline__ void mainloop(OCG_LDS char* smem, const TileCtx<BM, BN>& t,
                                          f32x16_t (&acc)[Gemm<BM, BN>::FM][Gemm<BM, BN>::FN]) {
@@ -288,10 +284,10 @@ __device__ __forceinline__ void mainloop(OCG_LDS char* smem, const TileCtx<BM, B
   for (int f = 0; f < G::FM; ++f)
 #pragma unroll
     for (int g = 0; g < G::FN; ++g) acc[f][g] = f32x16_t{};
-  // prologue: stages 0, 1, 2 (stage 2 sinks when nk == 2)
-  dma_stage<BM, BN>(base, false, base, d, t.brs, 0, wave);
-  dma_stage<BM, BN>(base + G::STAGE, false, base, d, t.brs, 1, wave);
-  dma_stage<BM, BN>(base + 2 * G::STAGE, nk <= 2, base, d, t.brs, nk <= 2 ? nk - 1 : 2, wave);
+  // prologue: stages 0, 1, 2 (stage 2 repeats stage 1 when nk == 2)
+  dma_stage<BM, BN>(base, d, t.brs, 0, wave);
+  dma_stage<BM, BN>(base + G::STAGE, d, t.brs, 1, wave);
+  dma_stage<BM, BN>(base + 2 * G::STAGE, d, t.brs, nk <= 2 ? nk - 1 : 2, wave);
   vm_wait<2 * G::NDMA>();
   lds_barrier();
   Frags<BM, BN> f0, f1;
@@ -300,9 +296,8 @@ __device__ __forceinline__ void mainloop(OCG_LDS char* smem, const TileCtx<BM, B
   auto step = [&](int k, Frags<BM, BN>& cur, Frags<BM, BN>& nxt) {
     vm_wait<G::NDMA>();
     lds_barrier();
-    const bool sink = k + 3 >= nk;
-    stage_body<BM, BN>(cur, nxt, smem + ((k + 1) & 3) * G::STAGE, fa, acc, base + ((k + 3) & 3) * G::STAGE, sink,
-                       base, d, t.brs, sink ? nk - 1 : k + 3, wave);
+    stage_body<BM, BN>(cur, nxt, smem + ((k + 1) & 3) * G::STAGE, fa, acc, base + ((k + 3) & 3) * G::STAGE, d, t.brs,
+                       k + 3 < nk ? k + 3 : nk - 1, wave);
   };
   for (int k = 0; k < nk; k += 2) {
     step(k, f0, f1);
