@@ -39,7 +39,7 @@ WsLayout layout(int op, int R, int64_t m, int64_t K, int64_t N, int E, int topk)
   off = align256(off + sizeof(uint32_t) * L.max_slabs);
   L.rs_flag = off;
   off = align256(off + sizeof(uint32_t) * L.max_rs_tiles);
-  L.moe_off = L.moe_lut = L.moe_perm = off;
+  L.moe_off = L.moe_lut = L.moe_perm = L.moe_bcnt = L.moe_bbase = off;
   L.max_moe_tiles = 0;
   if (op == OCG_OP_AG_GROUPED_GEMM) {
     int slots = (int)(rows * topk);
@@ -50,6 +50,11 @@ WsLayout layout(int op, int R, int64_t m, int64_t K, int64_t N, int E, int topk)
     off = align256(off + sizeof(int32_t) * 8 * (size_t)L.max_moe_tiles);
     L.moe_perm = off;
     off = align256(off + sizeof(int32_t) * (size_t)slots);
+    const int nb = cdiv((int)rows, kRouteBlock);
+    L.moe_bcnt = off;
+    off = align256(off + sizeof(int32_t) * (size_t)nb * E);
+    L.moe_bbase = off;
+    off = align256(off + sizeof(int32_t) * (size_t)nb * E);
   }
   (void)K;
   L.total = off;
@@ -317,16 +322,14 @@ int ocg_ag_grouped_gemm(ocg_handle h, const void* const* a_chunks, int R, int lo
   r.offsets = (int32_t*)((char*)ws + L.moe_off);
   r.user_offsets = expert_offsets;
   r.lut = (int32_t*)((char*)ws + L.moe_lut);
+  r.blk_cnt = (int32_t*)((char*)ws + L.moe_bcnt);
+  r.blk_base = (int32_t*)((char*)ws + L.moe_bbase);
   r.hdr = (WsHeader*)ws;
   r.T = (int)(R * m);
   r.E = E;
   r.topk = topk;
   r.BM = rv.BM;
   r.n_cb = cdiv((int)N, rv.BN);
-  r.m = (int)m;
-  r.S = rv.S;
-  r.bpr = a.plan.bpr;
-  r.local = local_rank;
   r.max_tiles = L.max_moe_tiles;
   int grid = grid_for(h, OCG_OP_AG_GROUPED_GEMM, rv.tile, a.plan.n_copy + L.max_moe_tiles, cfg);
   return launch_moe(r, a, grid, (hipStream_t)stream) == hipSuccess ? OCG_OK : OCG_ERR_HIP;

@@ -4,7 +4,7 @@
 // M: wave w owns rows [w*BM/4, (w+1)*BM/4) and every column, computed with
 // v_mfma_f32_32x32x16_bf16 (one 32x32 accumulator per (32-row, 32-col) block).
 //
-// Stage s of the K loop lives in slot s % S of an S-slot LDS ring:
+// Stage s of the K loop lives in slot s % S of an S-slot LDS ring (S = 4..6):
 //   A part [BM][32] bf16, 64-byte rows; the 16-byte chunk c of row r is stored
 //     at chunk position c ^ swz_a(r) (conflict-free 16-lane row reads);
 //   B part [BN/32 blocks][32 k][32 n] bf16, 64-byte rows, kept k-major as in
@@ -19,7 +19,7 @@
 // issues the same number of loads per stage, so the waits are constants and
 // the K loop has no branches. With one wave per SIMD an instruction only overlaps a 32-cycle
 // MFMA if it sits between MFMAs in program order, so the fragment reads of
-// stage k+1 and the loads of stage k+3 are interleaved with stage k's MFMAs.
+// stage k+1 and the loads of stage k+S-1 are interleaved with stage k's MFMAs.
 //
 // The MFMA's A operand carries B (rows = n) and its B operand carries A
 // (columns = m), so each lane ends with 4 consecutive output columns of one
@@ -44,12 +44,15 @@ constexpr int BKS = 32;   // K per stage
 
 template <int BM, int BN>
 struct Gemm {
-  static constexpr int S = 4;                       // LDS ring slots
   static constexpr int WM = BM / 4;                 // rows per wave
   static constexpr int FM = WM / 32, FN = BN / 32;  // 32x32 blocks per wave
   static constexpr int A_BYTES = BM * BKS * 2;
   static constexpr int B_BYTES = BN * BKS * 2;
   static constexpr int STAGE = A_BYTES + B_BYTES;
+  // LDS ring slots: as deep as ~150 KiB allows (loads of S-1 stages in flight
+  // hide HBM latency when a tile streams operands with little reuse), at most
+  // 6; the 128x128 tile keeps 4 so two workgroups fit on a CU.
+  static constexpr int S = (BM == 128 && BN == 128) ? 4 : ((150 * 1024 / STAGE) < 6 ? 150 * 1024 / STAGE : 6);
   static constexpr int A_INST = A_BYTES / 1024;     // 1 KiB DMA instructions per stage
   static constexpr int B_INST = B_BYTES / 1024;
   static constexpr int A_PER_WAVE = A_INST / 4;
@@ -61,6 +64,7 @@ struct Gemm {
   static_assert(WM % 32 == 0 && BN % 32 == 0, "whole 32x32 blocks per wave");
   static_assert(A_INST % 4 == 0, "A DMA instructions split evenly over the waves");
   static_assert(NDMA <= 2 * FN, "every load of a stage has an MFMA group to sit behind");
+  static_assert(S >= 4 && (S - 2) * NDMA <= 63, "vmcnt waits fit the 6-bit counter");
   static_assert(LDS_BYTES <= 160 * 1024 - 64, "fits the 160 KiB LDS of a gfx950 CU");
 };
 
@@ -262,19 +266,19 @@ __device__ __forceinline__ void stage_body(const Frags<BM, BN>& cur, Frags<BM, B
 // C tile += A[rows of t.rowp][0:K] x B[0:K][n0:n0+BN], K = 32 * t.nk (nk even).
 // Starts and ends with every wave past a barrier; LDS is free afterwards.
 //
-// Stage j lives in slot j % 4. Every step k is the same code: wait until at
-// most one stage of this wave's loads is in flight (stage k+1 has landed),
-// barrier (everyone's has, and every wave finished reading slot (k-1) % 4 in
+// Stage j lives in slot j % S. Every step k is the same code: wait until at
+// most S-3 stages of this wave's loads are in flight (stage k+1 has landed),
+// barrier (everyone's has, and every wave finished reading slot (k-1) % S in
 // step k-2), then compute stage k while reading stage k+1 and loading stage
-// k+3 into slot (k+3) % 4 = (k-1) % 4. Past the end the loads repeat stage
-// nk-1 into that free slot, which is never read again, so the per-step load
-// count and wait are constants; in the last step the fragment reads fetch a
-// stale slot whose values are never used.
+// k+S-1 into slot (k+S-1) % S = (k-1) % S. Past the end the loads repeat
+// stage nk-1 into that free slot, which is never read again, so the per-step
+// load count and wait are constants; in the last step the fragment reads
+// fetch a stale slot whose values are never used.
 template <int BM, int BN>
 __device__ __forceinline__ void mainloop(OCG_LDS char* smem, const TileCtx<BM, BN>& t,
                                          f32x16_t (&acc)[Gemm<BM, BN>::FM][Gemm<BM, BN>::FN]) {
   using G = Gemm<BM, BN>;
-  static_assert(G::S == 4, "slot arithmetic below assumes a 4-slot ring");
+  constexpr int S = G::S;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const uint32_t base = lds_u32(smem);
   const FragAddr fa = frag_addr<BM, BN>(wave);
@@ -284,20 +288,21 @@ __device__ __forceinline__ void mainloop(OCG_LDS char* smem, const TileCtx<BM, B
   for (int f = 0; f < G::FM; ++f)
 #pragma unroll
     for (int g = 0; g < G::FN; ++g) acc[f][g] = f32x16_t{};
-  // prologue: stages 0, 1, 2 (stage 2 repeats stage 1 when nk == 2)
-  dma_stage<BM, BN>(base, d, t.brs, 0, wave);
-  dma_stage<BM, BN>(base + G::STAGE, d, t.brs, 1, wave);
-  dma_stage<BM, BN>(base + 2 * G::STAGE, d, t.brs, nk <= 2 ? nk - 1 : 2, wave);
-  vm_wait<2 * G::NDMA>();
+  // prologue: stages 0 .. S-2 (repeating stage nk-1 past the end)
+#pragma unroll
+  for (int j = 0; j < S - 1; ++j) dma_stage<BM, BN>(base + j * G::STAGE, d, t.brs, j < nk ? j : nk - 1, wave);
+  vm_wait<(S - 2) * G::NDMA>();
   lds_barrier();
   Frags<BM, BN> f0, f1;
   read_frags<BM, BN>(smem, fa, f0);
   lds_reads_done();
+  uint32_t rd = G::STAGE, wr = (S - 1) * G::STAGE;   // slot offsets of stages k+1 and k+S-1
   auto step = [&](int k, Frags<BM, BN>& cur, Frags<BM, BN>& nxt) {
-    vm_wait<G::NDMA>();
+    vm_wait<(S - 3) * G::NDMA>();
     lds_barrier();
-    stage_body<BM, BN>(cur, nxt, smem + ((k + 1) & 3) * G::STAGE, fa, acc, base + ((k + 3) & 3) * G::STAGE, d, t.brs,
-                       k + 3 < nk ? k + 3 : nk - 1, wave);
+    stage_body<BM, BN>(cur, nxt, smem + rd, fa, acc, base + wr, d, t.brs, k + S - 1 < nk ? k + S - 1 : nk - 1, wave);
+    rd = (rd + G::STAGE == S * G::STAGE) ? 0u : rd + G::STAGE;
+    wr = (wr + G::STAGE == S * G::STAGE) ? 0u : wr + G::STAGE;
   };
   for (int k = 0; k < nk; k += 2) {
     step(k, f0, f1);

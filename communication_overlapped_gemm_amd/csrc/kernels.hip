@@ -405,26 +405,23 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_rs_kernel(RsArgs args) {
 
 // ---------------------------------------------------------------- MoE routing
 
-// Single-workgroup routing: top-k of the fp32 logits (ties -> lower expert),
-// softmax weights, per-expert counts, offsets, stable expert-sorted slot list
-// and the grouped-tile lookup table (the dynamic dependency table).
-__global__ __launch_bounds__(kRouteThreads, 1) void moe_route_kernel(RouteArgs a) {
-  __shared__ uint8_t s_ids[kMaxRouteSlots];
-  __shared__ uint16_t s_perm[kMaxRouteSlots];
-  __shared__ int s_cnt[kMaxExperts];
-  __shared__ int s_off[kMaxExperts + 1];
-  __shared__ int s_run[kMaxExperts];
-  __shared__ int s_tbase[kMaxExperts + 1];
-  __shared__ int s_wcnt[kRouteThreads / 64][kMaxExperts];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int T = a.T, E = a.E, K = a.topk, S = T * K;
-  if (tid < kMaxExperts) {
-    s_cnt[tid] = 0;
-    s_run[tid] = 0;
-  }
-  __syncthreads();
+// Routing runs as three small kernels over blocks of kRouteBlock tokens, so
+// every step is spread over the chip: (1) per token top-k of the fp32 logits
+// (ties -> lower expert, slot 0 = larger logit) and softmax weights, plus a
+// per-block expert histogram; (2) one workgroup scans the histograms into
+// per-block expert bases, the expert offsets and the grouped-tile lookup
+// table (the dynamic dependency table: expert, first row, rows, column block
+// per tile); (3) per block, a stable rank of the block's token slots within
+// each expert gives the expert-sorted slot list perm (stable in expert, then
+// token, then slot).
 
-  for (int t = tid; t < T; t += kRouteThreads) {
+__global__ __launch_bounds__(kRouteBlock) void moe_topk_kernel(RouteArgs a) {
+  __shared__ int s_cnt[kMaxExperts];
+  const int tid = threadIdx.x, E = a.E, K = a.topk;
+  if (tid < E) s_cnt[tid] = 0;
+  __syncthreads();
+  const int t = blockIdx.x * kRouteBlock + tid;
+  if (t < a.T) {
     const float* lg = a.logits + (size_t)t * E;
     float bv[kMaxTopk];
     int bi[kMaxTopk];
@@ -434,7 +431,7 @@ __global__ __launch_bounds__(kRouteThreads, 1) void moe_route_kernel(RouteArgs a
       bi[j] = -1;
     }
     for (int e = 0; e < E; ++e) {
-      float v = lg[e];
+      const float v = lg[e];
       // insertion keeping the first (lowest-index) of equal logits ahead
       int pos = K;
       for (int j = K - 1; j >= 0; --j)
@@ -454,9 +451,27 @@ __global__ __launch_bounds__(kRouteThreads, 1) void moe_route_kernel(RouteArgs a
     for (int j = 0; j < K; ++j) {
       a.topk_ids[t * K + j] = bi[j];
       a.topk_w[t * K + j] = __expf(bv[j] - mx) / sum;
-      s_ids[t * K + j] = (uint8_t)bi[j];
       atomicAdd(&s_cnt[bi[j]], 1);
     }
+  }
+  __syncthreads();
+  if (tid < E) a.blk_cnt[blockIdx.x * E + tid] = s_cnt[tid];
+}
+
+__global__ __launch_bounds__(kRouteBlock) void moe_scan_kernel(RouteArgs a) {
+  __shared__ int s_cnt[kMaxExperts];
+  __shared__ int s_off[kMaxExperts + 1];
+  __shared__ int s_tbase[kMaxExperts + 1];
+  const int tid = threadIdx.x, E = a.E;
+  const int nb = cdiv(a.T, kRouteBlock);
+  if (tid < E) {
+    int run = 0;
+    for (int b = 0; b < nb; ++b) {
+      const int c = a.blk_cnt[b * E + tid];
+      a.blk_base[b * E + tid] = run;   // slots of expert tid in blocks before b
+      run += c;
+    }
+    s_cnt[tid] = run;
   }
   __syncthreads();
   if (tid == 0) {
@@ -476,13 +491,38 @@ __global__ __launch_bounds__(kRouteThreads, 1) void moe_route_kernel(RouteArgs a
     a.offsets[tid] = s_off[tid];
     if (a.user_offsets) a.user_offsets[tid] = s_off[tid];
   }
+  // Lookup table: one entry per (expert, column block, row tile), in that
+  // nesting order.
+  const int n = min(s_tbase[E], a.max_tiles);
+  for (int i = tid; i < n; i += kRouteBlock) {
+    int e = 0;
+    while (e + 1 < E && s_tbase[e + 1] <= i) ++e;
+    const int nrt = cdiv(s_cnt[e], a.BM);
+    const int j = i - s_tbase[e];
+    const int cb = j / nrt, rt = j - cb * nrt;
+    const int r0 = s_off[e] + rt * a.BM;
+    int32_t* L = a.lut + (size_t)i * 8;
+    L[0] = e;
+    L[1] = r0;
+    L[2] = min(a.BM, s_off[e + 1] - r0);
+    L[3] = cb;
+    L[4] = L[5] = L[6] = L[7] = 0;
+  }
+}
 
-  // Stable positions: slots are visited in index order, 1024 per round.
-  for (int base = 0; base < S; base += kRouteThreads) {
-    for (int i = tid; i < (kRouteThreads / 64) * kMaxExperts; i += kRouteThreads) (&s_wcnt[0][0])[i] = 0;
+__global__ __launch_bounds__(kRouteBlock) void moe_scatter_kernel(RouteArgs a) {
+  __shared__ int s_run[kMaxExperts];
+  __shared__ int s_wcnt[kRouteBlock / 64][kMaxExperts];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int E = a.E, K = a.topk, S = a.T * K;
+  if (tid < E) s_run[tid] = a.offsets[tid] + a.blk_base[blockIdx.x * E + tid];
+  const int s0 = blockIdx.x * kRouteBlock * K;
+  // The block's slots in index order, kRouteBlock per round.
+  for (int c = 0; c < K; ++c) {
+    for (int i = tid; i < (kRouteBlock / 64) * kMaxExperts; i += kRouteBlock) (&s_wcnt[0][0])[i] = 0;
     __syncthreads();
-    const int s = base + tid;
-    const int e = s < S ? (int)s_ids[s] : -1;
+    const int s = s0 + c * kRouteBlock + tid;
+    const int e = s < S ? a.topk_ids[s] : -1;
     uint64_t todo = __ballot(e >= 0);
     int rank = 0;
     while (todo) {
@@ -496,43 +536,16 @@ __global__ __launch_bounds__(kRouteThreads, 1) void moe_route_kernel(RouteArgs a
     __syncthreads();
     if (tid < E) {
       int run = s_run[tid];
-      for (int w = 0; w < kRouteThreads / 64; ++w) {
-        int c = s_wcnt[w][tid];
+      for (int w = 0; w < kRouteBlock / 64; ++w) {
+        const int n = s_wcnt[w][tid];
         s_wcnt[w][tid] = run;
-        run += c;
+        run += n;
       }
       s_run[tid] = run;
     }
     __syncthreads();
-    if (e >= 0) {
-      const int pos = s_off[e] + s_wcnt[wave][e] + rank;
-      a.perm[pos] = s;
-      s_perm[pos] = (uint16_t)s;
-    }
+    if (e >= 0) a.perm[s_wcnt[wave][e] + rank] = s;
     __syncthreads();
-  }
-
-  // Lookup table: one entry per (expert, column block, row tile).
-  for (int e = 0; e < E; ++e) {
-    const int nrt = cdiv(s_cnt[e], a.BM);
-    const int n = nrt * a.n_cb;
-    for (int i = tid; i < n; i += kRouteThreads) {
-      const int cb = i / nrt, rt = i - cb * nrt;
-      const int idx = s_tbase[e] + i;
-      if (idx >= a.max_tiles) continue;
-      const int r0 = s_off[e] + rt * a.BM;
-      const int r1 = min(r0 + a.BM, s_off[e + 1]);
-      const int tf = s_perm[r0] / K, tl = s_perm[r1 - 1] / K;
-      int32_t* L = a.lut + (size_t)idx * 8;
-      L[0] = e;
-      L[1] = r0;
-      L[2] = r1 - r0;
-      L[3] = cb;
-      L[4] = (tf / a.m) * a.bpr + (tf % a.m) / a.S;
-      L[5] = (tl / a.m) * a.bpr + (tl % a.m) / a.S;
-      L[6] = 0;
-      L[7] = 0;
-    }
   }
 }
 
@@ -569,10 +582,15 @@ __global__ __launch_bounds__(kThreads, 1) void moe_gemm_kernel(MoeArgs args) {
     if (v < 0) break;
     const uint64_t t0 = now_ticks();
     const int32_t* L = args.lut + (size_t)v * 8;
-    const int e = L[0], r0 = L[1], nrows = L[2], cb = L[3], s_lo = L[4], s_hi = L[5];
+    const int e = L[0], r0 = L[1], nrows = L[2], cb = L[3];
     uint32_t seen = 0;
     int nwait = 0;
     if (p.mode == 0 && threadIdx.x == 0) {
+      // consume_tile_wait on every non-local slab between the slabs of the
+      // tile's first and last token (tokens ascend within an expert)
+      const int tf = args.perm[r0] / args.topk, tl = args.perm[r0 + nrows - 1] / args.topk;
+      const int s_lo = (tf / p.m) * p.bpr + (tf % p.m) / p.S;
+      const int s_hi = (tl / p.m) * p.bpr + (tl % p.m) / p.S;
       for (int s = s_lo; s <= s_hi; ++s) {
         if (s / p.bpr == p.local) continue;
         wait_flag(&args.slab_flag[s], epoch, cm, &seen);
@@ -655,8 +673,15 @@ hipError_t launch_gemm_rs(const RsArgs& a, int tile, int grid, hipStream_t s) {
 }
 
 hipError_t launch_moe(const RouteArgs& r, const MoeArgs& a, int grid, hipStream_t s) {
-  hipLaunchKernelGGL(moe_route_kernel, dim3(1), dim3(kRouteThreads), 0, s, r);
+  const int nb = cdiv(r.T, kRouteBlock);
+  hipLaunchKernelGGL(moe_topk_kernel, dim3(nb), dim3(kRouteBlock), 0, s, r);
   hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(moe_scan_kernel, dim3(1), dim3(kRouteBlock), 0, s, r);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(moe_scatter_kernel, dim3(nb), dim3(kRouteBlock), 0, s, r);
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((moe_gemm_kernel<128, 224>), dim3(grid), dim3(kThreads), 0, s, a);
   return hipGetLastError();

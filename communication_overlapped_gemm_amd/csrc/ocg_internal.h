@@ -12,8 +12,8 @@ namespace ocg {
 
 constexpr int kMaxRanks = 16;
 constexpr int kThreads = 256;         // every persistent kernel: 4 waves of 64
-constexpr int kRouteThreads = 1024;   // routing kernel: 16 waves
-constexpr int kMaxRouteSlots = 16384; // token slots the routing kernel holds in LDS
+constexpr int kRouteBlock = 256;      // tokens per routing block (threads of the routing kernels)
+constexpr int kMaxRouteSlots = 16384; // token slots (T * topk) per call
 constexpr int kMaxExperts = 64;
 constexpr int kMaxTopk = 4;
 constexpr int kMinSlabRows = 16;
@@ -33,7 +33,7 @@ static_assert(sizeof(WsHeader) == 256, "header is 256 bytes");
 
 // Byte offsets of the workspace sections for one call shape.
 struct WsLayout {
-  size_t slab_cnt, slab_flag, rs_flag, moe_off, moe_lut, moe_perm, total;
+  size_t slab_cnt, slab_flag, rs_flag, moe_off, moe_lut, moe_perm, moe_bcnt, moe_bbase, total;
   int max_slabs, max_rs_tiles, max_moe_tiles;
 };
 
@@ -76,7 +76,7 @@ struct MoeArgs {
   uint16_t* a_gathered;
   uint16_t* out;
   const int32_t* perm;          // expert-sorted token-slot list
-  const int32_t* lut;           // [tiles][8]: e, r0, nrows, cb, slab_lo, slab_hi
+  const int32_t* lut;           // [tiles][8]: e, r0, nrows, cb, 0, 0, 0, 0
   uint32_t* slab_cnt;
   uint32_t* slab_flag;
   int topk, E;
@@ -92,8 +92,10 @@ struct RouteArgs {
   int32_t* offsets;             // workspace copy [E+1]
   int32_t* user_offsets;        // optional
   int32_t* lut;
+  int32_t* blk_cnt;             // [blocks][E] slots per expert in each routing block
+  int32_t* blk_base;            // [blocks][E] slots per expert in the blocks before
   WsHeader* hdr;
-  int T, E, topk, BM, n_cb, m, S, bpr, local, max_tiles;
+  int T, E, topk, BM, n_cb, max_tiles;
 };
 
 // Launchers (kernels.hip). Return hipSuccess or the launch error.
