@@ -266,14 +266,16 @@ __device__ __forceinline__ void stage_body(const Frags<BM, BN>& cur, Frags<BM, B
 // C tile += A[rows of t.rowp][0:K] x B[0:K][n0:n0+BN], K = 32 * t.nk (nk even).
 // Starts and ends with every wave past a barrier; LDS is free afterwards.
 //
-// Stage j lives in slot j % S. Every step k is the same code: wait until at
-// most S-3 stages of this wave's loads are in flight (stage k+1 has landed),
-// barrier (everyone's has, and every wave finished reading slot (k-1) % S in
-// step k-2), then compute stage k while reading stage k+1 and loading stage
-// k+S-1 into slot (k+S-1) % S = (k-1) % S. Past the end the loads repeat
-// stage nk-1 into that free slot, which is never read again, so the per-step
-// load count and wait are constants; in the last step the fragment reads
-// fetch a stale slot whose values are never used.
+// Stage j lives in slot j % S. Step k computes stage k while reading stage
+// k+1 and loading stage k+S-1 into slot (k+S-1) % S = (k-1) % S. Steps come
+// in pairs (k even, k+1) with one wait + barrier per pair, at step k: wait
+// until at most S-4 stages of this wave's loads are in flight (stages k+1 and
+// k+2 have landed), then barrier (everyone's have, and every wave finished
+// reading stage k-1 (in step k-2) and stage k (in step k-1), the slots the
+// pair overwrites). Past the end the loads repeat stage nk-1 into the free
+// slot, which is never read again, so the per-step load count and the wait
+// are constants; in the last step the fragment reads fetch a stale slot whose
+// values are never used.
 template <int BM, int BN>
 __device__ __forceinline__ void mainloop(OCG_LDS char* smem, const TileCtx<BM, BN>& t,
                                          f32x16_t (&acc)[Gemm<BM, BN>::FM][Gemm<BM, BN>::FN]) {
@@ -298,13 +300,13 @@ __device__ __forceinline__ void mainloop(OCG_LDS char* smem, const TileCtx<BM, B
   lds_reads_done();
   uint32_t rd = G::STAGE, wr = (S - 1) * G::STAGE;   // slot offsets of stages k+1 and k+S-1
   auto step = [&](int k, Frags<BM, BN>& cur, Frags<BM, BN>& nxt) {
-    vm_wait<(S - 3) * G::NDMA>();
-    lds_barrier();
     stage_body<BM, BN>(cur, nxt, smem + rd, fa, acc, base + wr, d, t.brs, k + S - 1 < nk ? k + S - 1 : nk - 1, wave);
     rd = (rd + G::STAGE == S * G::STAGE) ? 0u : rd + G::STAGE;
     wr = (wr + G::STAGE == S * G::STAGE) ? 0u : wr + G::STAGE;
   };
   for (int k = 0; k < nk; k += 2) {
+    vm_wait<(S - 4) * G::NDMA>();
+    lds_barrier();
     step(k, f0, f1);
     step(k + 1, f1, f0);
   }
