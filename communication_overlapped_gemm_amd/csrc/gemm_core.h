@@ -219,8 +219,9 @@ __device__ __forceinline__ void lds_reads_done() {
 }
 
 // MFMA group G (k half G / FN, column block G % FN) of `cur`, preceded by the
-// two transposing reads of the same block of `nxt` and followed by load G of
-// stage `s` (G < NDMA).
+// two transposing reads of the same block of `nxt`; the NDMA loads of stage
+// `s` are spread evenly over the 2*FN groups (load I after group I*2FN/NDMA),
+// which keeps the per-CU memory pipe from queueing up behind a burst.
 template <int BM, int BN, int GI = 0>
 __device__ __forceinline__ void mfma_groups(const Frags<BM, BN>& cur, Frags<BM, BN>& nxt, OCG_LDS const char* st,
                                             const FragAddr& fa,
@@ -237,7 +238,9 @@ __device__ __forceinline__ void mfma_groups(const Frags<BM, BN>& cur, Frags<BM, 
 #pragma unroll
     for (int f = 0; f < G::FM; ++f)
       acc[f][g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur.b[g][ks], cur.a[f][ks], acc[f][g], 0, 0, 0);
-    if constexpr (GI < G::NDMA) dma_one<BM, BN, GI>(slot, d, brs, s, wave);
+    // loads spread evenly over the groups: load I follows group I*2FN/NDMA
+    constexpr int I = (GI * G::NDMA + 2 * G::FN - 1) / (2 * G::FN);   // ceil
+    if constexpr (I < G::NDMA && (I * 2 * G::FN) / G::NDMA == GI) dma_one<BM, BN, I>(slot, d, brs, s, wave);
     __builtin_amdgcn_sched_barrier(0);
     mfma_groups<BM, BN, GI + 1>(cur, nxt, st, fa, acc, slot, d, brs, s, wave);
   }
