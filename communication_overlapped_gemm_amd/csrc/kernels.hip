@@ -160,22 +160,38 @@ __device__ __forceinline__ uint32_t next_ticket(uint32_t* counter, uint32_t* s_b
   return s_bcast[0];
 }
 
-// Next tile from the XCD queues: own XCD first, then the others in turn.
-// `*q` carries the queue being drained between calls (starts at the XCD id,
-// `*tried` at 0). Returns the tile index, or -1 when every queue is empty.
+// Next tile from the XCD queues: own XCD first, then the others. `*q` is the
+// queue being drained (starts at the XCD id). When it runs dry, one relaxed
+// load per queue (all eight in parallel) finds the queues that may still hold
+// tiles -- a queue whose ticket is past its last tile is empty for good, since
+// tickets only grow within a launch -- and the search moves to the next of
+// them; -1 once none is left. `*tried` is unused (kept for the call sites).
 __device__ __forceinline__ int next_tile(WsHeader* hdr, int n_tiles, int* q, int* tried, uint32_t* s_bcast,
                                          uint32_t* t_out) {
-  while (*tried < kXcds) {
+  (void)tried;
+  for (;;) {
     const uint32_t t = next_ticket(&hdr->xtick[*q], s_bcast);
     const int v = xcd_tile(*q, (int)t, n_tiles);
     if (v >= 0) {
       *t_out = t;
       return v;
     }
-    *q = (*q + 1) % kXcds;
-    ++*tried;
+    if (threadIdx.x < 64) {
+      bool open = false;
+      if (threadIdx.x < kXcds) {
+        const uint32_t x = __hip_atomic_load(&hdr->xtick[threadIdx.x], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        open = xcd_tile((int)threadIdx.x, (int)x, n_tiles) >= 0;
+      }
+      const uint64_t m = __ballot(open);
+      if (threadIdx.x == 0) s_bcast[5] = (uint32_t)m;
+    }
+    __syncthreads();
+    const uint32_t mask = s_bcast[5];
+    if (mask == 0) return -1;
+    // next open queue after *q, cyclically
+    const uint32_t rot = ((mask >> ((*q + 1) % kXcds)) | (mask << (kXcds - (*q + 1) % kXcds))) & 0xFFu;
+    *q = (*q + 1 + __builtin_ctz(rot)) % kXcds;
   }
-  return -1;
 }
 
 // Last workgroup out resets the counters and records the epoch. Relaxed
