@@ -43,7 +43,8 @@ WsLayout layout(int op, int R, int64_t m, int64_t K, int64_t N, int E, int topk)
   L.max_moe_tiles = 0;
   if (op == OCG_OP_AG_GROUPED_GEMM) {
     int slots = (int)(rows * topk);
-    L.max_moe_tiles = (cdiv(slots, tile_bm(kMoeTile)) + E) * cdiv((int)N, tile_bn(kMoeTile));
+    // sized for the preset with the most tiles (128-row)
+    L.max_moe_tiles = (cdiv(slots, tile_bm(kMoeTileSmall)) + E) * cdiv((int)N, tile_bn(kMoeTileSmall));
     L.moe_off = off;
     off = align256(off + sizeof(int32_t) * (E + 1));
     L.moe_lut = off;
@@ -94,9 +95,12 @@ struct Resolved {
 
 int resolve(int op, int R, int64_t m, int64_t K, int64_t N, const ocg_config& c, int cus, Resolved* r) {
   int64_t M = (op == OCG_OP_GEMM_RS) ? m : R * m;
-  r->tile = (op == OCG_OP_AG_GROUPED_GEMM) ? kMoeTile : (c.tile < 0 ? choose_tile(M, N, cus) : c.tile);
+  if (op == OCG_OP_AG_GROUPED_GEMM)
+    r->tile = c.tile < 0 ? kMoeTile : c.tile;
+  else
+    r->tile = c.tile < 0 ? choose_tile(M, N, cus) : c.tile;
   if (r->tile < 0 || r->tile >= OCG_TILE_COUNT) return OCG_ERR_INVALID_ARG;
-  if (op == OCG_OP_AG_GROUPED_GEMM && c.tile >= 0 && c.tile != kMoeTile) return OCG_ERR_INVALID_ARG;
+  if (op == OCG_OP_AG_GROUPED_GEMM && r->tile != kMoeTile && r->tile != kMoeTileSmall) return OCG_ERR_INVALID_ARG;
   r->BM = tile_bm(r->tile);
   r->BN = tile_bn(r->tile);
   r->S = c.slab_rows > 0 ? c.slab_rows : r->BM;
@@ -332,7 +336,7 @@ int ocg_ag_grouped_gemm(ocg_handle h, const void* const* a_chunks, int R, int lo
   r.n_cb = cdiv((int)N, rv.BN);
   r.max_tiles = L.max_moe_tiles;
   int grid = grid_for(h, OCG_OP_AG_GROUPED_GEMM, rv.tile, a.plan.n_copy + L.max_moe_tiles, cfg);
-  return launch_moe(r, a, grid, (hipStream_t)stream) == hipSuccess ? OCG_OK : OCG_ERR_HIP;
+  return launch_moe(r, a, rv.tile, grid, (hipStream_t)stream) == hipSuccess ? OCG_OK : OCG_ERR_HIP;
 }
 
 int ocg_signal(uint32_t* flags, int count, uint32_t value, void* stream) {

@@ -688,7 +688,7 @@ hipError_t launch_gemm_rs(const RsArgs& a, int tile, int grid, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_moe(const RouteArgs& r, const MoeArgs& a, int grid, hipStream_t s) {
+hipError_t launch_moe(const RouteArgs& r, const MoeArgs& a, int tile, int grid, hipStream_t s) {
   const int nb = cdiv(r.T, kRouteBlock);
   hipLaunchKernelGGL(moe_topk_kernel, dim3(nb), dim3(kRouteBlock), 0, s, r);
   hipError_t e = hipGetLastError();
@@ -699,7 +699,10 @@ hipError_t launch_moe(const RouteArgs& r, const MoeArgs& a, int grid, hipStream_
   hipLaunchKernelGGL(moe_scatter_kernel, dim3(nb), dim3(kRouteBlock), 0, s, r);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((moe_gemm_kernel<128, 224>), dim3(grid), dim3(kThreads), 0, s, a);
+  if (tile == OCG_TILE_256x224)
+    hipLaunchKernelGGL((moe_gemm_kernel<256, 224>), dim3(grid), dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL((moe_gemm_kernel<128, 224>), dim3(grid), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
@@ -719,7 +722,8 @@ static int occ(K kern) {
 }
 
 int resident_per_cu(int op, int tile) {
-  if (op == OCG_OP_AG_GROUPED_GEMM) return occ(moe_gemm_kernel<128, 224>);
+  if (op == OCG_OP_AG_GROUPED_GEMM)
+    return tile == OCG_TILE_256x224 ? occ(moe_gemm_kernel<256, 224>) : occ(moe_gemm_kernel<128, 224>);
   if (op == OCG_OP_AG_GEMM) {
     switch (tile) {
       case OCG_TILE_256x224: return occ(ag_gemm_kernel<256, 224>);

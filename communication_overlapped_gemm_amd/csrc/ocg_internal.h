@@ -17,7 +17,8 @@ constexpr int kMaxRouteSlots = 16384; // token slots (T * topk) per call
 constexpr int kMaxExperts = 64;
 constexpr int kMaxTopk = 4;
 constexpr int kMinSlabRows = 16;
-constexpr int kMoeTile = OCG_TILE_128x224;
+constexpr int kMoeTile = OCG_TILE_256x224;      // grouped GEMM default preset
+constexpr int kMoeTileSmall = OCG_TILE_128x224; // the other preset it accepts
 
 // Workspace header (first 256 bytes of every workspace).
 struct WsHeader {
@@ -101,7 +102,7 @@ struct RouteArgs {
 // Launchers (kernels.hip). Return hipSuccess or the launch error.
 hipError_t launch_ag_gemm(const AgArgs& a, int tile, int grid, hipStream_t s);
 hipError_t launch_gemm_rs(const RsArgs& a, int tile, int grid, hipStream_t s);
-hipError_t launch_moe(const RouteArgs& r, const MoeArgs& a, int grid, hipStream_t s);
+hipError_t launch_moe(const RouteArgs& r, const MoeArgs& a, int tile, int grid, hipStream_t s);
 hipError_t launch_fill_u32(uint32_t* p, size_t n, uint32_t v, int release, hipStream_t s);
 // Resident workgroups per CU of each persistent kernel (op, tile preset).
 int resident_per_cu(int op, int tile);

@@ -179,7 +179,10 @@ int ocg_gemm_rs(ocg_handle h, const void* a, const void* b, int64_t M, int64_t K
  *                    expert in `perm`
  *   out         : bf16 [R*m*topk, N], written
  * The grouped tiles wait on the flags of every peer slab their tokens come
- * from (a per-tile lookup table built on the device after routing).
+ * from (a per-tile lookup table built on the device after routing). Tile
+ * presets: OCG_TILE_256x224 (default for OCG_TILE_AUTO: one tile holds an
+ * expert's rows when it has at most 256) or OCG_TILE_128x224; any other
+ * preset is OCG_ERR_INVALID_ARG.
  */
 int ocg_ag_grouped_gemm(ocg_handle h, const void* const* a_chunks, int R, int local_rank,
                         int64_t m, int64_t K, const float* logits, int E, int topk,

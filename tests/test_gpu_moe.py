@@ -47,13 +47,21 @@ SMALL = [
 ]
 
 
+@pytest.mark.parametrize("tile", ["auto", "128x224"])
 @pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
-def test_moe_small_full(ocg, case):
+def test_moe_small_full(ocg, case, tile):
     name, R, m, K, N, E, topk, local = case
     x = workloads.make_moe(R, m, K, N, E, seed=300 + E, topk=topk, scale=0.5)
-    say("moe", name)
-    o = run(ocg, x, local)
+    cfg = ocg.default_config(tile=ocg.TILE_AUTO if tile == "auto" else ocg.TILE_128x224)
+    say("moe", name, tile)
+    o = run(ocg, x, local, cfg)
     check(ocg, x, o, name)
+
+
+def test_moe_rejects_other_presets(ocg):
+    x = workloads.make_moe(2, 64, 128, 96, 6, seed=306, topk=2, scale=0.5)
+    with pytest.raises(ocg.OcgError):
+        run(ocg, x, 0, ocg.default_config(tile=ocg.TILE_128x128))
 
 
 def test_moe_ties_and_empty_experts(ocg):
