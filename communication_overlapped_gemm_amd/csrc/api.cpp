@@ -39,7 +39,7 @@ WsLayout layout(int op, int R, int64_t m, int64_t K, int64_t N, int E, int topk)
   off = align256(off + sizeof(uint32_t) * L.max_slabs);
   L.rs_flag = off;
   off = align256(off + sizeof(uint32_t) * L.max_rs_tiles);
-  L.moe_off = L.moe_lut = L.moe_perm = L.moe_bcnt = L.moe_bbase = off;
+  L.moe_off = L.moe_lut = L.moe_perm = L.moe_bcnt = off;
   L.max_moe_tiles = 0;
   if (op == OCG_OP_AG_GROUPED_GEMM) {
     int slots = (int)(rows * topk);
@@ -53,8 +53,6 @@ WsLayout layout(int op, int R, int64_t m, int64_t K, int64_t N, int E, int topk)
     off = align256(off + sizeof(int32_t) * (size_t)slots);
     const int nb = cdiv((int)rows, kRouteBlock);
     L.moe_bcnt = off;
-    off = align256(off + sizeof(int32_t) * (size_t)nb * E);
-    L.moe_bbase = off;
     off = align256(off + sizeof(int32_t) * (size_t)nb * E);
   }
   (void)K;
@@ -327,7 +325,6 @@ int ocg_ag_grouped_gemm(ocg_handle h, const void* const* a_chunks, int R, int lo
   r.user_offsets = expert_offsets;
   r.lut = (int32_t*)((char*)ws + L.moe_lut);
   r.blk_cnt = (int32_t*)((char*)ws + L.moe_bcnt);
-  r.blk_base = (int32_t*)((char*)ws + L.moe_bbase);
   r.hdr = (WsHeader*)ws;
   r.T = (int)(R * m);
   r.E = E;

@@ -421,22 +421,24 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_rs_kernel(RsArgs args) {
 
 // ---------------------------------------------------------------- MoE routing
 
-// Routing runs as three small kernels over blocks of kRouteBlock tokens, so
-// every step is spread over the chip: (1) per token top-k of the fp32 logits
-// (ties -> lower expert, slot 0 = larger logit) and softmax weights, plus a
-// per-block expert histogram; (2) one workgroup scans the histograms into
-// per-block expert bases, the expert offsets and the grouped-tile lookup
-// table (the dynamic dependency table: expert, first row, rows, column block
-// per tile); (3) per block, a stable rank of the block's token slots within
-// each expert gives the expert-sorted slot list perm (stable in expert, then
-// token, then slot).
+// Routing runs as two one-wave-per-block kernels over blocks of kRouteBlock
+// tokens, so every step is spread over the chip: (1) per token top-k of the
+// fp32 logits (ties -> lower expert, slot 0 = larger logit) and softmax
+// weights, plus a per-block expert histogram; (2) per block, the expert
+// bases of the block (histograms of the blocks before it) and the expert
+// offsets (totals, scanned across the wave), then a stable rank of the
+// block's token slots within each expert gives the expert-sorted slot list
+// perm (stable in expert, then token, then slot). Block 0 also writes the
+// offsets and the grouped-tile lookup table (the dynamic dependency table:
+// expert, first row, rows, column block per tile).
 
 __global__ __launch_bounds__(kRouteBlock) void moe_topk_kernel(RouteArgs a) {
   __shared__ int s_cnt[kMaxExperts];
-  const int tid = threadIdx.x, E = a.E, K = a.topk;
-  if (tid < E) s_cnt[tid] = 0;
+  static_assert(kRouteBlock == kMaxExperts, "one counter per lane");
+  const int lane = threadIdx.x, E = a.E, K = a.topk;
+  s_cnt[lane] = 0;
   __syncthreads();
-  const int t = blockIdx.x * kRouteBlock + tid;
+  const int t = blockIdx.x * kRouteBlock + lane;
   if (t < a.T) {
     const float* lg = a.logits + (size_t)t * E;
     float bv[kMaxTopk];
@@ -446,24 +448,32 @@ __global__ __launch_bounds__(kRouteBlock) void moe_topk_kernel(RouteArgs a) {
       bv[j] = 0.f;
       bi[j] = -1;
     }
-    for (int e = 0; e < E; ++e) {
-      const float v = lg[e];
-      // insertion keeping the first (lowest-index) of equal logits ahead
-      int pos = K;
-      for (int j = K - 1; j >= 0; --j)
-        if (bi[j] < 0 || v > bv[j]) pos = j;
-      if (pos < K) {
-        for (int j = K - 1; j > pos; --j) {
-          bv[j] = bv[j - 1];
-          bi[j] = bi[j - 1];
+    // all logits of the token at once (independent loads, then registers)
+    float v[kMaxExperts];
+#pragma unroll
+    for (int e = 0; e < kMaxExperts; ++e) v[e] = (e < E) ? lg[e] : 0.f;
+#pragma unroll
+    for (int e = 0; e < kMaxExperts; ++e) {
+      if (e < E) {
+        // insertion keeping the first (lowest-index) of equal logits ahead
+        int pos = K;
+        for (int j = K - 1; j >= 0; --j)
+          if (bi[j] < 0 || v[e] > bv[j]) pos = j;
+        if (pos < K) {
+          for (int j = K - 1; j > pos; --j) {
+            bv[j] = bv[j - 1];
+            bi[j] = bi[j - 1];
+          }
+          bv[pos] = v[e];
+          bi[pos] = e;
         }
-        bv[pos] = v;
-        bi[pos] = e;
       }
     }
     const float mx = bv[0];
     float sum = 0.f;
-    for (int e = 0; e < E; ++e) sum += __expf(lg[e] - mx);
+#pragma unroll
+    for (int e = 0; e < kMaxExperts; ++e)
+      if (e < E) sum += __expf(v[e] - mx);
     for (int j = 0; j < K; ++j) {
       a.topk_ids[t * K + j] = bi[j];
       a.topk_w[t * K + j] = __expf(bv[j] - mx) / sum;
@@ -471,97 +481,98 @@ __global__ __launch_bounds__(kRouteBlock) void moe_topk_kernel(RouteArgs a) {
     }
   }
   __syncthreads();
-  if (tid < E) a.blk_cnt[blockIdx.x * E + tid] = s_cnt[tid];
-}
-
-__global__ __launch_bounds__(kRouteBlock) void moe_scan_kernel(RouteArgs a) {
-  __shared__ int s_cnt[kMaxExperts];
-  __shared__ int s_off[kMaxExperts + 1];
-  __shared__ int s_tbase[kMaxExperts + 1];
-  const int tid = threadIdx.x, E = a.E;
-  const int nb = cdiv(a.T, kRouteBlock);
-  if (tid < E) {
-    int run = 0;
-    for (int b = 0; b < nb; ++b) {
-      const int c = a.blk_cnt[b * E + tid];
-      a.blk_base[b * E + tid] = run;   // slots of expert tid in blocks before b
-      run += c;
-    }
-    s_cnt[tid] = run;
-  }
-  __syncthreads();
-  if (tid == 0) {
-    int o = 0, tb = 0;
-    for (int e = 0; e < E; ++e) {
-      s_off[e] = o;
-      s_tbase[e] = tb;
-      o += s_cnt[e];
-      tb += cdiv(s_cnt[e], a.BM) * a.n_cb;
-    }
-    s_off[E] = o;
-    s_tbase[E] = tb;
-    a.hdr->n_tiles = (uint32_t)min(tb, a.max_tiles);
-  }
-  __syncthreads();
-  if (tid <= E) {
-    a.offsets[tid] = s_off[tid];
-    if (a.user_offsets) a.user_offsets[tid] = s_off[tid];
-  }
-  // Lookup table: one entry per (expert, column block, row tile), in that
-  // nesting order.
-  const int n = min(s_tbase[E], a.max_tiles);
-  for (int i = tid; i < n; i += kRouteBlock) {
-    int e = 0;
-    while (e + 1 < E && s_tbase[e + 1] <= i) ++e;
-    const int nrt = cdiv(s_cnt[e], a.BM);
-    const int j = i - s_tbase[e];
-    const int cb = j / nrt, rt = j - cb * nrt;
-    const int r0 = s_off[e] + rt * a.BM;
-    int32_t* L = a.lut + (size_t)i * 8;
-    L[0] = e;
-    L[1] = r0;
-    L[2] = min(a.BM, s_off[e + 1] - r0);
-    L[3] = cb;
-    L[4] = L[5] = L[6] = L[7] = 0;
-  }
+  if (lane < E) a.blk_cnt[blockIdx.x * E + lane] = s_cnt[lane];
 }
 
 __global__ __launch_bounds__(kRouteBlock) void moe_scatter_kernel(RouteArgs a) {
   __shared__ int s_run[kMaxExperts];
-  __shared__ int s_wcnt[kRouteBlock / 64][kMaxExperts];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  __shared__ int s_off[kMaxExperts + 1];
+  __shared__ int s_cnt[kMaxExperts];
+  __shared__ int s_tbase[kMaxExperts + 1];
+  const int lane = threadIdx.x;
   const int E = a.E, K = a.topk, S = a.T * K;
-  if (tid < E) s_run[tid] = a.offsets[tid] + a.blk_base[blockIdx.x * E + tid];
-  const int s0 = blockIdx.x * kRouteBlock * K;
-  // The block's slots in index order, kRouteBlock per round.
-  for (int c = 0; c < K; ++c) {
-    for (int i = tid; i < (kRouteBlock / 64) * kMaxExperts; i += kRouteBlock) (&s_wcnt[0][0])[i] = 0;
+  const int nb = cdiv(a.T, kRouteBlock);
+  // expert totals, and the slots of each expert in the blocks before this one
+  int tot = 0, before = 0;
+  if (lane < E) {
+    for (int b0 = 0; b0 < nb; b0 += 16) {
+      int c[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) c[i] = (b0 + i < nb) ? a.blk_cnt[(b0 + i) * E + lane] : 0;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        if (b0 + i < (int)blockIdx.x) before += c[i];
+        tot += c[i];
+      }
+    }
+  }
+  // exclusive scan of the totals across the wave (lanes >= E hold 0)
+  int incl = tot;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int o = __shfl_up(incl, d);
+    if (lane >= d) incl += o;
+  }
+  const int off = incl - tot;
+  if (lane < E) {
+    s_off[lane] = off;
+    s_cnt[lane] = tot;
+    s_run[lane] = off + before;
+  }
+  if (lane == E - 1) s_off[E] = incl;
+  __syncthreads();
+  if (blockIdx.x == 0) {
+    if (lane <= E) {
+      a.offsets[lane] = s_off[lane];
+      if (a.user_offsets) a.user_offsets[lane] = s_off[lane];
+    }
+    if (lane == 0) {
+      int tb = 0;
+      for (int e = 0; e < E; ++e) {
+        s_tbase[e] = tb;
+        tb += cdiv(s_cnt[e], a.BM) * a.n_cb;
+      }
+      s_tbase[E] = tb;
+      a.hdr->n_tiles = (uint32_t)min(tb, a.max_tiles);
+    }
     __syncthreads();
-    const int s = s0 + c * kRouteBlock + tid;
+    // lookup table: one entry per (expert, column block, row tile), in that
+    // nesting order
+    const int n = min(s_tbase[E], a.max_tiles);
+    for (int i = lane; i < n; i += kRouteBlock) {
+      int e = 0;
+      while (e + 1 < E && s_tbase[e + 1] <= i) ++e;
+      const int nrt = cdiv(s_cnt[e], a.BM);
+      const int j = i - s_tbase[e];
+      const int cb = j / nrt, rt = j - cb * nrt;
+      const int r0 = s_off[e] + rt * a.BM;
+      int32_t* L = a.lut + (size_t)i * 8;
+      L[0] = e;
+      L[1] = r0;
+      L[2] = min(a.BM, s_off[e + 1] - r0);
+      L[3] = cb;
+      L[4] = L[5] = L[6] = L[7] = 0;
+    }
+  }
+  // the block's slots in index order, one wave-wide round at a time
+  const int s0 = blockIdx.x * kRouteBlock * K;
+  for (int c = 0; c < K; ++c) {
+    const int s = s0 + c * kRouteBlock + lane;
     const int e = s < S ? a.topk_ids[s] : -1;
     uint64_t todo = __ballot(e >= 0);
-    int rank = 0;
+    int pos = -1;
     while (todo) {
       const int leader = __builtin_ctzll(todo);
       const int x = __shfl(e, leader);
       const uint64_t same = __ballot(e == x);
-      if (e == x) rank = __builtin_popcountll(same & ((1ull << lane) - 1ull));
-      if (lane == 0) s_wcnt[wave][x] = __builtin_popcountll(same);
+      const int base = s_run[x];
+      if (e == x) pos = base + __builtin_popcountll(same & ((1ull << lane) - 1ull));
+      __syncthreads();
+      if (lane == leader) s_run[x] = base + __builtin_popcountll(same);
+      __syncthreads();
       todo &= ~same;
     }
-    __syncthreads();
-    if (tid < E) {
-      int run = s_run[tid];
-      for (int w = 0; w < kRouteBlock / 64; ++w) {
-        const int n = s_wcnt[w][tid];
-        s_wcnt[w][tid] = run;
-        run += n;
-      }
-      s_run[tid] = run;
-    }
-    __syncthreads();
-    if (e >= 0) a.perm[s_wcnt[wave][e] + rank] = s;
-    __syncthreads();
+    if (e >= 0) a.perm[pos] = s;
   }
 }
 
@@ -692,9 +703,6 @@ hipError_t launch_moe(const RouteArgs& r, const MoeArgs& a, int tile, int grid, 
   const int nb = cdiv(r.T, kRouteBlock);
   hipLaunchKernelGGL(moe_topk_kernel, dim3(nb), dim3(kRouteBlock), 0, s, r);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(moe_scan_kernel, dim3(1), dim3(kRouteBlock), 0, s, r);
-  e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(moe_scatter_kernel, dim3(nb), dim3(kRouteBlock), 0, s, r);
   e = hipGetLastError();

@@ -12,7 +12,7 @@ namespace ocg {
 
 constexpr int kMaxRanks = 16;
 constexpr int kThreads = 256;         // every persistent kernel: 4 waves of 64
-constexpr int kRouteBlock = 256;      // tokens per routing block (threads of the routing kernels)
+constexpr int kRouteBlock = 64;       // tokens per routing block (one wave per routing block)
 constexpr int kMaxRouteSlots = 16384; // token slots (T * topk) per call
 constexpr int kMaxExperts = 64;
 constexpr int kMaxTopk = 4;
@@ -34,7 +34,7 @@ static_assert(sizeof(WsHeader) == 256, "header is 256 bytes");
 
 // Byte offsets of the workspace sections for one call shape.
 struct WsLayout {
-  size_t slab_cnt, slab_flag, rs_flag, moe_off, moe_lut, moe_perm, moe_bcnt, moe_bbase, total;
+  size_t slab_cnt, slab_flag, rs_flag, moe_off, moe_lut, moe_perm, moe_bcnt, total;
   int max_slabs, max_rs_tiles, max_moe_tiles;
 };
 
@@ -94,7 +94,6 @@ struct RouteArgs {
   int32_t* user_offsets;        // optional
   int32_t* lut;
   int32_t* blk_cnt;             // [blocks][E] slots per expert in each routing block
-  int32_t* blk_base;            // [blocks][E] slots per expert in the blocks before
   WsHeader* hdr;
   int T, E, topk, BM, n_cb, max_tiles;
 };
