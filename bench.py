@@ -117,14 +117,18 @@ def cpu_baseline(x, target_s=10.0, max_runs=40):
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--skip-extras", action="store_true")
+    ap.add_argument("--op", default=WORKLOAD, choices=[WORKLOAD, "ag_gemm_8b", "gemm_rs_8b", "ag_moe"],
+                    help="profiling aid: launch only this operation (no benchmark record)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("this build runs on one GPU: the R peer ranks are stand-in buffers in that GPU's HBM; "
               "use --gpus 1", file=sys.stderr)
         return 2
+    if args.op != WORKLOAD:
+        return profile_op(args.op, args.steps, args.warmup)
 
     import numpy as np
     import torch
@@ -228,60 +232,101 @@ def main() -> int:
     return 0
 
 
+def op_setups(torch, ocg, workloads, upload):
+    """name -> (workload, setup()) where setup() returns (launch_fused(), extras)
+    for the other operations (fused launches with caller-owned buffers)."""
+    def ag8():
+        w = workloads.workload("ag_gemm_8b")
+        x = w.make()
+        chunks = [upload(a) for a in x.a_chunks]
+        b = upload(x.b)
+        ag = torch.empty((x.R * x.m, x.K), dtype=torch.bfloat16, device="cuda")
+        c = torch.empty((x.R * x.m, x.N), dtype=torch.bfloat16, device="cuda")
+        ws = ocg.Workspace(ocg.OP_AG_GEMM, x.R, x.m, x.K, x.N)
+
+        def launch(mode=0):
+            ocg.ag_gemm(chunks, b, 0, a_gathered=ag, c=c, workspace=ws, config=ocg.default_config(mode=mode))
+        return w, x, ws, launch
+
+    def rs8():
+        w = workloads.workload("gemm_rs_8b")
+        x = w.make()
+        a, b = upload(x.a), upload(x.b)
+        peers = [None] + [upload(x.peers[s]) for s in range(1, x.R)]
+        part = torch.empty((x.M, x.N), dtype=torch.bfloat16, device="cuda")
+        o = torch.empty((x.M // x.R, x.N), dtype=torch.bfloat16, device="cuda")
+        ws = ocg.Workspace(ocg.OP_GEMM_RS, x.R, x.M, x.K, x.N)
+
+        def launch(mode=0):
+            ocg.gemm_rs(a, b, peers, 0, partial=part, out=o, workspace=ws)
+        return w, x, ws, launch
+
+    def moe():
+        w = workloads.workload("ag_moe")
+        x = w.make()
+        chunks = [upload(a) for a in x.a_chunks]
+        lg = torch.from_numpy(x.logits).to("cuda")
+        wt = upload(x.w)
+        ws = ocg.Workspace(ocg.OP_AG_GROUPED_GEMM, x.R, x.m, x.K, x.N, x.E, x.topk)
+        outs = ocg.ag_grouped_gemm(chunks, lg, wt, x.topk, 0, workspace=ws)
+
+        def launch(mode=0):
+            ocg.ag_grouped_gemm(chunks, lg, wt, x.topk, 0, workspace=ws, outputs=outs)
+        return w, x, ws, launch
+
+    return {"ag_gemm_8b": ag8, "gemm_rs_8b": rs8, "ag_moe": moe}
+
+
 def other_ops(torch, np, ocg, workloads, upload, stream, n):
     out = {}
+    setups = op_setups(torch, ocg, workloads, upload)
     # 8B-class AG-GEMM share
-    w = workloads.workload("ag_gemm_8b")
-    x = w.make()
-    chunks = [upload(a) for a in x.a_chunks]
-    b = upload(x.b)
-    ag = torch.empty((x.R * x.m, x.K), dtype=torch.bfloat16, device="cuda")
-    c = torch.empty((x.R * x.m, x.N), dtype=torch.bfloat16, device="cuda")
-    ws = ocg.Workspace(ocg.OP_AG_GEMM, x.R, x.m, x.K, x.N)
-    times = {}
-    for label, mode in (("fused", 0), ("gemm", 1), ("copy", 2)):
-        cfg = ocg.default_config(mode=mode)
-        times[label] = median_ms(torch, lambda: ocg.ag_gemm(chunks, b, 0, a_gathered=ag, c=c, workspace=ws,
-                                                              config=cfg), n, stream)
+    w, x, ws, launch = setups["ag_gemm_8b"]()
+    times = {label: median_ms(torch, lambda: launch(mode), n, stream)
+             for label, mode in (("fused", 0), ("gemm", 1), ("copy", 2))}
     ws.check()
     out["ag_gemm_8b"] = {"t_fused_us": round(times["fused"] * 1e3, 2), "t_gemm_us": round(times["gemm"] * 1e3, 2),
                          "t_copy_us": round(times["copy"] * 1e3, 2),
                          "tflops": round(w.flops() / (times["fused"] * 1e-3) / 1e12, 2),
                          "e_max": round(max(times["gemm"], times["copy"]) / times["fused"], 4)}
-    del chunks, ag, c
+    del launch
     # GEMM-ReduceScatter share
-    w = workloads.workload("gemm_rs_8b")
-    x = w.make()
-    a, b = upload(x.a), upload(x.b)
-    peers = [None] + [upload(x.peers[s]) for s in range(1, x.R)]
-    part = torch.empty((x.M, x.N), dtype=torch.bfloat16, device="cuda")
-    o = torch.empty((x.M // x.R, x.N), dtype=torch.bfloat16, device="cuda")
-    ws = ocg.Workspace(ocg.OP_GEMM_RS, x.R, x.M, x.K, x.N)
-    t = median_ms(torch, lambda: ocg.gemm_rs(a, b, peers, 0, partial=part, out=o, workspace=ws), n, stream)
+    w, x, ws, launch = setups["gemm_rs_8b"]()
+    t = median_ms(torch, launch, n, stream)
     ws.check()
     blk_bytes = (x.M // x.R) * x.N * 2
     out["gemm_rs_8b"] = {"t_us": round(t * 1e3, 2), "tflops": round(w.flops() / (t * 1e-3) / 1e12, 2),
                          "reduce_bytes": 9 * blk_bytes}
-    del a, b, peers, part, o
+    del launch
     # AllGather + MoE grouped GEMM
-    w = workloads.workload("ag_moe")
-    x = w.make()
-    chunks = [upload(a) for a in x.a_chunks]
-    lg = torch.from_numpy(x.logits).to("cuda")
-    wt = upload(x.w)
-    ws = ocg.Workspace(ocg.OP_AG_GROUPED_GEMM, x.R, x.m, x.K, x.N, x.E, x.topk)
-    outs = {}
-    outs_first = ocg.ag_grouped_gemm(chunks, lg, wt, x.topk, 0, workspace=ws)
-    t = median_ms(torch, lambda: ocg.ag_grouped_gemm(chunks, lg, wt, x.topk, 0, workspace=ws,
-                                                      outputs=outs_first), n, stream)
+    w, x, ws, launch = setups["ag_moe"]()
+    t = median_ms(torch, launch, n, stream)
     ws.check()
     T = x.R * x.m
     hbm = x.E * x.K * x.N * 2 + 2 * 7 * x.m * x.K * 2 + T * x.K * 2 + T * x.topk * x.N * 2 + T * x.E * 4
     out["ag_moe"] = {"t_us": round(t * 1e3, 2), "tflops": round(w.flops() / (t * 1e-3) / 1e12, 2),
                      "hbm_gbs_algorithmic": round(hbm / (t * 1e-3) / 1e9, 1),
                      "hbm_frac": round(hbm / (t * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
-    del outs
     return out
+
+
+def profile_op(op, steps, warmup):
+    """Launch one of the other operations `warmup + steps` times (fused), for
+    kernel profiles; prints one summary line."""
+    import numpy as np
+    import torch
+    import communication_overlapped_gemm_amd as ocg
+    import workloads
+
+    def upload(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to("cuda")
+    w, x, ws, launch = op_setups(torch, ocg, workloads, upload)[op]()
+    for _ in range(warmup + steps):
+        launch()
+    torch.cuda.synchronize()
+    ws.check()
+    print(json.dumps({"profile_op": op, "launches": warmup + steps}), flush=True)
+    return 0
 
 
 if __name__ == "__main__":
