@@ -24,7 +24,6 @@ import hashlib
 import json
 import os
 import statistics
-import subprocess
 import sys
 import time
 
@@ -75,17 +74,6 @@ def median_ms(torch, fn, n, stream, warm=2):
     for _ in range(warm):
         fn()
     return statistics.median(timed_launches(torch, fn, n, stream))
-
-
-def gpu_clock_mhz():
-    try:
-        out = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=20).stdout
-        for line in out.splitlines():
-            if "sclk" in line and "Mhz" in line:
-                return float(line.split("(")[-1].split("Mhz")[0])
-    except Exception:
-        pass
-    return None
 
 
 def cpu_baseline(x, target_s=10.0, max_runs=40):
@@ -223,10 +211,6 @@ def main() -> int:
         }
         del full
         rec["ops"] = other_ops(torch, np, ocg, workloads, upload, stream, n)
-        clk = gpu_clock_mhz()
-        if clk:
-            rec["sclk_mhz"] = clk
-            rec["pct_peak_clock_adjusted"] = round(100.0 * value / (PEAK_BF16_TFLOPS * clk / 2400.0), 2)
         rec["cpu_baseline"] = cpu_baseline(x)
     print(json.dumps(rec), flush=True)
     return 0
