@@ -20,9 +20,6 @@ SOURCES = ["kernels.hip", "api.cpp"]
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    # MFMA results stay in VGPRs: the bf16 epilogue reads the accumulators
-    # directly instead of copying them out of AGPRs through scratch.
-    "-mllvm", "--amdgpu-mfma-vgpr-form=true",
     "-Wall", "-Wno-unused-function", "-Wno-unknown-pragmas",
     # m0 is listed as clobbered by the direct-to-LDS load asm; the compiler
     # warns because m0 is reserved, and uses m0 nowhere else in these kernels.

@@ -1,8 +1,11 @@
 // bf16 MFMA tile engine for gfx950 (one workgroup = 4 waves, one tile).
 //
-// Tile BM x BN, K consumed in stages of 32. The four waves are stacked along
-// M: wave w owns rows [w*BM/4, (w+1)*BM/4) and every column, computed with
-// v_mfma_f32_32x32x16_bf16 (one 32x32 accumulator per (32-row, 32-col) block).
+// Tile BM x BN, K consumed in stages of 32. The four waves form a 2 x 2 grid:
+// wave w = 2*wm + wn owns rows [wm*BM/2, +BM/2) and columns [wn*BN/2, +BN/2),
+// computed with v_mfma_f32_16x16x32_bf16 (one 16x16 accumulator per (16-row,
+// 16-col) block; one MFMA covers the whole 32-deep stage). Compared with four
+// waves stacked along M, every wave reads half of B instead of all of it, which
+// halves the transposing LDS reads (the slowest LDS read form on gfx950).
 //
 // Stage s of the K loop lives in slot s % S of an S-slot LDS ring (S = 4..6):
 //   A part [BM][32] bf16, 64-byte rows; the 16-byte chunk c of row r is stored
@@ -15,16 +18,17 @@
 // A rows, buffer_load_dwordx4 ... lds for B with out-of-range reads returning
 // zero), S-1 stages ahead. They are issued from inline assembly so the
 // compiler does not add its own whole-queue waits before every LDS read; the
-// explicit vmcnt waits plus one barrier per stage order them. Every wave
-// issues the same number of loads per stage, so the waits are constants and
-// the K loop has no branches. With one wave per SIMD an instruction only overlaps a 32-cycle
-// MFMA if it sits between MFMAs in program order, so the fragment reads of
-// stage k+1 and the loads of stage k+S-1 are interleaved with stage k's MFMAs.
+// explicit vmcnt waits plus one barrier per pair of stages order them. Every
+// wave issues the same number of loads per stage, so the waits are constants
+// and the K loop has no branches. With one wave per SIMD an instruction only
+// overlaps an MFMA if it sits between MFMAs in program order, so the fragment
+// reads of stage k+1 and the loads of stage k+S-1 are interleaved with stage
+// k's MFMAs.
 //
 // The MFMA's A operand carries B (rows = n) and its B operand carries A
 // (columns = m), so each lane ends with 4 consecutive output columns of one
-// row: acc[f][g][4*q + r] = C[m = w*BM/4 + 32f + (lane & 31)]
-//                          [n = 32g + 8q + 4*(lane >> 5) + r].
+// row: acc.v[f][g][r] = C[m = wm*BM/2 + 16f + (lane & 15)]
+//                        [n = wn*BN/2 + 16g + 4*(lane >> 4) + r].
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -35,7 +39,7 @@ namespace ocg {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 #define OCG_LDS __attribute__((address_space(3)))
@@ -44,8 +48,8 @@ constexpr int BKS = 32;   // K per stage
 
 template <int BM, int BN>
 struct Gemm {
-  static constexpr int WM = BM / 4;                 // rows per wave
-  static constexpr int FM = WM / 32, FN = BN / 32;  // 32x32 blocks per wave
+  static constexpr int WM = BM / 2, WN = BN / 2;    // rows / columns per wave
+  static constexpr int FM = WM / 16, FN = WN / 16;  // 16x16 blocks per wave
   static constexpr int A_BYTES = BM * BKS * 2;
   static constexpr int B_BYTES = BN * BKS * 2;
   static constexpr int STAGE = A_BYTES + B_BYTES;
@@ -61,11 +65,17 @@ struct Gemm {
   static constexpr int RING = S * STAGE;
   static constexpr int LD_C = BN + 8;               // epilogue staging row (elements)
   static constexpr int LDS_BYTES = (RING > BM * LD_C * 2) ? RING : BM * LD_C * 2;
-  static_assert(WM % 32 == 0 && BN % 32 == 0, "whole 32x32 blocks per wave");
+  static_assert(WM % 16 == 0 && WN % 16 == 0 && BN % 32 == 0, "whole 16x16 blocks per wave, 32-column B blocks");
   static_assert(A_INST % 4 == 0, "A DMA instructions split evenly over the waves");
-  static_assert(NDMA <= 2 * FN, "every load of a stage has an MFMA group to sit behind");
+  static_assert(NDMA <= 2 * FN, "at most two loads behind each MFMA group");
   static_assert(S >= 4 && (S - 2) * NDMA <= 63, "vmcnt waits fit the 6-bit counter");
   static_assert(LDS_BYTES <= 160 * 1024 - 64, "fits the 160 KiB LDS of a gfx950 CU");
+};
+
+// fp32 accumulators of one wave's part of the tile.
+template <int BM, int BN>
+struct AccTile {
+  f32x4_t v[Gemm<BM, BN>::FM][Gemm<BM, BN>::FN];
 };
 
 __device__ __forceinline__ int swz_a(int r) { return ((r >> 1) & 3) ^ ((r >> 3) & 1); }
@@ -92,8 +102,8 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 
 template <int BM, int BN>
 struct Frags {
-  bf16x8_t a[Gemm<BM, BN>::FM][2];   // [32-row block][k16 half]
-  bf16x8_t b[Gemm<BM, BN>::FN][2];   // [32-col block][k16 half]
+  bf16x8_t a[Gemm<BM, BN>::FM];   // [16-row block]: 8 k of row (lane & 15), k group lane >> 4
+  bf16x8_t b[Gemm<BM, BN>::FN];   // [16-col block]: 8 k of column (lane & 15), k group lane >> 4
 };
 
 template <int BM, int BN>
@@ -171,42 +181,47 @@ __device__ __forceinline__ void dma_stage(uint32_t slot, const DmaPlan<BM, BN>& 
 }
 
 struct FragAddr {
-  uint32_t a0, a1;   // A block f=0 for k16 half 0 / 1 (block f adds f*2048)
-  uint32_t b;        // B block g, half ks, rows lo/hi: + g*2048 + ks*1024 + hi*256
+  uint32_t a;        // A block f = 0 (block f adds f*1024: 16 rows of 64 bytes)
+  uint32_t b[2];     // B block g, low 4 k rows: b[g & 1] + (g >> 1)*2048; high 4 rows +256
 };
 
+// Per-lane LDS byte offsets (within a slot) of this wave's fragments. Lane
+// l = 16q + j reads A row wm*BM/2 + j, k chunk q (8 k), and, for the 16-column
+// block c, the transposing reads of k rows 8q + j/4 (+4), columns 4(j & 3)..+3
+// of the block, which leave column j, k rows 8q..8q+3 (+4..7) in lane l.
 template <int BM, int BN>
 __device__ __forceinline__ FragAddr frag_addr(int wave) {
   using G = Gemm<BM, BN>;
   const int lane = threadIdx.x & 63;
-  FragAddr fa;
-  const int r = wave * G::WM + (lane & 31);
-  const int h = lane >> 5, s = swz_a(r);
-  fa.a0 = r * 64 + ((h ^ s) * 16);
-  fa.a1 = r * 64 + (((2 | h) ^ s) * 16);
+  const int wm = wave >> 1, wn = wave & 1;
   const int q = lane >> 4, j = lane & 15;
-  const int kk = 8 * (q >> 1) + (j >> 2);
-  fa.b = G::A_BYTES + kk * 64 + (((q & 1) ^ swz_b(kk)) * 32) + (j & 3) * 8;
+  FragAddr fa;
+  const int r = wm * G::WM + j;
+  fa.a = r * 64 + ((q ^ swz_a(r)) * 16);
+  const int kk = 8 * q + (j >> 2);
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int c = wn * G::FN + t;   // 16-column block of g = t
+    fa.b[t] = G::A_BYTES + (c >> 1) * 2048 + kk * 64 + (((c & 1) ^ swz_b(kk)) * 32) + (j & 3) * 8;
+  }
   return fa;
+}
+
+template <int BM, int BN>
+__device__ __forceinline__ bf16x8_t read_b_frag(OCG_LDS const char* st, const FragAddr& fa, int g) {
+  OCG_LDS const char* p = st + fa.b[g & 1] + (g >> 1) * 2048;
+  bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((OCG_LDS bf16x4_t*)p);
+  bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((OCG_LDS bf16x4_t*)(p + 256));
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
 template <int BM, int BN>
 __device__ __forceinline__ void read_frags(OCG_LDS const char* st, const FragAddr& fa, Frags<BM, BN>& fr) {
   using G = Gemm<BM, BN>;
 #pragma unroll
-  for (int ks = 0; ks < 2; ++ks)
+  for (int g = 0; g < G::FN; ++g) fr.b[g] = read_b_frag<BM, BN>(st, fa, g);
 #pragma unroll
-    for (int g = 0; g < G::FN; ++g) {
-      bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((OCG_LDS bf16x4_t*)(st + fa.b + g * 2048 + ks * 1024));
-      bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-          (OCG_LDS bf16x4_t*)(st + fa.b + g * 2048 + ks * 1024 + 256));
-      fr.b[g][ks] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-    }
-#pragma unroll
-  for (int f = 0; f < G::FM; ++f) {
-    fr.a[f][0] = *(OCG_LDS const bf16x8_t*)(st + fa.a0 + f * 2048);
-    fr.a[f][1] = *(OCG_LDS const bf16x8_t*)(st + fa.a1 + f * 2048);
-  }
+  for (int f = 0; f < G::FM; ++f) fr.a[f] = *(OCG_LDS const bf16x8_t*)(st + fa.a + f * 1024);
 }
 
 // s_waitcnt lgkmcnt(0) with vmcnt and expcnt left open (gfx9 encoding), as a
@@ -218,29 +233,33 @@ __device__ __forceinline__ void lds_reads_done() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// MFMA group G (k half G / FN, column block G % FN) of `cur`, preceded by the
-// two transposing reads of the same block of `nxt`; the NDMA loads of stage
-// `s` are spread evenly over the 2*FN groups (load I after group I*2FN/NDMA),
-// which keeps the per-CU memory pipe from queueing up behind a burst.
+// The loads I of stage `s` with I * FN / NDMA == GI (spread evenly over the
+// FN MFMA groups, which keeps the per-CU memory pipe from queueing up behind
+// a burst).
+template <int BM, int BN, int GI, int I = 0>
+__device__ __forceinline__ void dma_after_group(uint32_t slot, const DmaPlan<BM, BN>& d,
+                                                const __amdgpu_buffer_rsrc_t& brs, int s, int wave) {
+  using G = Gemm<BM, BN>;
+  if constexpr (I < G::NDMA) {
+    if constexpr ((I * G::FN) / G::NDMA == GI) dma_one<BM, BN, I>(slot, d, brs, s, wave);
+    dma_after_group<BM, BN, GI, I + 1>(slot, d, brs, s, wave);
+  }
+}
+
+// MFMA group GI (column block GI) of `cur`, preceded by the two transposing
+// reads of the same block of `nxt` and followed by its share of the loads.
 template <int BM, int BN, int GI = 0>
 __device__ __forceinline__ void mfma_groups(const Frags<BM, BN>& cur, Frags<BM, BN>& nxt, OCG_LDS const char* st,
-                                            const FragAddr& fa,
-                                            f32x16_t (&acc)[Gemm<BM, BN>::FM][Gemm<BM, BN>::FN],
-                                            uint32_t slot, const DmaPlan<BM, BN>& d,
-                                            const __amdgpu_buffer_rsrc_t& brs, int s, int wave) {
+                                            const FragAddr& fa, AccTile<BM, BN>& acc, uint32_t slot,
+                                            const DmaPlan<BM, BN>& d, const __amdgpu_buffer_rsrc_t& brs, int s,
+                                            int wave) {
   using G = Gemm<BM, BN>;
-  if constexpr (GI < 2 * G::FN) {
-    constexpr int ks = GI / G::FN, g = GI % G::FN;
-    bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((OCG_LDS bf16x4_t*)(st + fa.b + g * 2048 + ks * 1024));
-    bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-        (OCG_LDS bf16x4_t*)(st + fa.b + g * 2048 + ks * 1024 + 256));
-    nxt.b[g][ks] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  if constexpr (GI < G::FN) {
+    nxt.b[GI] = read_b_frag<BM, BN>(st, fa, GI);
 #pragma unroll
     for (int f = 0; f < G::FM; ++f)
-      acc[f][g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur.b[g][ks], cur.a[f][ks], acc[f][g], 0, 0, 0);
-    // loads spread evenly over the groups: load I follows group I*2FN/NDMA
-    constexpr int I = (GI * G::NDMA + 2 * G::FN - 1) / (2 * G::FN);   // ceil
-    if constexpr (I < G::NDMA && (I * 2 * G::FN) / G::NDMA == GI) dma_one<BM, BN, I>(slot, d, brs, s, wave);
+      acc.v[f][GI] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur.b[GI], cur.a[f], acc.v[f][GI], 0, 0, 0);
+    dma_after_group<BM, BN, GI>(slot, d, brs, s, wave);
     __builtin_amdgcn_sched_barrier(0);
     mfma_groups<BM, BN, GI + 1>(cur, nxt, st, fa, acc, slot, d, brs, s, wave);
   }
@@ -251,16 +270,12 @@ __device__ __forceinline__ void mfma_groups(const Frags<BM, BN>& cur, Frags<BM, 
 // them. No MFMA depends on a read issued in the same stage.
 template <int BM, int BN>
 __device__ __forceinline__ void stage_body(const Frags<BM, BN>& cur, Frags<BM, BN>& nxt, OCG_LDS const char* st,
-                                           const FragAddr& fa,
-                                           f32x16_t (&acc)[Gemm<BM, BN>::FM][Gemm<BM, BN>::FN],
-                                           uint32_t slot, const DmaPlan<BM, BN>& d,
-                                           const __amdgpu_buffer_rsrc_t& brs, int s, int wave) {
+                                           const FragAddr& fa, AccTile<BM, BN>& acc, uint32_t slot,
+                                           const DmaPlan<BM, BN>& d, const __amdgpu_buffer_rsrc_t& brs, int s,
+                                           int wave) {
   using G = Gemm<BM, BN>;
 #pragma unroll
-  for (int f = 0; f < G::FM; ++f) {
-    nxt.a[f][0] = *(OCG_LDS const bf16x8_t*)(st + fa.a0 + f * 2048);
-    nxt.a[f][1] = *(OCG_LDS const bf16x8_t*)(st + fa.a1 + f * 2048);
-  }
+  for (int f = 0; f < G::FM; ++f) nxt.a[f] = *(OCG_LDS const bf16x8_t*)(st + fa.a + f * 1024);
   mfma_groups<BM, BN>(cur, nxt, st, fa, acc, slot, d, brs, s, wave);
   // The reads of `nxt` had the whole MFMA block to land.
   lds_reads_done();
@@ -280,8 +295,7 @@ __device__ __forceinline__ void stage_body(const Frags<BM, BN>& cur, Frags<BM, B
 // are constants; in the last step the fragment reads fetch a stale slot whose
 // values are never used.
 template <int BM, int BN>
-__device__ __forceinline__ void mainloop(OCG_LDS char* smem, const TileCtx<BM, BN>& t,
-                                         f32x16_t (&acc)[Gemm<BM, BN>::FM][Gemm<BM, BN>::FN]) {
+__device__ __forceinline__ void mainloop(OCG_LDS char* smem, const TileCtx<BM, BN>& t, AccTile<BM, BN>& acc) {
   using G = Gemm<BM, BN>;
   constexpr int S = G::S;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -292,7 +306,7 @@ __device__ __forceinline__ void mainloop(OCG_LDS char* smem, const TileCtx<BM, B
 #pragma unroll
   for (int f = 0; f < G::FM; ++f)
 #pragma unroll
-    for (int g = 0; g < G::FN; ++g) acc[f][g] = f32x16_t{};
+    for (int g = 0; g < G::FN; ++g) acc.v[f][g] = f32x4_t{};
   // prologue: stages 0 .. S-2 (repeating stage nk-1 past the end)
 #pragma unroll
   for (int j = 0; j < S - 1; ++j) dma_stage<BM, BN>(base + j * G::STAGE, d, t.brs, j < nk ? j : nk - 1, wave);
@@ -325,24 +339,21 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 // Round the tile to bf16 (nearest-even, v_cvt_pk_bf16_f32) and stage it in
 // LDS as [BM][BN + 8]; ends with a barrier.
 template <int BM, int BN>
-__device__ __forceinline__ void stage_c(OCG_LDS char* smem, const f32x16_t (&acc)[Gemm<BM, BN>::FM][Gemm<BM, BN>::FN]) {
+__device__ __forceinline__ void stage_c(OCG_LDS char* smem, const AccTile<BM, BN>& acc) {
   using G = Gemm<BM, BN>;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
   OCG_LDS uint16_t* cst = (OCG_LDS uint16_t*)smem;
 #pragma unroll
   for (int f = 0; f < G::FM; ++f) {
-    const int row = wave * G::WM + 32 * f + (lane & 31);
+    const int row = wm * G::WM + 16 * f + (lane & 15);
 #pragma unroll
     for (int g = 0; g < G::FN; ++g) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int col = 32 * g + 8 * q + 4 * (lane >> 5);
-        u32x2_t v = {pack_bf16x2(acc[f][g][4 * q + 0], acc[f][g][4 * q + 1]),
-                     pack_bf16x2(acc[f][g][4 * q + 2], acc[f][g][4 * q + 3])};
-        *(OCG_LDS u32x2_t*)(cst + row * G::LD_C + col) = v;
-      }
-      __builtin_amdgcn_sched_barrier(0);
+      const int col = wn * G::WN + 16 * g + 4 * (lane >> 4);
+      u32x2_t v = {pack_bf16x2(acc.v[f][g][0], acc.v[f][g][1]), pack_bf16x2(acc.v[f][g][2], acc.v[f][g][3])};
+      *(OCG_LDS u32x2_t*)(cst + row * G::LD_C + col) = v;
     }
+    __builtin_amdgcn_sched_barrier(0);
   }
   __syncthreads();
 }

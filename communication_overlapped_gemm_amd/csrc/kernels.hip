@@ -277,7 +277,7 @@ __global__ __launch_bounds__(kThreads, 1) void ag_gemm_kernel(AgArgs args) {
     }
     const int n0 = cb * BN;
     t.n0 = n0;
-    f32x16_t acc[G::FM][G::FN];
+    AccTile<BM, BN> acc;
     mainloop<BM, BN>(smem, t, acc);
     stage_c<BM, BN>(smem, acc);
     for_each_c_chunk<BM, BN>(smem, [&](int row, int col, u32x4_t val) {
@@ -366,7 +366,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_rs_kernel(RsArgs args) {
     }
     const int n0 = cb * BN;
     t.n0 = n0;
-    f32x16_t acc[G::FM][G::FN];
+    AccTile<BM, BN> acc;
     mainloop<BM, BN>(smem, t, acc);
     stage_c<BM, BN>(smem, acc);
     // The bf16 partial tile (the send buffer) is consumed by reduce strips of
@@ -637,7 +637,7 @@ __global__ __launch_bounds__(kThreads, 1) void moe_gemm_kernel(MoeArgs args) {
     t.brs = make_rsrc(args.w + (size_t)e * wstride, (uint32_t)(wstride * 2));
     const int n0 = cb * BN;
     t.n0 = n0;
-    f32x16_t acc[G::FM][G::FN];
+    AccTile<BM, BN> acc;
     mainloop<BM, BN>(smem, t, acc);
     stage_c<BM, BN>(smem, acc);
     // local scatter: row rr of the tile is token-slot perm[r0 + rr]
