@@ -72,7 +72,7 @@ bool shape_ok(int R, int64_t m, int64_t K, int64_t N) {
 // Estimated cost of a tile preset: rounds of the persistent grid times the
 // tile area, derated for the smaller wave tiles.
 int choose_tile(int64_t M, int64_t N, int cus) {
-  static const double eff[OCG_TILE_COUNT] = {1.0, 0.9, 0.92, 0.75};
+  static const double eff[OCG_TILE_COUNT] = {1.0, 0.9, 0.92, 0.75, 0.9};
   int best = OCG_TILE_128x128;
   double best_cost = 1e300;
   for (int t = 0; t < OCG_TILE_COUNT; ++t) {

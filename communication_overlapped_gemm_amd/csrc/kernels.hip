@@ -50,24 +50,43 @@ __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as
 
 // ---------------------------------------------------------------- flags
 
-// consume_tile_wait: bounded relaxed poll, then one acquire fence.
-__device__ bool wait_flag(const uint32_t* flag, uint32_t want, const Common& cm, uint32_t* seen) {
-  uint64_t t0 = now_ticks();
-  uint32_t v = __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  bool ok = true;
-  while (v != want) {
-    if (now_ticks() - t0 > cm.timeout_ticks) {
-      ok = false;
-      break;
+// consume_tile_wait over all the flags a task depends on, run by one whole
+// wave: the k-th flag the task enumerates is polled by lane k % 64 (relaxed
+// loads, bounded by the timeout), so the flags are read in parallel, and one
+// acquire fence after the polls covers every one of them (an agent-scope
+// acquire invalidates the non-coherent cache lines, which costs about a
+// microsecond, too much to pay per flag). A timed-out wait sets the error
+// word and proceeds, so the grid always drains.
+struct FlagWait {
+  uint64_t t0, timeout;
+  int k, lane;
+  bool ok;
+  uint32_t seen;
+  __device__ explicit FlagWait(uint64_t timeout_ticks)
+      : t0(now_ticks()), timeout(timeout_ticks), k(0), lane(threadIdx.x & 63), ok(true), seen(0) {}
+  // The next flag the task depends on, and the value that means "ready".
+  __device__ void operator()(const uint32_t* flag, uint32_t want) {
+    if ((k++ & 63) != lane) return;
+    uint32_t v = __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    while (v != want && ok) {
+      if (now_ticks() - t0 > timeout) {
+        ok = false;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+      v = __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    __builtin_amdgcn_s_sleep(1);
-    v = __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    seen = v;
   }
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  if (!ok) __hip_atomic_fetch_or(&cm.hdr->error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  *seen = v;
-  return ok;
-}
+  // After the last flag: the fence and the error word; returns the number of
+  // flags and (in *seen_out) a value lane 0 observed.
+  __device__ int finish(const Common& cm, uint32_t* seen_out) {
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    if (!ok) __hip_atomic_fetch_or(&cm.hdr->error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *seen_out = __shfl(seen, 0);
+    return k;
+  }
+};
 
 // Wait until every store this thread issued has completed (for the
 // agent-coherent stores below: is visible at agent scope).
@@ -259,10 +278,10 @@ __global__ __launch_bounds__(kThreads, 1) void ag_gemm_kernel(AgArgs args) {
     const int r0 = rb * BM, r1 = min(r0 + BM, p.M);
     int nwait = 0;
     uint32_t seen = 0;
-    if (p.mode == 0 && threadIdx.x == 0) {
-      nwait = for_each_dep_slab(p.m, p.S, p.bpr, p.local, r0, r1, [&](int s) {
-        wait_flag(&args.slab_flag[s], epoch, cm, &seen);
-      });
+    if (p.mode == 0 && wave == 0) {
+      FlagWait w(cm.timeout_ticks);
+      for_each_dep_slab(p.m, p.S, p.bpr, p.local, r0, r1, [&](int s) { w(&args.slab_flag[s], epoch); });
+      nwait = w.finish(cm, &seen);
     }
     const uint64_t t1 = now_ticks();
     __syncthreads();
@@ -395,21 +414,19 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_rs_kernel(RsArgs args) {
     rs_strip(p, (int)j, &r0, &r1);
     uint32_t seen = 0;
     int nwait = 0;
-    if (threadIdx.x == 0) {
+    if (wave == 0) {
+      FlagWait w(cm.timeout_ticks);
       for (int rb = r0 / BM; rb <= (r1 - 1) / BM; ++rb)
         for (int cb = 0; cb < p.n_cb; ++cb) {
-          wait_flag(&args.tile_flag[rb * p.n_cb + cb], epoch, cm, &seen);
-          ++nwait;
+          w(&args.tile_flag[rb * p.n_cb + cb], epoch);
           if (args.peer_flags) {
             const int t_local = (rb - args.local_rb0) * p.n_cb + cb;
             const int per_rank = args.local_nrb * p.n_cb;
-            for (int s = 0; s < p.R; ++s) {
-              if (s == p.local) continue;
-              wait_flag(&args.peer_flags[s * per_rank + t_local], args.peer_flag_value, cm, &seen);
-              ++nwait;
-            }
+            for (int s = 0; s < p.R; ++s)
+              if (s != p.local) w(&args.peer_flags[s * per_rank + t_local], args.peer_flag_value);
           }
         }
+      nwait = w.finish(cm, &seen);
     }
     const uint64_t t1 = now_ticks();
     __syncthreads();
@@ -612,17 +629,16 @@ __global__ __launch_bounds__(kThreads, 1) void moe_gemm_kernel(MoeArgs args) {
     const int e = L[0], r0 = L[1], nrows = L[2], cb = L[3];
     uint32_t seen = 0;
     int nwait = 0;
-    if (p.mode == 0 && threadIdx.x == 0) {
+    if (p.mode == 0 && wave == 0) {
       // consume_tile_wait on every non-local slab between the slabs of the
       // tile's first and last token (tokens ascend within an expert)
       const int tf = args.perm[r0] / args.topk, tl = args.perm[r0 + nrows - 1] / args.topk;
       const int s_lo = (tf / p.m) * p.bpr + (tf % p.m) / p.S;
       const int s_hi = (tl / p.m) * p.bpr + (tl % p.m) / p.S;
-      for (int s = s_lo; s <= s_hi; ++s) {
-        if (s / p.bpr == p.local) continue;
-        wait_flag(&args.slab_flag[s], epoch, cm, &seen);
-        ++nwait;
-      }
+      FlagWait w(cm.timeout_ticks);
+      for (int s = s_lo; s <= s_hi; ++s)
+        if (s / p.bpr != p.local) w(&args.slab_flag[s], epoch);
+      nwait = w.finish(cm, &seen);
     }
     const uint64_t t1 = now_ticks();
     __syncthreads();
@@ -685,6 +701,7 @@ hipError_t launch_ag_gemm(const AgArgs& a, int tile, int grid, hipStream_t s) {
     case OCG_TILE_128x224: return ag_launch<128, 224>(a, grid, s);
     case OCG_TILE_128x256: return ag_launch<128, 256>(a, grid, s);
     case OCG_TILE_128x128: return ag_launch<128, 128>(a, grid, s);
+    case OCG_TILE_256x256: return ag_launch<256, 256>(a, grid, s);
   }
   return hipErrorInvalidValue;
 }
@@ -695,6 +712,7 @@ hipError_t launch_gemm_rs(const RsArgs& a, int tile, int grid, hipStream_t s) {
     case OCG_TILE_128x224: return rs_launch<128, 224>(a, grid, s);
     case OCG_TILE_128x256: return rs_launch<128, 256>(a, grid, s);
     case OCG_TILE_128x128: return rs_launch<128, 128>(a, grid, s);
+    case OCG_TILE_256x256: return rs_launch<256, 256>(a, grid, s);
   }
   return hipErrorInvalidValue;
 }
@@ -738,6 +756,7 @@ int resident_per_cu(int op, int tile) {
       case OCG_TILE_128x224: return occ(ag_gemm_kernel<128, 224>);
       case OCG_TILE_128x256: return occ(ag_gemm_kernel<128, 256>);
       case OCG_TILE_128x128: return occ(ag_gemm_kernel<128, 128>);
+      case OCG_TILE_256x256: return occ(ag_gemm_kernel<256, 256>);
     }
   } else {
     switch (tile) {
@@ -745,6 +764,7 @@ int resident_per_cu(int op, int tile) {
       case OCG_TILE_128x224: return occ(gemm_rs_kernel<128, 224>);
       case OCG_TILE_128x256: return occ(gemm_rs_kernel<128, 256>);
       case OCG_TILE_128x128: return occ(gemm_rs_kernel<128, 128>);
+      case OCG_TILE_256x256: return occ(gemm_rs_kernel<256, 256>);
     }
   }
   return 1;

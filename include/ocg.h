@@ -67,7 +67,8 @@ extern "C" {
 #define OCG_TILE_128x224 1
 #define OCG_TILE_128x256 2
 #define OCG_TILE_128x128 3
-#define OCG_TILE_COUNT 4
+#define OCG_TILE_256x256 4
+#define OCG_TILE_COUNT 5
 
 /* Trace record written per executed task when ocg_config.trace is set
  * (64 bytes), at slot: AG-GEMM / MoE copy task u -> u, tile v -> n_copy + v;

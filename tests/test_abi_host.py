@@ -89,6 +89,7 @@ AG_CASES = [
     (3, 100, 64, 72, 1, ocg.TILE_128x128),
     (5, 37, 128, 40, 4, ocg.TILE_128x128),
     (3, 300, 192, 520, 2, ocg.TILE_256x224),
+    (3, 300, 256, 600, 1, ocg.TILE_256x256),
 ]
 
 

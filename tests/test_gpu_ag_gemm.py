@@ -34,6 +34,7 @@ SMALL = [
     ("r2_128x256", 2, 256, 512, 264, 1, 2, "uniform"),
     ("r1_128x224", 1, 200, 128, 232, 0, 1, "uniform"),
     ("r8_128x224", 8, 96, 320, 448, 6, 1, "normal"),
+    ("ragged_256x256", 3, 300, 256, 600, 1, 4, "uniform"),
 ]
 
 

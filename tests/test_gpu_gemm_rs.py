@@ -40,6 +40,7 @@ SMALL = [
     ("r8_l0", 8, 1024, 256, 512, 0, -1),
     ("r8_l5", 8, 1024, 256, 512, 5, -1),
     ("r2_128x256", 2, 512, 192, 264, 1, 2),
+    ("r4_256x256", 4, 1024, 192, 600, 3, 4),
 ]
 
 
