@@ -24,7 +24,7 @@ ERR_NO_DEVICE = -6
 
 OP_AG_GEMM, OP_GEMM_RS, OP_AG_GROUPED_GEMM = 0, 1, 2
 MODE_FUSED, MODE_GEMM_ONLY, MODE_COPY_ONLY = 0, 1, 2
-TILE_AUTO, TILE_256x224, TILE_128x224, TILE_128x256, TILE_128x128, TILE_256x256 = -1, 0, 1, 2, 3, 4
+TILE_AUTO, TILE_256x224, TILE_128x224, TILE_128x256, TILE_128x128, TILE_256x256, TILE_320x224 = -1, 0, 1, 2, 3, 4, 5
 
 EXPORTS = [
     "ocg_config_default", "ocg_create", "ocg_destroy", "ocg_workspace_bytes",
@@ -76,7 +76,7 @@ def _declare(lib):
         "ocg_check": (C.c_int, [_P, _P]),
         "ocg_status_string": (C.c_char_p, [C.c_int]),
         "ocg_plan_info": (C.c_int, [C.c_int, C.c_int, C.c_int, C.c_int64, C.c_int64, C.c_int64,
-                                    C.POINTER(Config), I64x8]),
+                                    C.c_int, C.c_int, C.POINTER(Config), I64x8]),
         "ocg_plan_task": (C.c_int, [C.c_int, C.c_int, C.c_int, C.c_int64, C.c_int64, C.c_int64,
                                     C.POINTER(Config), C.c_int64, I64x8]),
     }

@@ -2,6 +2,7 @@
 // and launches. Every entry point returns an OCG_* status and enqueues
 // nothing when it returns an error.
 #include <hip/hip_runtime.h>
+#include <math.h>
 #include <stdint.h>
 #include <string.h>
 
@@ -72,10 +73,11 @@ bool shape_ok(int R, int64_t m, int64_t K, int64_t N) {
 // Estimated cost of a tile preset: rounds of the persistent grid times the
 // tile area, derated for the smaller wave tiles.
 int choose_tile(int64_t M, int64_t N, int cus) {
-  static const double eff[OCG_TILE_COUNT] = {1.0, 0.9, 0.92, 0.75, 0.9};
+  static const double eff[OCG_TILE_COUNT] = {1.0, 0.9, 0.92, 0.75, 0.9, 0.0};
   int best = OCG_TILE_128x128;
   double best_cost = 1e300;
   for (int t = 0; t < OCG_TILE_COUNT; ++t) {
+    if (eff[t] <= 0) continue;   // grouped-GEMM-only preset
     int64_t tiles = cdiv((int)M, tile_bm(t)) * (int64_t)cdiv((int)N, tile_bn(t));
     int64_t rounds = (tiles + cus - 1) / cus;
     double cost = (double)rounds * tile_bm(t) * tile_bn(t) / eff[t];
@@ -87,18 +89,34 @@ int choose_tile(int64_t M, int64_t N, int cus) {
   return best;
 }
 
+// Grouped GEMM: one row tile per expert where the rows an expert gets
+// (T*topk/E on average, plus three standard deviations of the count) fit in
+// a preset, the smallest such; 256-row tiles when experts are larger. A
+// second row tile for the few rows past a tile boundary would cost as much
+// as a full one.
+int choose_moe_tile(int64_t T, int E, int topk) {
+  if (E < 1) return OCG_TILE_256x224;
+  const double avg = (double)T * topk / E;
+  const double hi = avg + 3.0 * sqrt(avg) + 1.0;
+  if (hi <= 128) return OCG_TILE_128x224;
+  if (hi <= 256) return OCG_TILE_256x224;
+  if (hi <= 320) return OCG_TILE_320x224;
+  return OCG_TILE_256x224;
+}
+
 struct Resolved {
   int tile, BM, BN, S, CT;
 };
 
-int resolve(int op, int R, int64_t m, int64_t K, int64_t N, const ocg_config& c, int cus, Resolved* r) {
+int resolve(int op, int R, int64_t m, int64_t K, int64_t N, int E, int topk, const ocg_config& c, int cus,
+            Resolved* r) {
   int64_t M = (op == OCG_OP_GEMM_RS) ? m : R * m;
   if (op == OCG_OP_AG_GROUPED_GEMM)
-    r->tile = c.tile < 0 ? kMoeTile : c.tile;
+    r->tile = c.tile < 0 ? choose_moe_tile(M, E, topk) : c.tile;
   else
     r->tile = c.tile < 0 ? choose_tile(M, N, cus) : c.tile;
   if (r->tile < 0 || r->tile >= OCG_TILE_COUNT) return OCG_ERR_INVALID_ARG;
-  if (op == OCG_OP_AG_GROUPED_GEMM && r->tile != kMoeTile && r->tile != kMoeTileSmall) return OCG_ERR_INVALID_ARG;
+  if (op == OCG_OP_AG_GROUPED_GEMM ? !moe_tile_ok(r->tile) : r->tile == OCG_TILE_320x224) return OCG_ERR_INVALID_ARG;
   r->BM = tile_bm(r->tile);
   r->BN = tile_bn(r->tile);
   r->S = c.slab_rows > 0 ? c.slab_rows : r->BM;
@@ -118,8 +136,12 @@ int resolve(int op, int R, int64_t m, int64_t K, int64_t N, const ocg_config& c,
   return OCG_OK;
 }
 
-int reduce_rows(int64_t N) {
-  int64_t rr = (32 * 1024) / (2 * N);  // ~32 KiB of each partial per strip
+// Rows per reduce strip: at most ~32 KiB of each partial, and few enough
+// that every CU gets a strip (the strips run once the tiles are done).
+int reduce_rows(int64_t M, int R, int64_t N, int cus) {
+  int64_t rr = (32 * 1024) / (2 * N);
+  const int64_t spread = (M / R) / (cus > 0 ? cus : 1);
+  if (spread < rr) rr = spread;
   return rr < 1 ? 1 : (int)rr;
 }
 
@@ -223,7 +245,7 @@ int ocg_ag_gemm(ocg_handle h, const void* const* a_chunks, int R, int local_rank
   if (ws_bytes < L.total) return OCG_ERR_WORKSPACE_TOO_SMALL;
   if (!device_matches(h)) return OCG_ERR_INVALID_ARG;
   Resolved rv;
-  int st = resolve(OCG_OP_AG_GEMM, R, m, K, N, cfg, h->cus, &rv);
+  int st = resolve(OCG_OP_AG_GEMM, R, m, K, N, 0, 0, cfg, h->cus, &rv);
   if (st) return st;
   AgArgs a{};
   for (int r = 0; r < R; ++r) a.chunks[r] = (const uint16_t*)a_chunks[r];
@@ -257,7 +279,7 @@ int ocg_gemm_rs(ocg_handle h, const void* A, const void* B, int64_t M, int64_t K
   if (ws_bytes < L.total) return OCG_ERR_WORKSPACE_TOO_SMALL;
   if (!device_matches(h)) return OCG_ERR_INVALID_ARG;
   Resolved rv;
-  int st = resolve(OCG_OP_GEMM_RS, R, M, K, N, cfg, h->cus, &rv);
+  int st = resolve(OCG_OP_GEMM_RS, R, M, K, N, 0, 0, cfg, h->cus, &rv);
   if (st) return st;
   RsArgs a{};
   a.a = (const uint16_t*)A;
@@ -266,7 +288,7 @@ int ocg_gemm_rs(ocg_handle h, const void* A, const void* B, int64_t M, int64_t K
   a.partial = (uint16_t*)partial;
   a.out = (uint16_t*)out;
   a.tile_flag = (uint32_t*)((char*)ws + L.rs_flag);
-  a.plan = make_rs_plan(R, local_rank, (int)M, (int)K, (int)N, rv.BM, rv.BN, reduce_rows(N), cfg.swizzle ? 1 : 0);
+  a.plan = make_rs_plan(R, local_rank, (int)M, (int)K, (int)N, rv.BM, rv.BN, reduce_rows(M, R, N, h->cus), cfg.swizzle ? 1 : 0);
   if (a.plan.n_tiles > L.max_rs_tiles) return OCG_ERR_INVALID_ARG;
   a.peer_flags = cfg.peer_flags;
   a.peer_flag_value = cfg.peer_flag_value;
@@ -298,7 +320,7 @@ int ocg_ag_grouped_gemm(ocg_handle h, const void* const* a_chunks, int R, int lo
   if (ws_bytes < L.total) return OCG_ERR_WORKSPACE_TOO_SMALL;
   if (!device_matches(h)) return OCG_ERR_INVALID_ARG;
   Resolved rv;
-  int st = resolve(OCG_OP_AG_GROUPED_GEMM, R, m, K, N, cfg, h->cus, &rv);
+  int st = resolve(OCG_OP_AG_GROUPED_GEMM, R, m, K, N, E, topk, cfg, h->cus, &rv);
   if (st) return st;
   int32_t* perm_buf = perm ? perm : (int32_t*)((char*)ws + L.moe_perm);
   MoeArgs a{};
@@ -367,8 +389,8 @@ const char* ocg_status_string(int s) {
   return "unknown status";
 }
 
-int ocg_plan_info(int op, int R, int local_rank, int64_t m, int64_t K, int64_t N, const ocg_config* cfgp,
-                  int64_t out[8]) {
+int ocg_plan_info(int op, int R, int local_rank, int64_t m, int64_t K, int64_t N, int E, int topk,
+                  const ocg_config* cfgp, int64_t out[8]) {
   if (!out || op < 0 || op > 2) return OCG_ERR_INVALID_ARG;
   if (op == OCG_OP_GEMM_RS) {
     if (R < 1 || R > kMaxRanks || m < R || m % R || !shape_ok(1, m, K, N)) return OCG_ERR_UNSUPPORTED_SHAPE;
@@ -378,7 +400,7 @@ int ocg_plan_info(int op, int R, int local_rank, int64_t m, int64_t K, int64_t N
   if (local_rank < 0 || local_rank >= R) return OCG_ERR_INVALID_ARG;
   ocg_config cfg = cfg_or_default(cfgp);
   Resolved rv;
-  int st = resolve(op, R, m, K, N, cfg, 256, &rv);
+  int st = resolve(op, R, m, K, N, E, topk, cfg, 256, &rv);
   if (st) return st;
   out[0] = rv.tile;
   out[1] = rv.BM;
@@ -386,7 +408,7 @@ int ocg_plan_info(int op, int R, int local_rank, int64_t m, int64_t K, int64_t N
   out[3] = rv.S;
   out[4] = rv.CT;
   if (op == OCG_OP_GEMM_RS) {
-    RsPlan p = make_rs_plan(R, local_rank, (int)m, (int)K, (int)N, rv.BM, rv.BN, reduce_rows(N), cfg.swizzle);
+    RsPlan p = make_rs_plan(R, local_rank, (int)m, (int)K, (int)N, rv.BM, rv.BN, reduce_rows(m, R, N, 256), cfg.swizzle);
     out[5] = p.n_red;
     out[6] = p.n_tiles;
     out[7] = p.RR;
@@ -406,7 +428,7 @@ int ocg_plan_task(int op, int R, int local_rank, int64_t m, int64_t K, int64_t N
   for (int i = 0; i < 8; ++i) desc[i] = -1;
   desc[0] = 0;
   int64_t info[8];
-  int st = ocg_plan_info(op, R, local_rank, m, K, N, cfgp, info);
+  int st = ocg_plan_info(op, R, local_rank, m, K, N, 0, 0, cfgp, info);
   if (st) return st;
   ocg_config cfg = cfg_or_default(cfgp);
   if (op == OCG_OP_GEMM_RS) {

@@ -725,10 +725,12 @@ hipError_t launch_moe(const RouteArgs& r, const MoeArgs& a, int tile, int grid, 
   hipLaunchKernelGGL(moe_scatter_kernel, dim3(nb), dim3(kRouteBlock), 0, s, r);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (tile == OCG_TILE_256x224)
-    hipLaunchKernelGGL((moe_gemm_kernel<256, 224>), dim3(grid), dim3(kThreads), 0, s, a);
-  else
-    hipLaunchKernelGGL((moe_gemm_kernel<128, 224>), dim3(grid), dim3(kThreads), 0, s, a);
+  switch (tile) {
+    case OCG_TILE_128x224: hipLaunchKernelGGL((moe_gemm_kernel<128, 224>), dim3(grid), dim3(kThreads), 0, s, a); break;
+    case OCG_TILE_256x224: hipLaunchKernelGGL((moe_gemm_kernel<256, 224>), dim3(grid), dim3(kThreads), 0, s, a); break;
+    case OCG_TILE_320x224: hipLaunchKernelGGL((moe_gemm_kernel<320, 224>), dim3(grid), dim3(kThreads), 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
@@ -748,8 +750,14 @@ static int occ(K kern) {
 }
 
 int resident_per_cu(int op, int tile) {
-  if (op == OCG_OP_AG_GROUPED_GEMM)
-    return tile == OCG_TILE_256x224 ? occ(moe_gemm_kernel<256, 224>) : occ(moe_gemm_kernel<128, 224>);
+  if (op == OCG_OP_AG_GROUPED_GEMM) {
+    switch (tile) {
+      case OCG_TILE_128x224: return occ(moe_gemm_kernel<128, 224>);
+      case OCG_TILE_256x224: return occ(moe_gemm_kernel<256, 224>);
+      case OCG_TILE_320x224: return occ(moe_gemm_kernel<320, 224>);
+    }
+    return 1;
+  }
   if (op == OCG_OP_AG_GEMM) {
     switch (tile) {
       case OCG_TILE_256x224: return occ(ag_gemm_kernel<256, 224>);

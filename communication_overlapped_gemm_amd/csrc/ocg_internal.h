@@ -17,8 +17,10 @@ constexpr int kMaxRouteSlots = 16384; // token slots (T * topk) per call
 constexpr int kMaxExperts = 64;
 constexpr int kMaxTopk = 4;
 constexpr int kMinSlabRows = 16;
-constexpr int kMoeTile = OCG_TILE_256x224;      // grouped GEMM default preset
-constexpr int kMoeTileSmall = OCG_TILE_128x224; // the other preset it accepts
+// grouped GEMM presets: 128x224, 256x224, 320x224 (the smallest is used to
+// size the tile lookup table)
+constexpr int kMoeTileSmall = OCG_TILE_128x224;
+inline bool moe_tile_ok(int t) { return t == OCG_TILE_128x224 || t == OCG_TILE_256x224 || t == OCG_TILE_320x224; }
 
 // Workspace header (first 256 bytes of every workspace).
 struct WsHeader {

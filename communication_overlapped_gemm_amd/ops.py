@@ -182,11 +182,13 @@ def signal(flags: torch.Tensor, value: int, stream=None) -> None:
     check(lib.ocg_signal(flags.data_ptr(), flags.numel(), value & 0xFFFFFFFF, _stream_ptr(stream)), "ocg_signal")
 
 
-def plan_info(op: int, R: int, local_rank: int, m: int, K: int, N: int, config: Optional[Config] = None) -> dict:
-    """Host-only: the resolved tile/slab/copy plan of a call."""
+def plan_info(op: int, R: int, local_rank: int, m: int, K: int, N: int, config: Optional[Config] = None,
+              E: int = 0, topk: int = 0) -> dict:
+    """Host-only: the resolved tile/slab/copy plan of a call (E, topk: the
+    grouped GEMM's experts and picks per token)."""
     out = _lib.I64x8()
     cfg = _cfg(config)
-    check(lib.ocg_plan_info(op, R, local_rank, m, K, N, C.byref(cfg), out), "ocg_plan_info")
+    check(lib.ocg_plan_info(op, R, local_rank, m, K, N, E, topk, C.byref(cfg), out), "ocg_plan_info")
     keys = ["tile", "BM", "BN", "slab_rows", "copy_rows", "n_copy_or_strips", "n_tiles", "n_slabs_or_strip_rows"]
     return dict(zip(keys, list(out)))
 

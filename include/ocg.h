@@ -61,14 +61,16 @@ extern "C" {
 #define OCG_MODE_GEMM_ONLY 1
 #define OCG_MODE_COPY_ONLY 2
 
-/* Tile presets (rows x columns of C per workgroup tile, K step 64). */
+/* Tile presets (rows x columns of C per workgroup tile, K step 64);
+ * OCG_TILE_320x224 is for the grouped GEMM only. */
 #define OCG_TILE_AUTO (-1)
 #define OCG_TILE_256x224 0
 #define OCG_TILE_128x224 1
 #define OCG_TILE_128x256 2
 #define OCG_TILE_128x128 3
 #define OCG_TILE_256x256 4
-#define OCG_TILE_COUNT 5
+#define OCG_TILE_320x224 5
+#define OCG_TILE_COUNT 6
 
 /* Trace record written per executed task when ocg_config.trace is set
  * (64 bytes), at slot: AG-GEMM / MoE copy task u -> u, tile v -> n_copy + v;
@@ -181,9 +183,10 @@ int ocg_gemm_rs(ocg_handle h, const void* a, const void* b, int64_t M, int64_t K
  *   out         : bf16 [R*m*topk, N], written
  * The grouped tiles wait on the flags of every peer slab their tokens come
  * from (a per-tile lookup table built on the device after routing). Tile
- * presets: OCG_TILE_256x224 (default for OCG_TILE_AUTO: one tile holds an
- * expert's rows when it has at most 256) or OCG_TILE_128x224; any other
- * preset is OCG_ERR_INVALID_ARG.
+ * presets: OCG_TILE_128x224, OCG_TILE_256x224 or OCG_TILE_320x224 (the
+ * latter only here); OCG_TILE_AUTO takes the smallest whose rows hold the
+ * rows an expert is expected to get (R*m*topk/E plus three standard
+ * deviations), else 256x224. Any other preset is OCG_ERR_INVALID_ARG.
  */
 int ocg_ag_grouped_gemm(ocg_handle h, const void* const* a_chunks, int R, int local_rank,
                         int64_t m, int64_t K, const float* logits, int E, int topk,
@@ -207,8 +210,10 @@ const char* ocg_status_string(int status);
 /* Resolved plan parameters for a call with config `cfg` (NULL = defaults):
  * out[0]=tile preset, out[1]=BM, out[2]=BN, out[3]=slab rows,
  * out[4]=copy rows, out[5]=#copy tasks, out[6]=#tiles (static ops),
- * out[7]=#slabs. For GEMM_RS pass m = M. Returns OCG_OK or an error. */
-int ocg_plan_info(int op, int R, int local_rank, int64_t m, int64_t K, int64_t N,
+ * out[7]=#slabs. For GEMM_RS pass m = M. E and topk are the grouped GEMM's
+ * expert count and picks per token (they choose its default tile; ignored
+ * by the other ops). Returns OCG_OK or an error. */
+int ocg_plan_info(int op, int R, int local_rank, int64_t m, int64_t K, int64_t N, int E, int topk,
                   const ocg_config* cfg, int64_t out[8]);
 
 /* Task at trace slot `ticket` of the AG-GEMM / GEMM-RS plan (slots as for

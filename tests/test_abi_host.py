@@ -80,6 +80,21 @@ def test_plan_info_tile_choice():
     assert (p["BM"], p["BN"], p["n_tiles"]) == (128, 256, 512)
 
 
+def test_plan_info_moe_tile_choice():
+    # 4096 tokens x top-2 over 32 experts: 256 rows per expert on average,
+    # up to ~300 expected: one 320-row tile per expert
+    p = ocg.plan_info(ocg.OP_AG_GROUPED_GEMM, 8, 0, 512, 4096, 1792, E=32, topk=2)
+    assert (p["BM"], p["BN"]) == (320, 224)
+    p = ocg.plan_info(ocg.OP_AG_GROUPED_GEMM, 2, 0, 64, 128, 96, E=6, topk=2)
+    assert (p["BM"], p["BN"]) == (128, 224)
+    p = ocg.plan_info(ocg.OP_AG_GROUPED_GEMM, 8, 0, 1024, 128, 96, E=8, topk=2)
+    assert (p["BM"], p["BN"]) == (256, 224)   # ~2048 rows per expert: many 256-row tiles
+    # the 320-row preset is the grouped GEMM's only
+    for op, m in ((ocg.OP_AG_GEMM, 512), (ocg.OP_GEMM_RS, 4096)):
+        with pytest.raises(ocg.OcgError):
+            ocg.plan_info(op, 8, 0, m, 1792, 4096, ocg.default_config(tile=ocg.TILE_320x224))
+
+
 AG_CASES = [
     # R, m, K, N, local, tile
     (4, 128, 256, 256, 0, -1),

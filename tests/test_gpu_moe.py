@@ -47,12 +47,15 @@ SMALL = [
 ]
 
 
-@pytest.mark.parametrize("tile", ["auto", "128x224"])
+TILES = {"auto": -1, "128x224": 1, "256x224": 0, "320x224": 5}
+
+
+@pytest.mark.parametrize("tile", list(TILES))
 @pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
 def test_moe_small_full(ocg, case, tile):
     name, R, m, K, N, E, topk, local = case
     x = workloads.make_moe(R, m, K, N, E, seed=300 + E, topk=topk, scale=0.5)
-    cfg = ocg.default_config(tile=ocg.TILE_AUTO if tile == "auto" else ocg.TILE_128x224)
+    cfg = ocg.default_config(tile=TILES[tile])
     say("moe", name, tile)
     o = run(ocg, x, local, cfg)
     check(ocg, x, o, name)
@@ -80,7 +83,7 @@ def test_moe_ties_and_empty_experts(ocg):
 def test_moe_lookup_table_tiles(ocg):
     x = workloads.make_moe(4, 128, 128, 448, 8, seed=12, topk=2, scale=0.5)
     cfg = ocg.default_config()
-    info = ocg.plan_info(ocg.OP_AG_GROUPED_GEMM, 4, 0, 128, 128, 448, cfg)
+    info = ocg.plan_info(ocg.OP_AG_GROUPED_GEMM, 4, 0, 128, 128, 448, cfg, E=8, topk=2)
     res = oracle.ag_grouped_gemm(x.a_chunks, x.logits, x.w, 2)
     tiles = sch.moe_tiles(res["counts"], res["offsets"], res["perm"], 2, 4, 128, 448, 0, info["BM"],
                           info["BN"], info["slab_rows"])
