@@ -59,9 +59,14 @@ def traffic_record(kernel_hash: str, launches_per_step: int = 1):
     return rec.get("hbm_bytes_per_launch")
 
 
-def timed_launches(torch, fn, n, stream):
-    """Per-launch durations (ms) from HIP events on the launch stream."""
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+def make_events(torch, n):
+    return [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+
+
+def timed_launches(torch, fn, n, stream, ev=None):
+    """Per-launch durations (ms) from HIP events on the launch stream (events
+    created beforehand when `ev` is given, so their creation is not timed)."""
+    ev = ev or make_events(torch, n)
     for s, e in ev:
         s.record(stream)
         fn()
@@ -146,9 +151,10 @@ def main() -> int:
 
     for _ in range(args.warmup):
         step()
+    ev = make_events(torch, args.steps)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    per_launch = timed_launches(torch, step, args.steps, stream)   # ends with synchronize
+    per_launch = timed_launches(torch, step, args.steps, stream, ev)   # ends with synchronize
     wall = time.perf_counter() - t0
     ws.check()
     ms_per_step = wall * 1e3 / args.steps
