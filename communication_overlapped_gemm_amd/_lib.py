@@ -90,7 +90,7 @@ def load(path: str = LIB_PATH):
     if not os.path.exists(path):
         raise ImportError(
             f"{path} is missing: build the HIP library first "
-            "(python -m communication_overlapped_gemm_amd.build); there is no fallback path")
+            "(python communication_overlapped_gemm_amd/build.py); there is no fallback path")
     lib = C.CDLL(path)
     _declare(lib)
     return lib

@@ -1,6 +1,8 @@
 """Build libocg.so (HIP, gfx950) in-tree with hipcc.
 
-    python -m communication_overlapped_gemm_amd.build
+    python communication_overlapped_gemm_amd/build.py
+
+(run as a file: importing the package loads libocg.so, which this builds)
 """
 from __future__ import annotations
 

@@ -6,6 +6,7 @@ import ctypes as C
 import os
 import re
 import subprocess
+import sys
 
 import pytest
 
@@ -34,6 +35,24 @@ def test_library_exports_every_declared_symbol():
     assert not missing, f"not exported: {missing}"
     for f in declared_functions():
         assert hasattr(ocg.lib, f)
+
+
+def test_builder_loads_without_the_library(tmp_path):
+    """A fresh checkout has no libocg.so: the builder must load without
+    importing the package (whose import loads the library), as the build
+    entry point does."""
+    import shutil
+    pkg = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "communication_overlapped_gemm_amd")
+    dst = tmp_path / "communication_overlapped_gemm_amd"
+    shutil.copytree(pkg, dst, ignore=shutil.ignore_patterns("*.so", "__pycache__"))
+    code = ("import importlib.util, sys; "
+            f"spec = importlib.util.spec_from_file_location('b', {str(dst / 'build.py')!r}); "
+            "m = importlib.util.module_from_spec(spec); spec.loader.exec_module(m); "
+            "assert callable(m.build) and 'communication_overlapped_gemm_amd' not in sys.modules")
+    subprocess.run([sys.executable, "-c", code], check=True, cwd=str(tmp_path))
+    res = subprocess.run([sys.executable, "-c", "import communication_overlapped_gemm_amd"], cwd=str(tmp_path),
+                         capture_output=True, text=True)
+    assert res.returncode != 0 and "no fallback" in res.stderr   # the product path fails loudly
 
 
 def test_status_strings_and_defaults():
