@@ -75,6 +75,21 @@ def timed_launches(torch, fn, n, stream, ev=None):
     return [s.elapsed_time(e) for s, e in ev]
 
 
+def cold_launch_ms(torch, fn, n, stream, flush_bytes=512 << 20):
+    """Median launch time with the caches cold: a 512 MiB buffer is written
+    before each launch, more than the XCD L2s and the Infinity Cache hold."""
+    buf = torch.empty(flush_bytes // 4, dtype=torch.int32, device="cuda")
+    ev = make_events(torch, n)
+    for i, (s, e) in enumerate(ev):
+        buf.fill_(i)
+        s.record(stream)
+        fn()
+        e.record(stream)
+    torch.cuda.synchronize()
+    del buf
+    return statistics.median(s.elapsed_time(e) for s, e in ev)
+
+
 def median_ms(torch, fn, n, stream, warm=2):
     for _ in range(warm):
         fn()
@@ -216,6 +231,11 @@ def main() -> int:
             "torch_matmul_tflops_yardstick": round(flops / (t_mm * 1e-3) / 1e12, 2),
         }
         del full
+        q = sorted(per_launch)
+        pct = lambda f: q[min(len(q) - 1, int(round(f * (len(q) - 1))))] * 1e3
+        rec["launch_stats"] = {"p10_us": round(pct(0.1), 2), "p50_us": round(pct(0.5), 2),
+                               "p90_us": round(pct(0.9), 2),
+                               "cold_us": round(cold_launch_ms(torch, step, 10, stream) * 1e3, 2)}
         rec["ops"] = other_ops(torch, np, ocg, workloads, upload, stream, n)
         rec["cpu_baseline"] = cpu_baseline(x)
     print(json.dumps(rec), flush=True)
