@@ -26,7 +26,14 @@ Readings where the pages are silent (each is also listed in the design doc):
       probabilities of the chosen experts (not renormalised) and are not
       applied to the GEMM output;
   R4  "sorted by expert" is stable in (expert, token, slot); token-slot order
-      means output row t*topk + slot.
+      means output row t*topk + slot;
+  R5  TopK-Reduce: a token's output is the gate-weighted sum of its top-k
+      slot rows, P[t] = sum_j w[t, j] * Y[t*topk + j]; the ReduceScatter that
+      follows it is the fixed-order reduce of R2 over the ranks' combined
+      partials [T, N], row block l = the l-th rank's m tokens; the local
+      combined partial enters that reduce as bfloat16.
+  [TL-EXP] names TopK-Reduce among the MoE operators it overlaps; it prints
+  neither its formula nor its precision, hence R5.
 """
 from __future__ import annotations
 
@@ -239,3 +246,43 @@ def ag_grouped_gemm_entries(a_chunks, ids, w_bits, slots, cols):
         arow = decode_bf16(a_chunks[t // m][t % m])
         res[i] = float(arow @ decode_bf16(w_bits[e][:, int(c)]))
     return res
+
+
+# --------------------------------------------------------------------------
+# MoE TopK-Reduce + ReduceScatter  [TL-EXP] (reading R5)
+# --------------------------------------------------------------------------
+
+
+def topk_combine(y_bits, w, topk):
+    """P[t] = sum over j < topk of w[t, j] * Y[t*topk + j], float64 [T, N].
+
+    ``y_bits``: bf16 bits [T*topk, N] in token-slot order; ``w``: gate
+    weights [T, topk]."""
+    y = decode_bf16(np.asarray(y_bits))
+    wt = np.asarray(w, dtype=np.float64)
+    T = wt.shape[0]
+    if y.shape[0] != T * topk:
+        raise ValueError("Y must have T*topk rows")
+    out = np.zeros((T, y.shape[1]), dtype=np.float64)
+    for j in range(topk):
+        out += wt[:, j:j + 1] * y[j::topk]
+    return out
+
+
+def moe_combine_rs(y_bits, w, topk, peers, R, local_rank):
+    """Local combined partial P_l = topk_combine(Y, w), and
+    out_l = sum over ranks s of P_s[rows l*T/R .. (l+1)*T/R), float64.
+
+    ``peers`` maps every rank s != local_rank to its bf16 combined partial
+    [T, N]. Returns (partial, out)."""
+    partial = topk_combine(y_bits, w, topk)
+    T = partial.shape[0]
+    if T % R:
+        raise ValueError("T must be a multiple of R")
+    blk = T // R
+    r0 = local_rank * blk
+    out = partial[r0:r0 + blk].copy()
+    for s in range(R):
+        if s != local_rank:
+            out += decode_bf16(peers[s][r0:r0 + blk])
+    return partial, out

@@ -216,3 +216,29 @@ def moe_tiles(counts, offsets, perm, topk, R, m, N, local, BM, BN, S):
                 deps = tuple(s for s in range(s_lo, s_hi + 1) if s // bpr != local)
                 out.append((e, r0, r1 - r0, cb, deps))
     return out
+
+
+def combine_rs_plan(R, T, local, CR, RR):
+    """Ticket list of the TopK-Reduce + ReduceScatter kernel.
+
+    Combine tasks: ("combine", slot, rows) where rows are the CR token rows
+    (u*CR .. u*CR+CR) of the row order rotated to start at the local block
+    (row t = (r + local*T/R) mod T), so the local block's rows come first.
+    Reduce strips: ("reduce", slot, row0, row1, deps) over RR rows of the
+    local block, deps = the combine tasks holding those rows."""
+    blk = T // R
+    base = local * blk
+    n_comb = _cdiv(T, CR)
+    out = []
+    for u in range(n_comb):
+        rows = tuple((r + base) % T for r in range(u * CR, min((u + 1) * CR, T)))
+        out.append(("combine", u, rows))
+    t = n_comb
+    r = 0
+    while r < blk:
+        r1 = min(r + RR, blk)
+        deps = tuple(range(r // CR, (r1 - 1) // CR + 1))
+        out.append(("reduce", t, base + r, base + r1, deps))
+        t += 1
+        r = r1
+    return out

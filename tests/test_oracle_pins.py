@@ -349,3 +349,74 @@ def test_ag_grouped_gemm_entries_match_full():
     cols = rng.integers(0, N, 20)
     got = oracle.ag_grouped_gemm_entries(chunks, res["ids"], w, slots, cols)
     assert np.allclose(got, res["out"][slots, cols], rtol=1e-14)
+
+
+# ---------------------------------------------------------------- TopK-Reduce + ReduceScatter
+
+
+def brute_combine(y, w, topk):
+    T = len(w)
+    N = len(y[0])
+    return [[sum(w[t][j] * y[t * topk + j][n] for j in range(topk)) for n in range(N)] for t in range(T)]
+
+
+@pytest.mark.parametrize("T,N,topk,seed", [(3, 4, 2, 0), (5, 3, 1, 1), (4, 5, 3, 2)])
+def test_topk_combine_brute_force(T, N, topk, seed):
+    """Triple loop over tokens, columns and slots. Catches a slot taken from
+    the wrong token (row t*topk + j), a weight of the wrong slot, or a
+    transposed weight matrix."""
+    rng = np.random.default_rng(seed)
+    y = rand_bf16(rng, (T * topk, N))
+    w = rng.uniform(0, 1, (T, topk)).astype(np.float32)
+    want = np.array(brute_combine(ref.decode_bf16(y).tolist(), w.astype(np.float64).tolist(), topk))
+    assert np.allclose(oracle.topk_combine(y, w, topk), want, rtol=1e-13, atol=1e-13)
+
+
+def test_topk_combine_special_cases():
+    """topk = 1 with unit weights is the identity; a one-hot weight row picks
+    exactly that slot's row; the combine is linear in the weights. Catches a
+    dropped or extra slot and a scaled weight."""
+    rng = np.random.default_rng(21)
+    T, N = 6, 5
+    y1 = rand_bf16(rng, (T, N))
+    assert np.array_equal(oracle.topk_combine(y1, np.ones((T, 1), np.float32), 1), ref.decode_bf16(y1))
+    y2 = rand_bf16(rng, (T * 2, N))
+    onehot = np.zeros((T, 2), np.float32)
+    pick = rng.integers(0, 2, T)
+    onehot[np.arange(T), pick] = 1.0
+    assert np.array_equal(oracle.topk_combine(y2, onehot, 2), ref.decode_bf16(y2)[np.arange(T) * 2 + pick])
+    w = rng.uniform(0, 1, (T, 2)).astype(np.float32)
+    assert np.allclose(oracle.topk_combine(y2, 2 * w, 2), 2 * oracle.topk_combine(y2, w, 2), rtol=1e-14, atol=0)
+
+
+def test_moe_combine_rs_allreduce_identity():
+    """Every rank s holds its own Y_s and w_s with small integer values, so all
+    combined partials are exact. Concatenating out_l over l must equal the
+    sum over s of the combined partials (an all-reduce), computed by loops."""
+    R, m, N, topk = 4, 3, 5, 2
+    T = R * m
+    rng = np.random.default_rng(22)
+    Y = [bf16_of_ints(rng.integers(-4, 5, (T * topk, N))) for _ in range(R)]
+    W = [rng.integers(0, 3, (T, topk)).astype(np.float32) for _ in range(R)]
+    P = [np.array(brute_combine(ref.decode_bf16(Y[s]).tolist(), W[s].tolist(), topk)) for s in range(R)]
+    P_bits = [bf16_of_ints(p) for p in P]   # |x| <= 16: exact in bf16
+    blocks = []
+    for local in range(R):
+        part, out = oracle.moe_combine_rs(Y[local], W[local], topk, {s: P_bits[s] for s in range(R) if s != local},
+                                          R, local)
+        assert np.array_equal(part, P[local])
+        blocks.append(out)
+    assert np.array_equal(np.concatenate(blocks), sum(P))
+
+
+def test_moe_combine_rs_zero_peers():
+    """Zero peers: out is the local combined partial's row block (catches the
+    wrong block)."""
+    R, m, N, topk = 4, 5, 3, 2
+    rng = np.random.default_rng(23)
+    y = rand_bf16(rng, (R * m * topk, N))
+    w = rng.uniform(0, 1, (R * m, topk)).astype(np.float32)
+    zero = np.zeros((R * m, N), dtype=np.uint16)
+    for local in range(R):
+        p, out = oracle.moe_combine_rs(y, w, topk, {s: zero for s in range(R) if s != local}, R, local)
+        assert np.array_equal(out, p[local * m:(local + 1) * m])

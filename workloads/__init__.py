@@ -135,10 +135,38 @@ def make_moe(R: int, m: int, K: int, N: int, E: int, seed: int, topk: int = 2,
     return MoeInputs(R, m, K, N, E, topk, chunks, logits, w, seed)
 
 
+@dataclass
+class MoeCombineInputs:
+    """out_l = row block l of (TopK-Reduce of Y with gate weights w + the
+    peers' combined partials)."""
+    R: int
+    m: int
+    N: int
+    topk: int
+    local_rank: int
+    y: np.ndarray                       # uint16 [R*m*topk, N], token-slot order
+    w: np.ndarray                       # float32 [R*m, topk]
+    peers: Dict[int, np.ndarray]        # rank s != local -> uint16 [R*m, N]
+    seed: int = 0
+
+
+def make_moe_combine(R: int, m: int, N: int, topk: int, seed: int, local_rank: int = 0,
+                     scale: float = 0.02) -> MoeCombineInputs:
+    """Draw order: Y ~ N(0, scale) [R*m*topk, N]; gate weights float32
+    uniform [0, 0.5) [R*m, topk]; then the peer partials P_s (s != local_rank,
+    ascending) ~ N(0, scale) [R*m, N]."""
+    rng = np.random.default_rng(seed)
+    T = R * m
+    y = _draw_bf16(rng, (T * topk, N), "normal", scale)
+    w = rng.uniform(0.0, 0.5, size=(T, topk)).astype(np.float32)
+    peers = {s: _draw_bf16(rng, (T, N), "normal", scale) for s in range(R) if s != local_rank}
+    return MoeCombineInputs(R, m, N, topk, local_rank, y, w, peers, seed)
+
+
 @dataclass(frozen=True)
 class Workload:
     name: str
-    op: str            # "ag_gemm" | "gemm_rs" | "ag_grouped_gemm"
+    op: str            # "ag_gemm" | "gemm_rs" | "ag_grouped_gemm" | "moe_combine_rs"
     params: dict = field(default_factory=dict)
 
     def flops(self) -> float:
@@ -147,6 +175,8 @@ class Workload:
             return 2.0 * p["R"] * p["m"] * p["K"] * p["N"]
         if self.op == "gemm_rs":
             return 2.0 * p["M"] * p["K"] * p["N"]
+        if self.op == "moe_combine_rs":
+            return 2.0 * p["R"] * p["m"] * p["topk"] * p["N"]
         return 2.0 * p["R"] * p["m"] * p["topk"] * p["K"] * p["N"]
 
     def make(self, **over):
@@ -158,12 +188,14 @@ class Workload:
         if self.op == "gemm_rs":
             return make_gemm_rs(p["R"], p["M"], p["K"], p["N"], p["seed"],
                                 p.get("local_rank", 0))
+        if self.op == "moe_combine_rs":
+            return make_moe_combine(p["R"], p["m"], p["N"], p["topk"], p["seed"], p.get("local_rank", 0))
         return make_moe(p["R"], p["m"], p["K"], p["N"], p["E"], p["seed"], p["topk"])
 
 
-# The five workloads: one GPU's share of tensor-parallel (TP=8) LLM FFN layers
+# The workloads: one GPU's share of tensor-parallel (TP=8) LLM FFN layers
 # (8B-class: hidden 4096, FFN 14336; 70B-class: hidden 8192, FFN 28672) plus a
-# tiny case and a top-2 MoE layer with 32 experts.
+# tiny case, a top-2 MoE layer with 32 experts, and that layer's TopK-Reduce tail.
 WORKLOADS = {
     "ag_gemm_tiny": Workload("ag_gemm_tiny", "ag_gemm",
                              dict(R=4, m=128, K=256, N=256, seed=0, dist="uniform", scale=1.0)),
@@ -175,6 +207,10 @@ WORKLOADS = {
                             dict(R=8, m=1024, K=8192, N=3584, seed=3)),
     "ag_moe": Workload("ag_moe", "ag_grouped_gemm",
                        dict(R=8, m=512, K=4096, N=1792, E=32, topk=2, seed=4)),
+    # the MoE tail: TopK-Reduce of the grouped GEMM's output rows, then the
+    # ReduceScatter of the combined token rows (row block 0 kept)
+    "moe_combine_rs": Workload("moe_combine_rs", "moe_combine_rs",
+                               dict(R=8, m=512, N=1792, topk=2, seed=5, local_rank=0)),
 }
 
 
