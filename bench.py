@@ -128,7 +128,7 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--skip-extras", action="store_true")
-    ap.add_argument("--op", default=WORKLOAD, choices=[WORKLOAD, "ag_gemm_8b", "gemm_rs_8b", "ag_moe"],
+    ap.add_argument("--op", default=WORKLOAD, choices=[WORKLOAD, "ag_gemm_8b", "gemm_rs_8b", "ag_moe", "moe_combine_rs"],
                     help="profiling aid: launch only this operation (no benchmark record)")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -245,6 +245,8 @@ def main() -> int:
 def op_setups(torch, ocg, workloads, upload):
     """name -> (workload, setup()) where setup() returns (launch_fused(), extras)
     for the other operations (fused launches with caller-owned buffers)."""
+    import numpy as np
+
     def ag8():
         w = workloads.workload("ag_gemm_8b")
         x = w.make()
@@ -284,7 +286,22 @@ def op_setups(torch, ocg, workloads, upload):
             ocg.ag_grouped_gemm(chunks, lg, wt, x.topk, 0, workspace=ws, outputs=outs)
         return w, x, ws, launch
 
-    return {"ag_gemm_8b": ag8, "gemm_rs_8b": rs8, "ag_moe": moe}
+    def comb():
+        w = workloads.workload("moe_combine_rs")
+        x = w.make()
+        y = upload(x.y)
+        wt = torch.from_numpy(np.ascontiguousarray(x.w)).to("cuda")
+        T = x.R * x.m
+        peers = [None if s == x.local_rank else upload(x.peers[s]) for s in range(x.R)]
+        part = torch.empty((T, x.N), dtype=torch.bfloat16, device="cuda")
+        o = torch.empty((x.m, x.N), dtype=torch.bfloat16, device="cuda")
+        ws = ocg.Workspace(ocg.OP_MOE_COMBINE_RS, x.R, x.m, 0, x.N, 0, x.topk)
+
+        def launch(mode=0):
+            ocg.moe_combine_rs(y, wt, peers, x.local_rank, partial=part, out=o, workspace=ws)
+        return w, x, ws, launch
+
+    return {"ag_gemm_8b": ag8, "gemm_rs_8b": rs8, "ag_moe": moe, "moe_combine_rs": comb}
 
 
 def other_ops(torch, np, ocg, workloads, upload, stream, n):
@@ -317,6 +334,16 @@ def other_ops(torch, np, ocg, workloads, upload, stream, n):
     out["ag_moe"] = {"t_us": round(t * 1e3, 2), "tflops": round(w.flops() / (t * 1e-3) / 1e12, 2),
                      "hbm_gbs_algorithmic": round(hbm / (t * 1e-3) / 1e9, 1),
                      "hbm_frac": round(hbm / (t * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+    del launch
+    # MoE TopK-Reduce + ReduceScatter (HBM-bound)
+    w, x, ws, launch = setups["moe_combine_rs"]()
+    t = median_ms(torch, launch, n, stream)
+    ws.check()
+    T = x.R * x.m
+    hbm = T * x.topk * x.N * 2 + T * x.topk * 4 + T * x.N * 2 + x.R * x.m * x.N * 2 + x.m * x.N * 2
+    out["moe_combine_rs"] = {"t_us": round(t * 1e3, 2), "hbm_bytes": hbm,
+                             "hbm_gbs_algorithmic": round(hbm / (t * 1e-3) / 1e9, 1),
+                             "hbm_frac": round(hbm / (t * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
     return out
 
 

@@ -138,6 +138,28 @@ int resolve(int op, int R, int64_t m, int64_t K, int64_t N, int E, int topk, con
 
 // Rows per reduce strip: at most ~32 KiB of each partial, and few enough
 // that every CU gets a strip (the strips run once the tiles are done).
+// TopK-Reduce task sizes: about two tasks per CU, all running at once,
+// with equal bytes each -- a local row moves topk + R + 1 rows of data (the
+// slot rows, the peers' rows, the partial and out), another row topk + 1.
+// At the MoE share (R = 8, m = 512, top-2): 3 local rows or 11 other rows per
+// task, 497 tasks.
+void combine_rows(int R, int64_t m, int topk, int cus, int* crl, int* cr) {
+  const double bl = topk + R + 1.0, bo = topk + 1.0;
+  const double T = (double)R * (double)m;
+  const double per_task = ((double)m * bl + (T - (double)m) * bo) / (2.0 * (cus > 0 ? cus : 1));
+  const long l = llround(per_task / bl), o = llround(per_task / bo);
+  *crl = l < 1 ? 1 : (int)l;
+  *cr = o < 1 ? 1 : (int)o;
+}
+
+bool combine_shape_ok(int R, int64_t m, int64_t N, int topk) {
+  if (R < 1 || R > kMaxRanks || m < 1 || N < 8 || N % 8 || topk < 1 || topk > kMaxTopk) return false;
+  const int64_t T = (int64_t)R * m;
+  if (T > (1 << 24) || N > (1 << 20)) return false;
+  if (T * N * 2 >= ((int64_t)1 << 31)) return false;   // 32-bit offsets of the partial's stores
+  return true;
+}
+
 int reduce_rows(int64_t M, int R, int64_t N, int cus) {
   int64_t rr = (32 * 1024) / (2 * N);
   const int64_t spread = (M / R) / (cus > 0 ? cus : 1);
@@ -210,7 +232,8 @@ int ocg_create(int device, ocg_handle* out) {
 void ocg_destroy(ocg_handle h) { delete h; }
 
 size_t ocg_workspace_bytes(int op, int R, int64_t m, int64_t K, int64_t N, int E, int topk) {
-  if (op < 0 || op > 2) return 0;
+  if (op < 0 || op > 3) return 0;
+  if (op == OCG_OP_MOE_COMBINE_RS) return combine_shape_ok(R, m, N, topk) ? layout(op, R, m, 0, N, 0, topk).total : 0;
   if (op == OCG_OP_GEMM_RS) {
     if (R < 1 || R > kMaxRanks || m < R || m % R) return 0;
     if (!shape_ok(1, m, K, N)) return 0;
@@ -363,6 +386,42 @@ int ocg_signal(uint32_t* flags, int count, uint32_t value, void* stream) {
   return launch_fill_u32(flags, (size_t)count, value, 1, (hipStream_t)stream) == hipSuccess ? OCG_OK : OCG_ERR_HIP;
 }
 
+int ocg_moe_combine_rs(ocg_handle h, const void* y, const float* topk_w, int R, int local_rank, int64_t m,
+                       int64_t N, int topk, const void* const* peer_partials, void* partial, void* out, void* ws,
+                       size_t ws_bytes, const ocg_config* cfgp, void* stream) {
+  if (!h || !y || !topk_w || !peer_partials || !partial || !out || !ws) return OCG_ERR_INVALID_ARG;
+  if (!combine_shape_ok(R, m, N, topk)) return OCG_ERR_UNSUPPORTED_SHAPE;
+  if (local_rank < 0 || local_rank >= R) return OCG_ERR_INVALID_ARG;
+  for (int s = 0; s < R; ++s)
+    if (s != local_rank && (!peer_partials[s] || !aligned16(peer_partials[s]))) return OCG_ERR_INVALID_ARG;
+  if (!aligned16(y) || !aligned16(partial) || !aligned16(out) || !aligned16(ws) || ((uintptr_t)topk_w & 3))
+    return OCG_ERR_INVALID_ARG;
+  ocg_config cfg = cfg_or_default(cfgp);
+  WsLayout L = layout(OCG_OP_MOE_COMBINE_RS, R, m, 0, N, 0, topk);
+  if (ws_bytes < L.total) return OCG_ERR_WORKSPACE_TOO_SMALL;
+  if (!device_matches(h)) return OCG_ERR_INVALID_ARG;
+  const int64_t T = (int64_t)R * m;
+  CombArgs a{};
+  a.y = (const uint16_t*)y;
+  a.w = topk_w;
+  for (int s = 0; s < R; ++s) a.peers[s] = (s == local_rank) ? nullptr : (const uint16_t*)peer_partials[s];
+  a.partial = (uint16_t*)partial;
+  a.out = (uint16_t*)out;
+  a.topk = topk;
+  combine_rows(R, m, topk, h->cus, &a.CRL, &a.CR);
+  a.n_lt = cdiv((int)m, a.CRL);
+  a.n_comb = a.n_lt + cdiv((int)(T - m), a.CR);
+  a.R = R;
+  a.local = local_rank;
+  a.m = (int)m;
+  a.T = (int)T;
+  a.N = (int)N;
+  a.cm = make_common(ws, cfg);
+  int grid = cfg.grid > 0 ? cfg.grid : 2 * h->cus;   // no LDS: two workgroups per CU
+  if (grid > a.n_comb) grid = a.n_comb;
+  return launch_moe_combine_rs(a, grid, (hipStream_t)stream) == hipSuccess ? OCG_OK : OCG_ERR_HIP;
+}
+
 int ocg_check(ocg_handle h, void* ws) {
   if (!h || !ws) return OCG_ERR_INVALID_ARG;
   WsHeader* hdr = (WsHeader*)ws;
@@ -391,7 +450,22 @@ const char* ocg_status_string(int s) {
 
 int ocg_plan_info(int op, int R, int local_rank, int64_t m, int64_t K, int64_t N, int E, int topk,
                   const ocg_config* cfgp, int64_t out[8]) {
-  if (!out || op < 0 || op > 2) return OCG_ERR_INVALID_ARG;
+  if (!out || op < 0 || op > 3) return OCG_ERR_INVALID_ARG;
+  if (op == OCG_OP_MOE_COMBINE_RS) {
+    if (!combine_shape_ok(R, m, N, topk)) return OCG_ERR_UNSUPPORTED_SHAPE;
+    if (local_rank < 0 || local_rank >= R) return OCG_ERR_INVALID_ARG;
+    const int64_t T = (int64_t)R * m;
+    int cr, crl;
+    combine_rows(R, m, topk, 256, &crl, &cr);
+    const int n_lt = cdiv((int)m, crl);
+    out[0] = -1;
+    out[1] = out[2] = out[7] = 0;
+    out[3] = cr;
+    out[4] = crl;
+    out[5] = n_lt + cdiv((int)(T - m), cr);
+    out[6] = n_lt;
+    return OCG_OK;
+  }
   if (op == OCG_OP_GEMM_RS) {
     if (R < 1 || R > kMaxRanks || m < R || m % R || !shape_ok(1, m, K, N)) return OCG_ERR_UNSUPPORTED_SHAPE;
   } else if (!shape_ok(R, m, K, N)) {

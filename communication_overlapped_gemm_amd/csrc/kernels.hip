@@ -669,6 +669,107 @@ __global__ __launch_bounds__(kThreads, 1) void moe_gemm_kernel(MoeArgs args) {
   finish(cm.hdr, epoch);
 }
 
+// ---------------------------------------------------------------- TopK-Reduce + ReduceScatter
+
+// Rows [r0, r1) of the token order rotated to start at the local block
+// (row t = (r + local*m) mod T): each row's 16-byte column chunks summed over
+// its top-k slot rows in slot order, weight times value in fp32, rounded
+// once to bf16 and stored to the partial. LOCAL rows (r < m) also finish the
+// ReduceScatter on the spot: the R ranks' bf16 rows summed in ascending rank
+// order in fp32 (the local one as just rounded) and rounded once into out.
+// U chunks per thread in flight per round.
+template <bool LOCAL, int U, int K>
+__device__ void combine_rows(const CombArgs& a, int r0, int r1) {
+  const int T = a.T, N = a.N, n8 = N / 8, base = a.local * a.m;
+  const int n16 = (r1 - r0) * n8;
+  for (int b0 = threadIdx.x; b0 < n16; b0 += U * kThreads) {
+    u32x4_t v[U][K];
+    u32x4_t pv[U][LOCAL ? kMaxRanks : 1];
+    float wt[U][K];
+    int row[U], c8[U];
+#pragma unroll
+    for (int q = 0; q < U; ++q) {
+      const int i = b0 + q * kThreads;
+      row[q] = -1;
+      if (i >= n16) continue;
+      const int rr = r0 + i / n8;
+      const int t = rr + base < T ? rr + base : rr + base - T;
+      row[q] = t;
+      c8[q] = i - (i / n8) * n8;
+#pragma unroll
+      for (int j = 0; j < K; ++j) {
+        v[q][j] = gload16(a.y + ((size_t)t * K + j) * N + (size_t)c8[q] * 8);
+        wt[q][j] = a.w[(size_t)t * K + j];
+      }
+      if constexpr (LOCAL) {
+#pragma unroll
+        for (int s = 0; s < kMaxRanks; ++s)
+          if (s < a.R && s != a.local) pv[q][s] = gload16(a.peers[s] + (size_t)t * N + (size_t)c8[q] * 8);
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < U; ++q) {
+      if (row[q] < 0) continue;
+      float acc[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] = wt[q][0] * bf16_to_f32((v[q][0][e >> 1] >> ((e & 1) * 16)) & 0xFFFFu);
+#pragma unroll
+      for (int j = 1; j < K; ++j) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          acc[e] = __builtin_fmaf(wt[q][j], bf16_to_f32((v[q][j][e >> 1] >> ((e & 1) * 16)) & 0xFFFFu), acc[e]);
+      }
+      const u32x4_t o = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]), pack_bf16x2(acc[4], acc[5]),
+                         pack_bf16x2(acc[6], acc[7])};
+      gstore16(a.partial + (size_t)row[q] * N + (size_t)c8[q] * 8, o);
+      if constexpr (LOCAL) {
+        // rank order; the local rank's term is `o` (selected per unrolled
+        // rank, so the register arrays are never indexed at run time)
+        float r[8];
+#pragma unroll
+        for (int s = 0; s < kMaxRanks; ++s)
+          if (s < a.R) {
+            const u32x4_t x = (s == a.local) ? o : pv[q][s];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const float f = bf16_to_f32((x[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu);
+              r[e] = (s == 0) ? f : r[e] + f;
+            }
+          }
+        const u32x4_t ro = {pack_bf16x2(r[0], r[1]), pack_bf16x2(r[2], r[3]), pack_bf16x2(r[4], r[5]),
+                            pack_bf16x2(r[6], r[7])};
+        gstore16(a.out + (size_t)(row[q] - base) * N + (size_t)c8[q] * 8, ro);
+      }
+    }
+  }
+}
+
+// Tasks: first the local block's rows (rotated rows [0, m)) in tasks of CRL
+// rows, then the others in tasks of CR rows; a local row moves (topk + R + 1)
+// rows of data against topk + 1 for the others, hence the smaller tasks. The
+// local rows' reduce needs only the peers' rows (inputs of the call) and the
+// row's own combined value, so no task waits on another, and the tasks are
+// dealt round-robin (task u to workgroup u mod grid): the tasks are short
+// and alike, and a shared ticket counter became the bottleneck at this rate.
+template <int K>
+__global__ __launch_bounds__(kThreads) void moe_combine_rs_kernel(CombArgs args) {
+  __shared__ uint32_t s_bcast[8];
+  const Common& cm = args.cm;
+  const uint32_t epoch = read_epoch(cm.hdr, s_bcast);
+  for (uint32_t u = blockIdx.x; (int)u < args.n_comb; u += gridDim.x) {
+    const uint64_t t0 = now_ticks();
+    const bool local = (int)u < args.n_lt;
+    const int r0 = local ? (int)u * args.CRL : args.m + ((int)u - args.n_lt) * args.CR;
+    const int r1 = local ? min(r0 + args.CRL, args.m) : min(r0 + args.CR, args.T);
+    if (local)
+      combine_rows<true, kCombineChunksLocal, K>(args, r0, r1);
+    else
+      combine_rows<false, kCombineChunks, K>(args, r0, r1);
+    trace_task(cm, u, 6, (uint32_t)r0, (uint32_t)r1, local ? (uint32_t)(r1 - r0) : 0u, 0, epoch, t0, t0, 0, 0);
+  }
+  finish(cm.hdr, epoch);
+}
+
 // ---------------------------------------------------------------- fill
 
 __global__ void fill_u32_kernel(uint32_t* p, size_t n, uint32_t v, int release) {
@@ -729,6 +830,18 @@ hipError_t launch_moe(const RouteArgs& r, const MoeArgs& a, int tile, int grid, 
     case OCG_TILE_128x224: hipLaunchKernelGGL((moe_gemm_kernel<128, 224>), dim3(grid), dim3(kThreads), 0, s, a); break;
     case OCG_TILE_256x224: hipLaunchKernelGGL((moe_gemm_kernel<256, 224>), dim3(grid), dim3(kThreads), 0, s, a); break;
     case OCG_TILE_320x224: hipLaunchKernelGGL((moe_gemm_kernel<320, 224>), dim3(grid), dim3(kThreads), 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+// One kernel per slot count, so registers are sized for exactly topk rows.
+hipError_t launch_moe_combine_rs(const CombArgs& a, int grid, hipStream_t s) {
+  switch (a.topk) {
+    case 1: hipLaunchKernelGGL((moe_combine_rs_kernel<1>), dim3(grid), dim3(kThreads), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((moe_combine_rs_kernel<2>), dim3(grid), dim3(kThreads), 0, s, a); break;
+    case 3: hipLaunchKernelGGL((moe_combine_rs_kernel<3>), dim3(grid), dim3(kThreads), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((moe_combine_rs_kernel<4>), dim3(grid), dim3(kThreads), 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -16,6 +16,8 @@ constexpr int kRouteBlock = 64;       // tokens per routing block (one wave per 
 constexpr int kMaxRouteSlots = 16384; // token slots (T * topk) per call
 constexpr int kMaxExperts = 64;
 constexpr int kMaxTopk = 4;
+constexpr int kCombineChunks = 8;        // 16-byte chunks per thread and round of a TopK-Reduce task
+constexpr int kCombineChunksLocal = 2;   // the same for the local block's rows (R + topk loads each)
 constexpr int kMinSlabRows = 16;
 // grouped GEMM presets: 128x224, 256x224, 320x224 (the smallest is used to
 // size the tile lookup table)
@@ -73,6 +75,20 @@ struct RsArgs {
   Common cm;
 };
 
+// TopK-Reduce + ReduceScatter: tasks of CR rows of the token order rotated
+// to start at the local block; every row's combined value goes to the
+// partial, and the local block's rows are also reduced over the ranks.
+struct CombArgs {
+  const uint16_t* y;            // [T*topk][N], token-slot order
+  const float* w;               // [T][topk]
+  const uint16_t* peers[kMaxRanks];
+  uint16_t* partial;            // [T][N]
+  uint16_t* out;                // [m][N]
+  int topk, CR, CRL, n_lt, n_comb;   // rows per task (other / local rows), #local tasks, #tasks
+  int R, local, m, T, N;
+  Common cm;
+};
+
 struct MoeArgs {
   const uint16_t* chunks[kMaxRanks];
   const uint16_t* w;            // [E][K][N]
@@ -104,6 +120,7 @@ struct RouteArgs {
 hipError_t launch_ag_gemm(const AgArgs& a, int tile, int grid, hipStream_t s);
 hipError_t launch_gemm_rs(const RsArgs& a, int tile, int grid, hipStream_t s);
 hipError_t launch_moe(const RouteArgs& r, const MoeArgs& a, int tile, int grid, hipStream_t s);
+hipError_t launch_moe_combine_rs(const CombArgs& a, int grid, hipStream_t s);
 hipError_t launch_fill_u32(uint32_t* p, size_t n, uint32_t v, int release, hipStream_t s);
 // Resident workgroups per CU of each persistent kernel (op, tile preset).
 int resident_per_cu(int op, int tile);

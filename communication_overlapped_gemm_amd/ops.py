@@ -175,6 +175,43 @@ def ag_grouped_gemm(a_chunks: Sequence[torch.Tensor], logits: torch.Tensor, w: t
     return o
 
 
+def moe_combine_rs(y: torch.Tensor, topk_w: torch.Tensor, peer_partials: Sequence[Optional[torch.Tensor]],
+                   local_rank: int = 0, *, partial: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                   workspace: Optional[Workspace] = None, config: Optional[Config] = None,
+                   stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """MoE TopK-Reduce + ReduceScatter (one rank's share): y [T*topk, N] bf16
+    in token-slot order, topk_w [T, topk] fp32, R = len(peer_partials) peer
+    combined partials [T, N]. Returns (partial [T, N], out [T/R, N])."""
+    R = len(peer_partials)
+    _check_bf16(y, "y")
+    if topk_w.dtype != torch.float32 or not topk_w.is_contiguous() or topk_w.dim() != 2:
+        raise ValueError("topk_w must be a contiguous float32 [T, topk] CUDA tensor")
+    T, topk = topk_w.shape
+    N = y.shape[1]
+    if tuple(y.shape) != (T * topk, N) or T % R:
+        raise ValueError("y must be [T*topk, N] with T a multiple of R")
+    m = T // R
+    ptrs = (C.c_void_p * R)()
+    for s, p in enumerate(peer_partials):
+        if s == local_rank:
+            continue
+        _check_bf16(p, f"peer_partials[{s}]", (T, N))
+        ptrs[s] = p.data_ptr()
+    dev = y.device
+    if partial is None:
+        partial = torch.empty((T, N), dtype=torch.bfloat16, device=dev)
+    if out is None:
+        out = torch.empty((m, N), dtype=torch.bfloat16, device=dev)
+    _check_bf16(partial, "partial", (T, N))
+    _check_bf16(out, "out", (m, N))
+    ws = workspace or Workspace.cached(_lib.OP_MOE_COMBINE_RS, R, m, 0, N, 0, topk, device=dev.index)
+    cfg = _cfg(config)
+    check(lib.ocg_moe_combine_rs(handle(dev.index), y.data_ptr(), topk_w.data_ptr(), R, local_rank, m, N, topk, ptrs,
+                                 partial.data_ptr(), out.data_ptr(), ws.ptr, ws.nbytes, C.byref(cfg),
+                                 _stream_ptr(stream)), "ocg_moe_combine_rs")
+    return partial, out
+
+
 def signal(flags: torch.Tensor, value: int, stream=None) -> None:
     """Peer-notify stand-in: write `value` into every uint32 of `flags`."""
     if flags.dtype not in (torch.int32, torch.uint32) or not flags.is_contiguous():

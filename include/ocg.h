@@ -53,6 +53,7 @@ extern "C" {
 #define OCG_OP_AG_GEMM 0
 #define OCG_OP_GEMM_RS 1
 #define OCG_OP_AG_GROUPED_GEMM 2
+#define OCG_OP_MOE_COMBINE_RS 3
 
 /* Fused (default), GEMM tiles only with every flag treated as published
  * (measurement of the GEMM part; expects the gathered buffer filled), or
@@ -75,8 +76,9 @@ extern "C" {
 /* Trace record written per executed task when ocg_config.trace is set
  * (64 bytes), at slot: AG-GEMM / MoE copy task u -> u, tile v -> n_copy + v;
  * GEMM-RS tile v -> v, reduce strip j -> n_tiles + j (v = tile index in the
- * grouped tile order). kind: 1 copy task, 2 AG-GEMM tile, 3 GEMM-RS tile,
- * 4 MoE tile, 5 GEMM-RS reduce strip. Times are the GPU's constant 100 MHz
+ * grouped tile order; TopK-Reduce: task u -> u).
+ * kind: 1 copy task, 2 AG-GEMM tile, 3 GEMM-RS tile, 4 MoE tile, 5 GEMM-RS
+ * reduce strip, 6 TopK-Reduce task. Times are the GPU's constant 100 MHz
  * clock. */
 typedef struct ocg_trace_rec {
   uint32_t ticket, kind;
@@ -194,6 +196,36 @@ int ocg_ag_grouped_gemm(ocg_handle h, const void* const* a_chunks, int R, int lo
                         float* topk_w, int32_t* perm, int32_t* expert_offsets, void* out,
                         void* workspace, size_t ws_bytes, const ocg_config* cfg, void* stream);
 
+/* MoE TopK-Reduce + ReduceScatter, the tail of the MoE layer ("TileLink ...
+ * (MLSys 2025 talk summary)", section "Experimental Setup & Results", lists
+ * TopK-Reduce and ReduceScatter among the MoE operators it overlaps; the
+ * formula is the plain reading of a gate-weighted top-k combine followed by
+ * the ReduceScatter of the GEMM-ReduceScatter call):
+ *   P_l[t] = sum over j < topk of topk_w[t][j] * y[t*topk + j]   (t < T = R*m)
+ *   out    = sum over ranks s = 0..R-1 of P_s[rows local*m .. (local+1)*m)
+ * P_l is computed in fp32 (slot order, fma), rounded once to bf16 and stored
+ * in `partial` (the send buffer); the reduce sums the R bf16 partials in
+ * ascending rank order in fp32 with one rounding (as ocg_gemm_rs). Tasks of
+ * rows cover the local block's rows first (smaller tasks: a local row also
+ * reads the R-1 peer rows and writes out); a local row is reduced by the
+ * task that combines it (its inputs are the peers' rows and its own rounded
+ * value), so no task waits on another.
+ *   y             : bf16 [R*m*topk, N], token-slot order (row t*topk + j)
+ *   topk_w        : fp32 [R*m, topk] gate weights (4-byte aligned)
+ *   peer_partials : R device pointers, bf16 [R*m, N] each; entry local_rank
+ *                   is ignored (the local partial is computed here)
+ *   partial       : bf16 [R*m, N], written
+ *   out           : bf16 [m, N], written
+ * Requires N % 8 == 0, 1 <= topk <= 4, R*m*N*2 < 2^31, 16-byte aligned
+ * bf16 pointers; workspace from ocg_workspace_bytes(OCG_OP_MOE_COMBINE_RS,
+ * R, m, 0, N, 0, topk). Trace: kind 6 per task (a, b = rows [a, b) of the
+ * order rotated to start at the local block, c = b - a for a local task,
+ * else 0). Errors as for the other calls. */
+int ocg_moe_combine_rs(ocg_handle h, const void* y, const float* topk_w, int R, int local_rank,
+                       int64_t m, int64_t N, int topk, const void* const* peer_partials,
+                       void* partial, void* out, void* ws, size_t ws_bytes,
+                       const ocg_config* cfg, void* stream);
+
 /* Stand-in for a peer's remote notify: writes `value` into `count` uint32
  * flags at `flags` (device) with release semantics, on `stream`. */
 int ocg_signal(uint32_t* flags, int count, uint32_t value, void* stream);
@@ -210,7 +242,9 @@ const char* ocg_status_string(int status);
 /* Resolved plan parameters for a call with config `cfg` (NULL = defaults):
  * out[0]=tile preset, out[1]=BM, out[2]=BN, out[3]=slab rows,
  * out[4]=copy rows, out[5]=#copy tasks, out[6]=#tiles (static ops),
- * out[7]=#slabs. For GEMM_RS pass m = M. E and topk are the grouped GEMM's
+ * out[7]=#slabs. For OCG_OP_MOE_COMBINE_RS: out[0]=-1, out[3]=rows per
+ * task outside the local block, out[4]=rows per local task, out[5]=#tasks,
+ * out[6]=#local tasks (the first ones), the rest 0. For GEMM_RS pass m = M. E and topk are the grouped GEMM's
  * expert count and picks per token (they choose its default tile; ignored
  * by the other ops). Returns OCG_OK or an error. */
 int ocg_plan_info(int op, int R, int local_rank, int64_t m, int64_t K, int64_t N, int E, int topk,

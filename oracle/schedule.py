@@ -218,27 +218,17 @@ def moe_tiles(counts, offsets, perm, topk, R, m, N, local, BM, BN, S):
     return out
 
 
-def combine_rs_plan(R, T, local, CR, RR):
-    """Ticket list of the TopK-Reduce + ReduceScatter kernel.
-
-    Combine tasks: ("combine", slot, rows) where rows are the CR token rows
-    (u*CR .. u*CR+CR) of the row order rotated to start at the local block
-    (row t = (r + local*T/R) mod T), so the local block's rows come first.
-    Reduce strips: ("reduce", slot, row0, row1, deps) over RR rows of the
-    local block, deps = the combine tasks holding those rows."""
+def combine_rs_plan(R, T, local, CR, CRL):
+    """Ticket list of the TopK-Reduce + ReduceScatter kernel: tasks
+    ("combine", slot, rows, is_local) over the row order rotated to start at
+    the local block (row t = (r + local*T/R) mod T): first the local block's
+    rows (rotated [0, T/R)) in tasks of CRL rows, which also reduce those rows
+    over the ranks, then the other rows in tasks of CR rows."""
     blk = T // R
     base = local * blk
-    n_comb = _cdiv(T, CR)
     out = []
-    for u in range(n_comb):
-        rows = tuple((r + base) % T for r in range(u * CR, min((u + 1) * CR, T)))
-        out.append(("combine", u, rows))
-    t = n_comb
-    r = 0
-    while r < blk:
-        r1 = min(r + RR, blk)
-        deps = tuple(range(r // CR, (r1 - 1) // CR + 1))
-        out.append(("reduce", t, base + r, base + r1, deps))
-        t += 1
-        r = r1
+    spans = [(r, min(r + CRL, blk), True) for r in range(0, blk, CRL)]
+    spans += [(r, min(r + CR, T), False) for r in range(blk, T, CR)]
+    for u, (r0, r1, is_local) in enumerate(spans):
+        out.append(("combine", u, tuple((r + base) % T for r in range(r0, r1)), is_local))
     return out

@@ -150,23 +150,14 @@ def test_tile_queues_partition(n_tiles):
 
 
 def test_combine_rs_plan_covers_rows_once_local_block_first():
-    """Combine tasks cover every token row exactly once, the local block's rows
-    in the first tasks; each strip depends exactly on the tasks holding its
-    rows, all of them earlier tickets."""
-    for R, T, local, CR, RR in [(8, 4096, 0, 4, 2), (8, 4096, 5, 4, 2), (3, 30, 2, 7, 4), (1, 10, 0, 3, 5)]:
-        plan = sch.combine_rs_plan(R, T, local, CR, RR)
-        comb = [p for p in plan if p[0] == "combine"]
-        rows = [r for p in comb for r in p[2]]
+    """Tasks cover every token row exactly once; the local block's rows are
+    exactly the rows of the first (local) tasks."""
+    for R, T, local, CR, CRL in [(8, 4096, 0, 9, 2), (8, 4096, 5, 9, 2), (3, 30, 2, 7, 3), (1, 10, 0, 3, 4)]:
+        plan = sch.combine_rs_plan(R, T, local, CR, CRL)
+        rows = [r for p in plan for r in p[2]]
         assert sorted(rows) == list(range(T))
         blk = T // R
-        n_local_tasks = -(-blk // CR)
-        first = [r for p in comb[:n_local_tasks] for r in p[2]]
-        assert set(range(local * blk, (local + 1) * blk)) <= set(first)
-        strips = [p for p in plan if p[0] == "reduce"]
-        covered = []
-        for _, slot, r0, r1, deps in strips:
-            covered += list(range(r0, r1))
-            held = {r for d in deps for r in comb[d][2]}
-            assert set(range(r0, r1)) <= held and all(d < slot for d in deps)
-            assert all(set(comb[d][2]) & set(range(r0, r1)) for d in deps)
-        assert covered == list(range(local * blk, (local + 1) * blk))
+        n_lt = -(-blk // CRL)
+        assert all(p[3] for p in plan[:n_lt]) and not any(p[3] for p in plan[n_lt:])
+        assert {r for p in plan[:n_lt] for r in p[2]} == set(range(local * blk, (local + 1) * blk))
+        assert all(len(p[2]) <= (CRL if p[3] else CR) for p in plan)
