@@ -27,13 +27,13 @@ Readings where the pages are silent (each is also listed in the design doc):
       applied to the GEMM output;
   R4  "sorted by expert" is stable in (expert, token, slot); token-slot order
       means output row t*topk + slot;
-  R5  TopK-Reduce: a token's output is the gate-weighted sum of its top-k
+  R11 TopK-Reduce: a token's output is the gate-weighted sum of its top-k
       slot rows, P[t] = sum_j w[t, j] * Y[t*topk + j]; the ReduceScatter that
       follows it is the fixed-order reduce of R2 over the ranks' combined
       partials [T, N], row block l = the l-th rank's m tokens; the local
       combined partial enters that reduce as bfloat16.
   [TL-EXP] names TopK-Reduce among the MoE operators it overlaps; it prints
-  neither its formula nor its precision, hence R5.
+  neither its formula nor its precision, hence R11.
 """
 from __future__ import annotations
 
@@ -249,7 +249,7 @@ def ag_grouped_gemm_entries(a_chunks, ids, w_bits, slots, cols):
 
 
 # --------------------------------------------------------------------------
-# MoE TopK-Reduce + ReduceScatter  [TL-EXP] (reading R5)
+# MoE TopK-Reduce + ReduceScatter  [TL-EXP] (reading R11)
 # --------------------------------------------------------------------------
 
 
