@@ -24,7 +24,8 @@ ERR_NO_DEVICE = -6
 
 OP_AG_GEMM, OP_GEMM_RS, OP_AG_GROUPED_GEMM, OP_MOE_COMBINE_RS = 0, 1, 2, 3
 MODE_FUSED, MODE_GEMM_ONLY, MODE_COPY_ONLY = 0, 1, 2
-TILE_AUTO, TILE_256x224, TILE_128x224, TILE_128x256, TILE_128x128, TILE_256x256, TILE_320x224 = -1, 0, 1, 2, 3, 4, 5
+TILE_AUTO, TILE_256x224, TILE_128x224, TILE_128x256, TILE_128x128, TILE_256x256, TILE_320x224, TILE_288x224 = (
+    -1, 0, 1, 2, 3, 4, 5, 6)
 
 EXPORTS = [
     "ocg_config_default", "ocg_create", "ocg_destroy", "ocg_workspace_bytes",

@@ -73,7 +73,7 @@ bool shape_ok(int R, int64_t m, int64_t K, int64_t N) {
 // Estimated cost of a tile preset: rounds of the persistent grid times the
 // tile area, derated for the smaller wave tiles.
 int choose_tile(int64_t M, int64_t N, int cus) {
-  static const double eff[OCG_TILE_COUNT] = {1.0, 0.9, 0.92, 0.75, 0.9, 0.0};
+  static const double eff[OCG_TILE_COUNT] = {1.0, 0.9, 0.92, 0.75, 0.9, 0.0, 0.0};
   int best = OCG_TILE_128x128;
   double best_cost = 1e300;
   for (int t = 0; t < OCG_TILE_COUNT; ++t) {
@@ -89,17 +89,20 @@ int choose_tile(int64_t M, int64_t N, int cus) {
   return best;
 }
 
-// Grouped GEMM: one row tile per expert where the rows an expert gets
-// (T*topk/E on average, plus three standard deviations of the count) fit in
-// a preset, the smallest such; 256-row tiles when experts are larger. A
-// second row tile for the few rows past a tile boundary would cost as much
-// as a full one.
+// Grouped GEMM: one row tile per expert where the rows an expert gets fit
+// in a preset -- the count is binomial (T tokens, each picking the expert
+// with probability topk/E); its mean plus two standard deviations is taken
+// as the rows to hold -- the smallest such preset; 256-row tiles when experts
+// are larger. A second row tile for the few rows past a tile boundary would
+// cost as much as a full one; an expert past the estimate still gets one.
 int choose_moe_tile(int64_t T, int E, int topk) {
   if (E < 1) return OCG_TILE_256x224;
-  const double avg = (double)T * topk / E;
-  const double hi = avg + 3.0 * sqrt(avg) + 1.0;
+  const double p = (double)topk / E;
+  const double avg = (double)T * p;
+  const double hi = avg + 2.0 * sqrt(avg * (1.0 - p));
   if (hi <= 128) return OCG_TILE_128x224;
   if (hi <= 256) return OCG_TILE_256x224;
+  if (hi <= 288) return OCG_TILE_288x224;
   if (hi <= 320) return OCG_TILE_320x224;
   return OCG_TILE_256x224;
 }
@@ -116,7 +119,8 @@ int resolve(int op, int R, int64_t m, int64_t K, int64_t N, int E, int topk, con
   else
     r->tile = c.tile < 0 ? choose_tile(M, N, cus) : c.tile;
   if (r->tile < 0 || r->tile >= OCG_TILE_COUNT) return OCG_ERR_INVALID_ARG;
-  if (op == OCG_OP_AG_GROUPED_GEMM ? !moe_tile_ok(r->tile) : r->tile == OCG_TILE_320x224) return OCG_ERR_INVALID_ARG;
+  if (op == OCG_OP_AG_GROUPED_GEMM ? !moe_tile_ok(r->tile) : (r->tile == OCG_TILE_320x224 || r->tile == OCG_TILE_288x224))
+    return OCG_ERR_INVALID_ARG;
   r->BM = tile_bm(r->tile);
   r->BN = tile_bn(r->tile);
   r->S = c.slab_rows > 0 ? c.slab_rows : r->BM;

@@ -59,14 +59,20 @@ struct Gemm {
   static constexpr int S = (BM == 128 && BN == 128) ? 4 : ((150 * 1024 / STAGE) < 6 ? 150 * 1024 / STAGE : 6);
   static constexpr int A_INST = A_BYTES / 1024;     // 1 KiB DMA instructions per stage
   static constexpr int B_INST = B_BYTES / 1024;
-  static constexpr int A_PER_WAVE = A_INST / 4;
+  static constexpr int A_PER_WAVE = (A_INST + 3) / 4;  // A instruction of wave w: see a_block
   static constexpr int B_PER_WAVE = (B_INST + 3) / 4;  // B instruction j = wave + 4*i
   static constexpr int NDMA = A_PER_WAVE + B_PER_WAVE;  // loads per wave per stage
   static constexpr int RING = S * STAGE;
+  // Tiles with more accumulators than the 256-entry accumulator file keep
+  // one set of B fragments instead of two (block g of the next stage is read
+  // into b[g] right after MFMA group g used it): it lowers the register
+  // pressure of the 320x224 tile (280 accumulators per lane) and measured
+  // faster there, slower for tiles that fit.
+  static constexpr bool SINGLE_B = FM * FN * 4 > 256;
   static constexpr int LD_C = BN + 8;               // epilogue staging row (elements)
   static constexpr int LDS_BYTES = (RING > BM * LD_C * 2) ? RING : BM * LD_C * 2;
   static_assert(WM % 16 == 0 && WN % 16 == 0 && BN % 32 == 0, "whole 16x16 blocks per wave, 32-column B blocks");
-  static_assert(A_INST % 4 == 0, "A DMA instructions split evenly over the waves");
+  static_assert(A_INST >= 4, "every wave has A loads");
   static_assert(NDMA <= 2 * FN, "at most two loads behind each MFMA group");
   static_assert(S >= 4 && (S - 2) * NDMA <= 63, "vmcnt waits fit the 6-bit counter");
   static_assert(LDS_BYTES <= 160 * 1024 - 64, "fits the 160 KiB LDS of a gfx950 CU");
@@ -113,15 +119,30 @@ struct TileCtx {
   int N, n0, nk;
 };
 
+// 1 KiB block of the slot's A part (rows 16b..16b+15) that A instruction i
+// of wave `wave` loads: consecutive blocks per wave when they split evenly,
+// else block wave + 4i, a wave past the last block repeating its previous
+// one (same source, same LDS bytes), so every wave issues A_PER_WAVE loads.
+template <int BM, int BN>
+__device__ __forceinline__ int a_block(int wave, int i) {
+  using G = Gemm<BM, BN>;
+  if constexpr (G::A_INST % 4 == 0) {
+    return wave * G::A_PER_WAVE + i;
+  } else {
+    const int j = wave + 4 * i;
+    return j < G::A_INST ? j : j - 4;
+  }
+}
+
 // Row of the tile that lane `lane` of DMA instruction i (of wave `wave`) loads.
 template <int BM, int BN>
 __device__ __forceinline__ int dma_row(int wave, int i, int lane) {
-  return (wave * Gemm<BM, BN>::A_PER_WAVE + i) * 16 + (lane >> 2);
+  return a_block<BM, BN>(wave, i) * 16 + (lane >> 2);
 }
 
 // Per-tile constants of this wave's loads: the A instruction i loads rows
-// 16*(wave*A_PER_WAVE + i) + lane/4, chunk (lane & 3) ^ swz_a(row), into the
-// slot's 1 KiB block wave*A_PER_WAVE + i; B instruction i (j = wave + 4i)
+// 16*b + lane/4 (b = a_block(wave, i)), chunk (lane & 3) ^ swz_a(row), into
+// the slot's 1 KiB block b; B instruction i (j = wave + 4i)
 // loads k row (j & 1)*16 + lane/4 of column block j/2, chunk pair
 // (lane & 3) ^ 2*swz_b(k), into block j of the slot's B part. A wave whose
 // last j is past the B blocks repeats its previous B load (same source, same
@@ -141,7 +162,7 @@ __device__ __forceinline__ DmaPlan<BM, BN> make_dma_plan(const TileCtx<BM, BN>& 
   DmaPlan<BM, BN> d;
 #pragma unroll
   for (int i = 0; i < G::A_PER_WAVE; ++i) {
-    const int r = (wave * G::A_PER_WAVE + i) * 16 + (lane >> 2);
+    const int r = a_block<BM, BN>(wave, i) * 16 + (lane >> 2);
     d.a[i] = t.rowp[i] + ((lane & 3) ^ swz_a(r)) * 16;
   }
 #pragma unroll
@@ -164,7 +185,7 @@ __device__ __forceinline__ void dma_one(uint32_t slot, const DmaPlan<BM, BN>& d,
                                         int s, int wave) {
   using G = Gemm<BM, BN>;
   if constexpr (I < G::A_PER_WAVE) {
-    dma_global(slot + (wave * G::A_PER_WAVE + I) * 1024, d.a[I] + s * (BKS * 2));
+    dma_global(slot + a_block<BM, BN>(wave, I) * 1024, d.a[I] + s * (BKS * 2));
   } else {
     constexpr int i = I - G::A_PER_WAVE;
     dma_buffer(slot + d.b_dst[i], brs, d.b_off[i] + (uint32_t)s * d.b_step);
@@ -248,20 +269,29 @@ __device__ __forceinline__ void dma_after_group(uint32_t slot, const DmaPlan<BM,
 
 // MFMA group GI (column block GI) of `cur`, preceded by the two transposing
 // reads of the same block of `nxt` and followed by its share of the loads.
+// With SINGLE_B the B fragments live in `bs` only and the reads follow the
+// group's MFMAs.
 template <int BM, int BN, int GI = 0>
 __device__ __forceinline__ void mfma_groups(const Frags<BM, BN>& cur, Frags<BM, BN>& nxt, OCG_LDS const char* st,
                                             const FragAddr& fa, AccTile<BM, BN>& acc, uint32_t slot,
                                             const DmaPlan<BM, BN>& d, const __amdgpu_buffer_rsrc_t& brs, int s,
-                                            int wave) {
+                                            int wave, bf16x8_t (&bs)[Gemm<BM, BN>::FN]) {
   using G = Gemm<BM, BN>;
   if constexpr (GI < G::FN) {
-    nxt.b[GI] = read_b_frag<BM, BN>(st, fa, GI);
+    if constexpr (G::SINGLE_B) {
 #pragma unroll
-    for (int f = 0; f < G::FM; ++f)
-      acc.v[f][GI] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur.b[GI], cur.a[f], acc.v[f][GI], 0, 0, 0);
+      for (int f = 0; f < G::FM; ++f)
+        acc.v[f][GI] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bs[GI], cur.a[f], acc.v[f][GI], 0, 0, 0);
+      bs[GI] = read_b_frag<BM, BN>(st, fa, GI);
+    } else {
+      nxt.b[GI] = read_b_frag<BM, BN>(st, fa, GI);
+#pragma unroll
+      for (int f = 0; f < G::FM; ++f)
+        acc.v[f][GI] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur.b[GI], cur.a[f], acc.v[f][GI], 0, 0, 0);
+    }
     dma_after_group<BM, BN, GI>(slot, d, brs, s, wave);
     __builtin_amdgcn_sched_barrier(0);
-    mfma_groups<BM, BN, GI + 1>(cur, nxt, st, fa, acc, slot, d, brs, s, wave);
+    mfma_groups<BM, BN, GI + 1>(cur, nxt, st, fa, acc, slot, d, brs, s, wave, bs);
   }
 }
 
@@ -272,11 +302,11 @@ template <int BM, int BN>
 __device__ __forceinline__ void stage_body(const Frags<BM, BN>& cur, Frags<BM, BN>& nxt, OCG_LDS const char* st,
                                            const FragAddr& fa, AccTile<BM, BN>& acc, uint32_t slot,
                                            const DmaPlan<BM, BN>& d, const __amdgpu_buffer_rsrc_t& brs, int s,
-                                           int wave) {
+                                           int wave, bf16x8_t (&bs)[Gemm<BM, BN>::FN]) {
   using G = Gemm<BM, BN>;
 #pragma unroll
   for (int f = 0; f < G::FM; ++f) nxt.a[f] = *(OCG_LDS const bf16x8_t*)(st + fa.a + f * 1024);
-  mfma_groups<BM, BN>(cur, nxt, st, fa, acc, slot, d, brs, s, wave);
+  mfma_groups<BM, BN>(cur, nxt, st, fa, acc, slot, d, brs, s, wave, bs);
   // The reads of `nxt` had the whole MFMA block to land.
   lds_reads_done();
 }
@@ -315,9 +345,16 @@ __device__ __forceinline__ void mainloop(OCG_LDS char* smem, const TileCtx<BM, B
   Frags<BM, BN> f0, f1;
   read_frags<BM, BN>(smem, fa, f0);
   lds_reads_done();
+  // SINGLE_B: the one set of B fragments (unused otherwise)
+  bf16x8_t bs[G::FN];
+  if constexpr (G::SINGLE_B) {
+#pragma unroll
+    for (int g = 0; g < G::FN; ++g) bs[g] = f0.b[g];
+  }
   uint32_t rd = G::STAGE, wr = (S - 1) * G::STAGE;   // slot offsets of stages k+1 and k+S-1
   auto step = [&](int k, Frags<BM, BN>& cur, Frags<BM, BN>& nxt) {
-    stage_body<BM, BN>(cur, nxt, smem + rd, fa, acc, base + wr, d, t.brs, k + S - 1 < nk ? k + S - 1 : nk - 1, wave);
+    stage_body<BM, BN>(cur, nxt, smem + rd, fa, acc, base + wr, d, t.brs, k + S - 1 < nk ? k + S - 1 : nk - 1, wave,
+                       bs);
     rd = (rd + G::STAGE == S * G::STAGE) ? 0u : rd + G::STAGE;
     wr = (wr + G::STAGE == S * G::STAGE) ? 0u : wr + G::STAGE;
   };

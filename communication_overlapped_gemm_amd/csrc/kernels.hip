@@ -829,6 +829,7 @@ hipError_t launch_moe(const RouteArgs& r, const MoeArgs& a, int tile, int grid, 
   switch (tile) {
     case OCG_TILE_128x224: hipLaunchKernelGGL((moe_gemm_kernel<128, 224>), dim3(grid), dim3(kThreads), 0, s, a); break;
     case OCG_TILE_256x224: hipLaunchKernelGGL((moe_gemm_kernel<256, 224>), dim3(grid), dim3(kThreads), 0, s, a); break;
+    case OCG_TILE_288x224: hipLaunchKernelGGL((moe_gemm_kernel<288, 224>), dim3(grid), dim3(kThreads), 0, s, a); break;
     case OCG_TILE_320x224: hipLaunchKernelGGL((moe_gemm_kernel<320, 224>), dim3(grid), dim3(kThreads), 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
@@ -867,6 +868,7 @@ int resident_per_cu(int op, int tile) {
     switch (tile) {
       case OCG_TILE_128x224: return occ(moe_gemm_kernel<128, 224>);
       case OCG_TILE_256x224: return occ(moe_gemm_kernel<256, 224>);
+      case OCG_TILE_288x224: return occ(moe_gemm_kernel<288, 224>);
       case OCG_TILE_320x224: return occ(moe_gemm_kernel<320, 224>);
     }
     return 1;

@@ -19,10 +19,12 @@ constexpr int kMaxTopk = 4;
 constexpr int kCombineChunks = 8;        // 16-byte chunks per thread and round of a TopK-Reduce task
 constexpr int kCombineChunksLocal = 2;   // the same for the local block's rows (R + topk loads each)
 constexpr int kMinSlabRows = 16;
-// grouped GEMM presets: 128x224, 256x224, 320x224 (the smallest is used to
-// size the tile lookup table)
+// grouped GEMM presets: 128x224, 256x224, 288x224, 320x224 (the smallest is
+// used to size the tile lookup table)
 constexpr int kMoeTileSmall = OCG_TILE_128x224;
-inline bool moe_tile_ok(int t) { return t == OCG_TILE_128x224 || t == OCG_TILE_256x224 || t == OCG_TILE_320x224; }
+inline bool moe_tile_ok(int t) {
+  return t == OCG_TILE_128x224 || t == OCG_TILE_256x224 || t == OCG_TILE_288x224 || t == OCG_TILE_320x224;
+}
 
 // Workspace header (first 256 bytes of every workspace).
 struct WsHeader {

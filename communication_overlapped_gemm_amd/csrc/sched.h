@@ -177,7 +177,7 @@ OCG_HD bool rs_tile_touches_local(const RsPlan& p, int rb) {
 }
 
 // Tile presets: {BM, BN} = {256,224}, {128,224}, {128,256}, {128,128}.
-OCG_HD int tile_bm(int t) { return t == 5 ? 320 : ((t == 0 || t == 4) ? 256 : 128); }
+OCG_HD int tile_bm(int t) { return t == 6 ? 288 : t == 5 ? 320 : ((t == 0 || t == 4) ? 256 : 128); }
 OCG_HD int tile_bn(int t) { return (t == 2 || t == 4) ? 256 : (t == 3 ? 128 : 224); }
 
 }  // namespace ocg

@@ -63,7 +63,7 @@ extern "C" {
 #define OCG_MODE_COPY_ONLY 2
 
 /* Tile presets (rows x columns of C per workgroup tile, K step 64);
- * OCG_TILE_320x224 is for the grouped GEMM only. */
+ * OCG_TILE_288x224 and OCG_TILE_320x224 are for the grouped GEMM only. */
 #define OCG_TILE_AUTO (-1)
 #define OCG_TILE_256x224 0
 #define OCG_TILE_128x224 1
@@ -71,7 +71,8 @@ extern "C" {
 #define OCG_TILE_128x128 3
 #define OCG_TILE_256x256 4
 #define OCG_TILE_320x224 5
-#define OCG_TILE_COUNT 6
+#define OCG_TILE_288x224 6
+#define OCG_TILE_COUNT 7
 
 /* Trace record written per executed task when ocg_config.trace is set
  * (64 bytes), at slot: AG-GEMM / MoE copy task u -> u, tile v -> n_copy + v;
@@ -185,10 +186,13 @@ int ocg_gemm_rs(ocg_handle h, const void* a, const void* b, int64_t M, int64_t K
  *   out         : bf16 [R*m*topk, N], written
  * The grouped tiles wait on the flags of every peer slab their tokens come
  * from (a per-tile lookup table built on the device after routing). Tile
- * presets: OCG_TILE_128x224, OCG_TILE_256x224 or OCG_TILE_320x224 (the
- * latter only here); OCG_TILE_AUTO takes the smallest whose rows hold the
- * rows an expert is expected to get (R*m*topk/E plus three standard
- * deviations), else 256x224. Any other preset is OCG_ERR_INVALID_ARG.
+ * presets: OCG_TILE_128x224, OCG_TILE_256x224, OCG_TILE_288x224 or
+ * OCG_TILE_320x224 (the last two only here); OCG_TILE_AUTO takes the
+ * smallest whose rows hold the rows an expert is expected to get at most
+ * (mean R*m*topk/E plus two standard deviations of the binomial count),
+ * else 256x224. An expert with more rows than a tile gets further row tiles,
+ * so every preset gives the same results. Any other preset is
+ * OCG_ERR_INVALID_ARG.
  */
 int ocg_ag_grouped_gemm(ocg_handle h, const void* const* a_chunks, int R, int local_rank,
                         int64_t m, int64_t K, const float* logits, int E, int topk,

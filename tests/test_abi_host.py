@@ -101,17 +101,22 @@ def test_plan_info_tile_choice():
 
 def test_plan_info_moe_tile_choice():
     # 4096 tokens x top-2 over 32 experts: 256 rows per expert on average,
-    # up to ~300 expected: one 320-row tile per expert
+    # standard deviation 15.5: one 288-row tile per expert
     p = ocg.plan_info(ocg.OP_AG_GROUPED_GEMM, 8, 0, 512, 4096, 1792, E=32, topk=2)
+    assert (p["BM"], p["BN"]) == (288, 224)
+    # 2048 tokens x top-2 over 16: mean 256, deviation 15.5 -> 288 as well;
+    # 1536 tokens x top-3 over 16: mean 288, deviation 16.4 -> 320
+    p = ocg.plan_info(ocg.OP_AG_GROUPED_GEMM, 8, 0, 192, 128, 448, E=16, topk=3)
     assert (p["BM"], p["BN"]) == (320, 224)
     p = ocg.plan_info(ocg.OP_AG_GROUPED_GEMM, 2, 0, 64, 128, 96, E=6, topk=2)
     assert (p["BM"], p["BN"]) == (128, 224)
     p = ocg.plan_info(ocg.OP_AG_GROUPED_GEMM, 8, 0, 1024, 128, 96, E=8, topk=2)
     assert (p["BM"], p["BN"]) == (256, 224)   # ~2048 rows per expert: many 256-row tiles
-    # the 320-row preset is the grouped GEMM's only
+    # the 288- and 320-row presets are the grouped GEMM's only
     for op, m in ((ocg.OP_AG_GEMM, 512), (ocg.OP_GEMM_RS, 4096)):
-        with pytest.raises(ocg.OcgError):
-            ocg.plan_info(op, 8, 0, m, 1792, 4096, ocg.default_config(tile=ocg.TILE_320x224))
+        for t in (ocg.TILE_320x224, ocg.TILE_288x224):
+            with pytest.raises(ocg.OcgError):
+                ocg.plan_info(op, 8, 0, m, 1792, 4096, ocg.default_config(tile=t))
 
 
 AG_CASES = [

@@ -47,7 +47,7 @@ SMALL = [
 ]
 
 
-TILES = {"auto": -1, "128x224": 1, "256x224": 0, "320x224": 5}
+TILES = {"auto": -1, "128x224": 1, "256x224": 0, "288x224": 6, "320x224": 5}
 
 
 @pytest.mark.parametrize("tile", list(TILES))
