@@ -34,6 +34,12 @@ Readings where the pages are silent (each is also listed in the design doc):
       combined partial enters that reduce as bfloat16.
   [TL-EXP] names TopK-Reduce among the MoE operators it overlaps; it prints
   neither its formula nor its precision, hence R11.
+  R12 AllGather-KV attention ([TL-EXP]: the KV AllGather overlapped with the
+      attention computation; no formula, mask or shape): each rank holds a
+      contiguous chunk of m tokens of Q, K and V; K and V are gathered in
+      rank order and rank l's queries attend, per head, over all R*m keys
+      with softmax(q . k / sqrt(d)) and no mask (context-parallel attention
+      read plainly: every query sees the whole gathered sequence).
 """
 from __future__ import annotations
 
@@ -286,3 +292,31 @@ def moe_combine_rs(y_bits, w, topk, peers, R, local_rank):
         if s != local_rank:
             out += decode_bf16(peers[s][r0:r0 + blk])
     return partial, out
+
+
+# --------------------------------------------------------------------------
+# AllGather-KV attention  [TL-EXP] (reading R12)
+# --------------------------------------------------------------------------
+
+
+def ag_attention(q_bits, k_chunks, v_chunks):
+    """Gather K and V (ascending rank order) and attend the local queries over
+    them, per head, float64.
+
+    ``q_bits``: bf16 bits [m, H, d] (the local queries); ``k_chunks`` /
+    ``v_chunks``: R bf16 arrays [m, H, d]. Returns (k_full bits, v_full bits,
+    out [m, H, d]) with out[i, h] = sum_j softmax_j(q[i,h] . k[j,h] / sqrt(d)) v[j,h]."""
+    k_full = np.concatenate([np.asarray(c) for c in k_chunks], axis=0)
+    v_full = np.concatenate([np.asarray(c) for c in v_chunks], axis=0)
+    q = decode_bf16(np.asarray(q_bits))
+    k = decode_bf16(k_full)
+    v = decode_bf16(v_full)
+    m, H, d = q.shape
+    out = np.empty((m, H, d), dtype=np.float64)
+    for h in range(H):
+        s = (q[:, h, :] @ k[:, h, :].T) / np.sqrt(d)
+        s -= s.max(axis=1, keepdims=True)
+        p = np.exp(s)
+        p /= p.sum(axis=1, keepdims=True)
+        out[:, h, :] = p @ v[:, h, :]
+    return k_full, v_full, out

@@ -420,3 +420,70 @@ def test_moe_combine_rs_zero_peers():
     for local in range(R):
         p, out = oracle.moe_combine_rs(y, w, topk, {s: zero for s in range(R) if s != local}, R, local)
         assert np.array_equal(out, p[local * m:(local + 1) * m])
+
+
+# ---------------------------------------------------------------- AllGather-KV attention
+
+
+def brute_attention(q, k, v):
+    """Per query and head: explicit softmax over all keys, loops."""
+    m, H, d = len(q), len(q[0]), len(q[0][0])
+    S = len(k)
+    out = [[[0.0] * d for _ in range(H)] for _ in range(m)]
+    for i in range(m):
+        for h in range(H):
+            s = [sum(q[i][h][e] * k[j][h][e] for e in range(d)) / math.sqrt(d) for j in range(S)]
+            mx = max(s)
+            p = [math.exp(x - mx) for x in s]
+            tot = sum(p)
+            for e in range(d):
+                out[i][h][e] = sum(p[j] * v[j][h][e] for j in range(S)) / tot
+    return out
+
+
+def test_ag_attention_brute_force():
+    """Loops over queries, heads, keys and the head dimension on a tiny case
+    with R = 3 ranks. Catches a wrong scale, a softmax over the wrong axis, a
+    head mixed up, or keys gathered in the wrong order (the values would then
+    be paired with the wrong keys)."""
+    R, m, H, d = 3, 2, 2, 4
+    rng = np.random.default_rng(30)
+    q = rand_bf16(rng, (m, H, d), -1, 1)
+    ks = [rand_bf16(rng, (m, H, d), -1, 1) for _ in range(R)]
+    vs = [rand_bf16(rng, (m, H, d), -1, 1) for _ in range(R)]
+    kf, vf, out = oracle.ag_attention(q, ks, vs)
+    assert np.array_equal(kf, np.concatenate(ks)) and np.array_equal(vf, np.concatenate(vs))
+    want = np.array(brute_attention(ref.decode_bf16(q).tolist(), ref.decode_bf16(kf).tolist(),
+                                    ref.decode_bf16(vf).tolist()))
+    assert np.allclose(out, want, rtol=1e-12, atol=1e-12)
+
+
+def test_ag_attention_special_cases():
+    """Equal keys -> uniform softmax -> the mean of the values; one key ->
+    its value; shuffling key/value rows together leaves the output unchanged
+    (attention is a set function of the key/value pairs); a key far ahead of
+    the others (score gap 60) selects its value."""
+    rng = np.random.default_rng(31)
+    R, m, H, d = 4, 3, 2, 8
+    q = rand_bf16(rng, (m, H, d), -1, 1)
+    kconst = [bf16_of_ints(np.ones((m, H, d))) for _ in range(R)]
+    vs = [rand_bf16(rng, (m, H, d), -1, 1) for _ in range(R)]
+    _, vf, out = oracle.ag_attention(q, kconst, vs)
+    assert np.allclose(out, ref.decode_bf16(vf).mean(axis=0, keepdims=True).repeat(m, 0), rtol=0, atol=1e-12)
+    k1 = [rand_bf16(rng, (1, H, d), -1, 1)]
+    v1 = [rand_bf16(rng, (1, H, d), -1, 1)]
+    _, _, o1 = oracle.ag_attention(q, k1, v1)
+    assert np.allclose(o1, np.broadcast_to(ref.decode_bf16(v1[0]), o1.shape), rtol=0, atol=1e-15)
+    ks = [rand_bf16(rng, (m, H, d), -1, 1) for _ in range(R)]
+    _, _, o = oracle.ag_attention(q, ks, vs)
+    perm = rng.permutation(R * m)
+    kf = np.concatenate(ks)[perm]
+    vf = np.concatenate(vs)[perm]
+    _, _, op = oracle.ag_attention(q, [kf], [vf])
+    assert np.allclose(o, op, rtol=1e-12, atol=1e-13)
+    # one dominant key: q = e_0 * 8, that key = e_0 * 8 * sqrt(d) (score 64 more than any other)
+    qd = np.zeros((1, 1, d), np.float32); qd[0, 0, 0] = 8.0
+    kd = np.zeros((5, 1, d), np.float32); kd[3, 0, 0] = 8.0 * math.sqrt(d)
+    vd = rand_bf16(rng, (5, 1, d), -1, 1)
+    _, _, od = oracle.ag_attention(bf16_of_ints(qd), [bf16_of_ints(kd)], [vd])
+    assert np.allclose(od[0, 0], ref.decode_bf16(vd)[3, 0], rtol=0, atol=1e-20)

@@ -163,10 +163,34 @@ def make_moe_combine(R: int, m: int, N: int, topk: int, seed: int, local_rank: i
     return MoeCombineInputs(R, m, N, topk, local_rank, y, w, peers, seed)
 
 
+@dataclass
+class AttentionInputs:
+    """Rank l's queries attend over the gathered keys / values of R ranks."""
+    R: int
+    m: int
+    H: int
+    d: int
+    local_rank: int
+    q: np.ndarray                       # uint16 [m, H, d], the local queries
+    k_chunks: List[np.ndarray]          # R x uint16 [m, H, d]
+    v_chunks: List[np.ndarray]          # R x uint16 [m, H, d]
+    seed: int = 0
+
+
+def make_attention(R: int, m: int, H: int, d: int, seed: int, local_rank: int = 0) -> AttentionInputs:
+    """Draw order: Q (local) ~ N(0, 1) [m, H, d]; K_0..K_{R-1}; V_0..V_{R-1},
+    all N(0, 1)."""
+    rng = np.random.default_rng(seed)
+    q = _draw_bf16(rng, (m, H, d), "normal", 1.0)
+    ks = [_draw_bf16(rng, (m, H, d), "normal", 1.0) for _ in range(R)]
+    vs = [_draw_bf16(rng, (m, H, d), "normal", 1.0) for _ in range(R)]
+    return AttentionInputs(R, m, H, d, local_rank, q, ks, vs, seed)
+
+
 @dataclass(frozen=True)
 class Workload:
     name: str
-    op: str            # "ag_gemm" | "gemm_rs" | "ag_grouped_gemm" | "moe_combine_rs"
+    op: str            # "ag_gemm" | "gemm_rs" | "ag_grouped_gemm" | "moe_combine_rs" | "ag_attention"
     params: dict = field(default_factory=dict)
 
     def flops(self) -> float:
@@ -177,6 +201,8 @@ class Workload:
             return 2.0 * p["M"] * p["K"] * p["N"]
         if self.op == "moe_combine_rs":
             return 2.0 * p["R"] * p["m"] * p["topk"] * p["N"]
+        if self.op == "ag_attention":
+            return 4.0 * p["m"] * p["R"] * p["m"] * p["H"] * p["d"]
         return 2.0 * p["R"] * p["m"] * p["topk"] * p["K"] * p["N"]
 
     def make(self, **over):
@@ -190,12 +216,15 @@ class Workload:
                                 p.get("local_rank", 0))
         if self.op == "moe_combine_rs":
             return make_moe_combine(p["R"], p["m"], p["N"], p["topk"], p["seed"], p.get("local_rank", 0))
+        if self.op == "ag_attention":
+            return make_attention(p["R"], p["m"], p["H"], p["d"], p["seed"], p.get("local_rank", 0))
         return make_moe(p["R"], p["m"], p["K"], p["N"], p["E"], p["seed"], p["topk"])
 
 
 # The workloads: one GPU's share of tensor-parallel (TP=8) LLM FFN layers
 # (8B-class: hidden 4096, FFN 14336; 70B-class: hidden 8192, FFN 28672) plus a
-# tiny case, a top-2 MoE layer with 32 experts, and that layer's TopK-Reduce tail.
+# tiny case, a top-2 MoE layer with 32 experts, that layer's TopK-Reduce tail,
+# and a context-parallel attention layer.
 WORKLOADS = {
     "ag_gemm_tiny": Workload("ag_gemm_tiny", "ag_gemm",
                              dict(R=4, m=128, K=256, N=256, seed=0, dist="uniform", scale=1.0)),
@@ -211,6 +240,10 @@ WORKLOADS = {
     # ReduceScatter of the combined token rows (row block 0 kept)
     "moe_combine_rs": Workload("moe_combine_rs", "moe_combine_rs",
                                dict(R=8, m=512, N=1792, topk=2, seed=5, local_rank=0)),
+    # AllGather-KV attention: 16384-token context over 8 ranks (2048 each),
+    # 8 heads of 128 (one GPU's head share), every query over the whole context
+    "ag_attention": Workload("ag_attention", "ag_attention",
+                             dict(R=8, m=2048, H=8, d=128, seed=6, local_rank=0)),
 }
 
 
