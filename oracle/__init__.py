@@ -13,8 +13,8 @@ codec, its own routing and its own schedule re-derivation.
 
 Parity status per function (see each docstring for the pin):
   * ag_gemm, gemm_rs, reduce_fixed_order, route_topk, sort_by_expert,
-    ag_grouped_gemm, topk_combine, moe_combine_rs, ag_attention, schedule
-    re-derivations:
+    ag_grouped_gemm, topk_combine, moe_combine_rs, ag_attention,
+    ag_attention_rows, schedule re-derivations:
     pinned by the ``-m "not gpu"`` tests (brute force, closed forms,
     identities, library special cases).
 """
@@ -22,5 +22,6 @@ from .reference import (  # noqa: F401
     decode_bf16, encode_bf16_rne, ag_gemm, ag_gemm_entries, ag_gemm_block, gemm_rs,
     gemm_rs_entries, reduce_fixed_order, route_topk, sort_by_expert,
     ag_grouped_gemm, ag_grouped_gemm_entries, topk_combine, moe_combine_rs, ag_attention,
+    ag_attention_rows,
 )
 from . import schedule  # noqa: F401

@@ -39,7 +39,10 @@ Readings where the pages are silent (each is also listed in the design doc):
       contiguous chunk of m tokens of Q, K and V; K and V are gathered in
       rank order and rank l's queries attend, per head, over all R*m keys
       with softmax(q . k / sqrt(d)) and no mask (context-parallel attention
-      read plainly: every query sees the whole gathered sequence).
+      read plainly: every query sees the whole gathered sequence). With
+      fewer kv heads than query heads (Hq = G * Hkv), query head h reads kv
+      head h // G (grouped-query attention, the layout that makes gathering
+      K and V cheaper than moving Q).
 """
 from __future__ import annotations
 
@@ -303,20 +306,43 @@ def ag_attention(q_bits, k_chunks, v_chunks):
     """Gather K and V (ascending rank order) and attend the local queries over
     them, per head, float64.
 
-    ``q_bits``: bf16 bits [m, H, d] (the local queries); ``k_chunks`` /
-    ``v_chunks``: R bf16 arrays [m, H, d]. Returns (k_full bits, v_full bits,
-    out [m, H, d]) with out[i, h] = sum_j softmax_j(q[i,h] . k[j,h] / sqrt(d)) v[j,h]."""
+    ``q_bits``: bf16 bits [m, Hq, d] (the local queries); ``k_chunks`` /
+    ``v_chunks``: R bf16 arrays [m_r, Hkv, d] with Hq a multiple of Hkv.
+    Returns (k_full bits, v_full bits, out [m, Hq, d]) with
+    out[i, h] = sum_j softmax_j(q[i,h] . k[j,g] / sqrt(d)) v[j,g], g = h // (Hq/Hkv)."""
     k_full = np.concatenate([np.asarray(c) for c in k_chunks], axis=0)
     v_full = np.concatenate([np.asarray(c) for c in v_chunks], axis=0)
     q = decode_bf16(np.asarray(q_bits))
     k = decode_bf16(k_full)
     v = decode_bf16(v_full)
-    m, H, d = q.shape
-    out = np.empty((m, H, d), dtype=np.float64)
-    for h in range(H):
-        s = (q[:, h, :] @ k[:, h, :].T) / np.sqrt(d)
+    m, Hq, d = q.shape
+    Hkv = k.shape[1]
+    if Hq % Hkv:
+        raise ValueError("query heads must be a multiple of kv heads")
+    G = Hq // Hkv
+    out = np.empty((m, Hq, d), dtype=np.float64)
+    for h in range(Hq):
+        g = h // G
+        s = (q[:, h, :] @ k[:, g, :].T) / np.sqrt(d)
         s -= s.max(axis=1, keepdims=True)
         p = np.exp(s)
         p /= p.sum(axis=1, keepdims=True)
-        out[:, h, :] = p @ v[:, h, :]
+        out[:, h, :] = p @ v[:, g, :]
     return k_full, v_full, out
+
+
+def ag_attention_rows(q_bits, k_full_bits, v_full_bits, rows):
+    """out[i, h] of ag_attention for the (i, h) pairs in ``rows`` only, from
+    already gathered K and V [S, Hkv, d] (float64; for sampled checks at full
+    size)."""
+    Hq, d = q_bits.shape[1], q_bits.shape[2]
+    G = Hq // k_full_bits.shape[1]
+    res = np.empty((len(rows), d), dtype=np.float64)
+    for n, (i, h) in enumerate(rows):
+        q = decode_bf16(np.asarray(q_bits[i, h]))
+        k = decode_bf16(np.asarray(k_full_bits[:, h // G]))
+        v = decode_bf16(np.asarray(v_full_bits[:, h // G]))
+        s = (k @ q) / np.sqrt(d)
+        p = np.exp(s - s.max())
+        res[n] = (p / p.sum()) @ v
+    return res

@@ -426,18 +426,21 @@ def test_moe_combine_rs_zero_peers():
 
 
 def brute_attention(q, k, v):
-    """Per query and head: explicit softmax over all keys, loops."""
+    """Per query and head: explicit softmax over all keys, loops; query head
+    h reads kv head h // (Hq / Hkv)."""
     m, H, d = len(q), len(q[0]), len(q[0][0])
+    G = H // len(k[0])
     S = len(k)
     out = [[[0.0] * d for _ in range(H)] for _ in range(m)]
     for i in range(m):
         for h in range(H):
-            s = [sum(q[i][h][e] * k[j][h][e] for e in range(d)) / math.sqrt(d) for j in range(S)]
+            g = h // G
+            s = [sum(q[i][h][e] * k[j][g][e] for e in range(d)) / math.sqrt(d) for j in range(S)]
             mx = max(s)
             p = [math.exp(x - mx) for x in s]
             tot = sum(p)
             for e in range(d):
-                out[i][h][e] = sum(p[j] * v[j][h][e] for j in range(S)) / tot
+                out[i][h][e] = sum(p[j] * v[j][g][e] for j in range(S)) / tot
     return out
 
 
@@ -487,3 +490,27 @@ def test_ag_attention_special_cases():
     vd = rand_bf16(rng, (5, 1, d), -1, 1)
     _, _, od = oracle.ag_attention(bf16_of_ints(qd), [bf16_of_ints(kd)], [vd])
     assert np.allclose(od[0, 0], ref.decode_bf16(vd)[3, 0], rtol=0, atol=1e-20)
+
+
+def test_ag_attention_grouped_heads():
+    """Grouped kv heads: brute force with Hq = 6 over Hkv = 2 (G = 3; a
+    head mapped to the wrong kv head fails), the result equals plain
+    multi-head attention with every kv head repeated G times, and the per-row
+    form used for sampled checks gives the same rows."""
+    R, m, Hq, Hkv, d = 2, 3, 6, 2, 4
+    rng = np.random.default_rng(32)
+    q = rand_bf16(rng, (m, Hq, d), -1, 1)
+    ks = [rand_bf16(rng, (m, Hkv, d), -1, 1) for _ in range(R)]
+    vs = [rand_bf16(rng, (m, Hkv, d), -1, 1) for _ in range(R)]
+    kf, vf, out = oracle.ag_attention(q, ks, vs)
+    want = np.array(brute_attention(ref.decode_bf16(q).tolist(), ref.decode_bf16(kf).tolist(),
+                                    ref.decode_bf16(vf).tolist()))
+    assert np.allclose(out, want, rtol=1e-12, atol=1e-12)
+    G = Hq // Hkv
+    _, _, mha = oracle.ag_attention(q, [np.repeat(c, G, axis=1) for c in ks], [np.repeat(c, G, axis=1) for c in vs])
+    assert np.allclose(out, mha, rtol=1e-13, atol=1e-14)
+    rows = [(0, 0), (2, 5), (1, 3)]
+    got = oracle.ag_attention_rows(q, kf, vf, rows)
+    assert np.allclose(got, np.array([out[i, h] for i, h in rows]), rtol=1e-13, atol=1e-14)
+    with pytest.raises(ValueError):
+        oracle.ag_attention(rand_bf16(rng, (m, 5, d), -1, 1), ks, vs)

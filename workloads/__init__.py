@@ -168,23 +168,24 @@ class AttentionInputs:
     """Rank l's queries attend over the gathered keys / values of R ranks."""
     R: int
     m: int
-    H: int
+    Hq: int
+    Hkv: int
     d: int
     local_rank: int
-    q: np.ndarray                       # uint16 [m, H, d], the local queries
-    k_chunks: List[np.ndarray]          # R x uint16 [m, H, d]
-    v_chunks: List[np.ndarray]          # R x uint16 [m, H, d]
+    q: np.ndarray                       # uint16 [m, Hq, d], the local queries
+    k_chunks: List[np.ndarray]          # R x uint16 [m, Hkv, d]
+    v_chunks: List[np.ndarray]          # R x uint16 [m, Hkv, d]
     seed: int = 0
 
 
-def make_attention(R: int, m: int, H: int, d: int, seed: int, local_rank: int = 0) -> AttentionInputs:
-    """Draw order: Q (local) ~ N(0, 1) [m, H, d]; K_0..K_{R-1}; V_0..V_{R-1},
-    all N(0, 1)."""
+def make_attention(R: int, m: int, Hq: int, Hkv: int, d: int, seed: int, local_rank: int = 0) -> AttentionInputs:
+    """Draw order: Q (local) ~ N(0, 1) [m, Hq, d]; K_0..K_{R-1}; V_0..V_{R-1}
+    ([m, Hkv, d] each), all N(0, 1)."""
     rng = np.random.default_rng(seed)
-    q = _draw_bf16(rng, (m, H, d), "normal", 1.0)
-    ks = [_draw_bf16(rng, (m, H, d), "normal", 1.0) for _ in range(R)]
-    vs = [_draw_bf16(rng, (m, H, d), "normal", 1.0) for _ in range(R)]
-    return AttentionInputs(R, m, H, d, local_rank, q, ks, vs, seed)
+    q = _draw_bf16(rng, (m, Hq, d), "normal", 1.0)
+    ks = [_draw_bf16(rng, (m, Hkv, d), "normal", 1.0) for _ in range(R)]
+    vs = [_draw_bf16(rng, (m, Hkv, d), "normal", 1.0) for _ in range(R)]
+    return AttentionInputs(R, m, Hq, Hkv, d, local_rank, q, ks, vs, seed)
 
 
 @dataclass(frozen=True)
@@ -202,7 +203,7 @@ class Workload:
         if self.op == "moe_combine_rs":
             return 2.0 * p["R"] * p["m"] * p["topk"] * p["N"]
         if self.op == "ag_attention":
-            return 4.0 * p["m"] * p["R"] * p["m"] * p["H"] * p["d"]
+            return 4.0 * p["m"] * p["R"] * p["m"] * p["Hq"] * p["d"]
         return 2.0 * p["R"] * p["m"] * p["topk"] * p["K"] * p["N"]
 
     def make(self, **over):
@@ -217,7 +218,7 @@ class Workload:
         if self.op == "moe_combine_rs":
             return make_moe_combine(p["R"], p["m"], p["N"], p["topk"], p["seed"], p.get("local_rank", 0))
         if self.op == "ag_attention":
-            return make_attention(p["R"], p["m"], p["H"], p["d"], p["seed"], p.get("local_rank", 0))
+            return make_attention(p["R"], p["m"], p["Hq"], p["Hkv"], p["d"], p["seed"], p.get("local_rank", 0))
         return make_moe(p["R"], p["m"], p["K"], p["N"], p["E"], p["seed"], p["topk"])
 
 
@@ -240,10 +241,11 @@ WORKLOADS = {
     # ReduceScatter of the combined token rows (row block 0 kept)
     "moe_combine_rs": Workload("moe_combine_rs", "moe_combine_rs",
                                dict(R=8, m=512, N=1792, topk=2, seed=5, local_rank=0)),
-    # AllGather-KV attention: 16384-token context over 8 ranks (2048 each),
-    # 8 heads of 128 (one GPU's head share), every query over the whole context
+    # AllGather-KV attention: a 16384-token context over 8 ranks (2048 tokens
+    # each), 32 query heads over 8 kv heads of 128 (an 8B-class GQA layer),
+    # every query over the whole context
     "ag_attention": Workload("ag_attention", "ag_attention",
-                             dict(R=8, m=2048, H=8, d=128, seed=6, local_rank=0)),
+                             dict(R=8, m=2048, Hq=32, Hkv=8, d=128, seed=6, local_rank=0)),
 }
 
 
