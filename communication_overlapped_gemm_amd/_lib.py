@@ -22,7 +22,7 @@ ERR_HIP = -4
 ERR_TIMEOUT = -5
 ERR_NO_DEVICE = -6
 
-OP_AG_GEMM, OP_GEMM_RS, OP_AG_GROUPED_GEMM, OP_MOE_COMBINE_RS = 0, 1, 2, 3
+OP_AG_GEMM, OP_GEMM_RS, OP_AG_GROUPED_GEMM, OP_MOE_COMBINE_RS, OP_AG_ATTENTION = 0, 1, 2, 3, 4
 MODE_FUSED, MODE_GEMM_ONLY, MODE_COPY_ONLY = 0, 1, 2
 TILE_AUTO, TILE_256x224, TILE_128x224, TILE_128x256, TILE_128x128, TILE_256x256, TILE_320x224, TILE_288x224 = (
     -1, 0, 1, 2, 3, 4, 5, 6)
@@ -31,7 +31,7 @@ EXPORTS = [
     "ocg_config_default", "ocg_create", "ocg_destroy", "ocg_workspace_bytes",
     "ocg_workspace_init", "ocg_ag_gemm", "ocg_gemm_rs", "ocg_ag_grouped_gemm",
     "ocg_signal", "ocg_check", "ocg_status_string", "ocg_plan_info", "ocg_plan_task",
-    "ocg_moe_combine_rs",
+    "ocg_moe_combine_rs", "ocg_ag_attention",
 ]
 
 
@@ -77,6 +77,9 @@ def _declare(lib):
         "ocg_moe_combine_rs": (C.c_int, [_P, _P, _P, C.c_int, C.c_int, C.c_int64, C.c_int64, C.c_int, C.POINTER(_P),
                                          _P, _P,
                                          _P, C.c_size_t, C.POINTER(Config), _P]),
+        "ocg_ag_attention": (C.c_int, [_P, _P, C.POINTER(_P), C.POINTER(_P), C.c_int, C.c_int, C.c_int64,
+                                       C.c_int64, C.c_int64, C.c_int64, _P, _P, _P, _P, C.c_size_t,
+                                       C.POINTER(Config), _P]),
         "ocg_signal": (C.c_int, [_P, C.c_int, C.c_uint32, _P]),
         "ocg_check": (C.c_int, [_P, _P]),
         "ocg_status_string": (C.c_char_p, [C.c_int]),

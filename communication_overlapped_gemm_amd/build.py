@@ -14,7 +14,7 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libocg.so")
-SOURCES = ["kernels.hip", "api.cpp"]
+SOURCES = ["kernels.hip", "attention.hip", "api.cpp"]
 
 # Packed-fp32 instructions are disabled (v_pk_*_f32 forms are not trusted on
 # the test machines); hipcc's host pass warns that it does not know the

@@ -16,6 +16,7 @@ struct ocg_handle_s {
   int device;
   int cus;
   int resident[3][OCG_TILE_COUNT];  // per op and tile preset, 0 = not queried yet
+  int resident_attn;                // attention kernel, 0 = not queried yet
 };
 
 namespace {
@@ -164,6 +165,36 @@ bool combine_shape_ok(int R, int64_t m, int64_t N, int topk) {
   return true;
 }
 
+// AllGather-KV attention shapes: d = 128, Hq a multiple of Hkv, 32-bit
+// element offsets into every buffer.
+bool attn_shape_ok(int R, int64_t m, int64_t Hq, int64_t Hkv) {
+  if (R < 1 || R > kMaxRanks || m < 1 || Hkv < 1 || Hq < Hkv || Hq % Hkv) return false;
+  if ((int64_t)R * m * Hkv * kAttnD >= ((int64_t)1 << 31)) return false;
+  if (m * Hq * kAttnD >= ((int64_t)1 << 31)) return false;
+  return true;
+}
+
+// Slab rows default to the whole chunk (one flag per chunk: a tile waits per
+// chunk); copy tasks of about 128 KiB, a power of two dividing the slab.
+int resolve_attn(int64_t m, int64_t Hkv, const ocg_config& c, int* S, int* CT) {
+  *S = c.slab_rows > 0 ? c.slab_rows : (int)m;
+  if (*S > m) *S = (int)m;
+  if (*S < kMinSlabRows && *S < m) return OCG_ERR_INVALID_ARG;
+  const int64_t row_bytes = Hkv * kAttnD * 2;
+  if (c.copy_rows > 0) {
+    *CT = c.copy_rows;
+  } else {
+    int64_t ct = (128 * 1024) / row_bytes;
+    int p2 = 1;
+    while ((int64_t)p2 * 2 <= ct) p2 *= 2;
+    *CT = p2 < *S ? p2 : *S;
+    while (*S % *CT) *CT /= 2;
+  }
+  if (*CT < 1 || *S % *CT) return OCG_ERR_INVALID_ARG;
+  if ((int64_t)*CT * row_bytes >= ((int64_t)1 << 31)) return OCG_ERR_INVALID_ARG;
+  return OCG_OK;
+}
+
 int reduce_rows(int64_t M, int R, int64_t N, int cus) {
   int64_t rr = (32 * 1024) / (2 * N);
   const int64_t spread = (M / R) / (cus > 0 ? cus : 1);
@@ -236,7 +267,8 @@ int ocg_create(int device, ocg_handle* out) {
 void ocg_destroy(ocg_handle h) { delete h; }
 
 size_t ocg_workspace_bytes(int op, int R, int64_t m, int64_t K, int64_t N, int E, int topk) {
-  if (op < 0 || op > 3) return 0;
+  if (op < 0 || op > 4) return 0;
+  if (op == OCG_OP_AG_ATTENTION) return attn_shape_ok(R, m, K, N) ? layout(op, R, m, 0, 0, 0, 0).total : 0;
   if (op == OCG_OP_MOE_COMBINE_RS) return combine_shape_ok(R, m, N, topk) ? layout(op, R, m, 0, N, 0, topk).total : 0;
   if (op == OCG_OP_GEMM_RS) {
     if (R < 1 || R > kMaxRanks || m < R || m % R) return 0;
@@ -426,6 +458,50 @@ int ocg_moe_combine_rs(ocg_handle h, const void* y, const float* topk_w, int R, 
   return launch_moe_combine_rs(a, grid, (hipStream_t)stream) == hipSuccess ? OCG_OK : OCG_ERR_HIP;
 }
 
+int ocg_ag_attention(ocg_handle h, const void* q, const void* const* k_chunks, const void* const* v_chunks, int R,
+                     int local_rank, int64_t m, int64_t Hq, int64_t Hkv, int64_t d, void* k_gathered,
+                     void* v_gathered, void* out, void* ws, size_t ws_bytes, const ocg_config* cfgp, void* stream) {
+  if (!h || !q || !k_chunks || !v_chunks || !k_gathered || !v_gathered || !out || !ws) return OCG_ERR_INVALID_ARG;
+  if (d != kAttnD || !attn_shape_ok(R, m, Hq, Hkv)) return OCG_ERR_UNSUPPORTED_SHAPE;
+  if (local_rank < 0 || local_rank >= R) return OCG_ERR_INVALID_ARG;
+  for (int r = 0; r < R; ++r)
+    if (!k_chunks[r] || !v_chunks[r] || !aligned16(k_chunks[r]) || !aligned16(v_chunks[r])) return OCG_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k_gathered) || !aligned16(v_gathered) || !aligned16(out) || !aligned16(ws))
+    return OCG_ERR_INVALID_ARG;
+  ocg_config cfg = cfg_or_default(cfgp);
+  if (cfg.mode < 0 || cfg.mode > 2) return OCG_ERR_INVALID_ARG;
+  WsLayout L = layout(OCG_OP_AG_ATTENTION, R, m, 0, 0, 0, 0);
+  if (ws_bytes < L.total) return OCG_ERR_WORKSPACE_TOO_SMALL;
+  if (!device_matches(h)) return OCG_ERR_INVALID_ARG;
+  int S, CT;
+  int st = resolve_attn(m, Hkv, cfg, &S, &CT);
+  if (st) return st;
+  AttnArgs a{};
+  a.q = (const uint16_t*)q;
+  for (int r = 0; r < R; ++r) {
+    a.k_chunks[r] = (const uint16_t*)k_chunks[r];
+    a.v_chunks[r] = (const uint16_t*)v_chunks[r];
+  }
+  a.k_gathered = (uint16_t*)k_gathered;
+  a.v_gathered = (uint16_t*)v_gathered;
+  a.out = (uint16_t*)out;
+  a.slab_cnt = (uint32_t*)((char*)ws + L.slab_cnt);
+  a.slab_flag = (uint32_t*)((char*)ws + L.slab_flag);
+  a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)d));
+  a.plan = make_attn_plan(R, local_rank, (int)m, (int)Hq, (int)Hkv, S, CT, cfg.swizzle ? 1 : 0, cfg.mode);
+  if (a.plan.cp.R * a.plan.cp.bpr > L.max_slabs) return OCG_ERR_INVALID_ARG;
+  a.cm = make_common(ws, cfg);
+  int grid = cfg.grid;
+  if (grid <= 0) {
+    if (h->resident_attn == 0) h->resident_attn = resident_attention();
+    grid = h->resident_attn * h->cus;
+    const int tasks = a.plan.n_copy + a.plan.n_tiles;
+    if (tasks < grid) grid = tasks;
+    if (grid < 1) grid = 1;
+  }
+  return launch_ag_attention(a, grid, (hipStream_t)stream) == hipSuccess ? OCG_OK : OCG_ERR_HIP;
+}
+
 int ocg_check(ocg_handle h, void* ws) {
   if (!h || !ws) return OCG_ERR_INVALID_ARG;
   WsHeader* hdr = (WsHeader*)ws;
@@ -454,7 +530,25 @@ const char* ocg_status_string(int s) {
 
 int ocg_plan_info(int op, int R, int local_rank, int64_t m, int64_t K, int64_t N, int E, int topk,
                   const ocg_config* cfgp, int64_t out[8]) {
-  if (!out || op < 0 || op > 3) return OCG_ERR_INVALID_ARG;
+  if (!out || op < 0 || op > 4) return OCG_ERR_INVALID_ARG;
+  if (op == OCG_OP_AG_ATTENTION) {
+    if (!attn_shape_ok(R, m, K, N)) return OCG_ERR_UNSUPPORTED_SHAPE;
+    if (local_rank < 0 || local_rank >= R) return OCG_ERR_INVALID_ARG;
+    ocg_config cfg = cfg_or_default(cfgp);
+    int S, CT;
+    int st = resolve_attn(m, N, cfg, &S, &CT);
+    if (st) return st;
+    AttnPlan p = make_attn_plan(R, local_rank, (int)m, (int)K, (int)N, S, CT, cfg.swizzle ? 1 : 0, cfg.mode);
+    out[0] = -1;
+    out[1] = kAttnRows;
+    out[2] = kAttnKB;
+    out[3] = S;
+    out[4] = CT;
+    out[5] = p.n_copy;
+    out[6] = p.n_tiles;
+    out[7] = (int64_t)R * p.cp.bpr;
+    return OCG_OK;
+  }
   if (op == OCG_OP_MOE_COMBINE_RS) {
     if (!combine_shape_ok(R, m, N, topk)) return OCG_ERR_UNSUPPORTED_SHAPE;
     if (local_rank < 0 || local_rank >= R) return OCG_ERR_INVALID_ARG;
@@ -509,6 +603,32 @@ int ocg_plan_task(int op, int R, int local_rank, int64_t m, int64_t K, int64_t N
   int st = ocg_plan_info(op, R, local_rank, m, K, N, 0, 0, cfgp, info);
   if (st) return st;
   ocg_config cfg = cfg_or_default(cfgp);
+  if (op == OCG_OP_AG_ATTENTION) {
+    AttnPlan p = make_attn_plan(R, local_rank, (int)m, (int)K, (int)N, (int)info[3], (int)info[4], cfg.swizzle ? 1 : 0,
+                                cfg.mode);
+    if (ticket < 0 || ticket >= p.n_copy + p.n_tiles) return OCG_OK;
+    if (ticket < p.n_copy) {
+      CopyDesc d = copy_desc(p.cp, (int)(ticket >> 1));
+      desc[0] = 1;
+      desc[1] = d.chunk;
+      desc[2] = d.piece;
+      desc[3] = d.row0;
+      desc[4] = d.row1;
+      desc[5] = d.slab;
+      desc[6] = ticket & 1;
+      return OCG_OK;
+    }
+    const int v = (int)(ticket - p.n_copy);
+    desc[0] = 7;
+    desc[1] = v / p.n_rb;
+    desc[2] = v % p.n_rb;
+    desc[3] = p.cp.mode == 0 ? (int64_t)(R - 1) * p.cp.bpr : 0;
+    int q, t;
+    tile_queue(v, &q, &t);
+    desc[4] = q;
+    desc[5] = t;
+    return OCG_OK;
+  }
   if (op == OCG_OP_GEMM_RS) {
     RsPlan p = make_rs_plan(R, local_rank, (int)m, (int)K, (int)N, (int)info[1], (int)info[2], (int)info[7],
                             cfg.swizzle);

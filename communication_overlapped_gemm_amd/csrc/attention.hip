@@ -1,0 +1,364 @@
+// AllGather-KV attention on gfx950: the gather of the keys and values of R
+// context-parallel ranks overlapped with the attention of the local queries
+// over the gathered sequence ("TileLink: Generating Efficient
+// Compute-Communication Overlapping Kernels using Tile-Centric Primitives",
+// MLSys 2025 talk summary, section "Experimental Setup & Results": the
+// AllGather-KV attention, overlapped with the attention computation itself).
+//
+// One persistent kernel. Workgroups first take copy tasks (pull a piece of a
+// peer's key or value chunk into the gathered buffers, publish the slab flag
+// once its key and value pieces have landed), then attention tiles from the
+// XCD queues. A tile holds 256 query rows (query, head) that share one kv
+// head, 64 per wave, and streams the keys and values in blocks of 64 through
+// a 4-slot LDS ring filled by direct-to-LDS loads, starting with the local
+// chunk (read from the local shard, never waited on); before its first load
+// of a peer chunk each wave waits on that chunk's slab flags.
+//
+// Per wave and key block (flash-attention style online softmax, fp32):
+//   S^T = K Q^T      v_mfma_f32_16x16x32_bf16, A = key rows from LDS
+//                    (16-byte reads), B = the wave's query fragments, held in
+//                    registers for the whole tile;
+//   softmax          lane (l & 15) of every 16-lane row owns one query of a
+//                    16-query column block and 4 of its keys per 16-key tile,
+//                    so a row maximum is an in-lane maximum plus two lane
+//                    swaps (v_permlane16/32_swap);
+//   O^T += V^T P^T   A = value columns from LDS with the transposing read
+//                    ds_read_b64_tr_b16, B = the probabilities converted to
+//                    bf16 in registers. Each lane's 8 probabilities of a
+//                    32-key step are keys {4q..4q+3, 16+4q..16+4q+3}
+//                    (q = lane >> 4), the order the S^T accumulators leave
+//                    them in; the value reads fetch the same keys, so the
+//                    contraction pairs them up.
+// The output accumulators hold O^T: lane (q, j) has O[query j][d = 16t + 4q
+// .. +3] of each 16x16 block; the epilogue divides by the row sums and
+// stores 8-byte pieces.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gemm_core.h"
+#include "ocg_internal.h"
+#include "sync.h"
+
+namespace ocg {
+namespace {
+
+constexpr int kD = kAttnD;                  // head dimension (128)
+constexpr int kKB = kAttnKB;                // keys per block (64)
+constexpr int kSlots = 4;                   // LDS ring slots
+constexpr int kRowBytes = kD * 2;           // one head's key or value row (256 B)
+constexpr int kPart = kKB * kRowBytes;      // keys (or values) of one block: 16 KiB
+constexpr int kStage = 2 * kPart;           // keys, then values
+constexpr int kLoads = kPart / 1024 / 4;    // 1 KiB loads per wave per tensor per block (4)
+constexpr int kNdma = 2 * kLoads;           // loads per wave per block
+constexpr int kQTiles = 4;                  // 16-row query blocks per wave
+constexpr int kDSteps = kD / 32;            // MFMA k steps over the head dimension
+constexpr int kKTiles = kKB / 16;           // 16-key blocks per key block
+constexpr int kDTiles = kD / 16;            // 16-column blocks of the output
+
+static_assert(kSlots * kStage <= 160 * 1024 - 64, "ring fits the LDS");
+static_assert(kKB == 64 && kD == 128, "fragment maps below assume 64-key blocks of 128-wide heads");
+
+// LDS slot layout: keys [64][256 B] then values [64][256 B]. The 16-byte
+// chunk c of key row r sits at chunk position c ^ (r & 15): the 16 lanes of a
+// key-fragment read (16 rows, one chunk) hit 16 distinct positions. The
+// 32-byte chunk pair c2 of value row r sits at pair position c2 ^ (r & 7):
+// a transposing read touches 4 rows x 32 bytes per 16 lanes, and rows
+// 8n..8n+7 land on 8 distinct pairs (all 64 banks for 32 lanes).
+__device__ __forceinline__ int key_src_chunk(int pos, int r) { return pos ^ (r & 15); }
+__device__ __forceinline__ int val_src_chunk(int pos, int r) { return (((pos >> 1) ^ (r & 7)) << 1) | (pos & 1); }
+
+__device__ __forceinline__ float swap_max16(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float swap_max32(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float swap_sum16(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float swap_sum32(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// One copy task: piece u >> 1 of the AG copy order of tensor u & 1.
+__device__ void run_kv_copy(const AttnArgs& a, int u, uint32_t epoch) {
+  const AgPlan& p = a.plan.cp;
+  const uint64_t t0 = now_ticks();
+  const int tensor = u & 1;
+  const CopyDesc d = copy_desc(p, u >> 1);
+  const uint16_t* src = (tensor ? a.v_chunks[d.chunk] : a.k_chunks[d.chunk]) + (size_t)(d.row0 - d.chunk * p.m) * p.K;
+  uint16_t* dst = (tensor ? a.v_gathered : a.k_gathered) + (size_t)d.row0 * p.K;
+  copy_granules(src, dst, (uint32_t)((size_t)(d.row1 - d.row0) * p.K / 8));
+  const int target = 2 * slab_target(p.m, p.S, p.CT, p.bpr, d.slab);
+  const bool pub = publish_slab(a.slab_cnt, a.slab_flag, d.slab, target, epoch, a.cm);
+  trace_task(a.cm, (uint32_t)u, 1, d.chunk, (uint32_t)d.piece | ((uint32_t)tensor << 16), d.slab, pub ? 1u : 0u,
+             epoch, t0, now_ticks(), 0, 0);
+}
+
+// Per-lane constants of a tile's block loads: load ii of this wave fills
+// rows 4*i .. 4*i+3 (i = wave + 4*ii) of the slot's key and value parts;
+// lane L takes row 4*i + L/16, LDS chunk position L & 15, whose source chunk
+// is given by the swizzles above.
+struct BlockLoads {
+  uint32_t koff[kLoads], voff[kLoads];   // byte offset of the lane's chunk within its head row
+  int row[kLoads];                       // row within the block
+};
+
+struct TileState {
+  bf16x8_t qf[kQTiles][kDSteps];   // query fragments: row (lane & 15) of block qt, d = 32u + 8(lane >> 4) ..
+  f32x4_t o[kDTiles][kQTiles];     // O^T accumulators
+  float mrun[kQTiles];             // running maximum of the scaled scores (log2 units)
+  float lrun[kQTiles];             // this lane's part of the running row sum
+};
+
+// Key block j: issue this wave's 8 loads into `slot` (LDS byte address).
+// Rows past the chunk's end re-read its last row (masked in the softmax).
+__device__ __forceinline__ void issue_block(const AttnArgs& a, const BlockLoads& bl, int g, int j, uint32_t slot) {
+  const AttnPlan& p = a.plan;
+  const int c = attn_block_chunk(p, j);
+  const int key0 = (j % p.nbc) * kKB;
+  const size_t row_elems = (size_t)p.Hkv * kD;
+  const char* kb;
+  const char* vb;
+  if (c == p.cp.local) {
+    kb = (const char*)(a.k_chunks[c] + (size_t)g * kD);
+    vb = (const char*)(a.v_chunks[c] + (size_t)g * kD);
+  } else {
+    kb = (const char*)(a.k_gathered + ((size_t)c * p.cp.m) * row_elems + (size_t)g * kD);
+    vb = (const char*)(a.v_gathered + ((size_t)c * p.cp.m) * row_elems + (size_t)g * kD);
+  }
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+#pragma unroll
+  for (int ii = 0; ii < kLoads; ++ii) {
+    const int key = min(key0 + bl.row[ii], p.cp.m - 1);
+    const size_t rb = (size_t)key * row_elems * 2;
+    const int i = wave + 4 * ii;
+    dma_global(slot + i * 1024, kb + rb + bl.koff[ii]);
+    dma_global(slot + kPart + i * 1024, vb + rb + bl.voff[ii]);
+  }
+}
+
+// Wait (this wave) for every slab flag of chunk c; returns the flag count.
+__device__ __forceinline__ int wait_chunk(const AttnArgs& a, int c, uint32_t epoch, uint32_t* seen) {
+  const AgPlan& p = a.plan.cp;
+  FlagWait w(a.cm.timeout_ticks);
+  for (int s = 0; s < p.bpr; ++s) w(&a.slab_flag[c * p.bpr + s], epoch);
+  return w.finish(a.cm, seen);
+}
+
+// S^T, online softmax and O^T update of one key block held in LDS at `st`;
+// `valid` keys of the block are real (the rest are masked out).
+__device__ __forceinline__ void attend_block(TileState& ts, OCG_LDS const char* st, const uint32_t (&kfa)[kDSteps],
+                                             uint32_t vfa, int vx, int valid, float scale) {
+  const int lane = threadIdx.x & 63;
+  const int qg = lane >> 4;
+  f32x4_t s[kKTiles][kQTiles];
+#pragma unroll
+  for (int t = 0; t < kKTiles; ++t) {
+    bf16x8_t kf[kDSteps];
+#pragma unroll
+    for (int u = 0; u < kDSteps; ++u) kf[u] = *(OCG_LDS const bf16x8_t*)(st + t * 16 * kRowBytes + kfa[u]);
+#pragma unroll
+    for (int qt = 0; qt < kQTiles; ++qt) {
+      s[t][qt] = f32x4_t{};
+#pragma unroll
+      for (int u = 0; u < kDSteps; ++u)
+        s[t][qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[u], ts.qf[qt][u], s[t][qt], 0, 0, 0);
+    }
+  }
+  if (valid < kKB) {
+#pragma unroll
+    for (int t = 0; t < kKTiles; ++t)
+#pragma unroll
+      for (int qt = 0; qt < kQTiles; ++qt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (16 * t + 4 * qg + i >= valid) s[t][qt][i] = -INFINITY;
+  }
+  bf16x8_t pf[kQTiles][2];
+#pragma unroll
+  for (int qt = 0; qt < kQTiles; ++qt) {
+    float mx = s[0][qt][0];
+#pragma unroll
+    for (int t = 0; t < kKTiles; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[t][qt][i]);
+    mx = swap_max32(swap_max16(mx));
+    const float mnew = fmaxf(ts.mrun[qt], mx * scale);
+    const float alpha = __builtin_amdgcn_exp2f(ts.mrun[qt] - mnew);
+    ts.mrun[qt] = mnew;
+    float p[kKTiles][4];
+    float sum = 0.f;
+#pragma unroll
+    for (int t = 0; t < kKTiles; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        p[t][i] = __builtin_amdgcn_exp2f(fmaf(s[t][qt][i], scale, -mnew));
+        sum += p[t][i];
+      }
+    ts.lrun[qt] = fmaf(ts.lrun[qt], alpha, sum);
+#pragma unroll
+    for (int dt = 0; dt < kDTiles; ++dt) ts.o[dt][qt] *= alpha;
+#pragma unroll
+    for (int sp = 0; sp < 2; ++sp)
+      pf[qt][sp] = bf16x8_t{(__bf16)p[2 * sp][0], (__bf16)p[2 * sp][1], (__bf16)p[2 * sp][2], (__bf16)p[2 * sp][3],
+                            (__bf16)p[2 * sp + 1][0], (__bf16)p[2 * sp + 1][1], (__bf16)p[2 * sp + 1][2],
+                            (__bf16)p[2 * sp + 1][3]};
+  }
+  OCG_LDS const char* sv = st + kPart;
+#pragma unroll
+  for (int dt = 0; dt < kDTiles; ++dt) {
+#pragma unroll
+    for (int sp = 0; sp < 2; ++sp) {
+      OCG_LDS const char* pa = sv + vfa + sp * 32 * kRowBytes + ((dt ^ vx) << 5);
+      bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((OCG_LDS bf16x4_t*)pa);
+      bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((OCG_LDS bf16x4_t*)(pa + 16 * kRowBytes));
+      const bf16x8_t vf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+      for (int qt = 0; qt < kQTiles; ++qt)
+        ts.o[dt][qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[qt][sp], ts.o[dt][qt], 0, 0, 0);
+    }
+  }
+}
+
+// One attention tile v: kv head g, query rows [256 rb, 256 rb + 256).
+__device__ void attention_tile(const AttnArgs& a, OCG_LDS char* smem, int v, uint32_t epoch, uint32_t queue) {
+  const AttnPlan& p = a.plan;
+  const AgPlan& cp = p.cp;
+  const uint64_t t0 = now_ticks();
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int qg = lane >> 4, qj = lane & 15;
+  const int g = v / p.n_rb, rb = v - g * p.n_rb;
+  const int nrows = p.G * cp.m;
+
+  // query rows of this lane (one per 16-row block) and their element offsets
+  TileState ts;
+  size_t qoff[kQTiles];
+  bool qok[kQTiles];
+#pragma unroll
+  for (int qt = 0; qt < kQTiles; ++qt) {
+    const int r = rb * kAttnRows + wave * 64 + qt * 16 + qj;
+    qok[qt] = r < nrows;
+    const int rc = min(r, nrows - 1);
+    const int i = rc / p.G, h = g * p.G + (rc - (rc / p.G) * p.G);
+    qoff[qt] = ((size_t)i * p.Hq + h) * kD;
+#pragma unroll
+    for (int u = 0; u < kDSteps; ++u) ts.qf[qt][u] = *(const bf16x8_t*)(a.q + qoff[qt] + 32 * u + 8 * qg);
+    ts.mrun[qt] = -INFINITY;
+    ts.lrun[qt] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < kDTiles; ++dt) ts.o[dt][qt] = f32x4_t{};
+  }
+  // The query loads are the only loads the compiler tracks; waiting for them
+  // here (as a builtin, so its wait insertion knows) keeps it from adding a
+  // whole-queue wait inside the key loop, whose direct-to-LDS loads it does
+  // not see.
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0), expcnt and lgkmcnt open
+  BlockLoads bl;
+#pragma unroll
+  for (int ii = 0; ii < kLoads; ++ii) {
+    const int r = 4 * (wave + 4 * ii) + (lane >> 4);
+    bl.row[ii] = r;
+    bl.koff[ii] = (uint32_t)key_src_chunk(lane & 15, r) * 16u;
+    bl.voff[ii] = (uint32_t)val_src_chunk(lane & 15, r) * 16u;
+  }
+  // fragment read offsets within a slot
+  uint32_t kfa[kDSteps];
+#pragma unroll
+  for (int u = 0; u < kDSteps; ++u) kfa[u] = (uint32_t)(qj * kRowBytes + (((4 * u + qg) ^ qj) << 4));
+  const int vrow = 4 * qg + (qj >> 2);           // value row of the low transposing read (+32 per k step)
+  const uint32_t vfa = (uint32_t)(vrow * kRowBytes + (((qj >> 1) & 1) << 4) + ((qj & 1) << 3));
+  const int vx = vrow & 7;                       // pair swizzle of that row (same for +16, +32)
+
+  const uint32_t base = lds_u32(smem);
+  const int nblk = cp.R * p.nbc;
+  const bool fused = cp.mode == 0;
+  int nwait = 0;
+  uint32_t seen = 0;
+  uint64_t t_ready = t0;
+  // Block j's loads, preceded by the wait on its chunk's flags when it is
+  // the first block of a peer chunk. Past the end the last block is loaded
+  // again into the free slot (never read), so every step issues kNdma loads.
+  auto issue = [&](int j) {
+    const uint32_t slot = base + (uint32_t)(j % kSlots) * kStage;
+    const int jj = j < nblk ? j : nblk - 1;
+    if (fused && j < nblk && jj % p.nbc == 0) {
+      const int c = attn_block_chunk(p, jj);
+      if (c != cp.local) {
+        nwait += wait_chunk(a, c, epoch, &seen);
+        t_ready = now_ticks();
+      }
+    }
+    issue_block(a, bl, g, jj, slot);
+  };
+#pragma unroll
+  for (int j = 0; j < kSlots - 1; ++j) issue(j);
+  for (int k = 0; k < nblk; ++k) {
+    vm_wait<(kSlots - 2) * kNdma>();   // block k has landed (this wave's loads)
+    lds_barrier();                     // ... everyone's; slot (k-1) % kSlots is free
+    issue(k + kSlots - 1);
+    const int valid = min(kKB, cp.m - (k % p.nbc) * kKB);
+    attend_block(ts, smem + (k % kSlots) * kStage, kfa, vfa, vx, valid, a.scale_log2);
+  }
+  vm_wait<0>();
+  lds_barrier();
+
+  // epilogue: O / l, rounded to bf16, 8-byte stores
+#pragma unroll
+  for (int qt = 0; qt < kQTiles; ++qt) {
+    const float l = swap_sum32(swap_sum16(ts.lrun[qt]));
+    const float inv = 1.0f / l;
+    if (!qok[qt]) continue;
+    uint16_t* orow = a.out + qoff[qt] + 4 * qg;
+#pragma unroll
+    for (int dt = 0; dt < kDTiles; ++dt) {
+      const f32x4_t x = ts.o[dt][qt] * inv;
+      u32x2_t w = {pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
+      *(u32x2_t*)(orow + 16 * dt) = w;
+    }
+  }
+  trace_task(a.cm, (uint32_t)(p.n_copy + v), 7, (uint32_t)g, (uint32_t)rb, (uint32_t)nwait, 0, epoch, t0, t_ready,
+             seen, queue);
+}
+
+}  // namespace
+
+__global__ __launch_bounds__(kThreads, 1) void ag_attention_kernel(AttnArgs args) {
+  __shared__ __attribute__((aligned(1024))) char smem_raw[kSlots * kStage];
+  __shared__ uint32_t s_bcast[8];
+  OCG_LDS char* smem = (OCG_LDS char*)smem_raw;
+  const AttnPlan& p = args.plan;
+  const Common& cm = args.cm;
+  const uint32_t epoch = read_epoch(cm.hdr, s_bcast);
+  for (;;) {
+    const uint32_t u = next_ticket(&cm.hdr->ticket, s_bcast);
+    if ((int)u >= p.n_copy) break;
+    run_kv_copy(args, (int)u, epoch);
+  }
+  int q = (int)s_bcast[3] % kXcds, tried = 0;
+  uint32_t qt = 0;
+  for (;;) {
+    const int v = next_tile(cm.hdr, p.n_tiles, &q, &tried, s_bcast, &qt);
+    if (v < 0) break;
+    attention_tile(args, smem, v, epoch, ((uint32_t)q << 16) | qt);
+  }
+  finish(cm.hdr, epoch);
+}
+
+hipError_t launch_ag_attention(const AttnArgs& a, int grid, hipStream_t s) {
+  hipLaunchKernelGGL(ag_attention_kernel, dim3(grid), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+int resident_attention() {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, ag_attention_kernel, kThreads, 0) != hipSuccess) return 1;
+  return n > 0 ? n : 1;
+}
+
+}  // namespace ocg

@@ -105,6 +105,21 @@ struct MoeArgs {
   Common cm;
 };
 
+// AllGather-KV attention: copy tasks of both tensors, then attention tiles.
+struct AttnArgs {
+  const uint16_t* q;                      // [m][Hq][d], the local queries
+  const uint16_t* k_chunks[kMaxRanks];    // [m][Hkv][d] per rank
+  const uint16_t* v_chunks[kMaxRanks];
+  uint16_t* k_gathered;                   // [R*m][Hkv][d]
+  uint16_t* v_gathered;
+  uint16_t* out;                          // [m][Hq][d]
+  uint32_t* slab_cnt;
+  uint32_t* slab_flag;
+  float scale_log2;                       // log2(e) / sqrt(d)
+  AttnPlan plan;
+  Common cm;
+};
+
 struct RouteArgs {
   const float* logits;
   int32_t* topk_ids;
@@ -123,6 +138,8 @@ hipError_t launch_ag_gemm(const AgArgs& a, int tile, int grid, hipStream_t s);
 hipError_t launch_gemm_rs(const RsArgs& a, int tile, int grid, hipStream_t s);
 hipError_t launch_moe(const RouteArgs& r, const MoeArgs& a, int tile, int grid, hipStream_t s);
 hipError_t launch_moe_combine_rs(const CombArgs& a, int grid, hipStream_t s);
+hipError_t launch_ag_attention(const AttnArgs& a, int grid, hipStream_t s);
+int resident_attention();
 hipError_t launch_fill_u32(uint32_t* p, size_t n, uint32_t v, int release, hipStream_t s);
 // Resident workgroups per CU of each persistent kernel (op, tile preset).
 int resident_per_cu(int op, int tile);

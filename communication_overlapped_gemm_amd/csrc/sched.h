@@ -176,6 +176,44 @@ OCG_HD bool rs_tile_touches_local(const RsPlan& p, int rb) {
   return lo < (p.local + 1) * p.blk && hi > p.local * p.blk;
 }
 
+// AllGather-KV attention plan. The gathered keys / values are R chunks of m
+// tokens; a token row holds Hkv heads of d elements. Copy tasks are the AG
+// copy plan of one tensor (rows = tokens, K = Hkv * d) run for both tensors:
+// ticket u copies piece u >> 1 of that order for tensor u & 1 (0 keys, 1
+// values), so a slab's flag is published after 2 * slab_target tasks.
+// Attention tiles: the query rows of kv head g are the pairs (i, h), i < m,
+// h in [g*G, (g+1)*G), G = Hq / Hkv, numbered i-major (row r -> i = r / G,
+// h = g*G + r % G) and cut into blocks of kAttnRows; tile v -> (g = v / n_rb,
+// rb = v % n_rb), in the XCD queues of the GEMM tiles, so one XCD's tiles
+// share the keys and values of one head in its L2. A tile visits the keys in
+// blocks of kAttnKB, chunk by chunk, starting at the local chunk when swizzled
+// (its keys need no wait) and walking up the ranks from there.
+constexpr int kAttnRows = 256;   // query rows per tile (64 per wave)
+constexpr int kAttnKB = 64;      // keys per block
+constexpr int kAttnD = 128;      // head dimension
+
+struct AttnPlan {
+  AgPlan cp;                     // copy plan of one tensor
+  int Hq, Hkv, G, n_rb, n_tiles, nbc, n_copy;   // n_copy: tickets of both tensors
+};
+
+OCG_HD AttnPlan make_attn_plan(int R, int local, int m, int Hq, int Hkv, int S, int CT, int swizzle, int mode) {
+  AttnPlan p;
+  p.cp = make_ag_plan(R, local, m, Hkv * kAttnD, kAttnD, kAttnRows, kAttnKB, S, CT, swizzle, mode);
+  p.Hq = Hq; p.Hkv = Hkv; p.G = Hq / Hkv;
+  p.n_rb = cdiv(p.G * m, kAttnRows);
+  p.n_tiles = (mode == 2) ? 0 : Hkv * p.n_rb;
+  p.nbc = cdiv(m, kAttnKB);
+  p.n_copy = 2 * p.cp.n_copy;
+  return p;
+}
+
+// Chunk whose keys key block j (0 .. R*nbc-1) of a tile holds.
+OCG_HD int attn_block_chunk(const AttnPlan& p, int j) {
+  const int pos = j / p.nbc;
+  return p.cp.swizzle ? (p.cp.local + pos) % p.cp.R : pos;
+}
+
 // Tile presets: {BM, BN} = {256,224}, {128,224}, {128,256}, {128,128}.
 OCG_HD int tile_bm(int t) { return t == 6 ? 288 : t == 5 ? 320 : ((t == 0 || t == 4) ? 256 : 128); }
 OCG_HD int tile_bn(int t) { return (t == 2 || t == 4) ? 256 : (t == 3 ? 128 : 224); }

@@ -1,0 +1,236 @@
+// Device-side synchronisation and copy helpers shared by the persistent
+// kernels: flag waits and publishes, pull-copy tasks, ticket counters and the
+// XCD tile queues.
+//
+// Memory-model contract (agent scope, all 8 XCDs). Data that another
+// workgroup consumes inside the same launch (gathered rows, GEMM-RS partial
+// tiles) is written with agent-coherent stores (cache policy SC1, the
+// encoding of a relaxed agent-scope atomic store on this chip family), which
+// complete at the agent's point of coherence instead of staying dirty in one
+// XCD's L2. A producer therefore publishes by waiting for its own stores to
+// complete (vmcnt 0), a workgroup barrier, then one relaxed agent-scope atomic
+// on the counter / flag -- no L2 writeback, which measured ~20 us per publish
+// on a busy XCD. A consumer polls the flag with relaxed loads, bounded in
+// time, then issues one acquire fence (drops stale cache lines) before its
+// loads of the published data.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gemm_core.h"
+#include "ocg_internal.h"
+
+namespace ocg {
+
+typedef __attribute__((address_space(1))) const u32x4_t* gcptr16;
+typedef __attribute__((address_space(1))) u32x4_t* gptr16;
+
+__device__ __forceinline__ u32x4_t gload16(const void* p) { return *(gcptr16)p; }
+__device__ __forceinline__ void gstore16(void* p, u32x4_t v) { *(gptr16)p = v; }
+
+__device__ __forceinline__ uint64_t now_ticks() { return __builtin_amdgcn_s_memrealtime(); }
+
+__device__ __forceinline__ uint32_t xcc_id() {
+  uint32_t v;
+  asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(v));
+  return v & 0xf;
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+
+// ---------------------------------------------------------------- flags
+
+// consume_tile_wait over all the flags a task depends on, run by one whole
+// wave: the k-th flag the task enumerates is polled by lane k % 64 (relaxed
+// loads, bounded by the timeout), so the flags are read in parallel, and one
+// acquire fence after the polls covers every one of them (an agent-scope
+// acquire invalidates the non-coherent cache lines, which costs about a
+// microsecond, too much to pay per flag). A timed-out wait sets the error
+// word and proceeds, so the grid always drains.
+struct FlagWait {
+  uint64_t t0, timeout;
+  int k, lane;
+  bool ok;
+  uint32_t seen;
+  __device__ explicit FlagWait(uint64_t timeout_ticks)
+      : t0(now_ticks()), timeout(timeout_ticks), k(0), lane(threadIdx.x & 63), ok(true), seen(0) {}
+  // The next flag the task depends on, and the value that means "ready".
+  __device__ void operator()(const uint32_t* flag, uint32_t want) {
+    if ((k++ & 63) != lane) return;
+    uint32_t v = __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    while (v != want && ok) {
+      if (now_ticks() - t0 > timeout) {
+        ok = false;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+      v = __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    seen = v;
+  }
+  // After the last flag: the fence and the error word; returns the number of
+  // flags and (in *seen_out) a value lane 0 observed.
+  __device__ int finish(const Common& cm, uint32_t* seen_out) {
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    if (!ok) __hip_atomic_fetch_or(&cm.hdr->error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *seen_out = __shfl(seen, 0);
+    return k;
+  }
+};
+
+// Wait until every store this thread issued has completed (for the
+// agent-coherent stores below: is visible at agent scope).
+__device__ __forceinline__ void drain_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Cache-policy immediate of buffer stores: SC1 = agent-scope coherent.
+constexpr int kAgentCoherent = 16;
+
+__device__ __forceinline__ void store16_agent(__amdgpu_buffer_rsrc_t rs, uint32_t byte_off, u32x4_t v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, rs, (int)byte_off, 0, kAgentCoherent);
+}
+
+// produce_tile_notify for copy tasks: called by every thread after its
+// agent-coherent stores; returns (to thread 0) whether this task published
+// the slab flag (the last of the slab's copy tasks does).
+__device__ __forceinline__ bool publish_slab(uint32_t* cnt, uint32_t* flag, int slab, int target, uint32_t epoch,
+                             const Common& cm) {
+  drain_stores();
+  __syncthreads();
+  bool published = false;
+  if (threadIdx.x == 0) {
+    uint32_t old = __hip_atomic_fetch_add(&cnt[slab], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if ((int)old + 1 == target) {
+      __hip_atomic_store(&cnt[slab], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (slab != cm.fault_skip_slab)
+        __hip_atomic_store(&flag[slab], epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      published = true;
+    }
+  }
+  return published;
+}
+
+// ---------------------------------------------------------------- copy
+
+// Pull `n16` 16-byte granules from src to dst (agent-coherent stores) with
+// all 256 threads, 16 granules in flight per thread. n16 * 16 < 2^31.
+__device__ __forceinline__ void copy_granules(const uint16_t* src, uint16_t* dst, uint32_t n16) {
+  constexpr int U = 16;
+  const u32x4_t* s = (const u32x4_t*)src;
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(dst, n16 * 16u);
+  uint32_t i = threadIdx.x;
+  for (; i + (uint32_t)(U - 1) * kThreads < n16; i += (uint32_t)U * kThreads) {
+    u32x4_t v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = gload16(s + i + u * kThreads);
+#pragma unroll
+    for (int u = 0; u < U; ++u) store16_agent(rs, (i + u * kThreads) * 16u, v[u]);
+  }
+  for (; i < n16; i += kThreads) store16_agent(rs, i * 16u, gload16(s + i));
+}
+
+// One copy task of the AllGather (pull mode): rows [row0, row1) of the
+// gathered matrix come from rank `chunk`'s shard.
+__device__ __forceinline__ void run_copy_task(const AgPlan& p, const uint16_t* const* chunks, uint16_t* a_gathered,
+                              uint32_t* slab_cnt, uint32_t* slab_flag, int u, uint32_t epoch,
+                              const Common& cm) {
+  uint64_t t0 = now_ticks();
+  CopyDesc d = copy_desc(p, u);
+  const uint16_t* src = chunks[d.chunk] + (size_t)(d.row0 - d.chunk * p.m) * p.K;
+  uint16_t* dst = a_gathered + (size_t)d.row0 * p.K;
+  copy_granules(src, dst, (uint32_t)((size_t)(d.row1 - d.row0) * p.K / 8));
+  int target = slab_target(p.m, p.S, p.CT, p.bpr, d.slab);
+  bool pub = publish_slab(slab_cnt, slab_flag, d.slab, target, epoch, cm);
+  if (threadIdx.x == 0 && cm.trace && (uint32_t)u < cm.trace_cap) {
+    ocg_trace_rec* r = cm.trace + u;
+    uint64_t t1 = now_ticks();
+    r->ticket = u; r->kind = 1; r->a = d.chunk; r->b = d.piece; r->c = d.slab; r->d = pub;
+    r->hw = (xcc_id() << 16) | blockIdx.x; r->epoch = epoch;
+    r->t_start = t0; r->t_ready = t1; r->t_end = t1; r->flag_seen = 0; r->queue = 0;
+  }
+}
+
+// ---------------------------------------------------------------- scheduling helpers
+
+__device__ __forceinline__ uint32_t read_epoch(WsHeader* hdr, uint32_t* s_bcast) {
+  if (threadIdx.x == 0) {
+    uint32_t e = __hip_atomic_load(&hdr->epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
+    s_bcast[1] = e ? e : 1u;
+    s_bcast[3] = xcc_id();
+  }
+  __syncthreads();
+  return s_bcast[1];
+}
+
+__device__ __forceinline__ uint32_t next_ticket(uint32_t* counter, uint32_t* s_bcast) {
+  __syncthreads();
+  if (threadIdx.x == 0)
+    s_bcast[0] = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  return s_bcast[0];
+}
+
+// Next tile from the XCD queues: own XCD first, then the others. `*q` is the
+// queue being drained (starts at the XCD id). When it runs dry, one relaxed
+// load per queue (all eight in parallel) finds the queues that may still hold
+// tiles -- a queue whose ticket is past its last tile is empty for good, since
+// tickets only grow within a launch -- and the search moves to the next of
+// them; -1 once none is left. `*tried` is unused (kept for the call sites).
+__device__ __forceinline__ int next_tile(WsHeader* hdr, int n_tiles, int* q, int* tried, uint32_t* s_bcast,
+                                         uint32_t* t_out) {
+  (void)tried;
+  for (;;) {
+    const uint32_t t = next_ticket(&hdr->xtick[*q], s_bcast);
+    const int v = xcd_tile(*q, (int)t, n_tiles);
+    if (v >= 0) {
+      *t_out = t;
+      return v;
+    }
+    if (threadIdx.x < 64) {
+      bool open = false;
+      if (threadIdx.x < kXcds) {
+        const uint32_t x = __hip_atomic_load(&hdr->xtick[threadIdx.x], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        open = xcd_tile((int)threadIdx.x, (int)x, n_tiles) >= 0;
+      }
+      const uint64_t m = __ballot(open);
+      if (threadIdx.x == 0) s_bcast[5] = (uint32_t)m;
+    }
+    __syncthreads();
+    const uint32_t mask = s_bcast[5];
+    if (mask == 0) return -1;
+    // next open queue after *q, cyclically
+    const uint32_t rot = ((mask >> ((*q + 1) % kXcds)) | (mask << (kXcds - (*q + 1) % kXcds))) & 0xFFu;
+    *q = (*q + 1 + __builtin_ctz(rot)) % kXcds;
+  }
+}
+
+// Last workgroup out resets the counters and records the epoch. Relaxed
+// atomics suffice: a workgroup arrives here only after its last ticket
+// fetch returned (its value decided the exit), and the next launch on the
+// stream is ordered after this one by the kernel boundary.
+__device__ __forceinline__ void finish(WsHeader* hdr, uint32_t epoch) {
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t d = __hip_atomic_fetch_add(&hdr->done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (d + 1 == gridDim.x) {
+      __hip_atomic_store(&hdr->ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      for (int q = 0; q < kXcds; ++q)
+        __hip_atomic_store(&hdr->xtick[q], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(&hdr->done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(&hdr->epoch, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
+__device__ __forceinline__ void trace_task(const Common& cm, uint32_t slot, uint32_t kind, uint32_t a, uint32_t b,
+                                           uint32_t c, uint32_t d, uint32_t epoch, uint64_t t0, uint64_t t1,
+                                           uint32_t seen, uint32_t queue_ticket) {
+  if (threadIdx.x == 0 && cm.trace && slot < cm.trace_cap) {
+    ocg_trace_rec* r = cm.trace + slot;
+    r->ticket = slot; r->kind = kind; r->a = a; r->b = b; r->c = c; r->d = d;
+    r->hw = (xcc_id() << 16) | blockIdx.x; r->epoch = epoch;
+    r->t_start = t0; r->t_ready = t1; r->t_end = now_ticks(); r->flag_seen = seen; r->queue = queue_ticket;
+  }
+}
+
+}  // namespace ocg

@@ -212,6 +212,45 @@ def moe_combine_rs(y: torch.Tensor, topk_w: torch.Tensor, peer_partials: Sequenc
     return partial, out
 
 
+def ag_attention(q: torch.Tensor, k_chunks: Sequence[torch.Tensor], v_chunks: Sequence[torch.Tensor],
+                 local_rank: int = 0, *, k_gathered: Optional[torch.Tensor] = None,
+                 v_gathered: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                 workspace: Optional[Workspace] = None, config: Optional[Config] = None,
+                 stream=None) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """AllGather-KV attention (one context-parallel rank's share): q [m, Hq, d]
+    bf16, R = len(k_chunks) key / value chunks [m, Hkv, d]. Returns
+    (out [m, Hq, d], k_gathered [R*m, Hkv, d], v_gathered [R*m, Hkv, d])."""
+    R = len(k_chunks)
+    if len(v_chunks) != R:
+        raise ValueError("k_chunks and v_chunks must have one entry per rank")
+    _check_bf16(q, "q")
+    if q.dim() != 3:
+        raise ValueError("q must be [m, Hq, d]")
+    m, Hq, d = q.shape
+    Hkv = k_chunks[0].shape[1]
+    for r in range(R):
+        _check_bf16(k_chunks[r], f"k_chunks[{r}]", (m, Hkv, d))
+        _check_bf16(v_chunks[r], f"v_chunks[{r}]", (m, Hkv, d))
+    dev = q.device
+    if k_gathered is None:
+        k_gathered = torch.empty((R * m, Hkv, d), dtype=torch.bfloat16, device=dev)
+    if v_gathered is None:
+        v_gathered = torch.empty((R * m, Hkv, d), dtype=torch.bfloat16, device=dev)
+    if out is None:
+        out = torch.empty((m, Hq, d), dtype=torch.bfloat16, device=dev)
+    _check_bf16(k_gathered, "k_gathered", (R * m, Hkv, d))
+    _check_bf16(v_gathered, "v_gathered", (R * m, Hkv, d))
+    _check_bf16(out, "out", (m, Hq, d))
+    ws = workspace or Workspace.cached(_lib.OP_AG_ATTENTION, R, m, Hq, Hkv, device=dev.index)
+    kp = (C.c_void_p * R)(*[t.data_ptr() for t in k_chunks])
+    vp = (C.c_void_p * R)(*[t.data_ptr() for t in v_chunks])
+    cfg = _cfg(config)
+    check(lib.ocg_ag_attention(handle(dev.index), q.data_ptr(), kp, vp, R, local_rank, m, Hq, Hkv, d,
+                               k_gathered.data_ptr(), v_gathered.data_ptr(), out.data_ptr(), ws.ptr, ws.nbytes,
+                               C.byref(cfg), _stream_ptr(stream)), "ocg_ag_attention")
+    return out, k_gathered, v_gathered
+
+
 def signal(flags: torch.Tensor, value: int, stream=None) -> None:
     """Peer-notify stand-in: write `value` into every uint32 of `flags`."""
     if flags.dtype not in (torch.int32, torch.uint32) or not flags.is_contiguous():

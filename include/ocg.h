@@ -1,9 +1,10 @@
 /*
  * ocg.h -- communication-overlapped GEMM for AMD Instinct MI355X (gfx950).
  *
- * C ABI of the fused tile-centric AllGather-GEMM, GEMM-ReduceScatter and
- * AllGather + MoE grouped GEMM, each computing one GPU's share of a
- * tensor-parallel LLM layer. The operations are the ones named in
+ * C ABI of the fused tile-centric AllGather-GEMM, GEMM-ReduceScatter,
+ * AllGather + MoE grouped GEMM, MoE TopK-Reduce + ReduceScatter and
+ * AllGather-KV attention, each computing one GPU's share of a tensor- or
+ * context-parallel LLM layer. The operations are the ones named in
  * "TileLink: Generating Efficient Compute-Communication Overlapping Kernels
  * using Tile-Centric Primitives" (MLSys 2025 talk summary), sections "Key
  * Findings" (AllGather-GEMM, GEMM-ReduceScatter), "Technical Deep Dive"
@@ -28,7 +29,7 @@
  *     nothing has been enqueued. No C++ exception or abort crosses the ABI.
  *     A flag wait that exceeds its time bound is recorded in the workspace's
  *     error word and reported by ocg_check() after the stream has drained.
- *   - Shapes: K must be a multiple of 64, N a multiple of 8, 1 <= R <= 16.
+ *   - GEMM shapes: K must be a multiple of 64, N a multiple of 8, 1 <= R <= 16.
  *     M, N and the per-rank rows m may leave ragged tiles. Pointers to bf16
  *     matrices must be 16-byte aligned.
  */
@@ -54,6 +55,7 @@ extern "C" {
 #define OCG_OP_GEMM_RS 1
 #define OCG_OP_AG_GROUPED_GEMM 2
 #define OCG_OP_MOE_COMBINE_RS 3
+#define OCG_OP_AG_ATTENTION 4
 
 /* Fused (default), GEMM tiles only with every flag treated as published
  * (measurement of the GEMM part; expects the gathered buffer filled), or
@@ -79,15 +81,18 @@ extern "C" {
  * GEMM-RS tile v -> v, reduce strip j -> n_tiles + j (v = tile index in the
  * grouped tile order; TopK-Reduce: task u -> u).
  * kind: 1 copy task, 2 AG-GEMM tile, 3 GEMM-RS tile, 4 MoE tile, 5 GEMM-RS
- * reduce strip, 6 TopK-Reduce task. Times are the GPU's constant 100 MHz
- * clock. */
+ * reduce strip, 6 TopK-Reduce task, 7 attention tile (AllGather-KV
+ * attention: copy ticket u -> u, tile v -> #copy tickets + v). Times are the
+ * GPU's constant 100 MHz clock. */
 typedef struct ocg_trace_rec {
   uint32_t ticket, kind;
   uint32_t a, b, c, d;   /* copy: chunk, piece, slab, published(0/1)
                             AG tile: rb, cb, #slabs waited, 0
                             RS tile: rb, cb, local-block(0/1), 0
                             MoE tile: expert, row start, rows, cb | (#slabs waited << 16)
-                            RS strip: row0, row1, #flags waited, 0 */
+                            RS strip: row0, row1, #flags waited, 0
+                            KV copy: chunk, piece | (tensor << 16), slab, published
+                            attention tile: kv head, row block, #flags waited, 0 */
   uint32_t hw;           /* (XCC id << 16) | workgroup id */
   uint32_t epoch;        /* epoch of the call */
   uint64_t t_start, t_ready, t_end; /* ready = dependencies satisfied (tiles)
@@ -129,7 +134,9 @@ int ocg_create(int device, ocg_handle* out);
 void ocg_destroy(ocg_handle h);
 
 /* Workspace bytes for `op`: AG_GEMM (R, m = rows per rank, K, N),
- * GEMM_RS (R, m = M total rows, K, N), AG_GROUPED_GEMM (R, m, K, N, E, topk).
+ * GEMM_RS (R, m = M total rows, K, N), AG_GROUPED_GEMM (R, m, K, N, E, topk),
+ * MOE_COMBINE_RS (R, m, 0, N, 0, topk), AG_ATTENTION (R, m = tokens per
+ * rank, K = Hq, N = Hkv).
  * Unused arguments are ignored. Returns 0 on invalid arguments. */
 size_t ocg_workspace_bytes(int op, int R, int64_t m, int64_t K, int64_t N, int E, int topk);
 
@@ -230,6 +237,37 @@ int ocg_moe_combine_rs(ocg_handle h, const void* y, const float* topk_w, int R, 
                        void* partial, void* out, void* ws, size_t ws_bytes,
                        const ocg_config* cfg, void* stream);
 
+/* AllGather-KV attention (one context-parallel rank's share): "TileLink ...
+ * (MLSys 2025 talk summary)", section "Experimental Setup & Results", names
+ * an attention whose KV AllGather is overlapped with the attention itself;
+ * the formula is the plain reading of unmasked softmax attention of the local
+ * queries over the whole gathered sequence, with grouped kv heads:
+ *   k_gathered = concat_r k_chunks[r],  v_gathered = concat_r v_chunks[r]
+ *   out[i][h] = sum_j softmax_j( q[i][h] . k_gathered[j][h / G] / sqrt(d) )
+ *               * v_gathered[j][h / G]                  (G = Hq / Hkv)
+ * Scores and the softmax run in fp32 (running maximum and sum over key
+ * blocks of 64), the probabilities enter the value product as bf16, and out
+ * is rounded to bf16 (nearest-even).
+ *   q            : bf16 [m, Hq, d], the local queries, read
+ *   k_chunks[r], v_chunks[r] : bf16 [m, Hkv, d] of rank r (r = 0..R-1), read
+ *   k_gathered, v_gathered   : bf16 [R*m, Hkv, d], written (every chunk, the
+ *                  local one included)
+ *   out          : bf16 [m, Hq, d], written
+ * Copy tasks pull each peer chunk of keys and values into the gathered
+ * buffers slab by slab (slab_rows tokens, default the whole chunk) and
+ * publish a flag per slab; each tile (256 query rows of one kv head) starts
+ * on the local chunk, read from its own shard, and waits on a peer chunk's
+ * flags before loading it. Requires d == 128, Hq % Hkv == 0,
+ * R*m*Hkv*d < 2^31, m*Hq*d < 2^31, 16-byte aligned pointers; workspace from
+ * ocg_workspace_bytes(OCG_OP_AG_ATTENTION, R, m, Hq, Hkv, 0, 0). cfg.tile is
+ * ignored; cfg.mode GEMM_ONLY runs the attention with every flag treated as
+ * published (expects the gathered buffers filled), COPY_ONLY the copies.
+ * Errors as for the other calls. */
+int ocg_ag_attention(ocg_handle h, const void* q, const void* const* k_chunks, const void* const* v_chunks,
+                     int R, int local_rank, int64_t m, int64_t Hq, int64_t Hkv, int64_t d,
+                     void* k_gathered, void* v_gathered, void* out, void* ws, size_t ws_bytes,
+                     const ocg_config* cfg, void* stream);
+
 /* Stand-in for a peer's remote notify: writes `value` into `count` uint32
  * flags at `flags` (device) with release semantics, on `stream`. */
 int ocg_signal(uint32_t* flags, int count, uint32_t value, void* stream);
@@ -248,7 +286,10 @@ const char* ocg_status_string(int status);
  * out[4]=copy rows, out[5]=#copy tasks, out[6]=#tiles (static ops),
  * out[7]=#slabs. For OCG_OP_MOE_COMBINE_RS: out[0]=-1, out[3]=rows per
  * task outside the local block, out[4]=rows per local task, out[5]=#tasks,
- * out[6]=#local tasks (the first ones), the rest 0. For GEMM_RS pass m = M. E and topk are the grouped GEMM's
+ * out[6]=#local tasks (the first ones), the rest 0. For OCG_OP_AG_ATTENTION
+ * (K = Hq, N = Hkv): out[0]=-1, out[1]=query rows per tile, out[2]=keys per
+ * block, out[3]=slab tokens, out[4]=copy tokens, out[5]=#copy tickets (both
+ * tensors), out[6]=#tiles, out[7]=#slabs. For GEMM_RS pass m = M. E and topk are the grouped GEMM's
  * expert count and picks per token (they choose its default tile; ignored
  * by the other ops). Returns OCG_OK or an error. */
 int ocg_plan_info(int op, int R, int local_rank, int64_t m, int64_t K, int64_t N, int E, int topk,
@@ -262,7 +303,11 @@ int ocg_plan_info(int op, int R, int local_rank, int64_t m, int64_t K, int64_t N
  *          dependency slab ids (-1 if none);
  * RS tile: desc[1]=rb, [2]=cb, [3]=local-block (0/1), [4]=XCD queue,
  *          [5]=ticket within the queue;
- * RS strip: desc[1]=row0, [2]=row1. */
+ * RS strip: desc[1]=row0, [2]=row1;
+ * AG_ATTENTION (K = Hq, N = Hkv): copy ticket: desc[0]=1, [1..5] as for a
+ *          copy, [6]=tensor (0 keys, 1 values); tile: desc[0]=7, [1]=kv
+ *          head, [2]=row block, [3]=#flags each wave waits on, [4]=XCD
+ *          queue, [5]=ticket within the queue. */
 int ocg_plan_task(int op, int R, int local_rank, int64_t m, int64_t K, int64_t N,
                   const ocg_config* cfg, int64_t ticket, int64_t desc[8]);
 

@@ -43,6 +43,15 @@ GEMM-RS: slots [0, n_tiles) are GEMM tiles in the same order and queues,
   blk = M/R, in ascending row order; a strip waits for the flags of every
   tile of the row blocks it overlaps (and for the peers' flags of those
   tiles).
+AllGather-KV attention (R ranks of m tokens, Hq query heads over Hkv kv
+  heads, G = Hq/Hkv, ROWS query rows per tile): the AG copy list of one
+  tensor with rows = tokens, each entry taken twice in a row -- keys, then
+  values (tickets 2u and 2u+1) -- so a slab is complete after twice the AG
+  count of tasks. Then the tiles: for kv head g the query rows are the pairs
+  (i, h), h in [g*G, (g+1)*G), in i-major order, cut into ROWS-row blocks;
+  tile v = g * n_rb + rb, in the XCD queues above. Every tile visits the
+  chunks in the order local, local+1, ... (mod R) when swizzled, 0..R-1
+  otherwise, and waits for all slabs of every chunk but the local one.
 MoE: the AG-GEMM copy list, then one tile per (expert e, column block cb,
   row tile rt) in that nesting order; expert e's rows
   [off_e + rt*BM, min(off_e + (rt+1)*BM, off_{e+1})) of the expert-sorted slot
@@ -232,3 +241,35 @@ def combine_rs_plan(R, T, local, CR, CRL):
     for u, (r0, r1, is_local) in enumerate(spans):
         out.append(("combine", u, tuple((r + base) % T for r in range(r0, r1)), is_local))
     return out
+
+
+ATTN_ROWS = 256   # query rows per attention tile
+
+
+def attention_plan(R, m, Hq, Hkv, local, S, CT, swizzle=True, mode="fused"):
+    """Ticket list of the AllGather-KV attention kernel: ("copy", slot,
+    CopyTask, tensor) then ("tile", slot, g, rb, rows, deps, queue, qticket)
+    with rows the (i, h) pairs of the tile and deps the slabs waited on."""
+    G = Hq // Hkv
+    bpr = _cdiv(m, S)
+    out = []
+    if mode in ("fused", "copy_only"):
+        for t in copy_tasks(R, m, S, CT, local, swizzle):
+            for tensor in (0, 1):
+                out.append(("copy", len(out), t, tensor))
+    if mode in ("fused", "gemm_only"):
+        n_rb = _cdiv(G * m, ATTN_ROWS)
+        where = queue_of(Hkv * n_rb)
+        base = len(out)
+        deps = tuple(c * bpr + s for c in range(R) if c != local for s in range(bpr)) if mode == "fused" else ()
+        for g in range(Hkv):
+            for rb in range(n_rb):
+                rows = tuple((r // G, g * G + r % G) for r in range(rb * ATTN_ROWS, min((rb + 1) * ATTN_ROWS, G * m)))
+                v = g * n_rb + rb
+                out.append(("tile", base + v, g, rb, rows, deps, *where[v]))
+    return out
+
+
+def attention_chunk_order(R, local, swizzle=True):
+    """Chunks in the order a tile's key blocks visit them."""
+    return [(local + p) % R for p in range(R)] if swizzle else list(range(R))

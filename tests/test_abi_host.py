@@ -170,3 +170,53 @@ def test_rs_plan_matches_oracle_schedule(R, M, K, N, local, tile):
         else:
             assert d[:3] == [5, t[2], t[3]]
     assert ocg.plan_task(ocg.OP_GEMM_RS, R, local, M, K, N, len(want), cfg)[0] == 0
+
+
+ATTN_CASES = [
+    # R, m, Hq, Hkv, local, slab_rows, copy_rows
+    (8, 2048, 32, 8, 0, 0, 0),
+    (8, 2048, 32, 8, 5, 256, 0),
+    (3, 200, 8, 2, 2, 64, 16),
+    (4, 70, 6, 2, 1, 0, 0),
+    (2, 1, 4, 4, 1, 0, 0),
+]
+
+
+@pytest.mark.parametrize("case", ATTN_CASES)
+@pytest.mark.parametrize("swizzle", [1, 0])
+@pytest.mark.parametrize("mode", ["fused", "gemm_only", "copy_only"])
+def test_attention_plan_matches_oracle_schedule(case, swizzle, mode):
+    R, m, Hq, Hkv, local, S, CT = case
+    modes = {"fused": 0, "gemm_only": 1, "copy_only": 2}
+    cfg = ocg.default_config(swizzle=swizzle, mode=modes[mode], slab_rows=S, copy_rows=CT)
+    info = ocg.plan_info(ocg.OP_AG_ATTENTION, R, local, m, Hq, Hkv, cfg)
+    assert (info["BM"], info["BN"]) == (256, 64)
+    want = sch.attention_plan(R, m, Hq, Hkv, local, info["slab_rows"], info["copy_rows"], bool(swizzle), mode)
+    assert len(want) == info["n_copy_or_strips"] + info["n_tiles"]
+    assert info["n_slabs_or_strip_rows"] == R * (-(-m // info["slab_rows"]))
+    for t in want:
+        d = ocg.plan_task(ocg.OP_AG_ATTENTION, R, local, m, Hq, Hkv, t[1], cfg)
+        if t[0] == "copy":
+            c = t[2]
+            assert d[:7] == [1, c.chunk, c.piece, c.row0, c.row1, c.slab, t[3]]
+        else:
+            assert d[:6] == [7, t[2], t[3], len(t[5]), t[6], t[7]]
+    assert ocg.plan_task(ocg.OP_AG_ATTENTION, R, local, m, Hq, Hkv, len(want), cfg)[0] == 0
+
+
+def test_attention_plan_defaults_and_validation():
+    # the 16K-context GQA share: one flag per chunk, 64-token copy tasks,
+    # 256 tiles (one per CU), 512 copy tickets
+    p = ocg.plan_info(ocg.OP_AG_ATTENTION, 8, 0, 2048, 32, 8)
+    assert (p["slab_rows"], p["copy_rows"], p["n_tiles"], p["n_copy_or_strips"]) == (2048, 64, 256, 512)
+    lib = ocg.lib
+    assert lib.ocg_workspace_bytes(ocg.OP_AG_ATTENTION, 8, 2048, 32, 8, 0, 0) > 256
+    assert lib.ocg_workspace_bytes(ocg.OP_AG_ATTENTION, 8, 2048, 30, 8, 0, 0) == 0   # Hq % Hkv
+    assert lib.ocg_workspace_bytes(ocg.OP_AG_ATTENTION, 17, 2048, 32, 8, 0, 0) == 0  # R > 16
+    assert lib.ocg_workspace_bytes(ocg.OP_AG_ATTENTION, 8, 0, 32, 8, 0, 0) == 0      # m < 1
+    with pytest.raises(ocg.OcgError):
+        ocg.plan_info(ocg.OP_AG_ATTENTION, 8, 0, 2048, 32, 8, ocg.default_config(slab_rows=8))
+    cfg = ocg.default_config()
+    ptrs = (C.c_void_p * 2)()
+    assert lib.ocg_ag_attention(None, None, ptrs, ptrs, 2, 0, 64, 4, 1, 128, None, None, None, None, 0,
+                                C.byref(cfg), None) == ocg.ERR_INVALID_ARG

@@ -161,3 +161,29 @@ def test_combine_rs_plan_covers_rows_once_local_block_first():
         assert all(p[3] for p in plan[:n_lt]) and not any(p[3] for p in plan[n_lt:])
         assert {r for p in plan[:n_lt] for r in p[2]} == set(range(local * blk, (local + 1) * blk))
         assert all(len(p[2]) <= (CRL if p[3] else CR) for p in plan)
+
+
+@pytest.mark.parametrize("R,m,Hq,Hkv,local,S,CT", [(8, 2048, 32, 8, 0, 2048, 64), (3, 200, 8, 2, 2, 64, 16),
+                                                  (4, 70, 6, 2, 1, 70, 35)])
+def test_attention_plan_covers_rows_and_chunks_once(R, m, Hq, Hkv, local, S, CT):
+    plan = sch.attention_plan(R, m, Hq, Hkv, local, S, CT)
+    copies = [t for t in plan if t[0] == "copy"]
+    tiles = [t for t in plan if t[0] == "tile"]
+    assert [t[1] for t in plan] == list(range(len(plan)))
+    # every token row of every chunk copied once per tensor
+    for tensor in (0, 1):
+        rows = sorted(r for t in copies if t[3] == tensor for r in range(t[2].row0, t[2].row1))
+        assert rows == list(range(R * m))
+    # the slab count each slab needs is twice the AG count
+    tgt = sch.slab_targets(R, m, S, CT)
+    for s, n in enumerate(tgt):
+        assert sum(1 for t in copies if t[2].slab == s) == 2 * n
+    # every query row (i, h) in exactly one tile, with its own kv head
+    G = Hq // Hkv
+    seen = [r for t in tiles for r in t[4]]
+    assert sorted(seen) == [(i, h) for i in range(m) for h in range(Hq)]
+    for t in tiles:
+        assert all(h // G == t[2] for _, h in t[4])
+        assert len(t[5]) == (R - 1) * (-(-m // S)) and all(s // (-(-m // S)) != local for s in t[5])
+    assert sch.attention_chunk_order(R, local)[0] == local
+    assert sorted(sch.attention_chunk_order(R, local)) == list(range(R))

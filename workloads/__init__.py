@@ -188,6 +188,26 @@ def make_attention(R: int, m: int, Hq: int, Hkv: int, d: int, seed: int, local_r
     return AttentionInputs(R, m, Hq, Hkv, d, local_rank, q, ks, vs, seed)
 
 
+def make_attention_retrieval(R: int, m: int, Hq: int, Hkv: int, d: int, seed: int, local_rank: int = 0,
+                             gain: float = 4.0):
+    """Structured attention inputs in which every query picks out one key:
+    K entries are +-1, V ~ N(0, 1), and query (i, h) is ``gain`` times the
+    gathered key row targets[i, h] of its kv head h // (Hq / Hkv). Draw order:
+    K_0..K_{R-1} signs, V_0..V_{R-1}, then the targets. Returns (inputs,
+    targets [m, Hq] int64)."""
+    rng = np.random.default_rng(seed)
+    ks = [(rng.integers(0, 2, (m, Hkv, d)) * 2 - 1).astype(np.float32) for _ in range(R)]
+    vs = [_draw_bf16(rng, (m, Hkv, d), "normal", 1.0) for _ in range(R)]
+    targets = rng.integers(0, R * m, (m, Hq))
+    G = Hq // Hkv
+    k_full = np.concatenate(ks)
+    heads = np.arange(Hq) // G
+    q = gain * k_full[targets, heads[None, :], :]
+    as_bits = lambda a: (a.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)   # exact: +-1, +-gain
+    x = AttentionInputs(R, m, Hq, Hkv, d, local_rank, as_bits(q), [as_bits(c) for c in ks], vs, seed)
+    return x, targets
+
+
 @dataclass(frozen=True)
 class Workload:
     name: str
