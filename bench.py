@@ -128,7 +128,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--skip-extras", action="store_true")
-    ap.add_argument("--op", default=WORKLOAD, choices=[WORKLOAD, "ag_gemm_8b", "gemm_rs_8b", "ag_moe", "moe_combine_rs"],
+    ap.add_argument("--op", default=WORKLOAD, choices=[WORKLOAD, "ag_gemm_8b", "gemm_rs_8b", "ag_moe", "moe_combine_rs",
+                                                     "ag_attention"],
                     help="profiling aid: launch only this operation (no benchmark record)")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -301,7 +302,24 @@ def op_setups(torch, ocg, workloads, upload):
             ocg.moe_combine_rs(y, wt, peers, x.local_rank, partial=part, out=o, workspace=ws)
         return w, x, ws, launch
 
-    return {"ag_gemm_8b": ag8, "gemm_rs_8b": rs8, "ag_moe": moe, "moe_combine_rs": comb}
+    def attn():
+        w = workloads.workload("ag_attention")
+        x = w.make()
+        q = upload(x.q)
+        ks = [upload(c) for c in x.k_chunks]
+        vs = [upload(c) for c in x.v_chunks]
+        S = x.R * x.m
+        kg = torch.empty((S, x.Hkv, x.d), dtype=torch.bfloat16, device="cuda")
+        vg = torch.empty((S, x.Hkv, x.d), dtype=torch.bfloat16, device="cuda")
+        o = torch.empty((x.m, x.Hq, x.d), dtype=torch.bfloat16, device="cuda")
+        ws = ocg.Workspace(ocg.OP_AG_ATTENTION, x.R, x.m, x.Hq, x.Hkv)
+
+        def launch(mode=0):
+            ocg.ag_attention(q, ks, vs, x.local_rank, k_gathered=kg, v_gathered=vg, out=o, workspace=ws,
+                             config=ocg.default_config(mode=mode))
+        return w, x, ws, launch
+
+    return {"ag_gemm_8b": ag8, "gemm_rs_8b": rs8, "ag_moe": moe, "moe_combine_rs": comb, "ag_attention": attn}
 
 
 def other_ops(torch, np, ocg, workloads, upload, stream, n):
@@ -344,6 +362,17 @@ def other_ops(torch, np, ocg, workloads, upload, stream, n):
     out["moe_combine_rs"] = {"t_us": round(t * 1e3, 2), "hbm_bytes": hbm,
                              "hbm_gbs_algorithmic": round(hbm / (t * 1e-3) / 1e9, 1),
                              "hbm_frac": round(hbm / (t * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+    del launch
+    # AllGather-KV attention (MFMA-bound): fused, attention only, copies only
+    w, x, ws, launch = setups["ag_attention"]()
+    times = {label: median_ms(torch, lambda: launch(mode), n, stream)
+             for label, mode in (("fused", 0), ("attn", 1), ("copy", 2))}
+    ws.check()
+    tf = w.flops() / (times["fused"] * 1e-3) / 1e12
+    out["ag_attention"] = {"t_fused_us": round(times["fused"] * 1e3, 2), "t_attn_us": round(times["attn"] * 1e3, 2),
+                           "t_copy_us": round(times["copy"] * 1e3, 2), "tflops": round(tf, 2),
+                           "mfma_frac": round(tf / PEAK_BF16_TFLOPS, 4),
+                           "e_max": round(max(times["attn"], times["copy"]) / times["fused"], 4)}
     return out
 
 

@@ -15,12 +15,19 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libocg.so")
 SOURCES = ["kernels.hip", "attention.hip", "api.cpp"]
+# Per-source code-generation options. The attention kernel keeps its MFMA
+# accumulators in VGPRs (VGPR form): the softmax reads every score with VALU
+# instructions, which cannot take accumulation registers, and in the default
+# form each one would be moved through a VGPR per key block (the GEMM kernels
+# measured slower in that form). Its maxima assume no NaN inputs, so fmaxf
+# needs no quieting of its operands.
+SOURCE_FLAGS = {"attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-fno-honor-nans"]}
 
 # Packed-fp32 instructions are disabled (v_pk_*_f32 forms are not trusted on
 # the test machines); hipcc's host pass warns that it does not know the
 # feature, which is harmless.
 FLAGS = [
-    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function", "-Wno-unknown-pragmas",
     # m0 is listed as clobbered by the direct-to-LDS load asm; the compiler
@@ -37,8 +44,7 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build the HIP library)")
 
 
-def build(verbose: bool = False) -> str:
-    cmd = [hipcc(), *FLAGS, *[os.path.join(CSRC, s) for s in SOURCES], "-o", LIB + ".tmp"]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -48,6 +54,20 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
     if verbose and err.strip():
         print(err, file=sys.stderr)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source to an object (with its own options), in
+    parallel, then link libocg.so."""
+    from concurrent.futures import ThreadPoolExecutor
+    tmp = os.path.join(PKG, "_build")
+    os.makedirs(tmp, exist_ok=True)
+    objs = [os.path.join(tmp, s + ".o") for s in SOURCES]
+    cmds = [[hipcc(), *FLAGS, *SOURCE_FLAGS.get(s, []), "-c", os.path.join(CSRC, s), "-o", o]
+            for s, o in zip(SOURCES, objs)]
+    with ThreadPoolExecutor(len(cmds)) as ex:
+        list(ex.map(lambda c: _run(c, verbose), cmds))
+    _run([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", LIB + ".tmp"], verbose)
     os.replace(LIB + ".tmp", LIB)
     return LIB
 

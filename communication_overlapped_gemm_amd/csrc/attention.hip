@@ -9,10 +9,11 @@
 // peer's key or value chunk into the gathered buffers, publish the slab flag
 // once its key and value pieces have landed), then attention tiles from the
 // XCD queues. A tile holds 256 query rows (query, head) that share one kv
-// head, 64 per wave, and streams the keys and values in blocks of 64 through
-// a 4-slot LDS ring filled by direct-to-LDS loads, starting with the local
-// chunk (read from the local shard, never waited on); before its first load
-// of a peer chunk each wave waits on that chunk's slab flags.
+// head; its 8 waves (two per SIMD) take 32 rows each and stream the keys and
+// values in blocks of 64 through a 4-slot LDS ring filled by direct-to-LDS
+// loads, starting with the local chunk (read from the local shard, never
+// waited on); before its first load of a peer chunk each wave waits on that
+// chunk's slab flags.
 //
 // Per wave and key block (flash-attention style online softmax, fp32):
 //   S^T = K Q^T      v_mfma_f32_16x16x32_bf16, A = key rows from LDS
@@ -21,14 +22,24 @@
 //   softmax          lane (l & 15) of every 16-lane row owns one query of a
 //                    16-query column block and 4 of its keys per 16-key tile,
 //                    so a row maximum is an in-lane maximum plus two lane
-//                    swaps (v_permlane16/32_swap);
+//                    swaps (v_permlane16/32_swap); the exponentials are taken
+//                    against a reference that only moves when a block's
+//                    maximum passes it by 2^8, so the accumulators are
+//                    rarely rescaled;
 //   O^T += V^T P^T   A = value columns from LDS with the transposing read
 //                    ds_read_b64_tr_b16, B = the probabilities converted to
 //                    bf16 in registers. Each lane's 8 probabilities of a
 //                    32-key step are keys {4q..4q+3, 16+4q..16+4q+3}
 //                    (q = lane >> 4), the order the S^T accumulators leave
 //                    them in; the value reads fetch the same keys, so the
-//                    contraction pairs them up.
+//                    contraction pairs them up;
+//   row sums         one more MFMA per 32-key step against a 0/1 key
+//                    validity operand, so keys past a chunk's end (whose
+//                    value rows load as zeros) drop out without masking the
+//                    scores, and no VALU adds are spent on the sums.
+// On this chip the MFMA and VALU work of a SIMD mostly add up rather than
+// overlap (measured), so the loop is built to spend few VALU instructions per
+// score: an FMA, an exponential, half a conversion and part of a maximum.
 // The output accumulators hold O^T: lane (q, j) has O[query j][d = 16t + 4q
 // .. +3] of each 16x16 block; the epilogue divides by the row sums and
 // stores 8-byte pieces.
@@ -42,18 +53,21 @@
 namespace ocg {
 namespace {
 
+constexpr int kWaves = 8;                   // waves per workgroup (two per SIMD)
+constexpr int kAThreads = 64 * kWaves;
 constexpr int kD = kAttnD;                  // head dimension (128)
 constexpr int kKB = kAttnKB;                // keys per block (64)
 constexpr int kSlots = 4;                   // LDS ring slots
 constexpr int kRowBytes = kD * 2;           // one head's key or value row (256 B)
 constexpr int kPart = kKB * kRowBytes;      // keys (or values) of one block: 16 KiB
 constexpr int kStage = 2 * kPart;           // keys, then values
-constexpr int kLoads = kPart / 1024 / 4;    // 1 KiB loads per wave per tensor per block (4)
+constexpr int kLoads = kPart / 1024 / kWaves;   // 1 KiB loads per wave per tensor per block
 constexpr int kNdma = 2 * kLoads;           // loads per wave per block
-constexpr int kQTiles = 4;                  // 16-row query blocks per wave
+constexpr int kRowsW = kAttnRows / kWaves;  // query rows per wave
+constexpr int kQTiles = kRowsW / 16;        // 16-row query blocks per wave
 constexpr int kDSteps = kD / 32;            // MFMA k steps over the head dimension
-constexpr int kKTiles = kKB / 16;           // 16-key blocks per key block
 constexpr int kDTiles = kD / 16;            // 16-column blocks of the output
+constexpr float kLazy = 8.0f;               // reference lag of the online softmax (log2 units)
 
 static_assert(kSlots * kStage <= 160 * 1024 - 64, "ring fits the LDS");
 static_assert(kKB == 64 && kD == 128, "fragment maps below assume 64-key blocks of 128-wide heads");
@@ -75,15 +89,6 @@ __device__ __forceinline__ float swap_max32(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
-__device__ __forceinline__ float swap_sum16(float x) {
-  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-__device__ __forceinline__ float swap_sum32(float x) {
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
 // One copy task: piece u >> 1 of the AG copy order of tensor u & 1.
 __device__ void run_kv_copy(const AttnArgs& a, int u, uint32_t epoch) {
   const AgPlan& p = a.plan.cp;
@@ -92,7 +97,7 @@ __device__ void run_kv_copy(const AttnArgs& a, int u, uint32_t epoch) {
   const CopyDesc d = copy_desc(p, u >> 1);
   const uint16_t* src = (tensor ? a.v_chunks[d.chunk] : a.k_chunks[d.chunk]) + (size_t)(d.row0 - d.chunk * p.m) * p.K;
   uint16_t* dst = (tensor ? a.v_gathered : a.k_gathered) + (size_t)d.row0 * p.K;
-  copy_granules(src, dst, (uint32_t)((size_t)(d.row1 - d.row0) * p.K / 8));
+  copy_granules<kAThreads>(src, dst, (uint32_t)((size_t)(d.row1 - d.row0) * p.K / 8));
   const int target = 2 * slab_target(p.m, p.S, p.CT, p.bpr, d.slab);
   const bool pub = publish_slab(a.slab_cnt, a.slab_flag, d.slab, target, epoch, a.cm);
   trace_task(a.cm, (uint32_t)u, 1, d.chunk, (uint32_t)d.piece | ((uint32_t)tensor << 16), d.slab, pub ? 1u : 0u,
@@ -111,34 +116,38 @@ struct BlockLoads {
 struct TileState {
   bf16x8_t qf[kQTiles][kDSteps];   // query fragments: row (lane & 15) of block qt, d = 32u + 8(lane >> 4) ..
   f32x4_t o[kDTiles][kQTiles];     // O^T accumulators
-  float mrun[kQTiles];             // running maximum of the scaled scores (log2 units)
-  float lrun[kQTiles];             // this lane's part of the running row sum
+  f32x4_t l[kQTiles];              // row sums, from an MFMA against the key validity (all 4 entries equal)
+  float mrun[kQTiles];             // softmax reference of the query (log2 units)
 };
 
 // Key block j: issue this wave's 8 loads into `slot` (LDS byte address).
-// Rows past the chunk's end re-read its last row (masked in the softmax).
+// Key rows past the chunk's end re-read its last row (a duplicate score,
+// harmless to the running maximum); value rows past it read zeros (buffer
+// loads bounded to the chunk's rows of this head), and the row sums leave
+// those keys out, so they add nothing.
 __device__ __forceinline__ void issue_block(const AttnArgs& a, const BlockLoads& bl, int g, int j, uint32_t slot) {
   const AttnPlan& p = a.plan;
   const int c = attn_block_chunk(p, j);
+  const int m = p.cp.m;
   const int key0 = (j % p.nbc) * kKB;
-  const size_t row_elems = (size_t)p.Hkv * kD;
+  const uint32_t row_bytes = (uint32_t)p.Hkv * kRowBytes;
   const char* kb;
   const char* vb;
   if (c == p.cp.local) {
     kb = (const char*)(a.k_chunks[c] + (size_t)g * kD);
     vb = (const char*)(a.v_chunks[c] + (size_t)g * kD);
   } else {
-    kb = (const char*)(a.k_gathered + ((size_t)c * p.cp.m) * row_elems + (size_t)g * kD);
-    vb = (const char*)(a.v_gathered + ((size_t)c * p.cp.m) * row_elems + (size_t)g * kD);
+    kb = (const char*)(a.k_gathered + (size_t)c * m * p.Hkv * kD + (size_t)g * kD);
+    vb = (const char*)(a.v_gathered + (size_t)c * m * p.Hkv * kD + (size_t)g * kD);
   }
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vb, (uint32_t)(m - 1) * row_bytes + kRowBytes);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 #pragma unroll
   for (int ii = 0; ii < kLoads; ++ii) {
-    const int key = min(key0 + bl.row[ii], p.cp.m - 1);
-    const size_t rb = (size_t)key * row_elems * 2;
-    const int i = wave + 4 * ii;
-    dma_global(slot + i * 1024, kb + rb + bl.koff[ii]);
-    dma_global(slot + kPart + i * 1024, vb + rb + bl.voff[ii]);
+    const int i = wave + kWaves * ii;
+    const int key = key0 + bl.row[ii];
+    dma_global(slot + i * 1024, kb + (size_t)min(key, m - 1) * row_bytes + bl.koff[ii]);
+    dma_buffer(slot + kPart + i * 1024, vrs, (uint32_t)key * row_bytes + bl.voff[ii]);
   }
 }
 
@@ -150,80 +159,101 @@ __device__ __forceinline__ int wait_chunk(const AttnArgs& a, int c, uint32_t epo
   return w.finish(a.cm, seen);
 }
 
-// S^T, online softmax and O^T update of one key block held in LDS at `st`;
-// `valid` keys of the block are real (the rest are masked out).
-__device__ __forceinline__ void attend_block(TileState& ts, OCG_LDS const char* st, const uint32_t (&kfa)[kDSteps],
-                                             uint32_t vfa, int vx, int valid, float scale) {
-  const int lane = threadIdx.x & 63;
-  const int qg = lane >> 4;
-  f32x4_t s[kKTiles][kQTiles];
+// A half step covers 32 keys (key tiles 2h, 2h+1 of a block, one MFMA k
+// step of the value product). Scores of a half: s[tile][qt] = K_tile Q_qt^T.
+constexpr int kHalfTiles = 2;
+
+__device__ __forceinline__ void read_key_frags(OCG_LDS const char* st, const uint32_t (&kfa)[kDSteps], int t,
+                                               bf16x8_t (&kf)[kDSteps]) {
 #pragma unroll
-  for (int t = 0; t < kKTiles; ++t) {
-    bf16x8_t kf[kDSteps];
-#pragma unroll
-    for (int u = 0; u < kDSteps; ++u) kf[u] = *(OCG_LDS const bf16x8_t*)(st + t * 16 * kRowBytes + kfa[u]);
-#pragma unroll
-    for (int qt = 0; qt < kQTiles; ++qt) {
-      s[t][qt] = f32x4_t{};
-#pragma unroll
-      for (int u = 0; u < kDSteps; ++u)
-        s[t][qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[u], ts.qf[qt][u], s[t][qt], 0, 0, 0);
-    }
-  }
-  if (valid < kKB) {
-#pragma unroll
-    for (int t = 0; t < kKTiles; ++t)
-#pragma unroll
-      for (int qt = 0; qt < kQTiles; ++qt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (16 * t + 4 * qg + i >= valid) s[t][qt][i] = -INFINITY;
-  }
-  bf16x8_t pf[kQTiles][2];
+  for (int u = 0; u < kDSteps; ++u) kf[u] = *(OCG_LDS const bf16x8_t*)(st + t * 16 * kRowBytes + kfa[u]);
+}
+
+__device__ __forceinline__ void tile_scores(const TileState& ts, const bf16x8_t (&kf)[kDSteps],
+                                            f32x4_t (&sn)[kQTiles]) {
+  const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int qt = 0; qt < kQTiles; ++qt) {
-    float mx = s[0][qt][0];
+    sn[qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[0], ts.qf[qt][0], zero, 0, 0, 0);
 #pragma unroll
-    for (int t = 0; t < kKTiles; ++t)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[t][qt][i]);
-    mx = swap_max32(swap_max16(mx));
-    const float mnew = fmaxf(ts.mrun[qt], mx * scale);
-    const float alpha = __builtin_amdgcn_exp2f(ts.mrun[qt] - mnew);
-    ts.mrun[qt] = mnew;
-    float p[kKTiles][4];
-    float sum = 0.f;
-#pragma unroll
-    for (int t = 0; t < kKTiles; ++t)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        p[t][i] = __builtin_amdgcn_exp2f(fmaf(s[t][qt][i], scale, -mnew));
-        sum += p[t][i];
-      }
-    ts.lrun[qt] = fmaf(ts.lrun[qt], alpha, sum);
-#pragma unroll
-    for (int dt = 0; dt < kDTiles; ++dt) ts.o[dt][qt] *= alpha;
-#pragma unroll
-    for (int sp = 0; sp < 2; ++sp)
-      pf[qt][sp] = bf16x8_t{(__bf16)p[2 * sp][0], (__bf16)p[2 * sp][1], (__bf16)p[2 * sp][2], (__bf16)p[2 * sp][3],
-                            (__bf16)p[2 * sp + 1][0], (__bf16)p[2 * sp + 1][1], (__bf16)p[2 * sp + 1][2],
-                            (__bf16)p[2 * sp + 1][3]};
+    for (int u = 1; u < kDSteps; ++u) sn[qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[u], ts.qf[qt][u], sn[qt], 0, 0, 0);
   }
-  OCG_LDS const char* sv = st + kPart;
+}
+
+// Exponentials of query block qt of a half's scores against the reference,
+// as the bf16 MFMA B operand of the half's 32 keys.
+__device__ __forceinline__ bf16x8_t half_probs(const TileState& ts, const f32x4_t (&s)[kHalfTiles][kQTiles], int qt,
+                                               float scale) {
+  const float mref = ts.mrun[qt];
+  float p[kHalfTiles][4];
 #pragma unroll
-  for (int dt = 0; dt < kDTiles; ++dt) {
+  for (int t = 0; t < kHalfTiles; ++t)
 #pragma unroll
-    for (int sp = 0; sp < 2; ++sp) {
-      OCG_LDS const char* pa = sv + vfa + sp * 32 * kRowBytes + ((dt ^ vx) << 5);
-      bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((OCG_LDS bf16x4_t*)pa);
-      bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((OCG_LDS bf16x4_t*)(pa + 16 * kRowBytes));
-      const bf16x8_t vf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    for (int i = 0; i < 4; ++i) p[t][i] = __builtin_amdgcn_exp2f(fmaf(s[t][qt][i], scale, -mref));
+  return bf16x8_t{(__bf16)p[0][0], (__bf16)p[0][1], (__bf16)p[0][2], (__bf16)p[0][3],
+                  (__bf16)p[1][0], (__bf16)p[1][1], (__bf16)p[1][2], (__bf16)p[1][3]};
+}
+
+// Scaled row maxima of a half (log2 units), one per query block.
+__device__ __forceinline__ void half_max(const f32x4_t (&s)[kHalfTiles][kQTiles], float scale, float (&mx)[kQTiles]) {
 #pragma unroll
-      for (int qt = 0; qt < kQTiles; ++qt)
-        ts.o[dt][qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[qt][sp], ts.o[dt][qt], 0, 0, 0);
+  for (int qt = 0; qt < kQTiles; ++qt) {
+    const float v = fmaxf(fmaxf(fmaxf(s[0][qt][0], s[0][qt][1]), fmaxf(s[0][qt][2], s[0][qt][3])),
+                          fmaxf(fmaxf(s[1][qt][0], s[1][qt][1]), fmaxf(s[1][qt][2], s[1][qt][3])));
+    mx[qt] = swap_max32(swap_max16(v)) * scale;
+  }
+}
+
+// Online softmax with a lazily moved reference: the exponentials are taken
+// against mrun, which moves (rescaling the output accumulators and the row
+// sums) only when a half's maximum exceeds it by more than kLazy (log2
+// units), so every p <= 2^kLazy; the offset cancels in the final division.
+__device__ __forceinline__ void lazy_rescale(TileState& ts, const float (&mx)[kQTiles]) {
+  bool up = false;
+#pragma unroll
+  for (int qt = 0; qt < kQTiles; ++qt) up |= mx[qt] > ts.mrun[qt] + kLazy;
+  if (__builtin_amdgcn_ballot_w64(up)) {
+#pragma unroll
+    for (int qt = 0; qt < kQTiles; ++qt) {
+      const float mnew = mx[qt] > ts.mrun[qt] + kLazy ? mx[qt] : ts.mrun[qt];
+      const float alpha = __builtin_amdgcn_exp2f(ts.mrun[qt] - mnew);
+      ts.mrun[qt] = mnew;
+      ts.l[qt] *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < kDTiles; ++dt) ts.o[dt][qt] *= alpha;
     }
   }
 }
+
+// Value fragment of output column block dt, 32-key step sp.
+__device__ __forceinline__ bf16x8_t read_val_frag(OCG_LDS const char* sv, uint32_t vfa, int vx, int dt, int sp) {
+  OCG_LDS const char* pa = sv + vfa + sp * 32 * kRowBytes + ((dt ^ vx) << 5);
+  bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((OCG_LDS bf16x4_t*)pa);
+  bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((OCG_LDS bf16x4_t*)(pa + 16 * kRowBytes));
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// The lane's 8 key slots of a 32-key step as the MFMA A operand of the row
+// sums: 1 for keys below `valid` (counted from the step's first key), else 0.
+// Slot s of lane (q, j) is key 4q + s (s < 4) or 16 + 4q + s - 4.
+__device__ __forceinline__ bf16x8_t key_validity(int valid) {
+  const int qg = (threadIdx.x & 63) >> 4;
+  bf16x8_t v;
+#pragma unroll
+  for (int s = 0; s < 8; ++s) v[s] = (__bf16)((s < 4 ? 4 * qg + s : 16 + 4 * qg + s - 4) < valid ? 1.0f : 0.0f);
+  return v;
+}
+
+// Instruction classes of sched_group_barrier masks.
+constexpr int kSchedValu = 0x002, kSchedMfma = 0x008;
+
+struct StepCtx {
+  OCG_LDS char* smem;
+  uint32_t kfa[kDSteps];
+  uint32_t vfa;
+  int vx;
+  float scale;
+};
 
 // One attention tile v: kv head g, query rows [256 rb, 256 rb + 256).
 __device__ void attention_tile(const AttnArgs& a, OCG_LDS char* smem, int v, uint32_t epoch, uint32_t queue) {
@@ -242,7 +272,7 @@ __device__ void attention_tile(const AttnArgs& a, OCG_LDS char* smem, int v, uin
   bool qok[kQTiles];
 #pragma unroll
   for (int qt = 0; qt < kQTiles; ++qt) {
-    const int r = rb * kAttnRows + wave * 64 + qt * 16 + qj;
+    const int r = rb * kAttnRows + wave * kRowsW + qt * 16 + qj;
     qok[qt] = r < nrows;
     const int rc = min(r, nrows - 1);
     const int i = rc / p.G, h = g * p.G + (rc - (rc / p.G) * p.G);
@@ -250,7 +280,7 @@ __device__ void attention_tile(const AttnArgs& a, OCG_LDS char* smem, int v, uin
 #pragma unroll
     for (int u = 0; u < kDSteps; ++u) ts.qf[qt][u] = *(const bf16x8_t*)(a.q + qoff[qt] + 32 * u + 8 * qg);
     ts.mrun[qt] = -INFINITY;
-    ts.lrun[qt] = 0.f;
+    ts.l[qt] = f32x4_t{};
 #pragma unroll
     for (int dt = 0; dt < kDTiles; ++dt) ts.o[dt][qt] = f32x4_t{};
   }
@@ -262,7 +292,7 @@ __device__ void attention_tile(const AttnArgs& a, OCG_LDS char* smem, int v, uin
   BlockLoads bl;
 #pragma unroll
   for (int ii = 0; ii < kLoads; ++ii) {
-    const int r = 4 * (wave + 4 * ii) + (lane >> 4);
+    const int r = 4 * (wave + kWaves * ii) + (lane >> 4);
     bl.row[ii] = r;
     bl.koff[ii] = (uint32_t)key_src_chunk(lane & 15, r) * 16u;
     bl.voff[ii] = (uint32_t)val_src_chunk(lane & 15, r) * 16u;
@@ -283,7 +313,7 @@ __device__ void attention_tile(const AttnArgs& a, OCG_LDS char* smem, int v, uin
   uint64_t t_ready = t0;
   // Block j's loads, preceded by the wait on its chunk's flags when it is
   // the first block of a peer chunk. Past the end the last block is loaded
-  // again into the free slot (never read), so every step issues kNdma loads.
+  // again into the free slot (never used), so every step issues kNdma loads.
   auto issue = [&](int j) {
     const uint32_t slot = base + (uint32_t)(j % kSlots) * kStage;
     const int jj = j < nblk ? j : nblk - 1;
@@ -296,14 +326,98 @@ __device__ void attention_tile(const AttnArgs& a, OCG_LDS char* smem, int v, uin
     }
     issue_block(a, bl, g, jj, slot);
   };
+  auto valid_keys = [&](int j) { return min(kKB, cp.m - (j % p.nbc) * kKB); };
+  StepCtx c;
+  c.smem = smem;
+#pragma unroll
+  for (int u = 0; u < kDSteps; ++u) c.kfa[u] = kfa[u];
+  c.vfa = vfa;
+  c.vx = vx;
+  c.scale = a.scale_log2;
+  bf16x8_t all_valid;
+#pragma unroll
+  for (int s8 = 0; s8 < 8; ++s8) all_valid[s8] = (__bf16)1.0f;
 #pragma unroll
   for (int j = 0; j < kSlots - 1; ++j) issue(j);
+  // One block per step. The scores of the second 32-key half are computed
+  // under the maxima of the first; the value product of the first half runs
+  // under the exponentials of the second (the scheduling groups interleave
+  // them: an MFMA only overlaps VALU work of its own wave that follows it in
+  // program order).
   for (int k = 0; k < nblk; ++k) {
     vm_wait<(kSlots - 2) * kNdma>();   // block k has landed (this wave's loads)
     lds_barrier();                     // ... everyone's; slot (k-1) % kSlots is free
     issue(k + kSlots - 1);
-    const int valid = min(kKB, cp.m - (k % p.nbc) * kKB);
-    attend_block(ts, smem + (k % kSlots) * kStage, kfa, vfa, vx, valid, a.scale_log2);
+    OCG_LDS const char* st = smem + (k % kSlots) * kStage;
+    OCG_LDS const char* sv = st + kPart;
+    f32x4_t sh[2][kHalfTiles][kQTiles];
+    float m0[kQTiles], m1[kQTiles];
+    bf16x8_t vf[kDTiles];
+#pragma unroll
+    for (int t = 0; t < kHalfTiles; ++t) {
+      bf16x8_t kf[kDSteps];
+      read_key_frags(st, kfa, t, kf);
+      tile_scores(ts, kf, sh[0][t]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // second half's scores || first half's maxima; the first half's value
+    // fragments are read meanwhile
+#pragma unroll
+    for (int t = 0; t < kHalfTiles; ++t) {
+      bf16x8_t kf[kDSteps];
+      read_key_frags(st, kfa, 2 + t, kf);
+      tile_scores(ts, kf, sh[1][t]);
+    }
+#pragma unroll
+    for (int dt = 0; dt < kDTiles; ++dt) vf[dt] = read_val_frag(sv, vfa, vx, dt, 0);
+    half_max(sh[0], c.scale, m0);
+#pragma unroll
+    for (int i = 0; i < kHalfTiles * kQTiles * kDSteps; ++i) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedValu, 1, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    half_max(sh[1], c.scale, m1);
+#pragma unroll
+    for (int qt = 0; qt < kQTiles; ++qt) m0[qt] = fmaxf(m0[qt], m1[qt]);
+    lazy_rescale(ts, m0);
+    const int vk = valid_keys(k);
+    bf16x8_t vv0 = all_valid, vv1 = all_valid;
+    if (vk < kKB) {
+      vv0 = key_validity(vk);
+      vv1 = key_validity(vk - 32);
+    }
+    bf16x8_t pf0[kQTiles], pf1[kQTiles];
+#pragma unroll
+    for (int qt = 0; qt < kQTiles; ++qt) pf0[qt] = half_probs(ts, sh[0], qt, c.scale);
+    __builtin_amdgcn_sched_barrier(0);
+    // first half's value product || second half's exponentials
+#pragma unroll
+    for (int dt = 0; dt < kDTiles; ++dt)
+#pragma unroll
+      for (int qt = 0; qt < kQTiles; ++qt)
+        ts.o[dt][qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[dt], pf0[qt], ts.o[dt][qt], 0, 0, 0);
+#pragma unroll
+    for (int qt = 0; qt < kQTiles; ++qt) {
+      ts.l[qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vv0, pf0[qt], ts.l[qt], 0, 0, 0);
+      pf1[qt] = half_probs(ts, sh[1], qt, c.scale);
+    }
+#pragma unroll
+    for (int i = 0; i < kDTiles * kQTiles + kQTiles; ++i) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedValu, 2, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int dt = 0; dt < kDTiles; ++dt) vf[dt] = read_val_frag(sv, vfa, vx, dt, 1);
+#pragma unroll
+    for (int dt = 0; dt < kDTiles; ++dt)
+#pragma unroll
+      for (int qt = 0; qt < kQTiles; ++qt)
+        ts.o[dt][qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[dt], pf1[qt], ts.o[dt][qt], 0, 0, 0);
+#pragma unroll
+    for (int qt = 0; qt < kQTiles; ++qt)
+      ts.l[qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vv1, pf1[qt], ts.l[qt], 0, 0, 0);
   }
   vm_wait<0>();
   lds_barrier();
@@ -311,8 +425,7 @@ __device__ void attention_tile(const AttnArgs& a, OCG_LDS char* smem, int v, uin
   // epilogue: O / l, rounded to bf16, 8-byte stores
 #pragma unroll
   for (int qt = 0; qt < kQTiles; ++qt) {
-    const float l = swap_sum32(swap_sum16(ts.lrun[qt]));
-    const float inv = 1.0f / l;
+    const float inv = 1.0f / ts.l[qt][0];
     if (!qok[qt]) continue;
     uint16_t* orow = a.out + qoff[qt] + 4 * qg;
 #pragma unroll
@@ -328,7 +441,7 @@ __device__ void attention_tile(const AttnArgs& a, OCG_LDS char* smem, int v, uin
 
 }  // namespace
 
-__global__ __launch_bounds__(kThreads, 1) void ag_attention_kernel(AttnArgs args) {
+__global__ __launch_bounds__(kAThreads, 1) void ag_attention_kernel(AttnArgs args) {
   __shared__ __attribute__((aligned(1024))) char smem_raw[kSlots * kStage];
   __shared__ uint32_t s_bcast[8];
   OCG_LDS char* smem = (OCG_LDS char*)smem_raw;
@@ -351,13 +464,13 @@ __global__ __launch_bounds__(kThreads, 1) void ag_attention_kernel(AttnArgs args
 }
 
 hipError_t launch_ag_attention(const AttnArgs& a, int grid, hipStream_t s) {
-  hipLaunchKernelGGL(ag_attention_kernel, dim3(grid), dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL(ag_attention_kernel, dim3(grid), dim3(kAThreads), 0, s, a);
   return hipGetLastError();
 }
 
 int resident_attention() {
   int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, ag_attention_kernel, kThreads, 0) != hipSuccess) return 1;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, ag_attention_kernel, kAThreads, 0) != hipSuccess) return 1;
   return n > 0 ? n : 1;
 }
 

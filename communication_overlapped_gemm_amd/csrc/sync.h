@@ -113,20 +113,22 @@ __device__ __forceinline__ bool publish_slab(uint32_t* cnt, uint32_t* flag, int 
 // ---------------------------------------------------------------- copy
 
 // Pull `n16` 16-byte granules from src to dst (agent-coherent stores) with
-// all 256 threads, 16 granules in flight per thread. n16 * 16 < 2^31.
+// all NT threads of the workgroup, 16 granules in flight per thread.
+// n16 * 16 < 2^31.
+template <int NT = kThreads>
 __device__ __forceinline__ void copy_granules(const uint16_t* src, uint16_t* dst, uint32_t n16) {
   constexpr int U = 16;
   const u32x4_t* s = (const u32x4_t*)src;
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(dst, n16 * 16u);
   uint32_t i = threadIdx.x;
-  for (; i + (uint32_t)(U - 1) * kThreads < n16; i += (uint32_t)U * kThreads) {
+  for (; i + (uint32_t)(U - 1) * NT < n16; i += (uint32_t)U * NT) {
     u32x4_t v[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) v[u] = gload16(s + i + u * kThreads);
+    for (int u = 0; u < U; ++u) v[u] = gload16(s + i + u * NT);
 #pragma unroll
-    for (int u = 0; u < U; ++u) store16_agent(rs, (i + u * kThreads) * 16u, v[u]);
+    for (int u = 0; u < U; ++u) store16_agent(rs, (i + u * NT) * 16u, v[u]);
   }
-  for (; i < n16; i += kThreads) store16_agent(rs, i * 16u, gload16(s + i));
+  for (; i < n16; i += NT) store16_agent(rs, i * 16u, gload16(s + i));
 }
 
 // One copy task of the AllGather (pull mode): rows [row0, row1) of the
