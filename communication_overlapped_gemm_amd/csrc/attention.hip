@@ -109,9 +109,17 @@ __device__ void run_kv_copy(const AttnArgs& a, int u, uint32_t epoch) {
 // lane L takes row 4*i + L/16, LDS chunk position L & 15, whose source chunk
 // is given by the swizzles above.
 struct BlockLoads {
-  uint32_t koff[kLoads], voff[kLoads];   // byte offset of the lane's chunk within its head row
+  uint32_t kofs[kLoads], vofs[kLoads];   // byte offset of the lane's source chunk from the block's first row
+  uint32_t koff[kLoads], voff[kLoads];   // ... within its head row
   int row[kLoads];                       // row within the block
 };
+
+// Direct-to-LDS 16-byte load of buffer bytes soff + voff (the lane's
+// offset; out-of-range voff reads zeros, soff is not range-checked).
+__device__ __forceinline__ void dma_buffer_so(uint32_t lds, __amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds" ::"s"(lds), "v"(voff), "s"(r), "s"(soff)
+               : "memory", "m0");
+}
 
 struct TileState {
   bf16x8_t qf[kQTiles][kDSteps];   // query fragments: row (lane & 15) of block qt, d = 32u + 8(lane >> 4) ..
@@ -131,23 +139,36 @@ __device__ __forceinline__ void issue_block(const AttnArgs& a, const BlockLoads&
   const int m = p.cp.m;
   const int key0 = (j % p.nbc) * kKB;
   const uint32_t row_bytes = (uint32_t)p.Hkv * kRowBytes;
-  const char* kb;
-  const char* vb;
+  const uint16_t* kb;
+  const uint16_t* vb;
   if (c == p.cp.local) {
-    kb = (const char*)(a.k_chunks[c] + (size_t)g * kD);
-    vb = (const char*)(a.v_chunks[c] + (size_t)g * kD);
+    kb = a.k_chunks[c] + (size_t)g * kD;
+    vb = a.v_chunks[c] + (size_t)g * kD;
   } else {
-    kb = (const char*)(a.k_gathered + (size_t)c * m * p.Hkv * kD + (size_t)g * kD);
-    vb = (const char*)(a.v_gathered + (size_t)c * m * p.Hkv * kD + (size_t)g * kD);
+    kb = a.k_gathered + (size_t)c * m * p.Hkv * kD + (size_t)g * kD;
+    vb = a.v_gathered + (size_t)c * m * p.Hkv * kD + (size_t)g * kD;
   }
-  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vb, (uint32_t)(m - 1) * row_bytes + kRowBytes);
+  const uint32_t bound = (uint32_t)(m - 1) * row_bytes + kRowBytes;   // the chunk's rows of head g
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(kb, bound);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vb, bound);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (key0 + kKB <= m) {
+    // every row inside the chunk: the block's first row as the scalar offset
+    const uint32_t so = (uint32_t)key0 * row_bytes;
 #pragma unroll
-  for (int ii = 0; ii < kLoads; ++ii) {
-    const int i = wave + kWaves * ii;
-    const int key = key0 + bl.row[ii];
-    dma_global(slot + i * 1024, kb + (size_t)min(key, m - 1) * row_bytes + bl.koff[ii]);
-    dma_buffer(slot + kPart + i * 1024, vrs, (uint32_t)key * row_bytes + bl.voff[ii]);
+    for (int ii = 0; ii < kLoads; ++ii) {
+      const int i = wave + kWaves * ii;
+      dma_buffer_so(slot + i * 1024, krs, bl.kofs[ii], so);
+      dma_buffer_so(slot + kPart + i * 1024, vrs, bl.vofs[ii], so);
+    }
+  } else {
+#pragma unroll
+    for (int ii = 0; ii < kLoads; ++ii) {
+      const int i = wave + kWaves * ii;
+      const int key = key0 + bl.row[ii];
+      dma_buffer_so(slot + i * 1024, krs, (uint32_t)min(key, m - 1) * row_bytes + bl.koff[ii], 0u);
+      dma_buffer_so(slot + kPart + i * 1024, vrs, (uint32_t)key * row_bytes + bl.voff[ii], 0u);
+    }
   }
 }
 
@@ -194,15 +215,16 @@ __device__ __forceinline__ bf16x8_t half_probs(const TileState& ts, const f32x4_
                   (__bf16)p[1][0], (__bf16)p[1][1], (__bf16)p[1][2], (__bf16)p[1][3]};
 }
 
-// Scaled row maxima of a half (log2 units), one per query block.
-__device__ __forceinline__ void half_max(const f32x4_t (&s)[kHalfTiles][kQTiles], float scale, float (&mx)[kQTiles]) {
+// In-lane maxima of a half's scores, one per query block (the lane's 8 keys).
+__device__ __forceinline__ void half_lane_max(const f32x4_t (&s)[kHalfTiles][kQTiles], float (&mx)[kQTiles]) {
 #pragma unroll
-  for (int qt = 0; qt < kQTiles; ++qt) {
-    const float v = fmaxf(fmaxf(fmaxf(s[0][qt][0], s[0][qt][1]), fmaxf(s[0][qt][2], s[0][qt][3])),
-                          fmaxf(fmaxf(s[1][qt][0], s[1][qt][1]), fmaxf(s[1][qt][2], s[1][qt][3])));
-    mx[qt] = swap_max32(swap_max16(v)) * scale;
-  }
+  for (int qt = 0; qt < kQTiles; ++qt)
+    mx[qt] = fmaxf(fmaxf(fmaxf(s[0][qt][0], s[0][qt][1]), fmaxf(s[0][qt][2], s[0][qt][3])),
+                   fmaxf(fmaxf(s[1][qt][0], s[1][qt][1]), fmaxf(s[1][qt][2], s[1][qt][3])));
 }
+
+// Row maximum over the 4 lanes sharing a query, scaled to log2 units.
+__device__ __forceinline__ float row_max(float v, float scale) { return swap_max32(swap_max16(v)) * scale; }
 
 // Online softmax with a lazily moved reference: the exponentials are taken
 // against mrun, which moves (rescaling the output accumulators and the row
@@ -296,6 +318,8 @@ __device__ void attention_tile(const AttnArgs& a, OCG_LDS char* smem, int v, uin
     bl.row[ii] = r;
     bl.koff[ii] = (uint32_t)key_src_chunk(lane & 15, r) * 16u;
     bl.voff[ii] = (uint32_t)val_src_chunk(lane & 15, r) * 16u;
+    bl.kofs[ii] = (uint32_t)r * (uint32_t)p.Hkv * kRowBytes + bl.koff[ii];
+    bl.vofs[ii] = (uint32_t)r * (uint32_t)p.Hkv * kRowBytes + bl.voff[ii];
   }
   // fragment read offsets within a slot
   uint32_t kfa[kDSteps];
@@ -370,16 +394,16 @@ __device__ void attention_tile(const AttnArgs& a, OCG_LDS char* smem, int v, uin
     }
 #pragma unroll
     for (int dt = 0; dt < kDTiles; ++dt) vf[dt] = read_val_frag(sv, vfa, vx, dt, 0);
-    half_max(sh[0], c.scale, m0);
+    half_lane_max(sh[0], m0);
 #pragma unroll
     for (int i = 0; i < kHalfTiles * kQTiles * kDSteps; ++i) {
       __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
       __builtin_amdgcn_sched_group_barrier(kSchedValu, 1, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
-    half_max(sh[1], c.scale, m1);
+    half_lane_max(sh[1], m1);
 #pragma unroll
-    for (int qt = 0; qt < kQTiles; ++qt) m0[qt] = fmaxf(m0[qt], m1[qt]);
+    for (int qt = 0; qt < kQTiles; ++qt) m0[qt] = row_max(fmaxf(m0[qt], m1[qt]), c.scale);
     lazy_rescale(ts, m0);
     const int vk = valid_keys(k);
     bf16x8_t vv0 = all_valid, vv1 = all_valid;
