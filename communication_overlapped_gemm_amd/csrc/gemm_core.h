@@ -1,7 +1,8 @@
-// bf16 MFMA tile engine for gfx950 (one workgroup = 4 waves, one tile).
+// bf16 MFMA tile engine for gfx950 (one workgroup = 4 or 8 waves, one tile).
 //
-// Tile BM x BN, K consumed in stages of 32. The four waves form a 2 x 2 grid:
-// wave w = 2*wm + wn owns rows [wm*BM/2, +BM/2) and columns [wn*BN/2, +BN/2),
+// Tile BM x BN, K consumed in stages of 32. The NW waves (4 or 8, see
+// gemm_waves) form an NW/2 x 2 grid: wave w = 2*wm + wn owns rows
+// [wm*WM, +WM) (WM = 2*BM/NW) and columns [wn*BN/2, +BN/2),
 // computed with v_mfma_f32_16x16x32_bf16 (one 16x16 accumulator per (16-row,
 // 16-col) block; one MFMA covers the whole 32-deep stage). Compared with four
 // waves stacked along M, every wave reads half of B instead of all of it, which
@@ -46,9 +47,20 @@ typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int BKS = 32;   // K per stage
 
+// Waves per workgroup of a tile: 8 for the 320-row grouped-GEMM tile (a 4 x 2
+// wave grid, two waves per SIMD: 140 accumulators per wave instead of 280,
+// which the 256-entry accumulator file cannot hold), else 4 (2 x 2; measured
+// no faster with 8 for the other tiles).
+template <int BM, int BN>
+constexpr int gemm_waves() {
+  return BM == 320 ? 8 : 4;
+}
+
 template <int BM, int BN>
 struct Gemm {
-  static constexpr int WM = BM / 2, WN = BN / 2;    // rows / columns per wave
+  static constexpr int NW = gemm_waves<BM, BN>();   // waves per workgroup
+  static constexpr int NT = 64 * NW;                // threads per workgroup
+  static constexpr int WM = BM / (NW / 2), WN = BN / 2;   // rows / columns per wave
   static constexpr int FM = WM / 16, FN = WN / 16;  // 16x16 blocks per wave
   static constexpr int A_BYTES = BM * BKS * 2;
   static constexpr int B_BYTES = BN * BKS * 2;
@@ -59,8 +71,8 @@ struct Gemm {
   static constexpr int S = (BM == 128 && BN == 128) ? 4 : ((150 * 1024 / STAGE) < 6 ? 150 * 1024 / STAGE : 6);
   static constexpr int A_INST = A_BYTES / 1024;     // 1 KiB DMA instructions per stage
   static constexpr int B_INST = B_BYTES / 1024;
-  static constexpr int A_PER_WAVE = (A_INST + 3) / 4;  // A instruction of wave w: see a_block
-  static constexpr int B_PER_WAVE = (B_INST + 3) / 4;  // B instruction j = wave + 4*i
+  static constexpr int A_PER_WAVE = (A_INST + NW - 1) / NW;  // A instruction of wave w: see a_block
+  static constexpr int B_PER_WAVE = (B_INST + NW - 1) / NW;  // B instruction j = wave + NW*i
   static constexpr int NDMA = A_PER_WAVE + B_PER_WAVE;  // loads per wave per stage
   static constexpr int RING = S * STAGE;
   // Tiles with more accumulators than the 256-entry accumulator file keep
@@ -68,11 +80,11 @@ struct Gemm {
   // into b[g] right after MFMA group g used it): it lowers the register
   // pressure of the 320x224 tile (280 accumulators per lane) and measured
   // faster there, slower for tiles that fit.
-  static constexpr bool SINGLE_B = FM * FN * 4 > 256;
+  static constexpr bool SINGLE_B = FM * FN * 4 > 256 / (NW / 4);
   static constexpr int LD_C = BN + 8;               // epilogue staging row (elements)
   static constexpr int LDS_BYTES = (RING > BM * LD_C * 2) ? RING : BM * LD_C * 2;
   static_assert(WM % 16 == 0 && WN % 16 == 0 && BN % 32 == 0, "whole 16x16 blocks per wave, 32-column B blocks");
-  static_assert(A_INST >= 4, "every wave has A loads");
+  static_assert(A_INST >= NW, "every wave has A loads");
   static_assert(NDMA <= 2 * FN, "at most two loads behind each MFMA group");
   static_assert(S >= 4 && (S - 2) * NDMA <= 63, "vmcnt waits fit the 6-bit counter");
   static_assert(LDS_BYTES <= 160 * 1024 - 64, "fits the 160 KiB LDS of a gfx950 CU");
@@ -121,16 +133,16 @@ struct TileCtx {
 
 // 1 KiB block of the slot's A part (rows 16b..16b+15) that A instruction i
 // of wave `wave` loads: consecutive blocks per wave when they split evenly,
-// else block wave + 4i, a wave past the last block repeating its previous
+// else block wave + NW*i, a wave past the last block repeating its previous
 // one (same source, same LDS bytes), so every wave issues A_PER_WAVE loads.
 template <int BM, int BN>
 __device__ __forceinline__ int a_block(int wave, int i) {
   using G = Gemm<BM, BN>;
-  if constexpr (G::A_INST % 4 == 0) {
+  if constexpr (G::A_INST % G::NW == 0) {
     return wave * G::A_PER_WAVE + i;
   } else {
-    const int j = wave + 4 * i;
-    return j < G::A_INST ? j : j - 4;
+    const int j = wave + G::NW * i;
+    return j < G::A_INST ? j : j - G::NW;
   }
 }
 
@@ -142,7 +154,7 @@ __device__ __forceinline__ int dma_row(int wave, int i, int lane) {
 
 // Per-tile constants of this wave's loads: the A instruction i loads rows
 // 16*b + lane/4 (b = a_block(wave, i)), chunk (lane & 3) ^ swz_a(row), into
-// the slot's 1 KiB block b; B instruction i (j = wave + 4i)
+// the slot's 1 KiB block b; B instruction i (j = wave + NW*i)
 // loads k row (j & 1)*16 + lane/4 of column block j/2, chunk pair
 // (lane & 3) ^ 2*swz_b(k), into block j of the slot's B part. A wave whose
 // last j is past the B blocks repeats its previous B load (same source, same
@@ -167,8 +179,8 @@ __device__ __forceinline__ DmaPlan<BM, BN> make_dma_plan(const TileCtx<BM, BN>& 
   }
 #pragma unroll
   for (int i = 0; i < G::B_PER_WAVE; ++i) {
-    int j = wave + 4 * i;
-    if (j >= G::B_INST) j -= 4;
+    int j = wave + G::NW * i;
+    if (j >= G::B_INST) j -= G::NW;
     const int nb = j >> 1, k = (j & 1) * 16 + (lane >> 2);
     const int c = (lane & 3) ^ (2 * swz_b(k));
     // byte offset of B[k][n0 + 32*nb + 8*c]; K*N*2 < 2^32 (unsigned math)
@@ -402,7 +414,7 @@ __device__ __forceinline__ void for_each_c_chunk(OCG_LDS const char* smem, F f) 
   using G = Gemm<BM, BN>;
   constexpr int CPR = BN / 8;
   OCG_LDS const uint16_t* cst = (OCG_LDS const uint16_t*)smem;
-  for (int i = threadIdx.x; i < BM * CPR; i += 256) {
+  for (int i = threadIdx.x; i < BM * CPR; i += G::NT) {
     const int row = i / CPR, c8 = i - row * CPR;
     f(row, c8 * 8, *(OCG_LDS const u32x4_t*)(cst + row * G::LD_C + c8 * 8));
   }

@@ -26,7 +26,7 @@ namespace ocg {
 // ---------------------------------------------------------------- AG-GEMM
 
 template <int BM, int BN>
-__global__ __launch_bounds__(kThreads, 1) void ag_gemm_kernel(AgArgs args) {
+__global__ __launch_bounds__((Gemm<BM, BN>::NT), 1) void ag_gemm_kernel(AgArgs args) {
   using G = Gemm<BM, BN>;
   __shared__ __attribute__((aligned(1024))) char smem_raw[G::LDS_BYTES];
   __shared__ uint32_t s_bcast[8];
@@ -41,7 +41,7 @@ __global__ __launch_bounds__(kThreads, 1) void ag_gemm_kernel(AgArgs args) {
   for (;;) {
     const uint32_t u = next_ticket(&cm.hdr->ticket, s_bcast);
     if ((int)u >= p.n_copy) break;
-    run_copy_task(p, args.chunks, args.a_gathered, args.slab_cnt, args.slab_flag, (int)u, epoch, cm);
+    run_copy_task<G::NT>(p, args.chunks, args.a_gathered, args.slab_cnt, args.slab_flag, (int)u, epoch, cm);
   }
   // GEMM tiles
   int q = (int)s_bcast[3] % kXcds, tried = 0;
@@ -94,16 +94,17 @@ __global__ __launch_bounds__(kThreads, 1) void ag_gemm_kernel(AgArgs args) {
 // that order, of the bf16 partials P_s ), fp32 accumulation, one rounding.
 // Every 16-byte chunk issues the loads of all ranks before adding, U chunks
 // per round, so each thread keeps up to U * R loads in flight.
+template <int NT>
 __device__ void run_reduce_strip(const RsArgs& a, int r0, int r1) {
   constexpr int U = 2;
   const RsPlan& p = a.plan;
   const int lo = p.local * p.blk;
   const size_t first = (size_t)r0 * p.N / 8, n16 = (size_t)(r1 - r0) * p.N / 8;
-  for (size_t base = threadIdx.x; base < n16; base += (size_t)U * kThreads) {
+  for (size_t base = threadIdx.x; base < n16; base += (size_t)U * NT) {
     u32x4_t v[U][kMaxRanks];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const size_t i = base + (size_t)u * kThreads;
+      const size_t i = base + (size_t)u * NT;
       if (i >= n16) continue;
 #pragma unroll
       for (int s = 0; s < kMaxRanks; ++s) {
@@ -115,7 +116,7 @@ __device__ void run_reduce_strip(const RsArgs& a, int r0, int r1) {
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const size_t i = base + (size_t)u * kThreads;
+      const size_t i = base + (size_t)u * NT;
       if (i >= n16) continue;
       float acc[8];
 #pragma unroll
@@ -135,7 +136,7 @@ __device__ void run_reduce_strip(const RsArgs& a, int r0, int r1) {
 }
 
 template <int BM, int BN>
-__global__ __launch_bounds__(kThreads, 1) void gemm_rs_kernel(RsArgs args) {
+__global__ __launch_bounds__((Gemm<BM, BN>::NT), 1) void gemm_rs_kernel(RsArgs args) {
   using G = Gemm<BM, BN>;
   __shared__ __attribute__((aligned(1024))) char smem_raw[G::LDS_BYTES];
   __shared__ uint32_t s_bcast[8];
@@ -211,7 +212,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_rs_kernel(RsArgs args) {
     }
     const uint64_t t1 = now_ticks();
     __syncthreads();
-    run_reduce_strip(args, r0, r1);
+    run_reduce_strip<G::NT>(args, r0, r1);
     trace_task(cm, (uint32_t)(p.n_tiles + j), 5, r0, r1, nwait, 0, epoch, t0, t1, seen, 0);
   }
   finish(cm.hdr, epoch);
@@ -377,7 +378,7 @@ __global__ __launch_bounds__(kRouteBlock) void moe_scatter_kernel(RouteArgs a) {
 // ---------------------------------------------------------------- AG + grouped GEMM
 
 template <int BM, int BN>
-__global__ __launch_bounds__(kThreads, 1) void moe_gemm_kernel(MoeArgs args) {
+__global__ __launch_bounds__((Gemm<BM, BN>::NT), 1) void moe_gemm_kernel(MoeArgs args) {
   using G = Gemm<BM, BN>;
   __shared__ __attribute__((aligned(1024))) char smem_raw[G::LDS_BYTES];
   __shared__ uint32_t s_bcast[8];
@@ -395,7 +396,7 @@ __global__ __launch_bounds__(kThreads, 1) void moe_gemm_kernel(MoeArgs args) {
   for (;;) {
     const uint32_t u = next_ticket(&cm.hdr->ticket, s_bcast);
     if ((int)u >= p.n_copy) break;
-    run_copy_task(p, args.chunks, args.a_gathered, args.slab_cnt, args.slab_flag, (int)u, epoch, cm);
+    run_copy_task<G::NT>(p, args.chunks, args.a_gathered, args.slab_cnt, args.slab_flag, (int)u, epoch, cm);
   }
   int q = (int)s_bcast[3] % kXcds, tried = 0;
   uint32_t qt = 0;
@@ -567,13 +568,13 @@ __global__ void fill_u32_kernel(uint32_t* p, size_t n, uint32_t v, int release) 
 
 template <int BM, int BN>
 static hipError_t ag_launch(const AgArgs& a, int grid, hipStream_t s) {
-  hipLaunchKernelGGL((ag_gemm_kernel<BM, BN>), dim3(grid), dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL((ag_gemm_kernel<BM, BN>), dim3(grid), dim3(Gemm<BM, BN>::NT), 0, s, a);
   return hipGetLastError();
 }
 
 template <int BM, int BN>
 static hipError_t rs_launch(const RsArgs& a, int grid, hipStream_t s) {
-  hipLaunchKernelGGL((gemm_rs_kernel<BM, BN>), dim3(grid), dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL((gemm_rs_kernel<BM, BN>), dim3(grid), dim3(Gemm<BM, BN>::NT), 0, s, a);
   return hipGetLastError();
 }
 
@@ -608,10 +609,10 @@ hipError_t launch_moe(const RouteArgs& r, const MoeArgs& a, int tile, int grid, 
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   switch (tile) {
-    case OCG_TILE_128x224: hipLaunchKernelGGL((moe_gemm_kernel<128, 224>), dim3(grid), dim3(kThreads), 0, s, a); break;
-    case OCG_TILE_256x224: hipLaunchKernelGGL((moe_gemm_kernel<256, 224>), dim3(grid), dim3(kThreads), 0, s, a); break;
-    case OCG_TILE_288x224: hipLaunchKernelGGL((moe_gemm_kernel<288, 224>), dim3(grid), dim3(kThreads), 0, s, a); break;
-    case OCG_TILE_320x224: hipLaunchKernelGGL((moe_gemm_kernel<320, 224>), dim3(grid), dim3(kThreads), 0, s, a); break;
+    case OCG_TILE_128x224: hipLaunchKernelGGL((moe_gemm_kernel<128, 224>), dim3(grid), dim3(Gemm<128, 224>::NT), 0, s, a); break;
+    case OCG_TILE_256x224: hipLaunchKernelGGL((moe_gemm_kernel<256, 224>), dim3(grid), dim3(Gemm<256, 224>::NT), 0, s, a); break;
+    case OCG_TILE_288x224: hipLaunchKernelGGL((moe_gemm_kernel<288, 224>), dim3(grid), dim3(Gemm<288, 224>::NT), 0, s, a); break;
+    case OCG_TILE_320x224: hipLaunchKernelGGL((moe_gemm_kernel<320, 224>), dim3(grid), dim3(Gemm<320, 224>::NT), 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -638,37 +639,37 @@ hipError_t launch_fill_u32(uint32_t* p, size_t n, uint32_t v, int release, hipSt
 }
 
 template <class K>
-static int occ(K kern) {
+static int occ(K kern, int threads) {
   int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, kThreads, 0) != hipSuccess) return 1;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, threads, 0) != hipSuccess) return 1;
   return n > 0 ? n : 1;
 }
 
 int resident_per_cu(int op, int tile) {
   if (op == OCG_OP_AG_GROUPED_GEMM) {
     switch (tile) {
-      case OCG_TILE_128x224: return occ(moe_gemm_kernel<128, 224>);
-      case OCG_TILE_256x224: return occ(moe_gemm_kernel<256, 224>);
-      case OCG_TILE_288x224: return occ(moe_gemm_kernel<288, 224>);
-      case OCG_TILE_320x224: return occ(moe_gemm_kernel<320, 224>);
+      case OCG_TILE_128x224: return occ(moe_gemm_kernel<128, 224>, Gemm<128, 224>::NT);
+      case OCG_TILE_256x224: return occ(moe_gemm_kernel<256, 224>, Gemm<256, 224>::NT);
+      case OCG_TILE_288x224: return occ(moe_gemm_kernel<288, 224>, Gemm<288, 224>::NT);
+      case OCG_TILE_320x224: return occ(moe_gemm_kernel<320, 224>, Gemm<320, 224>::NT);
     }
     return 1;
   }
   if (op == OCG_OP_AG_GEMM) {
     switch (tile) {
-      case OCG_TILE_256x224: return occ(ag_gemm_kernel<256, 224>);
-      case OCG_TILE_128x224: return occ(ag_gemm_kernel<128, 224>);
-      case OCG_TILE_128x256: return occ(ag_gemm_kernel<128, 256>);
-      case OCG_TILE_128x128: return occ(ag_gemm_kernel<128, 128>);
-      case OCG_TILE_256x256: return occ(ag_gemm_kernel<256, 256>);
+      case OCG_TILE_256x224: return occ(ag_gemm_kernel<256, 224>, Gemm<256, 224>::NT);
+      case OCG_TILE_128x224: return occ(ag_gemm_kernel<128, 224>, Gemm<128, 224>::NT);
+      case OCG_TILE_128x256: return occ(ag_gemm_kernel<128, 256>, Gemm<128, 256>::NT);
+      case OCG_TILE_128x128: return occ(ag_gemm_kernel<128, 128>, Gemm<128, 128>::NT);
+      case OCG_TILE_256x256: return occ(ag_gemm_kernel<256, 256>, Gemm<256, 256>::NT);
     }
   } else {
     switch (tile) {
-      case OCG_TILE_256x224: return occ(gemm_rs_kernel<256, 224>);
-      case OCG_TILE_128x224: return occ(gemm_rs_kernel<128, 224>);
-      case OCG_TILE_128x256: return occ(gemm_rs_kernel<128, 256>);
-      case OCG_TILE_128x128: return occ(gemm_rs_kernel<128, 128>);
-      case OCG_TILE_256x256: return occ(gemm_rs_kernel<256, 256>);
+      case OCG_TILE_256x224: return occ(gemm_rs_kernel<256, 224>, Gemm<256, 224>::NT);
+      case OCG_TILE_128x224: return occ(gemm_rs_kernel<128, 224>, Gemm<128, 224>::NT);
+      case OCG_TILE_128x256: return occ(gemm_rs_kernel<128, 256>, Gemm<128, 256>::NT);
+      case OCG_TILE_128x128: return occ(gemm_rs_kernel<128, 128>, Gemm<128, 128>::NT);
+      case OCG_TILE_256x256: return occ(gemm_rs_kernel<256, 256>, Gemm<256, 256>::NT);
     }
   }
   return 1;

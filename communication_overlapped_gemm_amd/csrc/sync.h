@@ -133,6 +133,7 @@ __device__ __forceinline__ void copy_granules(const uint16_t* src, uint16_t* dst
 
 // One copy task of the AllGather (pull mode): rows [row0, row1) of the
 // gathered matrix come from rank `chunk`'s shard.
+template <int NT = kThreads>
 __device__ __forceinline__ void run_copy_task(const AgPlan& p, const uint16_t* const* chunks, uint16_t* a_gathered,
                               uint32_t* slab_cnt, uint32_t* slab_flag, int u, uint32_t epoch,
                               const Common& cm) {
@@ -140,7 +141,7 @@ __device__ __forceinline__ void run_copy_task(const AgPlan& p, const uint16_t* c
   CopyDesc d = copy_desc(p, u);
   const uint16_t* src = chunks[d.chunk] + (size_t)(d.row0 - d.chunk * p.m) * p.K;
   uint16_t* dst = a_gathered + (size_t)d.row0 * p.K;
-  copy_granules(src, dst, (uint32_t)((size_t)(d.row1 - d.row0) * p.K / 8));
+  copy_granules<NT>(src, dst, (uint32_t)((size_t)(d.row1 - d.row0) * p.K / 8));
   int target = slab_target(p.m, p.S, p.CT, p.bpr, d.slab);
   bool pub = publish_slab(slab_cnt, slab_flag, d.slab, target, epoch, cm);
   if (threadIdx.x == 0 && cm.trace && (uint32_t)u < cm.trace_cap) {
