@@ -370,8 +370,15 @@ def other_ops(torch, np, ocg, workloads, upload, stream, n):
     del launch
     # AllGather-KV attention (MFMA-bound): fused, attention only, copies only
     w, x, ws, launch = setups["ag_attention"]()
-    times = {label: median_ms(torch, lambda: launch(mode), n, stream)
-             for label, mode in (("fused", 0), ("attn", 1), ("copy", 2))}
+    # the modes alternate in three rounds (the clock drifts while the chip
+    # warms, and one block of launches per mode would fold that drift into
+    # the comparison); median over all of a mode's launches
+    samples = {"fused": [], "attn": [], "copy": []}
+    for _ in range(3):
+        for label, mode in (("fused", 0), ("attn", 1), ("copy", 2)):
+            launch(mode)
+            samples[label] += timed_launches(torch, lambda: launch(mode), max(n // 3, 5), stream)
+    times = {label: statistics.median(v) for label, v in samples.items()}
     ws.check()
     tf = w.flops() / (times["fused"] * 1e-3) / 1e12
     out["ag_attention"] = {"t_fused_us": round(times["fused"] * 1e3, 2), "t_attn_us": round(times["attn"] * 1e3, 2),
