@@ -72,8 +72,17 @@ struct Gemm {
   static constexpr int A_INST = A_BYTES / 1024;     // 1 KiB DMA instructions per stage
   static constexpr int B_INST = B_BYTES / 1024;
   static constexpr int A_PER_WAVE = (A_INST + NW - 1) / NW;  // A instruction of wave w: see a_block
-  static constexpr int B_PER_WAVE = (B_INST + NW - 1) / NW;  // B instruction j = wave + NW*i
-  static constexpr int NDMA = A_PER_WAVE + B_PER_WAVE;  // loads per wave per stage
+  // JOINT: the A blocks do not split evenly over the waves but A and B
+  // blocks together do (288x224: 18 + 14 = 32). The stage's loads are then
+  // numbered A blocks first, then B blocks, and load I of wave w is number
+  // w + NW*I: every wave issues the same count and none repeats a load.
+  // Otherwise A and B split separately and a wave past the last block of
+  // either repeats its previous load.
+  static constexpr bool JOINT = (A_INST % NW != 0) && ((A_INST + B_INST) % NW == 0);
+  static constexpr int A_MIN = JOINT ? A_INST / NW : A_PER_WAVE;  // loads I < A_MIN are A loads in every wave
+  static constexpr int NDMA = JOINT ? (A_INST + B_INST) / NW
+                                    : A_PER_WAVE + (B_INST + NW - 1) / NW;  // loads per wave per stage
+  static constexpr int B_PER_WAVE = NDMA - A_MIN;   // loads I >= A_MIN that may be B loads
   static constexpr int RING = S * STAGE;
   // Tiles with more accumulators than the 256-entry accumulator file keep
   // one set of B fragments instead of two (block g of the next stage is read
@@ -81,6 +90,11 @@ struct Gemm {
   // pressure of the 320x224 tile (280 accumulators per lane) and measured
   // faster there, slower for tiles that fit.
   static constexpr bool SINGLE_B = FM * FN * 4 > 256 / (NW / 4);
+  // 4-wave tiles that fill (nearly) the whole accumulator file: the MFMAs
+  // are issued with each accumulator tied to one register (inline assembly),
+  // since the compiler otherwise rotates accumulators through spare
+  // registers (a move between dependent MFMAs) once fewer than 8 are free.
+  static constexpr bool TIED_ACC = NW == 4 && FM * FN * 4 > 248;
   static constexpr int LD_C = BN + 8;               // epilogue staging row (elements)
   static constexpr int LDS_BYTES = (RING > BM * LD_C * 2) ? RING : BM * LD_C * 2;
   static_assert(WM % 16 == 0 && WN % 16 == 0 && BN % 32 == 0, "whole 16x16 blocks per wave, 32-column B blocks");
@@ -152,13 +166,34 @@ __device__ __forceinline__ int dma_row(int wave, int i, int lane) {
   return a_block<BM, BN>(wave, i) * 16 + (lane >> 2);
 }
 
+// Whether load I of wave `wave` is an A load (wave-uniform).
+template <int BM, int BN>
+__device__ __forceinline__ bool load_is_a(int wave, int I) {
+  using G = Gemm<BM, BN>;
+  if constexpr (G::JOINT) return wave + G::NW * I < G::A_INST;
+  return I < G::A_PER_WAVE;
+}
+
+// 1 KiB B block that B-capable load A_MIN + i of wave `wave` fetches (any
+// valid block where that load is an A load of this wave).
+template <int BM, int BN>
+__device__ __forceinline__ int b_block(int wave, int i) {
+  using G = Gemm<BM, BN>;
+  if constexpr (G::JOINT) {
+    const int j = wave + G::NW * (G::A_MIN + i) - G::A_INST;
+    return j < 0 ? 0 : j;
+  } else {
+    const int j = wave + G::NW * i;
+    return j >= G::B_INST ? j - G::NW : j;
+  }
+}
+
 // Per-tile constants of this wave's loads: the A instruction i loads rows
 // 16*b + lane/4 (b = a_block(wave, i)), chunk (lane & 3) ^ swz_a(row), into
-// the slot's 1 KiB block b; B instruction i (j = wave + NW*i)
-// loads k row (j & 1)*16 + lane/4 of column block j/2, chunk pair
-// (lane & 3) ^ 2*swz_b(k), into block j of the slot's B part. A wave whose
-// last j is past the B blocks repeats its previous B load (same source, same
-// LDS bytes), so every wave issues NDMA loads per stage.
+// the slot's 1 KiB block b; B-capable load i (j = b_block(wave, i)) loads k
+// row (j & 1)*16 + lane/4 of column block j/2, chunk pair
+// (lane & 3) ^ 2*swz_b(k), into block j of the slot's B part. Every wave
+// issues NDMA loads per stage.
 template <int BM, int BN>
 struct DmaPlan {
   const char* a[Gemm<BM, BN>::A_PER_WAVE];     // per lane, stage 0
@@ -179,8 +214,7 @@ __device__ __forceinline__ DmaPlan<BM, BN> make_dma_plan(const TileCtx<BM, BN>& 
   }
 #pragma unroll
   for (int i = 0; i < G::B_PER_WAVE; ++i) {
-    int j = wave + G::NW * i;
-    if (j >= G::B_INST) j -= G::NW;
+    const int j = b_block<BM, BN>(wave, i);
     const int nb = j >> 1, k = (j & 1) * 16 + (lane >> 2);
     const int c = (lane & 3) ^ (2 * swz_b(k));
     // byte offset of B[k][n0 + 32*nb + 8*c]; K*N*2 < 2^32 (unsigned math)
@@ -196,11 +230,18 @@ template <int BM, int BN, int I>
 __device__ __forceinline__ void dma_one(uint32_t slot, const DmaPlan<BM, BN>& d, const __amdgpu_buffer_rsrc_t& brs,
                                         int s, int wave) {
   using G = Gemm<BM, BN>;
-  if constexpr (I < G::A_PER_WAVE) {
+  if constexpr (I < G::A_MIN) {
     dma_global(slot + a_block<BM, BN>(wave, I) * 1024, d.a[I] + s * (BKS * 2));
-  } else {
-    constexpr int i = I - G::A_PER_WAVE;
+  } else if constexpr (I >= G::A_PER_WAVE) {
+    constexpr int i = I - G::A_MIN;
     dma_buffer(slot + d.b_dst[i], brs, d.b_off[i] + (uint32_t)s * d.b_step);
+  } else {
+    // JOINT: A load in the first waves, B load in the others
+    constexpr int i = I - G::A_MIN;
+    if (load_is_a<BM, BN>(wave, I))
+      dma_global(slot + a_block<BM, BN>(wave, I) * 1024, d.a[I] + s * (BKS * 2));
+    else
+      dma_buffer(slot + d.b_dst[i], brs, d.b_off[i] + (uint32_t)s * d.b_step);
   }
 }
 
@@ -279,6 +320,18 @@ __device__ __forceinline__ void dma_after_group(uint32_t slot, const DmaPlan<BM,
   }
 }
 
+// acc += a x b on one 16x16 block: the builtin, or with TIED the same
+// instruction with the accumulator in one fixed accumulator register tuple.
+template <bool TIED>
+__device__ __forceinline__ f32x4_t mfma16(bf16x8_t b, bf16x8_t a, f32x4_t acc) {
+  if constexpr (TIED) {
+    asm("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(b), "v"(a));
+    return acc;
+  } else {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(b, a, acc, 0, 0, 0);
+  }
+}
+
 // MFMA group GI (column block GI) of `cur`, preceded by the two transposing
 // reads of the same block of `nxt` and followed by its share of the loads.
 // With SINGLE_B the B fragments live in `bs` only and the reads follow the
@@ -293,13 +346,13 @@ __device__ __forceinline__ void mfma_groups(const Frags<BM, BN>& cur, Frags<BM, 
     if constexpr (G::SINGLE_B) {
 #pragma unroll
       for (int f = 0; f < G::FM; ++f)
-        acc.v[f][GI] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bs[GI], cur.a[f], acc.v[f][GI], 0, 0, 0);
+        acc.v[f][GI] = mfma16<G::TIED_ACC>(bs[GI], cur.a[f], acc.v[f][GI]);
       bs[GI] = read_b_frag<BM, BN>(st, fa, GI);
     } else {
       nxt.b[GI] = read_b_frag<BM, BN>(st, fa, GI);
 #pragma unroll
       for (int f = 0; f < G::FM; ++f)
-        acc.v[f][GI] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur.b[GI], cur.a[f], acc.v[f][GI], 0, 0, 0);
+        acc.v[f][GI] = mfma16<G::TIED_ACC>(cur.b[GI], cur.a[f], acc.v[f][GI]);
     }
     dma_after_group<BM, BN, GI>(slot, d, brs, s, wave);
     __builtin_amdgcn_sched_barrier(0);
@@ -332,7 +385,10 @@ __device__ __forceinline__ void stage_body(const Frags<BM, BN>& cur, Frags<BM, B
 // until at most S-4 stages of this wave's loads are in flight (stages k+1 and
 // k+2 have landed), then barrier (everyone's have, and every wave finished
 // reading stage k-1 (in step k-2) and stage k (in step k-1), the slots the
-// pair overwrites). Past the end the loads repeat stage nk-1 into the free
+// pair overwrites). A 4-slot ring waits and syncs before every step instead
+// (stage k+1 landed, stage k+2 may still be in flight; the barrier also
+// covers the slot of stage k-1 that step k overwrites). Past the end the
+// loads repeat stage nk-1 into the free
 // slot, which is never read again, so the per-step load count and the wait
 // are constants; in the last step the fragment reads fetch a stale slot whose
 // values are never used.
@@ -371,13 +427,39 @@ __device__ __forceinline__ void mainloop(OCG_LDS char* smem, const TileCtx<BM, B
     wr = (wr + G::STAGE == S * G::STAGE) ? 0u : wr + G::STAGE;
   };
   for (int k = 0; k < nk; k += 2) {
-    vm_wait<(S - 4) * G::NDMA>();
-    lds_barrier();
-    step(k, f0, f1);
-    step(k + 1, f1, f0);
+    if constexpr (S >= 5) {
+      vm_wait<(S - 4) * G::NDMA>();
+      lds_barrier();
+      step(k, f0, f1);
+      step(k + 1, f1, f0);
+    } else {
+      // A 4-slot ring would leave no load in flight at a pair's wait (stage
+      // k+2 is issued in step k-1): wait and barrier before every step
+      // instead, for stage k+1 only, so the loads of stage k+2 stay in
+      // flight and each stage has two steps to land, as with 5 slots.
+      vm_wait<(S - 3) * G::NDMA>();
+      lds_barrier();
+      step(k, f0, f1);
+      vm_wait<(S - 3) * G::NDMA>();
+      lds_barrier();
+      step(k + 1, f1, f0);
+    }
+    // The compiler does not see the tied MFMAs as MFMAs, so it does not pad
+    // a read of their results: 20 wait states (at least the 19 these 8-pass
+    // MFMAs need) end every pair of steps, before anything can read an
+    // accumulator (the copies the compiler places at the loop exit
+    // included). They overlap the last MFMA, which still occupies the pipe.
+    if constexpr (G::TIED_ACC) asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" ::: "memory");
   }
   vm_wait<0>();   // no load may still target LDS when the tile's LDS is reused
   lds_barrier();
+  if constexpr (G::TIED_ACC) {
+    // each accumulator leaves the loop in the register it was tied to
+#pragma unroll
+    for (int f = 0; f < G::FM; ++f)
+#pragma unroll
+      for (int g = 0; g < G::FN; ++g) asm volatile("" : "+a"(acc.v[f][g]));
+  }
 }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {

@@ -220,10 +220,10 @@ __global__ __launch_bounds__((Gemm<BM, BN>::NT), 1) void gemm_rs_kernel(RsArgs a
 
 // ---------------------------------------------------------------- MoE routing
 
-// Routing runs as two one-wave-per-block kernels over blocks of kRouteBlock
-// tokens, so every step is spread over the chip: (1) per token top-k of the
-// fp32 logits (ties -> lower expert, slot 0 = larger logit) and softmax
-// weights, plus a per-block expert histogram; (2) per block, the expert
+// Routing runs as two kernels over blocks of kRouteBlock tokens, so every
+// step is spread over the chip: (1) per token top-k of the fp32 logits (ties
+// -> lower expert, slot 0 = larger logit) and softmax weights, one lane per
+// expert, plus a per-block expert histogram; (2) per block, the expert
 // bases of the block (histograms of the blocks before it) and the expert
 // offsets (totals, scanned across the wave), then a stable rank of the
 // block's token slots within each expert gives the expert-sorted slot list
@@ -231,147 +231,152 @@ __global__ __launch_bounds__((Gemm<BM, BN>::NT), 1) void gemm_rs_kernel(RsArgs a
 // offsets and the grouped-tile lookup table (the dynamic dependency table:
 // expert, first row, rows, column block per tile).
 
-__global__ __launch_bounds__(kRouteBlock) void moe_topk_kernel(RouteArgs a) {
-  __shared__ int s_cnt[kMaxExperts];
-  static_assert(kRouteBlock == kMaxExperts, "one counter per lane");
-  const int lane = threadIdx.x, E = a.E, K = a.topk;
-  s_cnt[lane] = 0;
-  __syncthreads();
-  const int t = blockIdx.x * kRouteBlock + lane;
-  if (t < a.T) {
-    const float* lg = a.logits + (size_t)t * E;
-    float bv[kMaxTopk];
-    int bi[kMaxTopk];
-#pragma unroll
-    for (int j = 0; j < kMaxTopk; ++j) {
-      bv[j] = 0.f;
-      bi[j] = -1;
-    }
-    // all logits of the token at once (independent loads, then registers)
-    float v[kMaxExperts];
-#pragma unroll
-    for (int e = 0; e < kMaxExperts; ++e) v[e] = (e < E) ? lg[e] : 0.f;
-#pragma unroll
-    for (int e = 0; e < kMaxExperts; ++e) {
-      if (e < E) {
-        // insertion keeping the first (lowest-index) of equal logits ahead
-        int pos = K;
-        for (int j = K - 1; j >= 0; --j)
-          if (bi[j] < 0 || v[e] > bv[j]) pos = j;
-        if (pos < K) {
-          for (int j = K - 1; j > pos; --j) {
-            bv[j] = bv[j - 1];
-            bi[j] = bi[j - 1];
-          }
-          bv[pos] = v[e];
-          bi[pos] = e;
-        }
-      }
-    }
-    const float mx = bv[0];
-    float sum = 0.f;
-#pragma unroll
-    for (int e = 0; e < kMaxExperts; ++e)
-      if (e < E) sum += __expf(v[e] - mx);
-    for (int j = 0; j < K; ++j) {
-      a.topk_ids[t * K + j] = bi[j];
-      a.topk_w[t * K + j] = __expf(bv[j] - mx) / sum;
-      atomicAdd(&s_cnt[bi[j]], 1);
-    }
-  }
-  __syncthreads();
-  if (lane < E) a.blk_cnt[blockIdx.x * E + lane] = s_cnt[lane];
+// Wave-wide maximum / sum of one value per lane: DPP within rows of 16
+// lanes, then the lane swaps across rows (no LDS round trips).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
 }
 
-__global__ __launch_bounds__(kRouteBlock) void moe_scatter_kernel(RouteArgs a) {
-  __shared__ int s_run[kMaxExperts];
-  __shared__ int s_off[kMaxExperts + 1];
+template <bool MAX>
+__device__ __forceinline__ float wave_reduce(float x) {
+  auto op = [](float u, float v) { return MAX ? fmaxf(u, v) : u + v; };
+  x = op(x, dpp_f<0xB1>(x));    // quad_perm [1,0,3,2]
+  x = op(x, dpp_f<0x4E>(x));    // quad_perm [2,3,0,1]
+  x = op(x, dpp_f<0x141>(x));   // row_half_mirror
+  x = op(x, dpp_f<0x140>(x));   // row_mirror
+  auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = op(__uint_as_float(r16[0]), __uint_as_float(r16[1]));
+  auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return op(__uint_as_float(r32[0]), __uint_as_float(r32[1]));
+}
+
+// Top-k of each token with one lane per expert: a routing block of
+// kRouteBlock tokens per workgroup, kRouteTokW consecutive tokens per wave,
+// all their logit rows loaded at once (coalesced). Per token: the wave
+// maximum and softmax denominator, then k rounds of "largest remaining
+// logit, lowest expert among equals" (a wave maximum, then the lowest lane
+// holding it), each pick's weight and a count in the block histogram.
+constexpr int kRouteWaves = 16;
+constexpr int kRouteTokW = kRouteBlock / kRouteWaves;
+
+__global__ __launch_bounds__(64 * kRouteWaves) void moe_topk_kernel(RouteArgs a) {
   __shared__ int s_cnt[kMaxExperts];
-  __shared__ int s_tbase[kMaxExperts + 1];
-  const int lane = threadIdx.x;
-  const int E = a.E, K = a.topk, S = a.T * K;
-  const int nb = cdiv(a.T, kRouteBlock);
-  // expert totals, and the slots of each expert in the blocks before this one
-  int tot = 0, before = 0;
-  if (lane < E) {
-    for (int b0 = 0; b0 < nb; b0 += 16) {
-      int c[16];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, E = a.E, K = a.topk;
+  if (threadIdx.x < kMaxExperts) s_cnt[threadIdx.x] = 0;
+  __syncthreads();
+  const int t0 = blockIdx.x * kRouteBlock + wave * kRouteTokW;
+  float v[kRouteTokW];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) c[i] = (b0 + i < nb) ? a.blk_cnt[(b0 + i) * E + lane] : 0;
+  for (int i = 0; i < kRouteTokW; ++i)
+    v[i] = (t0 + i < a.T && lane < E) ? a.logits[(size_t)(t0 + i) * E + lane] : -INFINITY;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        if (b0 + i < (int)blockIdx.x) before += c[i];
-        tot += c[i];
+  for (int i = 0; i < kRouteTokW; ++i) {
+    const int t = t0 + i;
+    if (t >= a.T) break;
+    const float mx = wave_reduce<true>(v[i]);
+    const float sum = wave_reduce<false>(lane < E ? __expf(v[i] - mx) : 0.f);
+    float y = v[i];
+    for (int j = 0; j < K; ++j) {
+      const float m = wave_reduce<true>(y);
+      const int e = __builtin_ctzll(__ballot(lane < E && y == m));
+      if (lane == 0) {
+        a.topk_ids[t * K + j] = e;
+        a.topk_w[t * K + j] = __expf(m - mx) / sum;
+        atomicAdd(&s_cnt[e], 1);
       }
+      if (lane == e) y = -INFINITY;
     }
   }
-  // exclusive scan of the totals across the wave (lanes >= E hold 0)
-  int incl = tot;
+  __syncthreads();
+  if (threadIdx.x < E) a.blk_cnt[blockIdx.x * E + threadIdx.x] = s_cnt[threadIdx.x];
+}
+
+// Exclusive prefix sum across the wave; *total gets the wave's sum.
+__device__ __forceinline__ int wave_excl_scan(int x, int* total) {
+  const int lane = threadIdx.x & 63;
+  int incl = x;
 #pragma unroll
   for (int d = 1; d < 64; d <<= 1) {
     const int o = __shfl_up(incl, d);
     if (lane >= d) incl += o;
   }
-  const int off = incl - tot;
+  *total = __shfl(incl, 63);
+  return incl - x;
+}
+
+__global__ __launch_bounds__(kRouteBlock) void moe_scatter_kernel(RouteArgs a) {
+  __shared__ int s_run[kMaxExperts];
+  const int lane = threadIdx.x;
+  const int E = a.E, K = a.topk, S = a.T * K;
+  const int nb = cdiv(a.T, kRouteBlock);
+  // expert totals, and the slots of each expert in the blocks before this
+  // one (all histograms of a round of 64 blocks loaded at once)
+  int tot = 0, before = 0;
   if (lane < E) {
-    s_off[lane] = off;
-    s_cnt[lane] = tot;
-    s_run[lane] = off + before;
+    for (int b0 = 0; b0 < nb; b0 += 64) {
+      int c[64];
+#pragma unroll
+      for (int i = 0; i < 64; ++i) c[i] = (b0 + i < nb) ? a.blk_cnt[(b0 + i) * E + lane] : 0;
+#pragma unroll
+      for (int i = 0; i < 64; ++i) {
+        if (b0 + i < (int)blockIdx.x) before += c[i];
+        tot += c[i];
+      }
+    }
   }
-  if (lane == E - 1) s_off[E] = incl;
-  __syncthreads();
+  // expert offsets: exclusive scan of the totals (lanes >= E hold 0)
+  int n_slots;
+  const int off = wave_excl_scan(tot, &n_slots);
+  if (lane < E) s_run[lane] = off + before;
   if (blockIdx.x == 0) {
-    if (lane <= E) {
-      a.offsets[lane] = s_off[lane];
-      if (a.user_offsets) a.user_offsets[lane] = s_off[lane];
+    // E + 1 entries (E may be 64: the last one comes from lane 0)
+    if (lane < E) {
+      a.offsets[lane] = off;
+      if (a.user_offsets) a.user_offsets[lane] = off;
     }
     if (lane == 0) {
-      int tb = 0;
-      for (int e = 0; e < E; ++e) {
-        s_tbase[e] = tb;
-        tb += cdiv(s_cnt[e], a.BM) * a.n_cb;
-      }
-      s_tbase[E] = tb;
-      a.hdr->n_tiles = (uint32_t)min(tb, a.max_tiles);
+      a.offsets[E] = n_slots;
+      if (a.user_offsets) a.user_offsets[E] = n_slots;
     }
-    __syncthreads();
     // lookup table: one entry per (expert, column block, row tile), in that
-    // nesting order
-    const int n = min(s_tbase[E], a.max_tiles);
-    for (int i = lane; i < n; i += kRouteBlock) {
-      int e = 0;
-      while (e + 1 < E && s_tbase[e + 1] <= i) ++e;
-      const int nrt = cdiv(s_cnt[e], a.BM);
-      const int j = i - s_tbase[e];
+    // nesting order; lane e writes its expert's entries from its base
+    const int nrt = lane < E ? cdiv(tot, a.BM) : 0;
+    int n_ent;
+    const int tb = wave_excl_scan(nrt * a.n_cb, &n_ent);
+    if (lane == 0) a.hdr->n_tiles = (uint32_t)min(n_ent, a.max_tiles);
+    for (int j = 0; j < nrt * a.n_cb; ++j) {
+      const int i = tb + j;
+      if (i >= a.max_tiles) break;
       const int cb = j / nrt, rt = j - cb * nrt;
-      const int r0 = s_off[e] + rt * a.BM;
-      int32_t* L = a.lut + (size_t)i * 8;
-      L[0] = e;
-      L[1] = r0;
-      L[2] = min(a.BM, s_off[e + 1] - r0);
-      L[3] = cb;
-      L[4] = L[5] = L[6] = L[7] = 0;
+      const int r0 = off + rt * a.BM;
+      int4* L = reinterpret_cast<int4*>(a.lut + (size_t)i * 8);
+      L[0] = make_int4(lane, r0, min(a.BM, off + tot - r0), cb);
+      L[1] = make_int4(0, 0, 0, 0);
     }
   }
-  // the block's slots in index order, one wave-wide round at a time
+  __syncthreads();
+  // the block's slots in index order, one wave-wide round at a time: the
+  // lanes holding the same expert are found by matching its index bit by
+  // bit (E <= 64: six ballots), the lower lanes among them give the rank
   const int s0 = blockIdx.x * kRouteBlock * K;
   for (int c = 0; c < K; ++c) {
     const int s = s0 + c * kRouteBlock + lane;
     const int e = s < S ? a.topk_ids[s] : -1;
-    uint64_t todo = __ballot(e >= 0);
-    int pos = -1;
-    while (todo) {
-      const int leader = __builtin_ctzll(todo);
-      const int x = __shfl(e, leader);
-      const uint64_t same = __ballot(e == x);
-      const int base = s_run[x];
-      if (e == x) pos = base + __builtin_popcountll(same & ((1ull << lane) - 1ull));
-      __syncthreads();
-      if (lane == leader) s_run[x] = base + __builtin_popcountll(same);
-      __syncthreads();
-      todo &= ~same;
+    uint64_t same = __ballot(e >= 0);
+#pragma unroll
+    for (int bit = 0; bit < 6; ++bit) {
+      const uint64_t ones = __ballot(e >= 0 && ((e >> bit) & 1));
+      same &= ((e >> bit) & 1) ? ones : ~ones;
     }
-    if (e >= 0) a.perm[pos] = s;
+    if (e >= 0) {
+      const int base = s_run[e];
+      a.perm[base + __builtin_popcountll(same & ((1ull << lane) - 1ull))] = s;
+    }
+    __syncthreads();
+    // the highest lane of each expert's group advances that expert's base
+    if (e >= 0 && lane == 63 - __builtin_clzll(same)) s_run[e] += __builtin_popcountll(same);
+    __syncthreads();
   }
 }
 
@@ -602,7 +607,7 @@ hipError_t launch_gemm_rs(const RsArgs& a, int tile, int grid, hipStream_t s) {
 
 hipError_t launch_moe(const RouteArgs& r, const MoeArgs& a, int tile, int grid, hipStream_t s) {
   const int nb = cdiv(r.T, kRouteBlock);
-  hipLaunchKernelGGL(moe_topk_kernel, dim3(nb), dim3(kRouteBlock), 0, s, r);
+  hipLaunchKernelGGL(moe_topk_kernel, dim3(nb), dim3(64 * kRouteWaves), 0, s, r);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(moe_scatter_kernel, dim3(nb), dim3(kRouteBlock), 0, s, r);

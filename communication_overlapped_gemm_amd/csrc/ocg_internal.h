@@ -12,7 +12,7 @@ namespace ocg {
 
 constexpr int kMaxRanks = 16;
 constexpr int kThreads = 256;         // every persistent kernel: 4 waves of 64
-constexpr int kRouteBlock = 64;       // tokens per routing block (one wave per routing block)
+constexpr int kRouteBlock = 64;       // tokens per routing block
 constexpr int kMaxRouteSlots = 16384; // token slots (T * topk) per call
 constexpr int kMaxExperts = 64;
 constexpr int kMaxTopk = 4;

@@ -101,6 +101,20 @@ def test_moe_lookup_table_tiles(ocg):
     check(ocg, x, o, "lut")
 
 
+@pytest.mark.parametrize("case", [("e64_max_slots", 8, 1024, 2), ("e64_ragged_top3", 5, 1000, 3)],
+                         ids=["e64_max_slots", "e64_ragged_top3"])
+def test_moe_routing_limits(ocg, case):
+    """The routing at its limits: 64 experts (one per lane, E + 1 offsets),
+    16384 token slots (the most a call takes), more than 64 routing blocks of
+    64 tokens (histograms read in several rounds), a ragged last block."""
+    name, R, m, topk = case
+    x = workloads.make_moe(R, m, 64, 64, 64, seed=320 + topk, topk=topk, scale=0.5)
+    say("moe routing limits", name)
+    o = run(ocg, x, R - 1)
+    res = check(ocg, x, o, name)
+    assert len(res["offsets"]) == 65
+
+
 def test_moe_full_workload(ocg):
     x = workloads.workload("ag_moe").make()
     say("moe full workload")
