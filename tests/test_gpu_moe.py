@@ -22,6 +22,8 @@ def run(ocg, x, local=0, cfg=None, logits=None):
     outs = dict(a_gathered=poison((T, x.K)), out=poison((T * x.topk, x.N)))
     o = ocg.ag_grouped_gemm(chunks, lg, w, x.topk, local, config=cfg, outputs=outs)
     torch.cuda.synchronize()
+    # no wait of the call (routing counters, slab flags) timed out
+    ocg.Workspace.cached(ocg.OP_AG_GROUPED_GEMM, x.R, x.m, x.K, x.N, x.E, x.topk).check()
     return o
 
 
@@ -113,6 +115,17 @@ def test_moe_routing_limits(ocg, case):
     o = run(ocg, x, R - 1)
     res = check(ocg, x, o, name)
     assert len(res["offsets"]) == 65
+
+
+def test_moe_repeated_calls_one_workspace(ocg):
+    """Calls in a row on one workspace with new logits and values each time
+    and other tile presets: the routing (histograms, slot list, lookup table)
+    and the slab flags start over every call."""
+    for i, tile in enumerate(["128x224", "256x224", "288x224", "320x224", "128x224"]):
+        x = workloads.make_moe(3, 160, 128, 232, 8, seed=330 + i, topk=2, scale=0.5)
+        say("moe repeat", i, tile)
+        o = run(ocg, x, i % 3, ocg.default_config(tile=TILES[tile]))
+        check(ocg, x, o, f"repeat {i} {tile}")
 
 
 def test_moe_full_workload(ocg):
