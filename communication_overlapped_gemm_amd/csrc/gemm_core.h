@@ -95,6 +95,10 @@ struct Gemm {
   // since the compiler otherwise rotates accumulators through spare
   // registers (a move between dependent MFMAs) once fewer than 8 are free.
   static constexpr bool TIED_ACC = NW == 4 && FM * FN * 4 > 248;
+  // With SINGLE_B a fragment read overwrites the B registers right after the
+  // group's MFMAs read them, a hazard the compiler pads only for MFMAs it
+  // can see, so the two are never combined.
+  static_assert(!(TIED_ACC && SINGLE_B), "tied accumulators need double-buffered B fragments");
   static constexpr int LD_C = BN + 8;               // epilogue staging row (elements)
   static constexpr int LDS_BYTES = (RING > BM * LD_C * 2) ? RING : BM * LD_C * 2;
   static_assert(WM % 16 == 0 && WN % 16 == 0 && BN % 32 == 0, "whole 16x16 blocks per wave, 32-column B blocks");
