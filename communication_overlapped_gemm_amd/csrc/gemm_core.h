@@ -409,6 +409,15 @@ __device__ __forceinline__ void mainloop(OCG_LDS char* smem, const TileCtx<BM, B
   for (int f = 0; f < G::FM; ++f)
 #pragma unroll
     for (int g = 0; g < G::FN; ++g) acc.v[f][g] = f32x4_t{};
+  // Tied MFMAs: each zeroed accumulator passes through a 2-wait-state nop
+  // of its own before any MFMA can read it (the compiler pads only the
+  // MFMAs it sees).
+  if constexpr (G::TIED_ACC) {
+#pragma unroll
+    for (int f = 0; f < G::FM; ++f)
+#pragma unroll
+      for (int g = 0; g < G::FN; ++g) asm volatile("s_nop 1" : "+a"(acc.v[f][g]));
+  }
   // prologue: stages 0 .. S-2 (repeating stage nk-1 past the end)
 #pragma unroll
   for (int j = 0; j < S - 1; ++j) dma_stage<BM, BN>(base + j * G::STAGE, d, t.brs, j < nk ? j : nk - 1, wave);
