@@ -73,8 +73,13 @@ bool shape_ok(int R, int64_t m, int64_t K, int64_t N) {
 
 // Estimated cost of a tile preset: rounds of the persistent grid times the
 // tile area, derated for the smaller wave tiles.
+// Relative speed per output element of each preset, fitted to launches at
+// the 8B and 70B shares on one MI355X: 256x224 tiles 1.0; 128x256 tiles
+// came out 3 % faster than 128x224 at the 8B AllGather share (224 vs 256
+// tiles, one round each) and 256x256 tiles 3 % faster than 128x256 at the
+// 8B GEMM-RS share (one round of 256 vs two).
 int choose_tile(int64_t M, int64_t N, int cus) {
-  static const double eff[OCG_TILE_COUNT] = {1.0, 0.9, 0.92, 0.75, 0.9, 0.0, 0.0};
+  static const double eff[OCG_TILE_COUNT] = {1.0, 0.9, 1.03, 0.75, 1.035, 0.0, 0.0};
   int best = OCG_TILE_128x128;
   double best_cost = 1e300;
   for (int t = 0; t < OCG_TILE_COUNT; ++t) {
