@@ -91,12 +91,15 @@ def test_plan_info_tile_choice():
     # 70B share: 256x224 tiles (exactly 512 = two rounds of 256 CUs)
     p = ocg.plan_info(ocg.OP_AG_GEMM, 8, 0, 1024, 8192, 3584)
     assert (p["BM"], p["BN"], p["n_tiles"]) == (256, 224, 512)
-    # 8B share: 128x224 (256 tiles, one round)
+    # 8B share: 128x256 (224 tiles, one round)
     p = ocg.plan_info(ocg.OP_AG_GEMM, 8, 0, 512, 4096, 1792)
-    assert (p["BM"], p["BN"], p["n_tiles"]) == (128, 224, 256)
-    # GEMM-RS 4096 x 4096: 128x256 (512 tiles, two full rounds)
+    assert (p["BM"], p["BN"], p["n_tiles"]) == (128, 256, 224)
+    # GEMM-RS 4096 x 4096: 256x256 (256 tiles, one round)
     p = ocg.plan_info(ocg.OP_GEMM_RS, 8, 0, 4096, 1792, 4096)
-    assert (p["BM"], p["BN"], p["n_tiles"]) == (128, 256, 512)
+    assert (p["BM"], p["BN"], p["n_tiles"]) == (256, 256, 256)
+    # tiny AllGather share (4 x [128, 256] x [256, 256]): 128x128, 8 tiles
+    p = ocg.plan_info(ocg.OP_AG_GEMM, 4, 0, 128, 256, 256)
+    assert (p["BM"], p["BN"], p["n_tiles"]) == (128, 128, 8)
 
 
 def test_plan_info_moe_tile_choice():
