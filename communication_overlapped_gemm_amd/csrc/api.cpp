@@ -72,9 +72,9 @@ bool shape_ok(int R, int64_t m, int64_t K, int64_t N) {
 }
 
 // Estimated cost of a tile preset: rounds of the persistent grid times the
-// tile area, derated for the smaller wave tiles.
-// Relative speed per output element of each preset, fitted to launches at
-// the 8B and 70B shares on one MI355X: 256x224 tiles 1.0; 128x256 tiles
+// tile area, divided by the preset's relative speed per output element,
+// fitted to launches at the 8B and 70B shares on one MI355X: 256x224 tiles
+// 1.0; 128x224 0.9 (smaller wave tiles); 128x256 tiles
 // came out 3 % faster than 128x224 at the 8B AllGather share (224 vs 256
 // tiles, one round each) and 256x256 tiles 3 % faster than 128x256 at the
 // 8B GEMM-RS share (one round of 256 vs two).
@@ -189,7 +189,11 @@ int resolve_attn(int64_t m, int64_t Hkv, const ocg_config& c, int* S, int* CT) {
   if (c.copy_rows > 0) {
     *CT = c.copy_rows;
   } else {
-    int64_t ct = (128 * 1024) / row_bytes;
+    // about 1 MiB per copy task: at the 16K-context share (2 x 64 tasks)
+    // a quarter of the workgroups gathers while the rest start on the
+    // local chunk's keys; 128 KiB tasks kept every workgroup copying first
+    // (563 vs 544 us per fused launch)
+    int64_t ct = (1024 * 1024) / row_bytes;
     int p2 = 1;
     while ((int64_t)p2 * 2 <= ct) p2 *= 2;
     *CT = p2 < *S ? p2 : *S;
