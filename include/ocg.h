@@ -254,8 +254,9 @@ int ocg_moe_combine_rs(ocg_handle h, const void* y, const float* topk_w, int R, 
  *                  local one included)
  *   out          : bf16 [m, Hq, d], written
  * Copy tasks pull each peer chunk of keys and values into the gathered
- * buffers slab by slab (slab_rows tokens, default the whole chunk) and
- * publish a flag per slab; each tile (256 query rows of one kv head) starts
+ * buffers slab by slab (slab_rows tokens, default the whole chunk; tasks of
+ * copy_rows tokens, default about 1 MiB of one tensor) and publish a flag
+ * per slab; each tile (256 query rows of one kv head) starts
  * on the local chunk, read from its own shard, and waits on a peer chunk's
  * flags before loading it. Requires d == 128, Hq % Hkv == 0,
  * R*m*Hkv*d < 2^31, m*Hq*d < 2^31, 16-byte aligned pointers; workspace from
