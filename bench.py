@@ -3,19 +3,25 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--skip-extras]
 
-A step is one fused AG-GEMM call (copy tasks + flag waits + MFMA tiles, one
-persistent kernel) on the 70B-class TP=8 share: R = 8 ranks x [1024, 8192]
-bf16 shards gathered to [8192, 8192], times B [8192, 3584], bf16 output. All
-inputs are seeded synthetic data (N(0, 0.02), seed 3) already resident in HBM
-when the timed region starts. The same JSON line also reports:
-  * overlap: T_fused, T_gemm (GEMM tiles only, flags treated as published),
-    T_copy (copy tasks only), T_serial (copy kernel, event, GEMM kernel on a
-    second stream), E_max = max(T_copy, T_gemm) / T_fused, E_serial;
-  * the other hot-path operations at their workloads (8B-class AG-GEMM,
-    GEMM-ReduceScatter, AllGather + MoE grouped GEMM);
-  * roofline of the dominant kernel and the CPU oracle timed on a sample.
---skip-extras drops those extra measurements (profiler runs); the timed step
-is unchanged.
+A step is one fused AG-GEMM call on the 70B-class TP=8 share: R = 8 ranks x
+[1024, 8192] bf16 shards gathered to [8192, 8192], times B [8192, 3584], bf16
+output. With the default transfer mode the call is two kernels running at
+once on every compute unit -- the GEMM's persistent kernel and the side
+producer that copies the peers' rows K-slab by K-slab and publishes the flags
+the tiles wait on. All inputs are seeded synthetic data (N(0, 0.02), seed 3)
+already resident in HBM when the timed region starts.
+
+Order of work: (1) the overlap legs -- fused (side producer), fused with the
+copies inline, GEMM tiles only, copies only (both forms) and copy-then-GEMM
+on two streams -- timed in alternating rounds, so clock drift is shared by
+all legs; they also carry the chip through the power-management transient
+of its first ~35 ms under load (launches of a fresh process first run fast,
+then ~30 % slow, then settle), whose first launches are reported as
+`transient`; (2) W warm-up steps, then exactly K timed steps between
+synchronisations -- the headline; (3) the shader clock, read from traced
+launches (s_memtime cycles against the 100 MHz clock), the other operations
+and the CPU oracle. --skip-extras keeps (1)'s settling launches of the fused
+step only and drops (3) (profiler runs).
 """
 from __future__ import annotations
 
@@ -127,6 +133,51 @@ def cpu_baseline(x, target_s=10.0, max_runs=40):
                       f"{len(ts)} runs in {total:.1f} s (median run {statistics.median(ts):.2f} s)"}
 
 
+def git_sha() -> str:
+    try:
+        import subprocess
+        return subprocess.run(["git", "-C", ROOT, "rev-parse", "--short=12", "HEAD"], capture_output=True,
+                              text=True, timeout=10).stdout.strip() or "unknown"
+    except Exception:
+        return "unknown"
+
+
+def gpu_temperature():
+    """Edge/junction temperature from rocm-smi, or None if it cannot be read."""
+    try:
+        import subprocess
+        out = subprocess.run(["rocm-smi", "--showtemp", "--json"], capture_output=True, text=True, timeout=20).stdout
+        card = next(iter(json.loads(out).values()))
+        return {k: v for k, v in card.items() if "emperature" in k}
+    except Exception:
+        return None
+
+
+def traced_clock_ghz(torch, ocg, launch_cfg, n_rec, runs=5):
+    """Compute-unit clock while the tiles run: per tile, shader-clock cycles
+    (s_memtime) over its 100 MHz duration, median over the tiles of `runs`
+    traced launches."""
+    import numpy as np
+    buf = torch.zeros(n_rec * 80, dtype=torch.uint8, device="cuda")
+    cfg = launch_cfg[1]
+    cfg.trace = buf.data_ptr()
+    cfg.trace_capacity = n_rec
+    ghz = []
+    for _ in range(runs):
+        launch_cfg[0](cfg)
+        torch.cuda.synchronize()
+        rec = buf.cpu().numpy().view(np.dtype([("ticket", "<u4"), ("kind", "<u4"), ("a", "<u4"), ("b", "<u4"),
+                                               ("c", "<u4"), ("d", "<u4"), ("hw", "<u4"), ("epoch", "<u4"),
+                                               ("t_start", "<u8"), ("t_ready", "<u8"), ("t_end", "<u8"),
+                                               ("flag_seen", "<u4"), ("queue", "<u4"), ("cycles", "<u8"),
+                                               ("wait_ticks", "<u4"), ("pad", "<u4")]))
+        t = rec[(rec["kind"] == 2) & (rec["t_end"] > rec["t_start"])]
+        ghz += list(t["cycles"] / (t["t_end"] - t["t_start"]) * 0.1)   # 100 MHz ticks -> GHz
+    cfg.trace = None
+    cfg.trace_capacity = 0
+    return float(np.median(ghz)) if ghz else None
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -166,10 +217,51 @@ def main() -> int:
     c = torch.empty((M, x.N), dtype=torch.bfloat16, device=dev)
     ws = ocg.Workspace(ocg.OP_AG_GEMM, x.R, x.m, x.K, x.N)
     fused = ocg.default_config()
+    h = ocg.handle()
+    plan = ocg.plan_ag(x.R, 0, x.m, x.K, x.N, fused, handle=h)
+    transfer = {ocg.TRANSFER_INLINE: "inline", ocg.TRANSFER_SIDE: "side"}[plan["transfer"]]
+
+    def launch(cfg, s=None):
+        ocg.ag_gemm(chunks, b, 0, a_gathered=ag, c=c, workspace=ws, config=cfg, stream=s)
 
     def step():
-        ocg.ag_gemm(chunks, b, 0, a_gathered=ag, c=c, workspace=ws, config=fused)
+        launch(fused)
 
+    # (1) overlap legs in alternation (also the settling launches)
+    first = timed_launches(torch, step, 20, stream)
+    legs = {}
+    if not args.skip_extras:
+        gemm_only = ocg.default_config(mode=ocg.MODE_GEMM_ONLY)
+        copy_only = ocg.default_config(mode=ocg.MODE_COPY_ONLY)
+        copy_inline = ocg.default_config(mode=ocg.MODE_COPY_ONLY, transfer=ocg.TRANSFER_INLINE)
+        fused_inline = ocg.default_config(transfer=ocg.TRANSFER_INLINE)
+        s2 = torch.cuda.Stream()
+        ev = torch.cuda.Event()
+
+        def serial():
+            launch(copy_inline, stream)
+            ev.record(stream)
+            s2.wait_event(ev)
+            launch(gemm_only, s2)
+            stream.wait_stream(s2)
+        full = torch.cat(chunks)
+        legs = {"fused": step, "fused_inline": lambda: launch(fused_inline), "gemm": lambda: launch(gemm_only),
+                "copy": lambda: launch(copy_only), "copy_inline": lambda: launch(copy_inline), "serial": serial,
+                "d2d": lambda: ag.copy_(full), "matmul": lambda: torch.matmul(full, b)}
+        samples = {k: [] for k in legs}
+        for _ in range(6):
+            for k, fn in legs.items():
+                fn()
+                samples[k] += timed_launches(torch, fn, 8, stream)
+        ws.check()
+        med = {k: statistics.median(v) for k, v in samples.items()}
+        del full
+    else:
+        t_end = time.perf_counter() + 0.15      # settle: ~150 ms of fused launches
+        while time.perf_counter() < t_end:
+            timed_launches(torch, step, 20, stream)
+
+    # (2) the headline: W warm-up steps, K timed steps
     for _ in range(args.warmup):
         step()
     ev = make_events(torch, args.steps)
@@ -183,7 +275,7 @@ def main() -> int:
     avg_launch_ms = sum(per_launch) / len(per_launch)
     achieved = flops / (avg_launch_ms * 1e-3) / 1e12
     khash = kernel_source_hash()
-    info = ocg.plan_info(ocg.OP_AG_GEMM, x.R, 0, x.m, x.K, x.N)
+    info = ocg.plan_info(ocg.OP_AG_GEMM, x.R, 0, x.m, x.K, x.N, handle=h)
 
     rec = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
@@ -193,7 +285,8 @@ def main() -> int:
         "config": {"workload": f"{WORKLOAD}: fused AllGather-GEMM, R=8 simulated ranks x A_r bf16 [1024,8192] "
                                f"(M=8192), B bf16 [8192,3584], N(0,0.02) seed 3, C bf16 [8192,3584]",
                    "tile": f"{info['BM']}x{info['BN']}", "slab_rows": info["slab_rows"],
-                   "copy_rows": info["copy_rows"], "local_rank": 0},
+                   "copy_rows": info["copy_rows"], "kslab_cols": plan["kslab_cols"], "transfer": transfer,
+                   "local_rank": 0},
         "pct_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
@@ -201,48 +294,44 @@ def main() -> int:
                      "kernel": f"ag_gemm_kernel<{info['BM']},{info['BN']}>",
                      "avg_launch_us": round(avg_launch_ms * 1e3, 2),
                      "algorithmic_flops_per_launch": flops, "kernel_hash": khash},
+        "git_sha": git_sha(),
     }
+    q = sorted(per_launch)
+    pct = lambda f: q[min(len(q) - 1, int(round(f * (len(q) - 1))))] * 1e3
+    rec["launch_stats"] = {"p10_us": round(pct(0.1), 2), "p50_us": round(pct(0.5), 2), "p90_us": round(pct(0.9), 2)}
+    rec["transient"] = {"first_launches_us": [round(v * 1e3, 1) for v in first],
+                        "note": "the process's first 20 fused launches, before the overlap legs"}
 
     if not args.skip_extras:
-        n = max(10, args.steps)
-        gemm_only = ocg.default_config(mode=ocg.MODE_GEMM_ONLY)
-        copy_only = ocg.default_config(mode=ocg.MODE_COPY_ONLY)
-        t_fused = statistics.median(per_launch)
-        t_gemm = median_ms(torch, lambda: ocg.ag_gemm(chunks, b, 0, a_gathered=ag, c=c, workspace=ws,
-                                                       config=gemm_only), n, stream)
-        t_copy = median_ms(torch, lambda: ocg.ag_gemm(chunks, b, 0, a_gathered=ag, c=c, workspace=ws,
-                                                       config=copy_only), n, stream)
-        s2 = torch.cuda.Stream()
-        ev = torch.cuda.Event()
-
-        def serial():
-            ocg.ag_gemm(chunks, b, 0, a_gathered=ag, c=c, workspace=ws, config=copy_only, stream=stream)
-            ev.record(stream)
-            s2.wait_event(ev)
-            ocg.ag_gemm(chunks, b, 0, a_gathered=ag, c=c, workspace=ws, config=gemm_only, stream=s2)
-            stream.wait_stream(s2)
-        t_serial = median_ms(torch, serial, n, stream)
-        full = torch.cat(chunks)
-        t_d2d = median_ms(torch, lambda: ag.copy_(full), n, stream)
-        t_mm = median_ms(torch, lambda: torch.matmul(full, b), n, stream)
-        ws.check()
+        rec["launch_stats"]["cold_us"] = round(cold_launch_ms(torch, step, 10, stream) * 1e3, 2)
+        # (3) clock while the tiles run
+        n_rec = info["n_copy_or_strips"] + info["n_tiles"]
+        clk = traced_clock_ghz(torch, ocg, (lambda cfg: launch(cfg), ocg.default_config()), n_rec)
+        if clk:
+            peak_clk = PEAK_BF16_TFLOPS * clk / 2.4
+            rec["roofline"]["clock_ghz"] = round(clk, 3)
+            rec["roofline"]["peak_at_clock"] = round(peak_clk, 1)
+            rec["roofline"]["frac_at_clock"] = round(achieved / peak_clk, 4)
+        rec["temperature"] = gpu_temperature()
+        t_f = med["fused"]
         copy_bytes = 2.0 * M * x.K * 2
         rec["overlap"] = {
-            "t_fused_us": round(t_fused * 1e3, 2), "t_gemm_us": round(t_gemm * 1e3, 2),
-            "t_copy_us": round(t_copy * 1e3, 2), "t_serial_us": round(t_serial * 1e3, 2),
-            "e_max": round(max(t_copy, t_gemm) / t_fused, 4), "e_serial": round(t_serial / t_fused, 4),
-            "gemm_only_tflops": round(flops / (t_gemm * 1e-3) / 1e12, 2),
-            "copy_only_gbs": round(copy_bytes / (t_copy * 1e-3) / 1e9, 1),
-            "d2d_copy_gbs_yardstick": round(copy_bytes / (t_d2d * 1e-3) / 1e9, 1),
-            "torch_matmul_tflops_yardstick": round(flops / (t_mm * 1e-3) / 1e12, 2),
+            "timing": "medians of 6 alternating rounds x 8 launches per leg",
+            "transfer": transfer,
+            "t_fused_us": round(t_f * 1e3, 2), "t_fused_inline_us": round(med["fused_inline"] * 1e3, 2),
+            "t_gemm_us": round(med["gemm"] * 1e3, 2), "t_copy_us": round(med["copy"] * 1e3, 2),
+            "t_copy_inline_us": round(med["copy_inline"] * 1e3, 2), "t_serial_us": round(med["serial"] * 1e3, 2),
+            "e_max": round(max(med["copy"], med["gemm"]) / t_f, 4),
+            "e_serial": round(med["serial"] / t_f, 4),
+            "hidden_copy_frac": round((med["gemm"] + med["copy_inline"] - t_f) / med["copy_inline"], 4),
+            "gemm_only_tflops": round(flops / (med["gemm"] * 1e-3) / 1e12, 2),
+            "fused_inline_tflops": round(flops / (med["fused_inline"] * 1e-3) / 1e12, 2),
+            "copy_only_gbs": round(copy_bytes / (med["copy"] * 1e-3) / 1e9, 1),
+            "copy_inline_gbs": round(copy_bytes / (med["copy_inline"] * 1e-3) / 1e9, 1),
+            "d2d_copy_gbs_yardstick": round(copy_bytes / (med["d2d"] * 1e-3) / 1e9, 1),
+            "torch_matmul_tflops_yardstick": round(flops / (med["matmul"] * 1e-3) / 1e12, 2),
         }
-        del full
-        q = sorted(per_launch)
-        pct = lambda f: q[min(len(q) - 1, int(round(f * (len(q) - 1))))] * 1e3
-        rec["launch_stats"] = {"p10_us": round(pct(0.1), 2), "p50_us": round(pct(0.5), 2),
-                               "p90_us": round(pct(0.9), 2),
-                               "cold_us": round(cold_launch_ms(torch, step, 10, stream) * 1e3, 2)}
-        rec["ops"] = other_ops(torch, np, ocg, workloads, upload, stream, n)
+        rec["ops"] = other_ops(torch, np, ocg, workloads, upload, stream, max(10, args.steps))
         rec["cpu_baseline"] = cpu_baseline(x)
     print(json.dumps(rec), flush=True)
     return 0

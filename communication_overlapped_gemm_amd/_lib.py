@@ -24,6 +24,7 @@ ERR_NO_DEVICE = -6
 
 OP_AG_GEMM, OP_GEMM_RS, OP_AG_GROUPED_GEMM, OP_MOE_COMBINE_RS, OP_AG_ATTENTION = 0, 1, 2, 3, 4
 MODE_FUSED, MODE_GEMM_ONLY, MODE_COPY_ONLY = 0, 1, 2
+TRANSFER_AUTO, TRANSFER_INLINE, TRANSFER_SIDE = -1, 0, 1
 TILE_AUTO, TILE_256x224, TILE_128x224, TILE_128x256, TILE_128x128, TILE_256x256, TILE_320x224, TILE_288x224 = (
     -1, 0, 1, 2, 3, 4, 5, 6)
 
@@ -31,7 +32,7 @@ EXPORTS = [
     "ocg_config_default", "ocg_create", "ocg_destroy", "ocg_workspace_bytes",
     "ocg_workspace_init", "ocg_ag_gemm", "ocg_gemm_rs", "ocg_ag_grouped_gemm",
     "ocg_signal", "ocg_check", "ocg_status_string", "ocg_plan_info", "ocg_plan_task",
-    "ocg_moe_combine_rs", "ocg_ag_attention",
+    "ocg_moe_combine_rs", "ocg_ag_attention", "ocg_plan_ag",
 ]
 
 
@@ -42,6 +43,8 @@ class Config(C.Structure):
         ("spin_timeout_us", C.c_uint32), ("fault_skip_slab", C.c_int32),
         ("trace", C.c_void_p), ("trace_capacity", C.c_uint32),
         ("peer_flags", C.c_void_p), ("peer_flag_value", C.c_uint32),
+        ("transfer", C.c_int32), ("kslab_cols", C.c_int32), ("copy_delay", C.c_uint32),
+        ("xcd_remap", C.c_int32), ("side_grid", C.c_int32),
     ]
 
 
@@ -50,11 +53,12 @@ class TraceRec(C.Structure):
         ("ticket", C.c_uint32), ("kind", C.c_uint32), ("a", C.c_uint32), ("b", C.c_uint32),
         ("c", C.c_uint32), ("d", C.c_uint32), ("hw", C.c_uint32), ("epoch", C.c_uint32),
         ("t_start", C.c_uint64), ("t_ready", C.c_uint64), ("t_end", C.c_uint64),
-        ("flag_seen", C.c_uint32), ("queue", C.c_uint32),
+        ("flag_seen", C.c_uint32), ("queue", C.c_uint32), ("cycles", C.c_uint64),
+        ("wait_ticks", C.c_uint32), ("pad", C.c_uint32),
     ]
 
 
-assert C.sizeof(TraceRec) == 64
+assert C.sizeof(TraceRec) == 80
 
 I64x8 = C.c_int64 * 8
 _P = C.c_void_p
@@ -65,7 +69,7 @@ def _declare(lib):
         "ocg_config_default": (None, [C.POINTER(Config)]),
         "ocg_create": (C.c_int, [C.c_int, C.POINTER(C.c_void_p)]),
         "ocg_destroy": (None, [_P]),
-        "ocg_workspace_bytes": (C.c_size_t, [C.c_int, C.c_int, C.c_int64, C.c_int64, C.c_int64, C.c_int, C.c_int]),
+        "ocg_workspace_bytes": (C.c_size_t, [_P, C.c_int, C.c_int, C.c_int64, C.c_int64, C.c_int64, C.c_int, C.c_int]),
         "ocg_workspace_init": (C.c_int, [_P, _P, C.c_size_t, _P]),
         "ocg_ag_gemm": (C.c_int, [_P, C.POINTER(_P), C.c_int, C.c_int, C.c_int64, C.c_int64, _P, C.c_int64,
                                   _P, _P, _P, C.c_size_t, C.POINTER(Config), _P]),
@@ -83,9 +87,11 @@ def _declare(lib):
         "ocg_signal": (C.c_int, [_P, C.c_int, C.c_uint32, _P]),
         "ocg_check": (C.c_int, [_P, _P]),
         "ocg_status_string": (C.c_char_p, [C.c_int]),
-        "ocg_plan_info": (C.c_int, [C.c_int, C.c_int, C.c_int, C.c_int64, C.c_int64, C.c_int64,
+        "ocg_plan_info": (C.c_int, [_P, C.c_int, C.c_int, C.c_int, C.c_int64, C.c_int64, C.c_int64,
                                     C.c_int, C.c_int, C.POINTER(Config), I64x8]),
-        "ocg_plan_task": (C.c_int, [C.c_int, C.c_int, C.c_int, C.c_int64, C.c_int64, C.c_int64,
+        "ocg_plan_ag": (C.c_int, [_P, C.c_int, C.c_int, C.c_int64, C.c_int64, C.c_int64,
+                                  C.POINTER(Config), I64x8]),
+        "ocg_plan_task": (C.c_int, [_P, C.c_int, C.c_int, C.c_int, C.c_int64, C.c_int64, C.c_int64,
                                     C.POINTER(Config), C.c_int64, I64x8]),
     }
     for name, (res, args) in sig.items():

@@ -17,6 +17,9 @@ struct ocg_handle_s {
   int cus;
   int resident[3][OCG_TILE_COUNT];  // per op and tile preset, 0 = not queried yet
   int resident_attn;                // attention kernel, 0 = not queried yet
+  int side_fits[OCG_TILE_COUNT];    // AG-GEMM kernel + side producer fit on a CU: 0 unknown, 1 yes, -1 no
+  hipStream_t side;                 // side stream of the SIDE transfer mode (default priority)
+  hipEvent_t fork, join;            // caller stream -> side stream -> caller stream
 };
 
 namespace {
@@ -27,13 +30,18 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+constexpr int kMinKslabCols = 256;    // K-slab widths are multiples of this
+constexpr int kSideKslabCols = 512;   // default K-slab width of the SIDE transfer mode
+
 // Workspace sections, sized for the worst plan a call of this shape can pick
-// (smallest slab, tile and strip sizes).
+// (smallest slab, K-slab, tile and strip sizes). max_slabs counts flags:
+// (slab, K-slab) pairs for AG-GEMM, slabs for the other gathers.
 WsLayout layout(int op, int R, int64_t m, int64_t K, int64_t N, int E, int topk) {
   WsLayout L{};
   size_t off = sizeof(WsHeader);
   int64_t rows = (op == OCG_OP_GEMM_RS) ? m : (int64_t)R * m;
-  L.max_slabs = (op == OCG_OP_GEMM_RS) ? 0 : (int)(R * cdiv((int)m, kMinSlabRows));
+  const int nks = (op == OCG_OP_AG_GEMM) ? cdiv((int)K, kMinKslabCols) : 1;
+  L.max_slabs = (op == OCG_OP_GEMM_RS) ? 0 : (int)(R * cdiv((int)m, kMinSlabRows)) * nks;
   L.max_rs_tiles = (op == OCG_OP_GEMM_RS) ? cdiv((int)rows, 128) * cdiv((int)N, 128) : 0;
   L.slab_cnt = off;
   off = align256(off + sizeof(uint32_t) * L.max_slabs);
@@ -114,11 +122,11 @@ int choose_moe_tile(int64_t T, int E, int topk) {
 }
 
 struct Resolved {
-  int tile, BM, BN, S, CT;
+  int tile, BM, BN, S, CT, KS, transfer;
 };
 
 int resolve(int op, int R, int64_t m, int64_t K, int64_t N, int E, int topk, const ocg_config& c, int cus,
-            Resolved* r) {
+            Resolved* r, bool side_ok = true) {
   int64_t M = (op == OCG_OP_GEMM_RS) ? m : R * m;
   if (op == OCG_OP_AG_GROUPED_GEMM)
     r->tile = c.tile < 0 ? choose_moe_tile(M, E, topk) : c.tile;
@@ -131,11 +139,27 @@ int resolve(int op, int R, int64_t m, int64_t K, int64_t N, int E, int topk, con
   r->BN = tile_bn(r->tile);
   r->S = c.slab_rows > 0 ? c.slab_rows : r->BM;
   if (r->S < kMinSlabRows) return OCG_ERR_INVALID_ARG;
+  // transfer mode and K-slab width (AG-GEMM; the other ops copy whole rows)
+  r->transfer = OCG_TRANSFER_INLINE;
+  r->KS = (int)K;
+  if (op == OCG_OP_AG_GEMM) {
+    if (c.transfer < OCG_TRANSFER_AUTO || c.transfer > OCG_TRANSFER_SIDE) return OCG_ERR_INVALID_ARG;
+    r->transfer = c.transfer == OCG_TRANSFER_AUTO ? (side_ok ? OCG_TRANSFER_SIDE : OCG_TRANSFER_INLINE) : c.transfer;
+    if (c.mode == OCG_MODE_GEMM_ONLY) r->transfer = OCG_TRANSFER_INLINE;   // no copies to place
+    if (c.kslab_cols < 0 || c.kslab_cols % kMinKslabCols) return OCG_ERR_INVALID_ARG;
+    if (c.kslab_cols > 0)
+      r->KS = c.kslab_cols;
+    else if (r->transfer == OCG_TRANSFER_SIDE)
+      r->KS = kSideKslabCols;
+    if (r->KS > K) r->KS = (int)K;
+  }
   if (c.copy_rows > 0) {
     r->CT = c.copy_rows;
   } else {
-    // about 256 KiB per copy task, a power of two dividing the slab
-    int64_t ct = (128 * 1024) / (K > 0 ? K : 1);
+    // a power of two dividing the slab, about 256 KiB per copy task -- 32 KiB
+    // for the side producer, whose workgroups keep 16 KiB in flight: small
+    // tasks spread each K-slab over many of them
+    int64_t ct = (r->transfer == OCG_TRANSFER_SIDE ? 16 * 1024 : 128 * 1024) / (r->KS > 0 ? r->KS : 1);
     int p2 = 1;
     while ((int64_t)p2 * 2 <= ct) p2 *= 2;
     r->CT = p2 < r->S ? p2 : r->S;
@@ -144,6 +168,27 @@ int resolve(int op, int R, int64_t m, int64_t K, int64_t N, int E, int topk, con
   if (r->CT < 1 || r->S % r->CT) return OCG_ERR_INVALID_ARG;
   if ((int64_t)r->CT * K * 2 >= ((int64_t)1 << 31)) return OCG_ERR_INVALID_ARG;  // one copy task < 2 GiB
   return OCG_OK;
+}
+
+// Whether the AG-GEMM kernel of `tile` (at its resident count per CU) and
+// one side producer workgroup fit on a compute unit together: per SIMD the
+// registers of the GEMM waves plus a producer wave within 512, LDS within
+// 160 KiB. Queried once per handle and tile.
+bool side_fits(ocg_handle h, int tile) {
+  if (!h || tile < 0 || tile >= OCG_TILE_COUNT) return false;
+  int& f = h->side_fits[tile];
+  if (f == 0) {
+    int vg = 0, lg = 0, vs = 0, ls = 0;
+    f = -1;
+    if (kernel_resources(OCG_OP_AG_GEMM, tile, &vg, &lg) && kernel_resources(-1, 0, &vs, &ls)) {
+      int& r = h->resident[OCG_OP_AG_GEMM][tile];
+      if (r == 0) r = resident_per_cu(OCG_OP_AG_GEMM, tile);
+      const int waves_per_simd = r * (tile_bm(tile) == 320 ? 2 : 1);
+      const int regs = waves_per_simd * ((vg + 7) & ~7) + ((vs + 7) & ~7);
+      if (regs <= 512 && r * lg + ls <= 160 * 1024) f = 1;
+    }
+  }
+  return f == 1;
 }
 
 // Rows per reduce strip: at most ~32 KiB of each partial, and few enough
@@ -234,6 +279,9 @@ Common make_common(void* ws, const ocg_config& c) {
   cm.trace = (ocg_trace_rec*)c.trace;
   cm.trace_cap = c.trace ? c.trace_capacity : 0;
   cm.fault_skip_slab = c.fault_skip_slab;
+  cm.copy_delay = c.copy_delay;
+  cm.xcd_remap = c.xcd_remap ? 1 : 0;
+  cm.total_wgs = 0;
   return cm;
 }
 
@@ -254,6 +302,8 @@ void ocg_config_default(ocg_config* c) {
   c->swizzle = 1;
   c->mode = OCG_MODE_FUSED;
   c->fault_skip_slab = -1;
+  c->transfer = OCG_TRANSFER_AUTO;
+  c->xcd_remap = 1;
 }
 
 int ocg_create(int device, ocg_handle* out) {
@@ -269,13 +319,31 @@ int ocg_create(int device, ocg_handle* out) {
   if (!h) return OCG_ERR_HIP;
   h->device = device;
   h->cus = prop.multiProcessorCount;
+  // the side stream and its events live on `device`
+  int prev = -1;
+  if (hipGetDevice(&prev) != hipSuccess) prev = -1;
+  bool ok = hipSetDevice(device) == hipSuccess && hipStreamCreateWithFlags(&h->side, hipStreamNonBlocking) == hipSuccess &&
+            hipEventCreateWithFlags(&h->fork, hipEventDisableTiming) == hipSuccess &&
+            hipEventCreateWithFlags(&h->join, hipEventDisableTiming) == hipSuccess;
+  if (prev >= 0) (void)hipSetDevice(prev);
+  if (!ok) {
+    ocg_destroy(h);
+    return OCG_ERR_HIP;
+  }
   *out = h;
   return OCG_OK;
 }
 
-void ocg_destroy(ocg_handle h) { delete h; }
+void ocg_destroy(ocg_handle h) {
+  if (!h) return;
+  if (h->join) (void)hipEventDestroy(h->join);
+  if (h->fork) (void)hipEventDestroy(h->fork);
+  if (h->side) (void)hipStreamDestroy(h->side);
+  delete h;
+}
 
-size_t ocg_workspace_bytes(int op, int R, int64_t m, int64_t K, int64_t N, int E, int topk) {
+size_t ocg_workspace_bytes(ocg_handle h, int op, int R, int64_t m, int64_t K, int64_t N, int E, int topk) {
+  (void)h;
   if (op < 0 || op > 4) return 0;
   if (op == OCG_OP_AG_ATTENTION) return attn_shape_ok(R, m, K, N) ? layout(op, R, m, 0, 0, 0, 0).total : 0;
   if (op == OCG_OP_MOE_COMBINE_RS) return combine_shape_ok(R, m, N, topk) ? layout(op, R, m, 0, N, 0, topk).total : 0;
@@ -298,6 +366,50 @@ int ocg_workspace_init(ocg_handle h, void* ws, size_t bytes, void* stream) {
   return e == hipSuccess ? OCG_OK : OCG_ERR_HIP;
 }
 
+// The AG-GEMM plan of a call: tile, slabs, K-slabs and transfer (resolve),
+// the rounds of tiles of the persistent grid (copy phases), the copy tickets
+// the GEMM kernel runs itself, and the two grids (producer 0 unless SIDE).
+// h = NULL plans for a 256-CU MI355X on which the producer fits.
+struct AgSetup {
+  Resolved rv;
+  AgPlan plan;
+  int ggrid, pgrid;
+};
+
+int ag_setup(ocg_handle h, int R, int local_rank, int64_t m, int64_t K, int64_t N, const ocg_config& cfg,
+             AgSetup* o) {
+  const int cus = h ? h->cus : 256;
+  const int tile0 = cfg.tile < 0 ? choose_tile(R * m, N, cus) : cfg.tile;
+  int st = resolve(OCG_OP_AG_GEMM, R, m, K, N, 0, 0, cfg, cus, &o->rv, h ? side_fits(h, tile0) : true);
+  if (st) return st;
+  if (h && o->rv.transfer == OCG_TRANSFER_SIDE && !side_fits(h, o->rv.tile)) return OCG_ERR_UNSUPPORTED_SHAPE;
+  int resident = 1;
+  if (h) {
+    int& r = h->resident[OCG_OP_AG_GEMM][o->rv.tile];
+    if (r == 0) r = resident_per_cu(OCG_OP_AG_GEMM, o->rv.tile);
+    resident = r;
+  } else if (o->rv.tile == OCG_TILE_128x128) {
+    resident = 2;   // two 128x128 workgroups fit on a CU (LDS)
+  }
+  const int tpr = cfg.grid > 0 ? cfg.grid : resident * cus;
+  AgPlan& p = o->plan;
+  p = make_ag_plan(R, local_rank, (int)m, (int)K, (int)N, o->rv.BM, o->rv.BN, o->rv.S, o->rv.CT,
+                   cfg.swizzle ? 1 : 0, cfg.mode, o->rv.KS, tpr);
+  const bool side = o->rv.transfer == OCG_TRANSFER_SIDE;
+  if (side) {
+    const int first = first_kslab_tickets(p);
+    p.n_inline = first < p.n_copy ? first : p.n_copy;
+  }
+  const int gtasks = p.n_inline + p.n_tiles;
+  o->ggrid = gtasks < tpr ? gtasks : tpr;
+  o->pgrid = 0;
+  if (p.n_copy > p.n_inline) {
+    const int pg = cfg.side_grid > 0 ? cfg.side_grid : cus;
+    o->pgrid = pg < p.n_copy - p.n_inline ? pg : p.n_copy - p.n_inline;
+  }
+  return OCG_OK;
+}
+
 int ocg_ag_gemm(ocg_handle h, const void* const* a_chunks, int R, int local_rank, int64_t m, int64_t K,
                 const void* b, int64_t N, void* a_gathered, void* c, void* ws, size_t ws_bytes,
                 const ocg_config* cfgp, void* stream) {
@@ -312,8 +424,8 @@ int ocg_ag_gemm(ocg_handle h, const void* const* a_chunks, int R, int local_rank
   WsLayout L = layout(OCG_OP_AG_GEMM, R, m, K, N, 0, 0);
   if (ws_bytes < L.total) return OCG_ERR_WORKSPACE_TOO_SMALL;
   if (!device_matches(h)) return OCG_ERR_INVALID_ARG;
-  Resolved rv;
-  int st = resolve(OCG_OP_AG_GEMM, R, m, K, N, 0, 0, cfg, h->cus, &rv);
+  AgSetup su;
+  int st = ag_setup(h, R, local_rank, m, K, N, cfg, &su);
   if (st) return st;
   AgArgs a{};
   for (int r = 0; r < R; ++r) a.chunks[r] = (const uint16_t*)a_chunks[r];
@@ -322,13 +434,24 @@ int ocg_ag_gemm(ocg_handle h, const void* const* a_chunks, int R, int local_rank
   a.c = (uint16_t*)c;
   a.slab_cnt = (uint32_t*)((char*)ws + L.slab_cnt);
   a.slab_flag = (uint32_t*)((char*)ws + L.slab_flag);
-  a.plan = make_ag_plan(R, local_rank, (int)m, (int)K, (int)N, rv.BM, rv.BN, rv.S, rv.CT, cfg.swizzle ? 1 : 0,
-                        cfg.mode);
-  if (a.plan.R * a.plan.bpr > L.max_slabs) return OCG_ERR_INVALID_ARG;
+  a.plan = su.plan;
+  if (a.plan.R * a.plan.bpr * a.plan.nks > L.max_slabs) return OCG_ERR_INVALID_ARG;
   a.cm = make_common(ws, cfg);
-  int tasks = a.plan.n_copy + a.plan.n_tiles;
-  int grid = grid_for(h, OCG_OP_AG_GEMM, rv.tile, tasks, cfg);
-  return launch_ag_gemm(a, rv.tile, grid, (hipStream_t)stream) == hipSuccess ? OCG_OK : OCG_ERR_HIP;
+  hipStream_t s = (hipStream_t)stream;
+  if (su.pgrid == 0)
+    return launch_ag_gemm(a, su.rv.tile, su.ggrid < 1 ? 1 : su.ggrid, s) == hipSuccess ? OCG_OK : OCG_ERR_HIP;
+  // SIDE: the GEMM kernel on the caller's stream, the producer on the side
+  // stream, both after the caller's earlier work; the caller's stream then
+  // waits for the producer. The last workgroup of either kernel resets the
+  // workspace counters.
+  a.cm.total_wgs = su.ggrid + su.pgrid;
+  if (hipEventRecord(h->fork, s) != hipSuccess || hipStreamWaitEvent(h->side, h->fork, 0) != hipSuccess)
+    return OCG_ERR_HIP;
+  if (su.ggrid > 0 && launch_ag_gemm(a, su.rv.tile, su.ggrid, s) != hipSuccess) return OCG_ERR_HIP;
+  if (launch_ag_side_copy(a, su.pgrid, h->side) != hipSuccess) return OCG_ERR_HIP;
+  if (hipEventRecord(h->join, h->side) != hipSuccess || hipStreamWaitEvent(s, h->join, 0) != hipSuccess)
+    return OCG_ERR_HIP;
+  return OCG_OK;
 }
 
 int ocg_gemm_rs(ocg_handle h, const void* A, const void* B, int64_t M, int64_t K, int64_t N, int R, int local_rank,
@@ -537,9 +660,10 @@ const char* ocg_status_string(int s) {
   return "unknown status";
 }
 
-int ocg_plan_info(int op, int R, int local_rank, int64_t m, int64_t K, int64_t N, int E, int topk,
+int ocg_plan_info(ocg_handle h, int op, int R, int local_rank, int64_t m, int64_t K, int64_t N, int E, int topk,
                   const ocg_config* cfgp, int64_t out[8]) {
   if (!out || op < 0 || op > 4) return OCG_ERR_INVALID_ARG;
+  const int cus = h ? h->cus : 256;   // no handle: a full MI355X
   if (op == OCG_OP_AG_ATTENTION) {
     if (!attn_shape_ok(R, m, K, N)) return OCG_ERR_UNSUPPORTED_SHAPE;
     if (local_rank < 0 || local_rank >= R) return OCG_ERR_INVALID_ARG;
@@ -563,7 +687,7 @@ int ocg_plan_info(int op, int R, int local_rank, int64_t m, int64_t K, int64_t N
     if (local_rank < 0 || local_rank >= R) return OCG_ERR_INVALID_ARG;
     const int64_t T = (int64_t)R * m;
     int cr, crl;
-    combine_rows(R, m, topk, 256, &crl, &cr);
+    combine_rows(R, m, topk, cus, &crl, &cr);
     const int n_lt = cdiv((int)m, crl);
     out[0] = -1;
     out[1] = out[2] = out[7] = 0;
@@ -581,18 +705,29 @@ int ocg_plan_info(int op, int R, int local_rank, int64_t m, int64_t K, int64_t N
   if (local_rank < 0 || local_rank >= R) return OCG_ERR_INVALID_ARG;
   ocg_config cfg = cfg_or_default(cfgp);
   Resolved rv;
-  int st = resolve(op, R, m, K, N, E, topk, cfg, 256, &rv);
-  if (st) return st;
+  AgSetup su;
+  if (op == OCG_OP_AG_GEMM) {
+    int st = ag_setup(h, R, local_rank, m, K, N, cfg, &su);
+    if (st) return st;
+    rv = su.rv;
+  } else {
+    int st = resolve(op, R, m, K, N, E, topk, cfg, cus, &rv);
+    if (st) return st;
+  }
   out[0] = rv.tile;
   out[1] = rv.BM;
   out[2] = rv.BN;
   out[3] = rv.S;
   out[4] = rv.CT;
   if (op == OCG_OP_GEMM_RS) {
-    RsPlan p = make_rs_plan(R, local_rank, (int)m, (int)K, (int)N, rv.BM, rv.BN, reduce_rows(m, R, N, 256), cfg.swizzle);
+    RsPlan p = make_rs_plan(R, local_rank, (int)m, (int)K, (int)N, rv.BM, rv.BN, reduce_rows(m, R, N, cus), cfg.swizzle);
     out[5] = p.n_red;
     out[6] = p.n_tiles;
     out[7] = p.RR;
+  } else if (op == OCG_OP_AG_GEMM) {
+    out[5] = su.plan.n_copy;
+    out[6] = su.plan.n_tiles;
+    out[7] = (int64_t)R * su.plan.bpr * su.plan.nks;
   } else {
     AgPlan p = make_ag_plan(R, local_rank, (int)m, (int)K, (int)N, rv.BM, rv.BN, rv.S, rv.CT, cfg.swizzle,
                             cfg.mode);
@@ -603,13 +738,33 @@ int ocg_plan_info(int op, int R, int local_rank, int64_t m, int64_t K, int64_t N
   return OCG_OK;
 }
 
-int ocg_plan_task(int op, int R, int local_rank, int64_t m, int64_t K, int64_t N, const ocg_config* cfgp,
+int ocg_plan_ag(ocg_handle h, int R, int local_rank, int64_t m, int64_t K, int64_t N, const ocg_config* cfgp,
+                int64_t out[8]) {
+  if (!out) return OCG_ERR_INVALID_ARG;
+  if (!shape_ok(R, m, K, N)) return OCG_ERR_UNSUPPORTED_SHAPE;
+  if (local_rank < 0 || local_rank >= R) return OCG_ERR_INVALID_ARG;
+  ocg_config cfg = cfg_or_default(cfgp);
+  AgSetup su;
+  int st = ag_setup(h, R, local_rank, m, K, N, cfg, &su);
+  if (st) return st;
+  for (int i = 0; i < 8; ++i) out[i] = 0;
+  out[0] = su.plan.KS;
+  out[1] = su.plan.nks;
+  out[2] = su.rv.transfer;
+  out[3] = su.ggrid;
+  out[4] = su.pgrid;
+  out[5] = su.plan.n_inline;
+  out[6] = su.plan.rpr;
+  return OCG_OK;
+}
+
+int ocg_plan_task(ocg_handle h, int op, int R, int local_rank, int64_t m, int64_t K, int64_t N, const ocg_config* cfgp,
                   int64_t ticket, int64_t desc[8]) {
   if (!desc) return OCG_ERR_INVALID_ARG;
   for (int i = 0; i < 8; ++i) desc[i] = -1;
   desc[0] = 0;
   int64_t info[8];
-  int st = ocg_plan_info(op, R, local_rank, m, K, N, 0, 0, cfgp, info);
+  int st = ocg_plan_info(h, op, R, local_rank, m, K, N, 0, 0, cfgp, info);
   if (st) return st;
   ocg_config cfg = cfg_or_default(cfgp);
   if (op == OCG_OP_AG_ATTENTION) {
@@ -662,8 +817,16 @@ int ocg_plan_task(int op, int R, int local_rank, int64_t m, int64_t K, int64_t N
     }
     return OCG_OK;
   }
-  AgPlan p = make_ag_plan(R, local_rank, (int)m, (int)K, (int)N, (int)info[1], (int)info[2], (int)info[3],
-                          (int)info[4], cfg.swizzle, cfg.mode);
+  AgPlan p;
+  if (op == OCG_OP_AG_GEMM) {
+    AgSetup su;
+    st = ag_setup(h, R, local_rank, m, K, N, cfg, &su);
+    if (st) return st;
+    p = su.plan;
+  } else {
+    p = make_ag_plan(R, local_rank, (int)m, (int)K, (int)N, (int)info[1], (int)info[2], (int)info[3], (int)info[4],
+                     cfg.swizzle, cfg.mode);
+  }
   if (ticket < 0 || ticket >= p.n_copy + (op == OCG_OP_AG_GEMM ? p.n_tiles : 0)) return OCG_OK;
   if (ticket < p.n_copy) {
     CopyDesc d = copy_desc(p, (int)ticket);
@@ -673,6 +836,7 @@ int ocg_plan_task(int op, int R, int local_rank, int64_t m, int64_t K, int64_t N
     desc[3] = d.row0;
     desc[4] = d.row1;
     desc[5] = d.slab;
+    desc[6] = d.kslab;
     return OCG_OK;
   }
   int rb, cb;

@@ -480,7 +480,7 @@ __global__ __launch_bounds__(kAThreads, 1) void ag_attention_kernel(AttnArgs arg
   int q = (int)s_bcast[3] % kXcds, tried = 0;
   uint32_t qt = 0;
   for (;;) {
-    const int v = next_tile(cm.hdr, p.n_tiles, &q, &tried, s_bcast, &qt);
+    const int v = next_tile(cm.hdr, p.n_tiles, &q, &tried, s_bcast, &qt, cm.xcd_remap);
     if (v < 0) break;
     attention_tile(args, smem, v, epoch, ((uint32_t)q << 16) | qt);
   }

@@ -380,6 +380,15 @@ __device__ __forceinline__ void stage_body(const Frags<BM, BN>& cur, Frags<BM, B
   lds_reads_done();
 }
 
+// Per-pair hook of the K loop: prefetch(k) runs at the start of pair k, before
+// its wait; check(k) after the wait and before the barrier that releases the
+// pair's loads (stages k+S-1 and k+S). NoHook does nothing; the AG-GEMM tiles
+// use them to wait on the flags of the K-slabs they are about to load.
+struct NoHook {
+  __device__ __forceinline__ void prefetch(int) {}
+  __device__ __forceinline__ void check(int) {}
+};
+
 // C tile += A[rows of t.rowp][0:K] x B[0:K][n0:n0+BN], K = 32 * t.nk (nk even).
 // Starts and ends with every wave past a barrier; LDS is free afterwards.
 //
@@ -396,8 +405,9 @@ __device__ __forceinline__ void stage_body(const Frags<BM, BN>& cur, Frags<BM, B
 // slot, which is never read again, so the per-step load count and the wait
 // are constants; in the last step the fragment reads fetch a stale slot whose
 // values are never used.
-template <int BM, int BN>
-__device__ __forceinline__ void mainloop(OCG_LDS char* smem, const TileCtx<BM, BN>& t, AccTile<BM, BN>& acc) {
+template <int BM, int BN, class Hook>
+__device__ __forceinline__ void mainloop(OCG_LDS char* smem, const TileCtx<BM, BN>& t, AccTile<BM, BN>& acc,
+                                         Hook& hook) {
   using G = Gemm<BM, BN>;
   constexpr int S = G::S;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -440,8 +450,10 @@ __device__ __forceinline__ void mainloop(OCG_LDS char* smem, const TileCtx<BM, B
     wr = (wr + G::STAGE == S * G::STAGE) ? 0u : wr + G::STAGE;
   };
   for (int k = 0; k < nk; k += 2) {
+    hook.prefetch(k);
     if constexpr (S >= 5) {
       vm_wait<(S - 4) * G::NDMA>();
+      hook.check(k);
       lds_barrier();
       step(k, f0, f1);
       step(k + 1, f1, f0);
@@ -451,6 +463,7 @@ __device__ __forceinline__ void mainloop(OCG_LDS char* smem, const TileCtx<BM, B
       // instead, for stage k+1 only, so the loads of stage k+2 stay in
       // flight and each stage has two steps to land, as with 5 slots.
       vm_wait<(S - 3) * G::NDMA>();
+      hook.check(k);
       lds_barrier();
       step(k, f0, f1);
       vm_wait<(S - 3) * G::NDMA>();
@@ -473,6 +486,12 @@ __device__ __forceinline__ void mainloop(OCG_LDS char* smem, const TileCtx<BM, B
 #pragma unroll
       for (int g = 0; g < G::FN; ++g) asm volatile("" : "+a"(acc.v[f][g]));
   }
+}
+
+template <int BM, int BN>
+__device__ __forceinline__ void mainloop(OCG_LDS char* smem, const TileCtx<BM, BN>& t, AccTile<BM, BN>& acc) {
+  NoHook h;
+  mainloop<BM, BN, NoHook>(smem, t, acc, h);
 }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {

@@ -25,10 +25,91 @@ namespace ocg {
 
 // ---------------------------------------------------------------- AG-GEMM
 
+// Direct-to-LDS 4-byte load of *g (agent-coherent: SC1, as a relaxed
+// agent-scope atomic load) into LDS address lds + 4 * lane.
+__device__ __forceinline__ void dma_flag(uint32_t lds, const uint32_t* g) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off sc1" ::"s"(lds), "v"(g) : "memory", "m0");
+}
+
+// consume_tile_wait per K-slab inside an AG-GEMM tile's K loop. The tile
+// depends on `ndeps` peer slabs (lane i of wave 0 holds the flag row of dep
+// i). K-slabs are confirmed in groups that double in size (kgroup_first):
+// pair k of the loop loads stages up to min(k + S, nk - 1), so before the
+// first pair that loads a stage of group g, wave 0 confirms the flags of
+// every (dep, K-slab of g), one lane each, and all waves then pass the
+// pair's barrier. The flags are read one or two pairs early (PD) by a
+// direct-to-LDS load, which the loop's vmcnt waits count: it has landed by
+// the check, so the check costs no memory round trip. A flag not yet set
+// (or a group of more than 64 flags) is polled by wave 0 before the barrier,
+// bounded as FlagWait. After seeing the flags, wave 0 invalidates the
+// non-coherent cache lines (buffer_inv sc1, the acquire half of the
+// agent-scope handshake; the load that observed the flags has completed) --
+// without the vmcnt(0) a compiler acquire fence adds, which would drain the
+// ring's loads in flight. The invalidate is not free (it drops the XCD L2's
+// non-coherent lines that the other tiles reuse), hence the doubling groups.
+template <int S, int PD>
+struct KslabHook {
+  uint64_t flagrow;          // wave 0 lane i < ndeps: address of slab_flag + dep_i * nks
+  OCG_LDS uint32_t* land;    // 64 words of LDS the prefetched flags land in
+  const Common* cm;
+  uint32_t epoch, wait_ticks;
+  int wave, lane, ndeps, spk, nks, nk;
+  int g, j0, j1, check_k, prefetch_k;   // next group: K-slabs [j0, j1)
+  bool prefetched;
+
+  // flag of lane L in the group: dep L / gs, K-slab j0 + L % gs (lanes past
+  // the last pair repeat pair 0)
+  __device__ __forceinline__ const uint32_t* lane_flag(int L) const {
+    const int gs = j1 - j0;
+    const int i = (L / gs < ndeps) ? L / gs : 0;
+    const int j = (L / gs < ndeps) ? j0 + L % gs : j0;
+    return (const uint32_t*)__shfl(flagrow, i) + j;
+  }
+  __device__ void schedule() {
+    prefetched = false;
+    j0 = kgroup_first(g);
+    if (j0 >= nks || j0 * spk > nk - 1) {
+      check_k = prefetch_k = 1 << 30;
+      return;
+    }
+    j1 = min(kgroup_first(g + 1), nks);
+    int kc = j0 * spk - S;
+    kc = kc < 0 ? 0 : (kc + 1) & ~1;
+    check_k = kc;
+    prefetch_k = (ndeps * (j1 - j0) <= 64) ? kc - 2 * PD : -1;
+  }
+  __device__ __forceinline__ void prefetch(int k) {
+    if (k == prefetch_k) {
+      if (wave == 0) dma_flag(lds_u32(land), lane_flag(lane));
+      prefetched = true;
+    }
+  }
+  __device__ __forceinline__ void check(int k) {
+    if (k != check_k) return;
+    if (wave == 0) {
+      bool ok = false;
+      if (prefetched) ok = __ballot(land[lane] != epoch) == 0;
+      if (ok) {
+        asm volatile("buffer_inv sc1" ::: "memory");
+      } else {
+        const uint64_t t0 = now_ticks();
+        FlagWait w(cm->timeout_ticks);
+        for (int i = 0; i < ndeps; ++i)
+          for (int j = j0; j < j1; ++j) w((const uint32_t*)__shfl(flagrow, i) + j, epoch);
+        uint32_t seen;
+        w.finish(*cm, &seen);
+        wait_ticks += (uint32_t)(now_ticks() - t0);
+      }
+    }
+    ++g;
+    schedule();
+  }
+};
+
 template <int BM, int BN>
 __global__ __launch_bounds__((Gemm<BM, BN>::NT), 1) void ag_gemm_kernel(AgArgs args) {
   using G = Gemm<BM, BN>;
-  __shared__ __attribute__((aligned(1024))) char smem_raw[G::LDS_BYTES];
+  __shared__ __attribute__((aligned(1024))) char smem_raw[G::LDS_BYTES + 256];
   __shared__ uint32_t s_bcast[8];
   OCG_LDS char* smem = (OCG_LDS char*)smem_raw;
   const AgPlan& p = args.plan;
@@ -37,10 +118,12 @@ __global__ __launch_bounds__((Gemm<BM, BN>::NT), 1) void ag_gemm_kernel(AgArgs a
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
 
-  // copy tasks
+  // copy tasks: all of them, or (SIDE transfer) the first K-slab of the
+  // first phase, so the first tiles need not wait for the side producer to
+  // start; the producer takes the rest
   for (;;) {
     const uint32_t u = next_ticket(&cm.hdr->ticket, s_bcast);
-    if ((int)u >= p.n_copy) break;
+    if ((int)u >= p.n_inline) break;
     run_copy_task<G::NT>(p, args.chunks, args.a_gathered, args.slab_cnt, args.slab_flag, (int)u, epoch, cm);
   }
   // GEMM tiles
@@ -50,19 +133,29 @@ __global__ __launch_bounds__((Gemm<BM, BN>::NT), 1) void ag_gemm_kernel(AgArgs a
   t.brs = make_rsrc(args.b, (uint32_t)((size_t)p.K * p.N * 2));
   t.N = p.N;
   t.nk = p.K / BKS;
+  const int spk = p.KS / BKS;                       // stages per K-slab (>= 8)
   for (;;) {
-    const int v = next_tile(cm.hdr, p.n_tiles, &q, &tried, s_bcast, &qt);
+    const int v = next_tile(cm.hdr, p.n_tiles, &q, &tried, s_bcast, &qt, cm.xcd_remap);
     if (v < 0) break;
-    const uint64_t t0 = now_ticks();
+    const uint64_t t0 = now_ticks(), c0 = now_cycles();
     int rb, cb;
     tile_of(p.n_rb, p.n_cb, p.rb0, v, &rb, &cb);
     const int r0 = rb * BM, r1 = min(r0 + BM, p.M);
-    int nwait = 0;
+    // peer slabs the tile reads; wave 0 lane i keeps the flag row of dep i
+    int ndeps = 0;
+    uint64_t myrow = (uint64_t)args.slab_flag;
+    if (p.mode == 0)
+      for_each_dep_slab(p.m, p.S, p.bpr, p.local, r0, r1, [&](int sl) {
+        if (ndeps == 0 || ndeps == lane) myrow = (uint64_t)(args.slab_flag + (size_t)sl * p.nks);
+        ++ndeps;
+      });
     uint32_t seen = 0;
-    if (p.mode == 0 && wave == 0) {
+    if (ndeps > 0 && wave == 0) {
+      // consume_tile_wait on K-slab 0 (group 0), which holds every stage the
+      // prologue loads
       FlagWait w(cm.timeout_ticks);
-      for_each_dep_slab(p.m, p.S, p.bpr, p.local, r0, r1, [&](int s) { w(&args.slab_flag[s], epoch); });
-      nwait = w.finish(cm, &seen);
+      for (int i = 0; i < ndeps; ++i) w((const uint32_t*)__shfl(myrow, i), epoch);
+      w.finish(cm, &seen);
     }
     const uint64_t t1 = now_ticks();
     __syncthreads();
@@ -78,14 +171,48 @@ __global__ __launch_bounds__((Gemm<BM, BN>::NT), 1) void ag_gemm_kernel(AgArgs a
     const int n0 = cb * BN;
     t.n0 = n0;
     AccTile<BM, BN> acc;
-    mainloop<BM, BN>(smem, t, acc);
+    KslabHook<G::S, (G::S >= 6 ? 2 : 1)> hook;
+    hook.flagrow = myrow;
+    hook.land = (OCG_LDS uint32_t*)(smem + G::LDS_BYTES);
+    hook.cm = &cm;
+    hook.epoch = epoch;
+    hook.wait_ticks = 0;
+    hook.wave = wave;
+    hook.lane = lane;
+    hook.ndeps = ndeps;
+    hook.spk = spk;
+    hook.nks = ndeps > 0 ? p.nks : 0;   // no dependency: nothing to check
+    hook.nk = t.nk;
+    hook.g = 1;
+    hook.schedule();
+    mainloop<BM, BN>(smem, t, acc, hook);
     stage_c<BM, BN>(smem, acc);
     for_each_c_chunk<BM, BN>(smem, [&](int row, int col, u32x4_t val) {
       if (r0 + row < p.M && n0 + col < p.N) gstore16(args.c + (size_t)(r0 + row) * p.N + n0 + col, val);
     });
-    trace_task(cm, (uint32_t)(p.n_copy + v), 2, rb, cb, nwait, 0, epoch, t0, t1, seen, ((uint32_t)q << 16) | qt);
+    trace_task(cm, (uint32_t)(p.n_copy + v), 2, rb, cb, ndeps, 0, epoch, t0, t1, seen, ((uint32_t)q << 16) | qt, c0,
+               hook.wait_ticks);
   }
-  finish(cm.hdr, epoch);
+  finish(cm.hdr, epoch, cm.total_wgs);
+}
+
+// Side producer of the AllGather (transfer mode SIDE): the copy tasks of an
+// ocg_ag_gemm call, run by a small kernel on a second stream while the GEMM
+// kernel's tiles compute on the same compute units. It uses no LDS beyond
+// the ticket broadcast and at most 40 registers per lane (the GEMM wave of a
+// SIMD leaves that many of the 512 free), so one of its workgroups fits on
+// every compute unit next to a GEMM workgroup; its copies never wait.
+__global__ __launch_bounds__(kSideThreads) void ag_side_copy_kernel(AgArgs args) {
+  __shared__ uint32_t s_bcast[8];
+  const Common& cm = args.cm;
+  const uint32_t epoch = read_epoch(cm.hdr, s_bcast);
+  for (;;) {
+    const int u = args.plan.n_inline + (int)next_ticket(&cm.hdr->side_ticket, s_bcast);
+    if (u >= args.plan.n_copy) break;
+    run_copy_task<kSideThreads, 4, true>(args.plan, args.chunks, args.a_gathered, args.slab_cnt, args.slab_flag, u,
+                                         epoch, cm);
+  }
+  finish(cm.hdr, epoch, cm.total_wgs);
 }
 
 // ---------------------------------------------------------------- GEMM-RS
@@ -154,7 +281,7 @@ __global__ __launch_bounds__((Gemm<BM, BN>::NT), 1) void gemm_rs_kernel(RsArgs a
   t.N = p.N;
   t.nk = p.K / BKS;
   for (;;) {
-    const int v = next_tile(cm.hdr, p.n_tiles, &q, &tried, s_bcast, &qt);
+    const int v = next_tile(cm.hdr, p.n_tiles, &q, &tried, s_bcast, &qt, cm.xcd_remap);
     if (v < 0) break;
     const uint64_t t0 = now_ticks();
     int rb, cb;
@@ -409,7 +536,7 @@ __global__ __launch_bounds__((Gemm<BM, BN>::NT), 1) void moe_gemm_kernel(MoeArgs
   t.N = p.N;
   t.nk = p.K / BKS;
   for (;;) {
-    const int v = next_tile(cm.hdr, n_tiles, &q, &tried, s_bcast, &qt);
+    const int v = next_tile(cm.hdr, n_tiles, &q, &tried, s_bcast, &qt, cm.xcd_remap);
     if (v < 0) break;
     const uint64_t t0 = now_ticks();
     const int32_t* L = args.lut + (size_t)v * 8;
@@ -592,6 +719,33 @@ hipError_t launch_ag_gemm(const AgArgs& a, int tile, int grid, hipStream_t s) {
     case OCG_TILE_256x256: return ag_launch<256, 256>(a, grid, s);
   }
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_ag_side_copy(const AgArgs& a, int grid, hipStream_t s) {
+  hipLaunchKernelGGL(ag_side_copy_kernel, dim3(grid), dim3(kSideThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+template <class K>
+static bool attrs(K kern, int* vgprs, int* lds) {
+  hipFuncAttributes fa;
+  if (hipFuncGetAttributes(&fa, reinterpret_cast<const void*>(kern)) != hipSuccess) return false;
+  *vgprs = fa.numRegs;
+  *lds = (int)fa.sharedSizeBytes;
+  return true;
+}
+
+// op < 0: the side producer kernel; else the AG-GEMM kernel of `tile`.
+bool kernel_resources(int op, int tile, int* vgprs, int* lds) {
+  if (op < 0) return attrs(ag_side_copy_kernel, vgprs, lds);
+  switch (tile) {
+    case OCG_TILE_256x224: return attrs(ag_gemm_kernel<256, 224>, vgprs, lds);
+    case OCG_TILE_128x224: return attrs(ag_gemm_kernel<128, 224>, vgprs, lds);
+    case OCG_TILE_128x256: return attrs(ag_gemm_kernel<128, 256>, vgprs, lds);
+    case OCG_TILE_128x128: return attrs(ag_gemm_kernel<128, 128>, vgprs, lds);
+    case OCG_TILE_256x256: return attrs(ag_gemm_kernel<256, 256>, vgprs, lds);
+  }
+  return false;
 }
 
 hipError_t launch_gemm_rs(const RsArgs& a, int tile, int grid, hipStream_t s) {

@@ -29,12 +29,13 @@ inline bool moe_tile_ok(int t) {
 // Workspace header (first 256 bytes of every workspace).
 struct WsHeader {
   uint32_t ticket;     // next ticket of the running persistent kernel
-  uint32_t done;       // workgroups that finished the running kernel
+  uint32_t done;       // workgroups (of every kernel of the call) that finished
   uint32_t epoch;      // epoch of the last completed call (flags carry epochs)
   uint32_t error;      // bit 0: a flag wait timed out
   uint32_t n_tiles;    // MoE: grouped tiles of the current routing
   uint32_t xtick[8];   // next ticket of each XCD's tile queue
-  uint32_t pad[51];
+  uint32_t side_ticket;  // next copy ticket of the side producer kernel
+  uint32_t pad[50];
 };
 static_assert(sizeof(WsHeader) == 256, "header is 256 bytes");
 
@@ -49,7 +50,10 @@ struct Common {
   uint64_t timeout_ticks;   // bound on each wait, 100 MHz ticks
   ocg_trace_rec* trace;
   uint32_t trace_cap;
-  int fault_skip_slab;
+  int fault_skip_slab;      // flag index never published (test hook), -1 = off
+  uint32_t copy_delay;      // s_sleep 127 rounds before each copy task (test hook)
+  int xcd_remap;            // 1 = per-XCD tile queues, 0 = one queue
+  int total_wgs;            // workgroups of every kernel of the call (finish counter)
 };
 
 struct AgArgs {
@@ -57,9 +61,9 @@ struct AgArgs {
   const uint16_t* b;
   uint16_t* a_gathered;
   uint16_t* c;
-  uint32_t* slab_cnt;
-  uint32_t* slab_flag;
-  AgPlan plan;
+  uint32_t* slab_cnt;           // [flags]: copy tasks done per (slab, K-slab)
+  uint32_t* slab_flag;          // [flags]: epoch once the (slab, K-slab) has landed
+  AgPlan plan;                  // copy tickets >= plan.n_inline: the side producer's
   Common cm;
 };
 
@@ -135,6 +139,12 @@ struct RouteArgs {
 
 // Launchers (kernels.hip). Return hipSuccess or the launch error.
 hipError_t launch_ag_gemm(const AgArgs& a, int tile, int grid, hipStream_t s);
+// Side producer of ocg_ag_gemm's copy tasks (co-resident with the GEMM kernel).
+hipError_t launch_ag_side_copy(const AgArgs& a, int grid, hipStream_t s);
+constexpr int kSideThreads = 256;     // 4 waves: one per SIMD of a compute unit
+// Registers (VGPRs incl. accumulation registers) and LDS bytes of a kernel
+// per workgroup; false if the query fails.
+bool kernel_resources(int op, int tile, int* vgprs, int* lds_bytes);
 hipError_t launch_gemm_rs(const RsArgs& a, int tile, int grid, hipStream_t s);
 hipError_t launch_moe(const RouteArgs& r, const MoeArgs& a, int tile, int grid, hipStream_t s);
 hipError_t launch_moe_combine_rs(const CombArgs& a, int grid, hipStream_t s);

@@ -8,10 +8,22 @@
 // access and transfers so transfers line up with compute.
 //
 // AG-GEMM plan. Gathered rows M = R*m; rank chunk c owns rows [c*m, (c+1)*m).
-// A chunk is cut into slabs of S rows (one published flag each) and into copy
-// tasks of CT rows (S % CT == 0). Copy tasks are numbered 0..n_copy-1 in the
-// chunk sequence local+1, local+2, ..., local+R-1, local (swizzled) or
-// 0..R-1 (natural) and handed out by one global ticket counter. GEMM tiles are
+// A chunk is cut into slabs of S rows and its columns into K-slabs of KS
+// columns (the last one may be shorter); one flag is published per (slab,
+// K-slab), at index slab * nks + kslab. Copy tasks move CT rows (S % CT == 0)
+// of one K-slab. The chunk sequence is local+1, local+2, ..., local+R-1,
+// local (swizzled) or 0..R-1 (natural); when swizzled its peer chunks are cut
+// into phases by the round of tiles that first reads them (rows per round
+// rpr: the persistent grid's tiles cover rpr gathered rows of the rotated
+// order per round), and the local chunk, which no tile waits on, comes last.
+// Copy tickets run phase by phase, K-slab by K-slab within a phase, and over
+// the phase's chunks and their pieces within a K-slab. Tickets below
+// n_inline are taken by the GEMM kernel's own workgroups before their tiles;
+// the rest by the side producer kernel (SIDE transfer; n_inline = n_copy
+// otherwise). With one K-slab (KS = K) this is the plain per-slab plan; with
+// several, a tile can start on the first columns of a peer's rows while
+// later columns are still being copied, and it waits on each K-slab's flag
+// before its loads of that K-slab. GEMM tiles are
 // numbered 0..n_tiles-1 in grouped order: row blocks rotated to start at the
 // block holding the local chunk's first row, taken in groups of kGroup, each
 // group walked column block by column block. Tiles are cut into batches of
@@ -36,25 +48,50 @@ OCG_HD int cdiv(int a, int b) { return (a + b - 1) / b; }
 
 struct AgPlan {
   int R, local, m, M, K, N;
-  int BM, BN, S, CT;
+  int BM, BN, S, CT, KS;
   int swizzle, mode;
-  int n_rb, n_cb, bpr, n_tpc, n_copy, n_tiles, rb0;
+  int n_rb, n_cb, bpr, n_tpc, nks, n_copy, n_tiles, rb0;
+  int rpr;        // gathered rows per round of tiles (copy phases)
+  int n_inline;   // copy tickets the GEMM kernel runs itself (the rest: side producer)
 };
 
-// mode: 0 fused, 1 gemm only, 2 copy only
+// Copy phase of position q of the chunk sequence: swizzled, the peers by the
+// round whose tiles first read them (the rotated order starts at the local
+// chunk), the local chunk last; natural order, one phase.
+OCG_HD int copy_phase(const AgPlan& p, int q) {
+  if (!p.swizzle) return 0;
+  if (q == p.R - 1) return 1 << 20;
+  return (int)(((long long)(q + 1) * p.m) / p.rpr);
+}
+
+// mode: 0 fused, 1 gemm only, 2 copy only. KS <= 0 or KS >= K: one K-slab.
+// tpr: tiles per round (the persistent grid); 0 = all tiles in one round.
 OCG_HD AgPlan make_ag_plan(int R, int local, int m, int K, int N, int BM, int BN, int S, int CT,
-                           int swizzle, int mode) {
+                           int swizzle, int mode, int KS = 0, int tpr = 0) {
   AgPlan p;
   p.R = R; p.local = local; p.m = m; p.M = R * m; p.K = K; p.N = N;
   p.BM = BM; p.BN = BN; p.S = S; p.CT = CT; p.swizzle = swizzle; p.mode = mode;
+  p.KS = (KS <= 0 || KS > K) ? K : KS;
   p.n_rb = cdiv(p.M, BM);
   p.n_cb = cdiv(N, BN);
   p.bpr = cdiv(m, S);
   p.n_tpc = cdiv(m, CT);
-  p.n_copy = (mode == 1) ? 0 : R * p.n_tpc;
+  p.nks = cdiv(K, p.KS);
+  p.n_copy = (mode == 1) ? 0 : R * p.n_tpc * p.nks;
   p.n_tiles = (mode == 2) ? 0 : p.n_rb * p.n_cb;
   p.rb0 = swizzle ? (int)(((long long)local * m) / BM) : 0;
+  const int rb_per_round = tpr > 0 ? tpr / p.n_cb : p.n_rb;
+  p.rpr = (rb_per_round > 0 ? rb_per_round : 1) * BM;
+  p.n_inline = p.n_copy;
   return p;
+}
+
+// Copy tickets of the first phase's first K-slab (what the GEMM kernel
+// copies itself under the SIDE transfer before its tiles start).
+OCG_HD int first_kslab_tickets(const AgPlan& p) {
+  int q1 = 0;
+  while (q1 < p.R && copy_phase(p, q1) == copy_phase(p, 0)) ++q1;
+  return q1 * p.n_tpc;
 }
 
 // Chunk copied at position q of the copy sequence.
@@ -63,24 +100,52 @@ OCG_HD int copy_chunk(const AgPlan& p, int q) {
   return (q < p.R - 1) ? (p.local + 1 + q) % p.R : p.local;
 }
 
+// Copy task: gathered rows [row0, row1) x columns [k0, k1) of one chunk;
+// completes part of flag `flag` = slab * nks + kslab.
 struct CopyDesc {
-  int chunk, piece, row0, row1, slab;
+  int chunk, piece, row0, row1, slab, kslab, k0, k1, flag;
 };
 
 OCG_HD CopyDesc copy_desc(const AgPlan& p, int u) {
   CopyDesc d;
-  int q = u / p.n_tpc;
-  d.piece = u - q * p.n_tpc;
-  d.chunk = copy_chunk(p, q);
+  // the phase holding ticket u: sequence positions [q0, q1)
+  int q0 = 0, base = 0;
+  for (;;) {
+    int q1 = q0 + 1;
+    while (q1 < p.R && copy_phase(p, q1) == copy_phase(p, q0)) ++q1;
+    const int n = (q1 - q0) * p.n_tpc * p.nks;
+    if (u < base + n || q1 >= p.R) {
+      const int per_ks = (q1 - q0) * p.n_tpc;
+      const int w = u - base;
+      d.kslab = w / per_ks;
+      const int r = w - d.kslab * per_ks;
+      const int q = q0 + r / p.n_tpc;
+      d.piece = r - (q - q0) * p.n_tpc;
+      d.chunk = copy_chunk(p, q);
+      break;
+    }
+    base += n;
+    q0 = q1;
+  }
   int r0 = d.piece * p.CT;
   int r1 = r0 + p.CT < p.m ? r0 + p.CT : p.m;
   d.row0 = d.chunk * p.m + r0;
   d.row1 = d.chunk * p.m + r1;
   d.slab = d.chunk * p.bpr + r0 / p.S;
+  d.k0 = d.kslab * p.KS;
+  d.k1 = d.k0 + p.KS < p.K ? d.k0 + p.KS : p.K;
+  d.flag = d.slab * p.nks + d.kslab;
   return d;
 }
 
-// Copy tasks that complete slab `slab` (global id chunk*bpr + s).
+// K-slabs are confirmed by the tiles in groups that double in size: group g
+// holds K-slabs [2^g - 1, 2^(g+1) - 1) (clipped to nks), so a tile that
+// streams K pays one acquire per group instead of one per K-slab; the copy
+// front keeps ahead because the copies run K-slab by K-slab from the start.
+OCG_HD int kgroup_first(int g) { return (1 << g) - 1; }
+
+// Copy tasks that complete slab `slab` (global id chunk*bpr + s) in one
+// K-slab.
 OCG_HD int slab_target(int m, int S, int CT, int bpr, int slab) {
   int s = slab % bpr;
   int per = S / CT;

@@ -30,6 +30,8 @@ __device__ __forceinline__ u32x4_t gload16(const void* p) { return *(gcptr16)p; 
 __device__ __forceinline__ void gstore16(void* p, u32x4_t v) { *(gptr16)p = v; }
 
 __device__ __forceinline__ uint64_t now_ticks() { return __builtin_amdgcn_s_memrealtime(); }
+// Shader-clock cycle counter (its rate follows the compute-unit clock).
+__device__ __forceinline__ uint64_t now_cycles() { return __builtin_amdgcn_s_memtime(); }
 
 __device__ __forceinline__ uint32_t xcc_id() {
   uint32_t v;
@@ -92,22 +94,29 @@ __device__ __forceinline__ void store16_agent(__amdgpu_buffer_rsrc_t rs, uint32_
 
 // produce_tile_notify for copy tasks: called by every thread after its
 // agent-coherent stores; returns (to thread 0) whether this task published
-// the slab flag (the last of the slab's copy tasks does).
-__device__ __forceinline__ bool publish_slab(uint32_t* cnt, uint32_t* flag, int slab, int target, uint32_t epoch,
+// flag `f` (the last of its copy tasks does).
+__device__ __forceinline__ bool publish_slab(uint32_t* cnt, uint32_t* flag, int f, int target, uint32_t epoch,
                              const Common& cm) {
   drain_stores();
   __syncthreads();
   bool published = false;
   if (threadIdx.x == 0) {
-    uint32_t old = __hip_atomic_fetch_add(&cnt[slab], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    uint32_t old = __hip_atomic_fetch_add(&cnt[f], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if ((int)old + 1 == target) {
-      __hip_atomic_store(&cnt[slab], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (slab != cm.fault_skip_slab)
-        __hip_atomic_store(&flag[slab], epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(&cnt[f], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (f != cm.fault_skip_slab)
+        __hip_atomic_store(&flag[f], epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       published = true;
     }
   }
   return published;
+}
+
+// Test hook: hold a copy task back by `rounds` x s_sleep 127 (64 x 127
+// shader cycles each) before it moves any data, so the flags it completes
+// are published late and dependent tiles really wait.
+__device__ __forceinline__ void copy_delay(uint32_t rounds) {
+  for (uint32_t i = 0; i < rounds; ++i) __builtin_amdgcn_s_sleep(127);
 }
 
 // ---------------------------------------------------------------- copy
@@ -115,9 +124,8 @@ __device__ __forceinline__ bool publish_slab(uint32_t* cnt, uint32_t* flag, int 
 // Pull `n16` 16-byte granules from src to dst (agent-coherent stores) with
 // all NT threads of the workgroup, 16 granules in flight per thread.
 // n16 * 16 < 2^31.
-template <int NT = kThreads>
+template <int NT = kThreads, int U = 16>
 __device__ __forceinline__ void copy_granules(const uint16_t* src, uint16_t* dst, uint32_t n16) {
-  constexpr int U = 16;
   const u32x4_t* s = (const u32x4_t*)src;
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(dst, n16 * 16u);
   uint32_t i = threadIdx.x;
@@ -131,25 +139,92 @@ __device__ __forceinline__ void copy_granules(const uint16_t* src, uint16_t* dst
   for (; i < n16; i += NT) store16_agent(rs, i * 16u, gload16(s + i));
 }
 
-// One copy task of the AllGather (pull mode): rows [row0, row1) of the
-// gathered matrix come from rank `chunk`'s shard.
-template <int NT = kThreads>
+// Pull a rows x (gpr granules) block: row i of src (row stride `stride`
+// elements) to row i of dst (same stride), agent-coherent stores, U granules
+// in flight per thread, consecutive threads on consecutive granules of a row.
+// The block spans ((rows - 1) * stride + gpr * 8) * 2 < 2^31 bytes.
+template <int NT, int U>
+__device__ __forceinline__ void copy_block(const uint16_t* src, uint16_t* dst, uint32_t rows, uint32_t gpr,
+                                           uint32_t stride) {
+  const uint32_t n16 = rows * gpr;
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(dst, ((rows - 1) * stride + gpr * 8) * 2u);
+  // every round issues all of its (up to U) loads before its stores, the
+  // last, partial round included
+  for (uint32_t i = threadIdx.x; i < n16; i += (uint32_t)U * NT) {
+    u32x4_t v[U];
+    uint32_t off[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint32_t j = i + u * NT, r = j / gpr;
+      off[u] = r * stride + (j - r * gpr) * 8;
+      if (j < n16) v[u] = gload16(src + off[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (i + u * NT < n16) store16_agent(rs, off[u] * 2u, v[u]);
+  }
+}
+
+// The same rectangle with few registers, for the side producer: source and
+// destination through buffer descriptors (32-bit lane offsets), lane
+// positions stepped without division, and the descriptors' range checks in
+// place of per-granule bounds tests (a position past the last row lies past
+// the rectangle's last byte: loads return zeros, stores are dropped).
+// gpr * 8 <= stride; offsets stay below 2^32.
+template <int NT, int U>
+__device__ __forceinline__ void copy_rect(const uint16_t* src, uint16_t* dst, uint32_t rows, uint32_t gpr,
+                                          uint32_t stride) {
+  const uint32_t ext = ((rows - 1) * stride + gpr * 8) * 2u;
+  const __amdgpu_buffer_rsrc_t ss = make_rsrc(src, ext), ds = make_rsrc(dst, ext);
+  const uint32_t n16 = rows * gpr, dr = NT / gpr, dg = NT % gpr;
+  uint32_t r = threadIdx.x / gpr, g = threadIdx.x % gpr;
+  for (uint32_t base = 0; base < n16; base += (uint32_t)U * NT) {
+    uint32_t off[U];
+    u32x4_t v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      off[u] = (r * stride + g * 8) * 2u;
+      v[u] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(ss, (int)off[u], 0, 0));
+      r += dr;
+      g += dg;
+      if (g >= gpr) {
+        g -= gpr;
+        ++r;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) store16_agent(ds, off[u], v[u]);
+  }
+}
+
+// One copy task of the AllGather (pull mode): rows [row0, row1) x columns
+// [k0, k1) of the gathered matrix come from rank `chunk`'s shard; the last of
+// the tasks of a (slab, K-slab) publishes its flag.
+// LEAN: the side producer's form (copy_rect, few registers).
+template <int NT = kThreads, int U = 16, bool LEAN = false>
 __device__ __forceinline__ void run_copy_task(const AgPlan& p, const uint16_t* const* chunks, uint16_t* a_gathered,
                               uint32_t* slab_cnt, uint32_t* slab_flag, int u, uint32_t epoch,
                               const Common& cm) {
-  uint64_t t0 = now_ticks();
-  CopyDesc d = copy_desc(p, u);
-  const uint16_t* src = chunks[d.chunk] + (size_t)(d.row0 - d.chunk * p.m) * p.K;
-  uint16_t* dst = a_gathered + (size_t)d.row0 * p.K;
-  copy_granules<NT>(src, dst, (uint32_t)((size_t)(d.row1 - d.row0) * p.K / 8));
-  int target = slab_target(p.m, p.S, p.CT, p.bpr, d.slab);
-  bool pub = publish_slab(slab_cnt, slab_flag, d.slab, target, epoch, cm);
+  const uint64_t t0 = now_ticks(), c0 = now_cycles();
+  const CopyDesc d = copy_desc(p, u);
+  copy_delay(cm.copy_delay * (uint32_t)(d.kslab + 1));   // later K-slabs land later
+  const uint16_t* src = chunks[d.chunk] + (size_t)(d.row0 - d.chunk * p.m) * p.K + d.k0;
+  uint16_t* dst = a_gathered + (size_t)d.row0 * p.K + d.k0;
+  if constexpr (LEAN)
+    copy_rect<NT, U>(src, dst, (uint32_t)(d.row1 - d.row0), (uint32_t)(d.k1 - d.k0) / 8, (uint32_t)p.K);
+  else if (d.k1 - d.k0 == p.K)
+    copy_granules<NT, U>(src, dst, (uint32_t)((size_t)(d.row1 - d.row0) * p.K / 8));
+  else
+    copy_block<NT, U>(src, dst, (uint32_t)(d.row1 - d.row0), (uint32_t)(d.k1 - d.k0) / 8, (uint32_t)p.K);
+  const int target = slab_target(p.m, p.S, p.CT, p.bpr, d.slab);
+  const bool pub = publish_slab(slab_cnt, slab_flag, d.flag, target, epoch, cm);
   if (threadIdx.x == 0 && cm.trace && (uint32_t)u < cm.trace_cap) {
     ocg_trace_rec* r = cm.trace + u;
-    uint64_t t1 = now_ticks();
-    r->ticket = u; r->kind = 1; r->a = d.chunk; r->b = d.piece; r->c = d.slab; r->d = pub;
+    const uint64_t t1 = now_ticks();
+    r->ticket = u; r->kind = 1; r->a = d.chunk; r->b = d.piece; r->c = d.flag; r->d = (pub ? 1u : 0u) | (LEAN ? 2u : 0u);
     r->hw = (xcc_id() << 16) | blockIdx.x; r->epoch = epoch;
-    r->t_start = t0; r->t_ready = t1; r->t_end = t1; r->flag_seen = 0; r->queue = 0;
+    r->t_start = t0; r->t_ready = t1; r->t_end = t1; r->flag_seen = 0; r->queue = d.kslab;
+    r->cycles = now_cycles() - c0; r->wait_ticks = 0; r->pad = 0;
   }
 }
 
@@ -180,8 +255,15 @@ __device__ __forceinline__ uint32_t next_ticket(uint32_t* counter, uint32_t* s_b
 // tickets only grow within a launch -- and the search moves to the next of
 // them; -1 once none is left. `*tried` is unused (kept for the call sites).
 __device__ __forceinline__ int next_tile(WsHeader* hdr, int n_tiles, int* q, int* tried, uint32_t* s_bcast,
-                                         uint32_t* t_out) {
+                                         uint32_t* t_out, int xcd_remap = 1) {
   (void)tried;
+  if (!xcd_remap) {
+    // ablation: one queue (queue 0's ticket) in plain tile order
+    const uint32_t t = next_ticket(&hdr->xtick[0], s_bcast);
+    *q = 0;
+    *t_out = t;
+    return (int)t < n_tiles ? (int)t : -1;
+  }
   for (;;) {
     const uint32_t t = next_ticket(&hdr->xtick[*q], s_bcast);
     const int v = xcd_tile(*q, (int)t, n_tiles);
@@ -210,13 +292,17 @@ __device__ __forceinline__ int next_tile(WsHeader* hdr, int n_tiles, int* q, int
 // Last workgroup out resets the counters and records the epoch. Relaxed
 // atomics suffice: a workgroup arrives here only after its last ticket
 // fetch returned (its value decided the exit), and the next launch on the
-// stream is ordered after this one by the kernel boundary.
-__device__ __forceinline__ void finish(WsHeader* hdr, uint32_t epoch) {
+// stream is ordered after this one by the kernel boundary. When a call runs
+// two kernels at once (GEMM + side producer), `total` counts the workgroups
+// of both: the last of them resets, after every workgroup of either kernel
+// has read the call's epoch at its start.
+__device__ __forceinline__ void finish(WsHeader* hdr, uint32_t epoch, int total = 0) {
   __syncthreads();
   if (threadIdx.x == 0) {
     uint32_t d = __hip_atomic_fetch_add(&hdr->done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (d + 1 == gridDim.x) {
+    if (d + 1 == (total > 0 ? (uint32_t)total : gridDim.x)) {
       __hip_atomic_store(&hdr->ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(&hdr->side_ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       for (int q = 0; q < kXcds; ++q)
         __hip_atomic_store(&hdr->xtick[q], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_store(&hdr->done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -225,14 +311,18 @@ __device__ __forceinline__ void finish(WsHeader* hdr, uint32_t epoch) {
   }
 }
 
+// c0: shader-clock cycle count at t0 (0 = not measured); wait: ticks spent in
+// flag waits after t1.
 __device__ __forceinline__ void trace_task(const Common& cm, uint32_t slot, uint32_t kind, uint32_t a, uint32_t b,
                                            uint32_t c, uint32_t d, uint32_t epoch, uint64_t t0, uint64_t t1,
-                                           uint32_t seen, uint32_t queue_ticket) {
+                                           uint32_t seen, uint32_t queue_ticket, uint64_t c0 = 0,
+                                           uint32_t wait = 0) {
   if (threadIdx.x == 0 && cm.trace && slot < cm.trace_cap) {
     ocg_trace_rec* r = cm.trace + slot;
     r->ticket = slot; r->kind = kind; r->a = a; r->b = b; r->c = c; r->d = d;
     r->hw = (xcc_id() << 16) | blockIdx.x; r->epoch = epoch;
     r->t_start = t0; r->t_ready = t1; r->t_end = now_ticks(); r->flag_seen = seen; r->queue = queue_ticket;
+    r->cycles = c0 ? now_cycles() - c0 : 0; r->wait_ticks = wait; r->pad = 0;
   }
 }
 

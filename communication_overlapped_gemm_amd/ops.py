@@ -29,25 +29,38 @@ def handle(device: Optional[int] = None) -> C.c_void_p:
     return h
 
 
+def _stream(stream: Optional[torch.cuda.Stream]) -> torch.cuda.Stream:
+    return stream if stream is not None else torch.cuda.current_stream()
+
+
 def _stream_ptr(stream: Optional[torch.cuda.Stream]) -> int:
-    s = stream if stream is not None else torch.cuda.current_stream()
-    return s.cuda_stream
+    return _stream(stream).cuda_stream
 
 
 class Workspace:
     """Caller-owned scratch of one operation shape (flags, tickets, routing
-    tables), cleared once by the library's fill kernel."""
+    tables), cleared once by the library's fill kernel on `stream` (default:
+    the current stream) -- the stream its calls run on. Calls that share a
+    workspace must be ordered on one stream."""
 
     def __init__(self, op: int, R: int, m: int, K: int, N: int, E: int = 0, topk: int = 0,
                  device: Optional[int] = None, stream=None):
-        n = lib.ocg_workspace_bytes(op, R, m, K, N, E, topk)
+        n = lib.ocg_workspace_bytes(None, op, R, m, K, N, E, topk)
         if n == 0:
             raise _lib.OcgError(_lib.ERR_UNSUPPORTED_SHAPE, "ocg_workspace_bytes")
         dev = torch.cuda.current_device() if device is None else device
         self.buf = torch.empty(n, dtype=torch.uint8, device=f"cuda:{dev}")
         self.nbytes = n
         self.device = dev
-        check(lib.ocg_workspace_init(handle(dev), self.ptr, n, _stream_ptr(stream)), "ocg_workspace_init")
+        s = _stream(stream)
+        cur = torch.cuda.current_stream(dev)
+        if s != cur:
+            # the block came from the current stream's pool: order the clear
+            # after that stream's earlier work, and keep the block off the pool
+            # while `s` may still use it
+            s.wait_stream(cur)
+            self.buf.record_stream(s)
+        check(lib.ocg_workspace_init(handle(dev), self.ptr, n, s.cuda_stream), "ocg_workspace_init")
 
     @property
     def ptr(self) -> int:
@@ -59,12 +72,15 @@ class Workspace:
         check(lib.ocg_check(handle(self.device), self.ptr), "ocg_check")
 
     @classmethod
-    def cached(cls, op, R, m, K, N, E=0, topk=0, device=None):
+    def cached(cls, op, R, m, K, N, E=0, topk=0, device=None, stream=None):
+        """One workspace per (shape, device, stream): calls of one shape on
+        different streams do not share counters."""
         dev = torch.cuda.current_device() if device is None else device
-        key = (op, R, m, K, N, E, topk, dev)
+        sp = _stream_ptr(stream)
+        key = (op, R, m, K, N, E, topk, dev, sp)
         ws = _workspaces.get(key)
         if ws is None:
-            ws = _workspaces[key] = cls(op, R, m, K, N, E, topk, dev)
+            ws = _workspaces[key] = cls(op, R, m, K, N, E, topk, dev, stream)
         return ws
 
 
@@ -101,7 +117,7 @@ def ag_gemm(a_chunks: Sequence[torch.Tensor], b: torch.Tensor, local_rank: int =
         c = torch.empty((R * m, N), dtype=torch.bfloat16, device=dev)
     _check_bf16(a_gathered, "a_gathered", (R * m, K))
     _check_bf16(c, "c", (R * m, N))
-    ws = workspace or Workspace.cached(_lib.OP_AG_GEMM, R, m, K, N, device=dev.index)
+    ws = workspace or Workspace.cached(_lib.OP_AG_GEMM, R, m, K, N, device=dev.index, stream=stream)
     ptrs = (C.c_void_p * R)(*[t.data_ptr() for t in a_chunks])
     cfg = _cfg(config)
     check(lib.ocg_ag_gemm(handle(dev.index), ptrs, R, local_rank, m, K, b.data_ptr(), N, a_gathered.data_ptr(),
@@ -132,7 +148,7 @@ def gemm_rs(a: torch.Tensor, b: torch.Tensor, peer_partials: Sequence[Optional[t
         out = torch.empty((M // R, N), dtype=torch.bfloat16, device=dev)
     _check_bf16(partial, "partial", (M, N))
     _check_bf16(out, "out", (M // R, N))
-    ws = workspace or Workspace.cached(_lib.OP_GEMM_RS, R, M, K, N, device=dev.index)
+    ws = workspace or Workspace.cached(_lib.OP_GEMM_RS, R, M, K, N, device=dev.index, stream=stream)
     cfg = _cfg(config)
     check(lib.ocg_gemm_rs(handle(dev.index), a.data_ptr(), b.data_ptr(), M, K, N, R, local_rank, ptrs,
                           partial.data_ptr(), out.data_ptr(), ws.ptr, ws.nbytes, C.byref(cfg),
@@ -164,7 +180,7 @@ def ag_grouped_gemm(a_chunks: Sequence[torch.Tensor], logits: torch.Tensor, w: t
     o.setdefault("perm", torch.empty((T * topk,), dtype=torch.int32, device=dev))
     o.setdefault("expert_offsets", torch.empty((E + 1,), dtype=torch.int32, device=dev))
     o.setdefault("out", torch.empty((T * topk, N), dtype=torch.bfloat16, device=dev))
-    ws = workspace or Workspace.cached(_lib.OP_AG_GROUPED_GEMM, R, m, K, N, E, topk, device=dev.index)
+    ws = workspace or Workspace.cached(_lib.OP_AG_GROUPED_GEMM, R, m, K, N, E, topk, device=dev.index, stream=stream)
     ptrs = (C.c_void_p * R)(*[t.data_ptr() for t in a_chunks])
     cfg = _cfg(config)
     check(lib.ocg_ag_grouped_gemm(handle(dev.index), ptrs, R, local_rank, m, K, logits.data_ptr(), E, topk,
@@ -204,7 +220,7 @@ def moe_combine_rs(y: torch.Tensor, topk_w: torch.Tensor, peer_partials: Sequenc
         out = torch.empty((m, N), dtype=torch.bfloat16, device=dev)
     _check_bf16(partial, "partial", (T, N))
     _check_bf16(out, "out", (m, N))
-    ws = workspace or Workspace.cached(_lib.OP_MOE_COMBINE_RS, R, m, 0, N, 0, topk, device=dev.index)
+    ws = workspace or Workspace.cached(_lib.OP_MOE_COMBINE_RS, R, m, 0, N, 0, topk, device=dev.index, stream=stream)
     cfg = _cfg(config)
     check(lib.ocg_moe_combine_rs(handle(dev.index), y.data_ptr(), topk_w.data_ptr(), R, local_rank, m, N, topk, ptrs,
                                  partial.data_ptr(), out.data_ptr(), ws.ptr, ws.nbytes, C.byref(cfg),
@@ -241,7 +257,7 @@ def ag_attention(q: torch.Tensor, k_chunks: Sequence[torch.Tensor], v_chunks: Se
     _check_bf16(k_gathered, "k_gathered", (R * m, Hkv, d))
     _check_bf16(v_gathered, "v_gathered", (R * m, Hkv, d))
     _check_bf16(out, "out", (m, Hq, d))
-    ws = workspace or Workspace.cached(_lib.OP_AG_ATTENTION, R, m, Hq, Hkv, device=dev.index)
+    ws = workspace or Workspace.cached(_lib.OP_AG_ATTENTION, R, m, Hq, Hkv, device=dev.index, stream=stream)
     kp = (C.c_void_p * R)(*[t.data_ptr() for t in k_chunks])
     vp = (C.c_void_p * R)(*[t.data_ptr() for t in v_chunks])
     cfg = _cfg(config)
@@ -259,20 +275,30 @@ def signal(flags: torch.Tensor, value: int, stream=None) -> None:
 
 
 def plan_info(op: int, R: int, local_rank: int, m: int, K: int, N: int, config: Optional[Config] = None,
-              E: int = 0, topk: int = 0) -> dict:
+              E: int = 0, topk: int = 0, handle=None) -> dict:
     """Host-only: the resolved tile/slab/copy plan of a call (E, topk: the
-    grouped GEMM's experts and picks per token)."""
+    grouped GEMM's experts and picks per token). handle=None plans for a
+    full 256-CU MI355X without touching a device."""
     out = _lib.I64x8()
     cfg = _cfg(config)
-    check(lib.ocg_plan_info(op, R, local_rank, m, K, N, E, topk, C.byref(cfg), out), "ocg_plan_info")
+    check(lib.ocg_plan_info(handle, op, R, local_rank, m, K, N, E, topk, C.byref(cfg), out), "ocg_plan_info")
     keys = ["tile", "BM", "BN", "slab_rows", "copy_rows", "n_copy_or_strips", "n_tiles", "n_slabs_or_strip_rows"]
     return dict(zip(keys, list(out)))
 
 
+def plan_ag(R: int, local_rank: int, m: int, K: int, N: int, config: Optional[Config] = None, handle=None) -> dict:
+    """Host-only: AG-GEMM K-slab width, K-slab count, transfer mode and grids."""
+    out = _lib.I64x8()
+    cfg = _cfg(config)
+    check(lib.ocg_plan_ag(handle, R, local_rank, m, K, N, C.byref(cfg), out), "ocg_plan_ag")
+    return dict(kslab_cols=out[0], nks=out[1], transfer=out[2], gemm_grid=out[3], side_grid=out[4],
+                n_inline=out[5], rows_per_round=out[6])
+
+
 def plan_task(op: int, R: int, local_rank: int, m: int, K: int, N: int, ticket: int,
-              config: Optional[Config] = None) -> list:
+              config: Optional[Config] = None, handle=None) -> list:
     """Host-only: the task a ticket names (see ocg_plan_task)."""
     out = _lib.I64x8()
     cfg = _cfg(config)
-    check(lib.ocg_plan_task(op, R, local_rank, m, K, N, C.byref(cfg), ticket, out), "ocg_plan_task")
+    check(lib.ocg_plan_task(handle, op, R, local_rank, m, K, N, C.byref(cfg), ticket, out), "ocg_plan_task")
     return list(out)

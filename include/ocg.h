@@ -64,6 +64,23 @@ extern "C" {
 #define OCG_MODE_GEMM_ONLY 1
 #define OCG_MODE_COPY_ONLY 2
 
+/* How the AllGather part of ocg_ag_gemm moves the peers' rows (ocg_config.transfer):
+ *   INLINE -- copy tasks run in the GEMM's own persistent kernel: every
+ *             workgroup takes copy tickets first, then tiles;
+ *   SIDE   -- the copy tasks run in a small producer kernel on a side stream
+ *             owned by the handle, co-resident with the GEMM kernel on every
+ *             compute unit (it uses no LDS and few registers), so copies
+ *             proceed while the tiles compute. The caller's stream waits for
+ *             the producer before the call's later work; the GEMM tiles wait
+ *             on the per-(slab, K-slab) flags it publishes.
+ *   AUTO   -- SIDE when the two kernels fit on a compute unit together,
+ *             else INLINE.
+ * (Pull transfers with a "transfer complete" flag per slab: "TileLink ..."
+ * (MLSys 2025 talk summary), "Technical Deep Dive".) */
+#define OCG_TRANSFER_AUTO (-1)
+#define OCG_TRANSFER_INLINE 0
+#define OCG_TRANSFER_SIDE 1
+
 /* Tile presets (rows x columns of C per workgroup tile, K step 64);
  * OCG_TILE_288x224 and OCG_TILE_320x224 are for the grouped GEMM only. */
 #define OCG_TILE_AUTO (-1)
@@ -77,16 +94,18 @@ extern "C" {
 #define OCG_TILE_COUNT 7
 
 /* Trace record written per executed task when ocg_config.trace is set
- * (64 bytes), at slot: AG-GEMM / MoE copy task u -> u, tile v -> n_copy + v;
+ * (80 bytes), at slot: AG-GEMM / MoE copy task u -> u, tile v -> n_copy + v;
  * GEMM-RS tile v -> v, reduce strip j -> n_tiles + j (v = tile index in the
  * grouped tile order; TopK-Reduce: task u -> u).
  * kind: 1 copy task, 2 AG-GEMM tile, 3 GEMM-RS tile, 4 MoE tile, 5 GEMM-RS
  * reduce strip, 6 TopK-Reduce task, 7 attention tile (AllGather-KV
  * attention: copy ticket u -> u, tile v -> #copy tickets + v). Times are the
- * GPU's constant 100 MHz clock. */
+ * GPU's constant 100 MHz clock; `cycles` counts shader-clock cycles over the
+ * same interval (s_memtime), so cycles / (t_end - t_start) * 100 MHz is the
+ * compute-unit clock while the task ran. */
 typedef struct ocg_trace_rec {
   uint32_t ticket, kind;
-  uint32_t a, b, c, d;   /* copy: chunk, piece, slab, published(0/1)
+  uint32_t a, b, c, d;   /* copy: chunk, piece, flag index (slab * #K-slabs + K-slab), published(0/1)
                             AG tile: rb, cb, #slabs waited, 0
                             RS tile: rb, cb, local-block(0/1), 0
                             MoE tile: expert, row start, rows, cb | (#slabs waited << 16)
@@ -98,7 +117,12 @@ typedef struct ocg_trace_rec {
   uint64_t t_start, t_ready, t_end; /* ready = dependencies satisfied (tiles)
                                        or flag published (copy) */
   uint32_t flag_seen;
-  uint32_t queue;        /* tiles: (XCD queue << 16) | ticket within that queue */
+  uint32_t queue;        /* tiles: (XCD queue << 16) | ticket within that queue;
+                            AG copy: K-slab index */
+  uint64_t cycles;       /* shader-clock cycles from t_start to t_end */
+  uint32_t wait_ticks;   /* AG tile: 100 MHz ticks spent waiting on K-slab flags inside the
+                            K loop (after t_ready); 0 otherwise */
+  uint32_t pad;
 } ocg_trace_rec;
 
 typedef struct ocg_config {
@@ -118,6 +142,16 @@ typedef struct ocg_config {
                                  written by peers when their partial tile has landed;
                                  NULL = all peer partials are complete */
   uint32_t peer_flag_value;   /* value meaning "landed" in peer_flags */
+  int32_t transfer;         /* OCG_TRANSFER_* (ocg_ag_gemm only); default AUTO */
+  int32_t kslab_cols;       /* ocg_ag_gemm: columns of A per published flag (a multiple of 256);
+                               0 = auto: the whole K for INLINE, 512 for SIDE */
+  uint32_t copy_delay;      /* test hook: a copy task of K-slab j first sleeps (j + 1) x this many
+                               rounds of s_sleep 127 (~8k cycles each) -- forces late publishes,
+                               later K-slabs later; 0 = off */
+  int32_t xcd_remap;        /* 1 = tiles dealt in batches to per-XCD queues (default);
+                               0 = one queue in plain tile order (ablation) */
+  int32_t side_grid;        /* SIDE transfer: producer workgroups (one per compute unit at most
+                               counts); 0 = auto */
 } ocg_config;
 
 /* Opaque per-device handle: device id, compute-unit count and the resident
@@ -125,7 +159,7 @@ typedef struct ocg_config {
 typedef struct ocg_handle_s* ocg_handle;
 
 /* Fill `cfg` with defaults (auto tile, swizzled, fused, 1 s timeout, no
- * trace, no fault injection). */
+ * trace, no fault injection, auto transfer and K-slab width, XCD queues). */
 void ocg_config_default(ocg_config* cfg);
 
 /* Create a handle for `device` (HIP ordinal). Returns OCG_ERR_NO_DEVICE if no
@@ -136,9 +170,9 @@ void ocg_destroy(ocg_handle h);
 /* Workspace bytes for `op`: AG_GEMM (R, m = rows per rank, K, N),
  * GEMM_RS (R, m = M total rows, K, N), AG_GROUPED_GEMM (R, m, K, N, E, topk),
  * MOE_COMBINE_RS (R, m, 0, N, 0, topk), AG_ATTENTION (R, m = tokens per
- * rank, K = Hq, N = Hkv).
- * Unused arguments are ignored. Returns 0 on invalid arguments. */
-size_t ocg_workspace_bytes(int op, int R, int64_t m, int64_t K, int64_t N, int E, int topk);
+ * rank, K = Hq, N = Hkv). `h` may be NULL (the size does not depend on the
+ * device). Unused arguments are ignored. Returns 0 on invalid arguments. */
+size_t ocg_workspace_bytes(ocg_handle h, int op, int R, int64_t m, int64_t K, int64_t N, int E, int topk);
 
 /* Clear a workspace once before its first use (a fill kernel on `stream`). */
 int ocg_workspace_init(ocg_handle h, void* workspace, size_t ws_bytes, void* stream);
@@ -282,7 +316,9 @@ const char* ocg_status_string(int status);
 
 /* ---- host-only planning queries (no GPU needed; used by tests/tools) ---- */
 
-/* Resolved plan parameters for a call with config `cfg` (NULL = defaults):
+/* Resolved plan parameters for a call with config `cfg` (NULL = defaults) on
+ * the device of `h` (its compute-unit count sizes the automatic choices;
+ * h = NULL plans for a full 256-CU MI355X without touching any device): 
  * out[0]=tile preset, out[1]=BM, out[2]=BN, out[3]=slab rows,
  * out[4]=copy rows, out[5]=#copy tasks, out[6]=#tiles (static ops),
  * out[7]=#slabs. For OCG_OP_MOE_COMBINE_RS: out[0]=-1, out[3]=rows per
@@ -292,14 +328,26 @@ const char* ocg_status_string(int status);
  * block, out[3]=slab tokens, out[4]=copy tokens, out[5]=#copy tickets (both
  * tensors), out[6]=#tiles, out[7]=#slabs. For GEMM_RS pass m = M. E and topk are the grouped GEMM's
  * expert count and picks per token (they choose its default tile; ignored
- * by the other ops). Returns OCG_OK or an error. */
-int ocg_plan_info(int op, int R, int local_rank, int64_t m, int64_t K, int64_t N, int E, int topk,
-                  const ocg_config* cfg, int64_t out[8]);
+ * by the other ops). For OCG_OP_AG_GEMM, out[7] counts flags (slabs x
+ * K-slabs) and the K-slab width and transfer mode are returned by
+ * ocg_plan_ag(). Returns OCG_OK or an error. */
+int ocg_plan_info(ocg_handle h, int op, int R, int local_rank, int64_t m, int64_t K, int64_t N, int E,
+                  int topk, const ocg_config* cfg, int64_t out[8]);
+
+/* AG-GEMM plan details: out[0] = K-slab columns, out[1] = #K-slabs,
+ * out[2] = transfer mode the call would use (OCG_TRANSFER_INLINE or _SIDE),
+ * out[3] = persistent GEMM workgroups, out[4] = producer workgroups (SIDE)
+ * or 0, out[5] = copy tickets the GEMM kernel runs itself (the first K-slab
+ * of the first copy phase under SIDE, all of them otherwise), out[6] =
+ * gathered rows per round of tiles (copy phases), out[7] = 0. `h` as for
+ * ocg_plan_info. */
+int ocg_plan_ag(ocg_handle h, int R, int local_rank, int64_t m, int64_t K, int64_t N, const ocg_config* cfg,
+                int64_t out[8]);
 
 /* Task at trace slot `ticket` of the AG-GEMM / GEMM-RS plan (slots as for
  * ocg_trace_rec: AG copies, then AG tiles; RS tiles, then RS strips):
  * desc[0]=kind (1 copy, 2 AG tile, 3 RS tile, 5 RS strip, 0 none),
- * copy: desc[1]=chunk, [2]=piece, [3]=row0, [4]=row1, [5]=slab;
+ * copy: desc[1]=chunk, [2]=piece, [3]=row0, [4]=row1, [5]=slab, [6]=K-slab;
  * AG tile: desc[1]=rb, [2]=cb, [3]=#dependency slabs, [4..7]=first four
  *          dependency slab ids (-1 if none);
  * RS tile: desc[1]=rb, [2]=cb, [3]=local-block (0/1), [4]=XCD queue,
@@ -309,7 +357,7 @@ int ocg_plan_info(int op, int R, int local_rank, int64_t m, int64_t K, int64_t N
  *          copy, [6]=tensor (0 keys, 1 values); tile: desc[0]=7, [1]=kv
  *          head, [2]=row block, [3]=#flags each wave waits on, [4]=XCD
  *          queue, [5]=ticket within the queue. */
-int ocg_plan_task(int op, int R, int local_rank, int64_t m, int64_t K, int64_t N,
+int ocg_plan_task(ocg_handle h, int op, int R, int local_rank, int64_t m, int64_t K, int64_t N,
                   const ocg_config* cfg, int64_t ticket, int64_t desc[8]);
 
 #ifdef __cplusplus

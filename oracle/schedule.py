@@ -19,12 +19,22 @@ must reproduce it exactly. It follows the pages' tile-centric scheme:
 Schedule definition (shared contract with the device code; written here
 independently):
 
-AG-GEMM (rank count R, rows per rank m, gathered M = R*m, tile BM x BN, slab
-rows S, copy-task rows CT with S % CT == 0):
+AG-GEMM (rank count R, rows per rank m, gathered M = R*m, inner size K, tile
+BM x BN, slab rows S, copy-task rows CT with S % CT == 0, K-slab columns KS):
   chunk sequence for copies: swizzled -> (l+1, l+2, ..., l+R-1, l) mod R;
   natural -> (0, 1, ..., R-1).
-  copy ticket u < R*ceil(m/CT): chunk = seq[u // ceil(m/CT)], piece t = u % ..,
-  rows [c*m + t*CT, c*m + min((t+1)*CT, m)), slab (c, (t*CT)//S).
+  The columns are cut into K-slabs of KS (the last may be shorter). When
+  swizzled, the sequence is cut into phases: the peer at position q (chunk
+  l+1+q) belongs to phase ((q+1)*m) // RPR -- RPR gathered rows of the
+  rotated order are read per round of tiles of the persistent grid, so a
+  phase holds the peers a round first reads -- and the local chunk, which no
+  tile waits on, forms the last phase (natural order: one phase). Copy
+  tickets run phase by phase; within a phase K-slab by K-slab; within a
+  K-slab over the phase's chunks in sequence order and the pieces of each:
+  piece t of chunk c in K-slab j holds rows [c*m + t*CT, c*m +
+  min((t+1)*CT, m)), columns [j*KS, min((j+1)*KS, K)), slab (c, (t*CT)//S),
+  and completes part of flag slab*nks + j (nks = ceil(K/KS)). With KS = K
+  there is one K-slab and the flag is the slab.
   tiles follow the copies: tile v sits at slot n_copy + v. Tile order: the
   row blocks in rotated order rb0, rb0+1, ... (mod n_rb), rb0 = (l*m)//BM
   when swizzled, else 0, are cut into groups of GROUP consecutive blocks;
@@ -36,6 +46,10 @@ rows S, copy-task rows CT with S % CT == 0):
   Tiles are dealt to XCDS queues in batches of BATCH consecutive tiles, batch
   b to queue b % XCDS; a queue's tickets 0, 1, ... name its tiles in order.
   (The queue a tile sits in sets only which L2 serves it, not its result.)
+  Without the XCD remap (ablation) there is one queue: tile v is ticket v of
+  queue 0.
+  A tile waits, for every K-slab it loads, on that K-slab's flag of each of
+  its dependency slabs, before its first load of the K-slab.
 GEMM-RS: slots [0, n_tiles) are GEMM tiles in the same order and queues,
   with rb0 = (l*M/R)//BM when swizzled; each stores its bf16 partial and
   publishes its tile flag. Slots [n_tiles, n_tiles + ceil(blk/RR)) are
@@ -109,6 +123,10 @@ class CopyTask:
     row0: int       # first gathered row
     row1: int       # one past the last gathered row
     slab: int       # global slab id chunk*bpr + s
+    kslab: int = 0  # K-slab index (columns [k0, k1))
+    k0: int = 0
+    k1: int = -1    # -1: every column
+    flag: int = -1  # flag index slab * nks + kslab (-1: the slab)
 
 
 @dataclass(frozen=True)
@@ -127,21 +145,40 @@ def copy_sequence(R: int, local: int, swizzle: bool) -> List[int]:
     return list(range(R))
 
 
-def copy_tasks(R, m, S, CT, local, swizzle, first_ticket=0) -> List[CopyTask]:
+def copy_phases(R, m, local, swizzle, rpr=None) -> List[List[int]]:
+    """The chunk sequence cut into copy phases (see the module docstring)."""
+    seq = copy_sequence(R, local, swizzle)
+    if not swizzle or rpr is None:
+        return [seq]
+    phases: dict = {}
+    for q, c in enumerate(seq[:-1]):
+        phases.setdefault(((q + 1) * m) // rpr, []).append(c)
+    return [phases[k] for k in sorted(phases)] + [[seq[-1]]]
+
+
+def copy_tasks(R, m, S, CT, local, swizzle, first_ticket=0, K=None, KS=None, rpr=None) -> List[CopyTask]:
     if S % CT:
         raise ValueError("slab rows must be a multiple of copy-task rows")
     bpr = _cdiv(m, S)
+    if K is None or KS is None or KS >= K:
+        kslabs = [(0, -1)]
+    else:
+        kslabs = [(k0, min(k0 + KS, K)) for k0 in range(0, K, KS)]
+    nks = len(kslabs)
     out = []
     ticket = first_ticket
-    for c in copy_sequence(R, local, swizzle):
-        t = 0
-        r = 0
-        while r < m:
-            r1 = min(r + CT, m)
-            out.append(CopyTask(ticket, c, t, c * m + r, c * m + r1, c * bpr + r // S))
-            ticket += 1
-            t += 1
-            r = r1
+    for phase in copy_phases(R, m, local, swizzle, rpr):
+        for j, (k0, k1) in enumerate(kslabs):
+            for c in phase:
+                t = 0
+                r = 0
+                while r < m:
+                    r1 = min(r + CT, m)
+                    slab = c * bpr + r // S
+                    out.append(CopyTask(ticket, c, t, c * m + r, c * m + r1, slab, j, k0, k1, slab * nks + j))
+                    ticket += 1
+                    t += 1
+                    r = r1
     return out
 
 
@@ -157,18 +194,20 @@ def slab_targets(R, m, S, CT) -> List[int]:
     return tgt
 
 
-def ag_gemm_plan(R, m, K, N, local, BM, BN, S, CT, swizzle=True, mode="fused"):
-    """Full ticket list for the AG-GEMM kernel: list of CopyTask and Tile."""
+def ag_gemm_plan(R, m, K, N, local, BM, BN, S, CT, swizzle=True, mode="fused", KS=None, xcd_remap=True,
+                 rpr=None):
+    """Full ticket list for the AG-GEMM kernel: list of CopyTask and Tile.
+    rpr: gathered rows per round of tiles (copy phases); None = one round."""
     M = R * m
     n_rb, n_cb = _cdiv(M, BM), _cdiv(N, BN)
     bpr = _cdiv(m, S)
     tasks = []
     if mode in ("fused", "copy_only"):
-        tasks += copy_tasks(R, m, S, CT, local, swizzle)
+        tasks += copy_tasks(R, m, S, CT, local, swizzle, K=K, KS=KS, rpr=rpr)
     if mode in ("fused", "gemm_only"):
         rb0 = (local * m) // BM if swizzle else 0
         base = len(tasks)
-        where = queue_of(n_rb * n_cb)
+        where = queue_of(n_rb * n_cb) if xcd_remap else {v: (0, v) for v in range(n_rb * n_cb)}
         for v, (rb, cb) in enumerate(tile_order(n_rb, n_cb, rb0)):
             deps = set()
             if mode == "fused":

@@ -57,14 +57,16 @@ def assert_gate(got_bits: np.ndarray, want: np.ndarray, what: str, tight: bool =
 
 TRACE_DTYPE = np.dtype([("ticket", "<u4"), ("kind", "<u4"), ("a", "<u4"), ("b", "<u4"), ("c", "<u4"),
                         ("d", "<u4"), ("hw", "<u4"), ("epoch", "<u4"), ("t_start", "<u8"), ("t_ready", "<u8"),
-                        ("t_end", "<u8"), ("flag_seen", "<u4"), ("queue", "<u4")])
-assert TRACE_DTYPE.itemsize == 64
+                        ("t_end", "<u8"), ("flag_seen", "<u4"), ("queue", "<u4"), ("cycles", "<u8"),
+                        ("wait_ticks", "<u4"), ("pad", "<u4")])
+REC = TRACE_DTYPE.itemsize
+assert REC == 80
 
 
 class Trace:
     def __init__(self, capacity: int):
         self.capacity = capacity
-        self.buf = torch.zeros(capacity * 64, dtype=torch.uint8, device="cuda")
+        self.buf = torch.zeros(capacity * REC, dtype=torch.uint8, device="cuda")
 
     def attach(self, cfg):
         cfg.trace = self.buf.data_ptr()
@@ -73,4 +75,4 @@ class Trace:
 
     def read(self, n: int) -> np.ndarray:
         torch.cuda.synchronize()
-        return self.buf[: n * 64].cpu().numpy().view(TRACE_DTYPE)
+        return self.buf[: n * REC].cpu().numpy().view(TRACE_DTYPE)

@@ -64,15 +64,15 @@ def test_status_strings_and_defaults():
 
 def test_workspace_bytes_validation():
     lib = ocg.lib
-    assert lib.ocg_workspace_bytes(0, 8, 1024, 8192, 3584, 0, 0) > 256
-    assert lib.ocg_workspace_bytes(0, 8, 1024, 8190, 3584, 0, 0) == 0      # K % 64
-    assert lib.ocg_workspace_bytes(0, 8, 1024, 8192, 3583, 0, 0) == 0      # N % 8
-    assert lib.ocg_workspace_bytes(0, 17, 1024, 8192, 3584, 0, 0) == 0     # R > 16
-    assert lib.ocg_workspace_bytes(1, 8, 4095, 1792, 4096, 0, 0) == 0      # M % R
-    assert lib.ocg_workspace_bytes(2, 8, 512, 4096, 1792, 32, 2) > 0
-    assert lib.ocg_workspace_bytes(2, 8, 512, 4096, 1792, 65, 2) == 0      # E > 64
-    assert lib.ocg_workspace_bytes(2, 8, 512, 4096, 1792, 32, 5) == 0      # topk > 4
-    assert lib.ocg_workspace_bytes(3, 8, 512, 4096, 1792, 0, 0) == 0       # bad op
+    assert lib.ocg_workspace_bytes(None, 0, 8, 1024, 8192, 3584, 0, 0) > 256
+    assert lib.ocg_workspace_bytes(None, 0, 8, 1024, 8190, 3584, 0, 0) == 0      # K % 64
+    assert lib.ocg_workspace_bytes(None, 0, 8, 1024, 8192, 3583, 0, 0) == 0      # N % 8
+    assert lib.ocg_workspace_bytes(None, 0, 17, 1024, 8192, 3584, 0, 0) == 0     # R > 16
+    assert lib.ocg_workspace_bytes(None, 1, 8, 4095, 1792, 4096, 0, 0) == 0      # M % R
+    assert lib.ocg_workspace_bytes(None, 2, 8, 512, 4096, 1792, 32, 2) > 0
+    assert lib.ocg_workspace_bytes(None, 2, 8, 512, 4096, 1792, 65, 2) == 0      # E > 64
+    assert lib.ocg_workspace_bytes(None, 2, 8, 512, 4096, 1792, 32, 5) == 0      # topk > 4
+    assert lib.ocg_workspace_bytes(None, 3, 8, 512, 4096, 1792, 0, 0) == 0       # bad op
 
 
 def test_entry_points_reject_null_arguments_without_a_device():
@@ -135,24 +135,48 @@ AG_CASES = [
 ]
 
 
+def ag_grid_tiles(info, R, m, N):
+    """Tiles per round of the persistent GEMM grid on a 256-CU MI355X: one
+    workgroup per CU (two for the 128x128 tile, by LDS)."""
+    return 256 * (2 if (info["BM"], info["BN"]) == (128, 128) else 1)
+
+
 @pytest.mark.parametrize("case", AG_CASES)
 @pytest.mark.parametrize("swizzle", [1, 0])
 @pytest.mark.parametrize("mode", ["fused", "gemm_only", "copy_only"])
-def test_ag_plan_matches_oracle_schedule(case, swizzle, mode):
+@pytest.mark.parametrize("transfer,kslab", [(ocg.TRANSFER_INLINE, 0), (ocg.TRANSFER_SIDE, 0),
+                                            (ocg.TRANSFER_INLINE, 256)])
+def test_ag_plan_matches_oracle_schedule(case, swizzle, mode, transfer, kslab):
     R, m, K, N, local, tile = case
     modes = {"fused": 0, "gemm_only": 1, "copy_only": 2}
-    cfg = ocg.default_config(tile=tile, swizzle=swizzle, mode=modes[mode])
+    cfg = ocg.default_config(tile=tile, swizzle=swizzle, mode=modes[mode], transfer=transfer, kslab_cols=kslab)
     info = ocg.plan_info(ocg.OP_AG_GEMM, R, local, m, K, N, cfg)
+    ag = ocg.plan_ag(R, local, m, K, N, cfg)
+    # K-slab width: the whole K unless asked for, 512 by default for the side producer
+    side = transfer == ocg.TRANSFER_SIDE and mode != "gemm_only"
+    want_ks = min(K, kslab or (512 if side else K))
+    assert ag["kslab_cols"] == want_ks and ag["nks"] == -(-K // want_ks)
+    # rows per round: the persistent grid's tiles per round over the column blocks
+    n_cb = -(-N // info["BN"])
+    assert ag["rows_per_round"] == max(1, ag_grid_tiles(info, R, m, N) // n_cb) * info["BM"]
     want = sch.ag_gemm_plan(R, m, K, N, local, info["BM"], info["BN"], info["slab_rows"], info["copy_rows"],
-                            bool(swizzle), mode)
+                            bool(swizzle), mode, KS=ag["kslab_cols"], rpr=ag["rows_per_round"])
+    if side and mode != "gemm_only":
+        # the GEMM kernel copies the first K-slab of the first phase itself
+        first = sch.copy_phases(R, m, local, bool(swizzle), ag["rows_per_round"])[0]
+        n_inline = len(first) * -(-m // info["copy_rows"]) if ag["nks"] > 1 or len(first) < R else len(want)
+        assert ag["n_inline"] == min(n_inline, info["n_copy_or_strips"])
     assert len(want) == info["n_copy_or_strips"] + info["n_tiles"]
+    n_flags = R * -(-m // info["slab_rows"]) * ag["nks"]
+    assert info["n_slabs_or_strip_rows"] == n_flags
     for t in want + [None]:
         ticket = len(want) if t is None else t.ticket
         d = ocg.plan_task(ocg.OP_AG_GEMM, R, local, m, K, N, ticket, cfg)
         if t is None:
             assert d[0] == 0
         elif isinstance(t, sch.CopyTask):
-            assert d[:6] == [1, t.chunk, t.piece, t.row0, t.row1, t.slab]
+            assert d[:7] == [1, t.chunk, t.piece, t.row0, t.row1, t.slab, t.kslab]
+            assert 0 <= t.flag < n_flags
         else:
             deps = list(t.deps)
             assert d[:4] == [2, t.rb, t.cb, len(deps)]
@@ -213,10 +237,10 @@ def test_attention_plan_defaults_and_validation():
     p = ocg.plan_info(ocg.OP_AG_ATTENTION, 8, 0, 2048, 32, 8)
     assert (p["slab_rows"], p["copy_rows"], p["n_tiles"], p["n_copy_or_strips"]) == (2048, 512, 256, 64)
     lib = ocg.lib
-    assert lib.ocg_workspace_bytes(ocg.OP_AG_ATTENTION, 8, 2048, 32, 8, 0, 0) > 256
-    assert lib.ocg_workspace_bytes(ocg.OP_AG_ATTENTION, 8, 2048, 30, 8, 0, 0) == 0   # Hq % Hkv
-    assert lib.ocg_workspace_bytes(ocg.OP_AG_ATTENTION, 17, 2048, 32, 8, 0, 0) == 0  # R > 16
-    assert lib.ocg_workspace_bytes(ocg.OP_AG_ATTENTION, 8, 0, 32, 8, 0, 0) == 0      # m < 1
+    assert lib.ocg_workspace_bytes(None, ocg.OP_AG_ATTENTION, 8, 2048, 32, 8, 0, 0) > 256
+    assert lib.ocg_workspace_bytes(None, ocg.OP_AG_ATTENTION, 8, 2048, 30, 8, 0, 0) == 0   # Hq % Hkv
+    assert lib.ocg_workspace_bytes(None, ocg.OP_AG_ATTENTION, 17, 2048, 32, 8, 0, 0) == 0  # R > 16
+    assert lib.ocg_workspace_bytes(None, ocg.OP_AG_ATTENTION, 8, 0, 32, 8, 0, 0) == 0      # m < 1
     with pytest.raises(ocg.OcgError):
         ocg.plan_info(ocg.OP_AG_ATTENTION, 8, 0, 2048, 32, 8, ocg.default_config(slab_rows=8))
     cfg = ocg.default_config()
