@@ -20,6 +20,7 @@ struct ocg_handle_s {
   int side_fits[OCG_TILE_COUNT];    // AG-GEMM kernel + side producer fit on a CU: 0 unknown, 1 yes, -1 no
   hipStream_t side;                 // side stream of the SIDE transfer mode (default priority)
   hipEvent_t fork, join;            // caller stream -> side stream -> caller stream
+  void* scratch;                    // device address of the no-allocation scratch on `device`
 };
 
 namespace {
@@ -324,7 +325,8 @@ int ocg_create(int device, ocg_handle* out) {
   if (hipGetDevice(&prev) != hipSuccess) prev = -1;
   bool ok = hipSetDevice(device) == hipSuccess && hipStreamCreateWithFlags(&h->side, hipStreamNonBlocking) == hipSuccess &&
             hipEventCreateWithFlags(&h->fork, hipEventDisableTiming) == hipSuccess &&
-            hipEventCreateWithFlags(&h->join, hipEventDisableTiming) == hipSuccess;
+            hipEventCreateWithFlags(&h->join, hipEventDisableTiming) == hipSuccess &&
+            noalloc_scratch_setup(device, &h->scratch) == hipSuccess;
   if (prev >= 0) (void)hipSetDevice(prev);
   if (!ok) {
     ocg_destroy(h);
@@ -452,6 +454,16 @@ int ocg_ag_gemm(ocg_handle h, const void* const* a_chunks, int R, int local_rank
   if (hipEventRecord(h->join, h->side) != hipSuccess || hipStreamWaitEvent(s, h->join, 0) != hipSuccess)
     return OCG_ERR_HIP;
   return OCG_OK;
+}
+
+int ocg_ag_gemm_noalloc(ocg_handle h, const void* const* a_chunks, int R, int local_rank, int64_t m, int64_t K,
+                        const void* b, int64_t N, void* a_gathered, void* c, const ocg_config* cfg, void* stream) {
+  if (!h || !h->scratch) return OCG_ERR_INVALID_ARG;
+  if (!shape_ok(R, m, K, N)) return OCG_ERR_UNSUPPORTED_SHAPE;
+  // the shape's workspace must fit the fixed scratch (nothing is allocated)
+  if (layout(OCG_OP_AG_GEMM, R, m, K, N, 0, 0).total > kNoAllocScratchBytes) return OCG_ERR_WORKSPACE_TOO_SMALL;
+  return ocg_ag_gemm(h, a_chunks, R, local_rank, m, K, b, N, a_gathered, c, h->scratch, kNoAllocScratchBytes, cfg,
+                     stream);
 }
 
 int ocg_gemm_rs(ocg_handle h, const void* A, const void* B, int64_t M, int64_t K, int64_t N, int R, int local_rank,

@@ -17,6 +17,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "gemm_core.h"
 #include "ocg_internal.h"
 #include "sync.h"
@@ -694,6 +696,40 @@ __global__ void fill_u32_kernel(uint32_t* p, size_t n, uint32_t v, int release) 
     else
       p[i] = v;
   }
+}
+
+// ---------------------------------------------------------------- no-allocation scratch
+
+// Workspace of ocg_ag_gemm_noalloc, the entry point for callers that cannot
+// allocate: a file-scope device array, one copy per GPU the library runs on,
+// held until the process ends. Every call on a GPU shares that GPU's copy
+// (the header's counters return to zero at the end of each call and the
+// flags carry the call's epoch, so it is cleared once, at set-up).
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+namespace {
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];   // device address of `scratch` per device, null until set up
+}
+
+// Set-up, from ocg_create with `device` current: look up the array's device
+// address (in host code its name is only a host-side stand-in) and clear the
+// array, once per device.
+hipError_t noalloc_scratch_setup(int device, void** out) {
+  if (device < 0 || device >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[device]) {
+    void* ptr = nullptr;
+    hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!ptr) return hipErrorInvalidSymbol;
+    e = launch_fill_u32((uint32_t*)ptr, kNoAllocScratchBytes / 4, 0u, 0, nullptr);
+    if (e == hipSuccess) e = hipStreamSynchronize(nullptr);
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[device] = ptr;
+  }
+  *out = g_scratch_ptr[device];
+  return hipSuccess;
 }
 
 // ---------------------------------------------------------------- launchers

@@ -151,6 +151,11 @@ hipError_t launch_moe_combine_rs(const CombArgs& a, int grid, hipStream_t s);
 hipError_t launch_ag_attention(const AttnArgs& a, int grid, hipStream_t s);
 int resident_attention();
 hipError_t launch_fill_u32(uint32_t* p, size_t n, uint32_t v, int release, hipStream_t s);
+// No-allocation entry point: the device address of the file-scope scratch
+// array on `device` (which must be current), cleared on first use.
+constexpr size_t kNoAllocScratchBytes = (size_t)1 << 20;
+constexpr int kMaxDevices = 64;
+hipError_t noalloc_scratch_setup(int device, void** out);
 // Resident workgroups per CU of each persistent kernel (op, tile preset).
 int resident_per_cu(int op, int tile);
 

@@ -125,6 +125,26 @@ def ag_gemm(a_chunks: Sequence[torch.Tensor], b: torch.Tensor, local_rank: int =
     return c, a_gathered
 
 
+def ag_gemm_noalloc(a_chunks: Sequence[torch.Tensor], b: torch.Tensor, local_rank: int, a_gathered: torch.Tensor,
+                    c: torch.Tensor, *, config: Optional[Config] = None, stream=None) -> None:
+    """Fused AllGather-GEMM through the no-allocation entry point: the caller
+    passes every output; the library's per-GPU scratch stands in for the
+    workspace (calls that overlap on one GPU race)."""
+    R = len(a_chunks)
+    m, K = a_chunks[0].shape
+    N = b.shape[1]
+    for r, t in enumerate(a_chunks):
+        _check_bf16(t, f"a_chunks[{r}]", (m, K))
+    _check_bf16(b, "b", (K, N))
+    _check_bf16(a_gathered, "a_gathered", (R * m, K))
+    _check_bf16(c, "c", (R * m, N))
+    ptrs = (C.c_void_p * R)(*[t.data_ptr() for t in a_chunks])
+    cfg = _cfg(config)
+    check(lib.ocg_ag_gemm_noalloc(handle(b.device.index), ptrs, R, local_rank, m, K, b.data_ptr(), N,
+                                  a_gathered.data_ptr(), c.data_ptr(), C.byref(cfg), _stream_ptr(stream)),
+          "ocg_ag_gemm_noalloc")
+
+
 def gemm_rs(a: torch.Tensor, b: torch.Tensor, peer_partials: Sequence[Optional[torch.Tensor]], local_rank: int = 0,
             *, partial: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
             workspace: Optional[Workspace] = None, config: Optional[Config] = None,

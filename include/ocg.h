@@ -193,6 +193,26 @@ int ocg_ag_gemm(ocg_handle h, const void* const* a_chunks, int R, int local_rank
                 void* workspace, size_t ws_bytes, const ocg_config* cfg, void* stream);
 
 /*
+ * ocg_ag_gemm without a caller workspace, for callers that cannot allocate
+ * device memory (code under graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc). Same arguments, semantics and errors as
+ * ocg_ag_gemm minus the workspace: it uses a fixed 1 MiB scratch array that
+ * the library keeps on each GPU (a file-scope device array, set up and
+ * cleared once by ocg_create, held until the process ends), and allocates
+ * nothing itself. Limit: shapes whose AG-GEMM workspace
+ * (ocg_workspace_bytes(h, OCG_OP_AG_GEMM, R, m, K, N, 0, 0)) exceeds 1 MiB
+ * return OCG_ERR_WORKSPACE_TOO_SMALL and enqueue nothing (the 70B-class
+ * share needs about 130 KiB). All calls on one GPU share the scratch, which
+ * keeps the last call's state: calls that overlap on one GPU (on different
+ * streams, or from different handles or threads) race and must not be
+ * issued; calls ordered on one stream are fine. A timed-out flag wait is
+ * recorded in the scratch, not reported.
+ */
+int ocg_ag_gemm_noalloc(ocg_handle h, const void* const* a_chunks, int R, int local_rank,
+                        int64_t m, int64_t K, const void* b, int64_t N, void* a_gathered, void* c,
+                        const ocg_config* cfg, void* stream);
+
+/*
  * GEMM-ReduceScatter (one rank's share):
  *   partial = A x B rounded to bf16 (this rank's send buffer, every row);
  *   out     = bf16( sum_{s=0..R-1} P_s[rows local*M/R .. (local+1)*M/R) )
