@@ -184,7 +184,7 @@ bool side_fits(ocg_handle h, int tile) {
     if (kernel_resources(OCG_OP_AG_GEMM, tile, &vg, &lg) && kernel_resources(-1, 0, &vs, &ls)) {
       int& r = h->resident[OCG_OP_AG_GEMM][tile];
       if (r == 0) r = resident_per_cu(OCG_OP_AG_GEMM, tile);
-      const int waves_per_simd = r * (tile_bm(tile) == 320 ? 2 : 1);
+      const int waves_per_simd = r * tile_waves(tile) / 4;
       const int regs = waves_per_simd * ((vg + 7) & ~7) + ((vs + 7) & ~7);
       if (regs <= 512 && r * lg + ls <= 160 * 1024) f = 1;
     }
@@ -391,7 +391,7 @@ int ag_setup(ocg_handle h, int R, int local_rank, int64_t m, int64_t K, int64_t 
     if (r == 0) r = resident_per_cu(OCG_OP_AG_GEMM, o->rv.tile);
     resident = r;
   } else if (o->rv.tile == OCG_TILE_128x128) {
-    resident = 2;   // two 128x128 workgroups fit on a CU (LDS)
+    resident = 2;   // no handle: two 128x128 workgroups fit on a CU, one of every other preset
   }
   const int tpr = cfg.grid > 0 ? cfg.grid : resident * cus;
   AgPlan& p = o->plan;

@@ -49,8 +49,13 @@ constexpr int BKS = 32;   // K per stage
 
 // Waves per workgroup of a tile: 8 for the 320-row grouped-GEMM tile (a 4 x 2
 // wave grid, two waves per SIMD: 140 accumulators per wave instead of 280,
-// which the 256-entry accumulator file cannot hold), else 4 (2 x 2; measured
-// no faster with 8 for the other tiles).
+// which the 256-entry accumulator file cannot hold), else 4 (2 x 2). Eight
+// waves (4 x 2, two per SIMD) hide each wave's LDS reads and barrier waits
+// behind the other's MFMAs: at the 70B share a tile took 9 % fewer shader
+// cycles (319k vs 350k), but the clock under the chip's power limit fell by
+// as much (1.78 vs 2.00 GHz; 369 vs 372 us GEMM-only, 435 vs 412 us fused,
+// same process, alternating) -- the 4 x 2 grid reads 47 % more LDS bytes
+// per stage -- so the other tiles keep 4.
 template <int BM, int BN>
 constexpr int gemm_waves() {
   return BM == 320 ? 8 : 4;

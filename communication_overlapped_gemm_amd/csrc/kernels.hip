@@ -51,11 +51,12 @@ __device__ __forceinline__ void dma_flag(uint32_t lds, const uint32_t* g) {
 // non-coherent lines that the other tiles reuse), hence the doubling groups.
 template <int S, int PD>
 struct KslabHook {
-  uint64_t flagrow;          // wave 0 lane i < ndeps: address of slab_flag + dep_i * nks
-  OCG_LDS uint32_t* land;    // 64 words of LDS the prefetched flags land in
+  OCG_LDS const uint64_t* rows;   // LDS: address of slab_flag + dep_i * nks, i < ndeps (kept in
+                                  // LDS, not registers, for the whole K loop)
+  OCG_LDS uint32_t* land;         // 64 words of LDS the prefetched flags land in
   const Common* cm;
   uint32_t epoch, wait_ticks;
-  int wave, lane, ndeps, spk, nks, nk;
+  int wave, ndeps, spk, nks, nk;
   int g, j0, j1, check_k, prefetch_k;   // next group: K-slabs [j0, j1)
   bool prefetched;
 
@@ -65,7 +66,7 @@ struct KslabHook {
     const int gs = j1 - j0;
     const int i = (L / gs < ndeps) ? L / gs : 0;
     const int j = (L / gs < ndeps) ? j0 + L % gs : j0;
-    return (const uint32_t*)__shfl(flagrow, i) + j;
+    return (const uint32_t*)rows[i] + j;
   }
   __device__ void schedule() {
     prefetched = false;
@@ -82,7 +83,7 @@ struct KslabHook {
   }
   __device__ __forceinline__ void prefetch(int k) {
     if (k == prefetch_k) {
-      if (wave == 0) dma_flag(lds_u32(land), lane_flag(lane));
+      if (wave == 0) dma_flag(lds_u32(land), lane_flag(threadIdx.x & 63));
       prefetched = true;
     }
   }
@@ -90,14 +91,14 @@ struct KslabHook {
     if (k != check_k) return;
     if (wave == 0) {
       bool ok = false;
-      if (prefetched) ok = __ballot(land[lane] != epoch) == 0;
+      if (prefetched) ok = __ballot(land[threadIdx.x & 63] != epoch) == 0;
       if (ok) {
         asm volatile("buffer_inv sc1" ::: "memory");
       } else {
         const uint64_t t0 = now_ticks();
         FlagWait w(cm->timeout_ticks);
         for (int i = 0; i < ndeps; ++i)
-          for (int j = j0; j < j1; ++j) w((const uint32_t*)__shfl(flagrow, i) + j, epoch);
+          for (int j = j0; j < j1; ++j) w((const uint32_t*)rows[i] + j, epoch);
         uint32_t seen;
         w.finish(*cm, &seen);
         wait_ticks += (uint32_t)(now_ticks() - t0);
@@ -112,6 +113,7 @@ template <int BM, int BN>
 __global__ __launch_bounds__((Gemm<BM, BN>::NT), 1) void ag_gemm_kernel(AgArgs args) {
   using G = Gemm<BM, BN>;
   __shared__ __attribute__((aligned(1024))) char smem_raw[G::LDS_BYTES + 256];
+  __shared__ uint64_t s_deprow[64];   // flag rows of the tile's dependency slabs
   __shared__ uint32_t s_bcast[8];
   OCG_LDS char* smem = (OCG_LDS char*)smem_raw;
   const AgPlan& p = args.plan;
@@ -129,7 +131,7 @@ __global__ __launch_bounds__((Gemm<BM, BN>::NT), 1) void ag_gemm_kernel(AgArgs a
     run_copy_task<G::NT>(p, args.chunks, args.a_gathered, args.slab_cnt, args.slab_flag, (int)u, epoch, cm);
   }
   // GEMM tiles
-  int q = (int)s_bcast[3] % kXcds, tried = 0;
+  int q = (int)__builtin_amdgcn_readfirstlane(s_bcast[3]) % kXcds, tried = 0;
   uint32_t qt = 0;
   TileCtx<BM, BN> t;
   t.brs = make_rsrc(args.b, (uint32_t)((size_t)p.K * p.N * 2));
@@ -158,6 +160,8 @@ __global__ __launch_bounds__((Gemm<BM, BN>::NT), 1) void ag_gemm_kernel(AgArgs a
       FlagWait w(cm.timeout_ticks);
       for (int i = 0; i < ndeps; ++i) w((const uint32_t*)__shfl(myrow, i), epoch);
       w.finish(cm, &seen);
+      seen = __builtin_amdgcn_readfirstlane(seen);
+      s_deprow[lane] = myrow;
     }
     const uint64_t t1 = now_ticks();
     __syncthreads();
@@ -174,13 +178,12 @@ __global__ __launch_bounds__((Gemm<BM, BN>::NT), 1) void ag_gemm_kernel(AgArgs a
     t.n0 = n0;
     AccTile<BM, BN> acc;
     KslabHook<G::S, (G::S >= 6 ? 2 : 1)> hook;
-    hook.flagrow = myrow;
+    hook.rows = (OCG_LDS const uint64_t*)s_deprow;
     hook.land = (OCG_LDS uint32_t*)(smem + G::LDS_BYTES);
     hook.cm = &cm;
     hook.epoch = epoch;
     hook.wait_ticks = 0;
     hook.wave = wave;
-    hook.lane = lane;
     hook.ndeps = ndeps;
     hook.spk = spk;
     hook.nks = ndeps > 0 ? p.nks : 0;   // no dependency: nothing to check
@@ -276,7 +279,7 @@ __global__ __launch_bounds__((Gemm<BM, BN>::NT), 1) void gemm_rs_kernel(RsArgs a
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
 
-  int q = (int)s_bcast[3] % kXcds, tried = 0;
+  int q = (int)__builtin_amdgcn_readfirstlane(s_bcast[3]) % kXcds, tried = 0;
   uint32_t qt = 0;
   TileCtx<BM, BN> t;
   t.brs = make_rsrc(args.b, (uint32_t)((size_t)p.K * p.N * 2));
@@ -532,7 +535,7 @@ __global__ __launch_bounds__((Gemm<BM, BN>::NT), 1) void moe_gemm_kernel(MoeArgs
     if ((int)u >= p.n_copy) break;
     run_copy_task<G::NT>(p, args.chunks, args.a_gathered, args.slab_cnt, args.slab_flag, (int)u, epoch, cm);
   }
-  int q = (int)s_bcast[3] % kXcds, tried = 0;
+  int q = (int)__builtin_amdgcn_readfirstlane(s_bcast[3]) % kXcds, tried = 0;
   uint32_t qt = 0;
   TileCtx<BM, BN> t;
   t.N = p.N;
@@ -733,6 +736,11 @@ hipError_t noalloc_scratch_setup(int device, void** out) {
 }
 
 // ---------------------------------------------------------------- launchers
+
+static_assert(gemm_waves<256, 224>() == 4 && gemm_waves<128, 224>() == 4 && gemm_waves<128, 256>() == 4 &&
+                  gemm_waves<128, 128>() == 4 && gemm_waves<256, 256>() == 4 && gemm_waves<288, 224>() == 4 &&
+                  gemm_waves<320, 224>() == 8,
+              "tile_waves (host planning) must match the engine");
 
 template <int BM, int BN>
 static hipError_t ag_launch(const AgArgs& a, int grid, hipStream_t s) {

@@ -282,5 +282,7 @@ OCG_HD int attn_block_chunk(const AttnPlan& p, int j) {
 // Tile presets: {BM, BN} = {256,224}, {128,224}, {128,256}, {128,128}.
 OCG_HD int tile_bm(int t) { return t == 6 ? 288 : t == 5 ? 320 : ((t == 0 || t == 4) ? 256 : 128); }
 OCG_HD int tile_bn(int t) { return (t == 2 || t == 4) ? 256 : (t == 3 ? 128 : 224); }
+// Waves per workgroup of a preset's GEMM kernels (the engine's gemm_waves).
+OCG_HD int tile_waves(int t) { return tile_bm(t) == 320 ? 8 : 4; }
 
 }  // namespace ocg

@@ -237,7 +237,7 @@ __device__ __forceinline__ uint32_t read_epoch(WsHeader* hdr, uint32_t* s_bcast)
     s_bcast[3] = xcc_id();
   }
   __syncthreads();
-  return s_bcast[1];
+  return __builtin_amdgcn_readfirstlane(s_bcast[1]);   // uniform: kept in a scalar register
 }
 
 __device__ __forceinline__ uint32_t next_ticket(uint32_t* counter, uint32_t* s_bcast) {
@@ -245,7 +245,7 @@ __device__ __forceinline__ uint32_t next_ticket(uint32_t* counter, uint32_t* s_b
   if (threadIdx.x == 0)
     s_bcast[0] = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
-  return s_bcast[0];
+  return __builtin_amdgcn_readfirstlane(s_bcast[0]);
 }
 
 // Next tile from the XCD queues: own XCD first, then the others. `*q` is the
@@ -281,7 +281,7 @@ __device__ __forceinline__ int next_tile(WsHeader* hdr, int n_tiles, int* q, int
       if (threadIdx.x == 0) s_bcast[5] = (uint32_t)m;
     }
     __syncthreads();
-    const uint32_t mask = s_bcast[5];
+    const uint32_t mask = __builtin_amdgcn_readfirstlane(s_bcast[5]);
     if (mask == 0) return -1;
     // next open queue after *q, cyclically
     const uint32_t rot = ((mask >> ((*q + 1) % kXcds)) | (mask << (kXcds - (*q + 1) % kXcds))) & 0xFFu;

@@ -137,7 +137,7 @@ AG_CASES = [
 
 def ag_grid_tiles(info, R, m, N):
     """Tiles per round of the persistent GEMM grid on a 256-CU MI355X: one
-    workgroup per CU (two for the 128x128 tile, by LDS)."""
+    workgroup per CU (two for the 128x128 tile, by LDS and registers)."""
     return 256 * (2 if (info["BM"], info["BN"]) == (128, 128) else 1)
 
 
