@@ -363,9 +363,24 @@ def op_setups(torch, ocg, workloads, upload):
         part = torch.empty((x.M, x.N), dtype=torch.bfloat16, device="cuda")
         o = torch.empty((x.M // x.R, x.N), dtype=torch.bfloat16, device="cuda")
         ws = ocg.Workspace(ocg.OP_GEMM_RS, x.R, x.M, x.K, x.N)
+        # push transfers: stand-in receive buffers / flags of every rank; the
+        # peers' pushes into ours are in place and flagged before each call
+        blk = x.M // x.R
+        info = ocg.plan_info(ocg.OP_GEMM_RS, x.R, 0, x.M, x.K, x.N, handle=ocg.handle())
+        T = (blk // info["BM"]) * (-(-x.N // info["BN"]))
+        recv = [torch.empty((x.R, blk, x.N), dtype=torch.bfloat16, device="cuda") for _ in range(x.R)]
+        flags = [torch.zeros(x.R * T, dtype=torch.int32, device="cuda") for _ in range(x.R)]
+        for s in range(1, x.R):
+            recv[0][s].copy_(peers[s][:blk])
+        step = [0]
 
         def launch(mode=0):
-            ocg.gemm_rs(a, b, peers, 0, partial=part, out=o, workspace=ws)
+            if mode == 3:      # push
+                step[0] += 1
+                ocg.signal(flags[0][T:], step[0])
+                ocg.gemm_rs_push(a, b, recv, flags, step[0], 0, out=o, workspace=ws)
+            else:
+                ocg.gemm_rs(a, b, peers, 0, partial=part, out=o, workspace=ws)
         return w, x, ws, launch
 
     def moe():
@@ -429,12 +444,20 @@ def other_ops(torch, np, ocg, workloads, upload, stream, n):
                          "tflops": round(w.flops() / (times["fused"] * 1e-3) / 1e12, 2),
                          "e_max": round(max(times["gemm"], times["copy"]) / times["fused"], 4)}
     del launch
-    # GEMM-ReduceScatter share
+    # GEMM-ReduceScatter share: pull (the default) and push transfers, in
+    # alternation (push includes the peer-notify stand-in launch)
     w, x, ws, launch = setups["gemm_rs_8b"]()
-    t = median_ms(torch, launch, n, stream)
+    samples = {"pull": [], "push": []}
+    for _ in range(3):
+        for label, mode in (("pull", 0), ("push", 3)):
+            launch(mode)
+            samples[label] += timed_launches(torch, lambda: launch(mode), max(n // 3, 5), stream)
+    t, t_push = statistics.median(samples["pull"]), statistics.median(samples["push"])
     ws.check()
     blk_bytes = (x.M // x.R) * x.N * 2
     out["gemm_rs_8b"] = {"t_us": round(t * 1e3, 2), "tflops": round(w.flops() / (t * 1e-3) / 1e12, 2),
+                         "t_push_us": round(t_push * 1e3, 2),
+                         "push_tflops": round(w.flops() / (t_push * 1e-3) / 1e12, 2),
                          "reduce_bytes": 9 * blk_bytes}
     del launch
     # AllGather + MoE grouped GEMM

@@ -466,17 +466,20 @@ int ocg_ag_gemm_noalloc(ocg_handle h, const void* const* a_chunks, int R, int lo
                      stream);
 }
 
-int ocg_gemm_rs(ocg_handle h, const void* A, const void* B, int64_t M, int64_t K, int64_t N, int R, int local_rank,
-                const void* const* peer_partials, void* partial, void* out, void* ws, size_t ws_bytes,
-                const ocg_config* cfgp, void* stream) {
-  if (!h || !A || !B || !peer_partials || !partial || !out || !ws) return OCG_ERR_INVALID_ARG;
+}  // extern "C"
+
+namespace {
+
+// Shared part of the pull and push GEMM-ReduceScatter calls: checks, plan,
+// launch. `fill` sets the mode-specific fields of the arguments.
+template <class Fill>
+int gemm_rs_call(ocg_handle h, const void* A, const void* B, int64_t M, int64_t K, int64_t N, int R, int local_rank,
+                 void* out, void* ws, size_t ws_bytes, const ocg_config* cfgp, void* stream, bool push, Fill fill) {
+  if (!h || !A || !B || !out || !ws) return OCG_ERR_INVALID_ARG;
   if (R < 1 || R > kMaxRanks || M < R || M % R) return OCG_ERR_UNSUPPORTED_SHAPE;
   if (!shape_ok(1, M, K, N)) return OCG_ERR_UNSUPPORTED_SHAPE;
   if (local_rank < 0 || local_rank >= R) return OCG_ERR_INVALID_ARG;
-  for (int s = 0; s < R; ++s)
-    if (s != local_rank && (!peer_partials[s] || !aligned16(peer_partials[s]))) return OCG_ERR_INVALID_ARG;
-  if (!aligned16(A) || !aligned16(B) || !aligned16(partial) || !aligned16(out) || !aligned16(ws))
-    return OCG_ERR_INVALID_ARG;
+  if (!aligned16(A) || !aligned16(B) || !aligned16(out) || !aligned16(ws)) return OCG_ERR_INVALID_ARG;
   ocg_config cfg = cfg_or_default(cfgp);
   WsLayout L = layout(OCG_OP_GEMM_RS, R, M, K, N, 0, 0);
   if (ws_bytes < L.total) return OCG_ERR_WORKSPACE_TOO_SMALL;
@@ -487,20 +490,70 @@ int ocg_gemm_rs(ocg_handle h, const void* A, const void* B, int64_t M, int64_t K
   RsArgs a{};
   a.a = (const uint16_t*)A;
   a.b = (const uint16_t*)B;
-  for (int s = 0; s < R; ++s) a.peers[s] = (s == local_rank) ? nullptr : (const uint16_t*)peer_partials[s];
-  a.partial = (uint16_t*)partial;
   a.out = (uint16_t*)out;
   a.tile_flag = (uint32_t*)((char*)ws + L.rs_flag);
-  a.plan = make_rs_plan(R, local_rank, (int)M, (int)K, (int)N, rv.BM, rv.BN, reduce_rows(M, R, N, h->cus), cfg.swizzle ? 1 : 0);
+  a.plan = make_rs_plan(R, local_rank, (int)M, (int)K, (int)N, rv.BM, rv.BN, reduce_rows(M, R, N, h->cus),
+                        cfg.swizzle ? 1 : 0, push ? 1 : 0);
   if (a.plan.n_tiles > L.max_rs_tiles) return OCG_ERR_INVALID_ARG;
-  a.peer_flags = cfg.peer_flags;
-  a.peer_flag_value = cfg.peer_flag_value;
   a.local_rb0 = (local_rank * a.plan.blk) / rv.BM;
   a.local_nrb = cdiv(a.plan.blk, rv.BM);
-  if (cfg.peer_flags && a.plan.blk % rv.BM) return OCG_ERR_UNSUPPORTED_SHAPE;
+  a.tpb = a.local_nrb * a.plan.n_cb;
+  a.push = push ? 1 : 0;
+  st = fill(a, cfg, rv);
+  if (st) return st;
   a.cm = make_common(ws, cfg);
   int grid = grid_for(h, OCG_OP_GEMM_RS, rv.tile, a.plan.n_tiles + a.plan.n_red, cfg);
   return launch_gemm_rs(a, rv.tile, grid, (hipStream_t)stream) == hipSuccess ? OCG_OK : OCG_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ocg_gemm_rs(ocg_handle h, const void* A, const void* B, int64_t M, int64_t K, int64_t N, int R, int local_rank,
+                const void* const* peer_partials, void* partial, void* out, void* ws, size_t ws_bytes,
+                const ocg_config* cfgp, void* stream) {
+  if (!peer_partials || !partial) return OCG_ERR_INVALID_ARG;
+  if (R >= 1 && R <= kMaxRanks && local_rank >= 0 && local_rank < R)
+    for (int s = 0; s < R; ++s)
+      if (s != local_rank && (!peer_partials[s] || !aligned16(peer_partials[s]))) return OCG_ERR_INVALID_ARG;
+  if (!aligned16(partial)) return OCG_ERR_INVALID_ARG;
+  return gemm_rs_call(h, A, B, M, K, N, R, local_rank, out, ws, ws_bytes, cfgp, stream, false,
+                      [&](RsArgs& a, const ocg_config& cfg, const Resolved& rv) {
+                        for (int s = 0; s < R; ++s) {
+                          a.dst[s] = (uint16_t*)partial;
+                          a.src[s] = (s == local_rank) ? (const uint16_t*)partial : (const uint16_t*)peer_partials[s];
+                        }
+                        a.peer_flags = cfg.peer_flags;
+                        a.peer_flag_value = cfg.peer_flag_value;
+                        if (cfg.peer_flags && a.plan.blk % rv.BM) return OCG_ERR_UNSUPPORTED_SHAPE;
+                        return OCG_OK;
+                      });
+}
+
+int ocg_gemm_rs_push(ocg_handle h, const void* A, const void* B, int64_t M, int64_t K, int64_t N, int R,
+                     int local_rank, void* const* recv, uint32_t* const* recv_flags, uint32_t flag_value, void* out,
+                     void* ws, size_t ws_bytes, const ocg_config* cfgp, void* stream) {
+  if (!recv || !recv_flags) return OCG_ERR_INVALID_ARG;
+  if (R < 1 || R > kMaxRanks) return OCG_ERR_UNSUPPORTED_SHAPE;
+  for (int s = 0; s < R; ++s)
+    if (!recv[s] || !aligned16(recv[s]) || !recv_flags[s] || ((uintptr_t)recv_flags[s] & 3)) return OCG_ERR_INVALID_ARG;
+  return gemm_rs_call(h, A, B, M, K, N, R, local_rank, out, ws, ws_bytes, cfgp, stream, true,
+                      [&](RsArgs& a, const ocg_config& cfg, const Resolved& rv) {
+                        (void)cfg;
+                        if (a.plan.blk % rv.BM) return OCG_ERR_UNSUPPORTED_SHAPE;   // a tile in one row block
+                        const int64_t blk = a.plan.blk;
+                        for (int s = 0; s < R; ++s) {
+                          // rank s's slot `local` holds rows [s*blk, (s+1)*blk) of our partial:
+                          // global row r -> slot row r - s*blk
+                          a.dst[s] = (uint16_t*)recv[s] + (local_rank - s) * blk * N;
+                          // our slot s holds rank s's rows of our block: row r -> r - local*blk
+                          a.src[s] = (const uint16_t*)recv[local_rank] + (s - local_rank) * blk * N;
+                          a.rflag[s] = recv_flags[s];
+                        }
+                        a.flag_value = flag_value;
+                        return OCG_OK;
+                      });
 }
 
 int ocg_ag_grouped_gemm(ocg_handle h, const void* const* a_chunks, int R, int local_rank, int64_t m, int64_t K,

@@ -240,10 +240,7 @@ __device__ void run_reduce_strip(const RsArgs& a, int r0, int r1) {
       if (i >= n16) continue;
 #pragma unroll
       for (int s = 0; s < kMaxRanks; ++s) {
-        if (s < p.R) {
-          const uint16_t* src = (s == p.local) ? a.partial : a.peers[s];
-          v[u][s] = gload16(src + (first + i) * 8);
-        }
+        if (s < p.R) v[u][s] = gload16(a.src[s] + (first + i) * 8);
       }
     }
 #pragma unroll
@@ -302,18 +299,25 @@ __global__ __launch_bounds__((Gemm<BM, BN>::NT), 1) void gemm_rs_kernel(RsArgs a
     AccTile<BM, BN> acc;
     mainloop<BM, BN>(smem, t, acc);
     stage_c<BM, BN>(smem, acc);
-    // The bf16 partial tile (the send buffer) is consumed by reduce strips of
-    // this launch: agent-coherent stores, rows r0.. of the partial.
+    // The bf16 partial tile is consumed by reduce strips of this launch (or,
+    // pushed, by the rank that owns its row block): agent-coherent stores.
     const int rows = min(BM, p.M - r0);
-    const __amdgpu_buffer_rsrc_t prs = make_rsrc(args.partial + (size_t)r0 * p.N, (uint32_t)((size_t)rows * p.N * 2));
+    const int sblk = r0 / p.blk;   // row block (rank) the tile belongs to
+    const __amdgpu_buffer_rsrc_t prs =
+        make_rsrc(args.dst[sblk] + (size_t)r0 * p.N, (uint32_t)((size_t)rows * p.N * 2));
     for_each_c_chunk<BM, BN>(smem, [&](int row, int col, u32x4_t val) {
       if (row < rows && n0 + col < p.N) store16_agent(prs, (uint32_t)(((size_t)row * p.N + n0 + col) * 2), val);
     });
-    // produce_tile_notify
+    // produce_tile_notify (pull: our tile flag; push: the owner's receive flag)
     drain_stores();
     __syncthreads();
-    if (threadIdx.x == 0)
-      __hip_atomic_store(&args.tile_flag[rb * p.n_cb + cb], epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (threadIdx.x == 0) {
+      if (args.push)
+        __hip_atomic_store(&args.rflag[sblk][p.local * args.tpb + (rb - sblk * args.local_nrb) * p.n_cb + cb],
+                           args.flag_value, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      else
+        __hip_atomic_store(&args.tile_flag[rb * p.n_cb + cb], epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
     trace_task(cm, (uint32_t)v, 3, rb, cb, rs_tile_touches_local(p, rb) ? 1u : 0u, 0, epoch, t0, t0, 0,
                ((uint32_t)q << 16) | qt);
   }
@@ -332,9 +336,14 @@ __global__ __launch_bounds__((Gemm<BM, BN>::NT), 1) void gemm_rs_kernel(RsArgs a
       FlagWait w(cm.timeout_ticks);
       for (int rb = r0 / BM; rb <= (r1 - 1) / BM; ++rb)
         for (int cb = 0; cb < p.n_cb; ++cb) {
+          const int t_local = (rb - args.local_rb0) * p.n_cb + cb;
+          if (args.push) {
+            // every rank's pushed tile in our receive buffer, ours included
+            for (int s = 0; s < p.R; ++s) w(&args.rflag[p.local][s * args.tpb + t_local], args.flag_value);
+            continue;
+          }
           w(&args.tile_flag[rb * p.n_cb + cb], epoch);
           if (args.peer_flags) {
-            const int t_local = (rb - args.local_rb0) * p.n_cb + cb;
             const int per_rank = args.local_nrb * p.n_cb;
             for (int s = 0; s < p.R; ++s)
               if (s != p.local) w(&args.peer_flags[s * per_rank + t_local], args.peer_flag_value);

@@ -67,15 +67,27 @@ struct AgArgs {
   Common cm;
 };
 
+// GEMM-ReduceScatter. Pull (push = 0): tiles store the partial into
+// `partial` and notify tile_flag[rb * n_cb + cb] = epoch; the reduce reads
+// every rank's partial where it lives. Push (push = 1): the tile of row
+// block s goes straight to rank s's receive buffer, slot `local`, and sets
+// that rank's flag rflag[s][local * tpb + t] = flag_value (t: the tile
+// within the block); the reduce reads our own receive buffer's R slots.
+// Addressing by global row r and column c, for both:
+//   tile store      dst[s] + r * N + c      (s = block of r)
+//   reduce operand  src[s] + r * N + c      (r in the local block)
 struct RsArgs {
   const uint16_t* a;
   const uint16_t* b;
-  const uint16_t* peers[kMaxRanks];
-  uint16_t* partial;
+  const uint16_t* src[kMaxRanks];
+  uint16_t* dst[kMaxRanks];
   uint16_t* out;
-  uint32_t* tile_flag;          // notify flag per tile (row-major rb*n_cb+cb)
-  const uint32_t* peer_flags;   // [R][local-block tiles] or null (local block aligned to BM)
+  uint32_t* tile_flag;          // pull: notify flag per tile (row-major rb*n_cb+cb)
+  const uint32_t* peer_flags;   // pull: [R][local-block tiles] or null (local block aligned to BM)
   uint32_t peer_flag_value;
+  uint32_t* rflag[kMaxRanks];   // push: rank s's receive flags [R][tpb]
+  uint32_t flag_value;          // push: value of a set flag (this call's)
+  int push, tpb;                // tpb: tiles per row block (push)
   int local_rb0, local_nrb;     // row blocks of the local block (peer flag indexing)
   RsPlan plan;
   Common cm;

@@ -215,7 +215,12 @@ struct RsPlan {
   int n_rb, n_cb, n_tiles, n_red, rb0;
 };
 
-OCG_HD RsPlan make_rs_plan(int R, int local, int M, int K, int N, int BM, int BN, int RR, int swizzle) {
+// push: the partials are pushed to their owners, so the tiles start at the
+// block after the local one (local + 1, local + 2, ..., local last): every
+// peer's data leaves as early as possible and the local block, reduced here,
+// comes last.
+OCG_HD RsPlan make_rs_plan(int R, int local, int M, int K, int N, int BM, int BN, int RR, int swizzle,
+                           int push = 0) {
   RsPlan p;
   p.R = R; p.local = local; p.M = M; p.K = K; p.N = N; p.BM = BM; p.BN = BN; p.RR = RR;
   p.blk = M / R;
@@ -223,7 +228,8 @@ OCG_HD RsPlan make_rs_plan(int R, int local, int M, int K, int N, int BM, int BN
   p.n_cb = cdiv(N, BN);
   p.n_tiles = p.n_rb * p.n_cb;
   p.n_red = cdiv(p.blk, RR);
-  p.rb0 = swizzle ? (int)(((long long)local * p.blk) / BM) : 0;
+  const int first = push ? (local + 1) % R : local;
+  p.rb0 = swizzle ? (int)(((long long)first * p.blk) / BM) : 0;
   return p;
 }
 

@@ -176,6 +176,37 @@ def gemm_rs(a: torch.Tensor, b: torch.Tensor, peer_partials: Sequence[Optional[t
     return partial, out
 
 
+def gemm_rs_push(a: torch.Tensor, b: torch.Tensor, recv: Sequence[torch.Tensor], recv_flags: Sequence[torch.Tensor],
+                 flag_value: int, local_rank: int = 0, *, out: Optional[torch.Tensor] = None,
+                 workspace: Optional[Workspace] = None, config: Optional[Config] = None, stream=None) -> torch.Tensor:
+    """GEMM-ReduceScatter with push transfers: recv[r] bf16 [R, M/R, N] and
+    recv_flags[r] int32 [R, tiles per row block] of every rank r (stand-ins
+    on one GPU). Returns out [M/R, N]."""
+    R = len(recv)
+    M, K = a.shape
+    N = b.shape[1]
+    _check_bf16(a, "a")
+    _check_bf16(b, "b", (K, N))
+    if len(recv_flags) != R:
+        raise ValueError("one receive flag array per rank")
+    for r in range(R):
+        _check_bf16(recv[r], f"recv[{r}]", (R, M // R, N))
+        if recv_flags[r].dtype not in (torch.int32, torch.uint32) or not recv_flags[r].is_contiguous():
+            raise ValueError("recv_flags must be contiguous 32-bit tensors")
+    dev = a.device
+    if out is None:
+        out = torch.empty((M // R, N), dtype=torch.bfloat16, device=dev)
+    _check_bf16(out, "out", (M // R, N))
+    ws = workspace or Workspace.cached(_lib.OP_GEMM_RS, R, M, K, N, device=dev.index, stream=stream)
+    rp = (C.c_void_p * R)(*[t.data_ptr() for t in recv])
+    fp = (C.c_void_p * R)(*[t.data_ptr() for t in recv_flags])
+    cfg = _cfg(config)
+    check(lib.ocg_gemm_rs_push(handle(dev.index), a.data_ptr(), b.data_ptr(), M, K, N, R, local_rank, rp, fp,
+                               flag_value & 0xFFFFFFFF, out.data_ptr(), ws.ptr, ws.nbytes, C.byref(cfg),
+                               _stream_ptr(stream)), "ocg_gemm_rs_push")
+    return out
+
+
 def ag_grouped_gemm(a_chunks: Sequence[torch.Tensor], logits: torch.Tensor, w: torch.Tensor, topk: int = 2,
                     local_rank: int = 0, *, workspace: Optional[Workspace] = None,
                     config: Optional[Config] = None, stream=None, outputs: Optional[dict] = None) -> dict:

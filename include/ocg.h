@@ -231,6 +231,37 @@ int ocg_gemm_rs(ocg_handle h, const void* a, const void* b, int64_t M, int64_t K
                 void* workspace, size_t ws_bytes, const ocg_config* cfg, void* stream);
 
 /*
+ * GEMM-ReduceScatter with push transfers (the one-barrier protocol: the
+ * producer writes the data and the flag into the consumer's memory, so no
+ * "ready to receive" handshake is needed -- every sender owns a slot; "TileLink
+ * ..." (MLSys 2025 talk summary), "Technical Deep Dive", push versus pull).
+ * Each rank s has a receive buffer recv[s], bf16 [R][M/R][N] (slot q holds
+ * rank q's partial of row block s), and receive flags recv_flags[s], uint32
+ * [R][T] (T = tiles per row block: (M/R / BM) * ceil(N / BN) for the
+ * resolved tile). This call computes partial = A x B tile by tile; the tile
+ * of row block s is rounded to bf16 and stored into recv[s] slot local_rank,
+ * then recv_flags[s][local_rank * T + t] = flag_value (t = the tile's index
+ * within the block, row-major); row block local_rank goes to our own slot.
+ * Tiles run blocks local+1, local+2, ..., local last (peers' data first).
+ * Then, waiting on recv_flags[local_rank][q * T + t] == flag_value for every
+ * rank q (peers' pushes, and our own), the reduce
+ *   out = bf16( sum over q = 0..R-1, in that order, of recv[local_rank][q] )
+ * runs in fp32 with one rounding, as ocg_gemm_rs (identical results).
+ *   a, b, M, K, N, R, local_rank, out, workspace: as ocg_gemm_rs
+ *   recv        : R device pointers (rank r's receive buffer; on one GPU,
+ *                 stand-ins in this GPU's memory), 16-byte aligned
+ *   recv_flags  : R device pointers (rank r's receive flags), 4-byte aligned
+ *   flag_value  : the value this call's pushes write; it must differ from
+ *                 every value those flags held before (e.g. a call counter)
+ * Requires M/R to be a multiple of the tile's rows (OCG_ERR_UNSUPPORTED_SHAPE
+ * otherwise); tile rows: ocg_plan_info(h, OCG_OP_GEMM_RS, ...) out[1]. Errors
+ * as for the other calls. */
+int ocg_gemm_rs_push(ocg_handle h, const void* a, const void* b, int64_t M, int64_t K, int64_t N,
+                     int R, int local_rank, void* const* recv, uint32_t* const* recv_flags,
+                     uint32_t flag_value, void* out, void* workspace, size_t ws_bytes,
+                     const ocg_config* cfg, void* stream);
+
+/*
  * AllGather + MoE grouped GEMM: tokens t = 0..R*m-1 of the gathered
  * activations are routed to the top-k experts of their fp32 logits (equal
  * logits: lower expert first; slot 0 = largest), grouped by expert (stable

@@ -51,8 +51,9 @@ BM x BN, slab rows S, copy-task rows CT with S % CT == 0, K-slab columns KS):
   A tile waits, for every K-slab it loads, on that K-slab's flag of each of
   its dependency slabs, before its first load of the K-slab.
 GEMM-RS: slots [0, n_tiles) are GEMM tiles in the same order and queues,
-  with rb0 = (l*M/R)//BM when swizzled; each stores its bf16 partial and
-  publishes its tile flag. Slots [n_tiles, n_tiles + ceil(blk/RR)) are
+  with rb0 = (l*M/R)//BM when swizzled -- with push transfers rb0 =
+  (((l+1) mod R)*M/R)//BM, so the local block comes last; each stores its
+  bf16 partial and publishes its tile flag. Slots [n_tiles, n_tiles + ceil(blk/RR)) are
   reduce tasks over RR-row strips of the local block [l*blk, (l+1)*blk),
   blk = M/R, in ascending row order; a strip waits for the flags of every
   tile of the row blocks it overlaps (and for the peers' flags of those
@@ -219,7 +220,7 @@ def ag_gemm_plan(R, m, K, N, local, BM, BN, S, CT, swizzle=True, mode="fused", K
     return tasks
 
 
-def gemm_rs_plan(R, M, N, local, BM, BN, RR, swizzle=True):
+def gemm_rs_plan(R, M, N, local, BM, BN, RR, swizzle=True, push=False):
     """Ticket list of the GEMM-RS kernel.
 
     Tiles: ("tile", slot, rb, cb, touches_local_block, queue, queue_ticket).
@@ -227,7 +228,8 @@ def gemm_rs_plan(R, M, N, local, BM, BN, RR, swizzle=True):
     [row0, row1) inside the local block and deps the (rb, cb) tiles waited on."""
     n_rb, n_cb = _cdiv(M, BM), _cdiv(N, BN)
     blk = M // R
-    rb0 = (local * blk) // BM if swizzle else 0
+    first = (local + 1) % R if push else local
+    rb0 = (first * blk) // BM if swizzle else 0
     out = []
     where = queue_of(n_rb * n_cb)
     for v, (rb, cb) in enumerate(tile_order(n_rb, n_cb, rb0)):
