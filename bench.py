@@ -185,7 +185,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--skip-extras", action="store_true")
     ap.add_argument("--op", default=WORKLOAD, choices=[WORKLOAD, "ag_gemm_8b", "gemm_rs_8b", "ag_moe", "moe_combine_rs",
-                                                     "ag_attention"],
+                                                     "ag_attention", "ag_moe_layer"],
                     help="profiling aid: launch only this operation (no benchmark record)")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -396,6 +396,28 @@ def op_setups(torch, ocg, workloads, upload):
             ocg.ag_grouped_gemm(chunks, lg, wt, x.topk, 0, workspace=ws, outputs=outs)
         return w, x, ws, launch
 
+    def layer():
+        w = workloads.workload("ag_moe_layer")
+        x = w.make()
+        pr = w.params
+        peers = workloads.make_moe_peers(pr["R"], pr["m"], pr["N"], pr["peer_seed"], pr["local_rank"])
+        chunks = [upload(a) for a in x.a_chunks]
+        lg = torch.from_numpy(x.logits).to("cuda")
+        wt = upload(x.w)
+        pp = [None if s_ == pr["local_rank"] else upload(peers[s_]) for s_ in range(x.R)]
+        ws = ocg.Workspace(ocg.OP_AG_GROUPED_GEMM, x.R, x.m, x.K, x.N, x.E, x.topk)
+        ws2 = ocg.Workspace(ocg.OP_MOE_COMBINE_RS, x.R, x.m, 0, x.N, 0, x.topk)
+        outs = ocg.ag_moe_layer(chunks, lg, wt, pp, x.topk, 0, workspace=ws)
+        g = ocg.ag_grouped_gemm(chunks, lg, wt, x.topk, 0, workspace=ws)
+
+        def launch(mode=0):
+            if mode == 0:      # the chain in one call
+                ocg.ag_moe_layer(chunks, lg, wt, pp, x.topk, 0, workspace=ws, outputs=outs)
+            else:              # the two calls one after the other
+                ocg.ag_grouped_gemm(chunks, lg, wt, x.topk, 0, workspace=ws, outputs=g)
+                ocg.moe_combine_rs(g["out"], g["topk_w"], pp, 0, workspace=ws2)
+        return w, x, ws, launch
+
     def comb():
         w = workloads.workload("moe_combine_rs")
         x = w.make()
@@ -428,7 +450,8 @@ def op_setups(torch, ocg, workloads, upload):
                              config=ocg.default_config(mode=mode))
         return w, x, ws, launch
 
-    return {"ag_gemm_8b": ag8, "gemm_rs_8b": rs8, "ag_moe": moe, "moe_combine_rs": comb, "ag_attention": attn}
+    return {"ag_gemm_8b": ag8, "gemm_rs_8b": rs8, "ag_moe": moe, "moe_combine_rs": comb, "ag_attention": attn,
+            "ag_moe_layer": layer}
 
 
 def other_ops(torch, np, ocg, workloads, upload, stream, n):
@@ -469,6 +492,22 @@ def other_ops(torch, np, ocg, workloads, upload, stream, n):
     out["ag_moe"] = {"t_us": round(t * 1e3, 2), "tflops": round(w.flops() / (t * 1e-3) / 1e12, 2),
                      "hbm_gbs_algorithmic": round(hbm / (t * 1e-3) / 1e9, 1),
                      "hbm_frac": round(hbm / (t * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+    del launch
+    # the MoE layer chain in one call against the two calls in sequence
+    w, x, ws, launch = setups["ag_moe_layer"]()
+    samples = {"chain": [], "separate": []}
+    for _ in range(3):
+        for label, mode in (("chain", 0), ("separate", 1)):
+            launch(mode)
+            samples[label] += timed_launches(torch, lambda: launch(mode), max(n // 3, 5), stream)
+    ws.check()
+    tc, tsep = statistics.median(samples["chain"]), statistics.median(samples["separate"])
+    T = x.R * x.m
+    hbm = (x.E * x.K * x.N * 2 + 2 * 7 * x.m * x.K * 2 + T * x.K * 2 + T * x.topk * x.N * 2 + T * x.E * 4
+           + T * x.topk * x.N * 2 + T * x.topk * 4 + T * x.N * 2 + x.R * x.m * x.N * 2 + x.m * x.N * 2)
+    out["ag_moe_layer"] = {"t_chain_us": round(tc * 1e3, 2), "t_separate_us": round(tsep * 1e3, 2),
+                           "hbm_bytes_algorithmic": hbm,
+                           "hbm_frac": round(hbm / (tc * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
     del launch
     # MoE TopK-Reduce + ReduceScatter (HBM-bound)
     w, x, ws, launch = setups["moe_combine_rs"]()

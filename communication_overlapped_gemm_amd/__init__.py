@@ -15,5 +15,5 @@ from ._lib import (  # noqa: F401
 )
 from .ops import (  # noqa: F401
     Workspace, ag_gemm, gemm_rs, ag_grouped_gemm, moe_combine_rs, ag_attention, signal, plan_info, plan_task, handle,
-    plan_ag, ag_gemm_noalloc, gemm_rs_push,
+    plan_ag, ag_gemm_noalloc, gemm_rs_push, ag_moe_layer,
 )

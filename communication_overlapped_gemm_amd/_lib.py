@@ -33,7 +33,7 @@ EXPORTS = [
     "ocg_workspace_init", "ocg_ag_gemm", "ocg_gemm_rs", "ocg_ag_grouped_gemm",
     "ocg_signal", "ocg_check", "ocg_status_string", "ocg_plan_info", "ocg_plan_task",
     "ocg_moe_combine_rs", "ocg_ag_attention", "ocg_plan_ag", "ocg_ag_gemm_noalloc",
-    "ocg_gemm_rs_push",
+    "ocg_gemm_rs_push", "ocg_ag_moe_layer",
 ]
 
 
@@ -78,6 +78,9 @@ def _declare(lib):
                                           C.c_int64, _P, _P, C.POINTER(Config), _P]),
         "ocg_gemm_rs": (C.c_int, [_P, _P, _P, C.c_int64, C.c_int64, C.c_int64, C.c_int, C.c_int,
                                   C.POINTER(_P), _P, _P, _P, C.c_size_t, C.POINTER(Config), _P]),
+        "ocg_ag_moe_layer": (C.c_int, [_P, C.POINTER(_P), C.c_int, C.c_int, C.c_int64, C.c_int64, _P,
+                                       C.c_int, C.c_int, _P, C.c_int64, C.POINTER(_P), _P, _P, _P, _P, _P,
+                                       _P, _P, _P, _P, C.c_size_t, C.POINTER(Config), _P]),
         "ocg_gemm_rs_push": (C.c_int, [_P, _P, _P, C.c_int64, C.c_int64, C.c_int64, C.c_int, C.c_int,
                                        C.POINTER(_P), C.POINTER(_P), C.c_uint32, _P, _P, C.c_size_t,
                                        C.POINTER(Config), _P]),

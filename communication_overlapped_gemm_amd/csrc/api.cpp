@@ -50,7 +50,7 @@ WsLayout layout(int op, int R, int64_t m, int64_t K, int64_t N, int E, int topk)
   off = align256(off + sizeof(uint32_t) * L.max_slabs);
   L.rs_flag = off;
   off = align256(off + sizeof(uint32_t) * L.max_rs_tiles);
-  L.moe_off = L.moe_lut = L.moe_perm = L.moe_bcnt = off;
+  L.moe_off = L.moe_lut = L.moe_perm = L.moe_bcnt = L.moe_inv = L.moe_lbase = L.moe_tflag = off;
   L.max_moe_tiles = 0;
   if (op == OCG_OP_AG_GROUPED_GEMM) {
     int slots = (int)(rows * topk);
@@ -65,6 +65,12 @@ WsLayout layout(int op, int R, int64_t m, int64_t K, int64_t N, int E, int topk)
     const int nb = cdiv((int)rows, kRouteBlock);
     L.moe_bcnt = off;
     off = align256(off + sizeof(int32_t) * (size_t)nb * E);
+    L.moe_inv = off;       // position of each token-slot in the sorted order
+    off = align256(off + sizeof(int32_t) * (size_t)slots);
+    L.moe_lbase = off;     // first lookup-table entry of each expert
+    off = align256(off + sizeof(int32_t) * (size_t)E);
+    L.moe_tflag = off;     // per grouped tile: epoch once its rows are stored
+    off = align256(off + sizeof(uint32_t) * (size_t)L.max_moe_tiles);
   }
   (void)K;
   L.total = off;
@@ -556,10 +562,22 @@ int ocg_gemm_rs_push(ocg_handle h, const void* A, const void* B, int64_t M, int6
                       });
 }
 
-int ocg_ag_grouped_gemm(ocg_handle h, const void* const* a_chunks, int R, int local_rank, int64_t m, int64_t K,
-                        const float* logits, int E, int topk, const void* w, int64_t N, void* a_gathered,
-                        int32_t* topk_ids, float* topk_w, int32_t* perm, int32_t* expert_offsets, void* out,
-                        void* ws, size_t ws_bytes, const ocg_config* cfgp, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// AllGather + routing + grouped GEMM, and (layer != NULL) the TopK-Reduce +
+// ReduceScatter tasks of the layer chain in the same persistent kernel.
+struct LayerOut {
+  const void* const* peer_partials;
+  void* partial;
+  void* out;
+};
+
+int grouped_call(ocg_handle h, const void* const* a_chunks, int R, int local_rank, int64_t m, int64_t K,
+                 const float* logits, int E, int topk, const void* w, int64_t N, void* a_gathered, int32_t* topk_ids,
+                 float* topk_w, int32_t* perm, int32_t* expert_offsets, void* out, void* ws, size_t ws_bytes,
+                 const ocg_config* cfgp, void* stream, const LayerOut* layer) {
   if (!h || !a_chunks || !logits || !w || !a_gathered || !topk_ids || !topk_w || !out || !ws)
     return OCG_ERR_INVALID_ARG;
   if (!shape_ok(R, m, K, N)) return OCG_ERR_UNSUPPORTED_SHAPE;
@@ -603,6 +621,8 @@ int ocg_ag_grouped_gemm(ocg_handle h, const void* const* a_chunks, int R, int lo
   r.user_offsets = expert_offsets;
   r.lut = (int32_t*)((char*)ws + L.moe_lut);
   r.blk_cnt = (int32_t*)((char*)ws + L.moe_bcnt);
+  r.inv = (int32_t*)((char*)ws + L.moe_inv);
+  r.lut_base = (int32_t*)((char*)ws + L.moe_lbase);
   r.hdr = (WsHeader*)ws;
   r.T = (int)(R * m);
   r.E = E;
@@ -610,8 +630,64 @@ int ocg_ag_grouped_gemm(ocg_handle h, const void* const* a_chunks, int R, int lo
   r.BM = rv.BM;
   r.n_cb = cdiv((int)N, rv.BN);
   r.max_tiles = L.max_moe_tiles;
+  if (layer) {
+    const int64_t T = (int64_t)R * m;
+    if (!combine_shape_ok(R, m, N, topk) || T * topk * N * 2 >= ((int64_t)1 << 31)) return OCG_ERR_UNSUPPORTED_SHAPE;
+    a.combine = 1;
+    a.BM = rv.BM;
+    a.n_cb = cdiv((int)N, rv.BN);
+    a.tflag = (uint32_t*)((char*)ws + L.moe_tflag);
+    a.inv = r.inv;
+    a.lut_base = r.lut_base;
+    a.offsets = r.offsets;
+    a.topk_ids = topk_ids;
+    CombArgs& c = a.comb;
+    c.y = (const uint16_t*)out;
+    c.w = topk_w;
+    for (int s = 0; s < R; ++s)
+      c.peers[s] = (s == local_rank) ? nullptr : (const uint16_t*)layer->peer_partials[s];
+    c.partial = (uint16_t*)layer->partial;
+    c.out = (uint16_t*)layer->out;
+    c.topk = topk;
+    combine_rows(R, m, topk, h->cus, &c.CRL, &c.CR);
+    c.n_lt = cdiv((int)m, c.CRL);
+    c.n_comb = c.n_lt + cdiv((int)(T - m), c.CR);
+    c.R = R;
+    c.local = local_rank;
+    c.m = (int)m;
+    c.T = (int)T;
+    c.N = (int)N;
+    c.max_tiles = L.max_moe_tiles;
+  }
   int grid = grid_for(h, OCG_OP_AG_GROUPED_GEMM, rv.tile, a.plan.n_copy + L.max_moe_tiles, cfg);
   return launch_moe(r, a, rv.tile, grid, (hipStream_t)stream) == hipSuccess ? OCG_OK : OCG_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ocg_ag_grouped_gemm(ocg_handle h, const void* const* a_chunks, int R, int local_rank, int64_t m, int64_t K,
+                        const float* logits, int E, int topk, const void* w, int64_t N, void* a_gathered,
+                        int32_t* topk_ids, float* topk_w, int32_t* perm, int32_t* expert_offsets, void* out,
+                        void* ws, size_t ws_bytes, const ocg_config* cfgp, void* stream) {
+  return grouped_call(h, a_chunks, R, local_rank, m, K, logits, E, topk, w, N, a_gathered, topk_ids, topk_w, perm,
+                      expert_offsets, out, ws, ws_bytes, cfgp, stream, nullptr);
+}
+
+int ocg_ag_moe_layer(ocg_handle h, const void* const* a_chunks, int R, int local_rank, int64_t m, int64_t K,
+                     const float* logits, int E, int topk, const void* w, int64_t N,
+                     const void* const* peer_partials, void* a_gathered, int32_t* topk_ids, float* topk_w,
+                     int32_t* perm, int32_t* expert_offsets, void* y, void* partial, void* out, void* ws,
+                     size_t ws_bytes, const ocg_config* cfgp, void* stream) {
+  if (!peer_partials || !partial || !out || !y) return OCG_ERR_INVALID_ARG;
+  if (R < 1 || R > kMaxRanks || local_rank < 0 || local_rank >= R) return OCG_ERR_INVALID_ARG;
+  for (int s = 0; s < R; ++s)
+    if (s != local_rank && (!peer_partials[s] || !aligned16(peer_partials[s]))) return OCG_ERR_INVALID_ARG;
+  if (!aligned16(partial) || !aligned16(out) || ((uintptr_t)topk_w & 3)) return OCG_ERR_INVALID_ARG;
+  LayerOut lo{peer_partials, partial, out};
+  return grouped_call(h, a_chunks, R, local_rank, m, K, logits, E, topk, w, N, a_gathered, topk_ids, topk_w, perm,
+                      expert_offsets, y, ws, ws_bytes, cfgp, stream, &lo);
 }
 
 int ocg_signal(uint32_t* flags, int count, uint32_t value, void* stream) {

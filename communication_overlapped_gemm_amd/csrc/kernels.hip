@@ -486,6 +486,7 @@ __global__ __launch_bounds__(kRouteBlock) void moe_scatter_kernel(RouteArgs a) {
     int n_ent;
     const int tb = wave_excl_scan(nrt * a.n_cb, &n_ent);
     if (lane == 0) a.hdr->n_tiles = (uint32_t)min(n_ent, a.max_tiles);
+    if (lane < E) a.lut_base[lane] = tb;
     for (int j = 0; j < nrt * a.n_cb; ++j) {
       const int i = tb + j;
       if (i >= a.max_tiles) break;
@@ -512,7 +513,9 @@ __global__ __launch_bounds__(kRouteBlock) void moe_scatter_kernel(RouteArgs a) {
     }
     if (e >= 0) {
       const int base = s_run[e];
-      a.perm[base + __builtin_popcountll(same & ((1ull << lane) - 1ull))] = s;
+      const int pos = base + __builtin_popcountll(same & ((1ull << lane) - 1ull));
+      a.perm[pos] = s;
+      a.inv[s] = pos;
     }
     __syncthreads();
     // the highest lane of each expert's group advances that expert's base
@@ -521,7 +524,135 @@ __global__ __launch_bounds__(kRouteBlock) void moe_scatter_kernel(RouteArgs a) {
   }
 }
 
+// ---------------------------------------------------------------- TopK-Reduce + ReduceScatter
+
+// Rows [r0, r1) of the token order rotated to start at the local block
+// (row t = (r + local*m) mod T): each row's 16-byte column chunks summed over
+// its top-k slot rows in slot order, weight times value in fp32, rounded
+// once to bf16 and stored to the partial. LOCAL rows (r < m) also finish the
+// ReduceScatter on the spot: the R ranks' bf16 rows summed in ascending rank
+// order in fp32 (the local one as just rounded) and rounded once into out.
+// U chunks per thread in flight per round.
+template <bool LOCAL, int U, int K, int NT = kThreads>
+__device__ void combine_rows(const CombArgs& a, int r0, int r1) {
+  const int T = a.T, N = a.N, n8 = N / 8, base = a.local * a.m;
+  const int n16 = (r1 - r0) * n8;
+  for (int b0 = threadIdx.x; b0 < n16; b0 += U * NT) {
+    u32x4_t v[U][K];
+    u32x4_t pv[U][LOCAL ? kMaxRanks : 1];
+    float wt[U][K];
+    int row[U], c8[U];
+#pragma unroll
+    for (int q = 0; q < U; ++q) {
+      const int i = b0 + q * NT;
+      row[q] = -1;
+      if (i >= n16) continue;
+      const int rr = r0 + i / n8;
+      const int t = rr + base < T ? rr + base : rr + base - T;
+      row[q] = t;
+      c8[q] = i - (i / n8) * n8;
+#pragma unroll
+      for (int j = 0; j < K; ++j) {
+        v[q][j] = gload16(a.y + ((size_t)t * K + j) * N + (size_t)c8[q] * 8);
+        wt[q][j] = a.w[(size_t)t * K + j];
+      }
+      if constexpr (LOCAL) {
+#pragma unroll
+        for (int s = 0; s < kMaxRanks; ++s)
+          if (s < a.R && s != a.local) pv[q][s] = gload16(a.peers[s] + (size_t)t * N + (size_t)c8[q] * 8);
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < U; ++q) {
+      if (row[q] < 0) continue;
+      float acc[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] = wt[q][0] * bf16_to_f32((v[q][0][e >> 1] >> ((e & 1) * 16)) & 0xFFFFu);
+#pragma unroll
+      for (int j = 1; j < K; ++j) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          acc[e] = __builtin_fmaf(wt[q][j], bf16_to_f32((v[q][j][e >> 1] >> ((e & 1) * 16)) & 0xFFFFu), acc[e]);
+      }
+      const u32x4_t o = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]), pack_bf16x2(acc[4], acc[5]),
+                         pack_bf16x2(acc[6], acc[7])};
+      gstore16(a.partial + (size_t)row[q] * N + (size_t)c8[q] * 8, o);
+      if constexpr (LOCAL) {
+        // rank order; the local rank's term is `o` (selected per unrolled
+        // rank, so the register arrays are never indexed at run time)
+        float r[8];
+#pragma unroll
+        for (int s = 0; s < kMaxRanks; ++s)
+          if (s < a.R) {
+            const u32x4_t x = (s == a.local) ? o : pv[q][s];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const float f = bf16_to_f32((x[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu);
+              r[e] = (s == 0) ? f : r[e] + f;
+            }
+          }
+        const u32x4_t ro = {pack_bf16x2(r[0], r[1]), pack_bf16x2(r[2], r[3]), pack_bf16x2(r[4], r[5]),
+                            pack_bf16x2(r[6], r[7])};
+        gstore16(a.out + (size_t)(row[q] - base) * N + (size_t)c8[q] * 8, ro);
+      }
+    }
+  }
+}
+
 // ---------------------------------------------------------------- AG + grouped GEMM
+
+// consume_tile_wait of a TopK-Reduce task of the MoE layer chain (wave 0):
+// every grouped tile that wrote a slot row of the task's tokens (rotated
+// rows [r0, r1)) must have published. A dependency (token, slot j, column
+// block cb) resolves through the routing tables -- the slot's position in
+// the expert-sorted order, its expert's row tile, the lookup-table entry of
+// (expert, cb, row tile) -- the dynamic-dependency lookup the pages describe
+// for MoE. 64 dependencies per round, one lane each, polled in parallel,
+// then one acquire fence. Returns the number of dependencies.
+__device__ int wait_combine_deps(const MoeArgs& a, const Common& cm, int r0, int r1, uint32_t epoch,
+                                 uint32_t* seen_out) {
+  const int lane = threadIdx.x & 63;
+  const CombArgs& c = a.comb;
+  const int K = a.topk, base = c.local * c.m, T = c.T;
+  const int n = (r1 - r0) * K * a.n_cb;
+  const uint64_t t0 = now_ticks();
+  bool ok = true;
+  uint32_t v = epoch;
+  for (int b = 0; b < n; b += 64) {
+    const int it = b + lane;
+    if (it >= n) continue;
+    const int cb = it % a.n_cb, q = it / a.n_cb, j = q % K, rr = r0 + q / K;
+    const int t = rr + base < T ? rr + base : rr + base - T;
+    const int slot = t * K + j;
+    const int e = a.topk_ids[slot], pos = a.inv[slot];
+    const int off = a.offsets[e], nrt = cdiv(a.offsets[e + 1] - off, a.BM);
+    const int tile = min(a.lut_base[e] + cb * nrt + (pos - off) / a.BM, a.comb.max_tiles - 1);
+    const uint32_t* f = a.tflag + tile;
+    v = __hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    while (v != epoch && ok) {
+      if (now_ticks() - t0 > cm.timeout_ticks) {
+        ok = false;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+      v = __hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  if (__ballot(!ok)) {
+    if (lane == 0) __hip_atomic_fetch_or(&cm.hdr->error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  *seen_out = __shfl(v, 0);
+  return n;
+}
+
+template <int NT, int K>
+__device__ __forceinline__ void combine_task(const CombArgs& c, bool local, int r0, int r1) {
+  if (local)
+    combine_rows<true, kCombineChunksLocal, K, NT>(c, r0, r1);
+  else
+    combine_rows<false, kCombineChunks, K, NT>(c, r0, r1);
+}
 
 template <int BM, int BN>
 __global__ __launch_bounds__((Gemm<BM, BN>::NT), 1) void moe_gemm_kernel(MoeArgs args) {
@@ -585,91 +716,58 @@ __global__ __launch_bounds__((Gemm<BM, BN>::NT), 1) void moe_gemm_kernel(MoeArgs
     mainloop<BM, BN>(smem, t, acc);
     stage_c<BM, BN>(smem, acc);
     // local scatter: row rr of the tile is token-slot perm[r0 + rr]
-    for_each_c_chunk<BM, BN>(smem, [&](int rr, int col, u32x4_t val) {
-      if (rr < nrows && n0 + col < p.N) {
-        const int slot = args.perm[r0 + rr];
-        gstore16(args.out + (size_t)slot * p.N + n0 + col, val);
-      }
-    });
+    if (args.combine) {
+      // read by this launch's TopK-Reduce tasks: agent-coherent stores, then
+      // produce_tile_notify
+      const __amdgpu_buffer_rsrc_t ors = make_rsrc(args.out, (uint32_t)((size_t)args.comb.T * args.topk * p.N * 2));
+      for_each_c_chunk<BM, BN>(smem, [&](int rr, int col, u32x4_t val) {
+        if (rr < nrows && n0 + col < p.N) {
+          const int slot = args.perm[r0 + rr];
+          store16_agent(ors, (uint32_t)(((size_t)slot * p.N + n0 + col) * 2), val);
+        }
+      });
+      drain_stores();
+      __syncthreads();
+      if (threadIdx.x == 0) __hip_atomic_store(&args.tflag[v], epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+      for_each_c_chunk<BM, BN>(smem, [&](int rr, int col, u32x4_t val) {
+        if (rr < nrows && n0 + col < p.N) {
+          const int slot = args.perm[r0 + rr];
+          gstore16(args.out + (size_t)slot * p.N + n0 + col, val);
+        }
+      });
+    }
     trace_task(cm, (uint32_t)(p.n_copy + v), 4, e, r0, nrows, cb | ((uint32_t)nwait << 16), epoch, t0, t1, seen,
                ((uint32_t)q << 16) | qt);
   }
-  finish(cm.hdr, epoch);
-}
-
-// ---------------------------------------------------------------- TopK-Reduce + ReduceScatter
-
-// Rows [r0, r1) of the token order rotated to start at the local block
-// (row t = (r + local*m) mod T): each row's 16-byte column chunks summed over
-// its top-k slot rows in slot order, weight times value in fp32, rounded
-// once to bf16 and stored to the partial. LOCAL rows (r < m) also finish the
-// ReduceScatter on the spot: the R ranks' bf16 rows summed in ascending rank
-// order in fp32 (the local one as just rounded) and rounded once into out.
-// U chunks per thread in flight per round.
-template <bool LOCAL, int U, int K>
-__device__ void combine_rows(const CombArgs& a, int r0, int r1) {
-  const int T = a.T, N = a.N, n8 = N / 8, base = a.local * a.m;
-  const int n16 = (r1 - r0) * n8;
-  for (int b0 = threadIdx.x; b0 < n16; b0 += U * kThreads) {
-    u32x4_t v[U][K];
-    u32x4_t pv[U][LOCAL ? kMaxRanks : 1];
-    float wt[U][K];
-    int row[U], c8[U];
-#pragma unroll
-    for (int q = 0; q < U; ++q) {
-      const int i = b0 + q * kThreads;
-      row[q] = -1;
-      if (i >= n16) continue;
-      const int rr = r0 + i / n8;
-      const int t = rr + base < T ? rr + base : rr + base - T;
-      row[q] = t;
-      c8[q] = i - (i / n8) * n8;
-#pragma unroll
-      for (int j = 0; j < K; ++j) {
-        v[q][j] = gload16(a.y + ((size_t)t * K + j) * N + (size_t)c8[q] * 8);
-        wt[q][j] = a.w[(size_t)t * K + j];
+  // The layer chain's TopK-Reduce + ReduceScatter tasks, once every tile has
+  // been claimed: local block first; each waits on the tiles that wrote its
+  // tokens' slot rows (trace slot n_copy + #tiles + task).
+  if (args.combine) {
+    const CombArgs& c = args.comb;
+    for (;;) {
+      const uint32_t u = next_ticket(&cm.hdr->side_ticket, s_bcast);
+      if ((int)u >= c.n_comb) break;
+      const uint64_t t0 = now_ticks();
+      const bool local = (int)u < c.n_lt;
+      const int r0 = local ? (int)u * c.CRL : c.m + ((int)u - c.n_lt) * c.CR;
+      const int r1 = local ? min(r0 + c.CRL, c.m) : min(r0 + c.CR, c.T);
+      uint32_t seen = 0;
+      int nd = 0;
+      if (wave == 0) nd = wait_combine_deps(args, cm, r0, r1, epoch, &seen);
+      const uint64_t t1 = now_ticks();
+      __syncthreads();
+      switch (args.topk) {
+        case 1: combine_task<G::NT, 1>(c, local, r0, r1); break;
+        case 2: combine_task<G::NT, 2>(c, local, r0, r1); break;
+        case 3: combine_task<G::NT, 3>(c, local, r0, r1); break;
+        default: combine_task<G::NT, 4>(c, local, r0, r1); break;
       }
-      if constexpr (LOCAL) {
-#pragma unroll
-        for (int s = 0; s < kMaxRanks; ++s)
-          if (s < a.R && s != a.local) pv[q][s] = gload16(a.peers[s] + (size_t)t * N + (size_t)c8[q] * 8);
-      }
-    }
-#pragma unroll
-    for (int q = 0; q < U; ++q) {
-      if (row[q] < 0) continue;
-      float acc[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] = wt[q][0] * bf16_to_f32((v[q][0][e >> 1] >> ((e & 1) * 16)) & 0xFFFFu);
-#pragma unroll
-      for (int j = 1; j < K; ++j) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          acc[e] = __builtin_fmaf(wt[q][j], bf16_to_f32((v[q][j][e >> 1] >> ((e & 1) * 16)) & 0xFFFFu), acc[e]);
-      }
-      const u32x4_t o = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]), pack_bf16x2(acc[4], acc[5]),
-                         pack_bf16x2(acc[6], acc[7])};
-      gstore16(a.partial + (size_t)row[q] * N + (size_t)c8[q] * 8, o);
-      if constexpr (LOCAL) {
-        // rank order; the local rank's term is `o` (selected per unrolled
-        // rank, so the register arrays are never indexed at run time)
-        float r[8];
-#pragma unroll
-        for (int s = 0; s < kMaxRanks; ++s)
-          if (s < a.R) {
-            const u32x4_t x = (s == a.local) ? o : pv[q][s];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const float f = bf16_to_f32((x[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu);
-              r[e] = (s == 0) ? f : r[e] + f;
-            }
-          }
-        const u32x4_t ro = {pack_bf16x2(r[0], r[1]), pack_bf16x2(r[2], r[3]), pack_bf16x2(r[4], r[5]),
-                            pack_bf16x2(r[6], r[7])};
-        gstore16(a.out + (size_t)(row[q] - base) * N + (size_t)c8[q] * 8, ro);
-      }
+      trace_task(cm, (uint32_t)(p.n_copy + n_tiles) + u, 6, (uint32_t)r0, (uint32_t)r1,
+                 local ? (uint32_t)(r1 - r0) : 0u, (uint32_t)nd, epoch, t0, t1, seen, 0);
     }
   }
+  finish(cm.hdr, epoch);
 }
 
 // Tasks: first the local block's rows (rotated rows [0, m)) in tasks of CRL

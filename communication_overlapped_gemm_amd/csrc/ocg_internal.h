@@ -41,7 +41,7 @@ static_assert(sizeof(WsHeader) == 256, "header is 256 bytes");
 
 // Byte offsets of the workspace sections for one call shape.
 struct WsLayout {
-  size_t slab_cnt, slab_flag, rs_flag, moe_off, moe_lut, moe_perm, moe_bcnt, total;
+  size_t slab_cnt, slab_flag, rs_flag, moe_off, moe_lut, moe_perm, moe_bcnt, moe_inv, moe_lbase, moe_tflag, total;
   int max_slabs, max_rs_tiles, max_moe_tiles;
 };
 
@@ -104,6 +104,7 @@ struct CombArgs {
   uint16_t* out;                // [m][N]
   int topk, CR, CRL, n_lt, n_comb;   // rows per task (other / local rows), #local tasks, #tasks
   int R, local, m, T, N;
+  int max_tiles;                // MoE layer chain: entries of the grouped-tile flag array
   Common cm;
 };
 
@@ -119,6 +120,17 @@ struct MoeArgs {
   int topk, E;
   AgPlan plan;                  // copy plan (tiles come from the lookup table)
   Common cm;
+  // The MoE layer chain (combine = 1): after its tiles the kernel runs the
+  // TopK-Reduce + ReduceScatter tasks of `comb` on `out`, each waiting on the
+  // flags of the grouped tiles that wrote its tokens' slot rows.
+  int combine;
+  int BM, n_cb;
+  uint32_t* tflag;              // [tiles]: epoch once the grouped tile has stored its rows
+  const int32_t* inv;           // [slots]: position of each token-slot in the expert-sorted order
+  const int32_t* lut_base;      // [E]: first lookup-table entry of each expert
+  const int32_t* offsets;       // [E+1]: expert offsets in the sorted order
+  const int32_t* topk_ids;      // [T][topk]
+  CombArgs comb;
 };
 
 // AllGather-KV attention: copy tasks of both tensors, then attention tiles.
@@ -145,6 +157,8 @@ struct RouteArgs {
   int32_t* user_offsets;        // optional
   int32_t* lut;
   int32_t* blk_cnt;             // [blocks][E] slots per expert in each routing block
+  int32_t* inv;                 // [slots]: inverse of perm
+  int32_t* lut_base;            // [E]: first lookup-table entry of each expert
   WsHeader* hdr;
   int T, E, topk, BM, n_cb, max_tiles;
 };

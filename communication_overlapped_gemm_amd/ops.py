@@ -242,6 +242,54 @@ def ag_grouped_gemm(a_chunks: Sequence[torch.Tensor], logits: torch.Tensor, w: t
     return o
 
 
+def ag_moe_layer(a_chunks: Sequence[torch.Tensor], logits: torch.Tensor, w: torch.Tensor,
+                 peer_partials: Sequence[Optional[torch.Tensor]], topk: int = 2, local_rank: int = 0, *,
+                 workspace: Optional[Workspace] = None, config: Optional[Config] = None, stream=None,
+                 outputs: Optional[dict] = None) -> dict:
+    """The MoE layer chain in one call: AllGather + routing + grouped GEMM
+    (y, token-slot order) and TopK-Reduce + ReduceScatter of y (partial,
+    out). Returns a dict with out, partial, y, a_gathered, topk_ids, topk_w,
+    perm and expert_offsets."""
+    R = len(a_chunks)
+    m, K = a_chunks[0].shape
+    E, K2, N = w.shape
+    if K2 != K:
+        raise ValueError("w must be [E, K, N]")
+    for r, t in enumerate(a_chunks):
+        _check_bf16(t, f"a_chunks[{r}]", (m, K))
+    _check_bf16(w, "w")
+    if logits.dtype != torch.float32 or not logits.is_contiguous() or tuple(logits.shape) != (R * m, E):
+        raise ValueError("logits must be a contiguous float32 [R*m, E] CUDA tensor")
+    if len(peer_partials) != R:
+        raise ValueError("one peer partial entry per rank")
+    T = R * m
+    pp = (C.c_void_p * R)()
+    for s_, p_ in enumerate(peer_partials):
+        if s_ == local_rank:
+            continue
+        _check_bf16(p_, f"peer_partials[{s_}]", (T, N))
+        pp[s_] = p_.data_ptr()
+    dev = w.device
+    o = dict(outputs or {})
+    o.setdefault("a_gathered", torch.empty((T, K), dtype=torch.bfloat16, device=dev))
+    o.setdefault("topk_ids", torch.empty((T, topk), dtype=torch.int32, device=dev))
+    o.setdefault("topk_w", torch.empty((T, topk), dtype=torch.float32, device=dev))
+    o.setdefault("perm", torch.empty((T * topk,), dtype=torch.int32, device=dev))
+    o.setdefault("expert_offsets", torch.empty((E + 1,), dtype=torch.int32, device=dev))
+    o.setdefault("y", torch.empty((T * topk, N), dtype=torch.bfloat16, device=dev))
+    o.setdefault("partial", torch.empty((T, N), dtype=torch.bfloat16, device=dev))
+    o.setdefault("out", torch.empty((m, N), dtype=torch.bfloat16, device=dev))
+    ws = workspace or Workspace.cached(_lib.OP_AG_GROUPED_GEMM, R, m, K, N, E, topk, device=dev.index, stream=stream)
+    ptrs = (C.c_void_p * R)(*[t.data_ptr() for t in a_chunks])
+    cfg = _cfg(config)
+    check(lib.ocg_ag_moe_layer(handle(dev.index), ptrs, R, local_rank, m, K, logits.data_ptr(), E, topk,
+                               w.data_ptr(), N, pp, o["a_gathered"].data_ptr(), o["topk_ids"].data_ptr(),
+                               o["topk_w"].data_ptr(), o["perm"].data_ptr(), o["expert_offsets"].data_ptr(),
+                               o["y"].data_ptr(), o["partial"].data_ptr(), o["out"].data_ptr(), ws.ptr, ws.nbytes,
+                               C.byref(cfg), _stream_ptr(stream)), "ocg_ag_moe_layer")
+    return o
+
+
 def moe_combine_rs(y: torch.Tensor, topk_w: torch.Tensor, peer_partials: Sequence[Optional[torch.Tensor]],
                    local_rank: int = 0, *, partial: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
                    workspace: Optional[Workspace] = None, config: Optional[Config] = None,

@@ -292,6 +292,32 @@ int ocg_ag_grouped_gemm(ocg_handle h, const void* const* a_chunks, int R, int lo
                         float* topk_w, int32_t* perm, int32_t* expert_offsets, void* out,
                         void* workspace, size_t ws_bytes, const ocg_config* cfg, void* stream);
 
+/* The MoE layer chain in one call: ocg_ag_grouped_gemm (AllGather, routing,
+ * grouped GEMM, local scatter into y) followed by ocg_moe_combine_rs on its
+ * output (TopK-Reduce of y into `partial`, ReduceScatter of the ranks'
+ * partials into `out`), the operators "TileLink ..." (MLSys 2025 talk
+ * summary), "Experimental Setup & Results", overlaps in its MoE layer. The
+ * TopK-Reduce tasks run in the grouped GEMM's persistent kernel after its
+ * tiles: each grouped tile stores its rows and publishes a flag, and each
+ * task waits on the flags of exactly the tiles that wrote its tokens' slot
+ * rows -- found through the routing tables (the slot's position in the
+ * expert-sorted order, its expert's row tile, every column block), the
+ * dynamic dependencies resolved by lookup tables of "Technical Deep Dive" --
+ * so the tail of the grouped GEMM overlaps the first TopK-Reduce tasks.
+ * Arguments as ocg_ag_grouped_gemm (y = its `out`, bf16 [R*m*topk, N], here
+ * also an input of the combine) and ocg_moe_combine_rs (peer_partials,
+ * partial bf16 [R*m, N], out bf16 [m, N]; topk_w are the routing's gate
+ * weights). Results equal the two calls made in sequence. Requires the shapes
+ * of both calls and R*m*topk*N*2 < 2^31; workspace from
+ * ocg_workspace_bytes(h, OCG_OP_AG_GROUPED_GEMM, R, m, K, N, E, topk). Trace:
+ * copies and tiles as ocg_ag_grouped_gemm, then TopK-Reduce task u at slot
+ * n_copy + #tiles + u (kind 6; d = #dependencies waited on). */
+int ocg_ag_moe_layer(ocg_handle h, const void* const* a_chunks, int R, int local_rank,
+                     int64_t m, int64_t K, const float* logits, int E, int topk, const void* w,
+                     int64_t N, const void* const* peer_partials, void* a_gathered, int32_t* topk_ids,
+                     float* topk_w, int32_t* perm, int32_t* expert_offsets, void* y, void* partial,
+                     void* out, void* workspace, size_t ws_bytes, const ocg_config* cfg, void* stream);
+
 /* MoE TopK-Reduce + ReduceScatter, the tail of the MoE layer ("TileLink ...
  * (MLSys 2025 talk summary)", section "Experimental Setup & Results", lists
  * TopK-Reduce and ReduceScatter among the MoE operators it overlaps; the

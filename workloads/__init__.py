@@ -24,7 +24,7 @@ import numpy as np
 
 __all__ = [
     "f32_to_bf16_bits", "bf16_bits_to_f32", "AgGemmInputs", "GemmRsInputs",
-    "MoeInputs", "make_ag_gemm", "make_gemm_rs", "make_moe", "WORKLOADS",
+    "MoeInputs", "make_ag_gemm", "make_gemm_rs", "make_moe", "make_moe_peers", "WORKLOADS",
     "workload",
 ]
 
@@ -208,6 +208,14 @@ def make_attention_retrieval(R: int, m: int, Hq: int, Hkv: int, d: int, seed: in
     return x, targets
 
 
+def make_moe_peers(R: int, m: int, N: int, seed: int, local_rank: int = 0, scale: float = 0.02) -> Dict[int, np.ndarray]:
+    """The other ranks' combined partials of an MoE layer (stand-ins for
+    what the peers' TopK-Reduce would send): draw order P_s for s !=
+    local_rank ascending, N(0, scale) [R*m, N], from their own seed."""
+    rng = np.random.default_rng(seed)
+    return {s: _draw_bf16(rng, (R * m, N), "normal", scale) for s in range(R) if s != local_rank}
+
+
 @dataclass(frozen=True)
 class Workload:
     name: str
@@ -261,6 +269,11 @@ WORKLOADS = {
     # ReduceScatter of the combined token rows (row block 0 kept)
     "moe_combine_rs": Workload("moe_combine_rs", "moe_combine_rs",
                                dict(R=8, m=512, N=1792, topk=2, seed=5, local_rank=0)),
+    # the whole MoE layer chain: ag_moe's inputs (seed 4), then the grouped
+    # output's TopK-Reduce and the ReduceScatter against the peers' combined
+    # partials (seed 7)
+    "ag_moe_layer": Workload("ag_moe_layer", "ag_grouped_gemm",
+                             dict(R=8, m=512, K=4096, N=1792, E=32, topk=2, seed=4, peer_seed=7, local_rank=0)),
     # AllGather-KV attention: a 16384-token context over 8 ranks (2048 tokens
     # each), 32 query heads over 8 kv heads of 128 (an 8B-class GQA layer),
     # every query over the whole context
