@@ -5,14 +5,15 @@
 
 A step is one fused AG-GEMM call on the 70B-class TP=8 share: R = 8 ranks x
 [1024, 8192] bf16 shards gathered to [8192, 8192], times B [8192, 3584], bf16
-output. With the default transfer mode the call is two kernels running at
-once on every compute unit -- the GEMM's persistent kernel and the side
-producer that copies the peers' rows K-slab by K-slab and publishes the flags
-the tiles wait on. All inputs are seeded synthetic data (N(0, 0.02), seed 3)
-already resident in HBM when the timed region starts.
+output: one persistent kernel whose workgroups copy the peers' rows slab by
+slab and publish the flags the GEMM tiles then wait on (the default, inline
+transfer). The overlap legs also time the side transfer, in which a
+producer kernel on a second stream copies K-slab by K-slab beside the GEMM
+kernel. All inputs are seeded synthetic data (N(0, 0.02), seed 3) already
+resident in HBM when the timed region starts.
 
-Order of work: (1) the overlap legs -- fused (side producer), fused with the
-copies inline, GEMM tiles only, copies only (both forms) and copy-then-GEMM
+Order of work: (1) the overlap legs -- fused (inline copies), fused with the
+side producer, GEMM tiles only, copies only (both forms) and copy-then-GEMM
 on two streams -- timed in alternating rounds, so clock drift is shared by
 all legs; they also carry the chip through the power-management transient
 of its first ~35 ms under load (launches of a fresh process first run fast,
@@ -153,6 +154,15 @@ def gpu_temperature():
         return None
 
 
+def trace_dtype():
+    """One ocg_trace_rec (80 bytes) as a numpy record."""
+    import numpy as np
+    return np.dtype([("ticket", "<u4"), ("kind", "<u4"), ("a", "<u4"), ("b", "<u4"), ("c", "<u4"),
+                     ("d", "<u4"), ("hw", "<u4"), ("epoch", "<u4"), ("t_start", "<u8"), ("t_ready", "<u8"),
+                     ("t_end", "<u8"), ("flag_seen", "<u4"), ("queue", "<u4"), ("cycles", "<u8"),
+                     ("wait_ticks", "<u4"), ("pad", "<u4")])
+
+
 def traced_clock_ghz(torch, ocg, launch_cfg, n_rec, runs=5):
     """Compute-unit clock while the tiles run: per tile, shader-clock cycles
     (s_memtime) over its 100 MHz duration, median over the tiles of `runs`
@@ -166,16 +176,39 @@ def traced_clock_ghz(torch, ocg, launch_cfg, n_rec, runs=5):
     for _ in range(runs):
         launch_cfg[0](cfg)
         torch.cuda.synchronize()
-        rec = buf.cpu().numpy().view(np.dtype([("ticket", "<u4"), ("kind", "<u4"), ("a", "<u4"), ("b", "<u4"),
-                                               ("c", "<u4"), ("d", "<u4"), ("hw", "<u4"), ("epoch", "<u4"),
-                                               ("t_start", "<u8"), ("t_ready", "<u8"), ("t_end", "<u8"),
-                                               ("flag_seen", "<u4"), ("queue", "<u4"), ("cycles", "<u8"),
-                                               ("wait_ticks", "<u4"), ("pad", "<u4")]))
+        rec = buf.cpu().numpy().view(trace_dtype())
         t = rec[(rec["kind"] == 2) & (rec["t_end"] > rec["t_start"])]
         ghz += list(t["cycles"] / (t["t_end"] - t["t_start"]) * 0.1)   # 100 MHz ticks -> GHz
     cfg.trace = None
     cfg.trace_capacity = 0
     return float(np.median(ghz)) if ghz else None
+
+
+def side_trace_summary(torch, ocg, launch, n_rec):
+    """One traced fused call with the side transfer: when the producer's
+    copies ran, relative to the GEMM tiles (device clock, 100 MHz)."""
+    import numpy as np
+    buf = torch.zeros(n_rec * 80, dtype=torch.uint8, device="cuda")
+    cfg = ocg.default_config(transfer=ocg.TRANSFER_SIDE)
+    cfg.trace = buf.data_ptr()
+    cfg.trace_capacity = n_rec
+    launch(cfg)
+    torch.cuda.synchronize()
+    rec = buf.cpu().numpy().view(trace_dtype())
+    cp, tl = rec[rec["kind"] == 1], rec[rec["kind"] == 2]
+    if not len(cp) or not len(tl):
+        return None
+    t0 = int(min(cp["t_start"].min(), tl["t_start"].min()))
+    us = lambda v: round((float(v) - t0) / 100.0, 1)
+    prod = cp[(cp["d"] & 2) != 0]
+    last_copy = int(cp["t_end"].max())
+    return {"copies": int(len(cp)), "producer_copies": int(len(prod)),
+            "copies_us": [us(cp["t_start"].min()), us(last_copy)],
+            "tiles_started_us": [us(tl["t_start"].min()), us(tl["t_start"].max())],
+            "tiles_computing_while_copies_in_flight": int((tl["t_ready"] < last_copy).sum()),
+            "tile_start_wait_us_median": round(float(np.median(tl["t_ready"] - tl["t_start"])) / 100.0, 2),
+            "tile_kloop_wait_us_total": round(float(tl["wait_ticks"].sum()) / 100.0, 1),
+            "last_tile_end_us": us(tl["t_end"].max())}
 
 
 def main() -> int:
@@ -233,20 +266,20 @@ def main() -> int:
     if not args.skip_extras:
         gemm_only = ocg.default_config(mode=ocg.MODE_GEMM_ONLY)
         copy_only = ocg.default_config(mode=ocg.MODE_COPY_ONLY)
-        copy_inline = ocg.default_config(mode=ocg.MODE_COPY_ONLY, transfer=ocg.TRANSFER_INLINE)
-        fused_inline = ocg.default_config(transfer=ocg.TRANSFER_INLINE)
+        copy_side = ocg.default_config(mode=ocg.MODE_COPY_ONLY, transfer=ocg.TRANSFER_SIDE)
+        fused_side = ocg.default_config(transfer=ocg.TRANSFER_SIDE)
         s2 = torch.cuda.Stream()
         ev = torch.cuda.Event()
 
         def serial():
-            launch(copy_inline, stream)
+            launch(copy_only, stream)
             ev.record(stream)
             s2.wait_event(ev)
             launch(gemm_only, s2)
             stream.wait_stream(s2)
         full = torch.cat(chunks)
-        legs = {"fused": step, "fused_inline": lambda: launch(fused_inline), "gemm": lambda: launch(gemm_only),
-                "copy": lambda: launch(copy_only), "copy_inline": lambda: launch(copy_inline), "serial": serial,
+        legs = {"fused": step, "fused_side": lambda: launch(fused_side), "gemm": lambda: launch(gemm_only),
+                "copy": lambda: launch(copy_only), "copy_side": lambda: launch(copy_side), "serial": serial,
                 "d2d": lambda: ag.copy_(full), "matmul": lambda: torch.matmul(full, b)}
         samples = {k: [] for k in legs}
         for _ in range(6):
@@ -313,21 +346,26 @@ def main() -> int:
             rec["roofline"]["peak_at_clock"] = round(peak_clk, 1)
             rec["roofline"]["frac_at_clock"] = round(achieved / peak_clk, 4)
         rec["temperature"] = gpu_temperature()
+        side_plan = ocg.plan_info(ocg.OP_AG_GEMM, x.R, 0, x.m, x.K, x.N,
+                                  ocg.default_config(transfer=ocg.TRANSFER_SIDE), handle=h)
+        rec["side_trace"] = side_trace_summary(torch, ocg, lambda cfg: launch(cfg),
+                                               side_plan["n_copy_or_strips"] + side_plan["n_tiles"])
         t_f = med["fused"]
         copy_bytes = 2.0 * M * x.K * 2
         rec["overlap"] = {
             "timing": "medians of 6 alternating rounds x 8 launches per leg",
             "transfer": transfer,
-            "t_fused_us": round(t_f * 1e3, 2), "t_fused_inline_us": round(med["fused_inline"] * 1e3, 2),
+            "t_fused_us": round(t_f * 1e3, 2), "t_fused_side_us": round(med["fused_side"] * 1e3, 2),
             "t_gemm_us": round(med["gemm"] * 1e3, 2), "t_copy_us": round(med["copy"] * 1e3, 2),
-            "t_copy_inline_us": round(med["copy_inline"] * 1e3, 2), "t_serial_us": round(med["serial"] * 1e3, 2),
+            "t_copy_side_us": round(med["copy_side"] * 1e3, 2), "t_serial_us": round(med["serial"] * 1e3, 2),
             "e_max": round(max(med["copy"], med["gemm"]) / t_f, 4),
             "e_serial": round(med["serial"] / t_f, 4),
-            "hidden_copy_frac": round((med["gemm"] + med["copy_inline"] - t_f) / med["copy_inline"], 4),
+            "e_max_side": round(max(med["copy"], med["gemm"]) / med["fused_side"], 4),
+            "hidden_copy_frac": round((med["gemm"] + med["copy"] - t_f) / med["copy"], 4),
             "gemm_only_tflops": round(flops / (med["gemm"] * 1e-3) / 1e12, 2),
-            "fused_inline_tflops": round(flops / (med["fused_inline"] * 1e-3) / 1e12, 2),
+            "fused_side_tflops": round(flops / (med["fused_side"] * 1e-3) / 1e12, 2),
             "copy_only_gbs": round(copy_bytes / (med["copy"] * 1e-3) / 1e9, 1),
-            "copy_inline_gbs": round(copy_bytes / (med["copy_inline"] * 1e-3) / 1e9, 1),
+            "copy_side_gbs": round(copy_bytes / (med["copy_side"] * 1e-3) / 1e9, 1),
             "d2d_copy_gbs_yardstick": round(copy_bytes / (med["d2d"] * 1e-3) / 1e9, 1),
             "torch_matmul_tflops_yardstick": round(flops / (med["matmul"] * 1e-3) / 1e12, 2),
         }

@@ -73,8 +73,12 @@ extern "C" {
  *             proceed while the tiles compute. The caller's stream waits for
  *             the producer before the call's later work; the GEMM tiles wait
  *             on the per-(slab, K-slab) flags it publishes.
- *   AUTO   -- SIDE when the two kernels fit on a compute unit together,
- *             else INLINE.
+ *   AUTO   -- INLINE (the two measure the same per call on one MI355X:
+ *             the copies' energy counts against the chip's power limit
+ *             either way; one kernel stays safe under profilers that
+ *             serialise dispatches). SIDE is refused
+ *             (OCG_ERR_UNSUPPORTED_SHAPE) if the producer does not fit next
+ *             to the GEMM kernel's workgroup.
  * (Pull transfers with a "transfer complete" flag per slab: "TileLink ..."
  * (MLSys 2025 talk summary), "Technical Deep Dive".) */
 #define OCG_TRANSFER_AUTO (-1)

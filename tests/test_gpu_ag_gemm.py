@@ -256,8 +256,8 @@ def test_ag_gemm_70b_share(ocg, local):
     _full(ocg, "ag_gemm_70b", local=local)
 
 
-def test_ag_gemm_70b_share_inline(ocg):
-    _full(ocg, "ag_gemm_70b", local=3, cfg=ocg.default_config(transfer=INLINE))
+def test_ag_gemm_70b_share_side(ocg):
+    _full(ocg, "ag_gemm_70b", local=3, cfg=ocg.default_config(transfer=SIDE))
 
 
 def test_ag_plan_on_device_matches_host_plan(ocg):
