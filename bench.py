@@ -163,25 +163,29 @@ def trace_dtype():
                      ("wait_ticks", "<u4"), ("pad", "<u4")])
 
 
-def traced_clock_ghz(torch, ocg, launch_cfg, n_rec, runs=5):
+def traced_clock_ghz(torch, ocg, launch_cfg, n_rec, runs=5, with_cycles=False):
     """Compute-unit clock while the tiles run: per tile, shader-clock cycles
     (s_memtime) over its 100 MHz duration, median over the tiles of `runs`
-    traced launches."""
+    traced launches; with_cycles: also the median shader cycles per tile."""
     import numpy as np
     buf = torch.zeros(n_rec * 80, dtype=torch.uint8, device="cuda")
     cfg = launch_cfg[1]
     cfg.trace = buf.data_ptr()
     cfg.trace_capacity = n_rec
-    ghz = []
+    ghz, cyc = [], []
     for _ in range(runs):
         launch_cfg[0](cfg)
         torch.cuda.synchronize()
         rec = buf.cpu().numpy().view(trace_dtype())
         t = rec[(rec["kind"] == 2) & (rec["t_end"] > rec["t_start"])]
         ghz += list(t["cycles"] / (t["t_end"] - t["t_start"]) * 0.1)   # 100 MHz ticks -> GHz
+        cyc += list(t["cycles"])
     cfg.trace = None
     cfg.trace_capacity = 0
-    return float(np.median(ghz)) if ghz else None
+    clk = float(np.median(ghz)) if ghz else None
+    if with_cycles:
+        return clk, (int(np.median(cyc)) if cyc else None)
+    return clk
 
 
 def side_trace_summary(torch, ocg, launch, n_rec):
@@ -268,6 +272,8 @@ def main() -> int:
         copy_only = ocg.default_config(mode=ocg.MODE_COPY_ONLY)
         copy_side = ocg.default_config(mode=ocg.MODE_COPY_ONLY, transfer=ocg.TRANSFER_SIDE)
         fused_side = ocg.default_config(transfer=ocg.TRANSFER_SIDE)
+        fused_engine = ocg.default_config(transfer=ocg.TRANSFER_ENGINE)
+        copy_engine = ocg.default_config(mode=ocg.MODE_COPY_ONLY, transfer=ocg.TRANSFER_ENGINE)
         s2 = torch.cuda.Stream()
         ev = torch.cuda.Event()
 
@@ -280,6 +286,7 @@ def main() -> int:
         full = torch.cat(chunks)
         legs = {"fused": step, "fused_side": lambda: launch(fused_side), "gemm": lambda: launch(gemm_only),
                 "copy": lambda: launch(copy_only), "copy_side": lambda: launch(copy_side), "serial": serial,
+                "fused_engine": lambda: launch(fused_engine), "copy_engine": lambda: launch(copy_engine),
                 "d2d": lambda: ag.copy_(full), "matmul": lambda: torch.matmul(full, b)}
         samples = {k: [] for k in legs}
         for _ in range(6):
@@ -350,6 +357,13 @@ def main() -> int:
                                   ocg.default_config(transfer=ocg.TRANSFER_SIDE), handle=h)
         rec["side_trace"] = side_trace_summary(torch, ocg, lambda cfg: launch(cfg),
                                                side_plan["n_copy_or_strips"] + side_plan["n_tiles"])
+        legs_clock = {}
+        for name, lcfg in (("gemm", ocg.default_config(mode=ocg.MODE_GEMM_ONLY)), ("fused", ocg.default_config()),
+                           ("fused_side", ocg.default_config(transfer=ocg.TRANSFER_SIDE))):
+            clk_l, cyc_l = traced_clock_ghz(torch, ocg, (lambda cfg: launch(cfg), lcfg),
+                                            side_plan["n_copy_or_strips"] + side_plan["n_tiles"] + n_rec, runs=3,
+                                            with_cycles=True)
+            legs_clock[name] = {"clock_ghz": round(clk_l, 3) if clk_l else None, "tile_cycles_median": cyc_l}
         t_f = med["fused"]
         copy_bytes = 2.0 * M * x.K * 2
         rec["overlap"] = {
@@ -358,7 +372,10 @@ def main() -> int:
             "t_fused_us": round(t_f * 1e3, 2), "t_fused_side_us": round(med["fused_side"] * 1e3, 2),
             "t_gemm_us": round(med["gemm"] * 1e3, 2), "t_copy_us": round(med["copy"] * 1e3, 2),
             "t_copy_side_us": round(med["copy_side"] * 1e3, 2), "t_serial_us": round(med["serial"] * 1e3, 2),
+            "t_fused_engine_us": round(med["fused_engine"] * 1e3, 2),
+            "t_copy_engine_us": round(med["copy_engine"] * 1e3, 2),
             "e_max": round(max(med["copy"], med["gemm"]) / t_f, 4),
+            "legs_clock": legs_clock,
             "e_serial": round(med["serial"] / t_f, 4),
             "e_max_side": round(max(med["copy"], med["gemm"]) / med["fused_side"], 4),
             "hidden_copy_frac": round((med["gemm"] + med["copy"] - t_f) / med["copy"], 4),
@@ -366,6 +383,7 @@ def main() -> int:
             "fused_side_tflops": round(flops / (med["fused_side"] * 1e-3) / 1e12, 2),
             "copy_only_gbs": round(copy_bytes / (med["copy"] * 1e-3) / 1e9, 1),
             "copy_side_gbs": round(copy_bytes / (med["copy_side"] * 1e-3) / 1e9, 1),
+            "copy_engine_gbs": round(copy_bytes / (med["copy_engine"] * 1e-3) / 1e9, 1),
             "d2d_copy_gbs_yardstick": round(copy_bytes / (med["d2d"] * 1e-3) / 1e9, 1),
             "torch_matmul_tflops_yardstick": round(flops / (med["matmul"] * 1e-3) / 1e12, 2),
         }
