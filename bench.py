@@ -272,8 +272,6 @@ def main() -> int:
         copy_only = ocg.default_config(mode=ocg.MODE_COPY_ONLY)
         copy_side = ocg.default_config(mode=ocg.MODE_COPY_ONLY, transfer=ocg.TRANSFER_SIDE)
         fused_side = ocg.default_config(transfer=ocg.TRANSFER_SIDE)
-        fused_engine = ocg.default_config(transfer=ocg.TRANSFER_ENGINE)
-        copy_engine = ocg.default_config(mode=ocg.MODE_COPY_ONLY, transfer=ocg.TRANSFER_ENGINE)
         s2 = torch.cuda.Stream()
         ev = torch.cuda.Event()
 
@@ -286,7 +284,6 @@ def main() -> int:
         full = torch.cat(chunks)
         legs = {"fused": step, "fused_side": lambda: launch(fused_side), "gemm": lambda: launch(gemm_only),
                 "copy": lambda: launch(copy_only), "copy_side": lambda: launch(copy_side), "serial": serial,
-                "fused_engine": lambda: launch(fused_engine), "copy_engine": lambda: launch(copy_engine),
                 "d2d": lambda: ag.copy_(full), "matmul": lambda: torch.matmul(full, b)}
         samples = {k: [] for k in legs}
         for _ in range(6):
@@ -372,8 +369,6 @@ def main() -> int:
             "t_fused_us": round(t_f * 1e3, 2), "t_fused_side_us": round(med["fused_side"] * 1e3, 2),
             "t_gemm_us": round(med["gemm"] * 1e3, 2), "t_copy_us": round(med["copy"] * 1e3, 2),
             "t_copy_side_us": round(med["copy_side"] * 1e3, 2), "t_serial_us": round(med["serial"] * 1e3, 2),
-            "t_fused_engine_us": round(med["fused_engine"] * 1e3, 2),
-            "t_copy_engine_us": round(med["copy_engine"] * 1e3, 2),
             "e_max": round(max(med["copy"], med["gemm"]) / t_f, 4),
             "legs_clock": legs_clock,
             "e_serial": round(med["serial"] / t_f, 4),
@@ -383,7 +378,6 @@ def main() -> int:
             "fused_side_tflops": round(flops / (med["fused_side"] * 1e-3) / 1e12, 2),
             "copy_only_gbs": round(copy_bytes / (med["copy"] * 1e-3) / 1e9, 1),
             "copy_side_gbs": round(copy_bytes / (med["copy_side"] * 1e-3) / 1e9, 1),
-            "copy_engine_gbs": round(copy_bytes / (med["copy_engine"] * 1e-3) / 1e9, 1),
             "d2d_copy_gbs_yardstick": round(copy_bytes / (med["d2d"] * 1e-3) / 1e9, 1),
             "torch_matmul_tflops_yardstick": round(flops / (med["matmul"] * 1e-3) / 1e12, 2),
         }

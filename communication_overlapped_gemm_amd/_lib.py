@@ -24,7 +24,7 @@ ERR_NO_DEVICE = -6
 
 OP_AG_GEMM, OP_GEMM_RS, OP_AG_GROUPED_GEMM, OP_MOE_COMBINE_RS, OP_AG_ATTENTION = 0, 1, 2, 3, 4
 MODE_FUSED, MODE_GEMM_ONLY, MODE_COPY_ONLY = 0, 1, 2
-TRANSFER_AUTO, TRANSFER_INLINE, TRANSFER_SIDE, TRANSFER_ENGINE = -1, 0, 1, 2
+TRANSFER_AUTO, TRANSFER_INLINE, TRANSFER_SIDE = -1, 0, 1
 TILE_AUTO, TILE_256x224, TILE_128x224, TILE_128x256, TILE_128x128, TILE_256x256, TILE_320x224, TILE_288x224 = (
     -1, 0, 1, 2, 3, 4, 5, 6)
 

@@ -21,11 +21,6 @@ struct ocg_handle_s {
   hipStream_t side;                 // side stream of the SIDE transfer mode (default priority)
   hipEvent_t fork, join;            // caller stream -> side stream -> caller stream
   void* scratch;                    // device address of the no-allocation scratch on `device`
-  // ENGINE transfer: copy-engine streams and their join events, created on
-  // first use (n_engine of them)
-  int n_engine;
-  hipStream_t engine[kEngineStreams];
-  hipEvent_t engine_join[kEngineStreams];
 };
 
 namespace {
@@ -155,7 +150,7 @@ int resolve(int op, int R, int64_t m, int64_t K, int64_t N, int E, int topk, con
   r->transfer = OCG_TRANSFER_INLINE;
   r->KS = (int)K;
   if (op == OCG_OP_AG_GEMM) {
-    if (c.transfer < OCG_TRANSFER_AUTO || c.transfer > OCG_TRANSFER_ENGINE) return OCG_ERR_INVALID_ARG;
+    if (c.transfer < OCG_TRANSFER_AUTO || c.transfer > OCG_TRANSFER_SIDE) return OCG_ERR_INVALID_ARG;
     // AUTO: INLINE. Measured in one process, alternating, at the 70B share:
     // 412 us INLINE against 413 us SIDE per fused call -- under the chip's
     // power limit the copies cost the same energy wherever they run -- and
@@ -166,11 +161,7 @@ int resolve(int op, int R, int64_t m, int64_t K, int64_t N, int E, int topk, con
     r->transfer = c.transfer == OCG_TRANSFER_AUTO ? OCG_TRANSFER_INLINE : c.transfer;
     if (c.mode == OCG_MODE_GEMM_ONLY) r->transfer = OCG_TRANSFER_INLINE;   // no copies to place
     if (c.kslab_cols < 0 || c.kslab_cols % kMinKslabCols) return OCG_ERR_INVALID_ARG;
-    if (r->transfer == OCG_TRANSFER_ENGINE && c.kslab_cols > 0 && c.kslab_cols < K)
-      return OCG_ERR_INVALID_ARG;   // the copy engines move whole rows
-    if (r->transfer == OCG_TRANSFER_ENGINE)
-      r->KS = (int)K;
-    else if (c.kslab_cols > 0)
+    if (c.kslab_cols > 0)
       r->KS = c.kslab_cols;
     else if (r->transfer == OCG_TRANSFER_SIDE)
       r->KS = kSideKslabCols;
@@ -360,10 +351,6 @@ int ocg_create(int device, ocg_handle* out) {
 
 void ocg_destroy(ocg_handle h) {
   if (!h) return;
-  for (int i = 0; i < h->n_engine; ++i) {
-    if (h->engine_join[i]) (void)hipEventDestroy(h->engine_join[i]);
-    if (h->engine[i]) (void)hipStreamDestroy(h->engine[i]);
-  }
   if (h->join) (void)hipEventDestroy(h->join);
   if (h->fork) (void)hipEventDestroy(h->fork);
   if (h->side) (void)hipStreamDestroy(h->side);
@@ -390,18 +377,13 @@ size_t ocg_workspace_bytes(ocg_handle h, int op, int R, int64_t m, int64_t K, in
 int ocg_workspace_init(ocg_handle h, void* ws, size_t bytes, void* stream) {
   if (!h || !ws || bytes < sizeof(WsHeader) || (bytes & 3) || !aligned16(ws)) return OCG_ERR_INVALID_ARG;
   if (!device_matches(h)) return OCG_ERR_INVALID_ARG;
-  hipError_t e = launch_ws_init((uint32_t*)ws, bytes / 4, (hipStream_t)stream);
+  hipError_t e = launch_fill_u32((uint32_t*)ws, bytes / 4, 0u, 0, (hipStream_t)stream);
   return e == hipSuccess ? OCG_OK : OCG_ERR_HIP;
 }
 
-}  // extern "C"
-
-namespace {
-
 // The AG-GEMM plan of a call: tile, slabs, K-slabs and transfer (resolve),
 // the rounds of tiles of the persistent grid (copy phases), the copy tickets
-// the GEMM kernel runs itself (none under ENGINE), and the two grids
-// (producer 0 unless SIDE).
+// the GEMM kernel runs itself, and the two grids (producer 0 unless SIDE).
 // h = NULL plans for a 256-CU MI355X on which the producer fits.
 struct AgSetup {
   Resolved rv;
@@ -433,84 +415,15 @@ int ag_setup(ocg_handle h, int R, int local_rank, int64_t m, int64_t K, int64_t 
     const int first = first_kslab_tickets(p);
     p.n_inline = first < p.n_copy ? first : p.n_copy;
   }
-  if (o->rv.transfer == OCG_TRANSFER_ENGINE) p.n_inline = 0;   // the copy engines move every row
   const int gtasks = p.n_inline + p.n_tiles;
   o->ggrid = gtasks < tpr ? gtasks : tpr;
   o->pgrid = 0;
-  if (side && p.n_copy > p.n_inline) {
+  if (p.n_copy > p.n_inline) {
     const int pg = cfg.side_grid > 0 ? cfg.side_grid : cus;
     o->pgrid = pg < p.n_copy - p.n_inline ? pg : p.n_copy - p.n_inline;
   }
   return OCG_OK;
 }
-
-// The handle's copy-engine streams (default priority, non-blocking) and
-// their join events, created on first use.
-bool ensure_engine_streams(ocg_handle h, int n) {
-  if (n > kEngineStreams) n = kEngineStreams;
-  while (h->n_engine < n) {
-    const int i = h->n_engine;
-    if (hipStreamCreateWithFlags(&h->engine[i], hipStreamNonBlocking) != hipSuccess) return false;
-    if (hipEventCreateWithFlags(&h->engine_join[i], hipEventDisableTiming) != hipSuccess) {
-      (void)hipStreamDestroy(h->engine[i]);
-      h->engine[i] = nullptr;
-      return false;
-    }
-    ++h->n_engine;
-  }
-  return true;
-}
-
-// ENGINE transfer. Peer chunk q of the swizzled order (ℓ+1, ℓ+2, ...) goes
-// to engine stream q mod n: slab by slab, a no-compute-unit copy of the
-// slab's rows into the gathered buffer, then a 4-byte no-compute-unit copy
-// of the header's next-epoch word (this call's epoch) into the slab's flag;
-// the local chunk's rows go last, with no flag (the tiles read them from
-// the shard). Fused mode then launches the GEMM kernel, whose tiles wait on
-// those flags; copy-only mode launches nothing else. The caller's stream
-// waits for every engine stream before its later work.
-int ag_engine_call(ocg_handle h, const AgArgs& a, const AgSetup& su, const WsHeader* hdr, hipStream_t s) {
-  const AgPlan& p = a.plan;
-  const int n_peers = p.R - 1;
-  const int n = n_peers < 1 ? 1 : (n_peers < kEngineStreams ? n_peers : kEngineStreams);
-  if (!ensure_engine_streams(h, n)) return OCG_ERR_HIP;
-  if (hipEventRecord(h->fork, s) != hipSuccess) return OCG_ERR_HIP;
-  for (int i = 0; i < n; ++i)
-    if (hipStreamWaitEvent(h->engine[i], h->fork, 0) != hipSuccess) return OCG_ERR_HIP;
-  const size_t row_bytes = (size_t)p.K * 2;
-  const void* epoch_word = &hdr->next_epoch;
-  int peer = 0;
-  for (int q = 0; q < p.R; ++q) {
-    const int c = p.swizzle ? (p.local + 1 + q) % p.R : q;
-    if (c == p.local) continue;
-    hipStream_t es = h->engine[peer++ % n];
-    for (int j = 0; j < p.bpr; ++j) {
-      const int r0 = j * p.S, r1 = (r0 + p.S < p.m) ? r0 + p.S : p.m;
-      const size_t off = (size_t)r0 * p.K;
-      if (hipMemcpyAsync(a.a_gathered + (size_t)c * p.m * p.K + off, a.chunks[c] + off, (size_t)(r1 - r0) * row_bytes,
-                         hipMemcpyDeviceToDeviceNoCU, es) != hipSuccess)
-        return OCG_ERR_HIP;
-      const int flag = (c * p.bpr + j) * p.nks;
-      if (p.mode == OCG_MODE_FUSED && flag != a.cm.fault_skip_slab &&
-          hipMemcpyAsync(a.slab_flag + flag, epoch_word, 4, hipMemcpyDeviceToDeviceNoCU, es) != hipSuccess)
-        return OCG_ERR_HIP;
-    }
-  }
-  if (hipMemcpyAsync(a.a_gathered + (size_t)p.local * p.m * p.K, a.chunks[p.local], (size_t)p.m * row_bytes,
-                     hipMemcpyDeviceToDeviceNoCU, h->engine[(p.R - 1) % n]) != hipSuccess)
-    return OCG_ERR_HIP;
-  if (p.mode == OCG_MODE_FUSED && launch_ag_gemm(a, su.rv.tile, su.ggrid < 1 ? 1 : su.ggrid, s) != hipSuccess)
-    return OCG_ERR_HIP;
-  for (int i = 0; i < n; ++i)
-    if (hipEventRecord(h->engine_join[i], h->engine[i]) != hipSuccess ||
-        hipStreamWaitEvent(s, h->engine_join[i], 0) != hipSuccess)
-      return OCG_ERR_HIP;
-  return OCG_OK;
-}
-
-}  // namespace
-
-extern "C" {
 
 int ocg_ag_gemm(ocg_handle h, const void* const* a_chunks, int R, int local_rank, int64_t m, int64_t K,
                 const void* b, int64_t N, void* a_gathered, void* c, void* ws, size_t ws_bytes,
@@ -540,8 +453,6 @@ int ocg_ag_gemm(ocg_handle h, const void* const* a_chunks, int R, int local_rank
   if (a.plan.R * a.plan.bpr * a.plan.nks > L.max_slabs) return OCG_ERR_INVALID_ARG;
   a.cm = make_common(ws, cfg);
   hipStream_t s = (hipStream_t)stream;
-  if (su.rv.transfer == OCG_TRANSFER_ENGINE && cfg.mode != OCG_MODE_GEMM_ONLY)
-    return ag_engine_call(h, a, su, (const WsHeader*)ws, s);
   if (su.pgrid == 0)
     return launch_ag_gemm(a, su.rv.tile, su.ggrid < 1 ? 1 : su.ggrid, s) == hipSuccess ? OCG_OK : OCG_ERR_HIP;
   // SIDE: the GEMM kernel on the caller's stream, the producer on the side

@@ -15,7 +15,6 @@
 //
 // The memory-model contract of the flags and copies is stated in sync.h.
 #include <hip/hip_runtime.h>
-#include <stddef.h>
 #include <stdint.h>
 
 #include <mutex>
@@ -826,13 +825,6 @@ void* g_scratch_ptr[kMaxDevices];   // device address of `scratch` per device, n
 // Set-up, from ocg_create with `device` current: look up the array's device
 // address (in host code its name is only a host-side stand-in) and clear the
 // array, once per device.
-hipError_t launch_ws_init(uint32_t* ws, size_t words, hipStream_t s) {
-  hipError_t e = launch_fill_u32(ws, words, 0u, 0, s);
-  if (e != hipSuccess) return e;
-  // the first call runs with epoch 1
-  return launch_fill_u32(ws + offsetof(WsHeader, next_epoch) / 4, 1, 1u, 0, s);
-}
-
 hipError_t noalloc_scratch_setup(int device, void** out) {
   if (device < 0 || device >= kMaxDevices) return hipErrorInvalidDevice;
   std::lock_guard<std::mutex> lock(g_scratch_mu);
@@ -841,7 +833,7 @@ hipError_t noalloc_scratch_setup(int device, void** out) {
     hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
     if (e != hipSuccess) return e;
     if (!ptr) return hipErrorInvalidSymbol;
-    e = launch_ws_init((uint32_t*)ptr, kNoAllocScratchBytes / 4, nullptr);
+    e = launch_fill_u32((uint32_t*)ptr, kNoAllocScratchBytes / 4, 0u, 0, nullptr);
     if (e == hipSuccess) e = hipStreamSynchronize(nullptr);
     if (e != hipSuccess) return e;
     g_scratch_ptr[device] = ptr;

@@ -35,8 +35,7 @@ struct WsHeader {
   uint32_t n_tiles;    // MoE: grouped tiles of the current routing
   uint32_t xtick[8];   // next ticket of each XCD's tile queue
   uint32_t side_ticket;  // next copy ticket of the side producer kernel
-  uint32_t next_epoch;   // epoch of the next call (the value the copy engines write as a flag)
-  uint32_t pad[49];
+  uint32_t pad[50];
 };
 static_assert(sizeof(WsHeader) == 256, "header is 256 bytes");
 
@@ -169,7 +168,6 @@ hipError_t launch_ag_gemm(const AgArgs& a, int tile, int grid, hipStream_t s);
 // Side producer of ocg_ag_gemm's copy tasks (co-resident with the GEMM kernel).
 hipError_t launch_ag_side_copy(const AgArgs& a, int grid, hipStream_t s);
 constexpr int kSideThreads = 256;     // 4 waves: one per SIMD of a compute unit
-constexpr int kEngineStreams = 8;     // copy-engine streams of the ENGINE transfer (per handle)
 // Registers (VGPRs incl. accumulation registers) and LDS bytes of a kernel
 // per workgroup; false if the query fails.
 bool kernel_resources(int op, int tile, int* vgprs, int* lds_bytes);
@@ -179,9 +177,6 @@ hipError_t launch_moe_combine_rs(const CombArgs& a, int grid, hipStream_t s);
 hipError_t launch_ag_attention(const AttnArgs& a, int grid, hipStream_t s);
 int resident_attention();
 hipError_t launch_fill_u32(uint32_t* p, size_t n, uint32_t v, int release, hipStream_t s);
-// Clear a workspace of `words` 32-bit words: zeros, and the header's
-// next-epoch word 1 (the epoch of the first call).
-hipError_t launch_ws_init(uint32_t* ws, size_t words, hipStream_t s);
 // No-allocation entry point: the device address of the file-scope scratch
 // array on `device` (which must be current), cleared on first use.
 constexpr size_t kNoAllocScratchBytes = (size_t)1 << 20;

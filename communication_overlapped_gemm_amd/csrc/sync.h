@@ -306,8 +306,6 @@ __device__ __forceinline__ void finish(WsHeader* hdr, uint32_t epoch, int total 
       for (int q = 0; q < kXcds; ++q)
         __hip_atomic_store(&hdr->xtick[q], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_store(&hdr->done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(&hdr->next_epoch, epoch + 1u ? epoch + 1u : 1u, __ATOMIC_RELAXED,
-                         __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_store(&hdr->epoch, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }

@@ -73,34 +73,17 @@ extern "C" {
  *             proceed while the tiles compute. The caller's stream waits for
  *             the producer before the call's later work; the GEMM tiles wait
  *             on the per-(slab, K-slab) flags it publishes.
- *   ENGINE -- the copy engines (SDMA) move each peer slab, whole rows,
- *             with device-to-device copies that use no compute unit, on
- *             up to 8 streams owned by the handle (one per peer chunk, in
- *             the swizzled chunk order); after each slab the same engine
- *             writes its flag (a 4-byte copy of the workspace's next-epoch
- *             word), so the GEMM kernel, which holds every compute unit,
- *             sees the flag without any compute unit running a copy. One
- *             K-slab (kslab_cols must be 0 or >= K). The caller's stream
- *             waits for every engine stream before the call's later work.
- *             A copy engine moves about 60 GB/s, the rate of one
- *             inter-GPU link: on one GPU the call is bound by the engines,
- *             across GPUs it takes the transfers off the compute units.
- *             After a call that reported OCG_ERR_TIMEOUT, re-initialise the
- *             workspace before reusing it (an engine flag write may still
- *             have been in flight when the kernel gave up).
  *   AUTO   -- INLINE (the two measure the same per call on one MI355X:
  *             the copies' energy counts against the chip's power limit
  *             either way; one kernel stays safe under profilers that
  *             serialise dispatches). SIDE is refused
  *             (OCG_ERR_UNSUPPORTED_SHAPE) if the producer does not fit next
  *             to the GEMM kernel's workgroup.
- * (Pull transfers with a "transfer complete" flag per slab, and transfers
- * issued by copy engines rather than compute blocks: "TileLink ..." (MLSys
- * 2025 talk summary), "Technical Deep Dive".) */
+ * (Pull transfers with a "transfer complete" flag per slab: "TileLink ..."
+ * (MLSys 2025 talk summary), "Technical Deep Dive".) */
 #define OCG_TRANSFER_AUTO (-1)
 #define OCG_TRANSFER_INLINE 0
 #define OCG_TRANSFER_SIDE 1
-#define OCG_TRANSFER_ENGINE 2
 
 /* Tile presets (rows x columns of C per workgroup tile, K step 64);
  * OCG_TILE_288x224 and OCG_TILE_320x224 are for the grouped GEMM only. */
@@ -433,11 +416,10 @@ int ocg_plan_info(ocg_handle h, int op, int R, int local_rank, int64_t m, int64_
                   int topk, const ocg_config* cfg, int64_t out[8]);
 
 /* AG-GEMM plan details: out[0] = K-slab columns, out[1] = #K-slabs,
- * out[2] = transfer mode the call would use (OCG_TRANSFER_INLINE, _SIDE or
- * _ENGINE), out[3] = persistent GEMM workgroups, out[4] = producer
- * workgroups (SIDE) or 0, out[5] = copy tickets the GEMM kernel runs itself
- * (the first K-slab of the first copy phase under SIDE, none under ENGINE,
- * all of them otherwise), out[6] =
+ * out[2] = transfer mode the call would use (OCG_TRANSFER_INLINE or _SIDE),
+ * out[3] = persistent GEMM workgroups, out[4] = producer workgroups (SIDE)
+ * or 0, out[5] = copy tickets the GEMM kernel runs itself (the first K-slab
+ * of the first copy phase under SIDE, all of them otherwise), out[6] =
  * gathered rows per round of tiles (copy phases), out[7] = 0. `h` as for
  * ocg_plan_info. */
 int ocg_plan_ag(ocg_handle h, int R, int local_rank, int64_t m, int64_t K, int64_t N, const ocg_config* cfg,

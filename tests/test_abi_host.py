@@ -145,7 +145,7 @@ def ag_grid_tiles(info, R, m, N):
 @pytest.mark.parametrize("swizzle", [1, 0])
 @pytest.mark.parametrize("mode", ["fused", "gemm_only", "copy_only"])
 @pytest.mark.parametrize("transfer,kslab", [(ocg.TRANSFER_INLINE, 0), (ocg.TRANSFER_SIDE, 0),
-                                            (ocg.TRANSFER_INLINE, 256), (ocg.TRANSFER_ENGINE, 0)])
+                                            (ocg.TRANSFER_INLINE, 256)])
 def test_ag_plan_matches_oracle_schedule(case, swizzle, mode, transfer, kslab):
     R, m, K, N, local, tile = case
     modes = {"fused": 0, "gemm_only": 1, "copy_only": 2}
@@ -161,11 +161,6 @@ def test_ag_plan_matches_oracle_schedule(case, swizzle, mode, transfer, kslab):
     assert ag["rows_per_round"] == max(1, ag_grid_tiles(info, R, m, N) // n_cb) * info["BM"]
     want = sch.ag_gemm_plan(R, m, K, N, local, info["BM"], info["BN"], info["slab_rows"], info["copy_rows"],
                             bool(swizzle), mode, KS=ag["kslab_cols"], rpr=ag["rows_per_round"])
-    engine = transfer == ocg.TRANSFER_ENGINE and mode != "gemm_only"
-    assert ag["transfer"] == (transfer if mode != "gemm_only" else ocg.TRANSFER_INLINE)
-    if engine:
-        # the copy engines move every row: no copy ticket in the kernel, no producer
-        assert ag["n_inline"] == 0 and ag["side_grid"] == 0 and ag["nks"] == 1
     if side and mode != "gemm_only":
         # the GEMM kernel copies the first K-slab of the first phase itself
         first = sch.copy_phases(R, m, local, bool(swizzle), ag["rows_per_round"])[0]
@@ -186,17 +181,6 @@ def test_ag_plan_matches_oracle_schedule(case, swizzle, mode, transfer, kslab):
             deps = list(t.deps)
             assert d[:4] == [2, t.rb, t.cb, len(deps)]
             assert d[4:4 + min(4, len(deps))] == deps[:4]
-
-
-def test_engine_transfer_rejects_kslabs():
-    # the copy engines move whole rows: a K-slab narrower than K is refused
-    cfg = ocg.default_config(transfer=ocg.TRANSFER_ENGINE, kslab_cols=256)
-    with pytest.raises(ocg.OcgError):
-        ocg.plan_ag(4, 0, 256, 1024, 256, cfg)
-    cfg = ocg.default_config(transfer=ocg.TRANSFER_ENGINE, kslab_cols=1024)
-    assert ocg.plan_ag(4, 0, 256, 1024, 256, cfg)["nks"] == 1
-    with pytest.raises(ocg.OcgError):
-        ocg.plan_ag(4, 0, 256, 1024, 256, ocg.default_config(transfer=3))
 
 
 @pytest.mark.parametrize("R,M,K,N,local,tile", [(8, 4096, 1792, 4096, 0, -1), (8, 4096, 1792, 4096, 5, -1),

@@ -1,8 +1,7 @@
 """GPU parity of the fused AllGather-GEMM against the float64 oracle, through
-the C ABI: small and ragged shapes in full for the three transfer modes
-(copy tasks inline in the GEMM kernel, a side producer kernel co-resident
-with it, or the copy engines writing the slab flags themselves) and several
-K-slab widths, the 8B- and 70B-class shares on every output
+the C ABI: small and ragged shapes in full for both transfer modes (copy
+tasks inline in the GEMM kernel, or a side producer kernel co-resident with
+it) and several K-slab widths, the 8B- and 70B-class shares on every output
 element, the gathered buffer bit for bit, the schedule trace against the
 oracle's re-derivation, forced late publishes (tiles that really wait, also
 inside their K loop), the measurement modes, and the timeout path."""
@@ -17,7 +16,7 @@ from gpu_util import Trace, assert_gate, poison, say, to_bits, to_dev
 
 pytestmark = pytest.mark.gpu
 
-INLINE, SIDE, ENGINE = 0, 1, 2
+INLINE, SIDE = 0, 1
 
 
 def run(ocg, x, local=0, cfg=None):
@@ -48,12 +47,10 @@ SMALL = [
 ]
 
 
-@pytest.mark.parametrize("transfer", [INLINE, SIDE, ENGINE], ids=["inline", "side", "engine"])
+@pytest.mark.parametrize("transfer", [INLINE, SIDE], ids=["inline", "side"])
 @pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
 def test_ag_gemm_small_full(ocg, case, transfer):
     name, R, m, K, N, local, tile, dist, kslab = case
-    if transfer == ENGINE:
-        kslab = 0          # the copy engines move whole rows
     x = workloads.make_ag_gemm(R, m, K, N, seed=100 + R * 7 + local, dist=dist,
                                scale=1.0 if dist == "uniform" else 0.02)
     say("ag_gemm", name, R, m, K, N, local, tile, "transfer", transfer, "kslab", kslab)
@@ -158,44 +155,11 @@ def test_ag_gemm_late_publishes_make_tiles_wait(ocg, transfer):
         assert (dep["wait_ticks"] > 0).any(), "some tile waited inside its K loop"
 
 
-@pytest.mark.parametrize("local,swizzle", [(0, 1), (3, 1), (2, 0)])
-def test_ag_gemm_engine_trace(ocg, local, swizzle):
-    """ENGINE transfer: the kernel runs no copy task; every tile that reads
-    peer rows saw its slabs' flags at this call's epoch, written by the copy
-    engines, and the tiles are those of the oracle's plan."""
-    x = workloads.make_ag_gemm(4, 200, 1024, 456, seed=78, dist="uniform", scale=1.0)
-    cfg = ocg.default_config(tile=ocg.TILE_128x224, swizzle=swizzle, transfer=ENGINE)
-    info = ocg.plan_info(ocg.OP_AG_GEMM, x.R, local, x.m, x.K, x.N, cfg)
-    ag = ocg.plan_ag(x.R, local, x.m, x.K, x.N, cfg)
-    assert ag["transfer"] == ENGINE and ag["n_inline"] == 0 and ag["nks"] == 1
-    n = info["n_copy_or_strips"] + info["n_tiles"]
-    tr = Trace(n + 8)
-    tr.attach(cfg)
-    say("ag_gemm engine trace", local, swizzle)
-    c, g = run(ocg, x, local, cfg)
-    recs = tr.read(n)
-    ws = ocg.Workspace.cached(ocg.OP_AG_GEMM, x.R, x.m, x.K, x.N)
-    ws.check()
-    plan = sch.ag_gemm_plan(x.R, x.m, x.K, x.N, local, info["BM"], info["BN"], info["slab_rows"],
-                            info["copy_rows"], bool(swizzle), "fused", KS=x.K, rpr=ag["rows_per_round"])
-    n_copy = info["n_copy_or_strips"]
-    assert (recs[:n_copy]["kind"] == 0).all(), "no copy task ran on a compute unit"
-    tiles = recs[n_copy:]
-    epoch = int(tiles["epoch"][0])
-    assert (tiles["epoch"] == epoch).all()
-    for t, r in zip([t for t in plan if isinstance(t, sch.Tile)], tiles):
-        assert (r["kind"], r["a"], r["b"], r["c"]) == (2, t.rb, t.cb, len(t.deps))
-        if t.deps:
-            assert r["flag_seen"] == epoch, "the engines wrote this call's epoch"
-    assert np.array_equal(to_bits(g), np.concatenate(x.a_chunks))
-    assert_gate(to_bits(c), oracle.ag_gemm(x.a_chunks, x.b)[1], "engine trace case")
-
-
 def test_ag_gemm_modes_and_repeated_epochs(ocg):
     x = workloads.make_ag_gemm(4, 256, 256, 448, seed=5, dist="uniform", scale=1.0)
     chunks = [to_dev(c) for c in x.a_chunks]
     a_full, want = oracle.ag_gemm(x.a_chunks, x.b)
-    for transfer in (INLINE, SIDE, ENGINE):
+    for transfer in (INLINE, SIDE):
         ag = poison((x.R * x.m, x.K))
         say("ag_gemm copy_only", transfer)
         ocg.ag_gemm(chunks, to_dev(x.b), 1, a_gathered=ag,
@@ -210,32 +174,30 @@ def test_ag_gemm_modes_and_repeated_epochs(ocg):
     assert np.array_equal(to_bits(c_g), to_bits(c_f)), "same tiles, same arithmetic"
     assert_gate(to_bits(c_f), want, "fused")
     # several calls in a row on one workspace (epoch-tagged flags, no reset),
-    # cycling through the transfer modes
-    for i in range(9):
+    # alternating the transfer modes
+    for i in range(6):
         b2 = workloads.make_ag_gemm(4, 256, 256, 448, seed=50 + i, dist="uniform", scale=1.0).b
         say("ag_gemm repeat", i)
         c2, ag2 = ocg.ag_gemm(chunks, to_dev(b2), i % 4, a_gathered=poison((x.R * x.m, x.K)),
-                              config=ocg.default_config(transfer=i % 3))
+                              config=ocg.default_config(transfer=i % 2))
         torch.cuda.synchronize()
         assert np.array_equal(to_bits(ag2), a_full)
         assert_gate(to_bits(c2), oracle.ag_gemm(x.a_chunks, b2)[1], f"repeat {i}")
     ocg.Workspace.cached(ocg.OP_AG_GEMM, 4, 256, 256, 448).check()
 
 
-@pytest.mark.parametrize("transfer", [SIDE, ENGINE], ids=["side", "engine"])
-def test_ag_gemm_side_stream_ordering(ocg, transfer):
+def test_ag_gemm_side_stream_ordering(ocg):
     """A call on a non-default stream with a fresh workspace: the clear and
     the call are ordered on that stream, and the caller's stream waits for
-    the side producer or the copy engines (the gathered buffer is complete
-    for the next op)."""
+    the side producer (the gathered buffer is complete for the next op)."""
     x = workloads.make_ag_gemm(3, 160, 512, 256, seed=12, dist="uniform", scale=1.0)
     s = torch.cuda.Stream()
     with torch.cuda.stream(s):
         chunks = [to_dev(c) for c in x.a_chunks]
         b = to_dev(x.b)
         ag = poison((x.R * x.m, x.K))
-        say("ag_gemm on a side stream", transfer)
-        c, _ = ocg.ag_gemm(chunks, b, 2, a_gathered=ag, stream=s, config=ocg.default_config(transfer=transfer))
+        say("ag_gemm on a side stream")
+        c, _ = ocg.ag_gemm(chunks, b, 2, a_gathered=ag, stream=s, config=ocg.default_config(transfer=SIDE))
         snap = ag.clone()        # on s, after the call: must see every gathered row
     torch.cuda.synchronize()
     a_full, want = oracle.ag_gemm(x.a_chunks, x.b)
@@ -243,11 +205,38 @@ def test_ag_gemm_side_stream_ordering(ocg, transfer):
     assert_gate(to_bits(c), want, "side stream")
 
 
+def test_ag_gemm_transfers_back_to_back(ocg):
+    """Calls of both transfer modes and every measurement mode on one
+    workspace, back to back on one stream with timing events between them
+    and no host synchronisation (the bench's pattern): no wait times out, and
+    the last call's outputs are right."""
+    x = workloads.workload("ag_gemm_70b").make()
+    chunks = [to_dev(a) for a in x.a_chunks]
+    b = to_dev(x.b)
+    ag = poison((x.R * x.m, x.K))
+    c = poison((x.R * x.m, x.N))
+    ws = ocg.Workspace(ocg.OP_AG_GEMM, x.R, x.m, x.K, x.N)
+    s = torch.cuda.current_stream()
+    D = ocg.default_config
+    seq = [D(), D(transfer=SIDE), D(mode=ocg.MODE_COPY_ONLY, transfer=SIDE), D(mode=ocg.MODE_GEMM_ONLY),
+           D(transfer=SIDE), D(mode=ocg.MODE_COPY_ONLY), D(), D(transfer=SIDE)] * 3
+    say("ag_gemm back to back", len(seq), "calls")
+    for cf in seq:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(s)
+        ocg.ag_gemm(chunks, b, 0, a_gathered=ag, c=c, workspace=ws, config=cf)
+        e1.record(s)
+    ws.check()
+    a_full, want = oracle.ag_gemm(x.a_chunks, x.b)
+    assert np.array_equal(to_bits(ag), a_full)
+    assert_gate(to_bits(c), want, "back to back")
+
+
 def test_ag_gemm_timeout_is_reported_not_hung(ocg):
     """The host forces a flag that is never published and a 2 ms wait
     bound: the kernel still drains, and ocg_check reports the timeout."""
     x = workloads.make_ag_gemm(4, 128, 128, 224, seed=9, dist="uniform", scale=1.0)
-    for transfer in (INLINE, SIDE, ENGINE):
+    for transfer in (INLINE, SIDE):
         ws = ocg.Workspace(ocg.OP_AG_GEMM, 4, 128, 128, 224)
         # 128-row slabs, one K-slab: flag 2 is rank 2's chunk (a peer of rank 0)
         cfg = ocg.default_config(fault_skip_slab=2, spin_timeout_us=2000, transfer=transfer)
@@ -256,10 +245,6 @@ def test_ag_gemm_timeout_is_reported_not_hung(ocg):
         with pytest.raises(ocg.OcgError) as ei:
             ws.check()
         assert ei.value.code == ocg.ERR_TIMEOUT
-        if transfer == ENGINE:
-            # a copy engine's flag write may have landed after the kernel gave
-            # up: the workspace is cleared again before reuse
-            ws = ocg.Workspace(ocg.OP_AG_GEMM, 4, 128, 128, 224)
         say("ag_gemm after timeout", transfer)
         c, ag = ocg.ag_gemm([to_dev(c) for c in x.a_chunks], to_dev(x.b), 0, workspace=ws,
                             a_gathered=poison((512, 128)), config=ocg.default_config(transfer=transfer))
@@ -300,10 +285,6 @@ def test_ag_gemm_70b_share(ocg, local):
 
 def test_ag_gemm_70b_share_side(ocg):
     _full(ocg, "ag_gemm_70b", local=3, cfg=ocg.default_config(transfer=SIDE))
-
-
-def test_ag_gemm_70b_share_engine(ocg):
-    _full(ocg, "ag_gemm_70b", local=6, cfg=ocg.default_config(transfer=ENGINE))
 
 
 def test_ag_plan_on_device_matches_host_plan(ocg):
