@@ -50,6 +50,8 @@ WsLayout layout(int op, int R, int64_t m, int64_t K, int64_t N, int E, int topk)
   off = align256(off + sizeof(uint32_t) * L.max_slabs);
   L.rs_flag = off;
   off = align256(off + sizeof(uint32_t) * L.max_rs_tiles);
+  L.rs_sum = off;   // one word per row block of the local block (blocks of >= 128 rows)
+  off = align256(off + sizeof(uint32_t) * (op == OCG_OP_GEMM_RS ? cdiv((int)(rows / R), 128) + 1 : 0));
   L.moe_off = L.moe_lut = L.moe_perm = L.moe_bcnt = L.moe_inv = L.moe_lbase = L.moe_tflag = off;
   L.max_moe_tiles = 0;
   if (op == OCG_OP_AG_GROUPED_GEMM) {
@@ -508,6 +510,7 @@ int gemm_rs_call(ocg_handle h, const void* A, const void* B, int64_t M, int64_t 
   a.plan = make_rs_plan(R, local_rank, (int)M, (int)K, (int)N, rv.BM, rv.BN, reduce_rows(M, R, N, h->cus),
                         cfg.swizzle ? 1 : 0, push ? 1 : 0);
   if (a.plan.n_tiles > L.max_rs_tiles) return OCG_ERR_INVALID_ARG;
+  a.rs_sum = (uint32_t*)((char*)ws + L.rs_sum);
   a.local_rb0 = (local_rank * a.plan.blk) / rv.BM;
   a.local_nrb = cdiv(a.plan.blk, rv.BM);
   a.tpb = a.local_nrb * a.plan.n_cb;

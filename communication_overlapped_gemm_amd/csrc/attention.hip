@@ -176,8 +176,9 @@ __device__ __forceinline__ void issue_block(const AttnArgs& a, const BlockLoads&
 __device__ __forceinline__ int wait_chunk(const AttnArgs& a, int c, uint32_t epoch, uint32_t* seen) {
   const AgPlan& p = a.plan.cp;
   FlagWait w(a.cm.timeout_ticks);
-  for (int s = 0; s < p.bpr; ++s) w(&a.slab_flag[c * p.bpr + s], epoch);
-  return w.finish(a.cm, seen);
+  for (int s = threadIdx.x & 63; s < p.bpr; s += 64) w.add(&a.slab_flag[c * p.bpr + s], epoch);
+  w.finish(a.cm, seen);
+  return p.bpr;
 }
 
 // A half step covers 32 keys (key tiles 2h, 2h+1 of a block, one MFMA k

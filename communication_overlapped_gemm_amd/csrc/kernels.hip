@@ -97,8 +97,8 @@ struct KslabHook {
       } else {
         const uint64_t t0 = now_ticks();
         FlagWait w(cm->timeout_ticks);
-        for (int i = 0; i < ndeps; ++i)
-          for (int j = j0; j < j1; ++j) w((const uint32_t*)rows[i] + j, epoch);
+        const int gs = j1 - j0;
+        for (int L = threadIdx.x & 63; L < ndeps * gs; L += 64) w.add((const uint32_t*)rows[L / gs] + j0 + L % gs, epoch);
         uint32_t seen;
         w.finish(*cm, &seen);
         wait_ticks += (uint32_t)(now_ticks() - t0);
@@ -156,9 +156,9 @@ __global__ __launch_bounds__((Gemm<BM, BN>::NT), 1) void ag_gemm_kernel(AgArgs a
     uint32_t seen = 0;
     if (ndeps > 0 && wave == 0) {
       // consume_tile_wait on K-slab 0 (group 0), which holds every stage the
-      // prologue loads
+      // prologue loads: lane i polls dep i's flag
       FlagWait w(cm.timeout_ticks);
-      for (int i = 0; i < ndeps; ++i) w((const uint32_t*)__shfl(myrow, i), epoch);
+      if (lane < ndeps) w.add((const uint32_t*)myrow, epoch);
       w.finish(cm, &seen);
       seen = __builtin_amdgcn_readfirstlane(seen);
       s_deprow[lane] = myrow;
@@ -330,31 +330,71 @@ __global__ __launch_bounds__((Gemm<BM, BN>::NT), 1) void gemm_rs_kernel(RsArgs a
     // the peers' tiles, then the fixed-order reduce.
     int r0, r1;
     rs_strip(p, (int)j, &r0, &r1);
-    uint32_t seen = 0;
+    // The first strip of each row block (the lowest ticket among its strips,
+    // so it is claimed first) polls the flags of the block's tiles and then
+    // sets the block's summary word; every other strip of the block polls
+    // that one word. (Every strip polling every flag of its block put
+    // ~32K loads on a few flag lines at once: ~18 us per poll round.)
+    uint32_t seen = 0, designated = 0;
     int nwait = 0;
+    uint64_t t_own = 0;
     if (wave == 0) {
-      FlagWait w(cm.timeout_ticks);
-      for (int rb = r0 / BM; rb <= (r1 - 1) / BM; ++rb)
-        for (int cb = 0; cb < p.n_cb; ++cb) {
+      const int lo = p.local * p.blk;
+      for (int rb = r0 / BM; rb <= (r1 - 1) / BM; ++rb) {
+        const int first = rb * BM > lo ? rb * BM : lo;   // the block's first local row
+        if (first < r0 || first >= r1) continue;
+        // flag f of the block on lane f % 64: f = cb * per_tile + q, q = 0 the
+        // tile's own flag (pull) or rank 0's push, q > 0 a peer's
+        FlagWaitT<2> w(cm.timeout_ticks);
+        const int per_tile = args.push ? p.R : 1 + (args.peer_flags ? p.R - 1 : 0);
+        const int nf = p.n_cb * per_tile;
+        for (int f = lane; f < nf; f += 64) {
+          const int cb = f / per_tile, q = f - cb * per_tile;
           const int t_local = (rb - args.local_rb0) * p.n_cb + cb;
           if (args.push) {
             // every rank's pushed tile in our receive buffer, ours included
-            for (int s = 0; s < p.R; ++s) w(&args.rflag[p.local][s * args.tpb + t_local], args.flag_value);
-            continue;
-          }
-          w(&args.tile_flag[rb * p.n_cb + cb], epoch);
-          if (args.peer_flags) {
-            const int per_rank = args.local_nrb * p.n_cb;
-            for (int s = 0; s < p.R; ++s)
-              if (s != p.local) w(&args.peer_flags[s * per_rank + t_local], args.peer_flag_value);
+            w.add(&args.rflag[p.local][q * args.tpb + t_local], args.flag_value);
+          } else if (q == 0) {
+            w.add(&args.tile_flag[rb * p.n_cb + cb], epoch);
+          } else {
+            const int s = q - 1 < p.local ? q - 1 : q;   // the peers, skipping the local rank
+            w.add(&args.peer_flags[s * args.local_nrb * p.n_cb + t_local], args.peer_flag_value);
           }
         }
-      nwait = w.finish(cm, &seen);
+        const uint64_t tw = now_ticks();
+        w.finish(cm, &seen);   // ends with the acquire fence
+        nwait += nf;
+        t_own += now_ticks() - tw;
+        ++designated;
+        // set even after a timeout (the error word is set): the block's other
+        // strips must not wait on it for a second bound
+        if (lane == 0)
+          __hip_atomic_store(&args.rs_sum[rb - args.local_rb0], epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      FlagWait ws(cm.timeout_ticks);
+      int nsum = 0;
+      for (int rb = r0 / BM; rb <= (r1 - 1) / BM; ++rb) {
+        const int first = rb * BM > lo ? rb * BM : lo;
+        if (first >= r0 && first < r1) continue;
+        ws(&args.rs_sum[rb - args.local_rb0], epoch);
+        ++nsum;
+      }
+      if (nsum) {
+        uint32_t seen_sum;
+        nwait += ws.finish(cm, &seen_sum);
+        if (!seen) seen = seen_sum;
+      }
     }
+    // trace: the flags the strip depends on (polled by it or by its blocks'
+    // first strips), and in the next field the flags it polled itself
+    const int per_tile = args.push ? p.R : 1 + (args.peer_flags ? p.R - 1 : 0);
+    const int ndeps = ((r1 - 1) / BM - r0 / BM + 1) * p.n_cb * per_tile;
     const uint64_t t1 = now_ticks();
     __syncthreads();
     run_reduce_strip<G::NT>(args, r0, r1);
-    trace_task(cm, (uint32_t)(p.n_tiles + j), 5, r0, r1, nwait, 0, epoch, t0, t1, seen, 0);
+    // queue: row blocks this strip polled the tile flags of; wait ticks: time in those polls
+    trace_task(cm, (uint32_t)(p.n_tiles + j), 5, r0, r1, ndeps, nwait, epoch, t0, t1, seen, designated, 0,
+               (uint32_t)t_own);
   }
   finish(cm.hdr, epoch);
 }
@@ -695,9 +735,12 @@ __global__ __launch_bounds__((Gemm<BM, BN>::NT), 1) void moe_gemm_kernel(MoeArgs
       const int s_lo = (tf / p.m) * p.bpr + (tf % p.m) / p.S;
       const int s_hi = (tl / p.m) * p.bpr + (tl % p.m) / p.S;
       FlagWait w(cm.timeout_ticks);
-      for (int s = s_lo; s <= s_hi; ++s)
-        if (s / p.bpr != p.local) w(&args.slab_flag[s], epoch);
-      nwait = w.finish(cm, &seen);
+      for (int s = s_lo + lane; s <= s_hi; s += 64)
+        if (s / p.bpr != p.local) w.add(&args.slab_flag[s], epoch);
+      w.finish(cm, &seen);
+      nwait = s_hi - s_lo + 1 - (p.local * p.bpr + p.bpr - 1 >= s_lo && p.local * p.bpr <= s_hi
+                                   ? min(s_hi, p.local * p.bpr + p.bpr - 1) - max(s_lo, p.local * p.bpr) + 1
+                                   : 0);
     }
     const uint64_t t1 = now_ticks();
     __syncthreads();

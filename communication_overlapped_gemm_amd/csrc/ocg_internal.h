@@ -41,7 +41,7 @@ static_assert(sizeof(WsHeader) == 256, "header is 256 bytes");
 
 // Byte offsets of the workspace sections for one call shape.
 struct WsLayout {
-  size_t slab_cnt, slab_flag, rs_flag, moe_off, moe_lut, moe_perm, moe_bcnt, moe_inv, moe_lbase, moe_tflag, total;
+  size_t slab_cnt, slab_flag, rs_flag, rs_sum, moe_off, moe_lut, moe_perm, moe_bcnt, moe_inv, moe_lbase, moe_tflag, total;
   int max_slabs, max_rs_tiles, max_moe_tiles;
 };
 
@@ -89,6 +89,8 @@ struct RsArgs {
   uint32_t flag_value;          // push: value of a set flag (this call's)
   int push, tpb;                // tpb: tiles per row block (push)
   int local_rb0, local_nrb;     // row blocks of the local block (peer flag indexing)
+  uint32_t* rs_sum;             // [local row blocks]: epoch once the row block's first reduce strip
+                                // has seen every flag of the block's tiles
   RsPlan plan;
   Common cm;
 };

@@ -44,24 +44,45 @@ __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as
 // ---------------------------------------------------------------- flags
 
 // consume_tile_wait over all the flags a task depends on, run by one whole
-// wave: the k-th flag the task enumerates is polled by lane k % 64 (relaxed
-// loads, bounded by the timeout), so the flags are read in parallel, and one
-// acquire fence after the polls covers every one of them (an agent-scope
-// acquire invalidates the non-coherent cache lines, which costs about a
-// microsecond, too much to pay per flag). A timed-out wait sets the error
-// word and proceeds, so the grid always drains.
-struct FlagWait {
+// wave: the k-th flag the task enumerates belongs to lane k % 64 (relaxed
+// loads, bounded by the timeout); every lane loads its flags together, so a
+// round of polls over up to 64 * N flags costs one memory round trip (a
+// load per call, awaited before the next call, made a GEMM-RS strip's 128
+// pushed-tile flags cost ~23 us), and one acquire fence after the polls
+// covers every flag (an agent-scope acquire invalidates the non-coherent
+// cache lines, which costs about a microsecond, too much to pay per flag).
+// A timed-out wait sets the error word and proceeds, so the grid always
+// drains.
+template <int N>
+struct FlagWaitT {
   uint64_t t0, timeout;
-  int k, lane;
+  int k, lane, n;
   bool ok;
   uint32_t seen;
-  __device__ explicit FlagWait(uint64_t timeout_ticks)
-      : t0(now_ticks()), timeout(timeout_ticks), k(0), lane(threadIdx.x & 63), ok(true), seen(0) {}
+  const uint32_t* ptr[N > 0 ? N : 1];
+  uint32_t want[N > 0 ? N : 1];
+  __device__ explicit FlagWaitT(uint64_t timeout_ticks)
+      : t0(now_ticks()), timeout(timeout_ticks), k(0), lane(threadIdx.x & 63), n(0), ok(true), seen(0) {}
   // The next flag the task depends on, and the value that means "ready".
-  __device__ void operator()(const uint32_t* flag, uint32_t want) {
+  // Flag i goes to lane i % 64. With N slots a lane records its first N
+  // flags and polls them all at once in finish(); a flag beyond them (or
+  // every flag, N = 0) is polled here, one load after the other.
+  __device__ void operator()(const uint32_t* flag, uint32_t value) {
     if ((k++ & 63) != lane) return;
+    if constexpr (N > 0) {
+      if (n < N) {
+#pragma unroll
+        for (int i = 0; i < N; ++i)
+          if (i == n) {
+            ptr[i] = flag;
+            want[i] = value;
+          }
+        ++n;
+        return;
+      }
+    }
     uint32_t v = __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    while (v != want && ok) {
+    while (v != value && ok) {
       if (now_ticks() - t0 > timeout) {
         ok = false;
         break;
@@ -71,15 +92,51 @@ struct FlagWait {
     }
     seen = v;
   }
-  // After the last flag: the fence and the error word; returns the number of
-  // flags and (in *seen_out) a value lane 0 observed.
+  // A flag of this lane's own (the caller computes each lane's flags, flag
+  // i on lane i % 64, instead of walking every flag on every lane: a wave
+  // walking 128 flags spent ~18 us on the loop's control flow alone).
+  __device__ void add(const uint32_t* flag, uint32_t value) {
+    const int save = k;
+    k = lane;        // operator() takes the flag on this lane
+    (*this)(flag, value);
+    k = save;
+  }
+  // After the last flag: the recorded flags (their loads issued together,
+  // so a round of polls costs one memory round trip, not one per flag), the
+  // fence and the error word; returns the number of flags and (in
+  // *seen_out) a value lane 0 observed.
   __device__ int finish(const Common& cm, uint32_t* seen_out) {
+    if constexpr (N > 0) {
+      if (n > 0) {
+        for (;;) {
+          uint32_t v[N];
+          bool done = true;
+#pragma unroll
+          for (int i = 0; i < N; ++i)
+            if (i < n) v[i] = __hip_atomic_load(ptr[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+          for (int i = 0; i < N; ++i)
+            if (i < n && v[i] != want[i]) done = false;
+          seen = v[0];
+          if (done || !ok) break;
+          if (now_ticks() - t0 > timeout) {
+            ok = false;
+            break;
+          }
+          __builtin_amdgcn_s_sleep(1);
+        }
+      }
+    }
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     if (!ok) __hip_atomic_fetch_or(&cm.hdr->error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     *seen_out = __shfl(seen, 0);
     return k;
   }
 };
+// Flags polled one after the other: for waits on a flag or two (a tile's
+// start), where recorded flags would cost registers. Waits on many flags
+// (a GEMM-RS strip: 16 tile flags pulled, 128 pushed) use FlagWaitT<2>.
+using FlagWait = FlagWaitT<0>;
 
 // Wait until every store this thread issued has completed (for the
 // agent-coherent stores below: is visible at agent scope).
