@@ -193,7 +193,7 @@ __global__ __launch_bounds__((Gemm<BM, BN>::NT), 1) void ag_gemm_kernel(AgArgs a
     mainloop<BM, BN>(smem, t, acc, hook);
     stage_c<BM, BN>(smem, acc);
     for_each_c_chunk<BM, BN>(smem, [&](int row, int col, u32x4_t val) {
-      if (r0 + row < p.M && n0 + col < p.N) gstore16(args.c + (size_t)(r0 + row) * p.N + n0 + col, val);
+      if (r0 + row < p.M && n0 + col < p.N) gstore16_out(args.c + (size_t)(r0 + row) * p.N + n0 + col, val);
     });
     trace_task(cm, (uint32_t)(p.n_copy + v), 2, rb, cb, ndeps, 0, epoch, t0, t1, seen, ((uint32_t)q << 16) | qt, c0,
                hook.wait_ticks);
@@ -259,7 +259,7 @@ __device__ void run_reduce_strip(const RsArgs& a, int r0, int r1) {
       }
       u32x4_t o = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]), pack_bf16x2(acc[4], acc[5]),
                    pack_bf16x2(acc[6], acc[7])};
-      gstore16(a.out + (first + i) * 8 - (size_t)lo * p.N, o);
+      gstore16_out(a.out + (first + i) * 8 - (size_t)lo * p.N, o);
     }
   }
 }
@@ -776,7 +776,7 @@ __global__ __launch_bounds__((Gemm<BM, BN>::NT), 1) void moe_gemm_kernel(MoeArgs
       for_each_c_chunk<BM, BN>(smem, [&](int rr, int col, u32x4_t val) {
         if (rr < nrows && n0 + col < p.N) {
           const int slot = args.perm[r0 + rr];
-          gstore16(args.out + (size_t)slot * p.N + n0 + col, val);
+          gstore16_out(args.out + (size_t)slot * p.N + n0 + col, val);
         }
       });
     }

@@ -28,6 +28,11 @@ typedef __attribute__((address_space(1))) u32x4_t* gptr16;
 
 __device__ __forceinline__ u32x4_t gload16(const void* p) { return *(gcptr16)p; }
 __device__ __forceinline__ void gstore16(void* p, u32x4_t v) { *(gptr16)p = v; }
+// Store of a final output, written once and read only after the kernel:
+// non-temporal (streaming) cache policy, so the output does not crowd the
+// L2 lines the kernel's loads reuse (measured: 70B AG-GEMM launch 417.3 ->
+// 415.3 us, 8B 83.6 -> 82.0 us).
+__device__ __forceinline__ void gstore16_out(void* p, u32x4_t v) { __builtin_nontemporal_store(v, (gptr16)p); }
 
 __device__ __forceinline__ uint64_t now_ticks() { return __builtin_amdgcn_s_memrealtime(); }
 // Shader-clock cycle counter (its rate follows the compute-unit clock).
