@@ -176,6 +176,12 @@ int resolve(int op, int R, int64_t m, int64_t K, int64_t N, int E, int topk, con
     // for the side producer, whose workgroups keep 16 KiB in flight: small
     // tasks spread each K-slab over many of them
     int64_t ct = (r->transfer == OCG_TRANSFER_SIDE ? 16 * 1024 : 128 * 1024) / (r->KS > 0 ? r->KS : 1);
+    // grouped GEMM: every tile holds tokens of every rank, so no tile starts
+    // before the whole gather has landed; at least one task per workgroup
+    // spreads it over all of them (MoE share: 16-row tasks, 169 vs 175 us
+    // per step; the AllGather-GEMM, whose tiles wait only for their own
+    // rows' slabs, measured slower with such small tasks)
+    if (op == OCG_OP_AG_GROUPED_GEMM && cus > 0 && (int64_t)R * m / cus < ct) ct = (int64_t)R * m / cus;
     int p2 = 1;
     while ((int64_t)p2 * 2 <= ct) p2 *= 2;
     r->CT = p2 < r->S ? p2 : r->S;
