@@ -68,12 +68,21 @@ struct FlagWaitT {
   uint32_t want[N > 0 ? N : 1];
   __device__ explicit FlagWaitT(uint64_t timeout_ticks)
       : t0(now_ticks()), timeout(timeout_ticks), k(0), lane(threadIdx.x & 63), n(0), ok(true), seen(0) {}
-  // The next flag the task depends on, and the value that means "ready".
-  // Flag i goes to lane i % 64. With N slots a lane records its first N
-  // flags and polls them all at once in finish(); a flag beyond them (or
-  // every flag, N = 0) is polled here, one load after the other.
+  // The next flag the task depends on, and the value that means "ready":
+  // the task's k-th flag goes to lane k % 64.
   __device__ void operator()(const uint32_t* flag, uint32_t value) {
-    if ((k++ & 63) != lane) return;
+    if ((k++ & 63) == lane) take(flag, value);
+  }
+  // A flag of this lane's own: the caller computes each lane's flags (flag
+  // i on lane i % 64) instead of walking every flag on every lane -- a wave
+  // walking 128 flags spent ~18 us on the loop's control flow alone.
+  __device__ void add(const uint32_t* flag, uint32_t value) { take(flag, value); }
+
+ private:
+  // With N slots a lane records its first N flags and polls them all at
+  // once in finish(); a flag beyond them (or every flag, N = 0) is polled
+  // here, one load after the other.
+  __device__ void take(const uint32_t* flag, uint32_t value) {
     if constexpr (N > 0) {
       if (n < N) {
 #pragma unroll
@@ -97,15 +106,8 @@ struct FlagWaitT {
     }
     seen = v;
   }
-  // A flag of this lane's own (the caller computes each lane's flags, flag
-  // i on lane i % 64, instead of walking every flag on every lane: a wave
-  // walking 128 flags spent ~18 us on the loop's control flow alone).
-  __device__ void add(const uint32_t* flag, uint32_t value) {
-    const int save = k;
-    k = lane;        // operator() takes the flag on this lane
-    (*this)(flag, value);
-    k = save;
-  }
+
+ public:
   // After the last flag: the recorded flags (their loads issued together,
   // so a round of polls costs one memory round trip, not one per flag), the
   // fence and the error word; returns the number of flags and (in
