@@ -77,12 +77,23 @@ def test_gemm_rs_trace_notify_before_reduce(ocg):
             assert (r["kind"], r["a"], r["b"], r["c"]) == (3, t[2], t[3], int(t[4]))
             assert int(r["queue"]) == (t[5] << 16) | t[6], "tile taken from its XCD queue"
             done[(t[2], t[3])] = int(r["t_end"])
+    BM, blk = info["BM"], M // R
+    lo = local * blk
+    pollers = {}
     for t, r in zip(plan, recs):
         if t[0] == "reduce":
             assert (r["kind"], r["a"], r["b"], r["c"]) == (5, t[2], t[3], len(t[4]))
             assert r["flag_seen"] == r["epoch"]
             # the strip starts reducing only after every tile it reads was notified
             assert int(r["t_ready"]) >= max(done[d] for d in t[4]) - 0
+            # it polled the tile flags of the row blocks whose first local row it holds,
+            # and their summary words for the others
+            r0, r1 = t[2], t[3]
+            own = [rb for rb in range(r0 // BM, (r1 - 1) // BM + 1) if r0 <= max(rb * BM, lo) < r1]
+            assert int(r["queue"]) == len(own)
+            for rb in own:
+                pollers[rb] = pollers.get(rb, 0) + 1
+    assert pollers == {rb: 1 for rb in range(lo // BM, (lo + blk - 1) // BM + 1)}, "one poller per row block"
     check_reduce_bits(x, part, out)
 
 
