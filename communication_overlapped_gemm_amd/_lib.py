@@ -29,7 +29,7 @@ TILE_AUTO, TILE_256x224, TILE_128x224, TILE_128x256, TILE_128x128, TILE_256x256,
     -1, 0, 1, 2, 3, 4, 5, 6)
 
 EXPORTS = [
-    "ocg_config_default", "ocg_create", "ocg_destroy", "ocg_workspace_bytes",
+    "ocg_config_default", "ocg_create", "ocg_destroy", "ocg_workspace_bytes", "ocg_workspace_bytes_for",
     "ocg_workspace_init", "ocg_ag_gemm", "ocg_gemm_rs", "ocg_ag_grouped_gemm",
     "ocg_signal", "ocg_check", "ocg_status_string", "ocg_plan_info", "ocg_plan_task",
     "ocg_moe_combine_rs", "ocg_ag_attention", "ocg_plan_ag", "ocg_ag_gemm_noalloc",
@@ -45,7 +45,7 @@ class Config(C.Structure):
         ("trace", C.c_void_p), ("trace_capacity", C.c_uint32),
         ("peer_flags", C.c_void_p), ("peer_flag_value", C.c_uint32),
         ("transfer", C.c_int32), ("kslab_cols", C.c_int32), ("copy_delay", C.c_uint32),
-        ("xcd_remap", C.c_int32), ("side_grid", C.c_int32),
+        ("xcd_remap", C.c_int32), ("side_grid", C.c_int32), ("split_k", C.c_int32),
     ]
 
 
@@ -71,6 +71,8 @@ def _declare(lib):
         "ocg_create": (C.c_int, [C.c_int, C.POINTER(C.c_void_p)]),
         "ocg_destroy": (None, [_P]),
         "ocg_workspace_bytes": (C.c_size_t, [_P, C.c_int, C.c_int, C.c_int64, C.c_int64, C.c_int64, C.c_int, C.c_int]),
+        "ocg_workspace_bytes_for": (C.c_size_t, [_P, C.c_int, C.c_int, C.c_int64, C.c_int64, C.c_int64, C.c_int, C.c_int,
+                                                 _P]),
         "ocg_workspace_init": (C.c_int, [_P, _P, C.c_size_t, _P]),
         "ocg_ag_gemm": (C.c_int, [_P, C.POINTER(_P), C.c_int, C.c_int, C.c_int64, C.c_int64, _P, C.c_int64,
                                   _P, _P, _P, C.c_size_t, C.POINTER(Config), _P]),

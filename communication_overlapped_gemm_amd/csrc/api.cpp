@@ -16,6 +16,7 @@ struct ocg_handle_s {
   int device;
   int cus;
   int resident[3][OCG_TILE_COUNT];  // per op and tile preset, 0 = not queried yet
+  int resident_split[OCG_TILE_COUNT];   // AG-GEMM kernel of split-K units, per preset
   int resident_attn;                // attention kernel, 0 = not queried yet
   int side_fits[OCG_TILE_COUNT];    // AG-GEMM kernel + side producer fit on a CU: 0 unknown, 1 yes, -1 no
   hipStream_t side;                 // side stream of the SIDE transfer mode (default priority)
@@ -37,7 +38,10 @@ constexpr int kSideKslabCols = 512;   // default K-slab width of the SIDE transf
 // Workspace sections, sized for the worst plan a call of this shape can pick
 // (smallest slab, K-slab, tile and strip sizes). max_slabs counts flags:
 // (slab, K-slab) pairs for AG-GEMM, slabs for the other gathers.
-WsLayout layout(int op, int R, int64_t m, int64_t K, int64_t N, int E, int topk) {
+// sk_tiles > 0: an AG-GEMM plan that splits K, with tiles of sk_area
+// elements (per tile an arrival count, a flag and the first half's fp32 sums).
+WsLayout layout(int op, int R, int64_t m, int64_t K, int64_t N, int E, int topk, int64_t sk_tiles = 0,
+                int64_t sk_area = 0) {
   WsLayout L{};
   size_t off = sizeof(WsHeader);
   int64_t rows = (op == OCG_OP_GEMM_RS) ? m : (int64_t)R * m;
@@ -74,6 +78,15 @@ WsLayout layout(int op, int R, int64_t m, int64_t K, int64_t N, int E, int topk)
     L.moe_tflag = off;     // per grouped tile: epoch once its rows are stored
     off = align256(off + sizeof(uint32_t) * (size_t)L.max_moe_tiles);
   }
+  L.sk_cnt = L.sk_flag = L.sk_part = off;
+  if (op == OCG_OP_AG_GEMM && sk_tiles > 0) {
+    L.sk_cnt = off;
+    off = align256(off + sizeof(uint32_t) * (size_t)sk_tiles);
+    L.sk_flag = off;
+    off = align256(off + sizeof(uint32_t) * (size_t)sk_tiles);
+    L.sk_part = off;
+    off = align256(off + sizeof(float) * (size_t)sk_tiles * (size_t)sk_area);
+  }
   (void)K;
   L.total = off;
   return L;
@@ -88,28 +101,48 @@ bool shape_ok(int R, int64_t m, int64_t K, int64_t N) {
   return true;
 }
 
-// Estimated cost of a tile preset: rounds of the persistent grid times the
-// tile area, divided by the preset's relative speed per output element,
-// fitted to launches at the 8B and 70B shares on one MI355X: 256x224 tiles
-// 1.0; 128x224 0.9 (smaller wave tiles); 128x256 tiles
-// came out 3 % faster than 128x224 at the 8B AllGather share (224 vs 256
-// tiles, one round each) and 256x256 tiles 3 % faster than 128x256 at the
-// 8B GEMM-RS share (one round of 256 vs two).
-int choose_tile(int64_t M, int64_t N, int cus) {
-  static const double eff[OCG_TILE_COUNT] = {1.0, 0.9, 1.03, 0.75, 1.035, 0.0, 0.0};
-  int best = OCG_TILE_128x128;
+// Estimated cost of a tile preset split in sk K parts: rounds of the
+// persistent grid (of units, tiles x sk) times the tile area over the
+// preset's relative speed per output element, times the share of K a unit
+// runs plus, when split, a fixed cost worth the K loop over 1800 columns
+// (fitted: at the 8B share 256x224 halves ran their loops in 60 us against
+// 54 us for whole 128x224 tiles of the same MFMA work, and the combine --
+// one half's fp32 sums stored, then read and added -- took the other 12 us:
+// 85.3 against 72.0 us GEMM-only; on 512-1024-row shares with K 8192, whose
+// whole tiles fill under half the CUs, split 128x128 tiles were 8-10 %
+// faster).
+// Speeds from GEMM-only launches at the 8B AllGather share (M 4096, K 4096,
+// N 1792; one MI355X): 256x224 tiles 93.6 us for 128 tiles (one round, half
+// the CUs idle) = 1; 128x256 74.6 us for 224 tiles -> 0.717; 128x224 74.8 us
+// for 256 -> 0.626; 256x256 104.2 us for 112 -> 1.03; 128x128 94.0 us for
+// 448 (two rounds) -> 0.57.
+double tile_cost(int t, int64_t M, int64_t N, int64_t K, int cus, int sk) {
+  static const double eff[OCG_TILE_COUNT] = {1.0, 0.626, 0.717, 0.57, 1.03, 0.0, 0.0};
+  if (t < 0 || t >= OCG_TILE_COUNT || eff[t] <= 0) return 1e300;   // grouped-GEMM-only presets
+  const int64_t units = cdiv((int)M, tile_bm(t)) * (int64_t)cdiv((int)N, tile_bn(t)) * sk;
+  const int64_t rounds = (units + cus - 1) / cus;
+  const double part = 1.0 / sk + (sk > 1 ? 1800.0 / (double)K : 0.0);
+  return (double)rounds * tile_bm(t) * tile_bn(t) / eff[t] * part;
+}
+
+// The cheapest (preset, K parts): `tile` >= 0 fixes the preset; sk 2 is
+// considered only if `can_split`.
+void choose_tile(int64_t M, int64_t N, int64_t K, int cus, int tile, bool can_split, int* tile_out, int* sk_out) {
+  int best = tile >= 0 ? tile : OCG_TILE_128x128, best_sk = 1;
   double best_cost = 1e300;
   for (int t = 0; t < OCG_TILE_COUNT; ++t) {
-    if (eff[t] <= 0) continue;   // grouped-GEMM-only preset
-    int64_t tiles = cdiv((int)M, tile_bm(t)) * (int64_t)cdiv((int)N, tile_bn(t));
-    int64_t rounds = (tiles + cus - 1) / cus;
-    double cost = (double)rounds * tile_bm(t) * tile_bn(t) / eff[t];
-    if (cost < best_cost - 1e-9) {
-      best_cost = cost;
-      best = t;
+    if (tile >= 0 && t != tile) continue;
+    for (int sk = 1; sk <= (can_split ? 2 : 1); ++sk) {
+      const double cost = tile_cost(t, M, N, K, cus, sk);
+      if (cost < best_cost * (1.0 - 1e-9)) {
+        best_cost = cost;
+        best = t;
+        best_sk = sk;
+      }
     }
   }
-  return best;
+  *tile_out = best;
+  *sk_out = best_sk;
 }
 
 // Grouped GEMM: one row tile per expert where the rows an expert gets fit
@@ -131,26 +164,18 @@ int choose_moe_tile(int64_t T, int E, int topk) {
 }
 
 struct Resolved {
-  int tile, BM, BN, S, CT, KS, transfer;
+  int tile, BM, BN, S, CT, KS, transfer, SK;
 };
 
+// split_room: the caller's workspace can hold split-K sums (AG-GEMM; the
+// automatic choice splits only then).
 int resolve(int op, int R, int64_t m, int64_t K, int64_t N, int E, int topk, const ocg_config& c, int cus,
-            Resolved* r, bool side_ok = true) {
+            Resolved* r, bool split_room = true) {
   int64_t M = (op == OCG_OP_GEMM_RS) ? m : R * m;
-  if (op == OCG_OP_AG_GROUPED_GEMM)
-    r->tile = c.tile < 0 ? choose_moe_tile(M, E, topk) : c.tile;
-  else
-    r->tile = c.tile < 0 ? choose_tile(M, N, cus) : c.tile;
-  if (r->tile < 0 || r->tile >= OCG_TILE_COUNT) return OCG_ERR_INVALID_ARG;
-  if (op == OCG_OP_AG_GROUPED_GEMM ? !moe_tile_ok(r->tile) : (r->tile == OCG_TILE_320x224 || r->tile == OCG_TILE_288x224))
-    return OCG_ERR_INVALID_ARG;
-  r->BM = tile_bm(r->tile);
-  r->BN = tile_bn(r->tile);
-  r->S = c.slab_rows > 0 ? c.slab_rows : r->BM;
-  if (r->S < kMinSlabRows) return OCG_ERR_INVALID_ARG;
   // transfer mode and K-slab width (AG-GEMM; the other ops copy whole rows)
   r->transfer = OCG_TRANSFER_INLINE;
   r->KS = (int)K;
+  r->SK = 1;
   if (op == OCG_OP_AG_GEMM) {
     if (c.transfer < OCG_TRANSFER_AUTO || c.transfer > OCG_TRANSFER_SIDE) return OCG_ERR_INVALID_ARG;
     // AUTO: INLINE. Measured in one process, alternating, at the 70B share:
@@ -159,7 +184,6 @@ int resolve(int op, int R, int64_t m, int64_t K, int64_t N, int E, int topk, con
     // one kernel keeps the call simple for profilers that serialise
     // dispatches (the SIDE GEMM kernel would wait for a producer that has
     // not started).
-    (void)side_ok;
     r->transfer = c.transfer == OCG_TRANSFER_AUTO ? OCG_TRANSFER_INLINE : c.transfer;
     if (c.mode == OCG_MODE_GEMM_ONLY) r->transfer = OCG_TRANSFER_INLINE;   // no copies to place
     if (c.kslab_cols < 0 || c.kslab_cols % kMinKslabCols) return OCG_ERR_INVALID_ARG;
@@ -168,7 +192,39 @@ int resolve(int op, int R, int64_t m, int64_t K, int64_t N, int E, int topk, con
     else if (r->transfer == OCG_TRANSFER_SIDE)
       r->KS = kSideKslabCols;
     if (r->KS > K) r->KS = (int)K;
+    if (c.split_k < 0 || c.split_k > 2) return OCG_ERR_INVALID_ARG;
   }
+  // split K: AG-GEMM, inline copies, one K-slab, and halves of whole MFMA
+  // stage pairs (K % 128 == 0)
+  const bool can_split = op == OCG_OP_AG_GEMM && r->transfer == OCG_TRANSFER_INLINE && r->KS == K && K % 128 == 0 &&
+                         c.mode != OCG_MODE_COPY_ONLY;
+  if (op == OCG_OP_AG_GROUPED_GEMM) {
+    r->tile = c.tile < 0 ? choose_moe_tile(M, E, topk) : c.tile;
+  } else if (op == OCG_OP_AG_GEMM && c.split_k == 2) {
+    if (!can_split) return OCG_ERR_INVALID_ARG;
+    r->SK = 2;
+    r->tile = c.tile;
+    if (r->tile < 0) {   // the cheapest preset for halves
+      double best = 1e300;
+      for (int t = 0; t < OCG_TILE_COUNT; ++t) {
+        const double cost = tile_cost(t, M, N, K, cus, 2);
+        if (cost < best * (1.0 - 1e-9)) {
+          best = cost;
+          r->tile = t;
+        }
+      }
+    }
+  } else {
+    const bool auto_split = op == OCG_OP_AG_GEMM && c.split_k == 0 && can_split && split_room;
+    choose_tile(M, N, K, cus, c.tile, auto_split, &r->tile, &r->SK);
+  }
+  if (r->tile < 0 || r->tile >= OCG_TILE_COUNT) return OCG_ERR_INVALID_ARG;
+  if (op == OCG_OP_AG_GROUPED_GEMM ? !moe_tile_ok(r->tile) : (r->tile == OCG_TILE_320x224 || r->tile == OCG_TILE_288x224))
+    return OCG_ERR_INVALID_ARG;
+  r->BM = tile_bm(r->tile);
+  r->BN = tile_bn(r->tile);
+  r->S = c.slab_rows > 0 ? c.slab_rows : r->BM;
+  if (r->S < kMinSlabRows) return OCG_ERR_INVALID_ARG;
   if (c.copy_rows > 0) {
     r->CT = c.copy_rows;
   } else {
@@ -284,13 +340,25 @@ ocg_config cfg_or_default(const ocg_config* c) {
   return c ? *c : d;
 }
 
-int grid_for(ocg_handle h, int op, int tile, int tasks, const ocg_config& c) {
+// Persistent workgroups for `tasks` tickets of which `units` are GEMM tiles:
+// the kernel's resident capacity, except that a preset with two workgroups
+// per CU keeps one per CU when its tiles fit in one round -- a second
+// workgroup on a CU shares that CU's MFMA pipe, so tiles doubled up on some
+// CUs end late (128x128 tiles, 8 ranks x 256 rows, K 8192, N 1792: 224 tiles
+// plus 112 copy tasks on 336 workgroups took 150.6 us fused against 89.3 us
+// GEMM-only).
+int cap_grid(int resident, int cus, int tasks, int units) {
+  int g = resident * cus;
+  if (resident > 1 && units <= cus) g = cus;
+  if (tasks < g) g = tasks;
+  return g < 1 ? 1 : g;
+}
+
+int grid_for(ocg_handle h, int op, int tile, int tasks, int units, const ocg_config& c) {
   if (c.grid > 0) return c.grid;
   int& r = h->resident[op][tile];
   if (r == 0) r = resident_per_cu(op, tile);
-  int g = r * h->cus;
-  if (tasks < g) g = tasks;
-  return g < 1 ? 1 : g;
+  return cap_grid(r, h->cus, tasks, units);
 }
 
 Common make_common(void* ws, const ocg_config& c) {
@@ -310,6 +378,59 @@ Common make_common(void* ws, const ocg_config& c) {
 bool device_matches(ocg_handle h) {
   int d = -1;
   return hipGetDevice(&d) == hipSuccess && d == h->device;
+}
+
+// h = NULL plans for a 256-CU MI355X on which the producer fits.
+struct AgSetup {
+  Resolved rv;
+  AgPlan plan;
+  WsLayout L;   // the workspace this plan uses
+  int ggrid, pgrid;
+};
+
+int ag_setup(ocg_handle h, int R, int local_rank, int64_t m, int64_t K, int64_t N, const ocg_config& cfg,
+             AgSetup* o, size_t ws_bytes = SIZE_MAX) {
+  const int cus = h ? h->cus : 256;
+  int st = resolve(OCG_OP_AG_GEMM, R, m, K, N, 0, 0, cfg, cus, &o->rv, true);
+  if (st) return st;
+  auto need = [&](const Resolved& rv) {
+    const int64_t tiles = rv.SK > 1 ? (int64_t)cdiv((int)(R * m), rv.BM) * cdiv((int)N, rv.BN) : 0;
+    return layout(OCG_OP_AG_GEMM, R, m, K, N, 0, 0, tiles, (int64_t)rv.BM * rv.BN);
+  };
+  o->L = need(o->rv);
+  if (o->L.total > ws_bytes && o->rv.SK > 1) {
+    if (cfg.split_k == 2) return OCG_ERR_WORKSPACE_TOO_SMALL;
+    // the automatic choice splits only where the workspace holds the sums
+    st = resolve(OCG_OP_AG_GEMM, R, m, K, N, 0, 0, cfg, cus, &o->rv, false);
+    if (st) return st;
+    o->L = need(o->rv);
+  }
+  if (h && o->rv.transfer == OCG_TRANSFER_SIDE && !side_fits(h, o->rv.tile)) return OCG_ERR_UNSUPPORTED_SHAPE;
+  int resident = 1;
+  if (h) {
+    int& r = o->rv.SK > 1 ? h->resident_split[o->rv.tile] : h->resident[OCG_OP_AG_GEMM][o->rv.tile];
+    if (r == 0) r = resident_per_cu(OCG_OP_AG_GEMM, o->rv.tile, o->rv.SK);
+    resident = r;
+  } else if (o->rv.tile == OCG_TILE_128x128) {
+    resident = 2;   // no handle: two 128x128 workgroups fit on a CU, one of every other preset
+  }
+  const int tpr = cfg.grid > 0 ? cfg.grid : resident * cus;
+  AgPlan& p = o->plan;
+  p = make_ag_plan(R, local_rank, (int)m, (int)K, (int)N, o->rv.BM, o->rv.BN, o->rv.S, o->rv.CT,
+                   cfg.swizzle ? 1 : 0, cfg.mode, o->rv.KS, tpr, o->rv.SK);
+  const bool side = o->rv.transfer == OCG_TRANSFER_SIDE;
+  if (side) {
+    const int first = first_kslab_tickets(p);
+    p.n_inline = first < p.n_copy ? first : p.n_copy;
+  }
+  const int gtasks = p.n_inline + p.n_tiles * p.sk;
+  o->ggrid = cfg.grid > 0 ? (gtasks < tpr ? gtasks : tpr) : cap_grid(resident, cus, gtasks, p.n_tiles * p.sk);
+  o->pgrid = 0;
+  if (p.n_copy > p.n_inline) {
+    const int pg = cfg.side_grid > 0 ? cfg.side_grid : cus;
+    o->pgrid = pg < p.n_copy - p.n_inline ? pg : p.n_copy - p.n_inline;
+  }
+  return OCG_OK;
 }
 
 }  // namespace
@@ -366,7 +487,11 @@ void ocg_destroy(ocg_handle h) {
 }
 
 size_t ocg_workspace_bytes(ocg_handle h, int op, int R, int64_t m, int64_t K, int64_t N, int E, int topk) {
-  (void)h;
+  return ocg_workspace_bytes_for(h, op, R, m, K, N, E, topk, nullptr);
+}
+
+size_t ocg_workspace_bytes_for(ocg_handle h, int op, int R, int64_t m, int64_t K, int64_t N, int E, int topk,
+                               const ocg_config* cfgp) {
   if (op < 0 || op > 4) return 0;
   if (op == OCG_OP_AG_ATTENTION) return attn_shape_ok(R, m, K, N) ? layout(op, R, m, 0, 0, 0, 0).total : 0;
   if (op == OCG_OP_MOE_COMBINE_RS) return combine_shape_ok(R, m, N, topk) ? layout(op, R, m, 0, N, 0, topk).total : 0;
@@ -379,6 +504,12 @@ size_t ocg_workspace_bytes(ocg_handle h, int op, int R, int64_t m, int64_t K, in
   if (op == OCG_OP_AG_GROUPED_GEMM &&
       (E < 1 || E > kMaxExperts || topk < 1 || topk > kMaxTopk || topk > E || (int64_t)R * m * topk > kMaxRouteSlots))
     return 0;
+  if (op == OCG_OP_AG_GEMM) {
+    // with room for split-K sums where the plan splits
+    AgSetup su;
+    if (ag_setup(h, R, 0, m, K, N, cfg_or_default(cfgp), &su) != OCG_OK) return 0;
+    return su.L.total;
+  }
   return layout(op, R, m, K, N, E, topk).total;
 }
 
@@ -392,47 +523,6 @@ int ocg_workspace_init(ocg_handle h, void* ws, size_t bytes, void* stream) {
 // The AG-GEMM plan of a call: tile, slabs, K-slabs and transfer (resolve),
 // the rounds of tiles of the persistent grid (copy phases), the copy tickets
 // the GEMM kernel runs itself, and the two grids (producer 0 unless SIDE).
-// h = NULL plans for a 256-CU MI355X on which the producer fits.
-struct AgSetup {
-  Resolved rv;
-  AgPlan plan;
-  int ggrid, pgrid;
-};
-
-int ag_setup(ocg_handle h, int R, int local_rank, int64_t m, int64_t K, int64_t N, const ocg_config& cfg,
-             AgSetup* o) {
-  const int cus = h ? h->cus : 256;
-  const int tile0 = cfg.tile < 0 ? choose_tile(R * m, N, cus) : cfg.tile;
-  int st = resolve(OCG_OP_AG_GEMM, R, m, K, N, 0, 0, cfg, cus, &o->rv, h ? side_fits(h, tile0) : true);
-  if (st) return st;
-  if (h && o->rv.transfer == OCG_TRANSFER_SIDE && !side_fits(h, o->rv.tile)) return OCG_ERR_UNSUPPORTED_SHAPE;
-  int resident = 1;
-  if (h) {
-    int& r = h->resident[OCG_OP_AG_GEMM][o->rv.tile];
-    if (r == 0) r = resident_per_cu(OCG_OP_AG_GEMM, o->rv.tile);
-    resident = r;
-  } else if (o->rv.tile == OCG_TILE_128x128) {
-    resident = 2;   // no handle: two 128x128 workgroups fit on a CU, one of every other preset
-  }
-  const int tpr = cfg.grid > 0 ? cfg.grid : resident * cus;
-  AgPlan& p = o->plan;
-  p = make_ag_plan(R, local_rank, (int)m, (int)K, (int)N, o->rv.BM, o->rv.BN, o->rv.S, o->rv.CT,
-                   cfg.swizzle ? 1 : 0, cfg.mode, o->rv.KS, tpr);
-  const bool side = o->rv.transfer == OCG_TRANSFER_SIDE;
-  if (side) {
-    const int first = first_kslab_tickets(p);
-    p.n_inline = first < p.n_copy ? first : p.n_copy;
-  }
-  const int gtasks = p.n_inline + p.n_tiles;
-  o->ggrid = gtasks < tpr ? gtasks : tpr;
-  o->pgrid = 0;
-  if (p.n_copy > p.n_inline) {
-    const int pg = cfg.side_grid > 0 ? cfg.side_grid : cus;
-    o->pgrid = pg < p.n_copy - p.n_inline ? pg : p.n_copy - p.n_inline;
-  }
-  return OCG_OK;
-}
-
 int ocg_ag_gemm(ocg_handle h, const void* const* a_chunks, int R, int local_rank, int64_t m, int64_t K,
                 const void* b, int64_t N, void* a_gathered, void* c, void* ws, size_t ws_bytes,
                 const ocg_config* cfgp, void* stream) {
@@ -444,12 +534,13 @@ int ocg_ag_gemm(ocg_handle h, const void* const* a_chunks, int R, int local_rank
   if (!aligned16(b) || !aligned16(a_gathered) || !aligned16(c) || !aligned16(ws)) return OCG_ERR_INVALID_ARG;
   ocg_config cfg = cfg_or_default(cfgp);
   if (cfg.mode < 0 || cfg.mode > 2) return OCG_ERR_INVALID_ARG;
-  WsLayout L = layout(OCG_OP_AG_GEMM, R, m, K, N, 0, 0);
-  if (ws_bytes < L.total) return OCG_ERR_WORKSPACE_TOO_SMALL;
+  if (ws_bytes < layout(OCG_OP_AG_GEMM, R, m, K, N, 0, 0).total) return OCG_ERR_WORKSPACE_TOO_SMALL;
   if (!device_matches(h)) return OCG_ERR_INVALID_ARG;
   AgSetup su;
-  int st = ag_setup(h, R, local_rank, m, K, N, cfg, &su);
+  int st = ag_setup(h, R, local_rank, m, K, N, cfg, &su, ws_bytes);
   if (st) return st;
+  const WsLayout& L = su.L;
+  if (ws_bytes < L.total) return OCG_ERR_WORKSPACE_TOO_SMALL;
   AgArgs a{};
   for (int r = 0; r < R; ++r) a.chunks[r] = (const uint16_t*)a_chunks[r];
   a.b = (const uint16_t*)b;
@@ -457,6 +548,9 @@ int ocg_ag_gemm(ocg_handle h, const void* const* a_chunks, int R, int local_rank
   a.c = (uint16_t*)c;
   a.slab_cnt = (uint32_t*)((char*)ws + L.slab_cnt);
   a.slab_flag = (uint32_t*)((char*)ws + L.slab_flag);
+  a.sk_cnt = (uint32_t*)((char*)ws + L.sk_cnt);
+  a.sk_flag = (uint32_t*)((char*)ws + L.sk_flag);
+  a.sk_part = (float*)((char*)ws + L.sk_part);
   a.plan = su.plan;
   if (a.plan.R * a.plan.bpr * a.plan.nks > L.max_slabs) return OCG_ERR_INVALID_ARG;
   a.cm = make_common(ws, cfg);
@@ -524,7 +618,7 @@ int gemm_rs_call(ocg_handle h, const void* A, const void* B, int64_t M, int64_t 
   st = fill(a, cfg, rv);
   if (st) return st;
   a.cm = make_common(ws, cfg);
-  int grid = grid_for(h, OCG_OP_GEMM_RS, rv.tile, a.plan.n_tiles + a.plan.n_red, cfg);
+  int grid = grid_for(h, OCG_OP_GEMM_RS, rv.tile, a.plan.n_tiles + a.plan.n_red, a.plan.n_tiles, cfg);
   return launch_gemm_rs(a, rv.tile, grid, (hipStream_t)stream) == hipSuccess ? OCG_OK : OCG_ERR_HIP;
 }
 
@@ -675,7 +769,7 @@ int grouped_call(ocg_handle h, const void* const* a_chunks, int R, int local_ran
     c.N = (int)N;
     c.max_tiles = L.max_moe_tiles;
   }
-  int grid = grid_for(h, OCG_OP_AG_GROUPED_GEMM, rv.tile, a.plan.n_copy + L.max_moe_tiles, cfg);
+  int grid = grid_for(h, OCG_OP_AG_GROUPED_GEMM, rv.tile, a.plan.n_copy + L.max_moe_tiles, L.max_moe_tiles, cfg);
   return launch_moe(r, a, rv.tile, grid, (hipStream_t)stream) == hipSuccess ? OCG_OK : OCG_ERR_HIP;
 }
 
@@ -912,6 +1006,7 @@ int ocg_plan_ag(ocg_handle h, int R, int local_rank, int64_t m, int64_t K, int64
   out[4] = su.pgrid;
   out[5] = su.plan.n_inline;
   out[6] = su.plan.rpr;
+  out[7] = su.plan.sk;
   return OCG_OK;
 }
 
@@ -984,7 +1079,7 @@ int ocg_plan_task(ocg_handle h, int op, int R, int local_rank, int64_t m, int64_
     p = make_ag_plan(R, local_rank, (int)m, (int)K, (int)N, (int)info[1], (int)info[2], (int)info[3], (int)info[4],
                      cfg.swizzle, cfg.mode);
   }
-  if (ticket < 0 || ticket >= p.n_copy + (op == OCG_OP_AG_GEMM ? p.n_tiles : 0)) return OCG_OK;
+  if (ticket < 0 || ticket >= p.n_copy + (op == OCG_OP_AG_GEMM ? p.n_tiles * p.sk : 0)) return OCG_OK;
   if (ticket < p.n_copy) {
     CopyDesc d = copy_desc(p, (int)ticket);
     desc[0] = 1;
@@ -997,19 +1092,21 @@ int ocg_plan_task(ocg_handle h, int op, int R, int local_rank, int64_t m, int64_
     return OCG_OK;
   }
   int rb, cb;
-  tile_of(p.n_rb, p.n_cb, p.rb0, (int)(ticket - p.n_copy), &rb, &cb);
+  const int u = (int)(ticket - p.n_copy);
+  tile_of(p.n_rb, p.n_cb, p.rb0, u / p.sk, &rb, &cb);
   desc[0] = 2;
   desc[1] = rb;
   desc[2] = cb;
   int r0 = rb * p.BM, r1 = r0 + p.BM < p.M ? r0 + p.BM : p.M;
   int k = 0;
   int n = for_each_dep_slab(p.m, p.S, p.bpr, p.local, r0, r1, [&](int s) {
-    if (k < 4) desc[4 + k] = s;
+    if (k < 3) desc[4 + k] = s;
     ++k;
   });
   desc[3] = p.mode == 0 ? n : 0;
   if (p.mode != 0)
-    for (int i = 4; i < 8; ++i) desc[i] = -1;
+    for (int i = 4; i < 7; ++i) desc[i] = -1;
+  desc[7] = u % p.sk;
   return OCG_OK;
 }
 

@@ -109,7 +109,59 @@ struct KslabHook {
   }
 };
 
+// Split K, the combine of a tile's two K halves (called by every thread after
+// the half's K loop). The half that arrives first stores its fp32 sums (each
+// thread's 16-byte accumulator blocks at (block * NT + thread) * 16 bytes of
+// the tile's slot, agent-coherent) and publishes the tile's flag; it returns
+// false (nothing more to do). The second resets the arrival count, waits for
+// the flag -- the first half is already past its K loop, so the wait ends --
+// and adds the stored sums to its own: a + b rounds the same whichever half
+// came first, so C does not depend on the order. Returns true: the caller
+// writes the tile.
 template <int BM, int BN>
+__device__ bool combine_halves(const AgArgs& args, int v, AccTile<BM, BN>& acc, uint32_t epoch, uint32_t* s_bcast,
+                               uint32_t* seen) {
+  using G = Gemm<BM, BN>;
+  if (threadIdx.x == 0)
+    s_bcast[6] = __hip_atomic_fetch_add(&args.sk_cnt[v], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  const uint32_t before = __builtin_amdgcn_readfirstlane(s_bcast[6]);
+  float* slot = args.sk_part + (size_t)v * (BM * BN);
+  if (before == 0) {
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(slot, (uint32_t)(BM * BN * 4));
+#pragma unroll
+    for (int f = 0; f < G::FM; ++f)
+#pragma unroll
+      for (int g = 0; g < G::FN; ++g)
+        store16_agent(rs, (uint32_t)(((f * G::FN + g) * G::NT + threadIdx.x) * 16),
+                      __builtin_bit_cast(u32x4_t, acc.v[f][g]));
+    drain_stores();
+    __syncthreads();
+    if (threadIdx.x == 0) __hip_atomic_store(&args.sk_flag[v], epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return false;
+  }
+  if (threadIdx.x == 0) __hip_atomic_store(&args.sk_cnt[v], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (threadIdx.x < 64) {
+    FlagWait w(args.cm.timeout_ticks);
+    if (threadIdx.x == 0) w.add(&args.sk_flag[v], epoch);
+    w.finish(args.cm, seen);
+  }
+  __syncthreads();
+  const f32x4_t* src = (const f32x4_t*)slot;
+#pragma unroll
+  for (int f = 0; f < G::FM; ++f) {
+    f32x4_t x[G::FN];
+#pragma unroll
+    for (int g = 0; g < G::FN; ++g) x[g] = src[(f * G::FN + g) * G::NT + threadIdx.x];
+#pragma unroll
+    for (int g = 0; g < G::FN; ++g) acc.v[f][g] += x[g];
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  return true;
+}
+
+// SPLIT: work units are K halves of tiles (plan.sk == 2); otherwise tiles.
+template <int BM, int BN, bool SPLIT>
 __global__ __launch_bounds__((Gemm<BM, BN>::NT), 1) void ag_gemm_kernel(AgArgs args) {
   using G = Gemm<BM, BN>;
   __shared__ __attribute__((aligned(1024))) char smem_raw[G::LDS_BYTES + 256];
@@ -134,13 +186,16 @@ __global__ __launch_bounds__((Gemm<BM, BN>::NT), 1) void ag_gemm_kernel(AgArgs a
   int q = (int)__builtin_amdgcn_readfirstlane(s_bcast[3]) % kXcds, tried = 0;
   uint32_t qt = 0;
   TileCtx<BM, BN> t;
-  t.brs = make_rsrc(args.b, (uint32_t)((size_t)p.K * p.N * 2));
+  const int kl = SPLIT ? p.K / 2 : p.K;             // K columns of one work unit
   t.N = p.N;
-  t.nk = p.K / BKS;
+  t.nk = kl / BKS;
   const int spk = p.KS / BKS;                       // stages per K-slab (>= 8)
   for (;;) {
-    const int v = next_tile(cm.hdr, p.n_tiles, &q, &tried, s_bcast, &qt, cm.xcd_remap);
-    if (v < 0) break;
+    const int vu = next_tile(cm.hdr, SPLIT ? 2 * p.n_tiles : p.n_tiles, &q, &tried, s_bcast, &qt, cm.xcd_remap);
+    if (vu < 0) break;
+    const int v = SPLIT ? vu >> 1 : vu, half = SPLIT ? vu & 1 : 0;
+    const size_t k0 = (size_t)half * kl;           // first K column of the unit
+    t.brs = make_rsrc(args.b + k0 * p.N, (uint32_t)((size_t)kl * p.N * 2));
     const uint64_t t0 = now_ticks(), c0 = now_cycles();
     int rb, cb;
     tile_of(p.n_rb, p.n_cb, p.rb0, v, &rb, &cb);
@@ -171,32 +226,49 @@ __global__ __launch_bounds__((Gemm<BM, BN>::NT), 1) void ag_gemm_kernel(AgArgs a
     for (int i = 0; i < G::A_PER_WAVE; ++i) {
       const int row = min(r0 + dma_row<BM, BN>(wave, i, lane), p.M - 1);
       const int c = row / p.m;
-      t.rowp[i] = (const char*)((c == p.local) ? args.chunks[c] + (size_t)(row - c * p.m) * p.K
-                                               : args.a_gathered + (size_t)row * p.K);
+      t.rowp[i] = (const char*)(((c == p.local) ? args.chunks[c] + (size_t)(row - c * p.m) * p.K
+                                                : args.a_gathered + (size_t)row * p.K) + k0);
     }
     const int n0 = cb * BN;
     t.n0 = n0;
     AccTile<BM, BN> acc;
-    KslabHook<G::S, (G::S >= 6 ? 2 : 1)> hook;
-    hook.rows = (OCG_LDS const uint64_t*)s_deprow;
-    hook.land = (OCG_LDS uint32_t*)(smem + G::LDS_BYTES);
-    hook.cm = &cm;
-    hook.epoch = epoch;
-    hook.wait_ticks = 0;
-    hook.wave = wave;
-    hook.ndeps = ndeps;
-    hook.spk = spk;
-    hook.nks = ndeps > 0 ? p.nks : 0;   // no dependency: nothing to check
-    hook.nk = t.nk;
-    hook.g = 1;
-    hook.schedule();
-    mainloop<BM, BN>(smem, t, acc, hook);
+    uint32_t d = 0, wait_ticks = 0;
+    if constexpr (SPLIT) {
+      // one K-slab, which the start wait covered: nothing to check in the loop
+      mainloop<BM, BN>(smem, t, acc);
+      uint32_t seen2 = 0;
+      const uint64_t tc = now_ticks();
+      const bool writes = combine_halves<BM, BN>(args, v, acc, epoch, s_bcast, &seen2);
+      d = (uint32_t)half | (writes ? 2u : 0u);
+      if (!writes) {
+        trace_task(cm, (uint32_t)(p.n_copy + vu), 2, rb, cb, ndeps, d, epoch, t0, t1, seen,
+                   ((uint32_t)q << 16) | qt, c0, 0);
+        continue;
+      }
+      wait_ticks = (uint32_t)(now_ticks() - tc);
+    } else {
+      KslabHook<G::S, (G::S >= 6 ? 2 : 1)> hook;
+      hook.rows = (OCG_LDS const uint64_t*)s_deprow;
+      hook.land = (OCG_LDS uint32_t*)(smem + G::LDS_BYTES);
+      hook.cm = &cm;
+      hook.epoch = epoch;
+      hook.wait_ticks = 0;
+      hook.wave = wave;
+      hook.ndeps = ndeps;
+      hook.spk = spk;
+      hook.nks = ndeps > 0 ? p.nks : 0;   // no dependency: nothing to check
+      hook.nk = t.nk;
+      hook.g = 1;
+      hook.schedule();
+      mainloop<BM, BN>(smem, t, acc, hook);
+      wait_ticks = hook.wait_ticks;
+    }
     stage_c<BM, BN>(smem, acc);
     for_each_c_chunk<BM, BN>(smem, [&](int row, int col, u32x4_t val) {
       if (r0 + row < p.M && n0 + col < p.N) gstore16_out(args.c + (size_t)(r0 + row) * p.N + n0 + col, val);
     });
-    trace_task(cm, (uint32_t)(p.n_copy + v), 2, rb, cb, ndeps, 0, epoch, t0, t1, seen, ((uint32_t)q << 16) | qt, c0,
-               hook.wait_ticks);
+    trace_task(cm, (uint32_t)(p.n_copy + vu), 2, rb, cb, ndeps, d, epoch, t0, t1, seen, ((uint32_t)q << 16) | qt, c0,
+               wait_ticks);
   }
   finish(cm.hdr, epoch, cm.total_wgs);
 }
@@ -894,7 +966,10 @@ static_assert(gemm_waves<256, 224>() == 4 && gemm_waves<128, 224>() == 4 && gemm
 
 template <int BM, int BN>
 static hipError_t ag_launch(const AgArgs& a, int grid, hipStream_t s) {
-  hipLaunchKernelGGL((ag_gemm_kernel<BM, BN>), dim3(grid), dim3(Gemm<BM, BN>::NT), 0, s, a);
+  if (a.plan.sk == 2)
+    hipLaunchKernelGGL((ag_gemm_kernel<BM, BN, true>), dim3(grid), dim3(Gemm<BM, BN>::NT), 0, s, a);
+  else
+    hipLaunchKernelGGL((ag_gemm_kernel<BM, BN, false>), dim3(grid), dim3(Gemm<BM, BN>::NT), 0, s, a);
   return hipGetLastError();
 }
 
@@ -933,11 +1008,11 @@ static bool attrs(K kern, int* vgprs, int* lds) {
 bool kernel_resources(int op, int tile, int* vgprs, int* lds) {
   if (op < 0) return attrs(ag_side_copy_kernel, vgprs, lds);
   switch (tile) {
-    case OCG_TILE_256x224: return attrs(ag_gemm_kernel<256, 224>, vgprs, lds);
-    case OCG_TILE_128x224: return attrs(ag_gemm_kernel<128, 224>, vgprs, lds);
-    case OCG_TILE_128x256: return attrs(ag_gemm_kernel<128, 256>, vgprs, lds);
-    case OCG_TILE_128x128: return attrs(ag_gemm_kernel<128, 128>, vgprs, lds);
-    case OCG_TILE_256x256: return attrs(ag_gemm_kernel<256, 256>, vgprs, lds);
+    case OCG_TILE_256x224: return attrs(ag_gemm_kernel<256, 224, false>, vgprs, lds);
+    case OCG_TILE_128x224: return attrs(ag_gemm_kernel<128, 224, false>, vgprs, lds);
+    case OCG_TILE_128x256: return attrs(ag_gemm_kernel<128, 256, false>, vgprs, lds);
+    case OCG_TILE_128x128: return attrs(ag_gemm_kernel<128, 128, false>, vgprs, lds);
+    case OCG_TILE_256x256: return attrs(ag_gemm_kernel<256, 256, false>, vgprs, lds);
   }
   return false;
 }
@@ -998,7 +1073,7 @@ static int occ(K kern, int threads) {
   return n > 0 ? n : 1;
 }
 
-int resident_per_cu(int op, int tile) {
+int resident_per_cu(int op, int tile, int sk) {
   if (op == OCG_OP_AG_GROUPED_GEMM) {
     switch (tile) {
       case OCG_TILE_128x224: return occ(moe_gemm_kernel<128, 224>, Gemm<128, 224>::NT);
@@ -1010,11 +1085,16 @@ int resident_per_cu(int op, int tile) {
   }
   if (op == OCG_OP_AG_GEMM) {
     switch (tile) {
-      case OCG_TILE_256x224: return occ(ag_gemm_kernel<256, 224>, Gemm<256, 224>::NT);
-      case OCG_TILE_128x224: return occ(ag_gemm_kernel<128, 224>, Gemm<128, 224>::NT);
-      case OCG_TILE_128x256: return occ(ag_gemm_kernel<128, 256>, Gemm<128, 256>::NT);
-      case OCG_TILE_128x128: return occ(ag_gemm_kernel<128, 128>, Gemm<128, 128>::NT);
-      case OCG_TILE_256x256: return occ(ag_gemm_kernel<256, 256>, Gemm<256, 256>::NT);
+      case OCG_TILE_256x224: return sk == 2 ? occ(ag_gemm_kernel<256, 224, true>, Gemm<256, 224>::NT)
+                                           : occ(ag_gemm_kernel<256, 224, false>, Gemm<256, 224>::NT);
+      case OCG_TILE_128x224: return sk == 2 ? occ(ag_gemm_kernel<128, 224, true>, Gemm<128, 224>::NT)
+                                           : occ(ag_gemm_kernel<128, 224, false>, Gemm<128, 224>::NT);
+      case OCG_TILE_128x256: return sk == 2 ? occ(ag_gemm_kernel<128, 256, true>, Gemm<128, 256>::NT)
+                                           : occ(ag_gemm_kernel<128, 256, false>, Gemm<128, 256>::NT);
+      case OCG_TILE_128x128: return sk == 2 ? occ(ag_gemm_kernel<128, 128, true>, Gemm<128, 128>::NT)
+                                           : occ(ag_gemm_kernel<128, 128, false>, Gemm<128, 128>::NT);
+      case OCG_TILE_256x256: return sk == 2 ? occ(ag_gemm_kernel<256, 256, true>, Gemm<256, 256>::NT)
+                                           : occ(ag_gemm_kernel<256, 256, false>, Gemm<256, 256>::NT);
     }
   } else {
     switch (tile) {

@@ -41,7 +41,9 @@ static_assert(sizeof(WsHeader) == 256, "header is 256 bytes");
 
 // Byte offsets of the workspace sections for one call shape.
 struct WsLayout {
-  size_t slab_cnt, slab_flag, rs_flag, rs_sum, moe_off, moe_lut, moe_perm, moe_bcnt, moe_inv, moe_lbase, moe_tflag, total;
+  size_t slab_cnt, slab_flag, rs_flag, rs_sum, moe_off, moe_lut, moe_perm, moe_bcnt, moe_inv, moe_lbase, moe_tflag;
+  size_t sk_cnt, sk_flag, sk_part;   // AG-GEMM split K: per tile arrivals, flag, fp32 half (0 when unsplit)
+  size_t total;
   int max_slabs, max_rs_tiles, max_moe_tiles;
 };
 
@@ -63,6 +65,9 @@ struct AgArgs {
   uint16_t* c;
   uint32_t* slab_cnt;           // [flags]: copy tasks done per (slab, K-slab)
   uint32_t* slab_flag;          // [flags]: epoch once the (slab, K-slab) has landed
+  uint32_t* sk_cnt;             // split K, [tiles]: halves finished (back to 0 by the second)
+  uint32_t* sk_flag;            // split K, [tiles]: epoch once the first half's sums are stored
+  float* sk_part;               // split K, [tiles][BM * BN]: the first half's fp32 sums
   AgPlan plan;                  // copy tickets >= plan.n_inline: the side producer's
   Common cm;
 };
@@ -184,7 +189,8 @@ hipError_t launch_fill_u32(uint32_t* p, size_t n, uint32_t v, int release, hipSt
 constexpr size_t kNoAllocScratchBytes = (size_t)1 << 20;
 constexpr int kMaxDevices = 64;
 hipError_t noalloc_scratch_setup(int device, void** out);
-// Resident workgroups per CU of each persistent kernel (op, tile preset).
-int resident_per_cu(int op, int tile);
+// Resident workgroups per CU of each persistent kernel (op, tile preset; sk:
+// the AG-GEMM kernel for tiles split in sk K parts).
+int resident_per_cu(int op, int tile, int sk = 1);
 
 }  // namespace ocg

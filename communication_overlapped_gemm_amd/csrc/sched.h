@@ -32,6 +32,13 @@
 // one XCD thereby share A and B panels in that XCD's L2. A workgroup takes
 // tiles only once every copy ticket has been claimed, tiles wait only on copy
 // tasks, and copy tasks never wait: the schedule cannot deadlock.
+//
+// Split K (sk = 2): when the tiles would leave compute units idle for a
+// round, each tile becomes two units, its K halves, queued as consecutive
+// work items u = 2v, 2v + 1 of one XCD batch (the tile queues then hand out
+// units). The half that finishes first stores its fp32 accumulators; the
+// other adds them and writes the tile. Neither waits on a unit that has not
+// started, so this adds no deadlock either.
 #pragma once
 
 #include <stdint.h>
@@ -53,6 +60,7 @@ struct AgPlan {
   int n_rb, n_cb, bpr, n_tpc, nks, n_copy, n_tiles, rb0;
   int rpr;        // gathered rows per round of tiles (copy phases)
   int n_inline;   // copy tickets the GEMM kernel runs itself (the rest: side producer)
+  int sk;         // K parts per tile (1, or 2 = split K); work units = n_tiles * sk
 };
 
 // Copy phase of position q of the chunk sequence: swizzled, the peers by the
@@ -65,9 +73,10 @@ OCG_HD int copy_phase(const AgPlan& p, int q) {
 }
 
 // mode: 0 fused, 1 gemm only, 2 copy only. KS <= 0 or KS >= K: one K-slab.
-// tpr: tiles per round (the persistent grid); 0 = all tiles in one round.
+// tpr: work units per round (the persistent grid); 0 = all tiles in one round.
+// sk: K parts per tile (2 needs one K-slab and K % 128 == 0).
 OCG_HD AgPlan make_ag_plan(int R, int local, int m, int K, int N, int BM, int BN, int S, int CT,
-                           int swizzle, int mode, int KS = 0, int tpr = 0) {
+                           int swizzle, int mode, int KS = 0, int tpr = 0, int sk = 1) {
   AgPlan p;
   p.R = R; p.local = local; p.m = m; p.M = R * m; p.K = K; p.N = N;
   p.BM = BM; p.BN = BN; p.S = S; p.CT = CT; p.swizzle = swizzle; p.mode = mode;
@@ -80,7 +89,8 @@ OCG_HD AgPlan make_ag_plan(int R, int local, int m, int K, int N, int BM, int BN
   p.n_copy = (mode == 1) ? 0 : R * p.n_tpc * p.nks;
   p.n_tiles = (mode == 2) ? 0 : p.n_rb * p.n_cb;
   p.rb0 = swizzle ? (int)(((long long)local * m) / BM) : 0;
-  const int rb_per_round = tpr > 0 ? tpr / p.n_cb : p.n_rb;
+  p.sk = sk > 1 ? sk : 1;
+  const int rb_per_round = tpr > 0 ? tpr / (p.n_cb * p.sk) : p.n_rb;
   p.rpr = (rb_per_round > 0 ? rb_per_round : 1) * BM;
   p.n_inline = p.n_copy;
   return p;

@@ -44,11 +44,13 @@ class Workspace:
     workspace must be ordered on one stream."""
 
     def __init__(self, op: int, R: int, m: int, K: int, N: int, E: int = 0, topk: int = 0,
-                 device: Optional[int] = None, stream=None):
-        n = lib.ocg_workspace_bytes(None, op, R, m, K, N, E, topk)
-        if n == 0:
-            raise _lib.OcgError(_lib.ERR_UNSUPPORTED_SHAPE, "ocg_workspace_bytes")
+                 device: Optional[int] = None, stream=None, config: Optional[Config] = None):
         dev = torch.cuda.current_device() if device is None else device
+        # sized for calls with `config` (default: the default configuration)
+        n = lib.ocg_workspace_bytes_for(handle(dev), op, R, m, K, N, E, topk,
+                                        C.byref(config) if config is not None else None)
+        if n == 0:
+            raise _lib.OcgError(_lib.ERR_UNSUPPORTED_SHAPE, "ocg_workspace_bytes_for")
         self.buf = torch.empty(n, dtype=torch.uint8, device=f"cuda:{dev}")
         self.nbytes = n
         self.device = dev
@@ -72,15 +74,19 @@ class Workspace:
         check(lib.ocg_check(handle(self.device), self.ptr), "ocg_check")
 
     @classmethod
-    def cached(cls, op, R, m, K, N, E=0, topk=0, device=None, stream=None):
-        """One workspace per (shape, device, stream): calls of one shape on
-        different streams do not share counters."""
+    def cached(cls, op, R, m, K, N, E=0, topk=0, device=None, stream=None, config=None):
+        """One workspace per (shape, device, stream, size the call's
+        configuration needs -- an AG-GEMM plan that splits K needs room for
+        the halves' sums): calls of one shape on different streams do not
+        share counters."""
         dev = torch.cuda.current_device() if device is None else device
         sp = _stream_ptr(stream)
-        key = (op, R, m, K, N, E, topk, dev, sp)
+        n = lib.ocg_workspace_bytes_for(handle(dev), op, R, m, K, N, E, topk,
+                                        C.byref(config) if config is not None else None)
+        key = (op, R, m, K, N, E, topk, dev, sp, n)
         ws = _workspaces.get(key)
         if ws is None:
-            ws = _workspaces[key] = cls(op, R, m, K, N, E, topk, dev, stream)
+            ws = _workspaces[key] = cls(op, R, m, K, N, E, topk, dev, stream, config)
         return ws
 
 
@@ -117,9 +123,9 @@ def ag_gemm(a_chunks: Sequence[torch.Tensor], b: torch.Tensor, local_rank: int =
         c = torch.empty((R * m, N), dtype=torch.bfloat16, device=dev)
     _check_bf16(a_gathered, "a_gathered", (R * m, K))
     _check_bf16(c, "c", (R * m, N))
-    ws = workspace or Workspace.cached(_lib.OP_AG_GEMM, R, m, K, N, device=dev.index, stream=stream)
-    ptrs = (C.c_void_p * R)(*[t.data_ptr() for t in a_chunks])
     cfg = _cfg(config)
+    ws = workspace or Workspace.cached(_lib.OP_AG_GEMM, R, m, K, N, device=dev.index, stream=stream, config=cfg)
+    ptrs = (C.c_void_p * R)(*[t.data_ptr() for t in a_chunks])
     check(lib.ocg_ag_gemm(handle(dev.index), ptrs, R, local_rank, m, K, b.data_ptr(), N, a_gathered.data_ptr(),
                           c.data_ptr(), ws.ptr, ws.nbytes, C.byref(cfg), _stream_ptr(stream)), "ocg_ag_gemm")
     return c, a_gathered
@@ -391,7 +397,7 @@ def plan_ag(R: int, local_rank: int, m: int, K: int, N: int, config: Optional[Co
     cfg = _cfg(config)
     check(lib.ocg_plan_ag(handle, R, local_rank, m, K, N, C.byref(cfg), out), "ocg_plan_ag")
     return dict(kslab_cols=out[0], nks=out[1], transfer=out[2], gemm_grid=out[3], side_grid=out[4],
-                n_inline=out[5], rows_per_round=out[6])
+                n_inline=out[5], rows_per_round=out[6], split_k=out[7])
 
 
 def plan_task(op: int, R: int, local_rank: int, m: int, K: int, N: int, ticket: int,

@@ -156,6 +156,11 @@ typedef struct ocg_config {
                                0 = one queue in plain tile order (ablation) */
   int32_t side_grid;        /* SIDE transfer: producer workgroups (one per compute unit at most
                                counts); 0 = auto */
+  int32_t split_k;          /* ocg_ag_gemm: 0 = auto (split where the cost estimate favours it
+                               and the workspace holds the sums), 1 = off, 2 = every tile as two
+                               K halves (needs the INLINE transfer, one K-slab and K % 128 == 0:
+                               OCG_ERR_INVALID_ARG otherwise; OCG_ERR_WORKSPACE_TOO_SMALL if
+                               the workspace lacks room for the sums) */
 } ocg_config;
 
 /* Opaque per-device handle: device id, compute-unit count and the resident
@@ -171,12 +176,22 @@ void ocg_config_default(ocg_config* cfg);
 int ocg_create(int device, ocg_handle* out);
 void ocg_destroy(ocg_handle h);
 
-/* Workspace bytes for `op`: AG_GEMM (R, m = rows per rank, K, N),
- * GEMM_RS (R, m = M total rows, K, N), AG_GROUPED_GEMM (R, m, K, N, E, topk),
- * MOE_COMBINE_RS (R, m, 0, N, 0, topk), AG_ATTENTION (R, m = tokens per
- * rank, K = Hq, N = Hkv). `h` may be NULL (the size does not depend on the
- * device). Unused arguments are ignored. Returns 0 on invalid arguments. */
+/* Workspace bytes for `op` with the default configuration: AG_GEMM (R,
+ * m = rows per rank, K, N), GEMM_RS (R, m = M total rows, K, N),
+ * AG_GROUPED_GEMM (R, m, K, N, E, topk), MOE_COMBINE_RS (R, m, 0, N, 0,
+ * topk), AG_ATTENTION (R, m = tokens per rank, K = Hq, N = Hkv). For AG_GEMM
+ * this includes room for the fp32 sums of split-K tiles (BM x BN x 4 bytes
+ * per tile) where the default plan splits, which depends on the device's
+ * compute units (`h`; NULL = a 256-CU MI355X); the other sizes do not depend
+ * on the device. Unused arguments are ignored. Returns 0 on invalid
+ * arguments. */
 size_t ocg_workspace_bytes(ocg_handle h, int op, int R, int64_t m, int64_t K, int64_t N, int E, int topk);
+
+/* As ocg_workspace_bytes, for calls made with configuration `cfg` (NULL =
+ * default), e.g. ocg_ag_gemm with split_k = 2. Returns 0 on invalid
+ * arguments or configurations. */
+size_t ocg_workspace_bytes_for(ocg_handle h, int op, int R, int64_t m, int64_t K, int64_t N, int E, int topk,
+                               const ocg_config* cfg);
 
 /* Clear a workspace once before its first use (a fill kernel on `stream`). */
 int ocg_workspace_init(ocg_handle h, void* workspace, size_t ws_bytes, void* stream);
@@ -191,6 +206,13 @@ int ocg_workspace_init(ocg_handle h, void* workspace, size_t ws_bytes, void* str
  * Copy tasks pull each peer chunk into a_gathered slab by slab and publish a
  * per-slab flag; GEMM tiles wait on the flags of the slabs they read (the
  * local rank's rows are read from its own shard and never wait).
+ * Split K (cfg->split_k; chosen automatically when the tiles would leave
+ * compute units idle, e.g. 128 tiles on 256 CUs): each tile runs as two
+ * work units, one per K half; the half that finishes first stores its fp32
+ * sums in the workspace, and the other adds them to its own and writes the
+ * tile. C is then fp32(first half) + fp32(second half) rounded once --
+ * the same bits whichever half finishes first, but not always the same
+ * bits as the unsplit sum (another fp32 summation order).
  */
 int ocg_ag_gemm(ocg_handle h, const void* const* a_chunks, int R, int local_rank,
                 int64_t m, int64_t K, const void* b, int64_t N, void* a_gathered, void* c,
@@ -206,7 +228,11 @@ int ocg_ag_gemm(ocg_handle h, const void* const* a_chunks, int R, int local_rank
  * nothing itself. Limit: shapes whose AG-GEMM workspace
  * (ocg_workspace_bytes(h, OCG_OP_AG_GEMM, R, m, K, N, 0, 0)) exceeds 1 MiB
  * return OCG_ERR_WORKSPACE_TOO_SMALL and enqueue nothing (the 70B-class
- * share needs about 130 KiB). All calls on one GPU share the scratch, which
+ * share needs about 130 KiB). K is split (cfg->split_k) only where the
+ * split-K sums fit the scratch too: where ocg_ag_gemm would split and this
+ * entry point cannot, C can differ from ocg_ag_gemm's in the last bit (another
+ * fp32 summation order, the same error bound), and split_k = 2 returns
+ * OCG_ERR_WORKSPACE_TOO_SMALL. All calls on one GPU share the scratch, which
  * keeps the last call's state: calls that overlap on one GPU (on different
  * streams, or from different handles or threads) race and must not be
  * issued; calls ordered on one stream are fine. A timed-out flag wait is
@@ -420,8 +446,8 @@ int ocg_plan_info(ocg_handle h, int op, int R, int local_rank, int64_t m, int64_
  * out[3] = persistent GEMM workgroups, out[4] = producer workgroups (SIDE)
  * or 0, out[5] = copy tickets the GEMM kernel runs itself (the first K-slab
  * of the first copy phase under SIDE, all of them otherwise), out[6] =
- * gathered rows per round of tiles (copy phases), out[7] = 0. `h` as for
- * ocg_plan_info. */
+ * gathered rows per round of tiles (copy phases), out[7] = K parts per tile
+ * (1, or 2 when split). `h` as for ocg_plan_info. */
 int ocg_plan_ag(ocg_handle h, int R, int local_rank, int64_t m, int64_t K, int64_t N, const ocg_config* cfg,
                 int64_t out[8]);
 
@@ -429,8 +455,9 @@ int ocg_plan_ag(ocg_handle h, int R, int local_rank, int64_t m, int64_t K, int64
  * ocg_trace_rec: AG copies, then AG tiles; RS tiles, then RS strips):
  * desc[0]=kind (1 copy, 2 AG tile, 3 RS tile, 5 RS strip, 0 none),
  * copy: desc[1]=chunk, [2]=piece, [3]=row0, [4]=row1, [5]=slab, [6]=K-slab;
- * AG tile: desc[1]=rb, [2]=cb, [3]=#dependency slabs, [4..7]=first four
- *          dependency slab ids (-1 if none);
+ * AG tile (a work unit: a tile, or one K half of it when split):
+ *          desc[1]=rb, [2]=cb, [3]=#dependency slabs, [4..6]=first three
+ *          dependency slab ids (-1 if none), [7]=K part (0, or 0/1 when split);
  * RS tile: desc[1]=rb, [2]=cb, [3]=local-block (0/1), [4]=XCD queue,
  *          [5]=ticket within the queue;
  * RS strip: desc[1]=row0, [2]=row1;

@@ -50,6 +50,11 @@ BM x BN, slab rows S, copy-task rows CT with S % CT == 0, K-slab columns KS):
   queue 0.
   A tile waits, for every K-slab it loads, on that K-slab's flag of each of
   its dependency slabs, before its first load of the K-slab.
+  Split K (SK = 2 parts, one K-slab): tile v becomes two work units, u = 2v
+  (columns [0, K/2)) and u = 2v + 1 (columns [K/2, K)), both with the tile's
+  dependencies; the units take the slots n_copy + u and are what is dealt to
+  the queues (batches of BATCH units). The affine map from a slot to its
+  task keeps its form: tile = unit // SK, part = unit % SK.
 GEMM-RS: slots [0, n_tiles) are GEMM tiles in the same order and queues,
   with rb0 = (l*M/R)//BM when swizzled -- with push transfers rb0 =
   (((l+1) mod R)*M/R)//BM, so the local block comes last; each stores its
@@ -138,6 +143,7 @@ class Tile:
     deps: Tuple[int, ...]   # global slab ids waited on
     queue: int = 0          # XCD queue holding the tile
     qticket: int = 0        # ticket of the tile within that queue
+    part: int = 0           # K part of a split tile (0 when unsplit)
 
 
 def copy_sequence(R: int, local: int, swizzle: bool) -> List[int]:
@@ -196,8 +202,9 @@ def slab_targets(R, m, S, CT) -> List[int]:
 
 
 def ag_gemm_plan(R, m, K, N, local, BM, BN, S, CT, swizzle=True, mode="fused", KS=None, xcd_remap=True,
-                 rpr=None):
-    """Full ticket list for the AG-GEMM kernel: list of CopyTask and Tile.
+                 rpr=None, sk=1):
+    """Full ticket list for the AG-GEMM kernel: list of CopyTask and Tile
+    (one Tile per work unit: sk K parts per tile).
     rpr: gathered rows per round of tiles (copy phases); None = one round."""
     M = R * m
     n_rb, n_cb = _cdiv(M, BM), _cdiv(N, BN)
@@ -208,7 +215,8 @@ def ag_gemm_plan(R, m, K, N, local, BM, BN, S, CT, swizzle=True, mode="fused", K
     if mode in ("fused", "gemm_only"):
         rb0 = (local * m) // BM if swizzle else 0
         base = len(tasks)
-        where = queue_of(n_rb * n_cb) if xcd_remap else {v: (0, v) for v in range(n_rb * n_cb)}
+        n_units = n_rb * n_cb * sk
+        where = queue_of(n_units) if xcd_remap else {u: (0, u) for u in range(n_units)}
         for v, (rb, cb) in enumerate(tile_order(n_rb, n_cb, rb0)):
             deps = set()
             if mode == "fused":
@@ -216,7 +224,9 @@ def ag_gemm_plan(R, m, K, N, local, BM, BN, S, CT, swizzle=True, mode="fused", K
                     c = row // m
                     if c != local:
                         deps.add(c * bpr + (row % m) // S)
-            tasks.append(Tile(base + v, rb, cb, tuple(sorted(deps)), *where[v]))
+            for part in range(sk):
+                u = v * sk + part
+                tasks.append(Tile(base + u, rb, cb, tuple(sorted(deps)), *where[u], part=part))
     return tasks
 
 

@@ -91,15 +91,24 @@ def test_plan_info_tile_choice():
     # 70B share: 256x224 tiles (exactly 512 = two rounds of 256 CUs)
     p = ocg.plan_info(ocg.OP_AG_GEMM, 8, 0, 1024, 8192, 3584)
     assert (p["BM"], p["BN"], p["n_tiles"]) == (256, 224, 512)
-    # 8B share: 128x256 (224 tiles, one round)
+    assert ocg.plan_ag(8, 0, 1024, 8192, 3584)["split_k"] == 1
+    # 8B share: 128x256 (224 tiles, one round), whole tiles (K halves of
+    # 256x224 tiles measured slower)
     p = ocg.plan_info(ocg.OP_AG_GEMM, 8, 0, 512, 4096, 1792)
     assert (p["BM"], p["BN"], p["n_tiles"]) == (128, 256, 224)
+    assert ocg.plan_ag(8, 0, 512, 4096, 1792)["split_k"] == 1
+    # a 1024-row share with K 8192: 112 tiles of 128x128 fill under half the
+    # CUs, so they run as 224 K halves
+    p = ocg.plan_info(ocg.OP_AG_GEMM, 8, 0, 128, 8192, 1792)
+    assert (p["BM"], p["BN"], p["n_tiles"]) == (128, 128, 112)
+    assert ocg.plan_ag(8, 0, 128, 8192, 1792)["split_k"] == 2
     # GEMM-RS 4096 x 4096: 256x256 (256 tiles, one round)
     p = ocg.plan_info(ocg.OP_GEMM_RS, 8, 0, 4096, 1792, 4096)
     assert (p["BM"], p["BN"], p["n_tiles"]) == (256, 256, 256)
     # tiny AllGather share (4 x [128, 256] x [256, 256]): 128x128, 8 tiles
     p = ocg.plan_info(ocg.OP_AG_GEMM, 4, 0, 128, 256, 256)
     assert (p["BM"], p["BN"], p["n_tiles"]) == (128, 128, 8)
+    assert ocg.plan_ag(4, 0, 128, 256, 256)["split_k"] == 1
 
 
 def test_plan_info_moe_tile_choice():
@@ -158,15 +167,15 @@ def test_ag_plan_matches_oracle_schedule(case, swizzle, mode, transfer, kslab):
     assert ag["kslab_cols"] == want_ks and ag["nks"] == -(-K // want_ks)
     # rows per round: the persistent grid's tiles per round over the column blocks
     n_cb = -(-N // info["BN"])
-    assert ag["rows_per_round"] == max(1, ag_grid_tiles(info, R, m, N) // n_cb) * info["BM"]
+    assert ag["rows_per_round"] == max(1, ag_grid_tiles(info, R, m, N) // (n_cb * ag["split_k"])) * info["BM"]
     want = sch.ag_gemm_plan(R, m, K, N, local, info["BM"], info["BN"], info["slab_rows"], info["copy_rows"],
-                            bool(swizzle), mode, KS=ag["kslab_cols"], rpr=ag["rows_per_round"])
+                            bool(swizzle), mode, KS=ag["kslab_cols"], rpr=ag["rows_per_round"], sk=ag["split_k"])
     if side and mode != "gemm_only":
         # the GEMM kernel copies the first K-slab of the first phase itself
         first = sch.copy_phases(R, m, local, bool(swizzle), ag["rows_per_round"])[0]
         n_inline = len(first) * -(-m // info["copy_rows"]) if ag["nks"] > 1 or len(first) < R else len(want)
         assert ag["n_inline"] == min(n_inline, info["n_copy_or_strips"])
-    assert len(want) == info["n_copy_or_strips"] + info["n_tiles"]
+    assert len(want) == info["n_copy_or_strips"] + info["n_tiles"] * ag["split_k"]
     n_flags = R * -(-m // info["slab_rows"]) * ag["nks"]
     assert info["n_slabs_or_strip_rows"] == n_flags
     for t in want + [None]:
@@ -180,7 +189,74 @@ def test_ag_plan_matches_oracle_schedule(case, swizzle, mode, transfer, kslab):
         else:
             deps = list(t.deps)
             assert d[:4] == [2, t.rb, t.cb, len(deps)]
-            assert d[4:4 + min(4, len(deps))] == deps[:4]
+            assert d[4:4 + min(3, len(deps))] == deps[:3]
+            assert d[7] == t.part
+
+
+def test_split_k_rules_and_workspace():
+    lib = ocg.lib
+    ws = lambda R, m, K, N, cfg=None: lib.ocg_workspace_bytes_for(None, ocg.OP_AG_GEMM, R, m, K, N, 0, 0,
+                                                                  C.byref(cfg) if cfg is not None else None)
+    # a 1024-row share with K 8192 splits by default: room for 112 tiles of
+    # 128x128 fp32 sums
+    base = ws(8, 128, 8192, 1792, ocg.default_config(split_k=1))
+    assert ws(8, 128, 8192, 1792) == lib.ocg_workspace_bytes(None, ocg.OP_AG_GEMM, 8, 128, 8192, 1792, 0, 0)
+    assert ws(8, 128, 8192, 1792) >= base + 112 * 128 * 128 * 4
+    # the 8B share keeps whole tiles: flags only
+    assert lib.ocg_workspace_bytes(None, ocg.OP_AG_GEMM, 8, 512, 4096, 1792, 0, 0) < (1 << 20)
+    # the 70B share does not, unless asked
+    base70 = lib.ocg_workspace_bytes(None, ocg.OP_AG_GEMM, 8, 1024, 8192, 3584, 0, 0)
+    assert base70 < (1 << 20)
+    forced = ocg.default_config(split_k=2)
+    assert ocg.plan_ag(8, 0, 1024, 8192, 3584, forced)["split_k"] == 2
+    p = ocg.plan_info(ocg.OP_AG_GEMM, 8, 0, 1024, 8192, 3584, forced)
+    assert ws(8, 1024, 8192, 3584, forced) >= base70 + p["n_tiles"] * p["BM"] * p["BN"] * 4
+    # split off, explicitly
+    assert ocg.plan_ag(8, 0, 512, 4096, 1792, ocg.default_config(split_k=1))["split_k"] == 1
+    # split needs inline copies, one K-slab and K % 128 == 0; the knob is 0..2
+    for cfg, K in ((ocg.default_config(split_k=2, transfer=ocg.TRANSFER_SIDE), 4096),
+                   (ocg.default_config(split_k=2, kslab_cols=1024), 4096),
+                   (ocg.default_config(split_k=2), 4160),
+                   (ocg.default_config(split_k=2, mode=ocg.MODE_COPY_ONLY), 4096),
+                   (ocg.default_config(split_k=3), 4096), (ocg.default_config(split_k=-1), 4096)):
+        with pytest.raises(ocg.OcgError):
+            ocg.plan_ag(8, 0, 512, K, 1792, cfg)
+        assert ws(8, 512, K, 1792, cfg) == 0
+    # the automatic choice only splits where it can: SIDE and K-slabs keep whole tiles
+    assert ocg.plan_ag(8, 0, 128, 8192, 1792, ocg.default_config(transfer=ocg.TRANSFER_SIDE))["split_k"] == 1
+    assert ocg.plan_ag(8, 0, 128, 8192, 1792, ocg.default_config(kslab_cols=1024))["split_k"] == 1
+    assert ocg.plan_ag(8, 0, 128, 8128, 1792)["split_k"] == 1
+
+
+@pytest.mark.parametrize("case", [(8, 512, 4096, 1792, 0, -1), (8, 512, 4096, 1792, 5, -1),
+                                  (3, 300, 256, 600, 1, ocg.TILE_256x224), (5, 37, 128, 40, 4, ocg.TILE_128x128),
+                                  (2, 200, 384, 296, 1, ocg.TILE_256x256)])
+@pytest.mark.parametrize("mode", ["fused", "gemm_only"])
+def test_split_plan_matches_oracle_schedule(case, mode):
+    R, m, K, N, local, tile = case
+    modes = {"fused": 0, "gemm_only": 1}
+    cfg = ocg.default_config(tile=tile, mode=modes[mode], split_k=2)
+    info = ocg.plan_info(ocg.OP_AG_GEMM, R, local, m, K, N, cfg)
+    ag = ocg.plan_ag(R, local, m, K, N, cfg)
+    assert ag["split_k"] == 2 and ag["nks"] == 1
+    n_cb = -(-N // info["BN"])
+    assert ag["rows_per_round"] == max(1, ag_grid_tiles(info, R, m, N) // (n_cb * 2)) * info["BM"]
+    want = sch.ag_gemm_plan(R, m, K, N, local, info["BM"], info["BN"], info["slab_rows"], info["copy_rows"],
+                            True, mode, KS=K, rpr=ag["rows_per_round"], sk=2)
+    assert len(want) == info["n_copy_or_strips"] + 2 * info["n_tiles"]
+    units = [t for t in want if isinstance(t, sch.Tile)]
+    assert [t.part for t in units] == [0, 1] * info["n_tiles"]
+    for t in want + [None]:
+        ticket = len(want) if t is None else t.ticket
+        d = ocg.plan_task(ocg.OP_AG_GEMM, R, local, m, K, N, ticket, cfg)
+        if t is None:
+            assert d[0] == 0
+        elif isinstance(t, sch.CopyTask):
+            assert d[:7] == [1, t.chunk, t.piece, t.row0, t.row1, t.slab, t.kslab]
+        else:
+            deps = list(t.deps)
+            assert d[:4] == [2, t.rb, t.cb, len(deps)] and d[7] == t.part
+            assert d[4:4 + min(3, len(deps))] == deps[:3]
 
 
 @pytest.mark.parametrize("R,M,K,N,local,tile", [(8, 4096, 1792, 4096, 0, -1), (8, 4096, 1792, 4096, 5, -1),

@@ -54,11 +54,12 @@ def test_ag_gemm_small_full(ocg, case, transfer):
     x = workloads.make_ag_gemm(R, m, K, N, seed=100 + R * 7 + local, dist=dist,
                                scale=1.0 if dist == "uniform" else 0.02)
     say("ag_gemm", name, R, m, K, N, local, tile, "transfer", transfer, "kslab", kslab)
-    c, ag = run(ocg, x, local, ocg.default_config(tile=tile, transfer=transfer, kslab_cols=kslab))
+    cfg = ocg.default_config(tile=tile, transfer=transfer, kslab_cols=kslab)
+    c, ag = run(ocg, x, local, cfg)
     a_full, want = oracle.ag_gemm(x.a_chunks, x.b)
     assert np.array_equal(to_bits(ag), a_full), "gathered buffer must be a bit-exact copy"
     assert_gate(to_bits(c), want, name)
-    ws = ocg.Workspace.cached(ocg.OP_AG_GEMM, R, m, K, N)
+    ws = ocg.Workspace.cached(ocg.OP_AG_GEMM, R, m, K, N, config=cfg)
     ws.check()
 
 
@@ -68,7 +69,8 @@ def _check_trace(ocg, x, local, cfg, recs):
     ag = ocg.plan_ag(x.R, local, x.m, x.K, x.N, cfg, handle=h)
     plan = sch.ag_gemm_plan(x.R, x.m, x.K, x.N, local, info["BM"], info["BN"], info["slab_rows"],
                             info["copy_rows"], bool(cfg.swizzle), ["fused", "gemm_only", "copy_only"][cfg.mode],
-                            KS=ag["kslab_cols"], xcd_remap=bool(cfg.xcd_remap), rpr=ag["rows_per_round"])
+                            KS=ag["kslab_cols"], xcd_remap=bool(cfg.xcd_remap), rpr=ag["rows_per_round"],
+                            sk=ag["split_k"])
     nks = ag["nks"]
     assert len(recs) == len(plan)
     assert np.array_equal(recs["ticket"], np.arange(len(plan))), "every ticket executed exactly once"
@@ -83,16 +85,22 @@ def _check_trace(ocg, x, local, cfg, recs):
             if r["d"] & 1:
                 assert t.flag not in publish, "a flag is published once"
                 publish[t.flag] = int(r["t_ready"])
+    writers = {}
     for t, r in zip(plan, recs):
         if isinstance(t, sch.Tile):
             assert (r["kind"], r["a"], r["b"], r["c"]) == (2, t.rb, t.cb, len(t.deps))
             assert int(r["queue"]) == (t.queue << 16) | t.qticket, "tile taken from its queue"
+            # d: bit 0 the K part; bit 1 (split units) this half combined and wrote the tile
+            assert int(r["d"]) & 1 == t.part
+            writers[(t.rb, t.cb)] = writers.get((t.rb, t.cb), 0) + (1 if ag["split_k"] == 1 else int(r["d"]) >> 1)
             if t.deps:
                 assert r["flag_seen"] == epoch, "the tile saw its flag at this call's epoch"
                 # started on its first K-slab only after every slab it reads published it
                 assert int(r["t_ready"]) >= max(publish[s * nks] for s in t.deps)
                 # and finished after every K-slab of them was published
                 assert int(r["t_end"]) >= max(publish[s * nks + j] for s in t.deps for j in range(nks))
+    if cfg.mode != 2:
+        assert len(writers) == info["n_tiles"] and set(writers.values()) == {1}, "each tile written once"
     tgt = sch.slab_targets(x.R, x.m, info["slab_rows"], info["copy_rows"])
     if cfg.mode != 1:
         assert sorted(publish) == sorted(s * nks + j for s, n in enumerate(tgt) if n for j in range(nks))
@@ -108,7 +116,7 @@ def test_ag_gemm_trace_matches_schedule(ocg, local, swizzle, transfer, kslab, xc
     cfg = ocg.default_config(tile=ocg.TILE_128x224, swizzle=swizzle, transfer=transfer, kslab_cols=kslab,
                              xcd_remap=xcd)
     info = ocg.plan_info(ocg.OP_AG_GEMM, x.R, local, x.m, x.K, x.N, cfg)
-    n = info["n_copy_or_strips"] + info["n_tiles"]
+    n = info["n_copy_or_strips"] + info["n_tiles"] * ocg.plan_ag(x.R, local, x.m, x.K, x.N, cfg)["split_k"]
     tr = Trace(n + 8)
     tr.attach(cfg)
     say("ag_gemm trace", local, swizzle, transfer, kslab, xcd)
@@ -117,6 +125,90 @@ def test_ag_gemm_trace_matches_schedule(ocg, local, swizzle, transfer, kslab, xc
     _check_trace(ocg, x, local, cfg, recs)
     assert_gate(to_bits(c), oracle.ag_gemm(x.a_chunks, x.b)[1], "trace case")
     assert np.array_equal(to_bits(ag), np.concatenate(x.a_chunks))
+
+
+SPLIT = [
+    # name, R, m, K, N, local, tile
+    ("split_256x224", 3, 300, 512, 520, 2, 0),
+    ("split_128x128", 5, 37, 256, 40, 4, 3),
+    ("split_256x256", 2, 260, 768, 264, 0, 4),
+    ("split_128x256", 2, 256, 512, 264, 1, 2),
+    ("split_r1_128x224", 1, 200, 128, 232, 0, 1),
+]
+
+
+def _close_to(a_bits, b_bits, what):
+    """Two bf16 results of one product summed in another fp32 order: equal
+    but for last-bit rounding differences -- one bf16 step, or, for results
+    near zero (where the fp32 sums' own rounding, ~1e-8 here, exceeds a step),
+    a floor of 2^-16 of the outputs' RMS."""
+    a, b = oracle.decode_bf16(a_bits), oracle.decode_bf16(b_bits)
+    floor = 2.0 ** -16 * float(np.sqrt(np.mean(b.astype(np.float64) ** 2)))
+    step = 2.0 ** -7 * np.maximum(np.abs(a), np.abs(b)) + floor
+    assert np.all(np.abs(a - b) <= step), f"{what}: more than one bf16 step apart"
+    assert np.mean(a != b) < 0.05, f"{what}: {np.mean(a != b):.3f} of the outputs differ"
+
+
+@pytest.mark.parametrize("case", SPLIT, ids=[c[0] for c in SPLIT])
+def test_ag_gemm_split_k(ocg, case):
+    """Every tile as two K halves (split_k = 2): the gathered buffer bit for
+    bit, C within the gate of the float64 oracle, the same bits on repeated
+    calls (the halves' fp32 sums add the same whichever half finishes first),
+    and within a bf16 step of the unsplit kernel's C."""
+    name, R, m, K, N, local, tile = case
+    x = workloads.make_ag_gemm(R, m, K, N, seed=400 + R * 7 + local, dist="normal", scale=0.02)
+    split = ocg.default_config(tile=tile, split_k=2)
+    assert ocg.plan_ag(R, local, m, K, N, split)["split_k"] == 2
+    a_full, want = oracle.ag_gemm(x.a_chunks, x.b)
+    outs = []
+    for i in range(3):
+        say("ag_gemm split", name, "call", i)
+        c, ag = run(ocg, x, local, split)
+        assert np.array_equal(to_bits(ag), a_full), "gathered buffer must be a bit-exact copy"
+        outs.append(to_bits(c))
+    assert_gate(outs[0], want, name)
+    assert all(np.array_equal(o, outs[0]) for o in outs[1:]), "split-K output must not depend on timing"
+    say("ag_gemm unsplit", name)
+    c1, _ = run(ocg, x, local, ocg.default_config(tile=tile, split_k=1))
+    _close_to(outs[0], to_bits(c1), name)
+    ocg.Workspace.cached(ocg.OP_AG_GEMM, R, m, K, N, config=split).check()
+
+
+def test_ag_gemm_split_k_back_to_back_and_trace(ocg):
+    """Split calls back to back on one workspace with no host synchronisation
+    (every tile's arrival count returns to zero and its flag carries the
+    call's epoch), a traced call against the schedule oracle (each tile's two
+    halves, exactly one of them writing the tile), and GEMM-only against
+    fused (same units, same arithmetic)."""
+    x = workloads.make_ag_gemm(4, 200, 1024, 456, seed=78, dist="normal", scale=0.02)
+    chunks = [to_dev(a) for a in x.a_chunks]
+    b = to_dev(x.b)
+    cfg = ocg.default_config(tile=ocg.TILE_128x224, split_k=2)
+    ws = ocg.Workspace(ocg.OP_AG_GEMM, x.R, x.m, x.K, x.N, config=cfg)
+    a_full, want = oracle.ag_gemm(x.a_chunks, x.b)
+    c = poison((x.R * x.m, x.N))
+    say("ag_gemm split back to back")
+    for i in range(8):
+        ocg.ag_gemm(chunks, b, i % 4, a_gathered=poison((x.R * x.m, x.K)), c=c, workspace=ws, config=cfg)
+    ws.check()
+    assert_gate(to_bits(c), want, "split back to back")
+    info = ocg.plan_info(ocg.OP_AG_GEMM, x.R, 1, x.m, x.K, x.N, cfg)
+    n = info["n_copy_or_strips"] + 2 * info["n_tiles"]
+    tr = Trace(n + 8)
+    tr.attach(cfg)
+    say("ag_gemm split trace")
+    ag = poison((x.R * x.m, x.K))
+    c_t, _ = ocg.ag_gemm(chunks, b, 1, a_gathered=ag, workspace=ws, config=cfg)
+    torch.cuda.synchronize()
+    recs = tr.read(n)
+    ws.check()
+    assert _check_trace(ocg, x, 1, cfg, recs)["split_k"] == 2
+    assert np.array_equal(to_bits(ag), a_full)
+    say("ag_gemm split gemm only")
+    c_g, _ = ocg.ag_gemm(chunks, b, 1, a_gathered=ag, workspace=ws,
+                         config=ocg.default_config(tile=ocg.TILE_128x224, split_k=2, mode=ocg.MODE_GEMM_ONLY))
+    torch.cuda.synchronize()
+    assert np.array_equal(to_bits(c_g), to_bits(c_t)), "same units, same arithmetic"
 
 
 @pytest.mark.parametrize("transfer", [INLINE, SIDE], ids=["inline", "side"])
@@ -135,7 +227,7 @@ def test_ag_gemm_late_publishes_make_tiles_wait(ocg, transfer):
     say("ag_gemm late publishes", transfer)
     c, ag = run(ocg, x, 0, cfg)
     recs = tr.read(n)
-    ocg.Workspace.cached(ocg.OP_AG_GEMM, x.R, x.m, x.K, x.N).check()
+    ocg.Workspace.cached(ocg.OP_AG_GEMM, x.R, x.m, x.K, x.N, config=cfg).check()
     a_full, want = oracle.ag_gemm(x.a_chunks, x.b)
     assert np.array_equal(to_bits(ag), a_full)
     assert_gate(to_bits(c), want, "late publishes")

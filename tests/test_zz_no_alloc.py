@@ -31,7 +31,9 @@ def test_noalloc_matches_ag_gemm(ocg):
         x = workloads.make_ag_gemm(R, m, K, N, seed=300 + i, dist="normal", scale=0.02)
         chunks = [to_dev(a) for a in x.a_chunks]
         b = to_dev(x.b)
-        cfg = ocg.default_config(transfer=transfer)
+        # split_k = 1: the same kernels on both sides (ocg_ag_gemm may split K
+        # where the scratch has no room for the halves' sums)
+        cfg = ocg.default_config(transfer=transfer, split_k=1)
         say("ag_gemm reference call", i, R, m, K, N, local, transfer)
         ag_ref, c_ref = poison((R * m, K)), poison((R * m, N))
         ws = ocg.Workspace(ocg.OP_AG_GEMM, R, m, K, N)
@@ -46,6 +48,13 @@ def test_noalloc_matches_ag_gemm(ocg):
         a_full, want = oracle.ag_gemm(x.a_chunks, x.b)
         assert np.array_equal(to_bits(ag), a_full)
         assert_gate(to_bits(c), want, f"noalloc call {i}")
+        # the automatic configuration: split only where the scratch holds the sums
+        say("ag_gemm_noalloc default config", i)
+        ag, c = poison((R * m, K)), poison((R * m, N))
+        ocg.ag_gemm_noalloc(chunks, b, local, ag, c, config=ocg.default_config(transfer=transfer))
+        torch.cuda.synchronize()
+        assert np.array_equal(to_bits(ag), a_full)
+        assert_gate(to_bits(c), want, f"noalloc default call {i}")
 
 
 def test_noalloc_rejects_shapes_beyond_the_scratch(ocg):
