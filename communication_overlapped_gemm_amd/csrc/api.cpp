@@ -312,11 +312,12 @@ int resolve_attn(int64_t m, int64_t Hkv, const ocg_config& c, int* S, int* CT) {
   if (c.copy_rows > 0) {
     *CT = c.copy_rows;
   } else {
-    // about 1 MiB per copy task: at the 16K-context share (2 x 64 tasks)
-    // a quarter of the workgroups gathers while the rest start on the
-    // local chunk's keys; 128 KiB tasks kept every workgroup copying first
-    // (563 vs 544 us per fused launch)
-    int64_t ct = (1024 * 1024) / row_bytes;
+    // about 512 KiB per copy task: at the 16K-context share (2 x 64 tasks)
+    // half the workgroups gather first while the rest start on the local
+    // chunk's keys. Per fused launch (one process, alternating): 1 MiB
+    // tasks 530.3 us, 512 KiB 517.5, 256 KiB 520.7, 128 KiB 519.4, 2 MiB
+    // 540.5; attention alone 491.2, copies alone 35.6
+    int64_t ct = (512 * 1024) / row_bytes;
     int p2 = 1;
     while ((int64_t)p2 * 2 <= ct) p2 *= 2;
     *CT = p2 < *S ? p2 : *S;

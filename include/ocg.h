@@ -396,10 +396,10 @@ int ocg_moe_combine_rs(ocg_handle h, const void* y, const float* topk_w, int R, 
  *   out          : bf16 [m, Hq, d], written
  * Copy tasks pull each peer chunk of keys and values into the gathered
  * buffers slab by slab (slab_rows tokens, default the whole chunk; tasks of
- * copy_rows tokens, default about 1 MiB of one tensor) and publish a flag
+ * copy_rows tokens, default about 512 KiB of one tensor) and publish a flag
  * per slab; each tile (256 query rows of one kv head) starts
- * on the local chunk, read from its own shard, and waits on a peer chunk's
- * flags before loading it. Requires d == 128, Hq % Hkv == 0,
+ * on the local chunk, read from its own shard, and before its first load of
+ * a peer chunk waits on the flags of every peer chunk. Requires d == 128, Hq % Hkv == 0,
  * R*m*Hkv*d < 2^31, m*Hq*d < 2^31, 16-byte aligned pointers; workspace from
  * ocg_workspace_bytes(OCG_OP_AG_ATTENTION, R, m, Hq, Hkv, 0, 0). cfg.tile is
  * ignored; cfg.mode GEMM_ONLY runs the attention with every flag treated as

@@ -308,10 +308,10 @@ def test_attention_plan_matches_oracle_schedule(case, swizzle, mode):
 
 
 def test_attention_plan_defaults_and_validation():
-    # the 16K-context GQA share: one flag per chunk, 512-token (1 MiB) copy
-    # tasks, 256 tiles (one per CU), 64 copy tickets
+    # the 16K-context GQA share: one flag per chunk, 256-token (512 KiB) copy
+    # tasks, 256 tiles (one per CU), 128 copy tickets
     p = ocg.plan_info(ocg.OP_AG_ATTENTION, 8, 0, 2048, 32, 8)
-    assert (p["slab_rows"], p["copy_rows"], p["n_tiles"], p["n_copy_or_strips"]) == (2048, 512, 256, 64)
+    assert (p["slab_rows"], p["copy_rows"], p["n_tiles"], p["n_copy_or_strips"]) == (2048, 256, 256, 128)
     lib = ocg.lib
     assert lib.ocg_workspace_bytes(None, ocg.OP_AG_ATTENTION, 8, 2048, 32, 8, 0, 0) > 256
     assert lib.ocg_workspace_bytes(None, ocg.OP_AG_ATTENTION, 8, 2048, 30, 8, 0, 0) == 0   # Hq % Hkv
