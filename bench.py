@@ -323,12 +323,13 @@ def main() -> int:
                                f"(M=8192), B bf16 [8192,3584], N(0,0.02) seed 3, C bf16 [8192,3584]",
                    "tile": f"{info['BM']}x{info['BN']}", "slab_rows": info["slab_rows"],
                    "copy_rows": info["copy_rows"], "kslab_cols": plan["kslab_cols"], "transfer": transfer,
-                   "local_rank": 0},
+                   "split_k": plan["split_k"], "local_rank": 0},
         "pct_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic_record(khash),
-                     "kernel": f"ag_gemm_kernel<{info['BM']},{info['BN']}>",
+                     # as the profiler names it: the template flag marks split-K units
+                     "kernel": f"ag_gemm_kernel<{info['BM']}, {info['BN']}, {'true' if plan['split_k'] > 1 else 'false'}>",
                      "avg_launch_us": round(avg_launch_ms * 1e3, 2),
                      "algorithmic_flops_per_launch": flops, "kernel_hash": khash},
         "git_sha": git_sha(),
