@@ -4,7 +4,9 @@ tasks inline in the GEMM kernel, or a side producer kernel co-resident with
 it) and several K-slab widths, the 8B- and 70B-class shares on every output
 element, the gathered buffer bit for bit, the schedule trace against the
 oracle's re-derivation, forced late publishes (tiles that really wait, also
-inside their K loop), the measurement modes, and the timeout path."""
+inside their K loop), split K (tiles as two K halves: bit-stable across
+calls, one writer per tile, within a bf16 step of whole tiles), the
+measurement modes, and the timeout path."""
 import numpy as np
 import pytest
 import torch
