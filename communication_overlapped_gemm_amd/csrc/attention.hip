@@ -482,7 +482,7 @@ __global__ __launch_bounds__(kAThreads, 1) void ag_attention_kernel(AttnArgs arg
   const AttnPlan& p = args.plan;
   const Common& cm = args.cm;
   const uint32_t epoch = read_epoch(cm.hdr, s_bcast);
-  for (;;) {
+  while (p.n_copy > 0) {
     const uint32_t u = next_ticket(&cm.hdr->ticket, s_bcast);
     if ((int)u >= p.n_copy) break;
     run_kv_copy(args, (int)u, epoch);

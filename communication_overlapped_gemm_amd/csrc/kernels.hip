@@ -176,8 +176,8 @@ __global__ __launch_bounds__((Gemm<BM, BN>::NT), 1) void ag_gemm_kernel(AgArgs a
 
   // copy tasks: all of them, or (SIDE transfer) the first K-slab of the
   // first phase, so the first tiles need not wait for the side producer to
-  // start; the producer takes the rest
-  for (;;) {
+  // start; the producer takes the rest (none: no ticket to take)
+  while (p.n_inline > 0) {
     const uint32_t u = next_ticket(&cm.hdr->ticket, s_bcast);
     if ((int)u >= p.n_inline) break;
     run_copy_task<G::NT>(p, args.chunks, args.a_gathered, args.slab_cnt, args.slab_flag, (int)u, epoch, cm);
@@ -782,7 +782,7 @@ __global__ __launch_bounds__((Gemm<BM, BN>::NT), 1) void moe_gemm_kernel(MoeArgs
   const int lane = threadIdx.x & 63;
   const size_t wstride = (size_t)p.K * p.N;
 
-  for (;;) {
+  while (p.n_copy > 0) {
     const uint32_t u = next_ticket(&cm.hdr->ticket, s_bcast);
     if ((int)u >= p.n_copy) break;
     run_copy_task<G::NT>(p, args.chunks, args.a_gathered, args.slab_cnt, args.slab_flag, (int)u, epoch, cm);

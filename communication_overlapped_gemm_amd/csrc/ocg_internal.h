@@ -27,17 +27,25 @@ inline bool moe_tile_ok(int t) {
 }
 
 // Workspace header (first 256 bytes of every workspace).
+// Every counter the workgroups update sits in a 128-byte line of its own:
+// agent-scope atomics on one line are served one after the other, and with
+// all of them in one line the 224-256 workgroups of a launch took their
+// first ticket over ~10 us (the last XCD's tiles started that late).
+constexpr int kHdrWords = 32;    // uint32 words per 128-byte line
 struct WsHeader {
-  uint32_t ticket;     // next ticket of the running persistent kernel
-  uint32_t done;       // workgroups (of every kernel of the call) that finished
-  uint32_t epoch;      // epoch of the last completed call (flags carry epochs)
-  uint32_t error;      // bit 0: a flag wait timed out
-  uint32_t n_tiles;    // MoE: grouped tiles of the current routing
-  uint32_t xtick[8];   // next ticket of each XCD's tile queue
-  uint32_t side_ticket;  // next copy ticket of the side producer kernel
-  uint32_t pad[50];
+  uint32_t ticket;               // next ticket of the running persistent kernel
+  uint32_t pad_ticket[kHdrWords - 1];
+  uint32_t done;                 // workgroups (of every kernel of the call) that finished
+  uint32_t pad_done[kHdrWords - 1];
+  uint32_t side_ticket;          // next copy ticket of the side producer kernel
+  uint32_t pad_side[kHdrWords - 1];
+  uint32_t epoch;                // epoch of the last completed call (flags carry epochs)
+  uint32_t error;                // bit 0: a flag wait timed out
+  uint32_t n_tiles;              // MoE: grouped tiles of the current routing
+  uint32_t pad_misc[kHdrWords - 3];
+  uint32_t xtick[8 * kHdrWords]; // next ticket of XCD queue q at xtick[q * kHdrWords]
 };
-static_assert(sizeof(WsHeader) == 256, "header is 256 bytes");
+static_assert(sizeof(WsHeader) == 12 * 128, "header is twelve 128-byte lines");
 
 // Byte offsets of the workspace sections for one call shape.
 struct WsLayout {

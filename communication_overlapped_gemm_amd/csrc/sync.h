@@ -329,7 +329,7 @@ __device__ __forceinline__ int next_tile(WsHeader* hdr, int n_tiles, int* q, int
     return (int)t < n_tiles ? (int)t : -1;
   }
   for (;;) {
-    const uint32_t t = next_ticket(&hdr->xtick[*q], s_bcast);
+    const uint32_t t = next_ticket(&hdr->xtick[*q * kHdrWords], s_bcast);
     const int v = xcd_tile(*q, (int)t, n_tiles);
     if (v >= 0) {
       *t_out = t;
@@ -338,7 +338,7 @@ __device__ __forceinline__ int next_tile(WsHeader* hdr, int n_tiles, int* q, int
     if (threadIdx.x < 64) {
       bool open = false;
       if (threadIdx.x < kXcds) {
-        const uint32_t x = __hip_atomic_load(&hdr->xtick[threadIdx.x], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const uint32_t x = __hip_atomic_load(&hdr->xtick[threadIdx.x * kHdrWords], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         open = xcd_tile((int)threadIdx.x, (int)x, n_tiles) >= 0;
       }
       const uint64_t m = __ballot(open);
@@ -368,7 +368,7 @@ __device__ __forceinline__ void finish(WsHeader* hdr, uint32_t epoch, int total 
       __hip_atomic_store(&hdr->ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_store(&hdr->side_ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       for (int q = 0; q < kXcds; ++q)
-        __hip_atomic_store(&hdr->xtick[q], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&hdr->xtick[q * kHdrWords], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_store(&hdr->done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_store(&hdr->epoch, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
