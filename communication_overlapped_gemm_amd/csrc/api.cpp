@@ -232,12 +232,21 @@ int resolve(int op, int R, int64_t m, int64_t K, int64_t N, int E, int topk, con
     // for the side producer, whose workgroups keep 16 KiB in flight: small
     // tasks spread each K-slab over many of them
     int64_t ct = (r->transfer == OCG_TRANSFER_SIDE ? 16 * 1024 : 128 * 1024) / (r->KS > 0 ? r->KS : 1);
-    // grouped GEMM: every tile holds tokens of every rank, so no tile starts
-    // before the whole gather has landed; at least one task per workgroup
-    // spreads it over all of them (MoE share: 16-row tasks, 169 vs 175 us
-    // per step; the AllGather-GEMM, whose tiles wait only for their own
-    // rows' slabs, measured slower with such small tasks)
-    if (op == OCG_OP_AG_GROUPED_GEMM && cus > 0 && (int64_t)R * m / cus < ct) ct = (int64_t)R * m / cus;
+    // at least one task per workgroup, so the copies spread over all of
+    // them: the grouped GEMM's tiles hold tokens of every rank, so none
+    // starts before the whole gather has landed (MoE share: 16-row tasks,
+    // 169 vs 175 us per step); the AllGather-GEMM's tiles wait for their
+    // own rows' slabs, fed sooner the same way (8B share: 16-row tasks,
+    // 80.6-80.8 vs 82.3-82.8 us per fused launch; the 70B share keeps 16),
+    // but no task under 64 KiB, whose fixed cost (ticket, drain, publish)
+    // would outweigh its copy
+    const bool spread = op == OCG_OP_AG_GROUPED_GEMM || (op == OCG_OP_AG_GEMM && r->transfer == OCG_TRANSFER_INLINE);
+    if (spread && cus > 0) {
+      int64_t per_wg = (int64_t)R * m / cus;
+      const int64_t floor_rows = (32 * 1024) / (K > 0 ? K : 1);
+      if (per_wg < floor_rows) per_wg = floor_rows;
+      if (per_wg < ct) ct = per_wg;
+    }
     int p2 = 1;
     while ((int64_t)p2 * 2 <= ct) p2 *= 2;
     r->CT = p2 < r->S ? p2 : r->S;
