@@ -2,10 +2,12 @@
 ag_protocol_model.cpp) under ThreadSanitizer: std::thread workgroups run the
 kernels' ticket, counter and flag protocol on the library's closed-form
 schedule, for the inline and side-producer transfers, both chunk orders,
-several K-slab widths and repeated calls on one workspace. TSan must report
-no race (every read of gathered rows is ordered after its publish), and
-must report one when the model's publish is made relaxed (a planted
-mistake). A dead producer (a flag never published) must time out, set the
+several K-slab widths, split K (tiles as two K halves combined through a
+stored sum and a per-tile flag) and repeated calls on one workspace. TSan
+must report no race (every read of gathered rows, and of a stored half's
+sum, is ordered after its publish), and must report one when the model's
+publish is made relaxed (a planted mistake; also in the split-K combine
+alone). A dead producer (a flag never published) must time out, set the
 error word and still let every thread finish."""
 import os
 import shutil
@@ -39,7 +41,8 @@ def run(exe, *args, timeout=120):
 
 @pytest.mark.parametrize("args", [[], ["--inline"], ["--natural"], ["--local", "3"], ["--inline", "--local", "0"],
                                   ["--kslab", "1024"], ["--kslab", "512", "--local", "2"],
-                                  ["--calls", "5", "--natural", "--inline"]],
+                                  ["--calls", "5", "--natural", "--inline"], ["--split"],
+                                  ["--split", "--local", "0", "--calls", "5"], ["--split", "--natural"]],
                          ids=lambda a: " ".join(a) or "side")
 def test_protocol_race_free(model, args):
     r = run(model, *args)
@@ -51,6 +54,15 @@ def test_protocol_race_free(model, args):
 def test_planted_relaxed_publish_is_caught(model):
     r = run(model, "--relaxed", "--calls", "1")
     assert "WARNING: ThreadSanitizer: data race" in r.stderr
+    assert r.returncode == 66
+
+
+def test_planted_relaxed_split_publish_is_caught(model):
+    # split K: the halves' combine reads the first half's sum after the
+    # tile flag; a relaxed flag leaves that read unordered
+    r = run(model, "--split", "--relaxed-split", "--calls", "1")
+    assert "WARNING: ThreadSanitizer: data race" in r.stderr
+    assert "sk_part" in r.stderr or "tile(" in r.stderr, r.stderr[-3000:]
     assert r.returncode == 66
 
 
