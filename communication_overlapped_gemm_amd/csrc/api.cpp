@@ -178,12 +178,14 @@ int resolve(int op, int R, int64_t m, int64_t K, int64_t N, int E, int topk, con
   r->SK = 1;
   if (op == OCG_OP_AG_GEMM) {
     if (c.transfer < OCG_TRANSFER_AUTO || c.transfer > OCG_TRANSFER_SIDE) return OCG_ERR_INVALID_ARG;
-    // AUTO: INLINE. Measured in one process, alternating, at the 70B share:
-    // 412 us INLINE against 413 us SIDE per fused call -- under the chip's
-    // power limit the copies cost the same energy wherever they run -- and
-    // one kernel keeps the call simple for profilers that serialise
-    // dispatches (the SIDE GEMM kernel would wait for a producer that has
-    // not started).
+    // AUTO: INLINE. SIDE measures 1-3 % faster per fused call at the 70B
+    // share (two builds in one process, alternating: 391-412 against
+    // 402-416 us) and 12 % slower at the 8B share (one round of tiles), but
+    // its GEMM tiles wait on a second kernel: under a tool that runs
+    // dispatches one at a time they can wait out their bound. Guarding that
+    // (the producer marks itself started; a tile that finds it not started
+    // runs its copy tickets) was correct but cost ~10 us per 70B call, more
+    // than SIDE gains, so one kernel stays the default.
     r->transfer = c.transfer == OCG_TRANSFER_AUTO ? OCG_TRANSFER_INLINE : c.transfer;
     if (c.mode == OCG_MODE_GEMM_ONLY) r->transfer = OCG_TRANSFER_INLINE;   // no copies to place
     if (c.kslab_cols < 0 || c.kslab_cols % kMinKslabCols) return OCG_ERR_INVALID_ARG;
@@ -567,15 +569,19 @@ int ocg_ag_gemm(ocg_handle h, const void* const* a_chunks, int R, int local_rank
   hipStream_t s = (hipStream_t)stream;
   if (su.pgrid == 0)
     return launch_ag_gemm(a, su.rv.tile, su.ggrid < 1 ? 1 : su.ggrid, s) == hipSuccess ? OCG_OK : OCG_ERR_HIP;
-  // SIDE: the GEMM kernel on the caller's stream, the producer on the side
-  // stream, both after the caller's earlier work; the caller's stream then
-  // waits for the producer. The last workgroup of either kernel resets the
-  // workspace counters.
+  // SIDE: the producer on the side stream, then the GEMM kernel on the
+  // caller's stream, both after the caller's earlier work; the caller's
+  // stream then waits for the producer. The two kernels start a few
+  // microseconds apart, either one first; with the producer submitted first,
+  // a tool that runs dispatches one at a time (counter collection) mostly
+  // runs the copies before the tiles that wait on them (the other way round
+  // the tiles wait out their bound). The last workgroup of either kernel
+  // resets the workspace counters.
   a.cm.total_wgs = su.ggrid + su.pgrid;
   if (hipEventRecord(h->fork, s) != hipSuccess || hipStreamWaitEvent(h->side, h->fork, 0) != hipSuccess)
     return OCG_ERR_HIP;
-  if (su.ggrid > 0 && launch_ag_gemm(a, su.rv.tile, su.ggrid, s) != hipSuccess) return OCG_ERR_HIP;
   if (launch_ag_side_copy(a, su.pgrid, h->side) != hipSuccess) return OCG_ERR_HIP;
+  if (su.ggrid > 0 && launch_ag_gemm(a, su.rv.tile, su.ggrid, s) != hipSuccess) return OCG_ERR_HIP;
   if (hipEventRecord(h->join, h->side) != hipSuccess || hipStreamWaitEvent(s, h->join, 0) != hipSuccess)
     return OCG_ERR_HIP;
   return OCG_OK;

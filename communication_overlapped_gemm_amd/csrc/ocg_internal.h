@@ -26,7 +26,7 @@ inline bool moe_tile_ok(int t) {
   return t == OCG_TILE_128x224 || t == OCG_TILE_256x224 || t == OCG_TILE_288x224 || t == OCG_TILE_320x224;
 }
 
-// Workspace header (first 256 bytes of every workspace).
+// Workspace header (the first 1536 bytes of every workspace).
 // Every counter the workgroups update sits in a 128-byte line of its own:
 // agent-scope atomics on one line are served one after the other, and with
 // all of them in one line the 224-256 workgroups of a launch took their

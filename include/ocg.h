@@ -73,10 +73,11 @@ extern "C" {
  *             proceed while the tiles compute. The caller's stream waits for
  *             the producer before the call's later work; the GEMM tiles wait
  *             on the per-(slab, K-slab) flags it publishes.
- *   AUTO   -- INLINE (the two measure the same per call on one MI355X:
- *             the copies' energy counts against the chip's power limit
- *             either way; one kernel stays safe under profilers that
- *             serialise dispatches). SIDE is refused
+ *   AUTO   -- INLINE (SIDE measures 1-3 % faster per call at the 70B share
+ *             and slower at the 8B one; one kernel stays safe under
+ *             profilers that serialise dispatches, where SIDE's tiles may
+ *             wait out their bound for a producer that has not run:
+ *             ocg_check then reports the timeout). SIDE is refused
  *             (OCG_ERR_UNSUPPORTED_SHAPE) if the producer does not fit next
  *             to the GEMM kernel's workgroup.
  * (Pull transfers with a "transfer complete" flag per slab: "TileLink ..."
