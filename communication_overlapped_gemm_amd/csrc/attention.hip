@@ -95,6 +95,7 @@ __device__ void run_kv_copy(const AttnArgs& a, int u, uint32_t epoch) {
   const uint64_t t0 = now_ticks();
   const int tensor = u & 1;
   const CopyDesc d = copy_desc(p, u >> 1);
+  copy_delay(a.cm.copy_delay);   // test hook: publish late
   const uint16_t* src = (tensor ? a.v_chunks[d.chunk] : a.k_chunks[d.chunk]) + (size_t)(d.row0 - d.chunk * p.m) * p.K;
   uint16_t* dst = (tensor ? a.v_gathered : a.k_gathered) + (size_t)d.row0 * p.K;
   copy_granules<kAThreads>(src, dst, (uint32_t)((size_t)(d.row1 - d.row0) * p.K / 8));

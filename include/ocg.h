@@ -152,7 +152,9 @@ typedef struct ocg_config {
                                0 = auto: the whole K for INLINE, 512 for SIDE */
   uint32_t copy_delay;      /* test hook: a copy task of K-slab j first sleeps (j + 1) x this many
                                rounds of s_sleep 127 (~8k cycles each) -- forces late publishes,
-                               later K-slabs later; 0 = off */
+                               later K-slabs later (copy tasks of the AG-GEMM, the grouped GEMM and
+                               the MoE layer; the attention's copy tasks, which have no K-slabs,
+                               sleep this many rounds); 0 = off */
   int32_t xcd_remap;        /* 1 = tiles dealt in batches to per-XCD queues (default);
                                0 = one queue in plain tile order (ablation) */
   int32_t side_grid;        /* SIDE transfer: producer workgroups (one per compute unit at most

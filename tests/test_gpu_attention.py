@@ -203,3 +203,26 @@ def test_ag_attention_16k_retrieval_all_rows(ocg):
     got = oracle.decode_bf16(out)
     bad = np.abs(got - picked) > 2.0 ** -8 * np.abs(picked) + 1e-6
     assert not bad.any(), f"{bad.sum()} elements differ from their target value rows"
+
+
+def test_ag_attention_late_publishes_make_tiles_wait(ocg):
+    """Forced late publishes (copy_delay: every copy task first sleeps ~0.1 ms):
+    tiles reach their peer keys before the peer chunks land, spin on the slab
+    flags, see them only after a publish, and the output stays in the gate
+    (gathered buffers start poisoned with NaN)."""
+    x = workloads.make_attention(3, 200, 8, 2, D, seed=697, local_rank=1)
+    cfg = ocg.default_config(slab_rows=64, copy_delay=24)
+    info = ocg.plan_info(ocg.OP_AG_ATTENTION, 3, 1, 200, 8, 2, cfg)
+    n_copy, n_tiles = info["n_copy_or_strips"], info["n_tiles"]
+    tr = Trace(n_copy + n_tiles)
+    tr.attach(cfg)
+    say("ag_attention late publishes")
+    check(x, *run(ocg, x, cfg), "late publishes")
+    recs = tr.read(n_copy + n_tiles)
+    cp, tl = recs[:n_copy], recs[n_copy:]
+    assert (cp["kind"] == 1).all() and (tl["kind"] == 7).all()
+    first_pub = int(cp["t_ready"][cp["d"] == 1].min())
+    assert (tl["t_ready"] >= first_pub).all(), "a tile passed its wait before any publish"
+    spin = (tl["t_ready"].astype(np.int64) - tl["t_start"].astype(np.int64)).max()
+    assert spin > 2000, f"tiles really spun (longest wait {spin / 100:.1f} us, want > 20 us)"
+    ocg.Workspace.cached(ocg.OP_AG_ATTENTION, 3, 200, 8, 2).check()

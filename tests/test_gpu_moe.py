@@ -133,3 +133,32 @@ def test_moe_full_workload(ocg):
     say("moe full workload")
     o = run(ocg, x, 0)
     check(ocg, x, o, "ag_moe")
+
+
+def test_moe_late_publishes_make_tiles_wait(ocg):
+    """Forced late publishes (copy_delay: every copy task first sleeps ~0.1 ms):
+    grouped tiles whose tokens come from peer ranks spin on the slab flags,
+    see them only after a publish, and the results stay exact (buffers start
+    poisoned with NaN, so a read before a publish would show)."""
+    R, m, K, N, E, topk = 4, 100, 192, 232, 8, 2
+    x = workloads.make_moe(R, m, K, N, E, seed=331, topk=topk, scale=0.5)
+    cfg = ocg.default_config(copy_delay=24)
+    info = ocg.plan_info(ocg.OP_AG_GROUPED_GEMM, R, 1, m, K, N, cfg, E=E, topk=topk)
+    n_copy = info["n_copy_or_strips"]
+    tr = Trace(n_copy + 4096)
+    tr.attach(cfg)
+    say("moe late publishes")
+    o = run(ocg, x, 1, cfg)
+    check(ocg, x, o, "moe late publishes")
+    recs = tr.read(n_copy + 4096)
+    cp = recs[:n_copy]
+    assert (cp["kind"] == 1).all()
+    tiles = recs[recs["kind"] == 4]
+    tiles = tiles[tiles["epoch"] == cp["epoch"][0]]
+    assert len(tiles) > 0
+    waited = tiles[(tiles["d"] >> 16) > 0]
+    assert len(waited) > 0, "some grouped tile waited on slab flags"
+    first_pub = int(cp["t_ready"][cp["d"] & 1 == 1].min())
+    assert (waited["t_ready"] >= first_pub).all(), "a tile passed its wait before any publish"
+    spin = (waited["t_ready"].astype(np.int64) - waited["t_start"].astype(np.int64)).max()
+    assert spin > 2000, f"tiles really spun (longest wait {spin / 100:.1f} us, want > 20 us)"
