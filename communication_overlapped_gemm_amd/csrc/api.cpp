@@ -113,11 +113,14 @@ bool shape_ok(int R, int64_t m, int64_t K, int64_t N) {
 // faster).
 // Speeds from GEMM-only launches at the 8B AllGather share (M 4096, K 4096,
 // N 1792; one MI355X): 256x224 tiles 93.6 us for 128 tiles (one round, half
-// the CUs idle) = 1; 128x256 74.6 us for 224 tiles -> 0.717; 128x224 74.8 us
-// for 256 -> 0.626; 256x256 104.2 us for 112 -> 1.03; 128x128 94.0 us for
-// 448 (two rounds) -> 0.57.
+// the CUs idle) = 1; 128x256 74.6 us for 224 tiles -> 0.717; 256x256 104.2
+// us for 112 -> 1.03; 128x128 94.0 us for 448 (two rounds) -> 0.57. 128x224
+// (256 tiles, one per CU) measured 74.8 us then (0.626); since the workspace
+// counters got cache lines of their own it runs 61.9 us against 66.2 us for
+// 128x256 (same process, alternating): 0.935 of 128x256's speed per output
+// element -> 0.670.
 double tile_cost(int t, int64_t M, int64_t N, int64_t K, int cus, int sk) {
-  static const double eff[OCG_TILE_COUNT] = {1.0, 0.626, 0.717, 0.57, 1.03, 0.0, 0.0};
+  static const double eff[OCG_TILE_COUNT] = {1.0, 0.670, 0.717, 0.57, 1.03, 0.0, 0.0};
   if (t < 0 || t >= OCG_TILE_COUNT || eff[t] <= 0) return 1e300;   // grouped-GEMM-only presets
   const int64_t units = cdiv((int)M, tile_bm(t)) * (int64_t)cdiv((int)N, tile_bn(t)) * sk;
   const int64_t rounds = (units + cus - 1) / cus;

@@ -92,10 +92,10 @@ def test_plan_info_tile_choice():
     p = ocg.plan_info(ocg.OP_AG_GEMM, 8, 0, 1024, 8192, 3584)
     assert (p["BM"], p["BN"], p["n_tiles"]) == (256, 224, 512)
     assert ocg.plan_ag(8, 0, 1024, 8192, 3584)["split_k"] == 1
-    # 8B share: 128x256 (224 tiles, one round), whole tiles (K halves of
-    # 256x224 tiles measured slower)
+    # 8B share: 128x224 (256 tiles, one per CU), whole tiles (K halves of
+    # 256x224 tiles and 224 tiles of 128x256 measured slower)
     p = ocg.plan_info(ocg.OP_AG_GEMM, 8, 0, 512, 4096, 1792)
-    assert (p["BM"], p["BN"], p["n_tiles"]) == (128, 256, 224)
+    assert (p["BM"], p["BN"], p["n_tiles"]) == (128, 224, 256)
     assert ocg.plan_ag(8, 0, 512, 4096, 1792)["split_k"] == 1
     # a 1024-row share with K 8192: 112 tiles of 128x128 fill under half the
     # CUs, so they run as 224 K halves
