@@ -16,16 +16,15 @@ is not on that path). In the current code the loop exit also runs a dozen
 scalar instructions, a wait and a barrier before the first accumulator
 read, so the pad is a margin there rather than the only guard; the check is
 that the distance holds, whatever provides it."""
+import importlib.util
 import os
 import re
 import subprocess
-import sys
 import tempfile
 
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-sys.path.insert(0, os.path.join(ROOT, "communication_overlapped_gemm_amd"))
 
 WAIT_STATES = 19
 AREG = re.compile(r"\ba(\d+)\b|\ba\[(\d+):(\d+)\]")
@@ -93,7 +92,11 @@ def check_tied_hazards(asm: str):
 
 
 def _compile_asm(tmp):
-    import build as B
+    # the package's build script, loaded by path (no module-name lookup)
+    spec = importlib.util.spec_from_file_location(
+        "ocg_build", os.path.join(ROOT, "communication_overlapped_gemm_amd", "build.py"))
+    B = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(B)
     out = os.path.join(tmp, "kernels.s")
     cmd = [B.hipcc(), *B.FLAGS, "--cuda-device-only", "-S", os.path.join(B.CSRC, "kernels.hip"), "-o", out]
     res = subprocess.run(cmd, capture_output=True, text=True)
